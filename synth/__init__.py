@@ -1,0 +1,211 @@
+"""Seeded synthetic inputs for the KDA operator.
+
+This module is shared by the tests, the benchmark and the smoke check.  It
+draws random numbers and shapes them into operator inputs; it contains none
+of the operator's own arithmetic (no recurrence, no gate cumsum, no chunk
+math), so both the oracle and the HIP path can consume what it produces.
+
+Recipe (numpy ``Generator(PCG64(seed))``, every draw float32):
+
+* draw order: sequence lengths (packed-varlen workload only), q, k, v, z_beta,
+  z_alpha, the long-memory channel mask (long-sequence workload only), S0;
+* q and k are L2-normalised per (token, head) over the key dimension in
+  float32: x / max(||x||, 1e-6);
+* beta = sigmoid(z_beta);
+* log_alpha = -softplus(z_alpha) = -(max(z, 0) + log1p(exp(-|z|)));
+* bf16 tensors are rounded from float32 to nearest-even once, here, and both
+  sides read those same rounded values.
+
+The five standard workloads (``WORKLOADS``) mirror the operator's five
+reference shapes: a tiny fp32 case, a 4 x 4096 batch, one 131072-token
+sequence with 5% long-memory channels, a 64-sequence packed batch with
+log-uniform lengths and a random initial state, and a batched decode.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+
+
+# --------------------------------------------------------------------------
+# bf16 helpers (bit-level; numpy has no bfloat16)
+# --------------------------------------------------------------------------
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 -> bfloat16 (nearest-even); return the uint16 bit patterns."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    u = u + 0x7FFF + ((u >> 16) & 1)
+    return (u >> 16).astype(np.uint16)
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Expand bfloat16 bit patterns to the float32 values they denote."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """float32 values rounded to the nearest bfloat16 (returned as float32)."""
+    return bf16_to_f32(bf16_bits(x))
+
+
+# --------------------------------------------------------------------------
+# element-wise input shaping
+# --------------------------------------------------------------------------
+
+def l2norm_f32(x: np.ndarray) -> np.ndarray:
+    x = x.astype(np.float32, copy=False)
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True, dtype=np.float32))
+    return (x / np.maximum(n, np.float32(1e-6))).astype(np.float32)
+
+
+def sigmoid_f32(z: np.ndarray) -> np.ndarray:
+    return (1.0 / (1.0 + np.exp(-z.astype(np.float64)))).astype(np.float32)
+
+
+def neg_softplus_f32(z: np.ndarray) -> np.ndarray:
+    z64 = z.astype(np.float64)
+    return (-(np.maximum(z64, 0.0) + np.log1p(np.exp(-np.abs(z64))))).astype(np.float32)
+
+
+# --------------------------------------------------------------------------
+# workloads
+# --------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class PrefillInputs:
+    """Host-side prefill inputs.  Float arrays hold the exact values both sides
+    use (bf16-rounded where ``io_dtype == 'bf16'``)."""
+    q: np.ndarray            # [T_tot, H, dk] float32
+    k: np.ndarray            # [T_tot, H, dk] float32
+    v: np.ndarray            # [T_tot, H, dv] float32
+    log_alpha: np.ndarray    # [T_tot, H, dk] float32
+    beta: np.ndarray         # [T_tot, H]     float32
+    cu_seqlens: np.ndarray   # [N + 1]        int32
+    S0: Optional[np.ndarray]  # [N, H, dk, dv] float32 or None
+    io_dtype: str            # 'f32' or 'bf16'
+    chunk: int = 64
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.cu_seqlens.shape[0] - 1)
+
+    @property
+    def total_tokens(self) -> int:
+        return int(self.cu_seqlens[-1])
+
+    @property
+    def num_heads(self) -> int:
+        return int(self.q.shape[1])
+
+
+def make_prefill(lengths, H: int, dk: int, dv: int, io_dtype: str, seed: int,
+                 S0_std: Optional[float] = None, long_memory_frac: float = 0.0,
+                 chunk: int = 64, lengths_from_rng=None) -> PrefillInputs:
+    """Generic seeded prefill inputs.
+
+    lengths: list of sequence lengths, or None when ``lengths_from_rng`` (a
+    callable taking the Generator) draws them first.  ``long_memory_frac``
+    picks round(frac * dk) key channels per head whose forget gate stays
+    near 1: log_alpha = -1e-5 * softplus(z) on those channels for every token.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if lengths_from_rng is not None:
+        lengths = lengths_from_rng(rng)
+    lengths = [int(x) for x in lengths]
+    cu = np.zeros(len(lengths) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lengths)
+    T = int(cu[-1])
+    q = rng.standard_normal((T, H, dk), dtype=np.float32)
+    k = rng.standard_normal((T, H, dk), dtype=np.float32)
+    v = rng.standard_normal((T, H, dv), dtype=np.float32)
+    zb = rng.standard_normal((T, H), dtype=np.float32)
+    za = rng.standard_normal((T, H, dk), dtype=np.float32)
+    q = l2norm_f32(q)
+    k = l2norm_f32(k)
+    beta = sigmoid_f32(zb)
+    la = neg_softplus_f32(za)
+    if long_memory_frac > 0.0:
+        nlm = int(round(long_memory_frac * dk))
+        for h in range(H):
+            ch = rng.choice(dk, size=nlm, replace=False)
+            la[:, h, ch] = (np.float32(1e-5) * la[:, h, ch]).astype(np.float32)
+    S0 = None
+    if S0_std is not None:
+        S0 = (rng.standard_normal((len(lengths), H, dk, dv), dtype=np.float32) * np.float32(S0_std)).astype(np.float32)
+    if io_dtype == "bf16":
+        q, k, v = bf16_round(q), bf16_round(k), bf16_round(v)
+    elif io_dtype != "f32":
+        raise ValueError(io_dtype)
+    return PrefillInputs(q=q, k=k, v=v, log_alpha=la, beta=beta, cu_seqlens=cu, S0=S0,
+                         io_dtype=io_dtype, chunk=chunk)
+
+
+def _loguniform_lengths(n: int, lo: int, hi: int):
+    def draw(rng):
+        u = rng.uniform(math.log(lo), math.log(hi), size=n)
+        return [int(math.floor(math.exp(x))) for x in u]
+    return draw
+
+
+# Workload descriptors.  seed = 1000 + workload index.
+WORKLOADS = {
+    "tiny_f32": dict(index=0, kind="prefill", lengths=[256], H=2, dk=64, dv=64, io_dtype="f32"),
+    "batch4x4096_bf16": dict(index=1, kind="prefill", lengths=[4096] * 4, H=16, dk=128, dv=128, io_dtype="bf16"),
+    "long131072_bf16": dict(index=2, kind="prefill", lengths=[131072], H=32, dk=128, dv=128, io_dtype="bf16",
+                            long_memory_frac=0.05),
+    "varlen64_bf16": dict(index=3, kind="prefill", lengths=None, H=32, dk=128, dv=128, io_dtype="bf16",
+                          S0_std=0.02, varlen=(64, 128, 32768)),
+    "decode256x32_bf16": dict(index=4, kind="decode", B=256, H=32, dk=128, dv=128, io_dtype="bf16",
+                              steps=1024, S0_std=0.02),
+}
+
+
+def workload_prefill(name: str, lengths_override=None, H_override=None) -> PrefillInputs:
+    """Inputs of a standard prefill workload (optionally with fewer heads or
+    other lengths, keeping the same distributions and seed)."""
+    w = WORKLOADS[name]
+    assert w["kind"] == "prefill"
+    seed = 1000 + w["index"]
+    H = H_override or w["H"]
+    draw = None
+    lengths = lengths_override if lengths_override is not None else w["lengths"]
+    if lengths is None:
+        n, lo, hi = w["varlen"]
+        draw = _loguniform_lengths(n, lo, hi)
+    return make_prefill(lengths, H, w["dk"], w["dv"], w["io_dtype"], seed,
+                        S0_std=w.get("S0_std"), long_memory_frac=w.get("long_memory_frac", 0.0),
+                        lengths_from_rng=draw)
+
+
+@dataclasses.dataclass
+class DecodeStepInputs:
+    q: np.ndarray          # [B, H, dk] float32 (bf16-rounded for bf16 io)
+    k: np.ndarray
+    v: np.ndarray          # [B, H, dv]
+    log_alpha: np.ndarray  # [B, H, dk] float32
+    beta: np.ndarray       # [B, H]     float32
+
+
+def make_decode_state(B: int, H: int, dk: int, dv: int, std: float, seed: int) -> np.ndarray:
+    """Initial decode states S ~ N(0, std^2), float32 [B, H, dk, dv]."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return (rng.standard_normal((B, H, dk, dv), dtype=np.float32) * np.float32(std)).astype(np.float32)
+
+
+def make_decode_step(B: int, H: int, dk: int, dv: int, io_dtype: str, seed: int, step: int) -> DecodeStepInputs:
+    """Fresh per-token decode inputs for step ``step`` (its own PCG64 stream,
+    so any step can be regenerated without drawing the earlier ones)."""
+    rng = np.random.Generator(np.random.PCG64([seed, step]))
+    q = l2norm_f32(rng.standard_normal((B, H, dk), dtype=np.float32))
+    k = l2norm_f32(rng.standard_normal((B, H, dk), dtype=np.float32))
+    v = rng.standard_normal((B, H, dv), dtype=np.float32)
+    beta = sigmoid_f32(rng.standard_normal((B, H), dtype=np.float32))
+    la = neg_softplus_f32(rng.standard_normal((B, H, dk), dtype=np.float32))
+    if io_dtype == "bf16":
+        q, k, v = bf16_round(q), bf16_round(k), bf16_round(v)
+    return DecodeStepInputs(q=q, k=k, v=v, log_alpha=la, beta=beta)
