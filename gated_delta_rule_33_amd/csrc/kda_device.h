@@ -1,0 +1,72 @@
+// kda_device.h -- device-side helpers shared by the libkda kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+// bfloat16 stored as raw 16-bit patterns in memory.
+struct bf16_t {
+  uint16_t bits;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// float -> bfloat16, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Element type traits for the io dtype.
+template <typename T>
+struct io;
+
+template <>
+struct io<float> {
+  __device__ __forceinline__ static float load(const float* p) { return *p; }
+  __device__ __forceinline__ static void store(float* p, float x) { *p = x; }
+};
+
+template <>
+struct io<bf16_t> {
+  __device__ __forceinline__ static float load(const bf16_t* p) { return bf16_to_f32(p->bits); }
+  __device__ __forceinline__ static void store(bf16_t* p, float x) { p->bits = f32_to_bf16(x); }
+};
+
+// Load 4 consecutive io elements as floats.
+__device__ __forceinline__ f32x4 load4(const float* p) {
+  return *reinterpret_cast<const f32x4*>(p);
+}
+__device__ __forceinline__ f32x4 load4(const bf16_t* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  f32x4 r;
+  r[0] = __uint_as_float(u.x << 16);
+  r[1] = __uint_as_float(u.x & 0xFFFF0000u);
+  r[2] = __uint_as_float(u.y << 16);
+  r[3] = __uint_as_float(u.y & 0xFFFF0000u);
+  return r;
+}
+
+// Store 4 consecutive io elements.
+__device__ __forceinline__ void store4(float* p, f32x4 x) { *reinterpret_cast<f32x4*>(p) = x; }
+__device__ __forceinline__ void store4(bf16_t* p, f32x4 x) {
+  uint2 u;
+  u.x = static_cast<uint32_t>(f32_to_bf16(x[0])) | (static_cast<uint32_t>(f32_to_bf16(x[1])) << 16);
+  u.y = static_cast<uint32_t>(f32_to_bf16(x[2])) | (static_cast<uint32_t>(f32_to_bf16(x[3])) << 16);
+  *reinterpret_cast<uint2*>(p) = u;
+}
+
+// Cross-lane xor shuffle within a 64-wide wavefront.
+__device__ __forceinline__ float shfl_xor(float x, int m) { return __shfl_xor(x, m, 64); }
+
+}  // namespace kda

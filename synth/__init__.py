@@ -5,14 +5,20 @@ draws random numbers and shapes them into operator inputs; it contains none
 of the operator's own arithmetic (no recurrence, no gate cumsum, no chunk
 math), so both the oracle and the HIP path can consume what it produces.
 
-Recipe (numpy ``Generator(PCG64(seed))``, every draw float32):
+Recipe (numpy ``Generator(PCG64(...))``, every draw float32):
 
-* draw order: sequence lengths (packed-varlen workload only), q, k, v, z_beta,
-  z_alpha, the long-memory channel mask (long-sequence workload only), S0;
+* tokens are drawn in blocks of 4096; block ``j`` of a workload with seed
+  ``s`` uses its own stream ``PCG64([s, j])`` and draws, in this order, q, k,
+  v ([4096, H, d] each), z_beta ([4096, H]) and z_alpha ([4096, H, dk]).
+  Blocks are independent, so they are generated on several threads and the
+  result does not depend on the thread count;
+* sequence lengths (packed-varlen workload) come first, from ``PCG64([s])``;
+  the long-memory channel mask from ``PCG64([s, 2**20])``; S0 from
+  ``PCG64([s, 2**21])``;
 * q and k are L2-normalised per (token, head) over the key dimension in
   float32: x / max(||x||, 1e-6);
 * beta = sigmoid(z_beta);
-* log_alpha = -softplus(z_alpha) = -(max(z, 0) + log1p(exp(-|z|)));
+* log_alpha = -softplus(z_alpha) = -(max(z, 0) + log1p(exp(-|z|))), float32;
 * bf16 tensors are rounded from float32 to nearest-even once, here, and both
   sides read those same rounded values.
 
@@ -23,11 +29,21 @@ log-uniform lengths and a random initial state, and a batched decode.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 import math
+import os
 from typing import Optional
 
 import numpy as np
+
+BLOCK = 4096
+_MASK_STREAM = 1 << 20
+_S0_STREAM = 1 << 21
+
+
+def _workers() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
 
 
 # --------------------------------------------------------------------------
@@ -64,12 +80,13 @@ def l2norm_f32(x: np.ndarray) -> np.ndarray:
 
 
 def sigmoid_f32(z: np.ndarray) -> np.ndarray:
-    return (1.0 / (1.0 + np.exp(-z.astype(np.float64)))).astype(np.float32)
+    z = z.astype(np.float32, copy=False)
+    return (np.float32(1.0) / (np.float32(1.0) + np.exp(-z))).astype(np.float32)
 
 
 def neg_softplus_f32(z: np.ndarray) -> np.ndarray:
-    z64 = z.astype(np.float64)
-    return (-(np.maximum(z64, 0.0) + np.log1p(np.exp(-np.abs(z64))))).astype(np.float32)
+    z = z.astype(np.float32, copy=False)
+    return (-(np.maximum(z, np.float32(0.0)) + np.log1p(np.exp(-np.abs(z))))).astype(np.float32)
 
 
 # --------------------------------------------------------------------------
@@ -113,34 +130,49 @@ def make_prefill(lengths, H: int, dk: int, dv: int, io_dtype: str, seed: int,
     picks round(frac * dk) key channels per head whose forget gate stays
     near 1: log_alpha = -1e-5 * softplus(z) on those channels for every token.
     """
-    rng = np.random.Generator(np.random.PCG64(seed))
     if lengths_from_rng is not None:
-        lengths = lengths_from_rng(rng)
+        lengths = lengths_from_rng(np.random.Generator(np.random.PCG64([seed])))
     lengths = [int(x) for x in lengths]
     cu = np.zeros(len(lengths) + 1, dtype=np.int32)
     cu[1:] = np.cumsum(lengths)
     T = int(cu[-1])
-    q = rng.standard_normal((T, H, dk), dtype=np.float32)
-    k = rng.standard_normal((T, H, dk), dtype=np.float32)
-    v = rng.standard_normal((T, H, dv), dtype=np.float32)
-    zb = rng.standard_normal((T, H), dtype=np.float32)
-    za = rng.standard_normal((T, H, dk), dtype=np.float32)
-    q = l2norm_f32(q)
-    k = l2norm_f32(k)
-    beta = sigmoid_f32(zb)
-    la = neg_softplus_f32(za)
+    q = np.empty((T, H, dk), np.float32)
+    k = np.empty((T, H, dk), np.float32)
+    v = np.empty((T, H, dv), np.float32)
+    beta = np.empty((T, H), np.float32)
+    la = np.empty((T, H, dk), np.float32)
+
+    def fill(j: int):
+        a, b = j * BLOCK, min(T, (j + 1) * BLOCK)
+        n = b - a
+        rng = np.random.Generator(np.random.PCG64([seed, j]))
+        qb = rng.standard_normal((BLOCK, H, dk), dtype=np.float32)[:n]
+        kb = rng.standard_normal((BLOCK, H, dk), dtype=np.float32)[:n]
+        vb = rng.standard_normal((BLOCK, H, dv), dtype=np.float32)[:n]
+        zb = rng.standard_normal((BLOCK, H), dtype=np.float32)[:n]
+        za = rng.standard_normal((BLOCK, H, dk), dtype=np.float32)[:n]
+        qb, kb = l2norm_f32(qb), l2norm_f32(kb)
+        if io_dtype == "bf16":
+            qb, kb, vb = bf16_round(qb), bf16_round(kb), bf16_round(vb)
+        q[a:b], k[a:b], v[a:b] = qb, kb, vb
+        beta[a:b] = sigmoid_f32(zb)
+        la[a:b] = neg_softplus_f32(za)
+
+    if io_dtype not in ("bf16", "f32"):
+        raise ValueError(io_dtype)
+    nblk = (T + BLOCK - 1) // BLOCK
+    with concurrent.futures.ThreadPoolExecutor(_workers()) as ex:
+        list(ex.map(fill, range(nblk)))
     if long_memory_frac > 0.0:
         nlm = int(round(long_memory_frac * dk))
+        mrng = np.random.Generator(np.random.PCG64([seed, _MASK_STREAM]))
         for h in range(H):
-            ch = rng.choice(dk, size=nlm, replace=False)
+            ch = mrng.choice(dk, size=nlm, replace=False)
             la[:, h, ch] = (np.float32(1e-5) * la[:, h, ch]).astype(np.float32)
     S0 = None
     if S0_std is not None:
-        S0 = (rng.standard_normal((len(lengths), H, dk, dv), dtype=np.float32) * np.float32(S0_std)).astype(np.float32)
-    if io_dtype == "bf16":
-        q, k, v = bf16_round(q), bf16_round(k), bf16_round(v)
-    elif io_dtype != "f32":
-        raise ValueError(io_dtype)
+        srng = np.random.Generator(np.random.PCG64([seed, _S0_STREAM]))
+        S0 = (srng.standard_normal((len(lengths), H, dk, dv), dtype=np.float32) * np.float32(S0_std)).astype(np.float32)
     return PrefillInputs(q=q, k=k, v=v, log_alpha=la, beta=beta, cu_seqlens=cu, S0=S0,
                          io_dtype=io_dtype, chunk=chunk)
 

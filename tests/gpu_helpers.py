@@ -1,0 +1,88 @@
+"""Shared helpers for the GPU parity tests: upload seeded inputs, run the HIP
+path through the C ABI binding, run the oracle on the same values, compare."""
+from __future__ import annotations
+
+import os
+import sys
+
+import numpy as np
+
+import oracle
+import synth
+
+TOL = {"bf16": 1e-2, "f32": 1e-4}
+
+
+def torch_mod():
+    import torch
+    return torch
+
+
+def have_gpu() -> bool:
+    try:
+        return torch_mod().cuda.is_available()
+    except Exception:
+        return False
+
+
+def log(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev(x: np.ndarray, dtype: str = "f32"):
+    torch = torch_mod()
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    if dtype == "bf16":
+        t = t.to(torch.bfloat16)
+    return t.cuda()
+
+
+def host(t) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def rel_err(x: np.ndarray, ref: np.ndarray) -> float:
+    den = float(np.max(np.abs(ref))) if ref.size else 0.0
+    num = float(np.max(np.abs(x - ref))) if ref.size else 0.0
+    if den == 0.0:
+        return num
+    return num / den
+
+
+def gpu_prefill(w: synth.PrefillInputs, chunk: int = None, S0=None, in_place: bool = False, host_offsets=True):
+    """Run libkda prefill on the inputs; returns (o, S_T) as float64 numpy."""
+    import gated_delta_rule_33_amd as kda
+    torch = torch_mod()
+    dt = w.io_dtype
+    q, k, v = dev(w.q, dt), dev(w.k, dt), dev(w.v, dt)
+    la, b = dev(w.log_alpha), dev(w.beta)
+    cu = dev(w.cu_seqlens)
+    s0 = S0 if S0 is not None else w.S0
+    s0d = dev(s0) if s0 is not None else None
+    kw = {}
+    if in_place:
+        assert s0d is not None
+        kw["S_T"] = s0d
+    o, ST = kda.prefill(q, k, v, la, b, cu, s0d, chunk=chunk or w.chunk,
+                        cu_seqlens_host=w.cu_seqlens.tolist() if host_offsets else None, **kw)
+    torch.cuda.synchronize()
+    return host(o), host(ST)
+
+
+def oracle_prefill(w: synth.PrefillInputs, S0=None, heads=None, threads: int = 0):
+    """fp64 oracle on the same values; optionally on a subset of heads."""
+    s0 = S0 if S0 is not None else w.S0
+    if heads is None:
+        return oracle.prefill(w.q, w.k, w.v, w.log_alpha, w.beta, w.cu_seqlens, s0, threads=threads)
+    hs = list(heads)
+    return oracle.prefill(w.q[:, hs], w.k[:, hs], w.v[:, hs], w.log_alpha[:, hs], w.beta[:, hs], w.cu_seqlens,
+                          None if s0 is None else s0[:, hs], threads=threads)
+
+
+def check(name: str, got: np.ndarray, ref: np.ndarray, tol: float):
+    e = rel_err(got, ref)
+    log("  %-28s rel_err %.3e (tol %.0e) max|ref| %.3e" % (name, e, tol, float(np.max(np.abs(ref))) if ref.size else 0))
+    assert np.all(np.isfinite(got)), name + ": non-finite output"
+    assert e <= tol, "%s: rel err %.3e > %.0e" % (name, e, tol)
+    return e

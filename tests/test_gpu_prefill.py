@@ -1,0 +1,119 @@
+"""GPU parity of kda_prefill against the fp64 oracle, element by element on
+the same seeded inputs, plus invariants (chunk-size independence, in-place
+state, split/resume, decode equivalence, pure decay)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_helpers import TOL, check, dev, gpu_prefill, have_gpu, host, log, oracle_prefill
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not have_gpu(), reason="needs a GPU")]
+
+
+def test_tiny_f32_workload():
+    """1 x 256 tokens, H=2, d=64, fp32, chunk 64, S0 = 0."""
+    w = synth.workload_prefill("tiny_f32")
+    log("prefill tiny_f32")
+    o, S = gpu_prefill(w)
+    o_ref, S_ref = oracle_prefill(w)
+    check("o", o, o_ref, TOL["f32"])
+    check("S_T", S, S_ref, TOL["f32"])
+
+
+RAGGED = [1, 63, 64, 65, 200, 0, 31, 129]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (64, 128), (128, 64)])
+@pytest.mark.parametrize("chunk", [64, 32])
+def test_ragged_varlen(dt, dk, dv, chunk):
+    """Packed sequences of ragged lengths (incl. 0, 1, C-1, C, C+1) with a
+    nonzero initial state."""
+    log("prefill ragged dt=%s dk=%d dv=%d chunk=%d" % (dt, dk, dv, chunk))
+    w = synth.make_prefill(RAGGED, H=3, dk=dk, dv=dv, io_dtype=dt, seed=11, S0_std=0.05, chunk=chunk)
+    o, S = gpu_prefill(w)
+    o_ref, S_ref = oracle_prefill(w)
+    check("o", o, o_ref, TOL[dt])
+    check("S_T", S, S_ref, TOL[dt])
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_device_offsets_without_host_mirror(dt):
+    w = synth.make_prefill([70, 0, 5, 300], H=2, dk=128, dv=128, io_dtype=dt, seed=12, S0_std=0.02)
+    log("prefill no-host-offsets dt=%s" % dt)
+    o, S = gpu_prefill(w, host_offsets=False)
+    o_ref, S_ref = oracle_prefill(w)
+    check("o", o, o_ref, TOL[dt])
+    check("S_T", S, S_ref, TOL[dt])
+
+
+def test_in_place_state_and_zero_tokens():
+    w = synth.make_prefill([0, 0, 0], H=2, dk=64, dv=64, io_dtype="bf16", seed=13, S0_std=0.1)
+    log("prefill all-empty in-place")
+    o, S = gpu_prefill(w, in_place=True)
+    assert o.shape == (0, 2, 64)
+    assert np.array_equal(S, w.S0.astype(np.float64))
+    w = synth.make_prefill([100, 37], H=2, dk=128, dv=128, io_dtype="bf16", seed=14, S0_std=0.1)
+    o, S = gpu_prefill(w, in_place=True)
+    o_ref, S_ref = oracle_prefill(w)
+    check("o (in place)", o, o_ref, TOL["bf16"])
+    check("S_T (in place)", S, S_ref, TOL["bf16"])
+
+
+def test_chunk_size_independence_and_resume():
+    """C=32 and C=64 agree; a split at t then resume from S_t equals the whole."""
+    w = synth.make_prefill([333], H=2, dk=128, dv=128, io_dtype="f32", seed=15, S0_std=0.05)
+    log("prefill chunk independence + resume")
+    o64, S64 = gpu_prefill(w, chunk=64)
+    o32, S32 = gpu_prefill(w, chunk=32)
+    assert np.max(np.abs(o64 - o32)) <= 1e-4 * np.max(np.abs(o64))
+    assert np.max(np.abs(S64 - S32)) <= 1e-4 * np.max(np.abs(S64))
+    t = 150
+    a = synth.PrefillInputs(w.q[:t], w.k[:t], w.v[:t], w.log_alpha[:t], w.beta[:t], np.array([0, t], np.int32),
+                            w.S0, "f32")
+    oa, Sa = gpu_prefill(a)
+    b = synth.PrefillInputs(w.q[t:], w.k[t:], w.v[t:], w.log_alpha[t:], w.beta[t:], np.array([0, 333 - t], np.int32),
+                            Sa.astype(np.float32), "f32")
+    ob, Sb = gpu_prefill(b)
+    assert np.max(np.abs(np.concatenate([oa, ob]) - o64)) <= 1e-4 * np.max(np.abs(o64))
+    assert np.max(np.abs(Sb - S64)) <= 1e-4 * np.max(np.abs(S64))
+
+
+def test_pure_decay_closed_form_on_gpu():
+    """beta = 0: o_t = S0^T (exp(g_t) q_t) for each sequence."""
+    w = synth.make_prefill([150, 77], H=2, dk=128, dv=64, io_dtype="f32", seed=16, S0_std=0.3)
+    w.beta[:] = 0.0
+    log("prefill pure decay")
+    o, S = gpu_prefill(w)
+    for n in range(2):
+        s, e = int(w.cu_seqlens[n]), int(w.cu_seqlens[n + 1])
+        for h in range(2):
+            g = np.cumsum(w.log_alpha[s:e, h].astype(np.float64), axis=0)
+            ref = (np.exp(g) * w.q[s:e, h]) @ w.S0[n, h].astype(np.float64)
+            check("o seq%d head%d" % (n, h), o[s:e, h], ref, 1e-4)
+
+
+def test_prefill_equals_decode_steps():
+    """T tokens through prefill equal T decode steps on the same values."""
+    import torch
+    import gated_delta_rule_33_amd as kda
+    w = synth.make_prefill([70], H=4, dk=128, dv=128, io_dtype="bf16", seed=17, S0_std=0.05)
+    log("prefill vs decode steps")
+    o, S = gpu_prefill(w)
+    Sd = dev(w.S0)
+    outs = []
+    for t in range(70):
+        sl = slice(t, t + 1)
+        outs.append(host(kda.decode_step(dev(w.q[sl], "bf16"), dev(w.k[sl], "bf16"), dev(w.v[sl], "bf16"),
+                                         dev(w.log_alpha[sl]), dev(w.beta[sl]), Sd)))
+    torch.cuda.synchronize()
+    check("o prefill vs decode", o, np.concatenate(outs), 2e-2)
+    check("S prefill vs decode", S, host(Sd), 2e-2)
+
+
+def test_deterministic():
+    w = synth.make_prefill([500, 3], H=2, dk=128, dv=128, io_dtype="bf16", seed=18, S0_std=0.02)
+    o1, S1 = gpu_prefill(w)
+    o2, S2 = gpu_prefill(w)
+    assert np.array_equal(o1, o2) and np.array_equal(S1, S2)
