@@ -20,7 +20,7 @@ struct PrefillPlan {
   int64_t max_chunks;  // upper bound (exact when the host offsets are known)
   int sort;            // 1: longest-first order is computed on the device
   // byte offsets inside the workspace
-  size_t off_chunk_off, off_order, off_R, off_Q, off_Kt, off_P, off_T, off_G;
+  size_t off_chunk_off, off_order, off_blocks;
   size_t total_bytes;
 };
 

@@ -25,9 +25,10 @@
 //   prep_kernel           grid (chunk, head): everything that does not depend
 //                         on S (gate cumsum, A and P via MFMA, T by blocked
 //                         forward substitution, R, Qh, Kb^T, e^{g_last}),
-//                         written to the workspace
-//   scan_kernel           grid (sequence, head, 64-column value tile): the
-//                         serial chunk loop with S held in MFMA accumulators
+//                         written to one workspace block per (chunk, head)
+//   scan_kernel           grid (sequence, head, value tile): the serial chunk
+//                         loop with S held in MFMA accumulators, chunk blocks
+//                         streamed into LDS one chunk ahead
 //
 // Exponent safety.  e^{g_r-g_s} is factorised around references inside the
 // chunk so that no factor exceeds the fp32 range: for a 16-row block I below
@@ -122,7 +123,7 @@ __device__ __forceinline__ float frag_nat(const float* row, int k0, int g) { ret
 // (scan kernel).  For bf16, k-step s covers accumulator tiles 2s and 2s+1 and
 // slot j of lane group g is row 4g+j of tile 2s (j < 4) or row 4g+j-4 of tile
 // 2s+1; for fp32, k-step s is row 4g + (s % 4) of tile s / 4.  The A operand
-// X[row][k] must be read with the same map.
+// X[row][k] must be read with the same map (afrag below).
 // ---------------------------------------------------------------------------
 template <typename T>
 struct accb;
@@ -137,22 +138,12 @@ struct accb<bf16_t> {
     r[4] = to_bf(y[0]); r[5] = to_bf(y[1]); r[6] = to_bf(y[2]); r[7] = to_bf(y[3]);
     return r;
   }
-  // X row pointer (LDS), k-step s, lane group g
-  __device__ __forceinline__ static bf16x8 a(const bf16_t* row, int s, int g) {
-    const uint2 lo = *reinterpret_cast<const uint2*>(row + 32 * s + 4 * g);
-    const uint2 hi = *reinterpret_cast<const uint2*>(row + 32 * s + 16 + 4 * g);
-    const uint4 u = {lo.x, lo.y, hi.x, hi.y};
-    return __builtin_bit_cast(bf16x8, u);
-  }
 };
 
 template <>
 struct accb<float> {
   static constexpr int KS = 4;
   __device__ __forceinline__ static float b(const f32x4* tiles, int s) { return tiles[s >> 2][s & 3]; }
-  __device__ __forceinline__ static float a(const float* row, int s, int g) {
-    return row[16 * (s >> 2) + 4 * g + (s & 3)];
-  }
 };
 
 // ---------------------------------------------------------------------------
@@ -198,42 +189,134 @@ __global__ __launch_bounds__(1024) void chunk_offsets_kernel(const int32_t* __re
 }
 
 // ---------------------------------------------------------------------------
-// Workspace geometry per (chunk, head) slot.
+// Per-(chunk, head) workspace block.  Everything the serial pass needs for one
+// chunk is one contiguous block, so the scan streams it into LDS with plain
+// linear 16-byte direct-to-LDS loads; the LDS image equals this layout.
+//   R   [C][DK]  io   b_r e^{g_r} k_r
+//   Qh  [C][DK]  io   e^{g_r} q_r
+//   KbT [DK][C]  io   (e^{g_last - g_r} k_r)^T
+//   P   [C][C]   io   gated q k^T, lower triangle incl. diagonal
+//   T   [C][C]   io   (I + A)^{-1}
+//   Gam [DK]     f32  e^{g_last}
+//   Bet [C]      f32  beta
+// Tiles are stored with two index transforms that the scan's reads undo:
+//   * for bf16, each 32-column group is permuted so that the eight k values
+//     an MFMA A-fragment needs (4g..4g+3 and 16+4g..16+4g+3, matching the
+//     accumulator rows a lane holds) are one contiguous 16-byte granule;
+//   * the 16-byte granules of a row are XOR-swizzled by a function of the
+//     row so that 16 lanes reading the same logical granule of 16 rows hit
+//     16 different LDS bank groups (no padding needed).
 // ---------------------------------------------------------------------------
 template <typename T, int C, int DK>
-struct WsGeom {
-  static constexpr size_t R = static_cast<size_t>(C) * DK;   // elements of R (and Qh, Kb^T)
-  static constexpr size_t P = static_cast<size_t>(C) * C;    // elements of P (and T)
+struct Blk {
+  static constexpr int ES = sizeof(T);
+  static constexpr int RB_R = DK * ES;  // row bytes of R, Qh
+  static constexpr int RB_K = C * ES;   // row bytes of KbT, P, T
+  static constexpr size_t oR = 0;
+  static constexpr size_t oQ = oR + static_cast<size_t>(C) * DK * ES;
+  static constexpr size_t oK = oQ + static_cast<size_t>(C) * DK * ES;
+  static constexpr size_t oP = oK + static_cast<size_t>(DK) * C * ES;
+  static constexpr size_t oT = oP + static_cast<size_t>(C) * C * ES;
+  static constexpr size_t oG = oT + static_cast<size_t>(C) * C * ES;
+  static constexpr size_t oB = oG + static_cast<size_t>(DK) * 4;
+  static constexpr size_t bytes = (oB + static_cast<size_t>(C) * 4 + 1023) / 1024 * 1024;
+};
+
+template <int RB>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (RB >= 256) return row & 15;
+  else if constexpr (RB == 128) return (row >> 1) & 7;
+  else return (row >> 2) & 3;
+}
+
+template <typename T>
+__device__ __forceinline__ int pcol(int c);
+template <>
+__device__ __forceinline__ int pcol<float>(int c) { return c; }
+template <>
+__device__ __forceinline__ int pcol<bf16_t>(int c) {
+  const int k = c & 31;
+  return (c & ~31) | (8 * ((k & 15) >> 2) + 4 * (k >> 4) + (k & 3));
+}
+
+// byte offset of element (row, c) in a stored tile with RB-byte rows
+template <typename T, int RB>
+__device__ __forceinline__ int toff(int row, int c) {
+  constexpr int EPG = 16 / static_cast<int>(sizeof(T));
+  const int p = pcol<T>(c);
+  return row * RB + 16 * ((p / EPG) ^ swz<RB>(row)) + (p % EPG) * static_cast<int>(sizeof(T));
+}
+
+// byte offset of logical 16-byte granule gi of `row`
+template <int RB>
+__device__ __forceinline__ int goff(int row, int gi) { return row * RB + 16 * (gi ^ swz<RB>(row)); }
+
+// A fragment of a stored tile for the accumulator k map (see accb).
+template <typename T, int RB>
+struct afrag;
+template <int RB>
+struct afrag<bf16_t, RB> {
+  __device__ __forceinline__ static bf16x8 get(const unsigned char* tile, int row, int s, int g) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(tile + goff<RB>(row, 4 * s + g)));
+  }
+};
+template <int RB>
+struct afrag<float, RB> {
+  __device__ __forceinline__ static float get(const unsigned char* tile, int row, int s, int g) {
+    return reinterpret_cast<const float*>(tile + goff<RB>(row, 4 * (s >> 2) + g))[s & 3];
+  }
+};
+
+// hi / lo parts of accumulator tiles used as a B operand (bf16 only; the
+// fp32 path has no lo part)
+template <typename T>
+struct split;
+template <>
+struct split<bf16_t> {
+  static constexpr bool has_lo = true;
+  __device__ __forceinline__ static void hilo(const f32x4* tiles, int s, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float x = tiles[2 * s + (j >> 2)][j & 3];
+      const __bf16 h = to_bf(x);
+      hi[j] = h;
+      lo[j] = to_bf(x - from_bf(h));
+    }
+  }
+};
+template <>
+struct split<float> {
+  static constexpr bool has_lo = false;
+  __device__ __forceinline__ static void hilo(const f32x4* tiles, int s, float& hi, float& lo) {
+    hi = tiles[s >> 2][s & 3];
+    lo = 0.f;
+  }
 };
 
 // ---------------------------------------------------------------------------
-// Prep kernel LDS layout.
+// Prep kernel: one workgroup (256 threads) per (chunk, head).
 // ---------------------------------------------------------------------------
 template <typename T, int C, int DK>
 struct PrepLds {
   static constexpr int NB = C / 16;
   static constexpr int NPAIR = NB * (NB - 1) / 2;
-  static constexpr int PADG = 4;                          // fp32 G pitch pad
-  static constexpr int PADK = 8;                          // element pad for [C][DK] io arrays (16 B rows for bf16)
-  static constexpr int GP = DK + PADG;                    // G pitch (floats)
-  static constexpr int KP = DK + PADK;                    // Kr/Qr/Kc pitch (elements)
-  static constexpr int AP = C + 1;                        // A / Tinv pitch (floats)
-  static constexpr size_t szG = static_cast<size_t>(C) * GP * 4;
-  static constexpr size_t szKQ = static_cast<size_t>(2) * C * KP * sizeof(T);
-  static constexpr size_t szTi = static_cast<size_t>(C) * AP * 4;
-  static constexpr size_t reg0 = (((szG > szKQ ? szG : szKQ) > szTi ? (szG > szKQ ? szG : szKQ) : szTi) + 15) / 16 * 16;
-  static constexpr size_t reg1 = (static_cast<size_t>(C) * KP * sizeof(T) + 15) / 16 * 16;  // Kr
-  static constexpr size_t szVec = static_cast<size_t>(4 * NB + NPAIR) * DK * 4;   // eb ee dr dc pair
-  static constexpr size_t szX = static_cast<size_t>(NB > 1 ? NB - 1 : 1) * 256 * 4;
-  static constexpr size_t reg2 = ((szVec > szX ? szVec : szX) + 15) / 16 * 16;
-  static constexpr size_t szA = static_cast<size_t>(C) * AP * 4;
-  static constexpr size_t szKt = static_cast<size_t>(DK) * (C + PADK) * sizeof(T);
-  static constexpr size_t reg3 = ((szA > szKt ? szA : szKt) + 15) / 16 * 16;      // A, earlier Kb^T staging
-  static constexpr size_t szBeta = static_cast<size_t>(C) * 4;
-  static constexpr size_t szPart = static_cast<size_t>(256 / DK) * DK * 4;
-  static constexpr size_t o0 = 0, o1 = reg0, o2 = o1 + reg1, o3 = o2 + reg2, o4 = o3 + reg3,
-                          o5 = o4 + szBeta;
-  static constexpr size_t total = o5 + szPart;
+  static constexpr int NRB = 1024 / DK;      // row blocks (threads per channel group)
+  static constexpr int PADK = sizeof(T) == 2 ? 8 : 4;  // keeps 16-row fragment reads conflict-free
+  static constexpr int KP = DK + PADK;       // pitch (elements) of Kr / Qr / Kc
+  static constexpr int AP = C + 1;           // pitch (floats) of A / Ti
+  static constexpr int CP = C + PADK;        // pitch (elements) of the P staging tile
+  static constexpr size_t a16(size_t x) { return (x + 15) / 16 * 16; }
+  static constexpr size_t mx(size_t a, size_t b) { return a > b ? a : b; }
+  // region 0: Kr, Qr, Kc (io) -> later Ti (f32)
+  static constexpr size_t r0 = a16(mx(static_cast<size_t>(3) * C * KP * sizeof(T), static_cast<size_t>(C) * AP * 4));
+  // region 1: A (f32)
+  static constexpr size_t r1 = a16(static_cast<size_t>(C) * AP * 4);
+  // region 2: refs gB gM gE [NB][DK] + partial sums [NRB][DK] (f32) -> later P staging (io)
+  static constexpr size_t r2 = a16(mx(static_cast<size_t>(3 * NB + NRB) * DK * 4, static_cast<size_t>(C) * CP * sizeof(T)));
+  // region 3: dr, dc [NB][DK], pair [NPAIR][DK] (f32) -> later inverse scratch
+  static constexpr size_t r3 = a16(mx(static_cast<size_t>(2 * NB + NPAIR) * DK * 4, static_cast<size_t>(NB) * 256 * 4));
+  static constexpr size_t o0 = 0, o1 = r0, o2 = o1 + r1, o3 = o2 + r2, o4 = o3 + r3;
+  static constexpr size_t total = o4 + static_cast<size_t>(C) * 4;  // + beta
 };
 
 template <typename T, int C, int DK>
@@ -241,29 +324,30 @@ __global__ __launch_bounds__(256) void prep_kernel(const T* __restrict__ q, cons
                                                    const float* __restrict__ la, const float* __restrict__ beta,
                                                    const int32_t* __restrict__ cu,
                                                    const int32_t* __restrict__ chunk_off, int N, int H,
-                                                   T* __restrict__ wsR, T* __restrict__ wsQ,
-                                                   T* __restrict__ wsKt, T* __restrict__ wsP,
-                                                   T* __restrict__ wsT, float* __restrict__ wsG) {
+                                                   unsigned char* __restrict__ ws) {
   typedef PrepLds<T, C, DK> L;
+  typedef Blk<T, C, DK> B;
   typedef mma16<T> M;
   constexpr int NB = L::NB;
+  constexpr int NCG = DK / 4;     // channel groups of 4
+  constexpr int RPT = C / L::NRB; // rows per thread
+  static_assert(RPT >= 1 && 16 % RPT == 0, "row blocks must tile 16-row sub-blocks");
   extern __shared__ __align__(16) unsigned char smem[];
-  float* G = reinterpret_cast<float*>(smem + L::o0);             // [C][GP]
-  T* Kc = reinterpret_cast<T*>(smem + L::o0);                    // [C][KP]  (after G is consumed)
-  T* Qr = Kc + C * L::KP;                                        // [C][KP]
-  float* Ti = reinterpret_cast<float*>(smem + L::o0);            // [C][AP]  (after Kc/Qr are consumed)
-  T* Kr = reinterpret_cast<T*>(smem + L::o1);                    // [C][KP]
-  float* vec = reinterpret_cast<float*>(smem + L::o2);           // eb ee dr dc pair, [.][DK]
-  float* eb = vec;
-  float* ee = vec + NB * DK;
-  float* dr = vec + 2 * NB * DK;
-  float* dc = vec + 3 * NB * DK;
-  float* pr = vec + 4 * NB * DK;
-  float* X = vec;                                                // inverse scratch (after vectors)
-  float* A = reinterpret_cast<float*>(smem + L::o3);             // [C][AP]
-  T* Kts = reinterpret_cast<T*>(smem + L::o3);                   // [DK][C + PADK] staging
-  float* bet = reinterpret_cast<float*>(smem + L::o4);           // [C]
-  float* part = reinterpret_cast<float*>(smem + L::o5);          // [256/DK][DK]
+  T* Kr = reinterpret_cast<T*>(smem + L::o0);
+  T* Qr = Kr + C * L::KP;
+  T* Kc = Qr + C * L::KP;
+  float* Ti = reinterpret_cast<float*>(smem + L::o0);
+  float* A = reinterpret_cast<float*>(smem + L::o1);
+  float* gB = reinterpret_cast<float*>(smem + L::o2);
+  float* gM = gB + NB * DK;
+  float* gE = gM + NB * DK;
+  float* part = gE + NB * DK;
+  T* Ps = reinterpret_cast<T*>(smem + L::o2);
+  float* dr = reinterpret_cast<float*>(smem + L::o3);
+  float* dc = dr + NB * DK;
+  float* pr = dc + NB * DK;
+  float* X = reinterpret_cast<float*>(smem + L::o3);
+  float* bet = reinterpret_cast<float*>(smem + L::o4);
 
   const int c = blockIdx.x, h = blockIdx.y;
   const int total = chunk_off[N];
@@ -277,128 +361,120 @@ __global__ __launch_bounds__(256) void prep_kernel(const T* __restrict__ q, cons
   const int len = min(C, cu[lo + 1] - t0);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const size_t slot = static_cast<size_t>(c) * H + h;
-  const size_t rowstride = static_cast<size_t>(H) * DK;  // elements between tokens in q/k/la
+  unsigned char* blk = ws + (static_cast<size_t>(c) * H + h) * B::bytes;
 
-  // ---- a2: chunk-local inclusive cumsum of log_alpha per key channel ------
+  // ---- loads: thread owns channels c4..c4+3 of rows r0..r0+RPT-1 ---------
+  const int cg = tid % NCG, rbk = tid / NCG;
+  const int c4 = 4 * cg, r0 = rbk * RPT;
+  f32x4 lg[RPT], kv[RPT], qv[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int r = r0 + i;
+    if (r < len) {
+      const size_t e = (static_cast<size_t>(t0 + r) * H + h) * DK + c4;
+      lg[i] = *reinterpret_cast<const f32x4*>(la + e);
+      kv[i] = load4(k + e);
+      qv[i] = load4(q + e);
+    } else {
+      lg[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      kv[i] = lg[i];
+      qv[i] = lg[i];
+    }
+  }
+  if (tid < C) bet[tid] = tid < len ? beta[static_cast<size_t>(t0 + tid) * H + h] : 0.f;
+
+  // ---- a2: chunk-local inclusive cumsum of log_alpha ----------------------
+#pragma unroll
+  for (int i = 1; i < RPT; ++i) lg[i] += lg[i - 1];
+  *reinterpret_cast<f32x4*>(part + rbk * DK + c4) = lg[RPT - 1];
+  __syncthreads();
   {
-    constexpr int PARTS = 256 / DK;
-    constexpr int RPT = C / PARTS;
-    const int ch = tid % DK, pt = tid / DK;
-    float gl[RPT];
-    float run = 0.f;
-    const float* lap = la + (static_cast<size_t>(t0) * H + h) * DK + ch;
+    f32x4 off = {0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < rbk; ++p) off += *reinterpret_cast<const f32x4*>(part + p * DK + c4);
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      const int r = pt * RPT + i;
-      run += r < len ? lap[static_cast<size_t>(r) * rowstride] : 0.f;
-      gl[i] = run;
+      lg[i] += off;
+      const int r = r0 + i, I = r >> 4, rr = r & 15;
+      if (rr == 0) *reinterpret_cast<f32x4*>(gB + I * DK + c4) = lg[i];
+      if (rr == 8) *reinterpret_cast<f32x4*>(gM + I * DK + c4) = lg[i];
+      if (rr == 15) *reinterpret_cast<f32x4*>(gE + I * DK + c4) = lg[i];
     }
-    part[pt * DK + ch] = run;
-    if (tid < C) bet[tid] = tid < len ? beta[static_cast<size_t>(t0 + tid) * H + h] : 0.f;
-    __syncthreads();
-    float off = 0.f;
-    for (int p = 0; p < pt; ++p) off += part[p * DK + ch];
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) G[(pt * RPT + i) * L::GP + ch] = gl[i] + off;
-    __syncthreads();
   }
+  __syncthreads();
 
-  // ---- per-block reference vectors --------------------------------------
+  // ---- reference vectors for the gated matrices -------------------------
   for (int idx = tid; idx < NB * DK; idx += 256) {
-    const int I = idx / DK, ch = idx % DK;
-    const float gb = G[(16 * I) * L::GP + ch];
-    const float gm = G[(16 * I + 8) * L::GP + ch];
-    const float ge = G[(16 * I + 15) * L::GP + ch];
-    const float gz = G[(C - 1) * L::GP + ch];
-    eb[idx] = __expf(gb);         // e^{g_b}:          row-side ref -> chunk start
-    ee[idx] = __expf(gz - ge);    // e^{g_last - g_e}: column-side ref -> chunk end
-    dr[idx] = __expf(gb - gm);    // diagonal block row-side correction
-    dc[idx] = __expf(gm - ge);    // diagonal block column-side correction
+    dr[idx] = __expf(gB[idx] - gM[idx]);  // >= 1, bounded by 8 tokens of decay
+    dc[idx] = __expf(gM[idx] - gE[idx]);
   }
   for (int idx = tid; idx < L::NPAIR * DK; idx += 256) {
     const int p = idx / DK, ch = idx % DK;
     int I = 1;
     while ((I + 1) * I / 2 <= p) ++I;
     const int J = p - I * (I - 1) / 2;
-    pr[idx] = __expf(G[(16 * I) * L::GP + ch] - G[(16 * J + 15) * L::GP + ch]);
+    pr[idx] = __expf(gB[I * DK + ch] - gE[J * DK + ch]);  // <= 1
   }
-  for (int ch = tid; ch < DK; ch += 256) wsG[slot * DK + ch] = __expf(G[(C - 1) * L::GP + ch]);
-  __syncthreads();  // reference vectors visible to every thread
+  if (tid < DK) {
+    reinterpret_cast<float*>(blk + B::oG)[tid] = __expf(gE[(NB - 1) * DK + tid]);
+  }
+  if (tid < C) reinterpret_cast<float*>(blk + B::oB)[tid] = bet[tid];
 
-  // ---- element factors and the S-independent outputs ---------------------
-  // Each thread owns groups of 4 channels of one row.
-  constexpr int NG = C * DK / 4 / 256;  // groups per thread
-  f32x4 keepQ[NG], keepK[NG];
+  // ---- element factors, S-independent outputs ---------------------------
   {
-    typedef WsGeom<T, C, DK> W;
-    T* oR = wsR + slot * W::R;
-    T* oQ = wsQ + slot * W::R;
+    const int I = r0 >> 4;  // all of this thread's rows are in block I
+    const f32x4 gb = *reinterpret_cast<const f32x4*>(gB + I * DK + c4);
+    const f32x4 ge = *reinterpret_cast<const f32x4*>(gE + I * DK + c4);
+    const f32x4 gz = *reinterpret_cast<const f32x4*>(gE + (NB - 1) * DK + c4);
+    f32x4 ebv, eev, kb[RPT];
 #pragma unroll
-    for (int it = 0; it < NG; ++it) {
-      const int idx = tid + 256 * it;
-      const int r = idx / (DK / 4), c4 = (idx % (DK / 4)) * 4;
-      const int I = r >> 4;
-      const f32x4 g = *reinterpret_cast<const f32x4*>(G + r * L::GP + c4);
-      const f32x4 gb = *reinterpret_cast<const f32x4*>(G + (16 * I) * L::GP + c4);
-      const f32x4 ge = *reinterpret_cast<const f32x4*>(G + (16 * I + 15) * L::GP + c4);
-      f32x4 kk = {0.f, 0.f, 0.f, 0.f}, qq = {0.f, 0.f, 0.f, 0.f};
-      if (r < len) {
-        kk = load4(k + (static_cast<size_t>(t0 + r) * H + h) * DK + c4);
-        qq = load4(q + (static_cast<size_t>(t0 + r) * H + h) * DK + c4);
-      }
+    for (int j = 0; j < 4; ++j) {
+      ebv[j] = __expf(gb[j]);          // e^{g_b}, <= 1
+      eev[j] = __expf(gz[j] - ge[j]);  // e^{g_last - g_e}, <= 1
+    }
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int r = r0 + i;
       f32x4 fr, fc;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        fr[j] = __expf(g[j] - gb[j]);
-        fc[j] = __expf(ge[j] - g[j]);
+        fr[j] = __expf(lg[i][j] - gb[j]);  // e^{g_r - g_b} <= 1
+        fc[j] = __expf(ge[j] - lg[i][j]);  // e^{g_e - g_r} <= 1
       }
-      const f32x4 kr = kk * fr;
-      const f32x4 qr = qq * fr;
-      const f32x4 kc = kk * fc;
-      const f32x4 ebv = *reinterpret_cast<const f32x4*>(eb + I * DK + c4);
-      const f32x4 eev = *reinterpret_cast<const f32x4*>(ee + I * DK + c4);
-      store4(oQ + r * DK + c4, qr * ebv);              // Qh = e^{g_r} q_r
-      store4(oR + r * DK + c4, bet[r] * (kr * ebv));   // R  = b_r e^{g_r} k_r
-      const f32x4 kb = kc * eev;                       // Kb = e^{g_last - g_r} k_r
-#pragma unroll
-      for (int j = 0; j < 4; ++j) lds_put<T>(Kts + (c4 + j) * (C + L::PADK) + r, kb[j]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) lds_put<T>(Kr + r * L::KP + c4 + j, kr[j]);
-      keepQ[it] = qr;
-      keepK[it] = kc;
-    }
-  }
-  __syncthreads();  // G no longer read; Kb^T staged
-  {
-    typedef WsGeom<T, C, DK> W;
-    T* oK = wsKt + slot * W::R;
-#pragma unroll
-    for (int it = 0; it < NG; ++it) {
-      const int idx = tid + 256 * it;
-      const int r = idx / (DK / 4), c4 = (idx % (DK / 4)) * 4;
+      const f32x4 kr = kv[i] * fr, qr = qv[i] * fr, kc = kv[i] * fc;
+      store4(reinterpret_cast<T*>(blk + B::oQ + toff<T, B::RB_R>(r, c4)), qr * ebv);
+      store4(reinterpret_cast<T*>(blk + B::oR + toff<T, B::RB_R>(r, c4)), bet[r] * (kr * ebv));
+      kb[i] = kc * eev;  // e^{g_last - g_r} k_r
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        lds_put<T>(Qr + r * L::KP + c4 + j, keepQ[it][j]);
-        lds_put<T>(Kc + r * L::KP + c4 + j, keepK[it][j]);
+        lds_put<T>(Kr + r * L::KP + c4 + j, kr[j]);
+        lds_put<T>(Qr + r * L::KP + c4 + j, qr[j]);
+        lds_put<T>(Kc + r * L::KP + c4 + j, kc[j]);
       }
-      // Kb^T rows are [DK][C]: element (row ch, col rr)
-      const int ch = idx / (C / 4), r4 = (idx % (C / 4)) * 4;
-      f32x4 x;
+    }
+    // Kb^T tile (rows = key channel): this thread's rows are consecutive, so
+    // groups of 4 stay contiguous under the column permutation.
 #pragma unroll
-      for (int j = 0; j < 4; ++j) x[j] = lds_get<T>(Kts + ch * (C + L::PADK) + r4 + j);
-      store4(oK + ch * C + r4, x);
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (RPT % 4 == 0) {
+#pragma unroll
+        for (int i4 = 0; i4 < RPT; i4 += 4) {
+          const f32x4 x4 = {kb[i4][j], kb[i4 + 1][j], kb[i4 + 2][j], kb[i4 + 3][j]};
+          store4(reinterpret_cast<T*>(blk + B::oK + toff<T, B::RB_K>(c4 + j, r0 + i4)), x4);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < RPT; ++i)
+          io<T>::store(reinterpret_cast<T*>(blk + B::oK + toff<T, B::RB_K>(c4 + j, r0 + i)), kb[i][j]);
+      }
     }
   }
-  __syncthreads();  // Kr, Qr, Kc ready; Kb^T staging free for A
+  __syncthreads();
 
-  // ---- a3: gated k k^T (A) and q k^T (P), 16x16 blocks via MFMA ----------
+  // ---- a3: gated k k^T (A, fp32 in LDS) and q k^T (P) via MFMA ------------
   {
-    typedef WsGeom<T, C, DK> W;
-    T* oP = wsP + slot * W::P;
     const int n = lane & 15, g = lane >> 4;
-    for (int blk = wave; blk < NB * NB; blk += 4) {
-      const int I = blk / NB, J = blk % NB;
+    for (int bi = wave; bi < NB * NB; bi += 4) {
+      const int I = bi / NB, J = bi % NB;
       f32x4 aA = {0.f, 0.f, 0.f, 0.f}, aP = {0.f, 0.f, 0.f, 0.f};
       if (J <= I) {
         const float* rs = (I == J) ? dr + I * DK : pr + (I * (I - 1) / 2 + J) * DK;
@@ -410,10 +486,8 @@ __global__ __launch_bounds__(256) void prep_kernel(const T* __restrict__ q, cons
           typename M::frag bf;
           if (I == J) bf = frag_nat(crow, dc + I * DK, k0, g);
           else bf = frag_nat(crow, k0, g);
-          const typename M::frag ak = frag_nat(krow, rs, k0, g);
-          const typename M::frag aq = frag_nat(qrow, rs, k0, g);
-          aA = M::mma(ak, bf, aA);
-          aP = M::mma(aq, bf, aP);
+          aA = M::mma(frag_nat(krow, rs, k0, g), bf, aA);
+          aP = M::mma(frag_nat(qrow, rs, k0, g), bf, aP);
         }
       }
 #pragma unroll
@@ -425,11 +499,18 @@ __global__ __launch_bounds__(256) void prep_kernel(const T* __restrict__ q, cons
         if (J > I || (I == J && rr <= n)) a = 0.f;
         if (J > I || (I == J && rr < n)) p = 0.f;
         A[row * L::AP + col] = a;
-        io<T>::store(oP + row * C + col, p);
+        lds_put<T>(Ps + row * L::CP + col, p);
       }
     }
   }
   __syncthreads();
+  for (int idx = tid; idx < C * C / 4; idx += 256) {
+    const int r = idx / (C / 4), c4b = (idx % (C / 4)) * 4;
+    f32x4 x;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[j] = lds_get<T>(Ps + r * L::CP + c4b + j);
+    store4(reinterpret_cast<T*>(blk + B::oP + toff<T, B::RB_K>(r, c4b)), x);
+  }
 
   // ---- a4: T = (I + A)^{-1} by blocked forward substitution --------------
   // Diagonal 16x16 blocks: lane j of wave I solves column j.
@@ -442,14 +523,13 @@ __global__ __launch_bounds__(256) void prep_kernel(const T* __restrict__ q, cons
         float acc = (r == j) ? 1.f : 0.f;
         const float* arow = A + (16 * I + r) * L::AP + 16 * I;
 #pragma unroll
-        for (int s = 0; s < r; ++s) acc -= arow[s] * t[s];
+        for (int s2 = 0; s2 < r; ++s2) acc -= arow[s2] * t[s2];
         t[r] = acc;
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) Ti[(16 * I + r) * L::AP + 16 * I + j] = t[r];
     }
   }
-  // zero the strictly upper blocks
   for (int idx = tid; idx < C * C; idx += 256) {
     const int r = idx / C, cc = idx % C;
     if ((cc >> 4) > (r >> 4)) Ti[r * L::AP + cc] = 0.f;
@@ -466,7 +546,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const T* __restrict__ q, cons
         const float* arow = A + (16 * I + i) * L::AP + 16 * K;
         const float* tcol = Ti + (16 * K) * L::AP + 16 * J + jj;
 #pragma unroll
-        for (int s = 0; s < 16; ++s) x += arow[s] * tcol[s * L::AP];
+        for (int s2 = 0; s2 < 16; ++s2) x += arow[s2] * tcol[s2 * L::AP];
       }
       X[b * 256 + i * 16 + jj] = x;
     }
@@ -481,79 +561,93 @@ __global__ __launch_bounds__(256) void prep_kernel(const T* __restrict__ q, cons
     }
     __syncthreads();
   }
-
-  // ---- write T -----------------------------------------------------------
-  {
-    typedef WsGeom<T, C, DK> W;
-    T* oT = wsT + slot * W::P;
-    for (int idx = tid; idx < C * C / 4; idx += 256) {
-      const int r = idx / (C / 4), c4 = (idx % (C / 4)) * 4;
-      f32x4 x;
+  for (int idx = tid; idx < C * C / 4; idx += 256) {
+    const int r = idx / (C / 4), c4b = (idx % (C / 4)) * 4;
+    f32x4 x;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) x[j] = Ti[r * L::AP + c4 + j];
-      store4(oT + r * C + c4, x);
+    for (int j = 0; j < 4; ++j) x[j] = Ti[r * L::AP + c4b + j];
+    store4(reinterpret_cast<T*>(blk + B::oT + toff<T, B::RB_K>(r, c4b)), x);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Scan kernel: one workgroup per (sequence, head, value tile of 16*WAVES
+// columns); wave w owns 16 columns and keeps its dk x 16 slice of the state
+// in MFMA accumulators for the whole sequence.  Chunk blocks stream into LDS
+// (double-buffered when two fit) with direct 16-byte loads issued one chunk
+// ahead; the bf16 path splits Y and D into hi + lo bf16 parts where they feed
+// the output (T Y and P D), keeping those contractions at ~fp32 accuracy.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ void lds_load16(const unsigned char* src, unsigned char* dst_wave_base) {
+  __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
+                                   (__attribute__((address_space(3))) void*)(dst_wave_base), 16, 0, 0);
+}
+
+// The first NS k-step A fragments of one stored-tile row (accumulator k map).
+template <typename T, int RB, int NS>
+struct RowFrags;
+template <int RB, int NS>
+struct RowFrags<bf16_t, RB, NS> {
+  bf16x8 f[NS];
+  __device__ __forceinline__ void load(const unsigned char* tile, int row, int g) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      f[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(tile + goff<RB>(row, 4 * s + g)));
+  }
+};
+template <int RB, int NS>
+struct RowFrags<float, RB, NS> {
+  float f[NS];
+  __device__ __forceinline__ void load(const unsigned char* tile, int row, int g) {
+#pragma unroll
+    for (int t = 0; t < (NS + 3) / 4; ++t) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(tile + goff<RB>(row, 4 * t + g));
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (4 * t + j < NS) f[4 * t + j] = x[j];
     }
   }
-}
-
-// ---------------------------------------------------------------------------
-// Scan kernel: one workgroup per (sequence, head, 64-column value tile); four
-// waves, each owning 16 value columns.  The state tile lives in MFMA
-// accumulators (DK/16 tiles of 16x16 fp32 per wave) for the whole sequence.
-// ---------------------------------------------------------------------------
-template <typename T, int C, int DK>
-struct ScanLds {
-  static constexpr int PAD = 8;
-  static constexpr int RP = DK + PAD;  // pitch of R and Qh rows
-  static constexpr int CP = C + PAD;   // pitch of Kb^T, P and T rows
-  static constexpr size_t oR = 0;
-  static constexpr size_t oQ = oR + static_cast<size_t>(C) * RP * sizeof(T);
-  static constexpr size_t oK = oQ + static_cast<size_t>(C) * RP * sizeof(T);
-  static constexpr size_t oP = oK + static_cast<size_t>(DK) * CP * sizeof(T);
-  static constexpr size_t oT = oP + static_cast<size_t>(C) * CP * sizeof(T);
-  static constexpr size_t oG = oT + static_cast<size_t>(C) * CP * sizeof(T);
-  static constexpr size_t oB = oG + static_cast<size_t>(DK) * 4;
-  static constexpr size_t total = oB + static_cast<size_t>(C) * 4;
 };
 
-// Copy `rows` rows of `cols` io elements (contiguous in global) into LDS with
-// pitch `pitch`, 16 bytes per lane.
-template <typename T>
-__device__ __forceinline__ void copy_rows(T* dst, int pitch, const T* src, int rows, int cols, int tid) {
-  constexpr int E = 16 / sizeof(T);
-  const int per_row = cols / E;
-  for (int idx = tid; idx < rows * per_row; idx += 256) {
-    const int r = idx / per_row, c = (idx % per_row) * E;
-    *reinterpret_cast<uint4*>(dst + r * pitch + c) = *reinterpret_cast<const uint4*>(src + r * cols + c);
-  }
-}
+// Loader waves per scan workgroup: they only stream the next chunk into LDS.
+constexpr int kLoaderWaves = 2;
 
-template <typename T, int C, int DK, int DV>
-__global__ __launch_bounds__(256) void scan_kernel(const T* __restrict__ v, const float* __restrict__ beta,
-                                                   const int32_t* __restrict__ cu,
-                                                   const int32_t* __restrict__ chunk_off,
-                                                   const int32_t* __restrict__ order, int N, int H,
-                                                   const T* __restrict__ wsR, const T* __restrict__ wsQ,
-                                                   const T* __restrict__ wsKt, const T* __restrict__ wsP,
-                                                   const T* __restrict__ wsT, const float* __restrict__ wsG,
-                                                   const float* S0, T* __restrict__ o, float* S_T) {
-  typedef ScanLds<T, C, DK> L;
+template <typename T, int C, int DK, int TILE>
+struct ScanLds {
+  typedef Blk<T, C, DK> B;
+  static constexpr size_t vtile = static_cast<size_t>(C) * TILE * sizeof(T);  // v rows of this tile
+  static constexpr size_t vbytes = (vtile + 1023) / 1024 * 1024;
+  static constexpr size_t stage = B::bytes + vbytes;
+  static constexpr int NBUF = (2 * stage <= 160 * 1024) ? 2 : 1;
+  static constexpr size_t total = NBUF * stage;
+};
+
+template <typename T, int C, int DK, int DV, int WAVES>
+__global__ __launch_bounds__(64 * (WAVES + kLoaderWaves)) void scan_kernel(
+    const T* __restrict__ v, const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_off,
+    const int32_t* __restrict__ order, int N, int H, const unsigned char* __restrict__ ws, const float* S0,
+    T* __restrict__ o, float* S_T) {
+  typedef Blk<T, C, DK> B;
   typedef mma16<T> M;
   typedef accb<T> AB;
-  typedef WsGeom<T, C, DK> W;
-  constexpr int NSPLIT = DV / 64;
-  constexpr int MT = C / 16;   // chunk-row tiles
-  constexpr int ST = DK / 16;  // state row tiles
-  extern __shared__ __align__(16) unsigned char smem[];
-  T* Rs = reinterpret_cast<T*>(smem + L::oR);
-  T* Qs = reinterpret_cast<T*>(smem + L::oQ);
-  T* Ks = reinterpret_cast<T*>(smem + L::oK);
-  T* Ps = reinterpret_cast<T*>(smem + L::oP);
-  T* Ts = reinterpret_cast<T*>(smem + L::oT);
-  float* Gs = reinterpret_cast<float*>(smem + L::oG);
-  float* Bs = reinterpret_cast<float*>(smem + L::oB);
+  typedef split<T> SP;
+  typedef typename M::frag F;
+  constexpr int TILE = 16 * WAVES;
+  typedef ScanLds<T, C, DK, TILE> SL;
+  constexpr int NSPLIT = DV / TILE;
+  constexpr int MT = C / 16;
+  constexpr int ST = DK / 16;
+  constexpr int NSK = DK / AB::KS;  // k-steps over key channels
+  constexpr int NSC = C / AB::KS;   // k-steps over chunk rows
+  constexpr int NG = static_cast<int>(B::bytes / 1024);  // 1 KB wave-loads per block
+  constexpr int VROWB = TILE * static_cast<int>(sizeof(T));  // bytes of one v row of the tile
+  constexpr int VLPR = VROWB / 16;                            // lanes per v row
+  constexpr int VRPL = 64 / VLPR;                             // v rows per wave-load
+  constexpr int NVG = C / VRPL;                               // wave-loads per v tile
+  static_assert(VROWB % 16 == 0 && 64 % VLPR == 0 && C % VRPL == 0, "v tile geometry");
+  extern __shared__ __align__(1024) unsigned char smem[];
 
-  // blockIdx -> (pair, tile) with all tiles of a pair on one XCD (x % 8).
   const int x = blockIdx.x;
   const int xcd = x & 7, slot8 = x >> 3;
   const int tile = slot8 % NSPLIT, grp = slot8 / NSPLIT;
@@ -562,84 +656,161 @@ __global__ __launch_bounds__(256) void scan_kernel(const T* __restrict__ v, cons
   const int seq = order[p / H];
   const int h = p % H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = lane & 15, g = lane >> 4;
-  const int col = tile * 64 + wave * 16 + n;  // this lane's value column
+  const bool loader = wave >= WAVES;
   const int tbeg = cu[seq], L_seq = cu[seq + 1] - tbeg;
   const int c0 = chunk_off[seq];
   const int nch = (L_seq + C - 1) / C;
 
+  // Loader waves: block of chunk cc and its v tile into stage b.
+  auto issue = [&](int cc, int b) {
+    const int lw = wave - WAVES;
+    const unsigned char* src = ws + (static_cast<size_t>(c0 + cc) * H + h) * B::bytes;
+    unsigned char* dst = smem + b * SL::stage;
+    for (int j = lw; j < NG; j += kLoaderWaves) lds_load16(src + j * 1024 + lane * 16, dst + j * 1024);
+    const int t0 = tbeg + cc * C, len = min(C, L_seq - cc * C);
+    unsigned char* vdst = dst + B::bytes;
+    for (int j = lw; j < NVG; j += kLoaderWaves) {
+      const int r = j * VRPL + lane / VLPR;
+      const int rr = r < len ? r : len - 1;  // rows past the end are masked by beta = 0
+      const unsigned char* vsrc = reinterpret_cast<const unsigned char*>(
+                                      v + (static_cast<size_t>(t0 + rr) * H + h) * DV + tile * TILE) +
+                                  (lane % VLPR) * 16;
+      lds_load16(vsrc, vdst + j * 1024);
+    }
+  };
+
+  if (loader) {
+    if (nch > 0) issue(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int cc = 0; cc < nch; ++cc) {
+      const int b = (SL::NBUF == 2) ? (cc & 1) : 0;
+      if (SL::NBUF == 2 && cc + 1 < nch) {
+        issue(cc + 1, b ^ 1);
+        __builtin_amdgcn_s_waitcnt(0);
+      }
+      __syncthreads();  // chunk cc consumed; chunk cc+1 resident
+      if (SL::NBUF == 1 && cc + 1 < nch) {
+        issue(cc + 1, 0);
+        __builtin_amdgcn_s_waitcnt(0);
+      }
+      if (SL::NBUF == 1) __syncthreads();
+    }
+    return;
+  }
+
+  // Compute waves: wave w owns 16 value columns; state slice in accumulators.
+  const int n = lane & 15, g = lane >> 4;
+  const int col = tile * TILE + wave * 16 + n;
   f32x4 S[ST];
   const size_t sbase = (static_cast<size_t>(seq) * H + h) * DK * DV;
+  if (S0) {
 #pragma unroll
-  for (int st = 0; st < ST; ++st)
+    for (int st = 0; st < ST; ++st)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      S[st][i] = S0 ? S0[sbase + static_cast<size_t>(16 * st + 4 * g + i) * DV + col] : 0.f;
+      for (int i = 0; i < 4; ++i) S[st][i] = S0[sbase + static_cast<size_t>(16 * st + 4 * g + i) * DV + col];
+  } else {
+#pragma unroll
+    for (int st = 0; st < ST; ++st) S[st] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  __syncthreads();  // chunk 0 resident
 
   for (int cc = 0; cc < nch; ++cc) {
-    const size_t wslot = static_cast<size_t>(c0 + cc) * H + h;
-    const int t0 = tbeg + cc * C;
-    const int len = min(C, L_seq - cc * C);
-    __syncthreads();
-    copy_rows<T>(Rs, L::RP, wsR + wslot * W::R, C, DK, tid);
-    copy_rows<T>(Qs, L::RP, wsQ + wslot * W::R, C, DK, tid);
-    copy_rows<T>(Ks, L::CP, wsKt + wslot * W::R, DK, C, tid);
-    copy_rows<T>(Ps, L::CP, wsP + wslot * W::P, C, C, tid);
-    copy_rows<T>(Ts, L::CP, wsT + wslot * W::P, C, C, tid);
-    for (int i = tid; i < DK; i += 256) Gs[i] = wsG[wslot * DK + i];
-    if (tid < C) Bs[tid] = tid < len ? beta[static_cast<size_t>(t0 + tid) * H + h] : 0.f;
-    __syncthreads();
+    const int b = (SL::NBUF == 2) ? (cc & 1) : 0;
+    const unsigned char* blk = smem + b * SL::stage;
+    const T* vt = reinterpret_cast<const T*>(blk + B::bytes);
+    const float* Gam = reinterpret_cast<const float*>(blk + B::oG);
+    const float* Bet = reinterpret_cast<const float*>(blk + B::oB);
+    const int t0 = tbeg + cc * C, len = min(C, L_seq - cc * C);
 
-    // Y = b*V - R S
+    // B fragments of the state (shared by R S and Qh S)
+    F sb[NSK];
+#pragma unroll
+    for (int s = 0; s < NSK; ++s) sb[s] = AB::b(S, s);
+
+    // Y = b*V - R S, A fragments read one M-tile ahead
     f32x4 Y[MT];
+    {
+      RowFrags<T, B::RB_R, NSK> cur, nxt;
+      cur.load(blk + B::oR, n, g);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const T* arow = Rs + (16 * mt + n) * L::RP;
+      for (int mt = 0; mt < MT; ++mt) {
+        if (mt + 1 < MT) nxt.load(blk + B::oR, 16 * (mt + 1) + n, g);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < DK / AB::KS; ++s) acc = M::mma(AB::a(arow, s, g), AB::b(S, s), acc);
+        for (int s = 0; s < NSK; ++s) acc = M::mma(cur.f[s], sb[s], acc);
+        const f32x4 bt = *reinterpret_cast<const f32x4*>(Bet + 16 * mt + 4 * g);
+        f32x4 vv;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * mt + 4 * g + i;
-        const float vv = row < len ? io<T>::load(v + (static_cast<size_t>(t0 + row) * H + h) * DV + col) : 0.f;
-        Y[mt][i] = Bs[row] * vv - acc[i];
+        for (int i = 0; i < 4; ++i) vv[i] = io<T>::load(vt + (16 * mt + 4 * g + i) * TILE + wave * 16 + n);
+        Y[mt] = bt * vv - acc;
+        if (mt + 1 < MT) cur = nxt;
       }
     }
-    // D = T Y   (T unit lower triangular: k-steps past the diagonal are zero)
+    // D = T Y with Y split into hi + lo (T unit lower triangular)
     f32x4 D[MT];
+    {
+      F yh[NSC], yl[NSC];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const T* arow = Ts + (16 * mt + n) * L::CP;
+      for (int s = 0; s < NSC; ++s) SP::hilo(Y, s, yh[s], yl[s]);
+      RowFrags<T, B::RB_K, NSC> tf[MT];
 #pragma unroll
-      for (int s = 0; s <= (16 * mt + 15) / AB::KS; ++s) acc = M::mma(AB::a(arow, s, g), AB::b(Y, s), acc);
-      D[mt] = acc;
+      for (int mt = 0; mt < MT; ++mt) tf[mt].load(blk + B::oT, 16 * mt + n, g);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s <= (16 * mt + 15) / AB::KS; ++s) {
+          acc = M::mma(tf[mt].f[s], yh[s], acc);
+          if (SP::has_lo) acc = M::mma(tf[mt].f[s], yl[s], acc);
+        }
+        D[mt] = acc;
+      }
     }
-    // O = Qh S + P D
+    F dh[NSC], dl[NSC];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const T* qrow = Qs + (16 * mt + n) * L::RP;
+    for (int s = 0; s < NSC; ++s) SP::hilo(D, s, dh[s], dl[s]);
+    // O = Qh S + P D  (D split into hi + lo); stored as soon as it is formed
+    {
+      RowFrags<T, B::RB_K, NSC> pf[MT];
 #pragma unroll
-      for (int s = 0; s < DK / AB::KS; ++s) acc = M::mma(AB::a(qrow, s, g), AB::b(S, s), acc);
-      const T* prow = Ps + (16 * mt + n) * L::CP;
+      for (int mt = 0; mt < MT; ++mt) pf[mt].load(blk + B::oP, 16 * mt + n, g);
+      RowFrags<T, B::RB_R, NSK> cur, nxt;
+      cur.load(blk + B::oQ, n, g);
 #pragma unroll
-      for (int s = 0; s <= (16 * mt + 15) / AB::KS; ++s) acc = M::mma(AB::a(prow, s, g), AB::b(D, s), acc);
+      for (int mt = 0; mt < MT; ++mt) {
+        if (mt + 1 < MT) nxt.load(blk + B::oQ, 16 * (mt + 1) + n, g);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * mt + 4 * g + i;
-        if (row < len) io<T>::store(o + (static_cast<size_t>(t0 + row) * H + h) * DV + col, acc[i]);
+        for (int s = 0; s < NSK; ++s) acc = M::mma(cur.f[s], sb[s], acc);
+#pragma unroll
+        for (int s = 0; s <= (16 * mt + 15) / AB::KS; ++s) {
+          acc = M::mma(pf[mt].f[s], dh[s], acc);
+          if (SP::has_lo) acc = M::mma(pf[mt].f[s], dl[s], acc);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 16 * mt + 4 * g + i;
+          if (row < len) io<T>::store(o + (static_cast<size_t>(t0 + row) * H + h) * DV + col, acc[i]);
+        }
+        if (mt + 1 < MT) cur = nxt;
       }
     }
     // S = Diag(e^{g_last}) S + Kb^T D
+    {
+      RowFrags<T, B::RB_K, NSC> cur, nxt;
+      cur.load(blk + B::oK, n, g);
 #pragma unroll
-    for (int st = 0; st < ST; ++st) {
+      for (int st = 0; st < ST; ++st) {
+        if (st + 1 < ST) nxt.load(blk + B::oK, 16 * (st + 1) + n, g);
+        S[st] *= *reinterpret_cast<const f32x4*>(Gam + 16 * st + 4 * g);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) S[st][i] *= Gs[16 * st + 4 * g + i];
-      const T* krow = Ks + (16 * st + n) * L::CP;
-#pragma unroll
-      for (int s = 0; s < C / AB::KS; ++s) S[st] = M::mma(AB::a(krow, s, g), AB::b(D, s), S[st]);
+        for (int s = 0; s < NSC; ++s) S[st] = M::mma(cur.f[s], dh[s], S[st]);
+        if (st + 1 < ST) cur = nxt;
+      }
     }
+    __syncthreads();  // done with stage b; chunk cc+1 resident
+    if (SL::NBUF == 1) __syncthreads();
   }
   if (S_T) {
 #pragma unroll
@@ -654,6 +825,12 @@ __global__ __launch_bounds__(256) void scan_kernel(const T* __restrict__ v, cons
 // ---------------------------------------------------------------------------
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
+static size_t block_bytes(kda_dtype dt, int C, int dk) {
+  const size_t es = dt == KDA_BF16 ? 2 : 4;
+  const size_t b = static_cast<size_t>(C) * dk * es * 3 + static_cast<size_t>(C) * C * es * 2 + dk * 4 + C * 4;
+  return (b + 1023) / 1024 * 1024;
+}
+
 bool make_prefill_plan(const kda_prefill_desc* d, int64_t max_chunks, PrefillPlan* p) {
   p->N = d->num_seqs;
   p->T = d->total_tokens;
@@ -664,19 +841,31 @@ bool make_prefill_plan(const kda_prefill_desc* d, int64_t max_chunks, PrefillPla
   p->dt = d->io_dtype;
   p->max_chunks = max_chunks;
   p->sort = d->num_seqs <= 8192;
-  const size_t es = d->io_dtype == KDA_BF16 ? 2 : 4;
   const size_t slots = static_cast<size_t>(max_chunks) * d->num_heads;
   size_t off = 0;
   p->off_chunk_off = off; off = align256(off + 4 * (static_cast<size_t>(d->num_seqs) + 1));
   p->off_order = off;     off = align256(off + 4 * (static_cast<size_t>(d->num_seqs) + 1));
-  p->off_R = off;  off = align256(off + slots * d->chunk * d->dk * es);
-  p->off_Q = off;  off = align256(off + slots * d->chunk * d->dk * es);
-  p->off_Kt = off; off = align256(off + slots * d->chunk * d->dk * es);
-  p->off_P = off;  off = align256(off + slots * d->chunk * d->chunk * es);
-  p->off_T = off;  off = align256(off + slots * d->chunk * d->chunk * es);
-  p->off_G = off;  off = align256(off + slots * d->dk * 4);
-  p->total_bytes = off;
+  off = (off + 1023) / 1024 * 1024;
+  p->off_blocks = off;    off += slots * block_bytes(d->io_dtype, d->chunk, d->dk);
+  p->total_bytes = align256(off);
   return true;
+}
+
+template <typename T, int C, int DK, int DV, int WAVES>
+static hipError_t launch_scan(const PrefillPlan& p, const void* v, const int32_t* cu, const int32_t* chunk_off,
+                              const int32_t* order, const unsigned char* blocks, const float* S0, void* o,
+                              float* S_T, hipStream_t st) {
+  typedef ScanLds<T, C, DK, 16 * WAVES> SL;
+  static_assert(SL::total <= 160 * 1024, "scan LDS");
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_kernel<T, C, DK, DV, WAVES>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(SL::total));
+  if (e != hipSuccess) return e;
+  const int pairs = p.N * p.H;
+  const int nsplit = DV / (16 * WAVES);
+  const unsigned grid = static_cast<unsigned>((pairs + 7) / 8 * 8 * nsplit);
+  hipLaunchKernelGGL((scan_kernel<T, C, DK, DV, WAVES>), dim3(grid), dim3(64 * (WAVES + kLoaderWaves)), SL::total, st,
+                     static_cast<const T*>(v), cu, chunk_off, order, p.N, p.H, blocks, S0, static_cast<T*>(o), S_T);
+  return hipGetLastError();
 }
 
 template <typename T, int C, int DK, int DV>
@@ -686,12 +875,7 @@ static hipError_t launch_prefill_t(const PrefillPlan& p, const void* q, const vo
   unsigned char* w = static_cast<unsigned char*>(ws);
   int32_t* chunk_off = reinterpret_cast<int32_t*>(w + p.off_chunk_off);
   int32_t* order = reinterpret_cast<int32_t*>(w + p.off_order);
-  T* R = reinterpret_cast<T*>(w + p.off_R);
-  T* Q = reinterpret_cast<T*>(w + p.off_Q);
-  T* Kt = reinterpret_cast<T*>(w + p.off_Kt);
-  T* P = reinterpret_cast<T*>(w + p.off_P);
-  T* Tm = reinterpret_cast<T*>(w + p.off_T);
-  float* Gm = reinterpret_cast<float*>(w + p.off_G);
+  unsigned char* blocks = w + p.off_blocks;
   if (p.N == 0) return hipSuccess;
   hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(1024), 0, st, cu, p.N, C, chunk_off, order, p.sort);
   hipError_t e = hipGetLastError();
@@ -703,22 +887,16 @@ static hipError_t launch_prefill_t(const PrefillPlan& p, const void* q, const vo
                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lp));
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((prep_kernel<T, C, DK>), dim3(static_cast<unsigned>(p.max_chunks), p.H), dim3(256), lp, st,
-                       static_cast<const T*>(q), static_cast<const T*>(k), la, beta, cu, chunk_off, p.N, p.H, R, Q,
-                       Kt, P, Tm, Gm);
+                       static_cast<const T*>(q), static_cast<const T*>(k), la, beta, cu, chunk_off, p.N, p.H,
+                       blocks);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const size_t ls = ScanLds<T, C, DK>::total;
-  static_assert(ScanLds<T, C, DK>::total <= 160 * 1024, "scan LDS");
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_kernel<T, C, DK, DV>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(ls));
-  if (e != hipSuccess) return e;
-  const int pairs = p.N * p.H;
-  const int nsplit = DV / 64;
-  const unsigned grid = static_cast<unsigned>((pairs + 7) / 8 * 8 * nsplit);
-  hipLaunchKernelGGL((scan_kernel<T, C, DK, DV>), dim3(grid), dim3(256), ls, st, static_cast<const T*>(v), beta, cu,
-                     chunk_off, order, p.N, p.H, R, Q, Kt, P, Tm, Gm, S0, static_cast<T*>(o), S_T);
-  return hipGetLastError();
+  // Few (sequence, head) pairs: narrower value tiles to put more CUs on the
+  // serial pass; many pairs: wider tiles to load each chunk block fewer times.
+  const long wide_wgs = static_cast<long>(p.N) * p.H * (DV / 64);
+  if (wide_wgs < 512) return launch_scan<T, C, DK, DV, 2>(p, v, cu, chunk_off, order, blocks, S0, o, S_T, st);
+  return launch_scan<T, C, DK, DV, 4>(p, v, cu, chunk_off, order, blocks, S0, o, S_T, st);
 }
 
 template <typename T, int C>

@@ -117,3 +117,15 @@ def test_deterministic():
     o1, S1 = gpu_prefill(w)
     o2, S2 = gpu_prefill(w)
     assert np.array_equal(o1, o2) and np.array_equal(S1, S2)
+
+
+def test_many_pairs_wide_tiles():
+    """Enough (sequence, head) pairs that the scan uses its wide value tiles."""
+    rng = np.random.default_rng(19)
+    lengths = [int(x) for x in rng.integers(0, 200, size=64)]
+    w = synth.make_prefill(lengths, H=8, dk=128, dv=128, io_dtype="bf16", seed=19, S0_std=0.05)
+    log("prefill many pairs: %d seqs x 8 heads" % len(lengths))
+    o, S = gpu_prefill(w)
+    o_ref, S_ref = oracle_prefill(w)
+    check("o", o, o_ref, TOL["bf16"])
+    check("S_T", S, S_ref, TOL["bf16"])
