@@ -294,33 +294,99 @@ struct split<float> {
 };
 
 // ---------------------------------------------------------------------------
-// Prep kernel: one workgroup (256 threads) per (chunk, head).
+// Prep kernel: one workgroup (kPrepThreads threads) per (chunk, head).  The grid's x
+// index is the head, so the workgroups that run together cover whole token
+// rows of q, k and log_alpha.
+//
+// Gated products.  For rows r of 16-row block I and columns s of block J <= I
+//   e^{g_r - g_s} = [e^{g_r - g_{m_I}}] [e^{g_{m_I} - g_{e_J}}] [e^{g_{e_J} - g_s}]
+// with m_I the 9th row of block I and e_J the last row of block J.  The first
+// factor goes into the stored row operands (Krd, Qrd), the last into the
+// stored column operand (Kc), and the middle one is a per-channel vector that
+// scales the column fragment of block (I, J).  Every factor stays below
+// e^{8 max|log_alpha|}; the row operands are read raw.
 // ---------------------------------------------------------------------------
+constexpr int kPrepThreads = 512;
+
 template <typename T, int C, int DK>
 struct PrepLds {
   static constexpr int NB = C / 16;
-  static constexpr int NPAIR = NB * (NB - 1) / 2;
-  static constexpr int NRB = 1024 / DK;      // row blocks (threads per channel group)
-  static constexpr int PADK = sizeof(T) == 2 ? 8 : 4;  // keeps 16-row fragment reads conflict-free
-  static constexpr int KP = DK + PADK;       // pitch (elements) of Kr / Qr / Kc
-  static constexpr int AP = C + 1;           // pitch (floats) of A / Ti
-  static constexpr int CP = C + PADK;        // pitch (elements) of the P staging tile
+  static constexpr int NLB = NB * (NB + 1) / 2;  // lower blocks incl. the diagonal
+  static constexpr int NRB = 4 * kPrepThreads / DK;  // row blocks (threads per channel group)
+  static constexpr int RBK = DK * static_cast<int>(sizeof(T));  // row bytes of Krd / Qrd / Kc
+  static constexpr int AP = C + 1;               // pitch (floats) of A / Ti
+  static constexpr int CP = C + 8;               // pitch (elements) of the P staging tile
+  static constexpr int SP = 17;                  // pitch (floats) of 16x16 inverse scratch tiles
   static constexpr size_t a16(size_t x) { return (x + 15) / 16 * 16; }
   static constexpr size_t mx(size_t a, size_t b) { return a > b ? a : b; }
-  // region 0: Kr, Qr, Kc (io) -> later Ti (f32)
-  static constexpr size_t r0 = a16(mx(static_cast<size_t>(3) * C * KP * sizeof(T), static_cast<size_t>(C) * AP * 4));
+  static constexpr size_t szTi = static_cast<size_t>(C) * AP * 4;
+  static constexpr size_t szScr = static_cast<size_t>(NB) * 3 * 16 * SP * 4;  // NB waves x 3 tiles
+  // region 0: Krd, Qrd, Kc (io, swizzled rows) -> later Ti + inverse scratch (f32)
+  static constexpr size_t r0 = a16(mx(static_cast<size_t>(3) * C * RBK, szTi + szScr));
   // region 1: A (f32)
   static constexpr size_t r1 = a16(static_cast<size_t>(C) * AP * 4);
-  // region 2: refs gB gM gE [NB][DK] + partial sums [NRB][DK] (f32) -> later P staging (io)
+  // region 2: gB gM gE [NB][DK] + partial sums [NRB][DK] (f32) -> later P staging (io)
   static constexpr size_t r2 = a16(mx(static_cast<size_t>(3 * NB + NRB) * DK * 4, static_cast<size_t>(C) * CP * sizeof(T)));
-  // region 3: dr, dc [NB][DK], pair [NPAIR][DK] (f32) -> later inverse scratch
-  static constexpr size_t r3 = a16(mx(static_cast<size_t>(2 * NB + NPAIR) * DK * 4, static_cast<size_t>(NB) * 256 * 4));
+  // region 3: block-pair vectors f[NLB][DK] (f32)
+  static constexpr size_t r3 = a16(static_cast<size_t>(NLB) * DK * 4);
   static constexpr size_t o0 = 0, o1 = r0, o2 = o1 + r1, o3 = o2 + r2, o4 = o3 + r3;
   static constexpr size_t total = o4 + static_cast<size_t>(C) * 4;  // + beta
 };
 
+// byte offset of element (row, c) in an unpadded LDS tile with RB-byte rows,
+// 16-byte granules XOR-swizzled by row (conflict-free 16-row fragment reads)
+template <typename T, int RB>
+__device__ __forceinline__ int loff(int row, int c) {
+  constexpr int EPG = 16 / static_cast<int>(sizeof(T));
+  return row * RB + 16 * ((c / EPG) ^ swz<RB>(row)) + (c % EPG) * static_cast<int>(sizeof(T));
+}
+
+// natural-map fragments (slot (g, j) <-> k = k0 + 8 g + j for bf16, k0 + g for fp32)
+template <typename T, int RB>
+struct natf;
+template <int RB>
+struct natf<bf16_t, RB> {
+  __device__ __forceinline__ static bf16x8 raw(const unsigned char* t, int row, int k0, int g) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(t + loff<bf16_t, RB>(row, k0 + 8 * g)));
+  }
+  __device__ __forceinline__ static bf16x8 scaled(const unsigned char* t, int row, const float* sc, int k0, int g) {
+    const uint4 u = *reinterpret_cast<const uint4*>(t + loff<bf16_t, RB>(row, k0 + 8 * g));
+    const f32x4 s0 = *reinterpret_cast<const f32x4*>(sc + k0 + 8 * g);
+    const f32x4 s1 = *reinterpret_cast<const f32x4*>(sc + k0 + 8 * g + 4);
+    bf16x8 r;
+    r[0] = to_bf(__uint_as_float(u.x << 16) * s0[0]);
+    r[1] = to_bf(__uint_as_float(u.x & 0xFFFF0000u) * s0[1]);
+    r[2] = to_bf(__uint_as_float(u.y << 16) * s0[2]);
+    r[3] = to_bf(__uint_as_float(u.y & 0xFFFF0000u) * s0[3]);
+    r[4] = to_bf(__uint_as_float(u.z << 16) * s1[0]);
+    r[5] = to_bf(__uint_as_float(u.z & 0xFFFF0000u) * s1[1]);
+    r[6] = to_bf(__uint_as_float(u.w << 16) * s1[2]);
+    r[7] = to_bf(__uint_as_float(u.w & 0xFFFF0000u) * s1[3]);
+    return r;
+  }
+};
+template <int RB>
+struct natf<float, RB> {
+  __device__ __forceinline__ static float raw(const unsigned char* t, int row, int k0, int g) {
+    return *reinterpret_cast<const float*>(t + loff<float, RB>(row, k0 + g));
+  }
+  __device__ __forceinline__ static float scaled(const unsigned char* t, int row, const float* sc, int k0, int g) {
+    return raw(t, row, k0, g) * sc[k0 + g];
+  }
+};
+
+// 16x16x16 fp32 product X * Y on MFMA: X row-major in LDS (pitch xp floats),
+// Y in accumulator layout (lane (n, g) holds Y[4g + i][n]); k-step s pairs
+// X[m][4g + s] with Y[4g + s][n].
+__device__ __forceinline__ f32x4 mm16_lds_acc(const float* X, int xp, f32x4 Y, int m, int g, float xsign = 1.f) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) acc = mma16<float>::mma(xsign * X[m * xp + 4 * g + s], Y[s], acc);
+  return acc;
+}
+
 template <typename T, int C, int DK>
-__global__ __launch_bounds__(256) void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
+__global__ __launch_bounds__(kPrepThreads) void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                    const float* __restrict__ la, const float* __restrict__ beta,
                                                    const int32_t* __restrict__ cu,
                                                    const int32_t* __restrict__ chunk_off, int N, int H,
@@ -328,28 +394,27 @@ __global__ __launch_bounds__(256) void prep_kernel(const T* __restrict__ q, cons
   typedef PrepLds<T, C, DK> L;
   typedef Blk<T, C, DK> B;
   typedef mma16<T> M;
+  typedef mma16<float> MF;
   constexpr int NB = L::NB;
-  constexpr int NCG = DK / 4;     // channel groups of 4
-  constexpr int RPT = C / L::NRB; // rows per thread
+  constexpr int NCG = DK / 4;      // channel groups of 4
+  constexpr int RPT = C / L::NRB;  // rows per thread
   static_assert(RPT >= 1 && 16 % RPT == 0, "row blocks must tile 16-row sub-blocks");
   extern __shared__ __align__(16) unsigned char smem[];
-  T* Kr = reinterpret_cast<T*>(smem + L::o0);
-  T* Qr = Kr + C * L::KP;
-  T* Kc = Qr + C * L::KP;
+  unsigned char* Krd = smem + L::o0;
+  unsigned char* Qrd = Krd + C * L::RBK;
+  unsigned char* Kc = Qrd + C * L::RBK;
   float* Ti = reinterpret_cast<float*>(smem + L::o0);
+  float* scr = reinterpret_cast<float*>(smem + L::o0 + L::szTi);
   float* A = reinterpret_cast<float*>(smem + L::o1);
   float* gB = reinterpret_cast<float*>(smem + L::o2);
   float* gM = gB + NB * DK;
   float* gE = gM + NB * DK;
   float* part = gE + NB * DK;
   T* Ps = reinterpret_cast<T*>(smem + L::o2);
-  float* dr = reinterpret_cast<float*>(smem + L::o3);
-  float* dc = dr + NB * DK;
-  float* pr = dc + NB * DK;
-  float* X = reinterpret_cast<float*>(smem + L::o3);
+  float* fv = reinterpret_cast<float*>(smem + L::o3);
   float* bet = reinterpret_cast<float*>(smem + L::o4);
 
-  const int c = blockIdx.x, h = blockIdx.y;
+  const int h = blockIdx.x, c = blockIdx.y;
   const int total = chunk_off[N];
   if (c >= total) return;
   int lo = 0, hi = N - 1;
@@ -361,6 +426,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const T* __restrict__ q, cons
   const int len = min(C, cu[lo + 1] - t0);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
   unsigned char* blk = ws + (static_cast<size_t>(c) * H + h) * B::bytes;
 
   // ---- loads: thread owns channels c4..c4+3 of rows r0..r0+RPT-1 ---------
@@ -390,7 +456,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const T* __restrict__ q, cons
   __syncthreads();
   {
     f32x4 off = {0.f, 0.f, 0.f, 0.f};
-    for (int p = 0; p < rbk; ++p) off += *reinterpret_cast<const f32x4*>(part + p * DK + c4);
+    for (int pp = 0; pp < rbk; ++pp) off += *reinterpret_cast<const f32x4*>(part + pp * DK + c4);
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       lg[i] += off;
@@ -402,34 +468,30 @@ __global__ __launch_bounds__(256) void prep_kernel(const T* __restrict__ q, cons
   }
   __syncthreads();
 
-  // ---- reference vectors for the gated matrices -------------------------
-  for (int idx = tid; idx < NB * DK; idx += 256) {
-    dr[idx] = __expf(gB[idx] - gM[idx]);  // >= 1, bounded by 8 tokens of decay
-    dc[idx] = __expf(gM[idx] - gE[idx]);
+  // ---- block-pair vectors e^{g_{m_I} - g_{e_J}}, J <= I ---------------------
+  for (int idx = tid; idx < L::NLB * DK; idx += kPrepThreads) {
+    const int pp = idx / DK, ch = idx % DK;
+    int I = 0;
+    while ((I + 1) * (I + 2) / 2 <= pp) ++I;
+    const int J = pp - I * (I + 1) / 2;
+    fv[idx] = __expf(gM[I * DK + ch] - gE[J * DK + ch]);
   }
-  for (int idx = tid; idx < L::NPAIR * DK; idx += 256) {
-    const int p = idx / DK, ch = idx % DK;
-    int I = 1;
-    while ((I + 1) * I / 2 <= p) ++I;
-    const int J = p - I * (I - 1) / 2;
-    pr[idx] = __expf(gB[I * DK + ch] - gE[J * DK + ch]);  // <= 1
-  }
-  if (tid < DK) {
-    reinterpret_cast<float*>(blk + B::oG)[tid] = __expf(gE[(NB - 1) * DK + tid]);
-  }
+  if (tid < DK) reinterpret_cast<float*>(blk + B::oG)[tid] = __expf(gE[(NB - 1) * DK + tid]);
   if (tid < C) reinterpret_cast<float*>(blk + B::oB)[tid] = bet[tid];
 
   // ---- element factors, S-independent outputs ---------------------------
   {
     const int I = r0 >> 4;  // all of this thread's rows are in block I
     const f32x4 gb = *reinterpret_cast<const f32x4*>(gB + I * DK + c4);
+    const f32x4 gm = *reinterpret_cast<const f32x4*>(gM + I * DK + c4);
     const f32x4 ge = *reinterpret_cast<const f32x4*>(gE + I * DK + c4);
     const f32x4 gz = *reinterpret_cast<const f32x4*>(gE + (NB - 1) * DK + c4);
-    f32x4 ebv, eev, kb[RPT];
+    f32x4 drv, ebv, eev, kb[RPT];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      ebv[j] = __expf(gb[j]);          // e^{g_b}, <= 1
-      eev[j] = __expf(gz[j] - ge[j]);  // e^{g_last - g_e}, <= 1
+      drv[j] = __expf(gb[j] - gm[j]);  // e^{g_b - g_m}: >= 1, at most 8 tokens of decay
+      ebv[j] = __expf(gb[j]);          // e^{g_b} <= 1
+      eev[j] = __expf(gz[j] - ge[j]);  // e^{g_last - g_e} <= 1
     }
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
@@ -440,16 +502,15 @@ __global__ __launch_bounds__(256) void prep_kernel(const T* __restrict__ q, cons
         fr[j] = __expf(lg[i][j] - gb[j]);  // e^{g_r - g_b} <= 1
         fc[j] = __expf(ge[j] - lg[i][j]);  // e^{g_e - g_r} <= 1
       }
-      const f32x4 kr = kv[i] * fr, qr = qv[i] * fr, kc = kv[i] * fc;
-      store4(reinterpret_cast<T*>(blk + B::oQ + toff<T, B::RB_R>(r, c4)), qr * ebv);
-      store4(reinterpret_cast<T*>(blk + B::oR + toff<T, B::RB_R>(r, c4)), bet[r] * (kr * ebv));
+      const f32x4 frd = fr * drv;  // e^{g_r - g_m}
+      const f32x4 fre = fr * ebv;  // e^{g_r}
+      store4(reinterpret_cast<T*>(Krd + loff<T, L::RBK>(r, c4)), kv[i] * frd);
+      store4(reinterpret_cast<T*>(Qrd + loff<T, L::RBK>(r, c4)), qv[i] * frd);
+      const f32x4 kc = kv[i] * fc;
+      store4(reinterpret_cast<T*>(Kc + loff<T, L::RBK>(r, c4)), kc);
+      store4(reinterpret_cast<T*>(blk + B::oQ + toff<T, B::RB_R>(r, c4)), qv[i] * fre);
+      store4(reinterpret_cast<T*>(blk + B::oR + toff<T, B::RB_R>(r, c4)), bet[r] * (kv[i] * fre));
       kb[i] = kc * eev;  // e^{g_last - g_r} k_r
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        lds_put<T>(Kr + r * L::KP + c4 + j, kr[j]);
-        lds_put<T>(Qr + r * L::KP + c4 + j, qr[j]);
-        lds_put<T>(Kc + r * L::KP + c4 + j, kc[j]);
-      }
     }
     // Kb^T tile (rows = key channel): this thread's rows are consecutive, so
     // groups of 4 stay contiguous under the column permutation.
@@ -471,101 +532,97 @@ __global__ __launch_bounds__(256) void prep_kernel(const T* __restrict__ q, cons
   __syncthreads();
 
   // ---- a3: gated k k^T (A, fp32 in LDS) and q k^T (P) via MFMA ------------
-  {
-    const int n = lane & 15, g = lane >> 4;
-    for (int bi = wave; bi < NB * NB; bi += 4) {
-      const int I = bi / NB, J = bi % NB;
-      f32x4 aA = {0.f, 0.f, 0.f, 0.f}, aP = {0.f, 0.f, 0.f, 0.f};
-      if (J <= I) {
-        const float* rs = (I == J) ? dr + I * DK : pr + (I * (I - 1) / 2 + J) * DK;
-        const T* krow = Kr + (16 * I + n) * L::KP;
-        const T* qrow = Qr + (16 * I + n) * L::KP;
-        const T* crow = Kc + (16 * J + n) * L::KP;
+  for (int pp = wave; pp < L::NLB; pp += kPrepThreads / 64) {
+    int I = 0;
+    while ((I + 1) * (I + 2) / 2 <= pp) ++I;
+    const int J = pp - I * (I + 1) / 2;
+    const float* f = fv + pp * DK;
+    f32x4 aA = {0.f, 0.f, 0.f, 0.f}, aP = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int k0 = 0; k0 < DK; k0 += M::KS) {
-          typename M::frag bf;
-          if (I == J) bf = frag_nat(crow, dc + I * DK, k0, g);
-          else bf = frag_nat(crow, k0, g);
-          aA = M::mma(frag_nat(krow, rs, k0, g), bf, aA);
-          aP = M::mma(frag_nat(qrow, rs, k0, g), bf, aP);
-        }
-      }
+    for (int k0 = 0; k0 < DK; k0 += M::KS) {
+      const typename M::frag bf = natf<T, L::RBK>::scaled(Kc, 16 * J + n, f, k0, g);
+      aA = M::mma(natf<T, L::RBK>::raw(Krd, 16 * I + n, k0, g), bf, aA);
+      aP = M::mma(natf<T, L::RBK>::raw(Qrd, 16 * I + n, k0, g), bf, aP);
+    }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rr = 4 * g + i;
-        const int row = 16 * I + rr, col = 16 * J + n;
-        float a = aA[i] * bet[row];
-        float p = aP[i];
-        if (J > I || (I == J && rr <= n)) a = 0.f;
-        if (J > I || (I == J && rr < n)) p = 0.f;
-        A[row * L::AP + col] = a;
-        lds_put<T>(Ps + row * L::CP + col, p);
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int rr = 4 * g + i;
+      const int row = 16 * I + rr, col = 16 * J + n;
+      float a = aA[i] * bet[row];
+      float pv = aP[i];
+      if (I == J && rr <= n) a = 0.f;
+      if (I == J && rr < n) pv = 0.f;
+      A[row * L::AP + col] = a;
+      lds_put<T>(Ps + row * L::CP + col, pv);
     }
   }
   __syncthreads();
-  for (int idx = tid; idx < C * C / 4; idx += 256) {
+  for (int idx = tid; idx < C * C / 4; idx += kPrepThreads) {
     const int r = idx / (C / 4), c4b = (idx % (C / 4)) * 4;
-    f32x4 x;
+    f32x4 x = {0.f, 0.f, 0.f, 0.f};
+    if ((c4b >> 4) <= (r >> 4)) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) x[j] = lds_get<T>(Ps + r * L::CP + c4b + j);
+      for (int j = 0; j < 4; ++j) x[j] = lds_get<T>(Ps + r * L::CP + c4b + j);
+    }
     store4(reinterpret_cast<T*>(blk + B::oP + toff<T, B::RB_K>(r, c4b)), x);
   }
 
-  // ---- a4: T = (I + A)^{-1} by blocked forward substitution --------------
-  // Diagonal 16x16 blocks: lane j of wave I solves column j.
-  for (int I = wave; I < NB; I += 4) {
-    if (lane < 16) {
-      const int j = lane;
-      float t[16];
+  // ---- a4: T = (I + A)^{-1} ----------------------------------------------
+  // Diagonal blocks: with M = -A_II (strictly lower, M^16 = 0),
+  //   (I + A_II)^{-1} = (I + M)(I + M^2)(I + M^4)(I + M^8),
+  // six 16x16x16 fp32 MFMA products per block.
+  for (int I = wave; I < NB; I += kPrepThreads / 64) {
+    float* s1 = scr + wave * 3 * 16 * L::SP;
+    float* s2 = s1 + 16 * L::SP;
+    float* s3 = s2 + 16 * L::SP;
+    const float* Aii = A + (16 * I) * L::AP + 16 * I;
+    f32x4 m1;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float acc = (r == j) ? 1.f : 0.f;
-        const float* arow = A + (16 * I + r) * L::AP + 16 * I;
+    for (int i = 0; i < 4; ++i) m1[i] = -Aii[(4 * g + i) * L::AP + n];
+    const f32x4 m2 = mm16_lds_acc(Aii, L::AP, m1, n, g, -1.f);
 #pragma unroll
-        for (int s2 = 0; s2 < r; ++s2) acc -= arow[s2] * t[s2];
-        t[r] = acc;
-      }
+    for (int i = 0; i < 4; ++i) s1[(4 * g + i) * L::SP + n] = m2[i];
+    const f32x4 m4 = mm16_lds_acc(s1, L::SP, m2, n, g);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) Ti[(16 * I + r) * L::AP + 16 * I + j] = t[r];
-    }
-  }
-  for (int idx = tid; idx < C * C; idx += 256) {
-    const int r = idx / C, cc = idx % C;
-    if ((cc >> 4) > (r >> 4)) Ti[r * L::AP + cc] = 0.f;
+    for (int i = 0; i < 4; ++i) s2[(4 * g + i) * L::SP + n] = m4[i];
+    const f32x4 m8 = mm16_lds_acc(s2, L::SP, m4, n, g);
+    const f32x4 m12 = mm16_lds_acc(Aii, L::AP, m2, n, g, -1.f);  // M * M^2
+    f32x4 pc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pc[i] = ((4 * g + i) == n ? 1.f : 0.f) + m1[i] + m2[i] + m12[i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s3[(4 * g + i) * L::SP + n] = pc[i];
+    pc += mm16_lds_acc(s3, L::SP, m4, n, g);  // (I + M)(I + M^2)(I + M^4)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s3[(4 * g + i) * L::SP + n] = pc[i];
+    pc += mm16_lds_acc(s3, L::SP, m8, n, g);  // ... (I + M^8)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Ti[(16 * I + 4 * g + i) * L::AP + 16 * I + n] = pc[i];
   }
   __syncthreads();
   // Off-diagonal blocks by distance d: T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ.
   for (int d = 1; d < NB; ++d) {
-    const int nblk = NB - d;
-    const int i = tid >> 4, jj = tid & 15;
-    for (int b = 0; b < nblk; ++b) {
-      const int J = b, I = b + d;
-      float x = 0.f;
+    for (int J = wave; J < NB - d; J += kPrepThreads / 64) {
+      const int I = J + d;
+      f32x4 x = {0.f, 0.f, 0.f, 0.f};
       for (int K = J; K < I; ++K) {
-        const float* arow = A + (16 * I + i) * L::AP + 16 * K;
-        const float* tcol = Ti + (16 * K) * L::AP + 16 * J + jj;
 #pragma unroll
-        for (int s2 = 0; s2 < 16; ++s2) x += arow[s2] * tcol[s2 * L::AP];
+        for (int s = 0; s < 4; ++s)
+          x = MF::mma(A[(16 * I + n) * L::AP + 16 * K + 4 * s + g], Ti[(16 * K + 4 * s + g) * L::AP + 16 * J + n], x);
       }
-      X[b * 256 + i * 16 + jj] = x;
-    }
-    __syncthreads();
-    for (int b = 0; b < nblk; ++b) {
-      const int J = b, I = b + d;
-      const float* trow = Ti + (16 * I + i) * L::AP + 16 * I;
-      float y = 0.f;
+      const f32x4 t = mm16_lds_acc(Ti + (16 * I) * L::AP + 16 * I, L::AP, x, n, g);
 #pragma unroll
-      for (int m = 0; m < 16; ++m) y += trow[m] * X[b * 256 + m * 16 + jj];
-      Ti[(16 * I + i) * L::AP + 16 * J + jj] = -y;
+      for (int i = 0; i < 4; ++i) Ti[(16 * I + 4 * g + i) * L::AP + 16 * J + n] = -t[i];
     }
     __syncthreads();
   }
-  for (int idx = tid; idx < C * C / 4; idx += 256) {
+  for (int idx = tid; idx < C * C / 4; idx += kPrepThreads) {
     const int r = idx / (C / 4), c4b = (idx % (C / 4)) * 4;
-    f32x4 x;
+    f32x4 x = {0.f, 0.f, 0.f, 0.f};
+    if ((c4b >> 4) <= (r >> 4)) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) x[j] = Ti[r * L::AP + c4b + j];
+      for (int j = 0; j < 4; ++j) x[j] = Ti[r * L::AP + c4b + j];
+    }
     store4(reinterpret_cast<T*>(blk + B::oT + toff<T, B::RB_K>(r, c4b)), x);
   }
 }
@@ -886,7 +943,7 @@ static hipError_t launch_prefill_t(const PrefillPlan& p, const void* q, const vo
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prep_kernel<T, C, DK>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lp));
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((prep_kernel<T, C, DK>), dim3(static_cast<unsigned>(p.max_chunks), p.H), dim3(256), lp, st,
+    hipLaunchKernelGGL((prep_kernel<T, C, DK>), dim3(p.H, static_cast<unsigned>(p.max_chunks)), dim3(kPrepThreads), lp, st,
                        static_cast<const T*>(q), static_cast<const T*>(k), la, beta, cu, chunk_off, p.N, p.H,
                        blocks);
     e = hipGetLastError();
