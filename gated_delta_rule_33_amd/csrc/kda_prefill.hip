@@ -668,7 +668,7 @@ struct RowFrags<float, RB, NS> {
 };
 
 // Loader waves per scan workgroup: they only stream the next chunk into LDS.
-constexpr int kLoaderWaves = 2;
+constexpr int kLoaderWaves = 4;
 
 template <typename T, int C, int DK, int TILE>
 struct ScanLds {
@@ -785,28 +785,43 @@ __global__ __launch_bounds__(64 * (WAVES + kLoaderWaves)) void scan_kernel(
 #pragma unroll
     for (int s = 0; s < NSK; ++s) sb[s] = AB::b(S, s);
 
-    // Y = b*V - R S, A fragments read one M-tile ahead
-    f32x4 Y[MT];
+    // Y = R S and O = Qh S together: 2 MT independent accumulator chains.
+    f32x4 Y[MT], O[MT];
     {
-      RowFrags<T, B::RB_R, NSK> cur, nxt;
-      cur.load(blk + B::oR, n, g);
+      RowFrags<T, B::RB_R, NSK> rc, qc, rn, qn;
+      rc.load(blk + B::oR, n, g);
+      qc.load(blk + B::oQ, n, g);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        if (mt + 1 < MT) nxt.load(blk + B::oR, 16 * (mt + 1) + n, g);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (mt + 1 < MT) {
+          rn.load(blk + B::oR, 16 * (mt + 1) + n, g);
+          qn.load(blk + B::oQ, 16 * (mt + 1) + n, g);
+        }
+        f32x4 ay = {0.f, 0.f, 0.f, 0.f}, ao = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < NSK; ++s) acc = M::mma(cur.f[s], sb[s], acc);
+        for (int s = 0; s < NSK; ++s) {
+          ay = M::mma(rc.f[s], sb[s], ay);
+          ao = M::mma(qc.f[s], sb[s], ao);
+        }
+        Y[mt] = ay;
+        O[mt] = ao;
+        if (mt + 1 < MT) {
+          rc = rn;
+          qc = qn;
+        }
+      }
+    }
+    // Y = b*V - R S; D = T Y with Y split into hi + lo (T unit lower triangular)
+    f32x4 D[MT];
+    {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
         const f32x4 bt = *reinterpret_cast<const f32x4*>(Bet + 16 * mt + 4 * g);
         f32x4 vv;
 #pragma unroll
         for (int i = 0; i < 4; ++i) vv[i] = io<T>::load(vt + (16 * mt + 4 * g + i) * TILE + wave * 16 + n);
-        Y[mt] = bt * vv - acc;
-        if (mt + 1 < MT) cur = nxt;
+        Y[mt] = bt * vv - Y[mt];
       }
-    }
-    // D = T Y with Y split into hi + lo (T unit lower triangular)
-    f32x4 D[MT];
-    {
       F yh[NSC], yl[NSC];
 #pragma unroll
       for (int s = 0; s < NSC; ++s) SP::hilo(Y, s, yh[s], yl[s]);
@@ -824,47 +839,48 @@ __global__ __launch_bounds__(64 * (WAVES + kLoaderWaves)) void scan_kernel(
         D[mt] = acc;
       }
     }
-    F dh[NSC], dl[NSC];
-#pragma unroll
-    for (int s = 0; s < NSC; ++s) SP::hilo(D, s, dh[s], dl[s]);
-    // O = Qh S + P D  (D split into hi + lo); stored as soon as it is formed
+    // O += P D (D split into hi + lo) and S = Diag(e^{g_last}) S + Kb^T D,
+    // issued together
     {
+      F dh[NSC], dl[NSC];
+#pragma unroll
+      for (int s = 0; s < NSC; ++s) SP::hilo(D, s, dh[s], dl[s]);
       RowFrags<T, B::RB_K, NSC> pf[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) pf[mt].load(blk + B::oP, 16 * mt + n, g);
-      RowFrags<T, B::RB_R, NSK> cur, nxt;
-      cur.load(blk + B::oQ, n, g);
+      RowFrags<T, B::RB_K, NSC> kf[ST];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        if (mt + 1 < MT) nxt.load(blk + B::oQ, 16 * (mt + 1) + n, g);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int st = 0; st < ST; ++st) kf[st].load(blk + B::oK, 16 * st + n, g);
 #pragma unroll
-        for (int s = 0; s < NSK; ++s) acc = M::mma(cur.f[s], sb[s], acc);
+      for (int st = 0; st < ST; ++st) S[st] *= *reinterpret_cast<const f32x4*>(Gam + 16 * st + 4 * g);
 #pragma unroll
-        for (int s = 0; s <= (16 * mt + 15) / AB::KS; ++s) {
-          acc = M::mma(pf[mt].f[s], dh[s], acc);
-          if (SP::has_lo) acc = M::mma(pf[mt].f[s], dl[s], acc);
+      for (int st = 0; st < ST; ++st) {
+        if (st < MT) {
+#pragma unroll
+          for (int s = 0; s <= (16 * st + 15) / AB::KS; ++s) {
+            O[st] = M::mma(pf[st].f[s], dh[s], O[st]);
+            if (SP::has_lo) O[st] = M::mma(pf[st].f[s], dl[s], O[st]);
+          }
         }
+#pragma unroll
+        for (int s = 0; s < NSC; ++s) S[st] = M::mma(kf[st].f[s], dh[s], S[st]);
+      }
+    }
+    // store O (branch-free for full chunks)
+    if (len == C) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          io<T>::store(o + (static_cast<size_t>(t0 + 16 * mt + 4 * g + i) * H + h) * DV + col, O[mt][i]);
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int row = 16 * mt + 4 * g + i;
-          if (row < len) io<T>::store(o + (static_cast<size_t>(t0 + row) * H + h) * DV + col, acc[i]);
+          if (row < len) io<T>::store(o + (static_cast<size_t>(t0 + row) * H + h) * DV + col, O[mt][i]);
         }
-        if (mt + 1 < MT) cur = nxt;
-      }
-    }
-    // S = Diag(e^{g_last}) S + Kb^T D
-    {
-      RowFrags<T, B::RB_K, NSC> cur, nxt;
-      cur.load(blk + B::oK, n, g);
-#pragma unroll
-      for (int st = 0; st < ST; ++st) {
-        if (st + 1 < ST) nxt.load(blk + B::oK, 16 * (st + 1) + n, g);
-        S[st] *= *reinterpret_cast<const f32x4*>(Gam + 16 * st + 4 * g);
-#pragma unroll
-        for (int s = 0; s < NSC; ++s) S[st] = M::mma(cur.f[s], dh[s], S[st]);
-        if (st + 1 < ST) cur = nxt;
-      }
     }
     __syncthreads();  // done with stage b; chunk cc+1 resident
     if (SL::NBUF == 1) __syncthreads();
