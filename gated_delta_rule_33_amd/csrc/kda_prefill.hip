@@ -323,10 +323,10 @@ struct PrepLds {
   static constexpr size_t szScr = static_cast<size_t>(NB) * 3 * 16 * SP * 4;  // NB waves x 3 tiles
   // region 0: Krd, Qrd, Kc (io, swizzled rows) -> later Ti + inverse scratch (f32)
   static constexpr size_t r0 = a16(mx(static_cast<size_t>(3) * C * RBK, szTi + szScr));
-  // region 1: A (f32)
-  static constexpr size_t r1 = a16(static_cast<size_t>(C) * AP * 4);
-  // region 2: gB gM gE [NB][DK] + partial sums [NRB][DK] (f32) -> later P staging (io)
-  static constexpr size_t r2 = a16(mx(static_cast<size_t>(3 * NB + NRB) * DK * 4, static_cast<size_t>(C) * CP * sizeof(T)));
+  // region 1: cumsum partials [NRB][DK] (f32) -> later A (f32)
+  static constexpr size_t r1 = a16(mx(static_cast<size_t>(C) * AP * 4, static_cast<size_t>(NRB) * DK * 4));
+  // region 2: gB gM gE [NB][DK] (f32) -> later P staging (io)
+  static constexpr size_t r2 = a16(mx(static_cast<size_t>(3 * NB) * DK * 4, static_cast<size_t>(C) * CP * sizeof(T)));
   // region 3: block-pair vectors f[NLB][DK] (f32)
   static constexpr size_t r3 = a16(static_cast<size_t>(NLB) * DK * 4);
   static constexpr size_t o0 = 0, o1 = r0, o2 = o1 + r1, o3 = o2 + r2, o4 = o3 + r3;
@@ -409,7 +409,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const T* __restrict_
   float* gB = reinterpret_cast<float*>(smem + L::o2);
   float* gM = gB + NB * DK;
   float* gE = gM + NB * DK;
-  float* part = gE + NB * DK;
+  float* part = reinterpret_cast<float*>(smem + L::o1);
   T* Ps = reinterpret_cast<T*>(smem + L::o2);
   float* fv = reinterpret_cast<float*>(smem + L::o3);
   float* bet = reinterpret_cast<float*>(smem + L::o4);
