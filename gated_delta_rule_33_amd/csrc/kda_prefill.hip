@@ -38,6 +38,11 @@
 // blocks use the block's 9th row as reference, so a factor can reach
 // e^{8 * max|log_alpha|}; the library requires log_alpha >= -10.
 
+#include <hip/hip_ext.h>
+
+#include <mutex>
+#include <vector>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -390,7 +395,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const T* __restrict_
                                                    const float* __restrict__ la, const float* __restrict__ beta,
                                                    const int32_t* __restrict__ cu,
                                                    const int32_t* __restrict__ chunk_off, int N, int H,
-                                                   unsigned char* __restrict__ ws) {
+                                                   unsigned char* __restrict__ ws, int cbase) {
   typedef PrepLds<T, C, DK> L;
   typedef Blk<T, C, DK> B;
   typedef mma16<T> M;
@@ -414,7 +419,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const T* __restrict_
   float* fv = reinterpret_cast<float*>(smem + L::o3);
   float* bet = reinterpret_cast<float*>(smem + L::o4);
 
-  const int h = blockIdx.x, c = blockIdx.y;
+  const int h = blockIdx.x, c = cbase + static_cast<int>(blockIdx.y);
   const int total = chunk_off[N];
   if (c >= total) return;
   int lo = 0, hi = N - 1;
@@ -684,7 +689,7 @@ template <typename T, int C, int DK, int DV, int WAVES>
 __global__ __launch_bounds__(64 * (WAVES + kLoaderWaves)) void scan_kernel(
     const T* __restrict__ v, const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_off,
     const int32_t* __restrict__ order, int N, int H, const unsigned char* __restrict__ ws, const float* S0,
-    T* __restrict__ o, float* S_T) {
+    T* __restrict__ o, float* S_T, int gbeg, int gend, float* carry) {
   typedef Blk<T, C, DK> B;
   typedef mma16<T> M;
   typedef accb<T> AB;
@@ -712,11 +717,21 @@ __global__ __launch_bounds__(64 * (WAVES + kLoaderWaves)) void scan_kernel(
   if (p >= N * H) return;
   const int seq = order[p / H];
   const int h = p % H;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps loops scalar
   const bool loader = wave >= WAVES;
   const int tbeg = cu[seq], L_seq = cu[seq + 1] - tbeg;
   const int c0 = chunk_off[seq];
   const int nch = (L_seq + C - 1) / C;
+  // This launch covers global chunk indices [gbeg, gend): local chunks
+  // [cb, ce) of this sequence.  The state enters from S0 at the sequence's
+  // first chunk, else from carry (left there by the launch before), and
+  // leaves to S_T after its last chunk, else to carry.  An empty sequence
+  // is handled by the launch that starts at global chunk 0.
+  const int cb = max(0, gbeg - c0), ce = min(nch, gend - c0);
+  if (nch == 0 ? gbeg != 0 : cb >= ce) return;
+  const float* s_in = cb == 0 ? S0 : carry;
+  float* s_out = ce == nch ? S_T : carry;
 
   // Loader waves: block of chunk cc and its v tile into stage b.
   auto issue = [&](int cc, int b) {
@@ -737,17 +752,17 @@ __global__ __launch_bounds__(64 * (WAVES + kLoaderWaves)) void scan_kernel(
   };
 
   if (loader) {
-    if (nch > 0) issue(0, 0);
+    if (cb < ce) issue(cb, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int cc = 0; cc < nch; ++cc) {
-      const int b = (SL::NBUF == 2) ? (cc & 1) : 0;
-      if (SL::NBUF == 2 && cc + 1 < nch) {
+    for (int cc = cb; cc < ce; ++cc) {
+      const int b = (SL::NBUF == 2) ? ((cc - cb) & 1) : 0;
+      if (SL::NBUF == 2 && cc + 1 < ce) {
         issue(cc + 1, b ^ 1);
         __builtin_amdgcn_s_waitcnt(0);
       }
       __syncthreads();  // chunk cc consumed; chunk cc+1 resident
-      if (SL::NBUF == 1 && cc + 1 < nch) {
+      if (SL::NBUF == 1 && cc + 1 < ce) {
         issue(cc + 1, 0);
         __builtin_amdgcn_s_waitcnt(0);
       }
@@ -761,19 +776,19 @@ __global__ __launch_bounds__(64 * (WAVES + kLoaderWaves)) void scan_kernel(
   const int col = tile * TILE + wave * 16 + n;
   f32x4 S[ST];
   const size_t sbase = (static_cast<size_t>(seq) * H + h) * DK * DV;
-  if (S0) {
+  if (s_in) {
 #pragma unroll
     for (int st = 0; st < ST; ++st)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) S[st][i] = S0[sbase + static_cast<size_t>(16 * st + 4 * g + i) * DV + col];
+      for (int i = 0; i < 4; ++i) S[st][i] = s_in[sbase + static_cast<size_t>(16 * st + 4 * g + i) * DV + col];
   } else {
 #pragma unroll
     for (int st = 0; st < ST; ++st) S[st] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   __syncthreads();  // chunk 0 resident
 
-  for (int cc = 0; cc < nch; ++cc) {
-    const int b = (SL::NBUF == 2) ? (cc & 1) : 0;
+  for (int cc = cb; cc < ce; ++cc) {
+    const int b = (SL::NBUF == 2) ? ((cc - cb) & 1) : 0;
     const unsigned char* blk = smem + b * SL::stage;
     const T* vt = reinterpret_cast<const T*>(blk + B::bytes);
     const float* Gam = reinterpret_cast<const float*>(blk + B::oG);
@@ -866,30 +881,32 @@ __global__ __launch_bounds__(64 * (WAVES + kLoaderWaves)) void scan_kernel(
         for (int s = 0; s < NSC; ++s) S[st] = M::mma(kf[st].f[s], dh[s], S[st]);
       }
     }
-    // store O (branch-free for full chunks)
-    if (len == C) {
+    // store O: a wave-uniform row base plus a per-lane 32-bit offset
+    {
+      const int lane_off = 4 * g * H * DV + col;
+      if (len == C) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          io<T>::store(o + (static_cast<size_t>(t0 + 16 * mt + 4 * g + i) * H + h) * DV + col, O[mt][i]);
-    } else {
+          for (int i = 0; i < 4; ++i)
+            io<T>::store(o + (static_cast<size_t>(t0 + 16 * mt + i) * H + h) * DV + lane_off, O[mt][i]);
+      } else {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = 16 * mt + 4 * g + i;
-          if (row < len) io<T>::store(o + (static_cast<size_t>(t0 + row) * H + h) * DV + col, O[mt][i]);
-        }
+          for (int i = 0; i < 4; ++i)
+            if (16 * mt + 4 * g + i < len)
+              io<T>::store(o + (static_cast<size_t>(t0 + 16 * mt + i) * H + h) * DV + lane_off, O[mt][i]);
+      }
     }
     __syncthreads();  // done with stage b; chunk cc+1 resident
     if (SL::NBUF == 1) __syncthreads();
   }
-  if (S_T) {
+  if (s_out) {
 #pragma unroll
     for (int st = 0; st < ST; ++st)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) S_T[sbase + static_cast<size_t>(16 * st + 4 * g + i) * DV + col] = S[st][i];
+      for (int i = 0; i < 4; ++i) s_out[sbase + static_cast<size_t>(16 * st + 4 * g + i) * DV + col] = S[st][i];
   }
 }
 
@@ -897,6 +914,16 @@ __global__ __launch_bounds__(64 * (WAVES + kLoaderWaves)) void scan_kernel(
 // Host side: plan and launch.
 // ---------------------------------------------------------------------------
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Scan workgroups of the narrow (32-column) configuration.
+static int64_t narrow_scan_wgs(int64_t N, int64_t H, int dv) { return (N * H + 7) / 8 * 8 * (dv / 32); }
+
+// Overlapped schedule: when the scan has at most this many workgroups (one per
+// CU) it runs on half of the CUs while the prep of the next segment runs on
+// the other half.
+constexpr int64_t kPipeMaxScanWgs = 128;
+constexpr int64_t kPipeMinSeg = 64;    // chunks per segment, at least
+constexpr int64_t kPipeMaxSegs = 16;   // segments, at most
 
 static size_t block_bytes(kda_dtype dt, int C, int dk) {
   const size_t es = dt == KDA_BF16 ? 2 : 4;
@@ -920,6 +947,15 @@ bool make_prefill_plan(const kda_prefill_desc* d, int64_t max_chunks, PrefillPla
   p->off_order = off;     off = align256(off + 4 * (static_cast<size_t>(d->num_seqs) + 1));
   off = (off + 1023) / 1024 * 1024;
   p->off_blocks = off;    off += slots * block_bytes(d->io_dtype, d->chunk, d->dk);
+  off = align256(off);
+  p->seg = 0;
+  p->off_carry = 0;
+  if (narrow_scan_wgs(d->num_seqs, d->num_heads, d->dv) <= kPipeMaxScanWgs && max_chunks >= 2 * kPipeMinSeg) {
+    const int64_t seg = (max_chunks + kPipeMaxSegs - 1) / kPipeMaxSegs;
+    p->seg = seg > kPipeMinSeg ? seg : kPipeMinSeg;
+    p->off_carry = off;
+    off += static_cast<size_t>(d->num_seqs) * d->num_heads * d->dk * d->dv * 4;
+  }
   p->total_bytes = align256(off);
   return true;
 }
@@ -927,7 +963,8 @@ bool make_prefill_plan(const kda_prefill_desc* d, int64_t max_chunks, PrefillPla
 template <typename T, int C, int DK, int DV, int WAVES>
 static hipError_t launch_scan(const PrefillPlan& p, const void* v, const int32_t* cu, const int32_t* chunk_off,
                               const int32_t* order, const unsigned char* blocks, const float* S0, void* o,
-                              float* S_T, hipStream_t st) {
+                              float* S_T, hipStream_t st, int gbeg = 0, int gend = 0x7fffffff,
+                              float* carry = nullptr) {
   typedef ScanLds<T, C, DK, 16 * WAVES> SL;
   static_assert(SL::total <= 160 * 1024, "scan LDS");
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_kernel<T, C, DK, DV, WAVES>),
@@ -937,8 +974,65 @@ static hipError_t launch_scan(const PrefillPlan& p, const void* v, const int32_t
   const int nsplit = DV / (16 * WAVES);
   const unsigned grid = static_cast<unsigned>((pairs + 7) / 8 * 8 * nsplit);
   hipLaunchKernelGGL((scan_kernel<T, C, DK, DV, WAVES>), dim3(grid), dim3(64 * (WAVES + kLoaderWaves)), SL::total, st,
-                     static_cast<const T*>(v), cu, chunk_off, order, p.N, p.H, blocks, S0, static_cast<T*>(o), S_T);
+                     static_cast<const T*>(v), cu, chunk_off, order, p.N, p.H, blocks, S0, static_cast<T*>(o), S_T,
+                     gbeg, gend, carry);
   return hipGetLastError();
+}
+
+// Per-device pair of CU-masked streams (default priority) and the events of
+// the overlapped schedule; created on first use and kept for the process.
+struct PipeStreams {
+  hipStream_t prep = nullptr, scan = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr, ready[kPipeMaxSegs] = {};
+  int scan_cus = 0;
+  std::mutex mu;  // one schedule at a time may use the shared streams/events
+};
+
+// Returns in *out the current device's streams when the scan (scan_wgs
+// workgroups) fits on its half of the CUs, else nullptr.
+static hipError_t pipe_streams(int64_t scan_wgs, PipeStreams** out) {
+  constexpr int kMaxDev = 64;
+  static std::mutex mu;
+  static PipeStreams* cache[kMaxDev] = {};
+  static bool unavailable[kMaxDev] = {};
+  *out = nullptr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDev) return hipSuccess;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!cache[dev] && !unavailable[dev]) {
+    hipDeviceProp_t prop;
+    if ((e = hipGetDeviceProperties(&prop, dev)) != hipSuccess) return e;
+    const int cus = prop.multiProcessorCount, words = (cus + 31) / 32;
+    // Runs of 8 consecutive mask bits alternate between the two streams.  The
+    // runtime deals mask bit i to XCD i mod 8, so each stream gets half of the
+    // CUs of every XCD and the scan keeps its XCD-aware placement.
+    std::vector<uint32_t> ms(words, 0u), mp(words, 0u);
+    int ns = 0, np = 0;
+    for (int i = 0; i < cus; ++i) {
+      std::vector<uint32_t>& m = ((i >> 3) & 1) ? mp : ms;
+      m[i >> 5] |= 1u << (i & 31);
+      ++(((i >> 3) & 1) ? np : ns);
+    }
+    PipeStreams* ps = new PipeStreams;
+    bool ok = ns >= 8 && np >= 8 &&
+              hipExtStreamCreateWithCUMask(&ps->scan, words, ms.data()) == hipSuccess &&
+              hipExtStreamCreateWithCUMask(&ps->prep, words, mp.data()) == hipSuccess &&
+              hipEventCreateWithFlags(&ps->fork, hipEventDisableTiming) == hipSuccess &&
+              hipEventCreateWithFlags(&ps->join, hipEventDisableTiming) == hipSuccess;
+    for (int j = 0; ok && j < kPipeMaxSegs; ++j)
+      ok = hipEventCreateWithFlags(&ps->ready[j], hipEventDisableTiming) == hipSuccess;
+    if (ok) {
+      ps->scan_cus = ns;
+      cache[dev] = ps;
+    } else {  // no CU masks here: fall back to the single-stream schedule
+      (void)hipGetLastError();
+      unavailable[dev] = true;
+    }
+  }
+  if (cache[dev] && scan_wgs <= cache[dev]->scan_cus) *out = cache[dev];
+  return hipSuccess;
 }
 
 template <typename T, int C, int DK, int DV>
@@ -953,16 +1047,51 @@ static hipError_t launch_prefill_t(const PrefillPlan& p, const void* q, const vo
   hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(1024), 0, st, cu, p.N, C, chunk_off, order, p.sort);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (p.max_chunks > 0) {
-    const size_t lp = PrepLds<T, C, DK>::total;
-    static_assert(PrepLds<T, C, DK>::total <= 160 * 1024, "prep LDS");
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prep_kernel<T, C, DK>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lp));
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((prep_kernel<T, C, DK>), dim3(p.H, static_cast<unsigned>(p.max_chunks)), dim3(kPrepThreads), lp, st,
+  const size_t lp = PrepLds<T, C, DK>::total;
+  static_assert(PrepLds<T, C, DK>::total <= 160 * 1024, "prep LDS");
+  auto prep = [&](int64_t cbase, int64_t count, hipStream_t s) -> hipError_t {
+    hipError_t r = hipFuncSetAttribute(reinterpret_cast<const void*>(&prep_kernel<T, C, DK>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lp));
+    if (r != hipSuccess) return r;
+    hipLaunchKernelGGL((prep_kernel<T, C, DK>), dim3(p.H, static_cast<unsigned>(count)), dim3(kPrepThreads), lp, s,
                        static_cast<const T*>(q), static_cast<const T*>(k), la, beta, cu, chunk_off, p.N, p.H,
-                       blocks);
-    e = hipGetLastError();
+                       blocks, static_cast<int>(cbase));
+    return hipGetLastError();
+  };
+  // Overlapped schedule: segment j's scan (half of the CUs) runs beside
+  // segment j+1's prep (the other half), forked from and joined back into
+  // the caller's stream.  The first segment's prep has the whole device.
+  PipeStreams* ps = nullptr;
+  if (p.seg > 0) {
+    e = pipe_streams(narrow_scan_wgs(p.N, p.H, DV), &ps);
+    if (e != hipSuccess) return e;
+  }
+  if (ps) {
+    float* carry = S_T ? S_T : reinterpret_cast<float*>(w + p.off_carry);
+    const int64_t nseg = (p.max_chunks + p.seg - 1) / p.seg;
+    std::lock_guard<std::mutex> lock(ps->mu);
+    e = prep(0, p.seg < p.max_chunks ? p.seg : p.max_chunks, st);
+    if (e != hipSuccess) return e;
+    if ((e = hipEventRecord(ps->fork, st)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(ps->prep, ps->fork, 0)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(ps->scan, ps->fork, 0)) != hipSuccess) return e;
+    for (int64_t j = 0; j < nseg; ++j) {
+      const int64_t c0 = j * p.seg, c1 = c0 + p.seg < p.max_chunks ? c0 + p.seg : p.max_chunks;
+      if (j > 0) {
+        if ((e = prep(c0, c1 - c0, ps->prep)) != hipSuccess) return e;
+        if ((e = hipEventRecord(ps->ready[j], ps->prep)) != hipSuccess) return e;
+        if ((e = hipStreamWaitEvent(ps->scan, ps->ready[j], 0)) != hipSuccess) return e;
+      }
+      e = launch_scan<T, C, DK, DV, 2>(p, v, cu, chunk_off, order, blocks, S0, o, S_T, ps->scan,
+                                       static_cast<int>(c0), j + 1 == nseg ? 0x7fffffff : static_cast<int>(c1),
+                                       carry);
+      if (e != hipSuccess) return e;
+    }
+    if ((e = hipEventRecord(ps->join, ps->scan)) != hipSuccess) return e;
+    return hipStreamWaitEvent(st, ps->join, 0);
+  }
+  if (p.max_chunks > 0) {
+    e = prep(0, p.max_chunks, st);
     if (e != hipSuccess) return e;
   }
   // Few (sequence, head) pairs: narrower value tiles to put more CUs on the
