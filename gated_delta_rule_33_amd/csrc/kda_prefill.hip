@@ -279,14 +279,19 @@ struct split;
 template <>
 struct split<bf16_t> {
   static constexpr bool has_lo = true;
+  // hi = x with the low 16 bits cleared (a bf16 by truncation), lo = x - hi
+  // (exact in fp32) rounded to bf16: hi + lo = x to ~2^-16 relative.
   __device__ __forceinline__ static void hilo(const f32x4* tiles, int s, bf16x8& hi, bf16x8& lo) {
+    uint32_t h[4], l[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float x = tiles[2 * s + (j >> 2)][j & 3];
-      const __bf16 h = to_bf(x);
-      hi[j] = h;
-      lo[j] = to_bf(x - from_bf(h));
+    for (int j = 0; j < 8; j += 2) {
+      const float x0 = tiles[2 * s + (j >> 2)][j & 3], x1 = tiles[2 * s + (j >> 2)][(j & 3) + 1];
+      const uint32_t u0 = __float_as_uint(x0), u1 = __float_as_uint(x1);
+      h[j >> 1] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);  // upper halves of x0 | x1
+      l[j >> 1] = f32x2_to_bf16x2(x0 - __uint_as_float(u0 & 0xFFFF0000u), x1 - __uint_as_float(u1 & 0xFFFF0000u));
     }
+    hi = __builtin_bit_cast(bf16x8, uint4{h[0], h[1], h[2], h[3]});
+    lo = __builtin_bit_cast(bf16x8, uint4{l[0], l[1], l[2], l[3]});
   }
 };
 template <>
@@ -646,6 +651,14 @@ __device__ __forceinline__ void lds_load16(const unsigned char* src, unsigned ch
                                    (__attribute__((address_space(3))) void*)(dst_wave_base), 16, 0, 0);
 }
 
+// s_waitcnt for at most N outstanding vector-memory loads (lgkmcnt, expcnt
+// left unconstrained)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // The first NS k-step A fragments of one stored-tile row (accumulator k map).
 template <typename T, int RB, int NS>
 struct RowFrags;
@@ -672,9 +685,23 @@ struct RowFrags<float, RB, NS> {
   }
 };
 
-// Loader waves per scan workgroup: they only stream the next chunk into LDS.
+// Loader waves per scan workgroup: they only stream chunk blocks into LDS.
 constexpr int kLoaderWaves = 4;
 
+// Workgroup barrier that waits only for this wave's LDS traffic (lgkmcnt 0),
+// not for its global loads and stores, which may stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt 63, expcnt 7, lgkmcnt 0
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Scan LDS.  Double-buffered (NBUF = 2) when two chunks fit: the block is
+// split into an early part (R, Qh: read by the first products only) and a
+// late part (Kb^T, P, T, Gamma, beta, then the v tile), each with two slots,
+// so the early part of chunk cc + 2 can stream in from the middle of chunk cc.
+// Otherwise one slot holds the whole block and v tile.
 template <typename T, int C, int DK, int TILE>
 struct ScanLds {
   typedef Blk<T, C, DK> B;
@@ -682,6 +709,9 @@ struct ScanLds {
   static constexpr size_t vbytes = (vtile + 1023) / 1024 * 1024;
   static constexpr size_t stage = B::bytes + vbytes;
   static constexpr int NBUF = (2 * stage <= 160 * 1024) ? 2 : 1;
+  static constexpr size_t early = B::oK;                          // R, Qh
+  static constexpr size_t late = B::bytes - B::oK + vbytes;       // Kb^T, P, T, Gamma, beta, v
+  static constexpr size_t late0 = NBUF == 2 ? 2 * early : early;  // first late slot
   static constexpr size_t total = NBUF * stage;
 };
 
@@ -733,40 +763,98 @@ __global__ __launch_bounds__(64 * (WAVES + kLoaderWaves)) void scan_kernel(
   const float* s_in = cb == 0 ? S0 : carry;
   float* s_out = ce == nch ? S_T : carry;
 
-  // Loader waves: block of chunk cc and its v tile into stage b.
-  auto issue = [&](int cc, int b) {
+  // Single-slot scheme (NBUF = 1): the whole block of chunk cc and its v
+  // tile, one chunk ahead.
+  auto issue = [&](int cc) {
     const int lw = wave - WAVES;
     const unsigned char* src = ws + (static_cast<size_t>(c0 + cc) * H + h) * B::bytes;
-    unsigned char* dst = smem + b * SL::stage;
-    for (int j = lw; j < NG; j += kLoaderWaves) lds_load16(src + j * 1024 + lane * 16, dst + j * 1024);
+    for (int j = lw; j < NG; j += kLoaderWaves) lds_load16(src + j * 1024 + lane * 16, smem + j * 1024);
     const int t0 = tbeg + cc * C, len = min(C, L_seq - cc * C);
-    unsigned char* vdst = dst + B::bytes;
     for (int j = lw; j < NVG; j += kLoaderWaves) {
       const int r = j * VRPL + lane / VLPR;
       const int rr = r < len ? r : len - 1;  // rows past the end are masked by beta = 0
       const unsigned char* vsrc = reinterpret_cast<const unsigned char*>(
                                       v + (static_cast<size_t>(t0 + rr) * H + h) * DV + tile * TILE) +
                                   (lane % VLPR) * 16;
-      lds_load16(vsrc, vdst + j * 1024);
+      lds_load16(vsrc, smem + B::bytes + j * 1024);
     }
   };
 
   if (loader) {
-    if (cb < ce) issue(cb, 0);
+    if constexpr (SL::NBUF == 2) {
+      // Early part of chunk x: issued once chunk x - 2 has passed its first
+      // products (barrier M(x - 2)), needed at the end of chunk x - 1.  Late
+      // part of chunk x: issued at the end of chunk x - 2, needed at M(x).
+      // Every loader wave moves the same number of granules (the tail
+      // granule with Gamma, beta and v granules may be moved twice, with
+      // identical bytes), so one vmcnt bound serves every wait; chunks past
+      // the end re-load the last chunk into an idle slot.
+      constexpr int EG = static_cast<int>(B::oK / 1024);          // early granules
+      constexpr int LG = static_cast<int>((B::oG - B::oK) / 1024);  // late granules before the tail
+      static_assert(B::oK % 1024 == 0 && B::oG % 1024 == 0 && EG % kLoaderWaves == 0 && LG % kLoaderWaves == 0 &&
+                        B::bytes - B::oG == 1024,
+                    "block granules");
+      constexpr int NVW = (NVG + kLoaderWaves - 1) / kLoaderWaves;
+      constexpr int NE = EG / kLoaderWaves, NLT = LG / kLoaderWaves + 1 + NVW;
+      const int lw = wave - WAVES;
+      if (cb >= ce) {  // empty sequence: the compute waves only pass the first barrier
+        lds_barrier();
+        return;
+      }
+      auto blk_src = [&](int cc) {
+        return ws + (static_cast<size_t>(c0 + min(cc, ce - 1)) * H + h) * B::bytes + lane * 16;
+      };
+      auto early = [&](int cc, int slot) {
+        const unsigned char* src = blk_src(cc);
+        unsigned char* dst = smem + slot * SL::early;
+#pragma unroll
+        for (int m = 0; m < NE; ++m) lds_load16(src + (lw + kLoaderWaves * m) * 1024, dst + (lw + kLoaderWaves * m) * 1024);
+      };
+      auto late = [&](int cc, int slot) {
+        const unsigned char* src = blk_src(cc) + B::oK;
+        unsigned char* dst = smem + SL::late0 + slot * SL::late;
+#pragma unroll
+        for (int m = 0; m < LG / kLoaderWaves; ++m)
+          lds_load16(src + (lw + kLoaderWaves * m) * 1024, dst + (lw + kLoaderWaves * m) * 1024);
+        lds_load16(src + (B::oG - B::oK), dst + (B::oG - B::oK));
+        cc = min(cc, ce - 1);
+        const int t0 = tbeg + cc * C, len = min(C, L_seq - cc * C);
+#pragma unroll
+        for (int m = 0; m < NVW; ++m) {
+          const int j = (lw + kLoaderWaves * m) % NVG;
+          const int rr = min(j * VRPL + lane / VLPR, len - 1);  // rows past the end are masked by beta = 0
+          lds_load16(reinterpret_cast<const unsigned char*>(
+                         v + (static_cast<size_t>(t0 + rr) * H + h) * DV + tile * TILE) +
+                         (lane % VLPR) * 16,
+                     dst + (B::bytes - B::oK) + j * 1024);
+        }
+      };
+      early(cb, 0);
+      late(cb, 0);
+      early(cb + 1, 1);
+      wait_vm<NE + NLT>();  // early part of chunk cb
+      lds_barrier();
+      for (int cc = cb; cc < ce; ++cc) {
+        const int b = (cc - cb) & 1;
+        late(cc + 1, b ^ 1);
+        wait_vm<NE + NLT>();  // late part of chunk cc
+        lds_barrier();        // M(cc): early slot b free, late part of cc resident
+        early(cc + 2, b);
+        wait_vm<NE + NLT>();  // early part of chunk cc + 1
+        lds_barrier();        // end of chunk cc
+      }
+      return;
+    }
+    if (cb < ce) issue(cb);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int cc = cb; cc < ce; ++cc) {
-      const int b = (SL::NBUF == 2) ? ((cc - cb) & 1) : 0;
-      if (SL::NBUF == 2 && cc + 1 < ce) {
-        issue(cc + 1, b ^ 1);
+      __syncthreads();  // chunk cc consumed
+      if (cc + 1 < ce) {
+        issue(cc + 1);
         __builtin_amdgcn_s_waitcnt(0);
       }
-      __syncthreads();  // chunk cc consumed; chunk cc+1 resident
-      if (SL::NBUF == 1 && cc + 1 < ce) {
-        issue(cc + 1, 0);
-        __builtin_amdgcn_s_waitcnt(0);
-      }
-      if (SL::NBUF == 1) __syncthreads();
+      __syncthreads();  // chunk cc + 1 resident
     }
     return;
   }
@@ -785,14 +873,26 @@ __global__ __launch_bounds__(64 * (WAVES + kLoaderWaves)) void scan_kernel(
 #pragma unroll
     for (int st = 0; st < ST; ++st) S[st] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  __syncthreads();  // chunk 0 resident
+  // byte offset of output element (chunk row 16 mt + 4 g + i, column col)
+  // from the chunk's first row; the host keeps C H DV sizeof(T) below 2^31
+  uint32_t ooff[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      ooff[mt][i] = static_cast<uint32_t>(((16 * mt + 4 * g + i) * H * DV + col) * static_cast<int>(sizeof(T)));
+  if constexpr (SL::NBUF == 2) lds_barrier(); else __syncthreads();  // first chunk resident
 
   for (int cc = cb; cc < ce; ++cc) {
     const int b = (SL::NBUF == 2) ? ((cc - cb) & 1) : 0;
-    const unsigned char* blk = smem + b * SL::stage;
-    const T* vt = reinterpret_cast<const T*>(blk + B::bytes);
-    const float* Gam = reinterpret_cast<const float*>(blk + B::oG);
-    const float* Bet = reinterpret_cast<const float*>(blk + B::oB);
+    // early part (R, Qh) and late part (from Kb^T on, then the v tile);
+    // lat(off) addresses block offset off >= oK in the late slot
+    const unsigned char* eblk = smem + b * SL::early;
+    const unsigned char* lblk = smem + SL::late0 + b * SL::late;
+    auto lat = [&](size_t off) { return lblk + (off - B::oK); };
+    const T* vt = reinterpret_cast<const T*>(lat(B::bytes));
+    const float* Gam = reinterpret_cast<const float*>(lat(B::oG));
+    const float* Bet = reinterpret_cast<const float*>(lat(B::oB));
     const int t0 = tbeg + cc * C, len = min(C, L_seq - cc * C);
 
     // B fragments of the state (shared by R S and Qh S)
@@ -804,13 +904,13 @@ __global__ __launch_bounds__(64 * (WAVES + kLoaderWaves)) void scan_kernel(
     f32x4 Y[MT], O[MT];
     {
       RowFrags<T, B::RB_R, NSK> rc, qc, rn, qn;
-      rc.load(blk + B::oR, n, g);
-      qc.load(blk + B::oQ, n, g);
+      rc.load(eblk + B::oR, n, g);
+      qc.load(eblk + B::oQ, n, g);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         if (mt + 1 < MT) {
-          rn.load(blk + B::oR, 16 * (mt + 1) + n, g);
-          qn.load(blk + B::oQ, 16 * (mt + 1) + n, g);
+          rn.load(eblk + B::oR, 16 * (mt + 1) + n, g);
+          qn.load(eblk + B::oQ, 16 * (mt + 1) + n, g);
         }
         f32x4 ay = {0.f, 0.f, 0.f, 0.f}, ao = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -826,6 +926,9 @@ __global__ __launch_bounds__(64 * (WAVES + kLoaderWaves)) void scan_kernel(
         }
       }
     }
+    // barrier M: every wave is done with the early slot; the late part of
+    // this chunk is resident
+    if constexpr (SL::NBUF == 2) lds_barrier();
     // Y = b*V - R S; D = T Y with Y split into hi + lo (T unit lower triangular)
     f32x4 D[MT];
     {
@@ -842,7 +945,7 @@ __global__ __launch_bounds__(64 * (WAVES + kLoaderWaves)) void scan_kernel(
       for (int s = 0; s < NSC; ++s) SP::hilo(Y, s, yh[s], yl[s]);
       RowFrags<T, B::RB_K, NSC> tf[MT];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) tf[mt].load(blk + B::oT, 16 * mt + n, g);
+      for (int mt = 0; mt < MT; ++mt) tf[mt].load(lat(B::oT), 16 * mt + n, g);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -862,10 +965,10 @@ __global__ __launch_bounds__(64 * (WAVES + kLoaderWaves)) void scan_kernel(
       for (int s = 0; s < NSC; ++s) SP::hilo(D, s, dh[s], dl[s]);
       RowFrags<T, B::RB_K, NSC> pf[MT];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) pf[mt].load(blk + B::oP, 16 * mt + n, g);
+      for (int mt = 0; mt < MT; ++mt) pf[mt].load(lat(B::oP), 16 * mt + n, g);
       RowFrags<T, B::RB_K, NSC> kf[ST];
 #pragma unroll
-      for (int st = 0; st < ST; ++st) kf[st].load(blk + B::oK, 16 * st + n, g);
+      for (int st = 0; st < ST; ++st) kf[st].load(lat(B::oK), 16 * st + n, g);
 #pragma unroll
       for (int st = 0; st < ST; ++st) S[st] *= *reinterpret_cast<const f32x4*>(Gam + 16 * st + 4 * g);
 #pragma unroll
@@ -881,26 +984,28 @@ __global__ __launch_bounds__(64 * (WAVES + kLoaderWaves)) void scan_kernel(
         for (int s = 0; s < NSC; ++s) S[st] = M::mma(kf[st].f[s], dh[s], S[st]);
       }
     }
-    // store O: a wave-uniform row base plus a per-lane 32-bit offset
+    // store O: wave-uniform chunk base plus the per-lane byte offsets
     {
-      const int lane_off = 4 * g * H * DV + col;
+      unsigned char* ob = reinterpret_cast<unsigned char*>(o + (static_cast<size_t>(t0) * H + h) * DV);
       if (len == C) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            io<T>::store(o + (static_cast<size_t>(t0 + 16 * mt + i) * H + h) * DV + lane_off, O[mt][i]);
+          for (int i = 0; i < 4; ++i) io<T>::store(reinterpret_cast<T*>(ob + ooff[mt][i]), O[mt][i]);
       } else {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (16 * mt + 4 * g + i < len)
-              io<T>::store(o + (static_cast<size_t>(t0 + 16 * mt + i) * H + h) * DV + lane_off, O[mt][i]);
+            if (16 * mt + 4 * g + i < len) io<T>::store(reinterpret_cast<T*>(ob + ooff[mt][i]), O[mt][i]);
       }
     }
-    __syncthreads();  // done with stage b; chunk cc+1 resident
-    if (SL::NBUF == 1) __syncthreads();
+    if constexpr (SL::NBUF == 2) {
+      lds_barrier();  // end of chunk: late slot b free; early part of cc + 1 resident
+    } else {
+      __syncthreads();  // chunk consumed
+      __syncthreads();  // next chunk resident
+    }
   }
   if (s_out) {
 #pragma unroll
