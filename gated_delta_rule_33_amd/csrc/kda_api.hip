@@ -32,8 +32,9 @@ kda_status check_desc(const kda_prefill_desc* d, int64_t* max_chunks) {
   if (d->chunk != 32 && d->chunk != 64) return KDA_ERR_UNSUPPORTED;
   if (d->num_seqs == 0 && d->total_tokens != 0) return KDA_ERR_INVALID_ARGUMENT;
   const int64_t C = d->chunk;
-  // one chunk of output rows must span fewer than 2^31 bytes (32-bit offsets)
-  if (C * d->num_heads * d->dv * 4 >= (int64_t(1) << 31)) return KDA_ERR_UNSUPPORTED;
+  // one chunk of rows of any per-token tensor must span fewer than 2^31
+  // bytes (the kernels use 32-bit offsets within a chunk)
+  if (C * d->num_heads * (d->dk > d->dv ? d->dk : d->dv) * 4 >= (int64_t(1) << 31)) return KDA_ERR_UNSUPPORTED;
   if (d->cu_seqlens_host) {
     const int32_t* cu = d->cu_seqlens_host;
     if (cu[0] != 0) return KDA_ERR_INVALID_ARGUMENT;

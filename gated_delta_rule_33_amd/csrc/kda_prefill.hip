@@ -442,21 +442,20 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const T* __restrict_
   // ---- loads: thread owns channels c4..c4+3 of rows r0..r0+RPT-1 ---------
   const int cg = tid % NCG, rbk = tid / NCG;
   const int c4 = 4 * cg, r0 = rbk * RPT;
+  // Rows past the end re-read the last row (all loads issue back to back);
+  // their log_alpha is zeroed and beta = 0 masks them everywhere else.
+  const size_t tbase = (static_cast<size_t>(t0) * H + h) * DK;
   f32x4 lg[RPT], kv[RPT], qv[RPT];
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
-    const int r = r0 + i;
-    if (r < len) {
-      const size_t e = (static_cast<size_t>(t0 + r) * H + h) * DK + c4;
-      lg[i] = *reinterpret_cast<const f32x4*>(la + e);
-      kv[i] = load4(k + e);
-      qv[i] = load4(q + e);
-    } else {
-      lg[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-      kv[i] = lg[i];
-      qv[i] = lg[i];
-    }
+    const int e = min(r0 + i, len - 1) * H * DK + c4;  // < C H DK: 32-bit
+    lg[i] = *reinterpret_cast<const f32x4*>(la + tbase + e);
+    kv[i] = load4(k + tbase + e);
+    qv[i] = load4(q + tbase + e);
   }
+#pragma unroll
+  for (int i = 0; i < RPT; ++i)
+    if (r0 + i >= len) lg[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (tid < C) bet[tid] = tid < len ? beta[static_cast<size_t>(t0 + tid) * H + h] : 0.f;
 
   // ---- a2: chunk-local inclusive cumsum of log_alpha ----------------------
@@ -688,6 +687,48 @@ struct RowFrags<float, RB, NS> {
 // Loader waves per scan workgroup: they only stream chunk blocks into LDS.
 constexpr int kLoaderWaves = 4;
 
+// 4x4 transpose inside each quad of lanes: lane j of the quad holds x[i] =
+// element (row i, column j) on entry and (row j, column i) on exit.  Two
+// rounds of quad_perm swaps (partner lane j ^ 1, then j ^ 2).
+template <int D>
+__device__ __forceinline__ float quad_swap(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), D == 1 ? 0xB1 : 0x4E, 0xF, 0xF, true));
+}
+template <int D>
+__device__ __forceinline__ void quad_round(f32x4& x, bool up, int a, int b) {
+  const float r = quad_swap<D>(up ? x[a] : x[b]);
+  const float xa = up ? r : x[a], xb = up ? x[b] : r;
+  x[a] = xa;
+  x[b] = xb;
+}
+__device__ __forceinline__ f32x4 quad_transpose(f32x4 x, int j) {
+  quad_round<1>(x, (j & 1) != 0, 0, 1);
+  quad_round<1>(x, (j & 1) != 0, 2, 3);
+  quad_round<2>(x, (j & 2) != 0, 0, 2);
+  quad_round<2>(x, (j & 2) != 0, 1, 3);
+  return x;
+}
+
+// Four consecutive io elements into LDS.
+__device__ __forceinline__ void lds_put4(unsigned char* p, f32x4 x, const bf16_t*) {
+  typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+  *reinterpret_cast<u32x2*>(p) = u32x2{f32x2_to_bf16x2(x[0], x[1]), f32x2_to_bf16x2(x[2], x[3])};
+}
+__device__ __forceinline__ void lds_put4(unsigned char* p, f32x4 x, const float*) {
+  *reinterpret_cast<f32x4*>(p) = x;
+}
+
+// Four consecutive io elements through a buffer resource (out-of-range
+// offsets are dropped).
+__device__ __forceinline__ void buffer_store4(__amdgpu_buffer_rsrc_t r, int off, f32x4 x, const bf16_t*) {
+  typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+  const u32x2 u = {f32x2_to_bf16x2(x[0], x[1]), f32x2_to_bf16x2(x[2], x[3])};
+  __builtin_amdgcn_raw_buffer_store_b64(u, r, off, 0, 0);
+}
+__device__ __forceinline__ void buffer_store4(__amdgpu_buffer_rsrc_t r, int off, f32x4 x, const float*) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, off, 0, 0);
+}
+
 // Workgroup barrier that waits only for this wave's LDS traffic (lgkmcnt 0),
 // not for its global loads and stores, which may stay in flight across it.
 __device__ __forceinline__ void lds_barrier() {
@@ -712,11 +753,30 @@ struct ScanLds {
   static constexpr size_t early = B::oK;                          // R, Qh
   static constexpr size_t late = B::bytes - B::oK + vbytes;       // Kb^T, P, T, Gamma, beta, v
   static constexpr size_t late0 = NBUF == 2 ? 2 * early : early;  // first late slot
-  static constexpr size_t total = NBUF * stage;
+  // Output staging (double-buffered scheme only): the compute waves leave a
+  // chunk's output tile here; the loader waves store it to HBM.
+  static constexpr size_t orow = static_cast<size_t>(TILE) * sizeof(T);  // bytes per output row
+  static constexpr size_t ostage = NBUF * stage;
+  static constexpr bool stage_o = NBUF == 2 && ostage + C * orow <= 160 * 1024;
+  static constexpr size_t dx = ostage + (stage_o ? C * orow : 0);
+  // Split roles (with the staged output): per 16-column group a state wave
+  // (R S, T Y, Kb^T D) and an output wave (Qh S, P D) that takes the
+  // state's B fragments and D (hi and lo bf16 parts, or fp32) from LDS.
+  // Per lane: D takes C bytes, the state fragments DK / 2 (bf16) or DK (fp32).
+  static constexpr size_t sx_group = 64 * static_cast<size_t>(DK) * (sizeof(T) == 2 ? 1 : 2) / 2;
+  static constexpr size_t dx_group = 64 * static_cast<size_t>(C) + sx_group;
+  static constexpr bool split = stage_o && dx + (TILE / 16) * dx_group <= 160 * 1024;
+  static constexpr int roles = split ? 2 : 1;
+  static constexpr size_t total = dx + (split ? (TILE / 16) * dx_group : 0);
 };
 
+template <typename T, int C, int DK, int WAVES>
+constexpr int scan_threads() {
+  return 64 * (WAVES * ScanLds<T, C, DK, 16 * WAVES>::roles + kLoaderWaves);
+}
+
 template <typename T, int C, int DK, int DV, int WAVES>
-__global__ __launch_bounds__(64 * (WAVES + kLoaderWaves)) void scan_kernel(
+__global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel(
     const T* __restrict__ v, const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_off,
     const int32_t* __restrict__ order, int N, int H, const unsigned char* __restrict__ ws, const float* S0,
     T* __restrict__ o, float* S_T, int gbeg, int gend, float* carry) {
@@ -749,7 +809,8 @@ __global__ __launch_bounds__(64 * (WAVES + kLoaderWaves)) void scan_kernel(
   const int h = p % H;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps loops scalar
-  const bool loader = wave >= WAVES;
+  constexpr int CW = WAVES * SL::roles;  // compute waves
+  const bool loader = wave >= CW;
   const int tbeg = cu[seq], L_seq = cu[seq + 1] - tbeg;
   const int c0 = chunk_off[seq];
   const int nch = (L_seq + C - 1) / C;
@@ -766,7 +827,7 @@ __global__ __launch_bounds__(64 * (WAVES + kLoaderWaves)) void scan_kernel(
   // Single-slot scheme (NBUF = 1): the whole block of chunk cc and its v
   // tile, one chunk ahead.
   auto issue = [&](int cc) {
-    const int lw = wave - WAVES;
+    const int lw = wave - CW;
     const unsigned char* src = ws + (static_cast<size_t>(c0 + cc) * H + h) * B::bytes;
     for (int j = lw; j < NG; j += kLoaderWaves) lds_load16(src + j * 1024 + lane * 16, smem + j * 1024);
     const int t0 = tbeg + cc * C, len = min(C, L_seq - cc * C);
@@ -796,7 +857,7 @@ __global__ __launch_bounds__(64 * (WAVES + kLoaderWaves)) void scan_kernel(
                     "block granules");
       constexpr int NVW = (NVG + kLoaderWaves - 1) / kLoaderWaves;
       constexpr int NE = EG / kLoaderWaves, NLT = LG / kLoaderWaves + 1 + NVW;
-      const int lw = wave - WAVES;
+      const int lw = wave - CW;
       if (cb >= ce) {  // empty sequence: the compute waves only pass the first barrier
         lds_barrier();
         return;
@@ -829,6 +890,26 @@ __global__ __launch_bounds__(64 * (WAVES + kLoaderWaves)) void scan_kernel(
                      dst + (B::bytes - B::oK) + j * 1024);
         }
       };
+      // Output rows of chunk cc (staged in LDS by the compute waves before
+      // the end-of-chunk barrier): each wave stores NSW 16-byte row pieces
+      // per lane, through a buffer resource spanning the chunk's valid rows.
+      constexpr int LPR = static_cast<int>(SL::orow / 16), RPI = 64 / LPR, NSI = C / RPI;
+      constexpr int NSW = SL::stage_o ? (NSI + kLoaderWaves - 1) / kLoaderWaves : 0;
+      static_assert(!SL::stage_o || (SL::orow % 16 == 0 && 64 % LPR == 0 && C % RPI == 0), "output tile geometry");
+      auto ostore = [&](int cc) {
+        if constexpr (SL::stage_o) {
+          const int len = cc < cb ? 0 : min(C, L_seq - cc * C);  // nothing before the first chunk
+          const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+              o + (static_cast<size_t>(tbeg + max(cc, 0) * C) * H + h) * DV + tile * TILE, 0,
+              len * H * DV * static_cast<int>(sizeof(T)), 0x00020000);
+#pragma unroll
+          for (int m = 0; m < NSW; ++m) {
+            const int row = ((lw + kLoaderWaves * m) % NSI) * RPI + lane / LPR, cb16 = (lane % LPR) * 16;
+            const u32x4 x = *reinterpret_cast<const u32x4*>(smem + SL::ostage + row * SL::orow + cb16);
+            __builtin_amdgcn_raw_buffer_store_b128(x, ro, row * H * DV * static_cast<int>(sizeof(T)) + cb16, 0, 0);
+          }
+        }
+      };
       early(cb, 0);
       late(cb, 0);
       early(cb + 1, 1);
@@ -836,13 +917,16 @@ __global__ __launch_bounds__(64 * (WAVES + kLoaderWaves)) void scan_kernel(
       lds_barrier();
       for (int cc = cb; cc < ce; ++cc) {
         const int b = (cc - cb) & 1;
+        ostore(cc - 1);
         late(cc + 1, b ^ 1);
-        wait_vm<NE + NLT>();  // late part of chunk cc
-        lds_barrier();        // M(cc): early slot b free, late part of cc resident
+        wait_vm<NE + NSW + NLT>();  // late part of chunk cc
+        lds_barrier();              // M(cc): early slot b free, late part of cc resident
         early(cc + 2, b);
-        wait_vm<NE + NLT>();  // early part of chunk cc + 1
-        lds_barrier();        // end of chunk cc
+        if constexpr (SL::split) lds_barrier();  // X(cc): D of chunk cc in LDS
+        wait_vm<NE + NSW + NLT>();  // early part of chunk cc + 1
+        lds_barrier();              // end of chunk cc
       }
+      ostore(ce - 1);
       return;
     }
     if (cb < ce) issue(cb);
@@ -859,12 +943,18 @@ __global__ __launch_bounds__(64 * (WAVES + kLoaderWaves)) void scan_kernel(
     return;
   }
 
-  // Compute waves: wave w owns 16 value columns; state slice in accumulators.
+  // Compute waves: 16 value columns per column group; every compute wave
+  // keeps the group's dk x 16 state slice in MFMA accumulators.  With split
+  // roles, wave cg (< WAVES) is the group's state wave and wave WAVES + cg
+  // its output wave; otherwise one wave does both.
   const int n = lane & 15, g = lane >> 4;
-  const int col = tile * TILE + wave * 16 + n;
+  const int role = SL::split ? wave / WAVES : 0;
+  const int cg = SL::split ? wave % WAVES : wave;
+  const bool do_state = role == 0, do_out = !SL::split || role == 1;
+  const int col = tile * TILE + cg * 16 + n;
   f32x4 S[ST];
   const size_t sbase = (static_cast<size_t>(seq) * H + h) * DK * DV;
-  if (s_in) {
+  if (s_in && do_state) {
 #pragma unroll
     for (int st = 0; st < ST; ++st)
 #pragma unroll
@@ -873,145 +963,237 @@ __global__ __launch_bounds__(64 * (WAVES + kLoaderWaves)) void scan_kernel(
 #pragma unroll
     for (int st = 0; st < ST; ++st) S[st] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  // byte offset of output element (chunk row 16 mt + 4 g + i, column col)
-  // from the chunk's first row; the host keeps C H DV sizeof(T) below 2^31
-  uint32_t ooff[MT][4];
+  // Output tiles are stored after a quad transpose: lane (n, g) writes row
+  // 16 mt + 4 g + (n & 3), columns (n & ~3) .. (n & ~3) + 3 of its 16.  Byte
+  // offsets from the chunk's first row; the host keeps C H DV sizeof(T) < 2^31.
+  int ooff[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      ooff[mt][i] = static_cast<uint32_t>(((16 * mt + 4 * g + i) * H * DV + col) * static_cast<int>(sizeof(T)));
+    ooff[mt] = ((16 * mt + 4 * g + (n & 3)) * H * DV + col - (n & 3)) * static_cast<int>(sizeof(T));
   if constexpr (SL::NBUF == 2) lds_barrier(); else __syncthreads();  // first chunk resident
 
-  for (int cc = cb; cc < ce; ++cc) {
-    const int b = (SL::NBUF == 2) ? ((cc - cb) & 1) : 0;
-    // early part (R, Qh) and late part (from Kb^T on, then the v tile);
-    // lat(off) addresses block offset off >= oK in the late slot
-    const unsigned char* eblk = smem + b * SL::early;
-    const unsigned char* lblk = smem + SL::late0 + b * SL::late;
+  // Output tile of a chunk, transposed within lane quads (four consecutive
+  // columns of one row per lane): staged in LDS for the loader waves, or
+  // stored directly through a buffer resource spanning the chunk's valid
+  // rows (rows past the end are dropped by the hardware range check).
+  auto put_o = [&](const f32x4 (&O)[MT], int t0, int len) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const f32x4 x = quad_transpose(O[mt], n & 3);
+      if constexpr (SL::stage_o) {
+        unsigned char* dst = smem + SL::ostage + (16 * mt + 4 * g + (n & 3)) * SL::orow +
+                             (cg * 16 + (n & ~3)) * sizeof(T);
+        lds_put4(dst, x, static_cast<T*>(nullptr));
+      } else {
+        const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+            o + (static_cast<size_t>(t0) * H + h) * DV, 0, len * H * DV * static_cast<int>(sizeof(T)), 0x00020000);
+        buffer_store4(ro, ooff[mt], x, static_cast<T*>(nullptr));
+      }
+    }
+  };
+  // Per-chunk pieces.  View of chunk cc: early part (R, Qh) and late part
+  // (from Kb^T on, then the v tile); lat(off) addresses block offset
+  // off >= oK in the late slot.
+  auto eblk_of = [&](int cc) { return smem + ((SL::NBUF == 2) ? ((cc - cb) & 1) : 0) * SL::early; };
+  auto lblk_of = [&](int cc) { return smem + SL::late0 + ((SL::NBUF == 2) ? ((cc - cb) & 1) : 0) * SL::late; };
+  // rows of a stored tile times the state fragments: A[mt] = X[rows of mt] sb
+  auto rows_x_state = [&](const RowFrags<T, B::RB_R, NSK> (&fr)[MT], const F (&sb)[NSK], f32x4 (&A)[MT]) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NSK; ++s) a = M::mma(fr[mt].f[s], sb[s], a);
+      A[mt] = a;
+    }
+  };
+  // Y = b V - R S; D = T Y with Y split into hi + lo (T unit lower
+  // triangular); D split into hi + lo
+  auto make_d = [&](const unsigned char* lblk, f32x4 (&Y)[MT], F (&dh)[NSC], F (&dl)[NSC]) {
     auto lat = [&](size_t off) { return lblk + (off - B::oK); };
     const T* vt = reinterpret_cast<const T*>(lat(B::bytes));
-    const float* Gam = reinterpret_cast<const float*>(lat(B::oG));
     const float* Bet = reinterpret_cast<const float*>(lat(B::oB));
-    const int t0 = tbeg + cc * C, len = min(C, L_seq - cc * C);
-
-    // B fragments of the state (shared by R S and Qh S)
-    F sb[NSK];
 #pragma unroll
-    for (int s = 0; s < NSK; ++s) sb[s] = AB::b(S, s);
-
-    // Y = R S and O = Qh S together: 2 MT independent accumulator chains.
-    f32x4 Y[MT], O[MT];
-    {
-      RowFrags<T, B::RB_R, NSK> rc, qc, rn, qn;
-      rc.load(eblk + B::oR, n, g);
-      qc.load(eblk + B::oQ, n, g);
+    for (int mt = 0; mt < MT; ++mt) {
+      const f32x4 bt = *reinterpret_cast<const f32x4*>(Bet + 16 * mt + 4 * g);
+      f32x4 vv;
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        if (mt + 1 < MT) {
-          rn.load(eblk + B::oR, 16 * (mt + 1) + n, g);
-          qn.load(eblk + B::oQ, 16 * (mt + 1) + n, g);
-        }
-        f32x4 ay = {0.f, 0.f, 0.f, 0.f}, ao = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < NSK; ++s) {
-          ay = M::mma(rc.f[s], sb[s], ay);
-          ao = M::mma(qc.f[s], sb[s], ao);
-        }
-        Y[mt] = ay;
-        O[mt] = ao;
-        if (mt + 1 < MT) {
-          rc = rn;
-          qc = qn;
-        }
-      }
+      for (int i = 0; i < 4; ++i) vv[i] = io<T>::load(vt + (16 * mt + 4 * g + i) * TILE + cg * 16 + n);
+      Y[mt] = bt * vv - Y[mt];
     }
-    // barrier M: every wave is done with the early slot; the late part of
-    // this chunk is resident
-    if constexpr (SL::NBUF == 2) lds_barrier();
-    // Y = b*V - R S; D = T Y with Y split into hi + lo (T unit lower triangular)
+    F yh[NSC], yl[NSC];
+#pragma unroll
+    for (int s = 0; s < NSC; ++s) SP::hilo(Y, s, yh[s], yl[s]);
+    RowFrags<T, B::RB_K, NSC> tf[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) tf[mt].load(lat(B::oT), 16 * mt + n, g);
     f32x4 D[MT];
-    {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const f32x4 bt = *reinterpret_cast<const f32x4*>(Bet + 16 * mt + 4 * g);
-        f32x4 vv;
+    for (int mt = 0; mt < MT; ++mt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) vv[i] = io<T>::load(vt + (16 * mt + 4 * g + i) * TILE + wave * 16 + n);
-        Y[mt] = bt * vv - Y[mt];
+      for (int s = 0; s <= (16 * mt + 15) / AB::KS; ++s) {
+        acc = M::mma(tf[mt].f[s], yh[s], acc);
+        if (SP::has_lo) acc = M::mma(tf[mt].f[s], yl[s], acc);
       }
-      F yh[NSC], yl[NSC];
-#pragma unroll
-      for (int s = 0; s < NSC; ++s) SP::hilo(Y, s, yh[s], yl[s]);
-      RowFrags<T, B::RB_K, NSC> tf[MT];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) tf[mt].load(lat(B::oT), 16 * mt + n, g);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s <= (16 * mt + 15) / AB::KS; ++s) {
-          acc = M::mma(tf[mt].f[s], yh[s], acc);
-          if (SP::has_lo) acc = M::mma(tf[mt].f[s], yl[s], acc);
-        }
-        D[mt] = acc;
-      }
+      D[mt] = acc;
     }
-    // O += P D (D split into hi + lo) and S = Diag(e^{g_last}) S + Kb^T D,
-    // issued together
-    {
-      F dh[NSC], dl[NSC];
 #pragma unroll
-      for (int s = 0; s < NSC; ++s) SP::hilo(D, s, dh[s], dl[s]);
-      RowFrags<T, B::RB_K, NSC> pf[MT];
+    for (int s = 0; s < NSC; ++s) SP::hilo(D, s, dh[s], dl[s]);
+  };
+  // O += P D (D as hi + lo)
+  auto add_pd = [&](const RowFrags<T, B::RB_K, NSC> (&pf)[MT], const F (&dh)[NSC], const F (&dl)[NSC],
+                    f32x4 (&O)[MT]) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) pf[mt].load(lat(B::oP), 16 * mt + n, g);
-      RowFrags<T, B::RB_K, NSC> kf[ST];
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int st = 0; st < ST; ++st) kf[st].load(lat(B::oK), 16 * st + n, g);
-#pragma unroll
-      for (int st = 0; st < ST; ++st) S[st] *= *reinterpret_cast<const f32x4*>(Gam + 16 * st + 4 * g);
-#pragma unroll
-      for (int st = 0; st < ST; ++st) {
-        if (st < MT) {
-#pragma unroll
-          for (int s = 0; s <= (16 * st + 15) / AB::KS; ++s) {
-            O[st] = M::mma(pf[st].f[s], dh[s], O[st]);
-            if (SP::has_lo) O[st] = M::mma(pf[st].f[s], dl[s], O[st]);
-          }
-        }
-#pragma unroll
-        for (int s = 0; s < NSC; ++s) S[st] = M::mma(kf[st].f[s], dh[s], S[st]);
+      for (int s = 0; s <= (16 * mt + 15) / AB::KS; ++s) {
+        O[mt] = M::mma(pf[mt].f[s], dh[s], O[mt]);
+        if (SP::has_lo) O[mt] = M::mma(pf[mt].f[s], dl[s], O[mt]);
       }
-    }
-    // store O: wave-uniform chunk base plus the per-lane byte offsets
-    {
-      unsigned char* ob = reinterpret_cast<unsigned char*>(o + (static_cast<size_t>(t0) * H + h) * DV);
-      if (len == C) {
+  };
+  // S = Diag(e^{g_last}) S + Kb^T D (D's hi part)
+  auto update_s = [&](const unsigned char* lblk, const RowFrags<T, B::RB_K, NSC> (&kf)[ST], const F (&dh)[NSC]) {
+    const float* Gam = reinterpret_cast<const float*>(lblk + (B::oG - B::oK));
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+    for (int st = 0; st < ST; ++st) S[st] *= *reinterpret_cast<const f32x4*>(Gam + 16 * st + 4 * g);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) io<T>::store(reinterpret_cast<T*>(ob + ooff[mt][i]), O[mt][i]);
-      } else {
+    for (int st = 0; st < ST; ++st)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (16 * mt + 4 * g + i < len) io<T>::store(reinterpret_cast<T*>(ob + ooff[mt][i]), O[mt][i]);
-      }
-    }
+      for (int s = 0; s < NSC; ++s) S[st] = M::mma(kf[st].f[s], dh[s], S[st]);
+  };
+  auto chunk_end = [&]() {
     if constexpr (SL::NBUF == 2) {
-      lds_barrier();  // end of chunk: late slot b free; early part of cc + 1 resident
+      lds_barrier();  // end of chunk: late slot free; early part of the next chunk resident
     } else {
       __syncthreads();  // chunk consumed
       __syncthreads();  // next chunk resident
     }
-  }
-  if (s_out) {
+  };
+
+  if constexpr (SL::split) {
+    // D (hi, lo) and the state fragments pass from state to output wave here
+    F* const dxp = reinterpret_cast<F*>(smem + SL::dx + cg * SL::dx_group) + lane;
+    F* const sxp = dxp + 64 * C / static_cast<int>(sizeof(F));
+    if (do_state) {
+      for (int cc = cb; cc < ce; ++cc) {
+        const unsigned char* eblk = eblk_of(cc);
+        const unsigned char* lblk = lblk_of(cc);
+        F sb[NSK];
 #pragma unroll
-    for (int st = 0; st < ST; ++st)
+        for (int s = 0; s < NSK; ++s) {
+          sb[s] = AB::b(S, s);
+          sxp[64 * s] = sb[s];
+        }
+        RowFrags<T, B::RB_R, NSK> fr[MT];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s_out[sbase + static_cast<size_t>(16 * st + 4 * g + i) * DV + col] = S[st][i];
+        for (int mt = 0; mt < MT; ++mt) fr[mt].load(eblk + B::oR, 16 * mt + n, g);
+        f32x4 Y[MT];
+        rows_x_state(fr, sb, Y);
+        lds_barrier();  // M: early slot consumed; late part resident; state fragments in LDS
+        F dh[NSC], dl[NSC];
+        make_d(lblk, Y, dh, dl);
+#pragma unroll
+        for (int s = 0; s < NSC; ++s) {
+          dxp[64 * s] = dh[s];
+          if (SP::has_lo) dxp[64 * (NSC + s)] = dl[s];
+        }
+        RowFrags<T, B::RB_K, NSC> kf[ST];
+#pragma unroll
+        for (int st = 0; st < ST; ++st) kf[st].load(lblk, 16 * st + n, g);
+        lds_barrier();  // X: D in LDS
+        update_s(lblk, kf, dh);
+        chunk_end();
+      }
+      if (s_out) {
+#pragma unroll
+        for (int st = 0; st < ST; ++st)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s_out[sbase + static_cast<size_t>(16 * st + 4 * g + i) * DV + col] = S[st][i];
+      }
+    } else {
+      for (int cc = cb; cc < ce; ++cc) {
+        const unsigned char* eblk = eblk_of(cc);
+        const unsigned char* lblk = lblk_of(cc);
+        const int t0 = tbeg + cc * C, len = min(C, L_seq - cc * C);
+        RowFrags<T, B::RB_R, NSK> fr[MT];  // Qh rows: the early slot is refilled after M
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) fr[mt].load(eblk + B::oQ, 16 * mt + n, g);
+        lds_barrier();  // M
+        F sb[NSK];
+#pragma unroll
+        for (int s = 0; s < NSK; ++s) sb[s] = sxp[64 * s];
+        f32x4 O[MT];
+        rows_x_state(fr, sb, O);
+        RowFrags<T, B::RB_K, NSC> pf[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) pf[mt].load(lblk + (B::oP - B::oK), 16 * mt + n, g);
+        lds_barrier();  // X
+        F dh[NSC], dl[NSC];
+#pragma unroll
+        for (int s = 0; s < NSC; ++s) {
+          dh[s] = dxp[64 * s];
+          if (SP::has_lo) dl[s] = dxp[64 * (NSC + s)];
+        }
+        add_pd(pf, dh, dl, O);
+        put_o(O, t0, len);
+        chunk_end();
+      }
+    }
+  } else {
+    for (int cc = cb; cc < ce; ++cc) {
+      const unsigned char* eblk = eblk_of(cc);
+      const unsigned char* lblk = lblk_of(cc);
+      const int t0 = tbeg + cc * C, len = min(C, L_seq - cc * C);
+      // B fragments of the state (shared by R S and Qh S)
+      F sb[NSK];
+#pragma unroll
+      for (int s = 0; s < NSK; ++s) sb[s] = AB::b(S, s);
+      // Y = R S and O = Qh S together: 2 MT independent accumulator chains
+      f32x4 Y[MT], O[MT];
+      {
+        RowFrags<T, B::RB_R, NSK> rc, qc, rn, qn;
+        rc.load(eblk + B::oR, n, g);
+        qc.load(eblk + B::oQ, n, g);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          if (mt + 1 < MT) {
+            rn.load(eblk + B::oR, 16 * (mt + 1) + n, g);
+            qn.load(eblk + B::oQ, 16 * (mt + 1) + n, g);
+          }
+          f32x4 ay = {0.f, 0.f, 0.f, 0.f}, ao = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < NSK; ++s) {
+            ay = M::mma(rc.f[s], sb[s], ay);
+            ao = M::mma(qc.f[s], sb[s], ao);
+          }
+          Y[mt] = ay;
+          O[mt] = ao;
+          if (mt + 1 < MT) {
+            rc = rn;
+            qc = qn;
+          }
+        }
+      }
+      if constexpr (SL::NBUF == 2) lds_barrier();  // M: early slot consumed; late part resident
+      F dh[NSC], dl[NSC];
+      make_d(lblk, Y, dh, dl);
+      RowFrags<T, B::RB_K, NSC> pf[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) pf[mt].load(lblk + (B::oP - B::oK), 16 * mt + n, g);
+      RowFrags<T, B::RB_K, NSC> kf[ST];
+#pragma unroll
+      for (int st = 0; st < ST; ++st) kf[st].load(lblk, 16 * st + n, g);
+      add_pd(pf, dh, dl, O);
+      update_s(lblk, kf, dh);
+      put_o(O, t0, len);
+      chunk_end();
+    }
+    if (s_out) {
+#pragma unroll
+      for (int st = 0; st < ST; ++st)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s_out[sbase + static_cast<size_t>(16 * st + 4 * g + i) * DV + col] = S[st][i];
+    }
   }
 }
 
@@ -1078,7 +1260,7 @@ static hipError_t launch_scan(const PrefillPlan& p, const void* v, const int32_t
   const int pairs = p.N * p.H;
   const int nsplit = DV / (16 * WAVES);
   const unsigned grid = static_cast<unsigned>((pairs + 7) / 8 * 8 * nsplit);
-  hipLaunchKernelGGL((scan_kernel<T, C, DK, DV, WAVES>), dim3(grid), dim3(64 * (WAVES + kLoaderWaves)), SL::total, st,
+  hipLaunchKernelGGL((scan_kernel<T, C, DK, DV, WAVES>), dim3(grid), dim3(scan_threads<T, C, DK, WAVES>()), SL::total, st,
                      static_cast<const T*>(v), cu, chunk_off, order, p.N, p.H, blocks, S0, static_cast<T*>(o), S_T,
                      gbeg, gend, carry);
   return hipGetLastError();
