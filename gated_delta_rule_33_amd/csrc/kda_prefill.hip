@@ -709,13 +709,12 @@ __device__ __forceinline__ f32x4 quad_transpose(f32x4 x, int j) {
   return x;
 }
 
-// Four consecutive io elements into LDS.
-__device__ __forceinline__ void lds_put4(unsigned char* p, f32x4 x, const bf16_t*) {
-  typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
-  *reinterpret_cast<u32x2*>(p) = u32x2{f32x2_to_bf16x2(x[0], x[1]), f32x2_to_bf16x2(x[2], x[3])};
+// One io element into LDS.
+__device__ __forceinline__ void lds_put1(unsigned char* p, float x, const bf16_t*) {
+  *reinterpret_cast<uint16_t*>(p) = f32_to_bf16(x);
 }
-__device__ __forceinline__ void lds_put4(unsigned char* p, f32x4 x, const float*) {
-  *reinterpret_cast<f32x4*>(p) = x;
+__device__ __forceinline__ void lds_put1(unsigned char* p, float x, const float*) {
+  *reinterpret_cast<float*>(p) = x;
 }
 
 // Four consecutive io elements through a buffer resource (out-of-range
@@ -844,8 +843,8 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
   if (loader) {
     if constexpr (SL::NBUF == 2) {
       // Early part of chunk x: issued once chunk x - 2 has passed its first
-      // products (barrier M(x - 2)), needed at the end of chunk x - 1.  Late
-      // part of chunk x: issued at the end of chunk x - 2, needed at M(x).
+      // products (barrier M(x - 2)); late part of chunk x: issued at the end
+      // of chunk x - 2.  Both are resident by the end of chunk x - 1.
       // Every loader wave moves the same number of granules (the tail
       // granule with Gamma, beta and v granules may be moved twice, with
       // identical bytes), so one vmcnt bound serves every wait; chunks past
@@ -913,18 +912,17 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
       early(cb, 0);
       late(cb, 0);
       early(cb + 1, 1);
-      wait_vm<NE + NLT>();  // early part of chunk cb
+      wait_vm<NE>();  // chunk cb resident (early and late parts)
       lds_barrier();
       for (int cc = cb; cc < ce; ++cc) {
         const int b = (cc - cb) & 1;
-        ostore(cc - 1);
         late(cc + 1, b ^ 1);
-        wait_vm<NE + NSW + NLT>();  // late part of chunk cc
-        lds_barrier();              // M(cc): early slot b free, late part of cc resident
+        ostore(cc - 1);
+        lds_barrier();  // M(cc): early slot b free
         early(cc + 2, b);
         if constexpr (SL::split) lds_barrier();  // X(cc): D of chunk cc in LDS
-        wait_vm<NE + NSW + NLT>();  // early part of chunk cc + 1
-        lds_barrier();              // end of chunk cc
+        wait_vm<NE>();  // all but the early part of chunk cc + 2: chunk cc + 1 resident
+        lds_barrier();  // end of chunk cc
       }
       ostore(ce - 1);
       return;
@@ -972,19 +970,19 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
     ooff[mt] = ((16 * mt + 4 * g + (n & 3)) * H * DV + col - (n & 3)) * static_cast<int>(sizeof(T));
   if constexpr (SL::NBUF == 2) lds_barrier(); else __syncthreads();  // first chunk resident
 
-  // Output tile of a chunk, transposed within lane quads (four consecutive
-  // columns of one row per lane): staged in LDS for the loader waves, or
-  // stored directly through a buffer resource spanning the chunk's valid
-  // rows (rows past the end are dropped by the hardware range check).
+  // Output tile of a chunk: staged row-major in LDS for the loader waves, or
+  // transposed within lane quads (four consecutive columns of one row per
+  // lane) and stored directly through a buffer resource spanning the chunk's
+  // valid rows (rows past the end are dropped by the hardware range check).
   auto put_o = [&](const f32x4 (&O)[MT], int t0, int len) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const f32x4 x = quad_transpose(O[mt], n & 3);
       if constexpr (SL::stage_o) {
-        unsigned char* dst = smem + SL::ostage + (16 * mt + 4 * g + (n & 3)) * SL::orow +
-                             (cg * 16 + (n & ~3)) * sizeof(T);
-        lds_put4(dst, x, static_cast<T*>(nullptr));
+        unsigned char* dst = smem + SL::ostage + (16 * mt + 4 * g) * SL::orow + (cg * 16 + n) * sizeof(T);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lds_put1(dst + i * SL::orow, O[mt][i], static_cast<T*>(nullptr));
       } else {
+        const f32x4 x = quad_transpose(O[mt], n & 3);
         const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
             o + (static_cast<size_t>(t0) * H + h) * DV, 0, len * H * DV * static_cast<int>(sizeof(T)), 0x00020000);
         buffer_store4(ro, ooff[mt], x, static_cast<T*>(nullptr));
@@ -1006,26 +1004,32 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
       A[mt] = a;
     }
   };
-  // Y = b V - R S; D = T Y with Y split into hi + lo (T unit lower
-  // triangular); D split into hi + lo
-  auto make_d = [&](const unsigned char* lblk, f32x4 (&Y)[MT], F (&dh)[NSC], F (&dl)[NSC]) {
-    auto lat = [&](size_t off) { return lblk + (off - B::oK); };
-    const T* vt = reinterpret_cast<const T*>(lat(B::bytes));
-    const float* Bet = reinterpret_cast<const float*>(lat(B::oB));
+  // Late-part inputs of D: beta v (this lane's accumulator positions) and
+  // the row fragments of T.
+  struct DIn {
+    f32x4 bv[MT];
+    RowFrags<T, B::RB_K, NSC> tf[MT];
+  };
+  auto load_din = [&](const unsigned char* lblk, DIn& in) {
+    const T* vt = reinterpret_cast<const T*>(lblk + (B::bytes - B::oK));
+    const float* Bet = reinterpret_cast<const float*>(lblk + (B::oB - B::oK));
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const f32x4 bt = *reinterpret_cast<const f32x4*>(Bet + 16 * mt + 4 * g);
-      f32x4 vv;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) vv[i] = io<T>::load(vt + (16 * mt + 4 * g + i) * TILE + cg * 16 + n);
-      Y[mt] = bt * vv - Y[mt];
+      for (int i = 0; i < 4; ++i) in.bv[mt][i] = bt[i] * io<T>::load(vt + (16 * mt + 4 * g + i) * TILE + cg * 16 + n);
+      in.tf[mt].load(lblk + (B::oT - B::oK), 16 * mt + n, g);
     }
+  };
+  // Y = b V - R S; D = T Y with Y split into hi + lo (T unit lower
+  // triangular); D split into hi + lo
+  auto make_d = [&](const DIn& in, f32x4 (&Y)[MT], F (&dh)[NSC], F (&dl)[NSC]) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) Y[mt] = in.bv[mt] - Y[mt];
     F yh[NSC], yl[NSC];
 #pragma unroll
     for (int s = 0; s < NSC; ++s) SP::hilo(Y, s, yh[s], yl[s]);
-    RowFrags<T, B::RB_K, NSC> tf[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) tf[mt].load(lat(B::oT), 16 * mt + n, g);
+    const RowFrags<T, B::RB_K, NSC>(&tf)[MT] = in.tf;
     f32x4 D[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -1078,20 +1082,23 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
       for (int cc = cb; cc < ce; ++cc) {
         const unsigned char* eblk = eblk_of(cc);
         const unsigned char* lblk = lblk_of(cc);
+        // the whole chunk is resident: R rows and the late-part inputs now
+        RowFrags<T, B::RB_R, NSK> fr[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) fr[mt].load(eblk + B::oR, 16 * mt + n, g);
+        DIn din;
+        load_din(lblk, din);
         F sb[NSK];
 #pragma unroll
         for (int s = 0; s < NSK; ++s) {
           sb[s] = AB::b(S, s);
           sxp[64 * s] = sb[s];
         }
-        RowFrags<T, B::RB_R, NSK> fr[MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) fr[mt].load(eblk + B::oR, 16 * mt + n, g);
         f32x4 Y[MT];
         rows_x_state(fr, sb, Y);
-        lds_barrier();  // M: early slot consumed; late part resident; state fragments in LDS
+        lds_barrier();  // M: early slot consumed; state fragments in LDS
         F dh[NSC], dl[NSC];
-        make_d(lblk, Y, dh, dl);
+        make_d(din, Y, dh, dl);
 #pragma unroll
         for (int s = 0; s < NSC; ++s) {
           dxp[64 * s] = dh[s];
@@ -1118,15 +1125,15 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
         RowFrags<T, B::RB_R, NSK> fr[MT];  // Qh rows: the early slot is refilled after M
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) fr[mt].load(eblk + B::oQ, 16 * mt + n, g);
+        RowFrags<T, B::RB_K, NSC> pf[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) pf[mt].load(lblk + (B::oP - B::oK), 16 * mt + n, g);
         lds_barrier();  // M
         F sb[NSK];
 #pragma unroll
         for (int s = 0; s < NSK; ++s) sb[s] = sxp[64 * s];
         f32x4 O[MT];
         rows_x_state(fr, sb, O);
-        RowFrags<T, B::RB_K, NSC> pf[MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) pf[mt].load(lblk + (B::oP - B::oK), 16 * mt + n, g);
         lds_barrier();  // X
         F dh[NSC], dl[NSC];
 #pragma unroll
@@ -1174,9 +1181,11 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
           }
         }
       }
-      if constexpr (SL::NBUF == 2) lds_barrier();  // M: early slot consumed; late part resident
+      if constexpr (SL::NBUF == 2) lds_barrier();  // M: early slot consumed
+      DIn din;
+      load_din(lblk, din);
       F dh[NSC], dl[NSC];
-      make_d(lblk, Y, dh, dl);
+      make_d(din, Y, dh, dl);
       RowFrags<T, B::RB_K, NSC> pf[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) pf[mt].load(lblk + (B::oP - B::oK), 16 * mt + n, g);
