@@ -59,6 +59,29 @@ __device__ __forceinline__ f32x4 load4(const bf16_t* p) {
   return r;
 }
 
+// Raw storage of 4 consecutive io elements (loaded now, widened later).
+template <typename T>
+struct raw4;
+template <>
+struct raw4<float> {
+  typedef f32x4 type;
+};
+template <>
+struct raw4<bf16_t> {
+  typedef uint2 type;
+};
+__device__ __forceinline__ f32x4 load4raw(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ uint2 load4raw(const bf16_t* p) { return *reinterpret_cast<const uint2*>(p); }
+__device__ __forceinline__ f32x4 cvt4(f32x4 x) { return x; }
+__device__ __forceinline__ f32x4 cvt4(uint2 u) {
+  f32x4 r;
+  r[0] = __uint_as_float(u.x << 16);
+  r[1] = __uint_as_float(u.x & 0xFFFF0000u);
+  r[2] = __uint_as_float(u.y << 16);
+  r[3] = __uint_as_float(u.y & 0xFFFF0000u);
+  return r;
+}
+
 // Store 4 consecutive io elements.
 __device__ __forceinline__ void store4(float* p, f32x4 x) { *reinterpret_cast<f32x4*>(p) = x; }
 __device__ __forceinline__ void store4(bf16_t* p, f32x4 x) {

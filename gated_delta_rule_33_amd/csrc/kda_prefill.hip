@@ -395,12 +395,22 @@ __device__ __forceinline__ f32x4 mm16_lds_acc(const float* X, int xp, f32x4 Y, i
   return acc;
 }
 
+// Waves per SIMD the prep kernel is built for: as many workgroups as LDS
+// allows per CU, each of kPrepThreads / 64 waves over 4 SIMDs, at most 4
+// (128 registers per lane).
 template <typename T, int C, int DK>
-__global__ __launch_bounds__(kPrepThreads) void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
+constexpr int prep_waves_per_eu() {
+  constexpr int wgs = (160 * 1024) / PrepLds<T, C, DK>::total > 0 ? (160 * 1024) / PrepLds<T, C, DK>::total : 1;
+  return wgs * kPrepThreads / 256 < 4 ? wgs * kPrepThreads / 256 : 4;
+}
+
+template <typename T, int C, int DK>
+__global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(prep_waves_per_eu<T, C, DK>())))
+void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                    const float* __restrict__ la, const float* __restrict__ beta,
                                                    const int32_t* __restrict__ cu,
                                                    const int32_t* __restrict__ chunk_off, int N, int H,
-                                                   unsigned char* __restrict__ ws, int cbase) {
+                                                   unsigned char* __restrict__ ws, int cbase, int count) {
   typedef PrepLds<T, C, DK> L;
   typedef Blk<T, C, DK> B;
   typedef mma16<T> M;
@@ -424,39 +434,84 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const T* __restrict_
   float* fv = reinterpret_cast<float*>(smem + L::o3);
   float* bet = reinterpret_cast<float*>(smem + L::o4);
 
-  const int h = blockIdx.x, c = cbase + static_cast<int>(blockIdx.y);
-  const int total = chunk_off[N];
-  if (c >= total) return;
-  int lo = 0, hi = N - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (chunk_off[mid] <= c) lo = mid; else hi = mid - 1;
-  }
-  const int t0 = cu[lo] + (c - chunk_off[lo]) * C;
-  const int len = min(C, cu[lo + 1] - t0);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
-  unsigned char* blk = ws + (static_cast<size_t>(c) * H + h) * B::bytes;
-
-  // ---- loads: thread owns channels c4..c4+3 of rows r0..r0+RPT-1 ---------
+  // thread owns channels c4..c4+3 of rows r0..r0+RPT-1 in the elementwise steps
   const int cg = tid % NCG, rbk = tid / NCG;
   const int c4 = 4 * cg, r0 = rbk * RPT;
+
+  // Persistent: the workgroup walks items (chunk c = cbase + i / H, head
+  // h = i % H) with stride gridDim.x, loading the next item's inputs into
+  // registers while it works on the current one.
+  const int total = chunk_off[N];
+  const int nitems = count * H;
+  struct Item {
+    int c, h, t0, len;
+  };
+  auto locate = [&](int item) {
+    Item it{total, 0, 0, 0};  // c >= total: nothing to do
+    if (item >= nitems) return it;
+    it.c = cbase + item / H;
+    it.h = item % H;
+    if (it.c >= total) return it;
+    int lo = 0, hi = N - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (chunk_off[mid] <= it.c) lo = mid; else hi = mid - 1;
+    }
+    it.t0 = cu[lo] + (it.c - chunk_off[lo]) * C;
+    it.len = min(C, cu[lo + 1] - it.t0);
+    return it;
+  };
+  struct Raw {
+    f32x4 lg[RPT];
+    typename raw4<T>::type kr[RPT], qr[RPT];
+    float bt;
+  };
   // Rows past the end re-read the last row (all loads issue back to back);
   // their log_alpha is zeroed and beta = 0 masks them everywhere else.
-  const size_t tbase = (static_cast<size_t>(t0) * H + h) * DK;
+  auto fetch = [&](const Item& it, Raw& r) {
+    if (it.c >= total) return;
+    const size_t tbase = (static_cast<size_t>(it.t0) * H + it.h) * DK;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int e = min(r0 + i, it.len - 1) * H * DK + c4;  // < C H DK: 32-bit
+      r.lg[i] = *reinterpret_cast<const f32x4*>(la + tbase + e);
+      r.kr[i] = load4raw(k + tbase + e);
+      r.qr[i] = load4raw(q + tbase + e);
+    }
+    r.bt = (tid < C && tid < it.len) ? beta[static_cast<size_t>(it.t0 + tid) * H + it.h] : 0.f;
+  };
+  int item = blockIdx.x;
+  Item it = locate(item);
+  Raw cur;
+  fetch(it, cur);
+  for (; item < nitems; item += gridDim.x) {
+    const Item nit = locate(item + gridDim.x);
+    Raw nxt;
+    const int c = it.c, h = it.h, t0 = it.t0, len = it.len;
+    // Per-thread index math is redone per item (an opaque zero keeps the
+    // compiler from hoisting it out of the loop, where it would hold
+    // registers across every item).
+    int vz;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(vz));
+    const int tid = static_cast<int>(threadIdx.x) + vz;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 15, g = lane >> 4;
+    const int cg = tid % NCG, rbk = tid / NCG;
+    const int c4 = 4 * cg, r0 = rbk * RPT;
+    if (it.c < total) {
+  unsigned char* blk = ws + (static_cast<size_t>(c) * H + h) * B::bytes;
   f32x4 lg[RPT], kv[RPT], qv[RPT];
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
-    const int e = min(r0 + i, len - 1) * H * DK + c4;  // < C H DK: 32-bit
-    lg[i] = *reinterpret_cast<const f32x4*>(la + tbase + e);
-    kv[i] = load4(k + tbase + e);
-    qv[i] = load4(q + tbase + e);
+    lg[i] = r0 + i < len ? cur.lg[i] : f32x4{0.f, 0.f, 0.f, 0.f};
+    kv[i] = cvt4(cur.kr[i]);
+    qv[i] = cvt4(cur.qr[i]);
   }
-#pragma unroll
-  for (int i = 0; i < RPT; ++i)
-    if (r0 + i >= len) lg[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (tid < C) bet[tid] = tid < len ? beta[static_cast<size_t>(t0 + tid) * H + h] : 0.f;
+  if (tid < C) bet[tid] = cur.bt;
+  (void)t0;
 
   // ---- a2: chunk-local inclusive cumsum of log_alpha ----------------------
 #pragma unroll
@@ -539,6 +594,11 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const T* __restrict_
     }
   }
   __syncthreads();
+    }  // item, first half
+    // next item's inputs: issued once this item's elementwise inputs are dead
+    fetch(nit, nxt);
+    if (it.c < total) {
+  unsigned char* blk = ws + (static_cast<size_t>(c) * H + h) * B::bytes;
 
   // ---- a3: gated k k^T (A, fp32 in LDS) and q k^T (P) via MFMA ------------
   for (int pp = wave; pp < L::NLB; pp += kPrepThreads / 64) {
@@ -633,6 +693,11 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const T* __restrict_
       for (int j = 0; j < 4; ++j) x[j] = Ti[r * L::AP + c4b + j];
     }
     store4(reinterpret_cast<T*>(blk + B::oT + toff<T, B::RB_K>(r, c4b)), x);
+  }
+    }  // item
+    __syncthreads();  // LDS is reused by the next item
+    it = nit;
+    cur = nxt;
   }
 }
 
@@ -919,8 +984,10 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
         late(cc + 1, b ^ 1);
         ostore(cc - 1);
         lds_barrier();  // M(cc): early slot b free
+        // X(cc) (D of chunk cc in LDS) is passed before the next issue, which
+        // can stall on a full memory queue and would hold the barrier up
+        if constexpr (SL::split) lds_barrier();
         early(cc + 2, b);
-        if constexpr (SL::split) lds_barrier();  // X(cc): D of chunk cc in LDS
         wait_vm<NE>();  // all but the early part of chunk cc + 2: chunk cc + 1 resident
         lds_barrier();  // end of chunk cc
       }
@@ -1275,6 +1342,25 @@ static hipError_t launch_scan(const PrefillPlan& p, const void* v, const int32_t
   return hipGetLastError();
 }
 
+// Compute units of the current device (cached per device).
+static hipError_t device_cus(int* cus) {
+  constexpr int kMaxDev = 64;
+  static int cache[kMaxDev] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < kMaxDev && cache[dev] > 0) {
+    *cus = cache[dev];
+    return hipSuccess;
+  }
+  int n = 0;
+  if ((e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+  if (n < 1) n = 1;
+  if (dev >= 0 && dev < kMaxDev) cache[dev] = n;
+  *cus = n;
+  return hipSuccess;
+}
+
 // Per-device pair of CU-masked streams (default priority) and the events of
 // the overlapped schedule; created on first use and kept for the process.
 struct PipeStreams {
@@ -1345,15 +1431,22 @@ static hipError_t launch_prefill_t(const PrefillPlan& p, const void* q, const vo
   if (e != hipSuccess) return e;
   const size_t lp = PrepLds<T, C, DK>::total;
   static_assert(PrepLds<T, C, DK>::total <= 160 * 1024, "prep LDS");
-  auto prep = [&](int64_t cbase, int64_t count, hipStream_t s) -> hipError_t {
+  // Persistent prep: as many workgroups as fit on the CUs the stream may
+  // use (LDS-limited), each walking (chunk, head) items.
+  auto prep = [&](int64_t cbase, int64_t count, hipStream_t s, int cus) -> hipError_t {
     hipError_t r = hipFuncSetAttribute(reinterpret_cast<const void*>(&prep_kernel<T, C, DK>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lp));
     if (r != hipSuccess) return r;
-    hipLaunchKernelGGL((prep_kernel<T, C, DK>), dim3(p.H, static_cast<unsigned>(count)), dim3(kPrepThreads), lp, s,
+    const int64_t per_cu = (160 * 1024) / static_cast<int64_t>(lp) > 0 ? (160 * 1024) / static_cast<int64_t>(lp) : 1;
+    const int64_t items = count * p.H;
+    const int64_t grid = items < per_cu * cus ? items : per_cu * cus;
+    hipLaunchKernelGGL((prep_kernel<T, C, DK>), dim3(static_cast<unsigned>(grid)), dim3(kPrepThreads), lp, s,
                        static_cast<const T*>(q), static_cast<const T*>(k), la, beta, cu, chunk_off, p.N, p.H,
-                       blocks, static_cast<int>(cbase));
+                       blocks, static_cast<int>(cbase), static_cast<int>(count));
     return hipGetLastError();
   };
+  int cus = 0;
+  if ((e = device_cus(&cus)) != hipSuccess) return e;
   // Overlapped schedule: segment j's scan (half of the CUs) runs beside
   // segment j+1's prep (the other half), forked from and joined back into
   // the caller's stream.  The first segment's prep has the whole device.
@@ -1366,7 +1459,7 @@ static hipError_t launch_prefill_t(const PrefillPlan& p, const void* q, const vo
     float* carry = S_T ? S_T : reinterpret_cast<float*>(w + p.off_carry);
     const int64_t nseg = (p.max_chunks + p.seg - 1) / p.seg;
     std::lock_guard<std::mutex> lock(ps->mu);
-    e = prep(0, p.seg < p.max_chunks ? p.seg : p.max_chunks, st);
+    e = prep(0, p.seg < p.max_chunks ? p.seg : p.max_chunks, st, cus);
     if (e != hipSuccess) return e;
     if ((e = hipEventRecord(ps->fork, st)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(ps->prep, ps->fork, 0)) != hipSuccess) return e;
@@ -1374,7 +1467,7 @@ static hipError_t launch_prefill_t(const PrefillPlan& p, const void* q, const vo
     for (int64_t j = 0; j < nseg; ++j) {
       const int64_t c0 = j * p.seg, c1 = c0 + p.seg < p.max_chunks ? c0 + p.seg : p.max_chunks;
       if (j > 0) {
-        if ((e = prep(c0, c1 - c0, ps->prep)) != hipSuccess) return e;
+        if ((e = prep(c0, c1 - c0, ps->prep, cus - ps->scan_cus)) != hipSuccess) return e;
         if ((e = hipEventRecord(ps->ready[j], ps->prep)) != hipSuccess) return e;
         if ((e = hipStreamWaitEvent(ps->scan, ps->ready[j], 0)) != hipSuccess) return e;
       }
@@ -1387,7 +1480,7 @@ static hipError_t launch_prefill_t(const PrefillPlan& p, const void* q, const vo
     return hipStreamWaitEvent(st, ps->join, 0);
   }
   if (p.max_chunks > 0) {
-    e = prep(0, p.max_chunks, st);
+    e = prep(0, p.max_chunks, st, cus);
     if (e != hipSuccess) return e;
   }
   // Few (sequence, head) pairs: narrower value tiles to put more CUs on the
