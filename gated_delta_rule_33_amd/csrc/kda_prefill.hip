@@ -279,16 +279,17 @@ struct split;
 template <>
 struct split<bf16_t> {
   static constexpr bool has_lo = true;
-  // hi = x with the low 16 bits cleared (a bf16 by truncation), lo = x - hi
-  // (exact in fp32) rounded to bf16: hi + lo = x to ~2^-16 relative.
+  // hi = x rounded to bf16 (nearest even, so the hi part alone -- as used in
+  // the state update -- carries no bias), lo = x - hi (exact in fp32)
+  // rounded to bf16: hi + lo = x to ~2^-17 relative.  Six VALU per pair.
   __device__ __forceinline__ static void hilo(const f32x4* tiles, int s, bf16x8& hi, bf16x8& lo) {
     uint32_t h[4], l[4];
 #pragma unroll
     for (int j = 0; j < 8; j += 2) {
       const float x0 = tiles[2 * s + (j >> 2)][j & 3], x1 = tiles[2 * s + (j >> 2)][(j & 3) + 1];
-      const uint32_t u0 = __float_as_uint(x0), u1 = __float_as_uint(x1);
-      h[j >> 1] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);  // upper halves of x0 | x1
-      l[j >> 1] = f32x2_to_bf16x2(x0 - __uint_as_float(u0 & 0xFFFF0000u), x1 - __uint_as_float(u1 & 0xFFFF0000u));
+      const uint32_t hp = f32x2_to_bf16x2(x0, x1);
+      h[j >> 1] = hp;
+      l[j >> 1] = f32x2_to_bf16x2(x0 - __uint_as_float(hp << 16), x1 - __uint_as_float(hp & 0xFFFF0000u));
     }
     hi = __builtin_bit_cast(bf16x8, uint4{h[0], h[1], h[2], h[3]});
     lo = __builtin_bit_cast(bf16x8, uint4{l[0], l[1], l[2], l[3]});
