@@ -832,7 +832,9 @@ struct ScanLds {
   static constexpr size_t dx_group = 64 * static_cast<size_t>(C) + sx_group;
   static constexpr bool split = stage_o && dx + (TILE / 16) * dx_group <= 160 * 1024;
   static constexpr int roles = split ? 2 : 1;
-  static constexpr size_t total = dx + (split ? (TILE / 16) * dx_group : 0);
+  // per column group: a 4-byte counter of D hand-overs (state -> output wave)
+  static constexpr size_t xflag = dx + (split ? (TILE / 16) * dx_group : 0);
+  static constexpr size_t total = xflag + (split ? (TILE / 16) * 4 : 0);
 };
 
 template <typename T, int C, int DK, int WAVES>
@@ -985,9 +987,6 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
         late(cc + 1, b ^ 1);
         ostore(cc - 1);
         lds_barrier();  // M(cc): early slot b free
-        // X(cc) (D of chunk cc in LDS) is passed before the next issue, which
-        // can stall on a full memory queue and would hold the barrier up
-        if constexpr (SL::split) lds_barrier();
         early(cc + 2, b);
         wait_vm<NE>();  // all but the early part of chunk cc + 2: chunk cc + 1 resident
         lds_barrier();  // end of chunk cc
@@ -1036,6 +1035,9 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
     ooff[mt] = ((16 * mt + 4 * g + (n & 3)) * H * DV + col - (n & 3)) * static_cast<int>(sizeof(T));
+  if constexpr (SL::split) {
+    if (role == 0 && lane == 0) reinterpret_cast<int*>(smem + SL::xflag)[cg] = 0;  // D hand-over counter
+  }
   if constexpr (SL::NBUF == 2) lds_barrier(); else __syncthreads();  // first chunk resident
 
   // Output tile of a chunk: staged row-major in LDS for the loader waves, or
@@ -1146,6 +1148,7 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
     // D (hi, lo) and the state fragments pass from state to output wave here
     F* const dxp = reinterpret_cast<F*>(smem + SL::dx + cg * SL::dx_group) + lane;
     F* const sxp = dxp + 64 * C / static_cast<int>(sizeof(F));
+    int* const xfl = reinterpret_cast<int*>(smem + SL::xflag) + cg;
     if (do_state) {
       for (int cc = cb; cc < ce; ++cc) {
         const unsigned char* eblk = eblk_of(cc);
@@ -1172,10 +1175,12 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
           dxp[64 * s] = dh[s];
           if (SP::has_lo) dxp[64 * (NSC + s)] = dl[s];
         }
+        // hand D over: the counter is raised once this wave's D writes are done
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt 0
+        if (lane == 0) __hip_atomic_store(xfl, cc - cb + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         RowFrags<T, B::RB_K, NSC> kf[ST];
 #pragma unroll
         for (int st = 0; st < ST; ++st) kf[st].load(lblk, 16 * st + n, g);
-        lds_barrier();  // X: D in LDS
         update_s(lblk, kf, dh);
         chunk_end();
       }
@@ -1202,7 +1207,13 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
         for (int s = 0; s < NSK; ++s) sb[s] = sxp[64 * s];
         f32x4 O[MT];
         rows_x_state(fr, sb, O);
-        lds_barrier();  // X
+        // wait for the state wave's D of this chunk (bounded: the state wave
+        // raises the counter without waiting on this wave)
+        for (int spin = 0; spin < (1 << 26); ++spin) {
+          if (__hip_atomic_load(xfl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) > cc - cb) break;
+          __builtin_amdgcn_s_sleep(1);
+        }
+        asm volatile("" ::: "memory");
         F dh[NSC], dl[NSC];
 #pragma unroll
         for (int s = 0; s < NSC; ++s) {
@@ -1279,6 +1290,33 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
 // ---------------------------------------------------------------------------
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
+// Raise a kernel's dynamic LDS limit once per (kernel, device): the call is
+// slow enough on the host to open gaps between the launches of one call.
+static hipError_t set_lds_limit(const void* fn, size_t bytes) {
+  constexpr int kMaxDev = 64, kMaxFn = 64;
+  static std::mutex mu;
+  static const void* done[kMaxDev][kMaxFn] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  const bool cached = dev >= 0 && dev < kMaxDev;
+  if (cached) {
+    for (int i = 0; i < kMaxFn && done[dev][i]; ++i)
+      if (done[dev][i] == fn) return hipSuccess;
+  }
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
+  if (e == hipSuccess && cached) {
+    for (int i = 0; i < kMaxFn; ++i)
+      if (!done[dev][i]) {
+        done[dev][i] = fn;
+        break;
+      }
+  }
+  return e;
+}
+
+
 // Scan workgroups of the narrow (32-column) configuration.
 static int64_t narrow_scan_wgs(int64_t N, int64_t H, int dv) { return (N * H + 7) / 8 * 8 * (dv / 32); }
 
@@ -1287,7 +1325,7 @@ static int64_t narrow_scan_wgs(int64_t N, int64_t H, int dv) { return (N * H + 7
 // the other half.
 constexpr int64_t kPipeMaxScanWgs = 128;
 constexpr int64_t kPipeMinSeg = 64;    // chunks per segment, at least
-constexpr int64_t kPipeMaxSegs = 16;   // segments, at most
+constexpr int64_t kPipeMaxSegs = 8;    // segments, at most (each launch pair costs ~15-20 us)
 
 static size_t block_bytes(kda_dtype dt, int C, int dk) {
   const size_t es = dt == KDA_BF16 ? 2 : 4;
@@ -1331,8 +1369,7 @@ static hipError_t launch_scan(const PrefillPlan& p, const void* v, const int32_t
                               float* carry = nullptr) {
   typedef ScanLds<T, C, DK, 16 * WAVES> SL;
   static_assert(SL::total <= 160 * 1024, "scan LDS");
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_kernel<T, C, DK, DV, WAVES>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(SL::total));
+  hipError_t e = set_lds_limit(reinterpret_cast<const void*>(&scan_kernel<T, C, DK, DV, WAVES>), SL::total);
   if (e != hipSuccess) return e;
   const int pairs = p.N * p.H;
   const int nsplit = DV / (16 * WAVES);
@@ -1435,8 +1472,7 @@ static hipError_t launch_prefill_t(const PrefillPlan& p, const void* q, const vo
   // Persistent prep: as many workgroups as fit on the CUs the stream may
   // use (LDS-limited), each walking (chunk, head) items.
   auto prep = [&](int64_t cbase, int64_t count, hipStream_t s, int cus) -> hipError_t {
-    hipError_t r = hipFuncSetAttribute(reinterpret_cast<const void*>(&prep_kernel<T, C, DK>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lp));
+    hipError_t r = set_lds_limit(reinterpret_cast<const void*>(&prep_kernel<T, C, DK>), lp);
     if (r != hipSuccess) return r;
     const int64_t per_cu = (160 * 1024) / static_cast<int64_t>(lp) > 0 ? (160 * 1024) / static_cast<int64_t>(lp) : 1;
     const int64_t items = count * p.H;
