@@ -227,34 +227,36 @@ struct Blk {
   static constexpr size_t bytes = (oB + static_cast<size_t>(C) * 4 + 1023) / 1024 * 1024;
 };
 
+// Index helpers work in unsigned arithmetic (every index is non-negative), so
+// divisions and remainders by powers of two stay shifts and masks.
 template <int RB>
-__device__ __forceinline__ int swz(int row) {
-  if constexpr (RB >= 256) return row & 15;
-  else if constexpr (RB == 128) return (row >> 1) & 7;
-  else return (row >> 2) & 3;
+__device__ __forceinline__ unsigned swz(unsigned row) {
+  if constexpr (RB >= 256) return row & 15u;
+  else if constexpr (RB == 128) return (row >> 1) & 7u;
+  else return (row >> 2) & 3u;
 }
 
 template <typename T>
-__device__ __forceinline__ int pcol(int c);
+__device__ __forceinline__ unsigned pcol(unsigned c);
 template <>
-__device__ __forceinline__ int pcol<float>(int c) { return c; }
+__device__ __forceinline__ unsigned pcol<float>(unsigned c) { return c; }
 template <>
-__device__ __forceinline__ int pcol<bf16_t>(int c) {
-  const int k = c & 31;
-  return (c & ~31) | (8 * ((k & 15) >> 2) + 4 * (k >> 4) + (k & 3));
+__device__ __forceinline__ unsigned pcol<bf16_t>(unsigned c) {
+  const unsigned k = c & 31u;
+  return (c & ~31u) | (8u * ((k & 15u) >> 2) + 4u * (k >> 4) + (k & 3u));
 }
 
 // byte offset of element (row, c) in a stored tile with RB-byte rows
 template <typename T, int RB>
-__device__ __forceinline__ int toff(int row, int c) {
-  constexpr int EPG = 16 / static_cast<int>(sizeof(T));
-  const int p = pcol<T>(c);
-  return row * RB + 16 * ((p / EPG) ^ swz<RB>(row)) + (p % EPG) * static_cast<int>(sizeof(T));
+__device__ __forceinline__ unsigned toff(unsigned row, unsigned c) {
+  constexpr unsigned EPG = 16 / sizeof(T);
+  const unsigned p = pcol<T>(c);
+  return row * RB + 16u * ((p / EPG) ^ swz<RB>(row)) + (p % EPG) * static_cast<unsigned>(sizeof(T));
 }
 
 // byte offset of logical 16-byte granule gi of `row`
 template <int RB>
-__device__ __forceinline__ int goff(int row, int gi) { return row * RB + 16 * (gi ^ swz<RB>(row)); }
+__device__ __forceinline__ unsigned goff(unsigned row, unsigned gi) { return row * RB + 16u * (gi ^ swz<RB>(row)); }
 
 // A fragment of a stored tile for the accumulator k map (see accb).
 template <typename T, int RB>
@@ -304,6 +306,26 @@ struct split<float> {
   }
 };
 
+// Four consecutive io elements through a buffer resource (out-of-range
+// offsets are dropped).
+__device__ __forceinline__ void buffer_store4(__amdgpu_buffer_rsrc_t r, int off, f32x4 x, const bf16_t*) {
+  typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+  const u32x2 u = {f32x2_to_bf16x2(x[0], x[1]), f32x2_to_bf16x2(x[2], x[3])};
+  __builtin_amdgcn_raw_buffer_store_b64(u, r, off, 0, 0);
+}
+__device__ __forceinline__ void buffer_store4(__amdgpu_buffer_rsrc_t r, int off, f32x4 x, const float*) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, off, 0, 0);
+}
+
+// Four consecutive io elements already in io format (bf16 bits or fp32).
+__device__ __forceinline__ void buffer_store_raw4(__amdgpu_buffer_rsrc_t r, int off, uint2 x) {
+  typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{x.x, x.y}, r, off, 0, 0);
+}
+__device__ __forceinline__ void buffer_store_raw4(__amdgpu_buffer_rsrc_t r, int off, f32x4 x) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, off, 0, 0);
+}
+
 // ---------------------------------------------------------------------------
 // Prep kernel: one workgroup (kPrepThreads threads) per (chunk, head).  The grid's x
 // index is the head, so the workgroups that run together cover whole token
@@ -347,9 +369,9 @@ struct PrepLds {
 // byte offset of element (row, c) in an unpadded LDS tile with RB-byte rows,
 // 16-byte granules XOR-swizzled by row (conflict-free 16-row fragment reads)
 template <typename T, int RB>
-__device__ __forceinline__ int loff(int row, int c) {
-  constexpr int EPG = 16 / static_cast<int>(sizeof(T));
-  return row * RB + 16 * ((c / EPG) ^ swz<RB>(row)) + (c % EPG) * static_cast<int>(sizeof(T));
+__device__ __forceinline__ unsigned loff(unsigned row, unsigned c) {
+  constexpr unsigned EPG = 16 / sizeof(T);
+  return row * RB + 16u * ((c / EPG) ^ swz<RB>(row)) + (c % EPG) * static_cast<unsigned>(sizeof(T));
 }
 
 // natural-map fragments (slot (g, j) <-> k = k0 + 8 g + j for bf16, k0 + g for fp32)
@@ -417,7 +439,6 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
   typedef mma16<T> M;
   typedef mma16<float> MF;
   constexpr int NB = L::NB;
-  constexpr int NCG = DK / 4;      // channel groups of 4
   constexpr int RPT = C / L::NRB;  // rows per thread
   static_assert(RPT >= 1 && 16 % RPT == 0, "row blocks must tile 16-row sub-blocks");
   extern __shared__ __align__(16) unsigned char smem[];
@@ -430,17 +451,12 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
   float* gB = reinterpret_cast<float*>(smem + L::o2);
   float* gM = gB + NB * DK;
   float* gE = gM + NB * DK;
-  float* part = reinterpret_cast<float*>(smem + L::o1);
   T* Ps = reinterpret_cast<T*>(smem + L::o2);
   float* fv = reinterpret_cast<float*>(smem + L::o3);
   float* bet = reinterpret_cast<float*>(smem + L::o4);
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int n = lane & 15, g = lane >> 4;
   // thread owns channels c4..c4+3 of rows r0..r0+RPT-1 in the elementwise steps
-  const int cg = tid % NCG, rbk = tid / NCG;
-  const int c4 = 4 * cg, r0 = rbk * RPT;
+  constexpr int NCG = DK / 4;  // channel groups of 4
 
   // Persistent: the workgroup walks items (chunk c = cbase + i / H, head
   // h = i % H) with stride gridDim.x, loading the next item's inputs into
@@ -474,15 +490,19 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
   // their log_alpha is zeroed and beta = 0 masks them everywhere else.
   auto fetch = [&](const Item& it, Raw& r) {
     if (it.c >= total) return;
+    // thread indices from a zero the compiler cannot see (len <= C): they
+    // are recomputed here rather than held in registers across the item loop
+    const int t = static_cast<int>(threadIdx.x) + (it.len >> 30);
+    const int fr0 = (t / NCG) * RPT, fc4 = 4 * (t % NCG);
     const size_t tbase = (static_cast<size_t>(it.t0) * H + it.h) * DK;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      const int e = min(r0 + i, it.len - 1) * H * DK + c4;  // < C H DK: 32-bit
+      const int e = min(fr0 + i, it.len - 1) * H * DK + fc4;  // < C H DK: 32-bit
       r.lg[i] = *reinterpret_cast<const f32x4*>(la + tbase + e);
       r.kr[i] = load4raw(k + tbase + e);
       r.qr[i] = load4raw(q + tbase + e);
     }
-    r.bt = (tid < C && tid < it.len) ? beta[static_cast<size_t>(it.t0 + tid) * H + it.h] : 0.f;
+    r.bt = (t < C && t < it.len) ? beta[static_cast<size_t>(it.t0 + t) * H + it.h] : 0.f;
   };
   int item = blockIdx.x;
   Item it = locate(item);
@@ -492,22 +512,23 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
     const Item nit = locate(item + gridDim.x);
     Raw nxt;
     const int c = it.c, h = it.h, t0 = it.t0, len = it.len;
-    // Per-thread index math is redone per item (an opaque zero keeps the
-    // compiler from hoisting it out of the loop, where it would hold
-    // registers across every item).
-    int vz;
-    asm volatile("v_mov_b32 %0, 0" : "=v"(vz));
-    const int tid = static_cast<int>(threadIdx.x) + vz;
+    // Per-thread index math is redone per item (a zero the compiler cannot
+    // see, len <= C, keeps it from hoisting the math out of the loop, where
+    // it would hold registers across every item).
+    const int tid = static_cast<int>(threadIdx.x) + (len >> 30);
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, g = lane >> 4;
     const int cg = tid % NCG, rbk = tid / NCG;
     const int c4 = 4 * cg, r0 = rbk * RPT;
     if (it.c < total) {
   unsigned char* blk = ws + (static_cast<size_t>(c) * H + h) * B::bytes;
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(blk, 0, static_cast<int>(B::bytes), 0x00020000);
+  // Gates in base 2: g2 = log2(e) * g, so every factor is one v_exp_f32.
+  constexpr float kLog2e = 1.4426950408889634f;
   f32x4 lg[RPT], kv[RPT], qv[RPT];
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
-    lg[i] = r0 + i < len ? cur.lg[i] : f32x4{0.f, 0.f, 0.f, 0.f};
+    lg[i] = r0 + i < len ? cur.lg[i] * kLog2e : f32x4{0.f, 0.f, 0.f, 0.f};
     kv[i] = cvt4(cur.kr[i]);
     qv[i] = cvt4(cur.qr[i]);
   }
@@ -515,11 +536,13 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
   (void)t0;
 
   // ---- a2: chunk-local inclusive cumsum of log_alpha ----------------------
+  // inside the thread's rows, then across the row blocks of its channel group
 #pragma unroll
   for (int i = 1; i < RPT; ++i) lg[i] += lg[i - 1];
-  *reinterpret_cast<f32x4*>(part + rbk * DK + c4) = lg[RPT - 1];
-  __syncthreads();
   {
+    float* part = reinterpret_cast<float*>(smem + L::o1);
+    *reinterpret_cast<f32x4*>(part + rbk * DK + c4) = lg[RPT - 1];
+    __syncthreads();
     f32x4 off = {0.f, 0.f, 0.f, 0.f};
     for (int pp = 0; pp < rbk; ++pp) off += *reinterpret_cast<const f32x4*>(part + pp * DK + c4);
 #pragma unroll
@@ -535,13 +558,14 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
 
   // ---- block-pair vectors e^{g_{m_I} - g_{e_J}}, J <= I ---------------------
   for (int idx = tid; idx < L::NLB * DK; idx += kPrepThreads) {
-    const int pp = idx / DK, ch = idx % DK;
-    int I = 0;
-    while ((I + 1) * (I + 2) / 2 <= pp) ++I;
-    const int J = pp - I * (I + 1) / 2;
-    fv[idx] = __expf(gM[I * DK + ch] - gE[J * DK + ch]);
+    const unsigned pp = static_cast<unsigned>(idx) / DK, ch = static_cast<unsigned>(idx) % DK;
+    unsigned I = 0;
+#pragma unroll
+    for (unsigned t = 1; t < static_cast<unsigned>(NB); ++t) I += pp >= t * (t + 1) / 2 ? 1u : 0u;
+    const unsigned J = pp - I * (I + 1) / 2;
+    fv[idx] = __builtin_amdgcn_exp2f(gM[I * DK + ch] - gE[J * DK + ch]);
   }
-  if (tid < DK) reinterpret_cast<float*>(blk + B::oG)[tid] = __expf(gE[(NB - 1) * DK + tid]);
+  if (tid < DK) reinterpret_cast<float*>(blk + B::oG)[tid] = __builtin_amdgcn_exp2f(gE[(NB - 1) * DK + tid]);
   if (tid < C) reinterpret_cast<float*>(blk + B::oB)[tid] = bet[tid];
 
   // ---- element factors, S-independent outputs ---------------------------
@@ -552,29 +576,34 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
     const f32x4 ge = *reinterpret_cast<const f32x4*>(gE + I * DK + c4);
     const f32x4 gz = *reinterpret_cast<const f32x4*>(gE + (NB - 1) * DK + c4);
     f32x4 drv, ebv, eev, kb[RPT];
+    float bt[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) bt[i] = bet[r0 + i];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      drv[j] = __expf(gb[j] - gm[j]);  // e^{g_b - g_m}: >= 1, at most 8 tokens of decay
-      ebv[j] = __expf(gb[j]);          // e^{g_b} <= 1
-      eev[j] = __expf(gz[j] - ge[j]);  // e^{g_last - g_e} <= 1
+      drv[j] = __builtin_amdgcn_exp2f(gb[j] - gm[j]);  // e^{g_b - g_m}: >= 1, at most 8 tokens of decay
+      ebv[j] = __builtin_amdgcn_exp2f(gb[j]);          // e^{g_b} <= 1
+      eev[j] = __builtin_amdgcn_exp2f(gz[j] - ge[j]);  // e^{g_last - g_e} <= 1
     }
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      const int r = r0 + i;
+      const unsigned r = static_cast<unsigned>(r0 + i);
       f32x4 fr, fc;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        fr[j] = __expf(lg[i][j] - gb[j]);  // e^{g_r - g_b} <= 1
-        fc[j] = __expf(ge[j] - lg[i][j]);  // e^{g_e - g_r} <= 1
+        fr[j] = __builtin_amdgcn_exp2f(lg[i][j] - gb[j]);  // e^{g_r - g_b} <= 1
+        fc[j] = __builtin_amdgcn_exp2f(ge[j] - lg[i][j]);  // e^{g_e - g_r} <= 1
       }
       const f32x4 frd = fr * drv;  // e^{g_r - g_m}
       const f32x4 fre = fr * ebv;  // e^{g_r}
-      store4(reinterpret_cast<T*>(Krd + loff<T, L::RBK>(r, c4)), kv[i] * frd);
-      store4(reinterpret_cast<T*>(Qrd + loff<T, L::RBK>(r, c4)), qv[i] * frd);
+      const unsigned lo = loff<T, L::RBK>(r, static_cast<unsigned>(c4));
+      store4(reinterpret_cast<T*>(Krd + lo), kv[i] * frd);
+      store4(reinterpret_cast<T*>(Qrd + lo), qv[i] * frd);
       const f32x4 kc = kv[i] * fc;
-      store4(reinterpret_cast<T*>(Kc + loff<T, L::RBK>(r, c4)), kc);
-      store4(reinterpret_cast<T*>(blk + B::oQ + toff<T, B::RB_R>(r, c4)), qv[i] * fre);
-      store4(reinterpret_cast<T*>(blk + B::oR + toff<T, B::RB_R>(r, c4)), bet[r] * (kv[i] * fre));
+      store4(reinterpret_cast<T*>(Kc + lo), kc);
+      const int to = static_cast<int>(toff<T, B::RB_R>(r, static_cast<unsigned>(c4)));
+      buffer_store4(wr, static_cast<int>(B::oQ) + to, qv[i] * fre, static_cast<T*>(nullptr));
+      buffer_store4(wr, static_cast<int>(B::oR) + to, bt[i] * (kv[i] * fre), static_cast<T*>(nullptr));
       kb[i] = kc * eev;  // e^{g_last - g_r} k_r
     }
     // Kb^T tile (rows = key channel): this thread's rows are consecutive, so
@@ -585,7 +614,7 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
 #pragma unroll
         for (int i4 = 0; i4 < RPT; i4 += 4) {
           const f32x4 x4 = {kb[i4][j], kb[i4 + 1][j], kb[i4 + 2][j], kb[i4 + 3][j]};
-          store4(reinterpret_cast<T*>(blk + B::oK + toff<T, B::RB_K>(c4 + j, r0 + i4)), x4);
+          buffer_store4(wr, static_cast<int>(B::oK + toff<T, B::RB_K>(c4 + j, r0 + i4)), x4, static_cast<T*>(nullptr));
         }
       } else {
 #pragma unroll
@@ -627,14 +656,12 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
     }
   }
   __syncthreads();
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(blk, 0, static_cast<int>(B::bytes), 0x00020000);
   for (int idx = tid; idx < C * C / 4; idx += kPrepThreads) {
-    const int r = idx / (C / 4), c4b = (idx % (C / 4)) * 4;
-    f32x4 x = {0.f, 0.f, 0.f, 0.f};
-    if ((c4b >> 4) <= (r >> 4)) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) x[j] = lds_get<T>(Ps + r * L::CP + c4b + j);
-    }
-    store4(reinterpret_cast<T*>(blk + B::oP + toff<T, B::RB_K>(r, c4b)), x);
+    const unsigned r = static_cast<unsigned>(idx) / (C / 4), c4b = (static_cast<unsigned>(idx) % (C / 4)) * 4;
+    typename raw4<T>::type x = {};
+    if ((c4b >> 4) <= (r >> 4)) x = *reinterpret_cast<const typename raw4<T>::type*>(Ps + r * L::CP + c4b);
+    buffer_store_raw4(wr, static_cast<int>(B::oP + toff<T, B::RB_K>(r, c4b)), x);
   }
 
   // ---- a4: T = (I + A)^{-1} ----------------------------------------------
@@ -687,13 +714,13 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
     __syncthreads();
   }
   for (int idx = tid; idx < C * C / 4; idx += kPrepThreads) {
-    const int r = idx / (C / 4), c4b = (idx % (C / 4)) * 4;
+    const unsigned r = static_cast<unsigned>(idx) / (C / 4), c4b = (static_cast<unsigned>(idx) % (C / 4)) * 4;
     f32x4 x = {0.f, 0.f, 0.f, 0.f};
     if ((c4b >> 4) <= (r >> 4)) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) x[j] = Ti[r * L::AP + c4b + j];
     }
-    store4(reinterpret_cast<T*>(blk + B::oT + toff<T, B::RB_K>(r, c4b)), x);
+    buffer_store4(wr, static_cast<int>(B::oT + toff<T, B::RB_K>(r, c4b)), x, static_cast<T*>(nullptr));
   }
     }  // item
     __syncthreads();  // LDS is reused by the next item
@@ -781,17 +808,6 @@ __device__ __forceinline__ void lds_put1(unsigned char* p, float x, const bf16_t
 }
 __device__ __forceinline__ void lds_put1(unsigned char* p, float x, const float*) {
   *reinterpret_cast<float*>(p) = x;
-}
-
-// Four consecutive io elements through a buffer resource (out-of-range
-// offsets are dropped).
-__device__ __forceinline__ void buffer_store4(__amdgpu_buffer_rsrc_t r, int off, f32x4 x, const bf16_t*) {
-  typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
-  const u32x2 u = {f32x2_to_bf16x2(x[0], x[1]), f32x2_to_bf16x2(x[2], x[3])};
-  __builtin_amdgcn_raw_buffer_store_b64(u, r, off, 0, 0);
-}
-__device__ __forceinline__ void buffer_store4(__amdgpu_buffer_rsrc_t r, int off, f32x4 x, const float*) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, off, 0, 0);
 }
 
 // Workgroup barrier that waits only for this wave's LDS traffic (lgkmcnt 0),
