@@ -163,3 +163,15 @@ def test_segmented_schedule(dt, chunk, mode):
     check("o", o, o_ref, TOL[dt])
     if S is not None:
         check("S_T", S, S_ref, TOL[dt])
+
+
+def test_segmented_schedule_many_segments():
+    """674 chunks over 4 sequences x 2 heads: eight segments, with sequences
+    (one of 3 tokens) straddling the boundaries."""
+    lengths = [20000, 9000, 3, 14000]
+    log("prefill segmented, growing segments: %s x 2 heads" % lengths)
+    w = synth.make_prefill(lengths, H=2, dk=128, dv=128, io_dtype="bf16", seed=23, S0_std=0.05)
+    o, S = gpu_prefill(w)
+    o_ref, S_ref = oracle_prefill(w)
+    check("o", o, o_ref, TOL["bf16"])
+    check("S_T", S, S_ref, TOL["bf16"])
