@@ -850,7 +850,9 @@ struct ScanLds {
   static constexpr int roles = split ? 2 : 1;
   // per column group: a 4-byte counter of D hand-overs (state -> output wave)
   static constexpr size_t xflag = dx + (split ? (TILE / 16) * dx_group : 0);
-  static constexpr size_t total = xflag + (split ? (TILE / 16) * 4 : 0);
+  // 256 bytes that the loader waves' L2 prefetches land in (never read)
+  static constexpr size_t pfsink = xflag + (split ? (TILE / 16) * 4 : 0);
+  static constexpr size_t total = pfsink + (NBUF == 2 ? 256 : 0);
 };
 
 template <typename T, int C, int DK, int WAVES>
@@ -945,8 +947,23 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
         lds_barrier();
         return;
       }
-      auto blk_src = [&](int cc) {
-        return ws + (static_cast<size_t>(c0 + min(cc, ce - 1)) * H + h) * B::bytes + lane * 16;
+      auto blk_base = [&](int cc) { return ws + (static_cast<size_t>(c0 + min(cc, ce - 1)) * H + h) * B::bytes; };
+      auto blk_src = [&](int cc) { return blk_base(cc) + lane * 16; };
+      // L2 prefetch of a chunk's block two chunks before its loads: the
+      // value tiles of a (sequence, head) share their XCD's L2, so tile t
+      // touches a quarter of the block's 128-byte lines, one 4-byte
+      // direct-to-LDS load per lane into a sink nobody reads.
+      constexpr int LINES = static_cast<int>(B::bytes / 128);
+      constexpr int LPT = (LINES + NSPLIT - 1) / NSPLIT;                       // lines per tile
+      constexpr int NPF = (LPT + 64 * kLoaderWaves - 1) / (64 * kLoaderWaves);  // loads per loader wave
+      auto prefetch = [&](int cc) {
+        const unsigned char* base = blk_base(cc);
+#pragma unroll
+        for (int m = 0; m < NPF; ++m) {
+          const int line = min(tile * LPT + min((lw + kLoaderWaves * m) * 64 + lane, LPT - 1), LINES - 1);
+          __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(base + line * 128),
+                                           (__attribute__((address_space(3))) void*)(smem + SL::pfsink), 4, 0, 0);
+        }
       };
       auto early = [&](int cc, int slot) {
         const unsigned char* src = blk_src(cc);
@@ -1004,7 +1021,8 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
         ostore(cc - 1);
         lds_barrier();  // M(cc): early slot b free
         early(cc + 2, b);
-        wait_vm<NE>();  // all but the early part of chunk cc + 2: chunk cc + 1 resident
+        prefetch(cc + 3);
+        wait_vm<NE + NPF>();  // all but the early part of chunk cc + 2 and the prefetch: chunk cc + 1 resident
         lds_barrier();  // end of chunk cc
       }
       ostore(ce - 1);
