@@ -21,7 +21,7 @@ struct PrefillPlan {
   int sort;            // 1: longest-first order is computed on the device
   // byte offsets inside the workspace
   size_t off_chunk_off, off_order, off_blocks;
-  size_t off_carry;  // state hand-over between segment launches (0: none)
+  size_t off_ready;  // segment counter of the overlapped schedule (0: none)
   size_t total_bytes;
   // Segment length in global chunk indices for the overlapped two-stream
   // schedule (0: one prep launch, then one scan launch).

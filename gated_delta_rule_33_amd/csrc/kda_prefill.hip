@@ -157,9 +157,11 @@ struct accb<float> {
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void chunk_offsets_kernel(const int32_t* __restrict__ cu, int N, int C,
                                                              int32_t* __restrict__ chunk_off,
-                                                             int32_t* __restrict__ order, int sort) {
+                                                             int32_t* __restrict__ order, int sort,
+                                                             int32_t* __restrict__ ready) {
   __shared__ int32_t part[1024];
   const int tid = threadIdx.x;
+  if (tid == 0 && ready) *ready = 0;  // segment counter of the overlapped schedule
   const int per = (N + 1023) / 1024;
   const int b = min(N, tid * per), e = min(N, b + per);
   int s = 0;
@@ -191,6 +193,13 @@ __global__ __launch_bounds__(1024) void chunk_offsets_kernel(const int32_t* __re
       order[i] = i;
     }
   }
+}
+
+// Overlapped schedule: segments 0 .. j of the workspace blocks are written.
+// Launched on the prep stream after segment j's prep, so the prep's writes
+// are complete and visible before the counter moves.
+__global__ void ready_kernel(int32_t* ready, int j) {
+  if (threadIdx.x == 0) __hip_atomic_store(ready, j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
@@ -864,7 +873,7 @@ template <typename T, int C, int DK, int DV, int WAVES>
 __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel(
     const T* __restrict__ v, const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_off,
     const int32_t* __restrict__ order, int N, int H, const unsigned char* __restrict__ ws, const float* S0,
-    T* __restrict__ o, float* S_T, int gbeg, int gend, float* carry) {
+    T* __restrict__ o, float* S_T, const int* ready, int seg) {
   typedef Blk<T, C, DK> B;
   typedef mma16<T> M;
   typedef accb<T> AB;
@@ -899,19 +908,35 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
   const int tbeg = cu[seq], L_seq = cu[seq + 1] - tbeg;
   const int c0 = chunk_off[seq];
   const int nch = (L_seq + C - 1) / C;
-  // This launch covers global chunk indices [gbeg, gend): local chunks
-  // [cb, ce) of this sequence.  The state enters from S0 at the sequence's
-  // first chunk, else from carry (left there by the launch before), and
-  // leaves to S_T after its last chunk, else to carry.  An empty sequence
-  // is handled by the launch that starts at global chunk 0.
-  const int cb = max(0, gbeg - c0), ce = min(nch, gend - c0);
-  if (nch == 0 ? gbeg != 0 : cb >= ce) return;
-  const float* s_in = cb == 0 ? S0 : carry;
-  float* s_out = ce == nch ? S_T : carry;
+  // The whole sequence, chunks [cb, ce).  When `ready` is given, the blocks
+  // of global chunks [j seg, (j + 1) seg) exist once *ready >= j (segment 0
+  // from the start): the loader waves wait for that before they touch them.
+  const int cb = 0, ce = nch;
+  const float* s_in = S0;
+  float* s_out = S_T;
+
+  // Loader waves: segments written so far, as last read (wave-uniform),
+  // polled with device-scope loads before a block is touched.  The wait is
+  // bounded (~2^20 polls of ~500 cycles); a wave that runs out stops waiting
+  // for the rest of the launch, so a stalled producer cannot hold the GPU.
+  int seen = 0;
+  bool patient = true;
+  auto seg_of = [&](int cc) { return (c0 + min(cc, ce - 1)) / seg; };
+  auto ensure = [&](int cc) {
+    if (!ready || !patient) return;
+    const int need = seg_of(cc);
+    int spin = 0;
+    for (; seen < need && spin < (1 << 20); ++spin) {
+      seen = __builtin_amdgcn_readfirstlane(__hip_atomic_load(ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      if (seen < need) __builtin_amdgcn_s_sleep(8);
+    }
+    if (seen < need) patient = false;
+  };
 
   // Single-slot scheme (NBUF = 1): the whole block of chunk cc and its v
   // tile, one chunk ahead.
   auto issue = [&](int cc) {
+    ensure(cc);
     const int lw = wave - CW;
     const unsigned char* src = ws + (static_cast<size_t>(c0 + cc) * H + h) * B::bytes;
     for (int j = lw; j < NG; j += kLoaderWaves) lds_load16(src + j * 1024 + lane * 16, smem + j * 1024);
@@ -957,6 +982,7 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
       constexpr int LPT = (LINES + NSPLIT - 1) / NSPLIT;                       // lines per tile
       constexpr int NPF = (LPT + 64 * kLoaderWaves - 1) / (64 * kLoaderWaves);  // loads per loader wave
       auto prefetch = [&](int cc) {
+        if (ready && seg_of(cc) > seen) return;  // not written yet: touching it would cache stale lines
         const unsigned char* base = blk_base(cc);
 #pragma unroll
         for (int m = 0; m < NPF; ++m) {
@@ -1010,6 +1036,7 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
           }
         }
       };
+      ensure(cb + 1);
       early(cb, 0);
       late(cb, 0);
       early(cb + 1, 1);
@@ -1017,9 +1044,11 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
       lds_barrier();
       for (int cc = cb; cc < ce; ++cc) {
         const int b = (cc - cb) & 1;
+        ensure(cc + 1);
         late(cc + 1, b ^ 1);
         ostore(cc - 1);
         lds_barrier();  // M(cc): early slot b free
+        ensure(cc + 2);
         early(cc + 2, b);
         prefetch(cc + 3);
         wait_vm<NE + NPF>();  // all but the early part of chunk cc + 2 and the prefetch: chunk cc + 1 resident
@@ -1359,7 +1388,7 @@ static int64_t narrow_scan_wgs(int64_t N, int64_t H, int dv) { return (N * H + 7
 // the other half.
 constexpr int64_t kPipeMaxScanWgs = 128;
 constexpr int64_t kPipeMinSeg = 64;    // chunks per segment, at least
-constexpr int64_t kPipeMaxSegs = 8;    // segments, at most (each launch pair costs ~15-20 us)
+constexpr int64_t kPipeMaxSegs = 16;   // segments, at most (each adds a prep launch beside the scan)
 
 static size_t block_bytes(kda_dtype dt, int C, int dk) {
   const size_t es = dt == KDA_BF16 ? 2 : 4;
@@ -1385,12 +1414,12 @@ bool make_prefill_plan(const kda_prefill_desc* d, int64_t max_chunks, PrefillPla
   p->off_blocks = off;    off += slots * block_bytes(d->io_dtype, d->chunk, d->dk);
   off = align256(off);
   p->seg = 0;
-  p->off_carry = 0;
+  p->off_ready = 0;
   if (narrow_scan_wgs(d->num_seqs, d->num_heads, d->dv) <= kPipeMaxScanWgs && max_chunks >= 2 * kPipeMinSeg) {
     const int64_t seg = (max_chunks + kPipeMaxSegs - 1) / kPipeMaxSegs;
     p->seg = seg > kPipeMinSeg ? seg : kPipeMinSeg;
-    p->off_carry = off;
-    off += static_cast<size_t>(d->num_seqs) * d->num_heads * d->dk * d->dv * 4;
+    p->off_ready = off;
+    off += 256;
   }
   p->total_bytes = align256(off);
   return true;
@@ -1399,8 +1428,7 @@ bool make_prefill_plan(const kda_prefill_desc* d, int64_t max_chunks, PrefillPla
 template <typename T, int C, int DK, int DV, int WAVES>
 static hipError_t launch_scan(const PrefillPlan& p, const void* v, const int32_t* cu, const int32_t* chunk_off,
                               const int32_t* order, const unsigned char* blocks, const float* S0, void* o,
-                              float* S_T, hipStream_t st, int gbeg = 0, int gend = 0x7fffffff,
-                              float* carry = nullptr) {
+                              float* S_T, hipStream_t st, const int* ready = nullptr, int seg = 1) {
   typedef ScanLds<T, C, DK, 16 * WAVES> SL;
   static_assert(SL::total <= 160 * 1024, "scan LDS");
   hipError_t e = set_lds_limit(reinterpret_cast<const void*>(&scan_kernel<T, C, DK, DV, WAVES>), SL::total);
@@ -1410,7 +1438,7 @@ static hipError_t launch_scan(const PrefillPlan& p, const void* v, const int32_t
   const unsigned grid = static_cast<unsigned>((pairs + 7) / 8 * 8 * nsplit);
   hipLaunchKernelGGL((scan_kernel<T, C, DK, DV, WAVES>), dim3(grid), dim3(scan_threads<T, C, DK, WAVES>()), SL::total, st,
                      static_cast<const T*>(v), cu, chunk_off, order, p.N, p.H, blocks, S0, static_cast<T*>(o), S_T,
-                     gbeg, gend, carry);
+                     ready, seg);
   return hipGetLastError();
 }
 
@@ -1437,7 +1465,7 @@ static hipError_t device_cus(int* cus) {
 // the overlapped schedule; created on first use and kept for the process.
 struct PipeStreams {
   hipStream_t prep = nullptr, scan = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr, ready[kPipeMaxSegs] = {};
+  hipEvent_t fork = nullptr, join = nullptr, join_prep = nullptr;
   int scan_cus = 0;
   std::mutex mu;  // one schedule at a time may use the shared streams/events
 };
@@ -1475,8 +1503,7 @@ static hipError_t pipe_streams(int64_t scan_wgs, PipeStreams** out) {
               hipExtStreamCreateWithCUMask(&ps->prep, words, mp.data()) == hipSuccess &&
               hipEventCreateWithFlags(&ps->fork, hipEventDisableTiming) == hipSuccess &&
               hipEventCreateWithFlags(&ps->join, hipEventDisableTiming) == hipSuccess;
-    for (int j = 0; ok && j < kPipeMaxSegs; ++j)
-      ok = hipEventCreateWithFlags(&ps->ready[j], hipEventDisableTiming) == hipSuccess;
+    ok = ok && hipEventCreateWithFlags(&ps->join_prep, hipEventDisableTiming) == hipSuccess;
     if (ok) {
       ps->scan_cus = ns;
       cache[dev] = ps;
@@ -1498,7 +1525,8 @@ static hipError_t launch_prefill_t(const PrefillPlan& p, const void* q, const vo
   int32_t* order = reinterpret_cast<int32_t*>(w + p.off_order);
   unsigned char* blocks = w + p.off_blocks;
   if (p.N == 0) return hipSuccess;
-  hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(1024), 0, st, cu, p.N, C, chunk_off, order, p.sort);
+  int32_t* ready = p.seg > 0 ? reinterpret_cast<int32_t*>(w + p.off_ready) : nullptr;
+  hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(1024), 0, st, cu, p.N, C, chunk_off, order, p.sort, ready);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t lp = PrepLds<T, C, DK>::total;
@@ -1518,16 +1546,17 @@ static hipError_t launch_prefill_t(const PrefillPlan& p, const void* q, const vo
   };
   int cus = 0;
   if ((e = device_cus(&cus)) != hipSuccess) return e;
-  // Overlapped schedule: segment j's scan (half of the CUs) runs beside
-  // segment j+1's prep (the other half), forked from and joined back into
-  // the caller's stream.  The first segment's prep has the whole device.
+  // Overlapped schedule: one scan launch (half of the CUs) walks every
+  // chunk while the prep of segments 1, 2, ... runs beside it (the other
+  // half), each followed by a bump of the ready counter that the scan's
+  // loader waves wait on; both streams fork from and join back into the
+  // caller's stream.  Segment 0's prep has the whole device.
   PipeStreams* ps = nullptr;
   if (p.seg > 0) {
     e = pipe_streams(narrow_scan_wgs(p.N, p.H, DV), &ps);
     if (e != hipSuccess) return e;
   }
   if (ps) {
-    float* carry = S_T ? S_T : reinterpret_cast<float*>(w + p.off_carry);
     const int64_t nseg = (p.max_chunks + p.seg - 1) / p.seg;
     std::lock_guard<std::mutex> lock(ps->mu);
     e = prep(0, p.seg < p.max_chunks ? p.seg : p.max_chunks, st, cus);
@@ -1535,20 +1564,19 @@ static hipError_t launch_prefill_t(const PrefillPlan& p, const void* q, const vo
     if ((e = hipEventRecord(ps->fork, st)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(ps->prep, ps->fork, 0)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(ps->scan, ps->fork, 0)) != hipSuccess) return e;
-    for (int64_t j = 0; j < nseg; ++j) {
+    e = launch_scan<T, C, DK, DV, 2>(p, v, cu, chunk_off, order, blocks, S0, o, S_T, ps->scan, ready,
+                                     static_cast<int>(p.seg));
+    if (e != hipSuccess) return e;
+    for (int64_t j = 1; j < nseg; ++j) {
       const int64_t c0 = j * p.seg, c1 = c0 + p.seg < p.max_chunks ? c0 + p.seg : p.max_chunks;
-      if (j > 0) {
-        if ((e = prep(c0, c1 - c0, ps->prep, cus - ps->scan_cus)) != hipSuccess) return e;
-        if ((e = hipEventRecord(ps->ready[j], ps->prep)) != hipSuccess) return e;
-        if ((e = hipStreamWaitEvent(ps->scan, ps->ready[j], 0)) != hipSuccess) return e;
-      }
-      e = launch_scan<T, C, DK, DV, 2>(p, v, cu, chunk_off, order, blocks, S0, o, S_T, ps->scan,
-                                       static_cast<int>(c0), j + 1 == nseg ? 0x7fffffff : static_cast<int>(c1),
-                                       carry);
-      if (e != hipSuccess) return e;
+      if ((e = prep(c0, c1 - c0, ps->prep, cus - ps->scan_cus)) != hipSuccess) return e;
+      hipLaunchKernelGGL(ready_kernel, dim3(1), dim3(64), 0, ps->prep, ready, static_cast<int>(j));
+      if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if ((e = hipEventRecord(ps->join, ps->scan)) != hipSuccess) return e;
-    return hipStreamWaitEvent(st, ps->join, 0);
+    if ((e = hipEventRecord(ps->join_prep, ps->prep)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(st, ps->join, 0)) != hipSuccess) return e;
+    return hipStreamWaitEvent(st, ps->join_prep, 0);
   }
   if (p.max_chunks > 0) {
     e = prep(0, p.max_chunks, st, cus);
