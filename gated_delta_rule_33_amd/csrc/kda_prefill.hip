@@ -40,6 +40,8 @@
 
 #include <hip/hip_ext.h>
 
+#include <cstdlib>
+#include <cstring>
 #include <mutex>
 #include <vector>
 
@@ -1472,12 +1474,25 @@ struct PipeStreams {
 
 // Returns in *out the current device's streams when the scan (scan_wgs
 // workgroups) fits on its half of the CUs, else nullptr.
+// The overlapped schedule needs the scan and the prep kernels of one call
+// to run at the same time; a tool that serialises dispatches (hardware
+// counter collection) must turn it off: KDA_PREFILL_OVERLAP=0 selects the
+// one-stream schedule (same kernels, same bytes moved).
+static bool overlap_enabled() {
+  static const bool on = [] {
+    const char* v = std::getenv("KDA_PREFILL_OVERLAP");
+    return !(v && std::strcmp(v, "0") == 0);
+  }();
+  return on;
+}
+
 static hipError_t pipe_streams(int64_t scan_wgs, PipeStreams** out) {
   constexpr int kMaxDev = 64;
   static std::mutex mu;
   static PipeStreams* cache[kMaxDev] = {};
   static bool unavailable[kMaxDev] = {};
   *out = nullptr;
+  if (!overlap_enabled()) return hipSuccess;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
