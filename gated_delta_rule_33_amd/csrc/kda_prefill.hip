@@ -984,7 +984,11 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
       constexpr int LPT = (LINES + NSPLIT - 1) / NSPLIT;                       // lines per tile
       constexpr int NPF = (LPT + 64 * kLoaderWaves - 1) / (64 * kLoaderWaves);  // loads per loader wave
       auto prefetch = [&](int cc) {
-        if (ready && seg_of(cc) > seen) return;  // not written yet: touching it would cache stale lines
+        // A block not written yet must not be touched (its lines would be
+        // cached stale): then the last chunk of the newest written segment
+        // is touched instead, so every call issues exactly NPF loads and the
+        // loader's vmcnt bounds hold.
+        if (ready && seg_of(cc) > seen) cc = (seen + 1) * seg - 1 - c0;
         const unsigned char* base = blk_base(cc);
 #pragma unroll
         for (int m = 0; m < NPF; ++m) {
