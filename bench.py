@@ -68,12 +68,18 @@ def prefill_algorithmic(T_tok: int, N: int, H: int, dk: int, dv: int, es: int, C
     beta (fp32); write o (dv, io dtype); write S_T (and read S0 when given).
     Flops per token-head: 2 [ (C/2)(3 dk + 2 dv) + 3 dk dv ] -- the two gated
     intra-chunk matrices, the WY factors and the three state contractions,
-    triangular products counted at half."""
+    triangular products counted at half.  The dense-tile count (as the
+    matrix cores execute the triangular products, at full size) is
+    2 [ C (3 dk + 2 dv) + 3 dk dv ]."""
     th = T_tok * H
     per_th = (2 * dk + dv) * es + dk * 4 + 4 + dv * es
     state = N * H * dk * dv * 4 * (2 if with_s0 else 1)
     flops_th = 2 * ((C // 2) * (3 * dk + 2 * dv) + 3 * dk * dv)
     return th * per_th + state, th * flops_th, per_th, flops_th
+
+
+def prefill_dense_flops_th(dk: int, dv: int, C: int) -> int:
+    return 2 * (C * (3 * dk + 2 * dv) + 3 * dk * dv)
 
 
 def decode_algorithmic(BH: int, dk: int, dv: int, es: int):
@@ -135,7 +141,14 @@ def run_prefill(args, torch, kda, synth, oracle):
                       bytes_per_launch=int(nbytes), bytes_per_token_head=per_th,
                       mfma_tflops=round(nflops / avg_call_s / 1e12, 2),
                       mfma_frac=round(nflops / avg_call_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                      flops_per_token_head=flops_th),
+                      flops_per_token_head=flops_th,
+                      mfma_frac_dense_tiles=round(T_tok * H * prefill_dense_flops_th(dk, dv, w.chunk) / avg_call_s / 1e12
+                                                  / MFMA_BF16_PEAK_TFLOPS, 4),
+                      dense_flops_per_token_head=prefill_dense_flops_th(dk, dv, w.chunk),
+                      # attainable = min(MFMA peak, HBM peak x algorithmic intensity)
+                      attainable_tflops=round(min(MFMA_BF16_PEAK_TFLOPS, HBM_PEAK_GBS / 1e3 * flops_th / per_th), 1),
+                      attainable_frac=round(nflops / avg_call_s / 1e12
+                                            / min(MFMA_BF16_PEAK_TFLOPS, HBM_PEAK_GBS / 1e3 * flops_th / per_th), 4)),
         workload=dict(workload=wname, num_seqs=N, total_tokens=T_tok, heads=H, dk=dk, dv=dv, chunk=w.chunk,
                       io_dtype=w.io_dtype, state_dtype="f32"),
     )
@@ -150,6 +163,14 @@ def run_prefill(args, torch, kda, synth, oracle):
         res["cpu_baseline"] = dict(value=round(Ts / dt, 1), unit="tokens/s", cores=int(used), kind="oracle",
                                    sample="first %d of %d tokens, all %d heads, fp64 sequential recurrence, %.1f s"
                                           % (Ts, T_tok, H, dt))
+        T1 = min(2048, Ts)
+        t1 = time.perf_counter()
+        oracle.prefill(w.q[:T1], w.k[:T1], w.v[:T1], w.log_alpha[:T1], w.beta[:T1], [0, T1],
+                       None if w.S0 is None else w.S0[:1], threads=1)
+        dt1 = time.perf_counter() - t1
+        res["cpu_baseline"]["single_thread"] = dict(
+            value=round(T1 / dt1, 1), unit="tokens/s",
+            sample="first %d tokens, all %d heads, one thread, %.1f s" % (T1, H, dt1))
         og = o[:Ts].float().cpu().numpy().astype(np.float64)
         res["parity_sample"] = dict(o_rel_err=float(np.max(np.abs(og - o_ref)) / np.max(np.abs(o_ref))),
                                     tokens=Ts, tol=1e-2 if bf else 1e-4)
