@@ -983,6 +983,11 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
       constexpr int LINES = static_cast<int>(B::bytes / 128);
       constexpr int LPT = (LINES + NSPLIT - 1) / NSPLIT;                       // lines per tile
       constexpr int NPF = (LPT + 64 * kLoaderWaves - 1) / (64 * kLoaderWaves);  // loads per loader wave
+      // lanes of a loader wave's first prefetch that touch block lines; when
+      // there is room, the lanes after them touch C / kLoaderWaves rows of
+      // the chunk's v tile (read from the input, so not in L2 otherwise)
+      constexpr int LPW = (LPT + kLoaderWaves - 1) / kLoaderWaves;
+      constexpr bool PFV = NPF == 1 && LPW + C / kLoaderWaves <= 64;
       auto prefetch = [&](int cc) {
         // A block not written yet must not be touched (its lines would be
         // cached stale): then the last chunk of the newest written segment
@@ -990,11 +995,26 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
         // loader's vmcnt bounds hold.
         if (ready && seg_of(cc) > seen) cc = (seen + 1) * seg - 1 - c0;
         const unsigned char* base = blk_base(cc);
-#pragma unroll
-        for (int m = 0; m < NPF; ++m) {
-          const int line = min(tile * LPT + min((lw + kLoaderWaves * m) * 64 + lane, LPT - 1), LINES - 1);
-          __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(base + line * 128),
+        if constexpr (PFV) {
+          const unsigned char* src;
+          if (lane < LPW) {
+            src = base + min(tile * LPT + min(lw + kLoaderWaves * lane, LPT - 1), LINES - 1) * 128;
+          } else {
+            const int cx = min(cc, ce - 1);
+            const int len = min(C, L_seq - cx * C);
+            const int r = min(lw * (C / kLoaderWaves) + min(lane - LPW, C / kLoaderWaves - 1), len - 1);
+            src = reinterpret_cast<const unsigned char*>(v + (static_cast<size_t>(tbeg + cx * C + r) * H + h) * DV +
+                                                         tile * TILE);
+          }
+          __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
                                            (__attribute__((address_space(3))) void*)(smem + SL::pfsink), 4, 0, 0);
+        } else {
+#pragma unroll
+          for (int m = 0; m < NPF; ++m) {
+            const int line = min(tile * LPT + min((lw + kLoaderWaves * m) * 64 + lane, LPT - 1), LINES - 1);
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(base + line * 128),
+                                             (__attribute__((address_space(3))) void*)(smem + SL::pfsink), 4, 0, 0);
+          }
         }
       };
       auto early = [&](int cc, int slot) {
