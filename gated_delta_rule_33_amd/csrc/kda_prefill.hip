@@ -228,12 +228,18 @@ struct Blk {
   static constexpr int ES = sizeof(T);
   static constexpr int RB_R = DK * ES;  // row bytes of R, Qh
   static constexpr int RB_K = C * ES;   // row bytes of KbT, P, T
+  // P and T are lower triangular; with C = 64 the scan reads rows 0..31
+  // only in their first 32 columns (one k-step), so those rows are stored
+  // at half width
+  static constexpr bool TRI = C == 64;
+  static constexpr size_t tri_bytes = TRI ? static_cast<size_t>(32) * (RB_K / 2) + static_cast<size_t>(C - 32) * RB_K
+                                          : static_cast<size_t>(C) * RB_K;
   static constexpr size_t oR = 0;
   static constexpr size_t oQ = oR + static_cast<size_t>(C) * DK * ES;
   static constexpr size_t oK = oQ + static_cast<size_t>(C) * DK * ES;
   static constexpr size_t oP = oK + static_cast<size_t>(DK) * C * ES;
-  static constexpr size_t oT = oP + static_cast<size_t>(C) * C * ES;
-  static constexpr size_t oG = oT + static_cast<size_t>(C) * C * ES;
+  static constexpr size_t oT = oP + tri_bytes;
+  static constexpr size_t oG = oT + tri_bytes;
   static constexpr size_t oB = oG + static_cast<size_t>(DK) * 4;
   static constexpr size_t bytes = (oB + static_cast<size_t>(C) * 4 + 1023) / 1024 * 1024;
 };
@@ -268,6 +274,29 @@ __device__ __forceinline__ unsigned toff(unsigned row, unsigned c) {
 // byte offset of logical 16-byte granule gi of `row`
 template <int RB>
 __device__ __forceinline__ unsigned goff(unsigned row, unsigned gi) { return row * RB + 16u * (gi ^ swz<RB>(row)); }
+
+// Triangular tiles (P, T) with C = 64: rows 0..31 are half width (their
+// own swizzle), rows 32..63 follow at full width.
+template <typename T, int C>
+__device__ __forceinline__ unsigned tri_off(unsigned row, unsigned c) {
+  constexpr int RB = C * static_cast<int>(sizeof(T));
+  if constexpr (C == 64) {
+    if (row < 32) return toff<T, RB / 2>(row, c);
+    return 32 * (RB / 2) + toff<T, RB>(row - 32, c);
+  } else {
+    return toff<T, RB>(row, c);
+  }
+}
+template <typename T, int C>
+__device__ __forceinline__ unsigned tri_goff(unsigned row, unsigned gi) {
+  constexpr int RB = C * static_cast<int>(sizeof(T));
+  if constexpr (C == 64) {
+    if (row < 32) return goff<RB / 2>(row, gi);
+    return 32 * (RB / 2) + goff<RB>(row - 32, gi);
+  } else {
+    return goff<RB>(row, gi);
+  }
+}
 
 // A fragment of a stored tile for the accumulator k map (see accb).
 template <typename T, int RB>
@@ -672,7 +701,7 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
     const unsigned r = static_cast<unsigned>(idx) / (C / 4), c4b = (static_cast<unsigned>(idx) % (C / 4)) * 4;
     typename raw4<T>::type x = {};
     if ((c4b >> 4) <= (r >> 4)) x = *reinterpret_cast<const typename raw4<T>::type*>(Ps + r * L::CP + c4b);
-    buffer_store_raw4(wr, static_cast<int>(B::oP + toff<T, B::RB_K>(r, c4b)), x);
+    if (!B::TRI || r >= 32 || c4b < 32) buffer_store_raw4(wr, static_cast<int>(B::oP + tri_off<T, C>(r, c4b)), x);
   }
 
   // ---- a4: T = (I + A)^{-1} ----------------------------------------------
@@ -731,7 +760,8 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
 #pragma unroll
       for (int j = 0; j < 4; ++j) x[j] = Ti[r * L::AP + c4b + j];
     }
-    buffer_store4(wr, static_cast<int>(B::oT + toff<T, B::RB_K>(r, c4b)), x, static_cast<T*>(nullptr));
+    if (!B::TRI || r >= 32 || c4b < 32)
+      buffer_store4(wr, static_cast<int>(B::oT + tri_off<T, C>(r, c4b)), x, static_cast<T*>(nullptr));
   }
     }  // item
     __syncthreads();  // LDS is reused by the next item
@@ -784,6 +814,36 @@ struct RowFrags<float, RB, NS> {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         if (4 * t + j < NS) f[4 * t + j] = x[j];
+    }
+  }
+};
+
+// The k-steps a 16-row block mt of a triangular tile (P, T) needs: those
+// covering columns 0 .. 16 mt + 15.
+template <typename T, int C, int NS>
+struct TriFrags;
+template <int C, int NS>
+struct TriFrags<bf16_t, C, NS> {
+  bf16x8 f[NS];
+  __device__ __forceinline__ void load(const unsigned char* tile, int mt, int n, int g) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      if (s <= (16 * mt + 15) / 32)
+        f[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(tile + tri_goff<bf16_t, C>(16 * mt + n, 4 * s + g)));
+  }
+};
+template <int C, int NS>
+struct TriFrags<float, C, NS> {
+  float f[NS];
+  __device__ __forceinline__ void load(const unsigned char* tile, int mt, int n, int g) {
+#pragma unroll
+    for (int t = 0; t < (NS + 3) / 4; ++t) {
+      if (4 * t <= (16 * mt + 15) / 4) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(tile + tri_goff<float, C>(16 * mt + n, 4 * t + g));
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (4 * t + j < NS) f[4 * t + j] = x[j];
+      }
     }
   }
 };
@@ -1167,7 +1227,7 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
   // the row fragments of T.
   struct DIn {
     f32x4 bv[MT];
-    RowFrags<T, B::RB_K, NSC> tf[MT];
+    TriFrags<T, C, NSC> tf[MT];
   };
   auto load_din = [&](const unsigned char* lblk, DIn& in) {
     const T* vt = reinterpret_cast<const T*>(lblk + (B::bytes - B::oK));
@@ -1177,7 +1237,7 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
       const f32x4 bt = *reinterpret_cast<const f32x4*>(Bet + 16 * mt + 4 * g);
 #pragma unroll
       for (int i = 0; i < 4; ++i) in.bv[mt][i] = bt[i] * io<T>::load(vt + (16 * mt + 4 * g + i) * TILE + cg * 16 + n);
-      in.tf[mt].load(lblk + (B::oT - B::oK), 16 * mt + n, g);
+      in.tf[mt].load(lblk + (B::oT - B::oK), mt, n, g);
     }
   };
   // Y = b V - R S; D = T Y with Y split into hi + lo (T unit lower
@@ -1188,7 +1248,7 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
     F yh[NSC], yl[NSC];
 #pragma unroll
     for (int s = 0; s < NSC; ++s) SP::hilo(Y, s, yh[s], yl[s]);
-    const RowFrags<T, B::RB_K, NSC>(&tf)[MT] = in.tf;
+    const TriFrags<T, C, NSC>(&tf)[MT] = in.tf;
     f32x4 D[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -1204,7 +1264,7 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
     for (int s = 0; s < NSC; ++s) SP::hilo(D, s, dh[s], dl[s]);
   };
   // O += P D (D as hi + lo)
-  auto add_pd = [&](const RowFrags<T, B::RB_K, NSC> (&pf)[MT], const F (&dh)[NSC], const F (&dl)[NSC],
+  auto add_pd = [&](const TriFrags<T, C, NSC> (&pf)[MT], const F (&dh)[NSC], const F (&dl)[NSC],
                     f32x4 (&O)[MT]) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -1287,9 +1347,9 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
         RowFrags<T, B::RB_R, NSK> fr[MT];  // Qh rows: the early slot is refilled after M
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) fr[mt].load(eblk + B::oQ, 16 * mt + n, g);
-        RowFrags<T, B::RB_K, NSC> pf[MT];
+        TriFrags<T, C, NSC> pf[MT];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) pf[mt].load(lblk + (B::oP - B::oK), 16 * mt + n, g);
+        for (int mt = 0; mt < MT; ++mt) pf[mt].load(lblk + (B::oP - B::oK), mt, n, g);
         lds_barrier();  // M
         F sb[NSK];
 #pragma unroll
@@ -1354,9 +1414,9 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
       load_din(lblk, din);
       F dh[NSC], dl[NSC];
       make_d(din, Y, dh, dl);
-      RowFrags<T, B::RB_K, NSC> pf[MT];
+      TriFrags<T, C, NSC> pf[MT];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) pf[mt].load(lblk + (B::oP - B::oK), 16 * mt + n, g);
+      for (int mt = 0; mt < MT; ++mt) pf[mt].load(lblk + (B::oP - B::oK), mt, n, g);
       RowFrags<T, B::RB_K, NSC> kf[ST];
 #pragma unroll
       for (int st = 0; st < ST; ++st) kf[st].load(lblk, 16 * st + n, g);
@@ -1418,7 +1478,10 @@ constexpr int64_t kPipeMaxSegs = 16;   // segments, at most (each adds a prep la
 
 static size_t block_bytes(kda_dtype dt, int C, int dk) {
   const size_t es = dt == KDA_BF16 ? 2 : 4;
-  const size_t b = static_cast<size_t>(C) * dk * es * 3 + static_cast<size_t>(C) * C * es * 2 + dk * 4 + C * 4;
+  // P and T: rows 0..31 at half width when C = 64 (see Blk)
+  const size_t tri = (C == 64 ? static_cast<size_t>(32) * (C / 2) + static_cast<size_t>(C - 32) * C
+                              : static_cast<size_t>(C) * C) * es;
+  const size_t b = static_cast<size_t>(C) * dk * es * 3 + tri * 2 + dk * 4 + C * 4;
   return (b + 1023) / 1024 * 1024;
 }
 
