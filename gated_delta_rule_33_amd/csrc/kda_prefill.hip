@@ -20,15 +20,19 @@
 //   S   <- Diag(e^{g_last}) S + Kb^T D
 // Every equation of the state pass acts column by column on the value axis.
 //
-// Kernels (all on the caller's stream):
+// Kernels:
 //   chunk_offsets_kernel  chunk offsets per sequence + longest-first order
-//   prep_kernel           grid (chunk, head): everything that does not depend
-//                         on S (gate cumsum, A and P via MFMA, T by blocked
-//                         forward substitution, R, Qh, Kb^T, e^{g_last}),
-//                         written to one workspace block per (chunk, head)
+//   prep_kernel           persistent, (chunk, head) items: everything that
+//                         does not depend on S (gate cumsum, A and P via MFMA,
+//                         T by blocked forward substitution, R, Qh, Kb^T,
+//                         e^{g_last}), written to one workspace block per
+//                         (chunk, head)
 //   scan_kernel           grid (sequence, head, value tile): the serial chunk
 //                         loop with S held in MFMA accumulators, chunk blocks
 //                         streamed into LDS one chunk ahead
+//   ready_kernel          segment counter of the overlapped schedule
+// With few (sequence, head) pairs the scan runs on half of the CUs beside
+// the prep of later chunks on the other half (launch_prefill below).
 //
 // Exponent safety.  e^{g_r-g_s} is factorised around references inside the
 // chunk so that no factor exceeds the fp32 range: for a 16-row block I below

@@ -65,7 +65,7 @@ typedef struct {
   int32_t total_tokens;  /* T_tot = cu_seqlens[N] >= 0 */
   int32_t num_heads;     /* H >= 1 */
   int32_t dk, dv;        /* key / value head dims, each 64 or 128 */
-  int32_t chunk;         /* tokens per chunk: 64 (16 and 32 also accepted) */
+  int32_t chunk;         /* tokens per chunk: 64 (32 also accepted) */
   kda_dtype io_dtype;    /* dtype of q, k, v and o */
   const int32_t* cu_seqlens_host; /* optional HOST copy of cu_seqlens [N+1]; when
                                      given it is validated and used to size the
@@ -104,9 +104,18 @@ size_t kda_prefill_workspace_size(const kda_prefill_desc* desc);
  *              its contents on entry are ignored and on return undefined.
  *   stream     hipStream_t or NULL.
  *
+ * Streams: the work is ordered on `stream`.  For few (sequence, head) pairs
+ * (N * H * dv / 32 <= 128) the call forks onto two library-owned streams that
+ * split the CUs (one runs the serial state pass, the other prepares later
+ * chunks and advances a counter in the workspace that the first waits on) and
+ * joins back into `stream` with events.  Tools that serialise kernel
+ * dispatches (hardware-counter collection) cannot run that schedule: the
+ * environment variable KDA_PREFILL_OVERLAP=0, read once per process, selects
+ * the one-stream schedule (same kernels and results).
+ *
  * Errors: KDA_ERR_INVALID_ARGUMENT (null pointer where data is required,
  * negative sizes, bad host offsets, misaligned workspace, overlapping buffers),
- * KDA_ERR_UNSUPPORTED (dk/dv not in {64,128}, chunk not in {16,32,64}),
+ * KDA_ERR_UNSUPPORTED (dk/dv not in {64,128}, chunk not in {32,64}),
  * KDA_ERR_WORKSPACE_TOO_SMALL, KDA_ERR_DEVICE (launch failure).  With
  * total_tokens == 0 only S_T = S0 (or zero) is written.
  */
