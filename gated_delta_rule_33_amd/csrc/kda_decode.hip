@@ -11,54 +11,82 @@
 // Every value column j of S evolves independently (r_j, d_j, o_j use only
 // column j), so the state can be split by columns without communication.
 //
-// Mapping.  One workgroup per (b, h); one wavefront per 32 value columns.
-// Lane l of a wave owns 4 adjacent columns (l % 8) and the key rows
-// (l / 8) + 8 i, i = 0 .. dk/8 - 1, held in VGPRs for the whole step: each
-// float4 load instruction of the wave covers 8 rows x 128 contiguous bytes,
-// i.e. whole 128-byte lines, and the state is read once and written once.
-// The two column reductions (S~^T k and S~^T q) and k^T q run over the 8 row
-// phases with cross-lane xor shuffles; there is no LDS and no barrier.
-// The kernel is HBM-bound: 2 * 4 * dk * dv bytes of state per update against
-// ~4 * dk * dv flops.
+// Mapping.  One workgroup per (b, h, slice of CW = min(64, dv) value
+// columns); its waves split the key rows, kNR = 2 consecutive rows per lane.
+// Lane l of a wave owns 4 adjacent columns (l mod CW/4) and its rows' state
+// values stay in VGPRs for the whole step; one float4 load instruction of a
+// wave covers 256 / CW rows x 4 CW contiguous bytes (whole 128-byte lines),
+// the lane's gates, k and q come in one load each, and the state is read
+// once and written once.  The column sums (S~^T k, S~^T q) and k^T q are
+// reduced over the row phases of a wave with xor shuffles, then over the
+// waves through LDS (one barrier).  Shape choice (in-place 512 MiB stream,
+// measured): few loads per lane and row pieces of at least 256 bytes per
+// instruction matter most — 16 float4 loads per lane in one 64 KiB
+// workgroup per state ran 13% slower, 32-column slices (128-byte pieces)
+// 7% slower, 16-column slices twice as slow.  The kernel is HBM-bound:
+// 2 * 4 * dk * dv bytes of state per update against ~4 * dk * dv flops.
 
 #include "kda_device.h"
 #include "kda_internal.h"
 
 namespace kda {
 
+constexpr int kNR = 2;   // key rows per lane
+constexpr int kCW = 64;  // value columns per workgroup (at most dv)
+
+template <int DV>
+struct DecodeShape {
+  static constexpr int CW = kCW < DV ? kCW : DV;
+  static constexpr int LPR = CW / 4;   // lanes per key row (4 columns each)
+  static constexpr int RPI = 64 / LPR;  // key rows per wave load instruction
+};
+
+// kNR consecutive elements, loaded with one instruction
+template <typename T>
+struct alignas(sizeof(T) * kNR) RowPack {
+  T x[kNR];
+};
+
 template <typename T, int DK, int DV>
-__global__ __launch_bounds__(DV * 2) void decode_kernel(const T* __restrict__ q, const T* __restrict__ k,
-                                                        const T* __restrict__ v, const float* __restrict__ la,
-                                                        const float* __restrict__ beta, float* __restrict__ S,
-                                                        T* __restrict__ o) {
-  constexpr int NR = DK / 8;  // key rows per lane
-  const int bh = blockIdx.x;
+__global__ __launch_bounds__(DK / kNR * DecodeShape<DV>::LPR) void decode_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                              const T* __restrict__ v, const float* __restrict__ la,
+                                                              const float* __restrict__ beta, float* __restrict__ S,
+                                                              T* __restrict__ o) {
+  typedef DecodeShape<DV> DS;
+  constexpr int RW = DK / (DS::RPI * kNR);  // row waves per workgroup
+  constexpr int NS = DV / DS::CW;           // column slices per state
+  __shared__ f32x4 red[RW][2][DS::LPR];     // per wave: S~^T k and S~^T q of its rows
+  __shared__ float redkq[RW];            // per wave: k^T q of its rows
+  const int bh = blockIdx.x / NS;
+  const int slice = blockIdx.x % NS;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int c4 = lane & 7;
-  const int rph = lane >> 3;
-  const int col = wave * 32 + c4 * 4;
+  const int c4 = lane % DS::LPR;
+  const int row0 = (wave * DS::RPI + lane / DS::LPR) * kNR;
+  const int col = slice * DS::CW + c4 * 4;
 
   float* Sb = S + static_cast<size_t>(bh) * DK * DV;
   const T* qb = q + static_cast<size_t>(bh) * DK;
   const T* kb = k + static_cast<size_t>(bh) * DK;
   const float* lab = la + static_cast<size_t>(bh) * DK;
 
-  f32x4 s[NR];
+  f32x4 s[kNR];
 #pragma unroll
-  for (int i = 0; i < NR; ++i)
-    s[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Sb + (rph + 8 * i) * DV + col));
+  for (int i = 0; i < kNR; ++i)
+    s[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Sb + (row0 + i) * DV + col));
 
-  float kr[NR];
+  const RowPack<float> lr = *reinterpret_cast<const RowPack<float>*>(lab + row0);
+  const RowPack<T> kp = *reinterpret_cast<const RowPack<T>*>(kb + row0);
+  const RowPack<T> qp = *reinterpret_cast<const RowPack<T>*>(qb + row0);
+  float kr[kNR];
   f32x4 r = {0.f, 0.f, 0.f, 0.f};
   f32x4 sq = {0.f, 0.f, 0.f, 0.f};
   float kq = 0.f;
 #pragma unroll
-  for (int i = 0; i < NR; ++i) {
-    const int row = rph + 8 * i;
-    const float a = __expf(lab[row]);
-    const float kk = io<T>::load(kb + row);
-    const float qq = io<T>::load(qb + row);
+  for (int i = 0; i < kNR; ++i) {
+    const float a = __expf(lr.x[i]);
+    const float kk = io<T>::load(&kp.x[i]);
+    const float qq = io<T>::load(&qp.x[i]);
     s[i] *= a;
     r += kk * s[i];
     sq += qq * s[i];
@@ -66,7 +94,7 @@ __global__ __launch_bounds__(DV * 2) void decode_kernel(const T* __restrict__ q,
     kr[i] = kk;
   }
 #pragma unroll
-  for (int m = 8; m < 64; m <<= 1) {
+  for (int m = DS::LPR; m < 64; m <<= 1) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       r[c] += shfl_xor(r[c], m);
@@ -74,23 +102,39 @@ __global__ __launch_bounds__(DV * 2) void decode_kernel(const T* __restrict__ q,
     }
     kq += shfl_xor(kq, m);
   }
+  if (lane < DS::LPR) {
+    red[wave][0][c4] = r;
+    red[wave][1][c4] = sq;
+    if (lane == 0) redkq[wave] = kq;
+  }
   const f32x4 vv = load4(v + static_cast<size_t>(bh) * DV + col);
   const float b = beta[bh];
-  const f32x4 d = b * (vv - r);
-  const f32x4 out = sq + d * kq;
+  __syncthreads();
+  r = red[0][0][c4];
+  sq = red[0][1][c4];
+  kq = redkq[0];
 #pragma unroll
-  for (int i = 0; i < NR; ++i) {
-    s[i] += kr[i] * d;
-    __builtin_nontemporal_store(s[i], reinterpret_cast<f32x4*>(Sb + (rph + 8 * i) * DV + col));
+  for (int w = 1; w < RW; ++w) {
+    r += red[w][0][c4];
+    sq += red[w][1][c4];
+    kq += redkq[w];
   }
-  if (rph == 0) store4(o + static_cast<size_t>(bh) * DV + col, out);
+  const f32x4 d = b * (vv - r);
+#pragma unroll
+  for (int i = 0; i < kNR; ++i) {
+    s[i] += kr[i] * d;
+    __builtin_nontemporal_store(s[i], reinterpret_cast<f32x4*>(Sb + (row0 + i) * DV + col));
+  }
+  if (threadIdx.x < DS::LPR) store4(o + static_cast<size_t>(bh) * DV + col, sq + d * kq);
 }
 
 template <typename T, int DK, int DV>
 static hipError_t launch_decode_t(int BH, const void* q, const void* k, const void* v, const float* la,
                                   const float* beta, float* S, void* o, hipStream_t st) {
-  hipLaunchKernelGGL((decode_kernel<T, DK, DV>), dim3(BH), dim3(DV * 2), 0, st, static_cast<const T*>(q),
-                     static_cast<const T*>(k), static_cast<const T*>(v), la, beta, S, static_cast<T*>(o));
+  hipLaunchKernelGGL((decode_kernel<T, DK, DV>), dim3(BH * (DV / DecodeShape<DV>::CW)),
+                     dim3(DK / kNR * DecodeShape<DV>::LPR), 0, st,
+                     static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), la, beta, S,
+                     static_cast<T*>(o));
   return hipGetLastError();
 }
 
