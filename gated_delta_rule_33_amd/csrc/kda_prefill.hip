@@ -981,22 +981,26 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
   const float* s_in = S0;
   float* s_out = S_T;
 
-  // Loader waves: segments written so far, as last read (wave-uniform),
-  // polled with device-scope loads before a block is touched.  The wait is
-  // bounded (~2^20 polls of ~500 cycles); a wave that runs out stops waiting
-  // for the rest of the launch, so a stalled producer cannot hold the GPU.
-  int seen = 0;
+  // Loader waves: `upto` is the last chunk of this sequence (index relative
+  // to it) whose segment the counter showed as written when last read
+  // (wave-uniform), so the common case is one compare, not a division per
+  // chunk on the scalar unit the CU's waves share.  The counter is polled
+  // with device-scope loads before a block is touched.  The wait is bounded
+  // (~2^20 polls of ~500 cycles); a wave that runs out stops waiting for the
+  // rest of the launch, so a stalled producer cannot hold the GPU.
+  auto upto_of = [&](int seen) { return (seen + 1) * seg - 1 - c0; };
+  int upto = ready ? upto_of(0) : 0x7fffffff;
   bool patient = true;
-  auto seg_of = [&](int cc) { return (c0 + min(cc, ce - 1)) / seg; };
   auto ensure = [&](int cc) {
-    if (!ready || !patient) return;
-    const int need = seg_of(cc);
+    const int need = min(cc, ce - 1);
+    if (need <= upto || !patient) return;
     int spin = 0;
-    for (; seen < need && spin < (1 << 20); ++spin) {
-      seen = __builtin_amdgcn_readfirstlane(__hip_atomic_load(ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-      if (seen < need) __builtin_amdgcn_s_sleep(8);
+    for (; need > upto && spin < (1 << 20); ++spin) {
+      upto = upto_of(
+          __builtin_amdgcn_readfirstlane(__hip_atomic_load(ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)));
+      if (need > upto) __builtin_amdgcn_s_sleep(8);
     }
-    if (seen < need) patient = false;
+    if (need > upto) patient = false;
   };
 
   // Single-slot scheme (NBUF = 1): the whole block of chunk cc and its v
@@ -1057,7 +1061,7 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
         // cached stale): then the last chunk of the newest written segment
         // is touched instead, so every call issues exactly NPF loads and the
         // loader's vmcnt bounds hold.
-        if (ready && seg_of(cc) > seen) cc = (seen + 1) * seg - 1 - c0;
+        if (cc > upto) cc = upto;
         const unsigned char* base = blk_base(cc);
         if constexpr (PFV) {
           const unsigned char* src;
@@ -1130,14 +1134,18 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
       early(cb, 0);
       late(cb, 0);
       early(cb + 1, 1);
-      wait_vm<NE>();  // chunk cb resident (early and late parts)
+      prefetch(cb + 2);
+      wait_vm<NE + NPF>();  // chunk cb resident (early and late parts)
       lds_barrier();
       for (int cc = cb; cc < ce; ++cc) {
         const int b = (cc - cb) & 1;
         ensure(cc + 1);
         late(cc + 1, b ^ 1);
         ostore(cc - 1);
-        lds_barrier();  // M(cc): early slot b free
+        // in flight, oldest first: early part of chunk cc + 1, prefetch of
+        // cc + 2, late part of cc + 1, output stores of cc - 1
+        wait_vm<NPF + NLT + NSW>();  // early part of chunk cc + 1 resident
+        lds_barrier();  // M(cc): early slot b free; the state waves read chunk cc + 1's R rows from here on
         ensure(cc + 2);
         early(cc + 2, b);
         prefetch(cc + 3);
@@ -1303,13 +1311,20 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
     F* const sxp = dxp + 64 * C / static_cast<int>(sizeof(F));
     int* const xfl = reinterpret_cast<int*>(smem + SL::xflag) + cg;
     if (do_state) {
-      for (int cc = cb; cc < ce; ++cc) {
-        const unsigned char* eblk = eblk_of(cc);
-        const unsigned char* lblk = lblk_of(cc);
-        // the whole chunk is resident: R rows and the late-part inputs now
-        RowFrags<T, B::RB_R, NSK> fr[MT];
+      // R rows of the first chunk; with two slots, the rows of chunk cc + 1
+      // are read during chunk cc, after M (the loaders have its early part
+      // resident by then), so the next chunk's products start at once
+      RowFrags<T, B::RB_R, NSK> fr[MT];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) fr[mt].load(eblk + B::oR, 16 * mt + n, g);
+      for (int mt = 0; mt < MT; ++mt) fr[mt].load(eblk_of(cb) + B::oR, 16 * mt + n, g);
+      for (int cc = cb; cc < ce; ++cc) {
+        const unsigned char* lblk = lblk_of(cc);
+        if constexpr (SL::NBUF == 1) {
+          if (cc > cb) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) fr[mt].load(eblk_of(cc) + B::oR, 16 * mt + n, g);
+          }
+        }
         DIn din;
         load_din(lblk, din);
         F sb[NSK];
@@ -1334,6 +1349,12 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
         RowFrags<T, B::RB_K, NSC> kf[ST];
 #pragma unroll
         for (int st = 0; st < ST; ++st) kf[st].load(lblk, 16 * st + n, g);
+        if constexpr (SL::NBUF == 2) {
+          // next chunk's R rows (past the last chunk: a slot no load is
+          // filling, values unused)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) fr[mt].load(eblk_of(cc + 1) + B::oR, 16 * mt + n, g);
+        }
         update_s(lblk, kf, dh);
         chunk_end();
       }

@@ -138,14 +138,13 @@ SEG_LENGTHS = [5000, 0, 3000, 777, 4096]
 @pytest.mark.parametrize("chunk", [64, 32])
 @pytest.mark.parametrize("mode", ["state", "nostate", "inplace"])
 def test_segmented_schedule(dt, chunk, mode):
-    """Few (sequence, head) pairs and 200+ chunks: prep and scan run as
-    overlapped segments on two CU-masked streams.  Sequences straddle segment
-    boundaries, so the state crosses launches (through S_T, or through the
-    workspace when no final state is asked for)."""
+    """Few (sequence, head) pairs and 200+ chunk indices: one scan launch on
+    half of the CUs beside the prep of 4 (chunk 64) or 7 (chunk 32) segments
+    of 64 chunk indices on the other half.  Sequences straddle segment
+    boundaries, so the scan waits on the segment counter mid-sequence; the
+    final state is written to S_T, to S0 in place, or not at all."""
     import torch
     import gated_delta_rule_33_amd as kda
-    if mode != "state" and dt == "f32":
-        pytest.skip("state hand-over modes are covered in bf16")
     log("prefill segmented dt=%s chunk=%d mode=%s" % (dt, chunk, mode))
     w = synth.make_prefill(SEG_LENGTHS, H=4, dk=128, dv=128, io_dtype=dt, seed=20, S0_std=0.05, chunk=chunk)
     o_ref, S_ref = oracle_prefill(w)
@@ -166,10 +165,10 @@ def test_segmented_schedule(dt, chunk, mode):
 
 
 def test_segmented_schedule_many_segments():
-    """674 chunks over 4 sequences x 2 heads: eight segments, with sequences
-    (one of 3 tokens) straddling the boundaries."""
+    """674 chunk indices over 4 sequences x 2 heads: eleven segments of 64,
+    with sequences (one of 3 tokens) straddling the boundaries."""
     lengths = [20000, 9000, 3, 14000]
-    log("prefill segmented, growing segments: %s x 2 heads" % lengths)
+    log("prefill segmented, 11 segments: %s x 2 heads" % lengths)
     w = synth.make_prefill(lengths, H=2, dk=128, dv=128, io_dtype="bf16", seed=23, S0_std=0.05)
     o, S = gpu_prefill(w)
     o_ref, S_ref = oracle_prefill(w)
