@@ -7,7 +7,9 @@ sequence of 131072 tokens, 32 heads, dk = dv = 128, bf16 q/k/v/o, fp32
 log_alpha/beta/state, chunk 64, 5% long-memory key channels; it returns o and
 the final state.  Inputs are resident in HBM before timing starts.  The
 decode workload (256 requests x 32 heads, fp32 128x128 states updated in
-place for 1024 tokens) is timed in the same run and reported under "decode".
+place for 1024 tokens) is timed in the same run and reported under "decode";
+the call rates of the 4 x 4096-token batch and of the 64-sequence varlen
+workload follow under "prefill_other" (skip with --no-other).
 
 Prints ONE JSON line.  `value` is prefill tokens/s.  Each roofline block
 prices the operator's algorithmic bytes per launch against MI355X's 8 TB/s
@@ -179,6 +181,46 @@ def run_prefill(args, torch, kda, synth, oracle):
     return res
 
 
+def run_prefill_rate(wname, args, torch, kda, synth):
+    """Call time and rate of another prefill workload (no CPU baseline):
+    context for the main line, which times the 131072-token workload."""
+    w = synth.workload_prefill(wname)
+    bf = w.io_dtype == "bf16"
+    tdt = torch.bfloat16 if bf else torch.float32
+
+    def up(x, io=False):
+        t = torch.from_numpy(np.ascontiguousarray(x))
+        return (t.to(tdt) if io else t).cuda()
+
+    q, k, v = up(w.q, True), up(w.k, True), up(w.v, True)
+    la, b, cu = up(w.log_alpha), up(w.beta), up(w.cu_seqlens)
+    S0 = up(w.S0) if w.S0 is not None else None
+    T_tok, H, dk = w.q.shape
+    dv = w.v.shape[2]
+    N = w.num_seqs
+    o = torch.empty((T_tok, H, dv), dtype=tdt, device="cuda")
+    ST = torch.empty((N, H, dk, dv), dtype=torch.float32, device="cuda")
+    host_cu = w.cu_seqlens.tolist()
+    stream = torch.cuda.current_stream()
+    for _ in range(2):
+        kda.prefill(q, k, v, la, b, cu, S0, o=o, S_T=ST, cu_seqlens_host=host_cu, chunk=w.chunk)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 5
+    e0.record(stream)
+    for _ in range(n):
+        kda.prefill(q, k, v, la, b, cu, S0, o=o, S_T=ST, cu_seqlens_host=host_cu, chunk=w.chunk)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    call_s = e0.elapsed_time(e1) / n / 1e3
+    nbytes, _, _, _ = prefill_algorithmic(T_tok, N, H, dk, dv, 2 if bf else 4, w.chunk, S0 is not None)
+    del q, k, v, la, b, o, ST, S0
+    torch.cuda.empty_cache()
+    return dict(workload=wname, num_seqs=N, total_tokens=T_tok, heads=H, call_ms=round(call_s * 1e3, 4),
+                tokens_per_s=round(T_tok / call_s, 1),
+                hbm_frac=round(nbytes / call_s / 1e9 / HBM_PEAK_GBS, 4))
+
+
 def run_decode(args, torch, kda, synth):
     wd = synth.WORKLOADS["decode256x32_bf16"]
     B, H, dk, dv, steps = wd["B"], wd["H"], wd["dk"], wd["dv"], args.decode_steps
@@ -254,6 +296,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other", action="store_true", help="skip the 4x4096 and varlen prefill rates")
     ap.add_argument("--cpu-sample-tokens", type=int, default=65536)
     ap.add_argument("--cpu-threads", type=int, default=0)
     ap.add_argument("--copy-probe", type=int, default=0, help="run only a device copy of this many bytes")
@@ -276,6 +319,8 @@ def main():
 
     pre = run_prefill(args, torch, kda, synth, oracle)
     dec = None if args.no_decode else run_decode(args, torch, kda, synth)
+    other = [] if args.no_other else [run_prefill_rate(n, args, torch, kda, synth)
+                                      for n in ("batch4x4096_bf16", "varlen64_bf16")]
     wl = pre["workload"]
     line = {
         "metric": "KDA prefill tokens/s (MFMA % peak) at T=128k; decode state-updates/s (HBM %)",
@@ -301,6 +346,8 @@ def main():
         line["parity_sample"] = pre["parity_sample"]
     if dec is not None:
         line["decode"] = dec
+    if other:
+        line["prefill_other"] = other
     print(json.dumps(line), flush=True)
 
 
