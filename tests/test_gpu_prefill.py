@@ -174,3 +174,37 @@ def test_segmented_schedule_many_segments():
     o_ref, S_ref = oracle_prefill(w)
     check("o", o, o_ref, TOL["bf16"])
     check("S_T", S, S_ref, TOL["bf16"])
+
+
+def test_one_stream_schedule_is_bitwise_equal():
+    """KDA_PREFILL_OVERLAP=0 (every prep segment, then the scan, on the
+    caller's stream; the schedule hardware-counter runs use) returns bitwise
+    the same o and S_T as the overlapped two-stream schedule.  The variable
+    is read once per process, so that side runs in a child process."""
+    import os
+    import subprocess
+    import sys
+    import tempfile
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    lengths = [5000, 0, 3000, 777, 4096]
+    log("prefill one-stream vs overlapped schedule, %s x 4 heads" % lengths)
+    w = synth.make_prefill(lengths, H=4, dk=128, dv=128, io_dtype="bf16", seed=20, S0_std=0.05)
+    o_ov, S_ov = gpu_prefill(w)
+    with tempfile.TemporaryDirectory() as td:
+        out = os.path.join(td, "one_stream.npz")
+        child = (
+            "import sys, numpy as np\n"
+            "sys.path.insert(0, %r)\n"
+            "import synth\n"
+            "from tests.gpu_helpers import gpu_prefill\n"
+            "w = synth.make_prefill(%r, H=4, dk=128, dv=128, io_dtype='bf16', seed=20, S0_std=0.05)\n"
+            "o, S = gpu_prefill(w)\n"
+            "np.savez(%r, o=o, S=S)\n" % (root, lengths, out))
+        env = dict(os.environ, KDA_PREFILL_OVERLAP="0")
+        r = subprocess.run([sys.executable, "-c", child], env=env, cwd=root, timeout=300,
+                           capture_output=True, text=True)
+        assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
+        z = np.load(out)
+        o_one, S_one = z["o"], z["S"]
+    assert np.array_equal(o_one, o_ov)
+    assert np.array_equal(S_one, S_ov)
