@@ -29,7 +29,8 @@
 //                         (chunk, head)
 //   scan_kernel           grid (sequence, head, value tile): the serial chunk
 //                         loop with S held in MFMA accumulators, chunk blocks
-//                         streamed into LDS one chunk ahead
+//                         streamed into LDS ahead of use (their first
+//                         products' operands two chunks ahead, the rest one)
 //   ready_kernel          segment counter of the overlapped schedule
 // With few (sequence, head) pairs the scan runs on half of the CUs beside
 // the prep of later chunks on the other half (launch_prefill below).
