@@ -1045,7 +1045,7 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
       }
       auto blk_base = [&](int cc) { return ws + (static_cast<size_t>(c0 + min(cc, ce - 1)) * H + h) * B::bytes; };
       auto blk_src = [&](int cc) { return blk_base(cc) + lane * 16; };
-      // L2 prefetch of a chunk's block two chunks before its loads: the
+      // L2 prefetch of a chunk's block two chunks before its first loads: the
       // value tiles of a (sequence, head) share their XCD's L2, so tile t
       // touches a quarter of the block's 128-byte lines, one 4-byte
       // direct-to-LDS load per lane into a sink nobody reads.
@@ -1143,13 +1143,13 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
         ensure(cc + 1);
         late(cc + 1, b ^ 1);
         ostore(cc - 1);
-        // in flight, oldest first: early part of chunk cc + 1, prefetch of
-        // cc + 2, late part of cc + 1, output stores of cc - 1
+        // in flight, oldest first: early part of chunk cc + 1, the previous
+        // prefetch, late part of cc + 1, output stores of cc - 1
         wait_vm<NPF + NLT + NSW>();  // early part of chunk cc + 1 resident
         lds_barrier();  // M(cc): early slot b free; the state waves read chunk cc + 1's R rows from here on
         ensure(cc + 2);
         early(cc + 2, b);
-        prefetch(cc + 3);
+        prefetch(cc + 4);
         wait_vm<NE + NPF>();  // all but the early part of chunk cc + 2 and the prefetch: chunk cc + 1 resident
         lds_barrier();  // end of chunk cc
       }
