@@ -107,3 +107,37 @@ def test_decode_validation_codes():
     bad = list(ptrs)
     bad[6] = ptrs[5] + 128  # o overlaps S
     assert f(4, 2, 128, 128, kda.KDA_BF16, *bad) == kda.KDA_ERR_INVALID_ARGUMENT
+
+
+def block_bytes(C: int, dk: int, es: int) -> int:
+    """Bytes of one workspace block per (chunk, head), from the documented
+    layout: R, Qh [C][dk] and Kb^T [dk][C] in the io dtype; P and T [C][C]
+    in the io dtype, with rows 0..31 at half width when C = 64 (their columns
+    32..63 are zero); Gamma [dk] and beta [C] in fp32; rounded up to 1 KiB."""
+    tri = 32 * (C // 2) * es + (C - 32) * C * es if C == 64 else C * C * es
+    raw = 3 * C * dk * es + 2 * tri + dk * 4 + C * 4
+    return (raw + 1023) // 1024 * 1024
+
+
+def test_workspace_layout_sizes():
+    """The workspace is the chunk-block array plus a small header (chunk
+    offsets, order and, for the overlapped schedule, the segment counter)."""
+    def ws(**kw):
+        base = dict(num_seqs=1, total_tokens=131072, num_heads=32, dk=128, dv=128, chunk=64,
+                    io_dtype=kda.KDA_BF16, cu_seqlens_host=[0, 131072])
+        base.update(kw)
+        d, keep = kda.make_desc(**base)
+        return kda.prefill_workspace_size(d)
+    assert block_bytes(64, 128, 2) == 62464
+    cases = [
+        (dict(), 2048 * 32, block_bytes(64, 128, 2)),
+        (dict(io_dtype=kda.KDA_F32), 2048 * 32, block_bytes(64, 128, 4)),
+        (dict(chunk=32), 4096 * 32, block_bytes(32, 128, 2)),
+        (dict(dk=64, dv=64, num_heads=4), 2048 * 4, block_bytes(64, 64, 2)),
+        (dict(num_seqs=3, total_tokens=4161, cu_seqlens_host=[0, 65, 65, 4161], num_heads=2),
+         (2 + 0 + 64) * 2, block_bytes(64, 128, 2)),
+    ]
+    for kw, chunk_heads, blk in cases:
+        total = ws(**kw)
+        header = total - chunk_heads * blk
+        assert 0 < header < 4096, (kw, total, header)
