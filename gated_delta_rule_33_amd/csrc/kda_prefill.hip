@@ -203,8 +203,10 @@ __global__ __launch_bounds__(1024) void chunk_offsets_kernel(const int32_t* __re
 }
 
 // Overlapped schedule: segments 0 .. j of the workspace blocks are written.
-// Launched on the prep stream after segment j's prep, so the prep's writes
-// are complete and visible before the counter moves.
+// Launched on the prep stream after the last segment's prep, so the prep's
+// writes are complete and visible before the counter moves (the prep
+// launches of segments 2, 3, ... publish their predecessor the same way, from
+// their first thread).
 __global__ void ready_kernel(int32_t* ready, int j) {
   if (threadIdx.x == 0) __hip_atomic_store(ready, j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -478,11 +480,16 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                    const float* __restrict__ la, const float* __restrict__ beta,
                                                    const int32_t* __restrict__ cu,
                                                    const int32_t* __restrict__ chunk_off, int N, int H,
-                                                   unsigned char* __restrict__ ws, int cbase, int count) {
+                                                   unsigned char* __restrict__ ws, int cbase, int count,
+                                                   int32_t* publish, int published) {
   typedef PrepLds<T, C, DK> L;
   typedef Blk<T, C, DK> B;
   typedef mma16<T> M;
   typedef mma16<float> MF;
+  // Stream order started this launch after the previous one on its stream
+  // had ended (and released its writes): tell the scan those blocks exist.
+  if (publish && blockIdx.x == 0 && threadIdx.x == 0)
+    __hip_atomic_store(publish, published, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   constexpr int NB = L::NB;
   constexpr int RPT = C / L::NRB;  // rows per thread
   static_assert(RPT >= 1 && 16 % RPT == 0, "row blocks must tile 16-row sub-blocks");
@@ -1661,7 +1668,7 @@ static hipError_t launch_prefill_t(const PrefillPlan& p, const void* q, const vo
   static_assert(PrepLds<T, C, DK>::total <= 160 * 1024, "prep LDS");
   // Persistent prep: as many workgroups as fit on the CUs the stream may
   // use (LDS-limited), each walking (chunk, head) items.
-  auto prep = [&](int64_t cbase, int64_t count, hipStream_t s, int cus) -> hipError_t {
+  auto prep = [&](int64_t cbase, int64_t count, hipStream_t s, int cus, int32_t* publish, int published) -> hipError_t {
     hipError_t r = set_lds_limit(reinterpret_cast<const void*>(&prep_kernel<T, C, DK>), lp);
     if (r != hipSuccess) return r;
     const int64_t per_cu = (160 * 1024) / static_cast<int64_t>(lp) > 0 ? (160 * 1024) / static_cast<int64_t>(lp) : 1;
@@ -1669,16 +1676,17 @@ static hipError_t launch_prefill_t(const PrefillPlan& p, const void* q, const vo
     const int64_t grid = items < per_cu * cus ? items : per_cu * cus;
     hipLaunchKernelGGL((prep_kernel<T, C, DK>), dim3(static_cast<unsigned>(grid)), dim3(kPrepThreads), lp, s,
                        static_cast<const T*>(q), static_cast<const T*>(k), la, beta, cu, chunk_off, p.N, p.H,
-                       blocks, static_cast<int>(cbase), static_cast<int>(count));
+                       blocks, static_cast<int>(cbase), static_cast<int>(count), publish, published);
     return hipGetLastError();
   };
   int cus = 0;
   if ((e = device_cus(&cus)) != hipSuccess) return e;
   // Overlapped schedule: one scan launch (half of the CUs) walks every
   // chunk while the prep of segments 1, 2, ... runs beside it (the other
-  // half), each followed by a bump of the ready counter that the scan's
-  // loader waves wait on; both streams fork from and join back into the
-  // caller's stream.  Segment 0's prep has the whole device.
+  // half); the ready counter that the scan's loader waves wait on is
+  // raised to j - 1 by the first thread of segment j's prep launch and to
+  // the last segment by a ready_kernel; both streams fork from and join
+  // back into the caller's stream.  Segment 0's prep has the whole device.
   PipeStreams* ps = nullptr;
   if (p.seg > 0) {
     e = pipe_streams(narrow_scan_wgs(p.N, p.H, DV), &ps);
@@ -1687,7 +1695,7 @@ static hipError_t launch_prefill_t(const PrefillPlan& p, const void* q, const vo
   if (ps) {
     const int64_t nseg = (p.max_chunks + p.seg - 1) / p.seg;
     std::lock_guard<std::mutex> lock(ps->mu);
-    e = prep(0, p.seg < p.max_chunks ? p.seg : p.max_chunks, st, cus);
+    e = prep(0, p.seg < p.max_chunks ? p.seg : p.max_chunks, st, cus, nullptr, 0);
     if (e != hipSuccess) return e;
     if ((e = hipEventRecord(ps->fork, st)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(ps->prep, ps->fork, 0)) != hipSuccess) return e;
@@ -1697,17 +1705,19 @@ static hipError_t launch_prefill_t(const PrefillPlan& p, const void* q, const vo
     if (e != hipSuccess) return e;
     for (int64_t j = 1; j < nseg; ++j) {
       const int64_t c0 = j * p.seg, c1 = c0 + p.seg < p.max_chunks ? c0 + p.seg : p.max_chunks;
-      if ((e = prep(c0, c1 - c0, ps->prep, cus - ps->scan_cus)) != hipSuccess) return e;
-      hipLaunchKernelGGL(ready_kernel, dim3(1), dim3(64), 0, ps->prep, ready, static_cast<int>(j));
-      if ((e = hipGetLastError()) != hipSuccess) return e;
+      if ((e = prep(c0, c1 - c0, ps->prep, cus - ps->scan_cus, j > 1 ? ready : nullptr, static_cast<int>(j - 1))) !=
+          hipSuccess)
+        return e;
     }
+    hipLaunchKernelGGL(ready_kernel, dim3(1), dim3(64), 0, ps->prep, ready, static_cast<int>(nseg - 1));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = hipEventRecord(ps->join, ps->scan)) != hipSuccess) return e;
     if ((e = hipEventRecord(ps->join_prep, ps->prep)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(st, ps->join, 0)) != hipSuccess) return e;
     return hipStreamWaitEvent(st, ps->join_prep, 0);
   }
   if (p.max_chunks > 0) {
-    e = prep(0, p.max_chunks, st, cus);
+    e = prep(0, p.max_chunks, st, cus, nullptr, 0);
     if (e != hipSuccess) return e;
   }
   // Few (sequence, head) pairs: narrower value tiles to put more CUs on the
