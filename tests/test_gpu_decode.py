@@ -26,6 +26,24 @@ def test_decode_steps_match_oracle(dt, dk, dv):
     check("S after %d steps" % steps, host(Sd), Sref, TOL[dt])
 
 
+@pytest.mark.parametrize("B,H", [(1, 1), (3, 1), (1, 17), (43, 3)])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 128), (128, 64)])
+def test_decode_odd_batch_counts(B, H, dk, dv):
+    """Batch x head counts that fill no power-of-two grid (1, 3, 17 and 129
+    states), bf16 io, three steps."""
+    import gated_delta_rule_33_amd as kda
+    log("decode odd counts B=%d H=%d dk=%d dv=%d" % (B, H, dk, dv))
+    S = synth.make_decode_state(B, H, dk, dv, 0.02, seed=91)
+    Sd = dev(S)
+    Sref = S.astype(np.float64)
+    for t in range(3):
+        x = synth.make_decode_step(B, H, dk, dv, "bf16", seed=92, step=t)
+        o = kda.decode_step(dev(x.q, "bf16"), dev(x.k, "bf16"), dev(x.v, "bf16"), dev(x.log_alpha), dev(x.beta), Sd)
+        o_ref, Sref = oracle.decode_step(x.q, x.k, x.v, x.log_alpha, x.beta, Sref)
+        check("o step %d" % t, host(o), o_ref, TOL["bf16"])
+    check("S after 3 steps", host(Sd), Sref, TOL["bf16"])
+
+
 def test_decode_full_size_sampled():
     """The benchmark's decode workload (B=256, H=32, d=128, bf16 q/k/v, fp32
     state, 1024 steps); the oracle follows 64 sampled states."""
