@@ -27,7 +27,11 @@
  *   - Arguments are validated on the host before anything is launched; a
  *     failed validation returns an error and launches nothing.  No C++
  *     exception crosses this boundary.
- *   - Calls are thread-safe (no global mutable state).
+ *   - Calls are thread-safe.  The library's only process state is created
+ *     once under a lock: per-device kernel attributes and, for the
+ *     overlapped prefill schedule, two CU-masked streams with their events
+ *     per device, on which concurrent overlapped calls for one device take
+ *     turns to enqueue their work.
  *   - Device-side preconditions that are documented but not checked:
  *     finite inputs; log_alpha <= 0; for the chunked prefill additionally
  *     log_alpha >= -10 per element (the intra-chunk gate ratios are
