@@ -168,7 +168,9 @@ __global__ __launch_bounds__(1024) void chunk_offsets_kernel(const int32_t* __re
                                                              int32_t* __restrict__ ready) {
   __shared__ int32_t part[1024];
   const int tid = threadIdx.x;
-  if (tid == 0 && ready) *ready = 0;  // segment counter of the overlapped schedule
+  // overlapped schedule: [0] last segment written, [1] set when a scan
+  // loader wave stopped waiting for a segment (its results are then wrong)
+  if (tid < 2 && ready) ready[tid] = 0;
   const int per = (N + 1023) / 1024;
   const int b = min(N, tid * per), e = min(N, b + per);
   int s = 0;
@@ -947,7 +949,7 @@ template <typename T, int C, int DK, int DV, int WAVES>
 __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel(
     const T* __restrict__ v, const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_off,
     const int32_t* __restrict__ order, int N, int H, const unsigned char* __restrict__ ws, const float* S0,
-    T* __restrict__ o, float* S_T, const int* ready, int seg) {
+    T* __restrict__ o, float* S_T, int* ready, int seg) {
   typedef Blk<T, C, DK> B;
   typedef mma16<T> M;
   typedef accb<T> AB;
@@ -1008,7 +1010,10 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
           __builtin_amdgcn_readfirstlane(__hip_atomic_load(ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)));
       if (need > upto) __builtin_amdgcn_s_sleep(8);
     }
-    if (need > upto) patient = false;
+    if (need > upto) {
+      patient = false;
+      if (lane == 0) __hip_atomic_store(ready + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   };
 
   // Single-slot scheme (NBUF = 1): the whole block of chunk cc and its v
@@ -1550,7 +1555,7 @@ bool make_prefill_plan(const kda_prefill_desc* d, int64_t max_chunks, PrefillPla
 template <typename T, int C, int DK, int DV, int WAVES>
 static hipError_t launch_scan(const PrefillPlan& p, const void* v, const int32_t* cu, const int32_t* chunk_off,
                               const int32_t* order, const unsigned char* blocks, const float* S0, void* o,
-                              float* S_T, hipStream_t st, const int* ready = nullptr, int seg = 1) {
+                              float* S_T, hipStream_t st, int* ready = nullptr, int seg = 1) {
   typedef ScanLds<T, C, DK, 16 * WAVES> SL;
   static_assert(SL::total <= 160 * 1024, "scan LDS");
   hipError_t e = set_lds_limit(reinterpret_cast<const void*>(&scan_kernel<T, C, DK, DV, WAVES>), SL::total);
@@ -1643,6 +1648,12 @@ static hipError_t pipe_streams(int64_t scan_wgs, PipeStreams** out) {
       ps->scan_cus = ns;
       cache[dev] = ps;
     } else {  // no CU masks here: fall back to the single-stream schedule
+      if (ps->scan) (void)hipStreamDestroy(ps->scan);
+      if (ps->prep) (void)hipStreamDestroy(ps->prep);
+      if (ps->fork) (void)hipEventDestroy(ps->fork);
+      if (ps->join) (void)hipEventDestroy(ps->join);
+      if (ps->join_prep) (void)hipEventDestroy(ps->join_prep);
+      delete ps;
       (void)hipGetLastError();
       unavailable[dev] = true;
     }

@@ -112,10 +112,15 @@ size_t kda_prefill_workspace_size(const kda_prefill_desc* desc);
  * (N * H * dv / 32 <= 128) the call forks onto two library-owned streams that
  * split the CUs (one runs the serial state pass, the other prepares later
  * chunks and advances a counter in the workspace that the first waits on) and
- * joins back into `stream` with events.  Tools that serialise kernel
- * dispatches (hardware-counter collection) cannot run that schedule: the
+ * joins back into `stream` with events.  That schedule needs the device to
+ * run the two library streams at the same time (each has its own CU-masked
+ * hardware queue): the state pass waits, for a bounded time, for the other
+ * stream's prepared chunks, and if they never come (a tool that serialises
+ * kernel dispatches, such as hardware-counter collection, or an
+ * oversubscribed device) it stops waiting and its results are wrong; it then
+ * sets the second 4-byte word of the workspace's last 256 bytes.  The
  * environment variable KDA_PREFILL_OVERLAP=0, read once per process, selects
- * the one-stream schedule (same kernels and results).
+ * the one-stream schedule (same kernels and results) for such settings.
  *
  * Errors: KDA_ERR_INVALID_ARGUMENT (null pointer where data is required,
  * negative sizes, bad host offsets, misaligned workspace, overlapping buffers),

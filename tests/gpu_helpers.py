@@ -86,3 +86,24 @@ def check(name: str, got: np.ndarray, ref: np.ndarray, tol: float):
     assert np.all(np.isfinite(got)), name + ": non-finite output"
     assert e <= tol, "%s: rel err %.3e > %.0e" % (name, e, tol)
     return e
+
+
+def overlap_counters():
+    """(last segment written, gave-up flag) of the overlapped prefill
+    schedule after the most recent kda.prefill call that used the cached
+    workspace: the workspace's last 256 bytes hold these counters."""
+    import gated_delta_rule_33_amd as kda
+    torch = torch_mod()
+    torch.cuda.synchronize()
+    ws = list(kda._ws_cache.values())[0]
+    w = ws[-256:].view(torch.int32)[:2].cpu().numpy()
+    return int(w[0]), int(w[1])
+
+
+def assert_overlapped_ok():
+    """The call ran the overlapped schedule to the end: more than one segment
+    was published and no scan loader wave stopped waiting for a segment."""
+    last, gave_up = overlap_counters()
+    log("  overlapped schedule: last segment %d, gave up %d" % (last, gave_up))
+    assert gave_up == 0, "a scan loader wave stopped waiting for a prep segment"
+    assert last > 0

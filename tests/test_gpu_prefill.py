@@ -6,7 +6,8 @@ import pytest
 
 import oracle
 import synth
-from tests.gpu_helpers import TOL, check, dev, gpu_prefill, have_gpu, host, log, oracle_prefill
+from tests.gpu_helpers import (TOL, assert_overlapped_ok, check, dev, gpu_prefill, have_gpu, host, log,
+                                oracle_prefill)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not have_gpu(), reason="needs a GPU")]
 
@@ -159,6 +160,7 @@ def test_segmented_schedule(dt, chunk, mode):
         torch.cuda.synchronize()
         assert Sd is None
         o, S = host(od), None
+    assert_overlapped_ok()
     check("o", o, o_ref, TOL[dt])
     if S is not None:
         check("S_T", S, S_ref, TOL[dt])
@@ -171,6 +173,7 @@ def test_segmented_schedule_many_segments():
     log("prefill segmented, 11 segments: %s x 2 heads" % lengths)
     w = synth.make_prefill(lengths, H=2, dk=128, dv=128, io_dtype="bf16", seed=23, S0_std=0.05)
     o, S = gpu_prefill(w)
+    assert_overlapped_ok()
     o_ref, S_ref = oracle_prefill(w)
     check("o", o, o_ref, TOL["bf16"])
     check("S_T", S, S_ref, TOL["bf16"])
@@ -190,6 +193,7 @@ def test_one_stream_schedule_is_bitwise_equal():
     log("prefill one-stream vs overlapped schedule, %s x 4 heads" % lengths)
     w = synth.make_prefill(lengths, H=4, dk=128, dv=128, io_dtype="bf16", seed=20, S0_std=0.05)
     o_ov, S_ov = gpu_prefill(w)
+    assert_overlapped_ok()
     with tempfile.TemporaryDirectory() as td:
         out = os.path.join(td, "one_stream.npz")
         child = (
