@@ -1319,25 +1319,20 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
   };
 
   if constexpr (SL::split) {
+    static_assert(SL::NBUF == 2, "split roles come with the staged output, which needs two slots");
     // D (hi, lo) and the state fragments pass from state to output wave here
     F* const dxp = reinterpret_cast<F*>(smem + SL::dx + cg * SL::dx_group) + lane;
     F* const sxp = dxp + 64 * C / static_cast<int>(sizeof(F));
     int* const xfl = reinterpret_cast<int*>(smem + SL::xflag) + cg;
     if (do_state) {
-      // R rows of the first chunk; with two slots, the rows of chunk cc + 1
-      // are read during chunk cc, after M (the loaders have its early part
-      // resident by then), so the next chunk's products start at once
+      // R rows of the first chunk; the rows of chunk cc + 1 are read during
+      // chunk cc, after M (the loaders have its early part resident by
+      // then), so the next chunk's products start at once
       RowFrags<T, B::RB_R, NSK> fr[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) fr[mt].load(eblk_of(cb) + B::oR, 16 * mt + n, g);
       for (int cc = cb; cc < ce; ++cc) {
         const unsigned char* lblk = lblk_of(cc);
-        if constexpr (SL::NBUF == 1) {
-          if (cc > cb) {
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) fr[mt].load(eblk_of(cc) + B::oR, 16 * mt + n, g);
-          }
-        }
         DIn din;
         load_din(lblk, din);
         F sb[NSK];
@@ -1362,12 +1357,10 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
         RowFrags<T, B::RB_K, NSC> kf[ST];
 #pragma unroll
         for (int st = 0; st < ST; ++st) kf[st].load(lblk, 16 * st + n, g);
-        if constexpr (SL::NBUF == 2) {
-          // next chunk's R rows (past the last chunk: a slot no load is
-          // filling, values unused)
+        // next chunk's R rows (past the last chunk: a slot no load is
+        // filling, values unused)
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) fr[mt].load(eblk_of(cc + 1) + B::oR, 16 * mt + n, g);
-        }
+        for (int mt = 0; mt < MT; ++mt) fr[mt].load(eblk_of(cc + 1) + B::oR, 16 * mt + n, g);
         update_s(lblk, kf, dh);
         chunk_end();
       }
