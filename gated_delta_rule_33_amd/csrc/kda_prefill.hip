@@ -541,8 +541,9 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
     float bt;
   };
   // Rows past the end re-read the last row (all loads issue back to back);
-  // their log_alpha is zeroed and beta = 0 masks them everywhere else.
-  auto fetch = [&](const Item& it, Raw& r) {
+  // their log_alpha is zeroed and beta = 0 masks them everywhere else.  The
+  // gates (log_alpha, beta) and q, k can be fetched separately.
+  auto fetch = [&](const Item& it, Raw& r, bool gates, bool qk) {
     if (it.c >= total) return;
     // thread indices from a zero the compiler cannot see (len <= C): they
     // are recomputed here rather than held in registers across the item loop
@@ -552,16 +553,18 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int e = min(fr0 + i, it.len - 1) * H * DK + fc4;  // < C H DK: 32-bit
-      r.lg[i] = *reinterpret_cast<const f32x4*>(la + tbase + e);
-      r.kr[i] = load4raw(k + tbase + e);
-      r.qr[i] = load4raw(q + tbase + e);
+      if (gates) r.lg[i] = *reinterpret_cast<const f32x4*>(la + tbase + e);
+      if (qk) {
+        r.kr[i] = load4raw(k + tbase + e);
+        r.qr[i] = load4raw(q + tbase + e);
+      }
     }
-    r.bt = (t < C && t < it.len) ? beta[static_cast<size_t>(it.t0 + t) * H + it.h] : 0.f;
+    if (gates) r.bt = (t < C && t < it.len) ? beta[static_cast<size_t>(it.t0 + t) * H + it.h] : 0.f;
   };
   int item = blockIdx.x;
   Item it = locate(item);
   Raw cur;
-  fetch(it, cur);
+  fetch(it, cur, true, true);
   for (; item < nitems; item += gridDim.x) {
     const Item nit = locate(item + gridDim.x);
     Raw nxt;
@@ -622,6 +625,12 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
   if (tid < DK) reinterpret_cast<float*>(blk + B::oG)[tid] = __builtin_amdgcn_exp2f(gE[(NB - 1) * DK + tid]);
   if (tid < C) reinterpret_cast<float*>(blk + B::oB)[tid] = bet[tid];
 
+  // The next item's gates (half of its input bytes) load from here on: this
+  // item's copies are dead and the registers stay free through the factor
+  // pass.  Issued one phase later, behind this item's block stores, the
+  // prep ran 4-6% slower.
+  fetch(nit, nxt, true, false);
+
   // ---- element factors, S-independent outputs ---------------------------
   {
     const int I = r0 >> 4;  // all of this thread's rows are in block I
@@ -679,8 +688,10 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
   }
   __syncthreads();
     }  // item, first half
-    // next item's inputs: issued once this item's elementwise inputs are dead
-    fetch(nit, nxt);
+    // The next item's q and k, whose registers are free from here on.  Issued
+    // before this barrier (among or right after the block stores), or row by
+    // row inside the factor pass, the prep ran 11-16% slower.
+    fetch(nit, nxt, false, true);
     if (it.c < total) {
   unsigned char* blk = ws + (static_cast<size_t>(c) * H + h) * B::bytes;
 
