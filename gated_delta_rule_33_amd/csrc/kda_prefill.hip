@@ -398,13 +398,11 @@ struct PrepLds {
   static constexpr int RBK = DK * static_cast<int>(sizeof(T));  // row bytes of Krd / Qrd / Kc
   static constexpr int AP = C + 1;               // pitch (floats) of A / Ti
   static constexpr int CP = C + 8;               // pitch (elements) of the P staging tile
-  static constexpr int SP = 17;                  // pitch (floats) of 16x16 inverse scratch tiles
   static constexpr size_t a16(size_t x) { return (x + 15) / 16 * 16; }
   static constexpr size_t mx(size_t a, size_t b) { return a > b ? a : b; }
   static constexpr size_t szTi = static_cast<size_t>(C) * AP * 4;
-  static constexpr size_t szScr = static_cast<size_t>(NB) * 3 * 16 * SP * 4;  // NB waves x 3 tiles
-  // region 0: Krd, Qrd, Kc (io, swizzled rows) -> later Ti + inverse scratch (f32)
-  static constexpr size_t r0 = a16(mx(static_cast<size_t>(3) * C * RBK, szTi + szScr));
+  // region 0: Krd, Qrd, Kc (io, swizzled rows) -> later Ti (f32)
+  static constexpr size_t r0 = a16(mx(static_cast<size_t>(3) * C * RBK, szTi));
   // region 1: cumsum partials [NRB][DK] (f32) -> later A (f32)
   static constexpr size_t r1 = a16(mx(static_cast<size_t>(C) * AP * 4, static_cast<size_t>(NRB) * DK * 4));
   // region 2: gB gM gE [NB][DK] (f32) -> later P staging (io)
@@ -457,14 +455,30 @@ struct natf<float, RB> {
   }
 };
 
-// 16x16x16 fp32 product X * Y on MFMA: X row-major in LDS (pitch xp floats),
-// Y in accumulator layout (lane (n, g) holds Y[4g + i][n]); k-step s pairs
-// X[m][4g + s] with Y[4g + s][n].
-__device__ __forceinline__ f32x4 mm16_lds_acc(const float* X, int xp, f32x4 Y, int m, int g, float xsign = 1.f) {
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+// (I + A_II)^{-1} of one 16x16 diagonal block on fp32 MFMA, in registers.
+// With M = -A_II (strictly lower, so M^16 = 0) the inverse is
+// (I + M)(I + M^2)(I + M^4)(I + M^8).  m and mt hold M and M^T in accumulator
+// layout (lane (n, g) holds X[4g + i][n] in slot i).  A product X Y takes its
+// left factor as X^T in accumulator layout, so the powers of M are formed in
+// both layouts (M^8 only transposed), and since powers of M commute with each
+// other and with the partial products, every product puts a power on the left.
+__device__ __forceinline__ f32x4 unit_lower_inverse16(f32x4 m, f32x4 mt, int n, int g) {
+  auto mul = [](f32x4 xt, f32x4 y) {  // X Y
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int s = 0; s < 4; ++s) acc = mma16<float>::mma(xsign * X[m * xp + 4 * g + s], Y[s], acc);
-  return acc;
+    for (int s = 0; s < 4; ++s) acc = mma16<float>::mma(xt[s], y[s], acc);
+    return acc;
+  };
+  const f32x4 m2 = mul(mt, m), m2t = mul(m, mt);
+  const f32x4 m4t = mul(m2, m2t);
+  const f32x4 m8t = mul(mul(m2t, m2), m4t);  // (M^4 M^4)^T from M^4 and (M^4)^T
+  const f32x4 m3 = mul(mt, m2);
+  f32x4 p;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) p[i] = ((4 * g + i) == n ? 1.f : 0.f) + m[i] + m2[i] + m3[i];  // (I + M)(I + M^2)
+  p += mul(m4t, p);  // ... (I + M^4)
+  p += mul(m8t, p);  // ... (I + M^8)
+  return p;
 }
 
 // Waves per SIMD the prep kernel is built for: as many workgroups as LDS
@@ -495,12 +509,12 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
   constexpr int NB = L::NB;
   constexpr int RPT = C / L::NRB;  // rows per thread
   static_assert(RPT >= 1 && 16 % RPT == 0, "row blocks must tile 16-row sub-blocks");
+  static_assert(NB < kPrepThreads / 64, "diagonal pairs take one wave each, and at least one wave is left");
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* Krd = smem + L::o0;
   unsigned char* Qrd = Krd + C * L::RBK;
   unsigned char* Kc = Qrd + C * L::RBK;
   float* Ti = reinterpret_cast<float*>(smem + L::o0);
-  float* scr = reinterpret_cast<float*>(smem + L::o0 + L::szTi);
   float* A = reinterpret_cast<float*>(smem + L::o1);
   float* gB = reinterpret_cast<float*>(smem + L::o2);
   float* gM = gB + NB * DK;
@@ -695,14 +709,13 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
     if (it.c < total) {
   unsigned char* blk = ws + (static_cast<size_t>(c) * H + h) * B::bytes;
 
-  // ---- a3: gated k k^T (A, fp32 in LDS) and q k^T (P) via MFMA ------------
-  for (int pp = wave; pp < L::NLB; pp += kPrepThreads / 64) {
-    int I = 0;
-    while ((I + 1) * (I + 2) / 2 <= pp) ++I;
-    const int J = pp - I * (I + 1) / 2;
-    const float* f = fv + pp * DK;
+  // ---- a3: gated k k^T (A, fp32 in LDS) and q k^T (P) via MFMA, and the
+  // diagonal blocks of the UT inverse T = (I + A)^{-1} ----------------------
+  // Block pair (I, J <= I); returns this lane's A values (beta-scaled, masked).
+  auto pair = [&](int I, int J) {
+    const float* f = fv + (I * (I + 1) / 2 + J) * DK;
     f32x4 aA = {0.f, 0.f, 0.f, 0.f}, aP = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
+#pragma unroll 8
     for (int k0 = 0; k0 < DK; k0 += M::KS) {
       const typename M::frag bf = natf<T, L::RBK>::scaled(Kc, 16 * J + n, f, k0, g);
       aA = M::mma(natf<T, L::RBK>::raw(Krd, 16 * I + n, k0, g), bf, aA);
@@ -718,66 +731,79 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
       if (I == J && rr < n) pv = 0.f;
       A[row * L::AP + col] = a;
       lds_put<T>(Ps + row * L::CP + col, pv);
+      aA[i] = a;
+    }
+    return aA;
+  };
+  // Waves 0..NB-1 take one diagonal pair each and invert I + A_II right away
+  // from registers; the other waves take the off-diagonal pairs.  Until the
+  // barrier the T tile's LDS still holds Krd/Qrd/Kc, so the inverse stays in
+  // registers and a transposed copy goes to the upper triangle of A's block
+  // (I, I), which A (strictly lower) leaves unused: T_II[r][c], r >= c, at
+  // A_II's position (c, r).
+  f32x4 tii = {0.f, 0.f, 0.f, 0.f};
+  if (wave < NB) {
+    const f32x4 a = pair(wave, wave);
+    float* Ab = A + (16 * wave) * L::AP + 16 * wave;
+    f32x4 m, mt;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      m[i] = -a[i];
+      mt[i] = -Ab[n * L::AP + 4 * g + i];  // written by other lanes of this wave
+    }
+    tii = unit_lower_inverse16(m, mt, n, g);
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (4 * g + i >= n) Ab[n * L::AP + 4 * g + i] = tii[i];
+  } else {
+    // the o-th off-diagonal pair, row by row: (1,0), (2,0), (2,1), (3,0), ...
+    for (int o = wave - NB; o < NB * (NB - 1) / 2; o += kPrepThreads / 64 - NB) {
+      int I = 1;
+      while ((I + 1) * I / 2 <= o) ++I;
+      pair(I, o - I * (I - 1) / 2);
     }
   }
   __syncthreads();
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(blk, 0, static_cast<int>(B::bytes), 0x00020000);
-  for (int idx = tid; idx < C * C / 4; idx += kPrepThreads) {
-    const unsigned r = static_cast<unsigned>(idx) / (C / 4), c4b = (static_cast<unsigned>(idx) % (C / 4)) * 4;
-    typename raw4<T>::type x = {};
-    if ((c4b >> 4) <= (r >> 4)) x = *reinterpret_cast<const typename raw4<T>::type*>(Ps + r * L::CP + c4b);
-    if (!B::TRI || r >= 32 || c4b < 32) buffer_store_raw4(wr, static_cast<int>(B::oP + tri_off<T, C>(r, c4b)), x);
+  if (wave < NB) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Ti[(16 * wave + 4 * g + i) * L::AP + 16 * wave + n] = tii[i];
   }
-
-  // ---- a4: T = (I + A)^{-1} ----------------------------------------------
-  // Diagonal blocks: with M = -A_II (strictly lower, M^16 = 0),
-  //   (I + A_II)^{-1} = (I + M)(I + M^2)(I + M^4)(I + M^8),
-  // six 16x16x16 fp32 MFMA products per block.
-  for (int I = wave; I < NB; I += kPrepThreads / 64) {
-    float* s1 = scr + wave * 3 * 16 * L::SP;
-    float* s2 = s1 + 16 * L::SP;
-    float* s3 = s2 + 16 * L::SP;
-    const float* Aii = A + (16 * I) * L::AP + 16 * I;
-    f32x4 m1;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) m1[i] = -Aii[(4 * g + i) * L::AP + n];
-    const f32x4 m2 = mm16_lds_acc(Aii, L::AP, m1, n, g, -1.f);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s1[(4 * g + i) * L::SP + n] = m2[i];
-    const f32x4 m4 = mm16_lds_acc(s1, L::SP, m2, n, g);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s2[(4 * g + i) * L::SP + n] = m4[i];
-    const f32x4 m8 = mm16_lds_acc(s2, L::SP, m4, n, g);
-    const f32x4 m12 = mm16_lds_acc(Aii, L::AP, m2, n, g, -1.f);  // M * M^2
-    f32x4 pc;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pc[i] = ((4 * g + i) == n ? 1.f : 0.f) + m1[i] + m2[i] + m12[i];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s3[(4 * g + i) * L::SP + n] = pc[i];
-    pc += mm16_lds_acc(s3, L::SP, m4, n, g);  // (I + M)(I + M^2)(I + M^4)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s3[(4 * g + i) * L::SP + n] = pc[i];
-    pc += mm16_lds_acc(s3, L::SP, m8, n, g);  // ... (I + M^8)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) Ti[(16 * I + 4 * g + i) * L::AP + 16 * I + n] = pc[i];
-  }
-  __syncthreads();
-  // Off-diagonal blocks by distance d: T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ.
-  for (int d = 1; d < NB; ++d) {
-    for (int J = wave; J < NB - d; J += kPrepThreads / 64) {
-      const int I = J + d;
+  if (wave < NB - 1) {
+    // ---- a4: column J of T below the diagonal, top to bottom, one wave:
+    //   T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ
+    // every T_KJ is this wave's own earlier result; T_II is read from its
+    // transposed copy in A.
+    const int J = wave;
+    asm volatile("" ::: "memory");
+    for (int I = J + 1; I < NB; ++I) {
       f32x4 x = {0.f, 0.f, 0.f, 0.f};
       for (int K = J; K < I; ++K) {
 #pragma unroll
         for (int s = 0; s < 4; ++s)
           x = MF::mma(A[(16 * I + n) * L::AP + 16 * K + 4 * s + g], Ti[(16 * K + 4 * s + g) * L::AP + 16 * J + n], x);
       }
-      const f32x4 t = mm16_lds_acc(Ti + (16 * I) * L::AP + 16 * I, L::AP, x, n, g);
+      const float* Ab = A + (16 * I) * L::AP + 16 * I;
+      f32x4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int cc = 4 * g + s;  // T_II[n][cc]
+        t = MF::mma(cc <= n ? Ab[cc * L::AP + n] : 0.f, x[s], t);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) Ti[(16 * I + 4 * g + i) * L::AP + 16 * J + n] = -t[i];
     }
-    __syncthreads();
+  } else {
+    // the remaining waves store P meanwhile
+    for (int idx = tid - 64 * (NB - 1); idx < C * C / 4; idx += kPrepThreads - 64 * (NB - 1)) {
+      const unsigned r = static_cast<unsigned>(idx) / (C / 4), c4b = (static_cast<unsigned>(idx) % (C / 4)) * 4;
+      typename raw4<T>::type x = {};
+      if ((c4b >> 4) <= (r >> 4)) x = *reinterpret_cast<const typename raw4<T>::type*>(Ps + r * L::CP + c4b);
+      if (!B::TRI || r >= 32 || c4b < 32) buffer_store_raw4(wr, static_cast<int>(B::oP + tri_off<T, C>(r, c4b)), x);
+    }
   }
+  __syncthreads();
   for (int idx = tid; idx < C * C / 4; idx += kPrepThreads) {
     const unsigned r = static_cast<unsigned>(idx) / (C / 4), c4b = (static_cast<unsigned>(idx) % (C / 4)) * 4;
     f32x4 x = {0.f, 0.f, 0.f, 0.f};
