@@ -24,7 +24,8 @@
 //   chunk_offsets_kernel  chunk offsets per sequence + longest-first order
 //   prep_kernel           persistent, (chunk, head) items: everything that
 //                         does not depend on S (gate cumsum, A and P via MFMA,
-//                         T by blocked forward substitution, R, Qh, Kb^T,
+//                         T by blocked forward substitution with the diagonal
+//                         blocks from a nilpotent product, R, Qh, Kb^T,
 //                         e^{g_last}), written to one workspace block per
 //                         (chunk, head)
 //   scan_kernel           grid (sequence, head, value tile): the serial chunk
