@@ -746,6 +746,7 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
   if (wave < NB) {
     const f32x4 a = pair(wave, wave);
     float* Ab = A + (16 * wave) * L::AP + 16 * wave;
+    __builtin_amdgcn_wave_barrier();  // other lanes' A_II stores before the reads below
     f32x4 m, mt;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -753,7 +754,7 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
       mt[i] = -Ab[n * L::AP + 4 * g + i];  // written by other lanes of this wave
     }
     tii = unit_lower_inverse16(m, mt, n, g);
-    asm volatile("" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (4 * g + i >= n) Ab[n * L::AP + 4 * g + i] = tii[i];
@@ -777,8 +778,8 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
     // every T_KJ is this wave's own earlier result; T_II is read from its
     // transposed copy in A.
     const int J = wave;
-    asm volatile("" ::: "memory");
     for (int I = J + 1; I < NB; ++I) {
+      __builtin_amdgcn_wave_barrier();  // T_KJ stored by other lanes of this wave
       f32x4 x = {0.f, 0.f, 0.f, 0.f};
       for (int K = J; K < I; ++K) {
 #pragma unroll
