@@ -36,13 +36,18 @@
 // With few (sequence, head) pairs the scan runs on half of the CUs beside
 // the prep of later chunks on the other half (launch_prefill below).
 //
-// Exponent safety.  e^{g_r-g_s} is factorised around references inside the
-// chunk so that no factor exceeds the fp32 range: for a 16-row block I below
-// the diagonal (rows r in I, columns s in J < I) the row side uses
-// e^{g_r - g_{b_I}} e^{g_{b_I} - g_{e_J}} and the column side e^{g_{e_J} - g_s}
-// (b_I first row of I, e_J last row of J; every factor <= 1).  Diagonal
-// blocks use the block's 9th row as reference, so a factor can reach
-// e^{8 * max|log_alpha|}; the library requires log_alpha >= -10.
+// Exponent safety.  e^{g_r-g_s} (s <= r) is formed as the product
+// [e^{g_r - g_{m_I}}] [e^{g_{m_I} - g_{e_J}}] [e^{g_{e_J} - g_s}] for r in the
+// 16-row block I and s in block J <= I (m_I the 9th row of I, e_J the last row
+// of J), see the prep kernel.  The first factor, and the middle one of a
+// diagonal block, grow with the decay over at most 8 and 7 tokens; the last
+// factor, and the middle one of an off-diagonal block, shrink with the decay
+// over at most 15 and 9 tokens.  All of them stay in the fp32 normal range
+// when, per channel, any 15 consecutive tokens have log_alpha summing to at
+// least -80 (log_alpha >= -5 per element suffices); a product below that
+// range is then below e^{-80} too.  Beyond it the column operand of a
+// diagonal block underflows while the ratio it stands for (1 for s = r) does
+// not, so the library requires the bound.
 
 #include <hip/hip_ext.h>
 
@@ -386,8 +391,9 @@ __device__ __forceinline__ void buffer_store_raw4(__amdgpu_buffer_rsrc_t r, int 
 // with m_I the 9th row of block I and e_J the last row of block J.  The first
 // factor goes into the stored row operands (Krd, Qrd), the last into the
 // stored column operand (Kc), and the middle one is a per-channel vector that
-// scales the column fragment of block (I, J).  Every factor stays below
-// e^{8 max|log_alpha|}; the row operands are read raw.
+// scales the column fragment of block (I, J); the row operands are read raw.
+// The range each factor spans is bounded in the exponent-safety note at the
+// top of this file.
 // ---------------------------------------------------------------------------
 constexpr int kPrepThreads = 512;
 

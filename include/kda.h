@@ -33,10 +33,13 @@
  *     per device, on which concurrent overlapped calls for one device take
  *     turns to enqueue their work.
  *   - Device-side preconditions that are documented but not checked:
- *     finite inputs; log_alpha <= 0; for the chunked prefill additionally
- *     log_alpha >= -10 per element (the intra-chunk gate ratios are
- *     factorised around references at most 8 tokens away, which stays inside
- *     the fp32 exponent range only under this bound); when no host mirror of
+ *     finite inputs; log_alpha <= 0; for the chunked prefill additionally,
+ *     per channel, the log_alpha of any 15 consecutive tokens of a sequence
+ *     sum to at least -80 (log_alpha >= -5 per element suffices): the
+ *     intra-chunk gate ratios are factorised around references inside each
+ *     16-token block, and every factor must stay inside the fp32 range
+ *     (beyond it the column operand of a diagonal block underflows while the
+ *     ratio it stands for does not, so results are wrong); when no host mirror of
  *     cu_seqlens is given, cu_seqlens[0] = 0, non-decreasing and
  *     cu_seqlens[N] = total_tokens.
  */
