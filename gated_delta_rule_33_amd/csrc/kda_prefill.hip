@@ -36,18 +36,20 @@
 // With few (sequence, head) pairs the scan runs on half of the CUs beside
 // the prep of later chunks on the other half (launch_prefill below).
 //
-// Exponent safety.  e^{g_r-g_s} (s <= r) is formed as the product
-// [e^{g_r - g_{m_I}}] [e^{g_{m_I} - g_{e_J}}] [e^{g_{e_J} - g_s}] for r in the
-// 16-row block I and s in block J <= I (m_I the 9th row of I, e_J the last row
-// of J), see the prep kernel.  The first factor, and the middle one of a
-// diagonal block, grow with the decay over at most 8 and 7 tokens; the last
-// factor, and the middle one of an off-diagonal block, shrink with the decay
-// over at most 15 and 9 tokens.  All of them stay in the fp32 normal range
-// when, per channel, any 15 consecutive tokens have log_alpha summing to at
-// least -80 (log_alpha >= -5 per element suffices); a product below that
-// range is then below e^{-80} too.  Beyond it the column operand of a
-// diagonal block underflows while the ratio it stands for (1 for s = r) does
-// not, so the library requires the bound.
+// Exponent safety.  e^{g_r-g_s} (s <= r, r in the 16-row block I, s in block
+// J <= I) is built from factors around references inside the blocks (m_I
+// the 9th row of I, e_J the last row of J), see the prep kernel: the row
+// operands carry e^{g_r - g_{m_I}} and the column operand e^{g_{m_J} - g_s},
+// each spanning the decay over at most 8 tokens either way.  A diagonal pair
+// (I = J) multiplies them as they are; an off-diagonal pair first turns the
+// column operand into e^{g_{e_J} - g_s} (<= 1) and then scales it by
+// e^{g_{m_I} - g_{e_J}} (<= 1, the decay over at least 9 tokens).  All
+// factors stay in the fp32 normal range when, per channel, any 9
+// consecutive tokens have log_alpha summing to at least -80 (log_alpha >= -8
+// per element suffices); an intermediate that still underflows then stands
+// for a ratio below e^{-15}.  Past the bound the last scale factor of an
+// off-diagonal block next to the diagonal underflows while the ratio it
+// stands for need not be small, so the library requires it.
 
 #include <hip/hip_ext.h>
 
@@ -387,13 +389,14 @@ __device__ __forceinline__ void buffer_store_raw4(__amdgpu_buffer_rsrc_t r, int 
 // rows of q, k and log_alpha.
 //
 // Gated products.  For rows r of 16-row block I and columns s of block J <= I
-//   e^{g_r - g_s} = [e^{g_r - g_{m_I}}] [e^{g_{m_I} - g_{e_J}}] [e^{g_{e_J} - g_s}]
+//   e^{g_r - g_s} = [e^{g_r - g_{m_I}}] [e^{g_{m_J} - g_s}]                      (I = J)
+//                 = [e^{g_r - g_{m_I}}] [e^{g_{m_J} - g_s} e^{g_{e_J} - g_{m_J}}] e^{g_{m_I} - g_{e_J}}  (J < I)
 // with m_I the 9th row of block I and e_J the last row of block J.  The first
-// factor goes into the stored row operands (Krd, Qrd), the last into the
-// stored column operand (Kc), and the middle one is a per-channel vector that
-// scales the column fragment of block (I, J); the row operands are read raw.
-// The range each factor spans is bounded in the exponent-safety note at the
-// top of this file.
+// factor goes into the stored row operands (Krd, Qrd), e^{g_{m_J} - g_s} into
+// the stored column operand (Kc); a diagonal pair reads both raw, an
+// off-diagonal pair scales the column fragment by the two per-channel
+// vectors, left to right.  The range each factor spans is bounded in the
+// exponent-safety note at the top of this file.
 // ---------------------------------------------------------------------------
 constexpr int kPrepThreads = 512;
 
@@ -412,8 +415,8 @@ struct PrepLds {
   static constexpr size_t r0 = a16(mx(static_cast<size_t>(3) * C * RBK, szTi));
   // region 1: cumsum partials [NRB][DK] (f32) -> later A (f32)
   static constexpr size_t r1 = a16(mx(static_cast<size_t>(C) * AP * 4, static_cast<size_t>(NRB) * DK * 4));
-  // region 2: gB gM gE [NB][DK] (f32) -> later P staging (io)
-  static constexpr size_t r2 = a16(mx(static_cast<size_t>(3 * NB) * DK * 4, static_cast<size_t>(C) * CP * sizeof(T)));
+  // region 2: gM gE [NB][DK] (f32) -> later P staging (io)
+  static constexpr size_t r2 = a16(mx(static_cast<size_t>(2 * NB) * DK * 4, static_cast<size_t>(C) * CP * sizeof(T)));
   // region 3: block-pair vectors f[NLB][DK] (f32)
   static constexpr size_t r3 = a16(static_cast<size_t>(NLB) * DK * 4);
   static constexpr size_t o0 = 0, o1 = r0, o2 = o1 + r1, o3 = o2 + r2, o4 = o3 + r3;
@@ -436,19 +439,24 @@ struct natf<bf16_t, RB> {
   __device__ __forceinline__ static bf16x8 raw(const unsigned char* t, int row, int k0, int g) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(t + loff<bf16_t, RB>(row, k0 + 8 * g)));
   }
-  __device__ __forceinline__ static bf16x8 scaled(const unsigned char* t, int row, const float* sc, int k0, int g) {
+  // (x * a) * b per channel, in that order (x * a may underflow where the
+  // product is negligible; a * b may underflow where it is not)
+  __device__ __forceinline__ static bf16x8 scaled(const unsigned char* t, int row, const float* a, const float* b,
+                                                  int k0, int g) {
     const uint4 u = *reinterpret_cast<const uint4*>(t + loff<bf16_t, RB>(row, k0 + 8 * g));
-    const f32x4 s0 = *reinterpret_cast<const f32x4*>(sc + k0 + 8 * g);
-    const f32x4 s1 = *reinterpret_cast<const f32x4*>(sc + k0 + 8 * g + 4);
+    const f32x4 a0 = *reinterpret_cast<const f32x4*>(a + k0 + 8 * g);
+    const f32x4 a1 = *reinterpret_cast<const f32x4*>(a + k0 + 8 * g + 4);
+    const f32x4 b0 = *reinterpret_cast<const f32x4*>(b + k0 + 8 * g);
+    const f32x4 b1 = *reinterpret_cast<const f32x4*>(b + k0 + 8 * g + 4);
     bf16x8 r;
-    r[0] = to_bf(__uint_as_float(u.x << 16) * s0[0]);
-    r[1] = to_bf(__uint_as_float(u.x & 0xFFFF0000u) * s0[1]);
-    r[2] = to_bf(__uint_as_float(u.y << 16) * s0[2]);
-    r[3] = to_bf(__uint_as_float(u.y & 0xFFFF0000u) * s0[3]);
-    r[4] = to_bf(__uint_as_float(u.z << 16) * s1[0]);
-    r[5] = to_bf(__uint_as_float(u.z & 0xFFFF0000u) * s1[1]);
-    r[6] = to_bf(__uint_as_float(u.w << 16) * s1[2]);
-    r[7] = to_bf(__uint_as_float(u.w & 0xFFFF0000u) * s1[3]);
+    r[0] = to_bf(__uint_as_float(u.x << 16) * a0[0] * b0[0]);
+    r[1] = to_bf(__uint_as_float(u.x & 0xFFFF0000u) * a0[1] * b0[1]);
+    r[2] = to_bf(__uint_as_float(u.y << 16) * a0[2] * b0[2]);
+    r[3] = to_bf(__uint_as_float(u.y & 0xFFFF0000u) * a0[3] * b0[3]);
+    r[4] = to_bf(__uint_as_float(u.z << 16) * a1[0] * b1[0]);
+    r[5] = to_bf(__uint_as_float(u.z & 0xFFFF0000u) * a1[1] * b1[1]);
+    r[6] = to_bf(__uint_as_float(u.w << 16) * a1[2] * b1[2]);
+    r[7] = to_bf(__uint_as_float(u.w & 0xFFFF0000u) * a1[3] * b1[3]);
     return r;
   }
 };
@@ -457,8 +465,9 @@ struct natf<float, RB> {
   __device__ __forceinline__ static float raw(const unsigned char* t, int row, int k0, int g) {
     return *reinterpret_cast<const float*>(t + loff<float, RB>(row, k0 + g));
   }
-  __device__ __forceinline__ static float scaled(const unsigned char* t, int row, const float* sc, int k0, int g) {
-    return raw(t, row, k0, g) * sc[k0 + g];
+  __device__ __forceinline__ static float scaled(const unsigned char* t, int row, const float* a, const float* b,
+                                                int k0, int g) {
+    return raw(t, row, k0, g) * a[k0 + g] * b[k0 + g];
   }
 };
 
@@ -523,8 +532,7 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
   unsigned char* Kc = Qrd + C * L::RBK;
   float* Ti = reinterpret_cast<float*>(smem + L::o0);
   float* A = reinterpret_cast<float*>(smem + L::o1);
-  float* gB = reinterpret_cast<float*>(smem + L::o2);
-  float* gM = gB + NB * DK;
+  float* gM = reinterpret_cast<float*>(smem + L::o2);
   float* gE = gM + NB * DK;
   T* Ps = reinterpret_cast<T*>(smem + L::o2);
   float* fv = reinterpret_cast<float*>(smem + L::o3);
@@ -627,21 +635,22 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
     for (int i = 0; i < RPT; ++i) {
       lg[i] += off;
       const int r = r0 + i, I = r >> 4, rr = r & 15;
-      if (rr == 0) *reinterpret_cast<f32x4*>(gB + I * DK + c4) = lg[i];
       if (rr == 8) *reinterpret_cast<f32x4*>(gM + I * DK + c4) = lg[i];
       if (rr == 15) *reinterpret_cast<f32x4*>(gE + I * DK + c4) = lg[i];
     }
   }
   __syncthreads();
 
-  // ---- block-pair vectors e^{g_{m_I} - g_{e_J}}, J <= I ---------------------
+  // ---- block-pair vectors: e^{g_{m_I} - g_{e_J}} for J < I; the slot of the
+  // diagonal pair (J, J), which needs no scaling, holds e^{g_{e_J} - g_{m_J}}
   for (int idx = tid; idx < L::NLB * DK; idx += kPrepThreads) {
     const unsigned pp = static_cast<unsigned>(idx) / DK, ch = static_cast<unsigned>(idx) % DK;
     unsigned I = 0;
 #pragma unroll
     for (unsigned t = 1; t < static_cast<unsigned>(NB); ++t) I += pp >= t * (t + 1) / 2 ? 1u : 0u;
     const unsigned J = pp - I * (I + 1) / 2;
-    fv[idx] = __builtin_amdgcn_exp2f(gM[I * DK + ch] - gE[J * DK + ch]);
+    fv[idx] = I == J ? __builtin_amdgcn_exp2f(gE[J * DK + ch] - gM[J * DK + ch])
+                     : __builtin_amdgcn_exp2f(gM[I * DK + ch] - gE[J * DK + ch]);
   }
   if (tid < DK) reinterpret_cast<float*>(blk + B::oG)[tid] = __builtin_amdgcn_exp2f(gE[(NB - 1) * DK + tid]);
   if (tid < C) reinterpret_cast<float*>(blk + B::oB)[tid] = bet[tid];
@@ -655,31 +664,30 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
   // ---- element factors, S-independent outputs ---------------------------
   {
     const int I = r0 >> 4;  // all of this thread's rows are in block I
-    const f32x4 gb = *reinterpret_cast<const f32x4*>(gB + I * DK + c4);
     const f32x4 gm = *reinterpret_cast<const f32x4*>(gM + I * DK + c4);
-    const f32x4 ge = *reinterpret_cast<const f32x4*>(gE + I * DK + c4);
     const f32x4 gz = *reinterpret_cast<const f32x4*>(gE + (NB - 1) * DK + c4);
-    f32x4 drv, ebv, eev, kb[RPT];
+    f32x4 emv, eev, kb[RPT];
     float bt[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) bt[i] = bet[r0 + i];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      drv[j] = __builtin_amdgcn_exp2f(gb[j] - gm[j]);  // e^{g_b - g_m}: >= 1, at most 8 tokens of decay
-      ebv[j] = __builtin_amdgcn_exp2f(gb[j]);          // e^{g_b} <= 1
-      eev[j] = __builtin_amdgcn_exp2f(gz[j] - ge[j]);  // e^{g_last - g_e} <= 1
+      emv[j] = __builtin_amdgcn_exp2f(gm[j]);          // e^{g_m} <= 1
+      eev[j] = __builtin_amdgcn_exp2f(gz[j] - gm[j]);  // e^{g_last - g_m} <= 1
     }
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const unsigned r = static_cast<unsigned>(r0 + i);
-      f32x4 fr, fc;
+      // e^{g_r - g_m} and e^{g_m - g_r}: each spans the decay over at most 8
+      // tokens either way (computed directly: a product through a farther
+      // reference can underflow where the ratio does not)
+      f32x4 frd, fc;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        fr[j] = __builtin_amdgcn_exp2f(lg[i][j] - gb[j]);  // e^{g_r - g_b} <= 1
-        fc[j] = __builtin_amdgcn_exp2f(ge[j] - lg[i][j]);  // e^{g_e - g_r} <= 1
+        frd[j] = __builtin_amdgcn_exp2f(lg[i][j] - gm[j]);
+        fc[j] = __builtin_amdgcn_exp2f(gm[j] - lg[i][j]);
       }
-      const f32x4 frd = fr * drv;  // e^{g_r - g_m}
-      const f32x4 fre = fr * ebv;  // e^{g_r}
+      const f32x4 fre = frd * emv;  // e^{g_r}: underflows only where e^{g_r} is negligible
       const unsigned lo = loff<T, L::RBK>(r, static_cast<unsigned>(c4));
       store4(reinterpret_cast<T*>(Krd + lo), kv[i] * frd);
       store4(reinterpret_cast<T*>(Qrd + lo), qv[i] * frd);
@@ -719,12 +727,14 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
   // ---- a3: gated k k^T (A, fp32 in LDS) and q k^T (P) via MFMA, and the
   // diagonal blocks of the UT inverse T = (I + A)^{-1} ----------------------
   // Block pair (I, J <= I); returns this lane's A values (beta-scaled, masked).
-  auto pair = [&](int I, int J) {
-    const float* f = fv + (I * (I + 1) / 2 + J) * DK;
+  auto pair = [&](int I, int J, bool diag) {
+    const float* fe = fv + (J * (J + 1) / 2 + J) * DK;  // e^{g_{e_J} - g_{m_J}}
+    const float* f = fv + (I * (I + 1) / 2 + J) * DK;   // e^{g_{m_I} - g_{e_J}}
     f32x4 aA = {0.f, 0.f, 0.f, 0.f}, aP = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
     for (int k0 = 0; k0 < DK; k0 += M::KS) {
-      const typename M::frag bf = natf<T, L::RBK>::scaled(Kc, 16 * J + n, f, k0, g);
+      const typename M::frag bf = diag ? natf<T, L::RBK>::raw(Kc, 16 * J + n, k0, g)
+                                       : natf<T, L::RBK>::scaled(Kc, 16 * J + n, fe, f, k0, g);
       aA = M::mma(natf<T, L::RBK>::raw(Krd, 16 * I + n, k0, g), bf, aA);
       aP = M::mma(natf<T, L::RBK>::raw(Qrd, 16 * I + n, k0, g), bf, aP);
     }
@@ -750,7 +760,7 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
   // A_II's position (c, r).
   f32x4 tii = {0.f, 0.f, 0.f, 0.f};
   if (wave < NB) {
-    const f32x4 a = pair(wave, wave);
+    const f32x4 a = pair(wave, wave, true);
     float* Ab = A + (16 * wave) * L::AP + 16 * wave;
     __builtin_amdgcn_wave_barrier();  // other lanes' A_II stores before the reads below
     f32x4 m, mt;
@@ -769,7 +779,7 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
     for (int o = wave - NB; o < NB * (NB - 1) / 2; o += kPrepThreads / 64 - NB) {
       int I = 1;
       while ((I + 1) * I / 2 <= o) ++I;
-      pair(I, o - I * (I - 1) / 2);
+      pair(I, o - I * (I - 1) / 2, false);
     }
   }
   __syncthreads();
@@ -1234,7 +1244,7 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
   const int n = lane & 15, g = lane >> 4;
   const int role = SL::split ? wave / WAVES : 0;
   const int cg = SL::split ? wave % WAVES : wave;
-  const bool do_state = role == 0, do_out = !SL::split || role == 1;
+  const bool do_state = role == 0;
   const int col = tile * TILE + cg * 16 + n;
   f32x4 S[ST];
   const size_t sbase = (static_cast<size_t>(seq) * H + h) * DK * DV;

@@ -34,12 +34,12 @@
  *     turns to enqueue their work.
  *   - Device-side preconditions that are documented but not checked:
  *     finite inputs; log_alpha <= 0; for the chunked prefill additionally,
- *     per channel, the log_alpha of any 15 consecutive tokens of a sequence
- *     sum to at least -80 (log_alpha >= -5 per element suffices): the
+ *     per channel, the log_alpha of any 9 consecutive tokens of a sequence
+ *     sum to at least -80 (log_alpha >= -8 per element suffices): the
  *     intra-chunk gate ratios are factorised around references inside each
  *     16-token block, and every factor must stay inside the fp32 range
- *     (beyond it the column operand of a diagonal block underflows while the
- *     ratio it stands for does not, so results are wrong); when no host mirror of
+ *     (beyond it a scale factor of an off-diagonal block underflows while the
+ *     ratio it stands for need not be small, so results are wrong); when no host mirror of
  *     cu_seqlens is given, cu_seqlens[0] = 0, non-decreasing and
  *     cu_seqlens[N] = total_tokens.
  */

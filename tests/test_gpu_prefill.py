@@ -97,20 +97,21 @@ def test_pure_decay_closed_form_on_gpu():
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 @pytest.mark.parametrize("pattern", ["half", "all"])
-def test_gate_decay_at_documented_limit(dt, pattern):
-    """log_alpha = -5 on every token (the per-element bound of the chunked
-    prefill: any 15 consecutive tokens sum to -75 >= -80) on every channel,
-    or on every other channel with no decay (log_alpha = 0) on the rest;
-    beta = 1.  The intra-chunk factors then span their widest range: up to
-    e^{40} on the row side and down to e^{-75} on the column side."""
+@pytest.mark.parametrize("la", [-5.0, -8.0])
+def test_gate_decay_at_documented_limit(dt, pattern, la):
+    """log_alpha = la on every token, on every channel or on every other
+    channel with no decay (log_alpha = 0) on the rest; beta = 1.  -8 is the
+    per-element bound of the chunked prefill (any 9 consecutive tokens sum to
+    -72 >= -80): the intra-chunk factors then span their widest range, up to
+    e^{64} on the row side and down to e^{-72} for a scale factor."""
     w = synth.make_prefill([200, 64, 17, 1], H=2, dk=128, dv=128, io_dtype=dt, seed=19, S0_std=0.05)
     if pattern == "half":
-        w.log_alpha[:, :, 0::2] = -5.0
+        w.log_alpha[:, :, 0::2] = la
         w.log_alpha[:, :, 1::2] = 0.0
     else:
-        w.log_alpha[:] = -5.0
+        w.log_alpha[:] = la
     w.beta[:] = 1.0
-    log("prefill gate limit dt=%s pattern=%s" % (dt, pattern))
+    log("prefill gate limit dt=%s pattern=%s la=%g" % (dt, pattern, la))
     o, S = gpu_prefill(w)
     o_ref, S_ref = oracle_prefill(w)
     check("o", o, o_ref, TOL[dt])
