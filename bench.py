@@ -14,8 +14,13 @@ workload follow under "prefill_other" (skip with --no-other).
 Prints ONE JSON line.  `value` is prefill tokens/s.  Each roofline block
 prices the operator's algorithmic bytes per launch against MI355X's 8 TB/s
 HBM peak, using HIP-event durations taken on the stream the kernels run on.
-The fp64 oracle is timed on a bounded sample on the host CPU ("cpu_baseline")
-and its outputs double as a sampled parity check.
+The fp64 oracle is timed on the host CPU ("cpu_baseline"): for prefill over
+the whole sequence and every head of the last timed call, whose outputs it
+also checks element by element ("parity"); for decode over the first steps
+of the decode workload ("decode.cpu_baseline").  After the timed loop the
+prefill call's recovery flag is read: if the overlapped schedule had to fall
+back (its two streams did not run side by side), the timing is not that
+schedule's and the script exits with status 3.
 """
 from __future__ import annotations
 
@@ -115,7 +120,8 @@ def run_prefill(args, torch, kda, synth, oracle):
     stream = torch.cuda.current_stream()
 
     def step():
-        kda.prefill(q, k, v, la, b, cu, S0, o=o, S_T=ST, cu_seqlens_host=host_cu, chunk=w.chunk)
+        kda.prefill(q, k, v, la, b, cu, S0, o=o, S_T=ST, cu_seqlens_host=host_cu, chunk=w.chunk,
+                    one_stream=args.one_stream)
 
     for _ in range(args.warmup):
         step()
@@ -130,6 +136,7 @@ def run_prefill(args, torch, kda, synth, oracle):
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     call_ms = [a.elapsed_time(z) for a, z in ev]
+    recovered = kda.prefill_recovered(q, v, cu, chunk=w.chunk, cu_seqlens_host=host_cu, one_stream=args.one_stream)
     avg_call_s = float(np.mean(call_ms)) / 1e3
     es = 2 if bf else 4
     nbytes, nflops, per_th, flops_th = prefill_algorithmic(T_tok, N, H, dk, dv, es, w.chunk, S0 is not None)
@@ -154,13 +161,14 @@ def run_prefill(args, torch, kda, synth, oracle):
         workload=dict(workload=wname, num_seqs=N, total_tokens=T_tok, heads=H, dk=dk, dv=dv, chunk=w.chunk,
                       io_dtype=w.io_dtype, state_dtype="f32"),
     )
+    res["recovered"] = recovered
     if not args.no_cpu_baseline:
         Ts = min(args.cpu_sample_tokens, int(w.cu_seqlens[1]))  # a prefix of the first sequence
         log("cpu baseline: oracle on the first %d tokens x %d heads ..." % (Ts, H))
         t1 = time.perf_counter()
-        o_ref, _, used = oracle.prefill(w.q[:Ts], w.k[:Ts], w.v[:Ts], w.log_alpha[:Ts], w.beta[:Ts], [0, Ts],
-                                        None if w.S0 is None else w.S0[:1], threads=args.cpu_threads,
-                                        return_threads=True)
+        o_ref, S_ref, used = oracle.prefill(w.q[:Ts], w.k[:Ts], w.v[:Ts], w.log_alpha[:Ts], w.beta[:Ts], [0, Ts],
+                                            None if w.S0 is None else w.S0[:1], threads=args.cpu_threads,
+                                            return_threads=True)
         dt = time.perf_counter() - t1
         res["cpu_baseline"] = dict(value=round(Ts / dt, 1), unit="tokens/s", cores=int(used), kind="oracle",
                                    sample="first %d of %d tokens, all %d heads, fp64 sequential recurrence, %.1f s"
@@ -173,9 +181,17 @@ def run_prefill(args, torch, kda, synth, oracle):
         res["cpu_baseline"]["single_thread"] = dict(
             value=round(T1 / dt1, 1), unit="tokens/s",
             sample="first %d tokens, all %d heads, one thread, %.1f s" % (T1, H, dt1))
+        # parity of the last timed call over every element the oracle covered
         og = o[:Ts].float().cpu().numpy().astype(np.float64)
-        res["parity_sample"] = dict(o_rel_err=float(np.max(np.abs(og - o_ref)) / np.max(np.abs(o_ref))),
-                                    tokens=Ts, tol=1e-2 if bf else 1e-4)
+        par = dict(o_rel_err=float(np.max(np.abs(og - o_ref)) / np.max(np.abs(o_ref))), tokens=Ts, heads=H,
+                   tol=1e-2 if bf else 1e-4)
+        del og
+        if Ts == T_tok and N == 1:
+            sg = ST.cpu().numpy().astype(np.float64)
+            par["S_T_rel_err"] = float(np.max(np.abs(sg - S_ref)) / np.max(np.abs(S_ref)))
+        par["pass"] = par["o_rel_err"] <= par["tol"] and par.get("S_T_rel_err", 0.0) <= par["tol"]
+        res["parity"] = par
+        del o_ref, S_ref
     del q, k, v, la, b, o, ST
     torch.cuda.empty_cache()
     return res
@@ -203,13 +219,15 @@ def run_prefill_rate(wname, args, torch, kda, synth):
     host_cu = w.cu_seqlens.tolist()
     stream = torch.cuda.current_stream()
     for _ in range(2):
-        kda.prefill(q, k, v, la, b, cu, S0, o=o, S_T=ST, cu_seqlens_host=host_cu, chunk=w.chunk)
+        kda.prefill(q, k, v, la, b, cu, S0, o=o, S_T=ST, cu_seqlens_host=host_cu, chunk=w.chunk,
+                    one_stream=args.one_stream)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     n = 5
     e0.record(stream)
     for _ in range(n):
-        kda.prefill(q, k, v, la, b, cu, S0, o=o, S_T=ST, cu_seqlens_host=host_cu, chunk=w.chunk)
+        kda.prefill(q, k, v, la, b, cu, S0, o=o, S_T=ST, cu_seqlens_host=host_cu, chunk=w.chunk,
+                    one_stream=args.one_stream)
     e1.record(stream)
     torch.cuda.synchronize()
     call_s = e0.elapsed_time(e1) / n / 1e3
@@ -221,7 +239,32 @@ def run_prefill_rate(wname, args, torch, kda, synth):
                 hbm_frac=round(nbytes / call_s / 1e9 / HBM_PEAK_GBS, 4))
 
 
-def run_decode(args, torch, kda, synth):
+def decode_cpu_baseline(args, synth, oracle, B, H, dk, dv, std, seed):
+    """fp64 oracle decode rate: the first steps of the decode workload on all
+    host cores (every state), and on one thread (a slice of the states)."""
+    S = synth.make_decode_state(B, H, dk, dv, std, seed).astype(np.float64)
+    n = max(1, args.cpu_decode_steps)
+    xs = [synth.make_decode_step(B, H, dk, dv, "bf16", seed, t) for t in range(n)]
+    t0 = time.perf_counter()
+    for x in xs:
+        _, S = oracle.decode_step(x.q, x.k, x.v, x.log_alpha, x.beta, S, threads=args.cpu_threads, inplace=True)
+    dt = time.perf_counter() - t0
+    cores = os.cpu_count() if args.cpu_threads <= 0 else args.cpu_threads
+    res = dict(value=round(B * H * n / dt, 1), unit="state-updates/s", cores=int(cores), kind="oracle",
+               sample="first %d of the workload's steps, all %d states, fp64, %.1f s" % (n, B * H, dt))
+    Bs = max(1, B // 16)
+    S1 = S[:Bs].copy()
+    t0 = time.perf_counter()
+    for x in xs[:2]:
+        _, S1 = oracle.decode_step(x.q[:Bs], x.k[:Bs], x.v[:Bs], x.log_alpha[:Bs], x.beta[:Bs], S1, threads=1,
+                                   inplace=True)
+    dt1 = time.perf_counter() - t0
+    res["single_thread"] = dict(value=round(Bs * H * 2 / dt1, 1), unit="state-updates/s",
+                                sample="2 steps of %d states, one thread, %.1f s" % (Bs * H, dt1))
+    return res
+
+
+def run_decode(args, torch, kda, synth, oracle=None):
     wd = synth.WORKLOADS["decode256x32_bf16"]
     B, H, dk, dv, steps = wd["B"], wd["H"], wd["dk"], wd["dv"], args.decode_steps
     seed = 1000 + wd["index"]
@@ -273,6 +316,9 @@ def run_decode(args, torch, kda, synth):
     )
     del qs, ks, vs, las, bs, S, S0
     torch.cuda.empty_cache()
+    if oracle is not None and not args.no_cpu_baseline:
+        log("cpu baseline: decode oracle ...")
+        res["cpu_baseline"] = decode_cpu_baseline(args, synth, oracle, B, H, dk, dv, wd["S0_std"], seed)
     return res
 
 
@@ -297,8 +343,11 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other", action="store_true", help="skip the 4x4096 and varlen prefill rates")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=65536)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=1 << 30, help="oracle tokens (default: all)")
     ap.add_argument("--cpu-threads", type=int, default=0)
+    ap.add_argument("--cpu-decode-steps", type=int, default=16)
+    ap.add_argument("--one-stream", action="store_true",
+                    help="prefill on the caller's stream only (for hardware-counter runs)")
     ap.add_argument("--copy-probe", type=int, default=0, help="run only a device copy of this many bytes")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -318,7 +367,7 @@ def main():
     kda.load_library()
 
     pre = run_prefill(args, torch, kda, synth, oracle)
-    dec = None if args.no_decode else run_decode(args, torch, kda, synth)
+    dec = None if args.no_decode else run_decode(args, torch, kda, synth, oracle)
     other = [] if args.no_other else [run_prefill_rate(n, args, torch, kda, synth)
                                       for n in ("batch4x4096_bf16", "varlen64_bf16")]
     wl = pre["workload"]
@@ -341,14 +390,21 @@ def main():
         "roofline": pre["roofline"],
         "prefill_call_ms": {"mean": round(pre["call_ms_mean"], 4), "min": round(pre["call_ms_min"], 4)},
     }
+    line["prefill_recovered"] = pre["recovered"]
     if "cpu_baseline" in pre:
         line["cpu_baseline"] = pre["cpu_baseline"]
-        line["parity_sample"] = pre["parity_sample"]
+        line["parity"] = pre["parity"]
     if dec is not None:
         line["decode"] = dec
     if other:
         line["prefill_other"] = other
     print(json.dumps(line), flush=True)
+    if pre["recovered"]:
+        log("the overlapped prefill schedule fell back to its recovery launches: timing invalid")
+        sys.exit(3)
+    if "parity" in pre and not pre["parity"]["pass"]:
+        log("parity of the last timed call failed")
+        sys.exit(4)
 
 
 if __name__ == "__main__":

@@ -8,6 +8,7 @@ these functions raise.
 
     o, S_T = prefill(q, k, v, log_alpha, beta, cu_seqlens, S0=None)
     o      = decode_step(q, k, v, log_alpha, beta, S)      # S updated in place
+    prefill_recovered(...)   # did the last overlapped call fall back?
 """
 from __future__ import annotations
 
@@ -26,8 +27,10 @@ KDA_ERR_WORKSPACE_TOO_SMALL = 3
 KDA_ERR_DEVICE = 4
 KDA_F32 = 0
 KDA_BF16 = 1
+KDA_PREFILL_ONE_STREAM = 1
 
-EXPORTED = ("kda_prefill", "kda_prefill_workspace_size", "kda_decode_step", "kda_status_string", "kda_version")
+EXPORTED = ("kda_prefill", "kda_prefill_workspace_size", "kda_prefill_recovered", "kda_prefill_set_wait_limit",
+            "kda_decode_step", "kda_status_string", "kda_version")
 
 
 class KdaError(RuntimeError):
@@ -46,6 +49,7 @@ class PrefillDesc(ctypes.Structure):
         ("chunk", ctypes.c_int32),
         ("io_dtype", ctypes.c_int),
         ("cu_seqlens_host", ctypes.POINTER(ctypes.c_int32)),
+        ("flags", ctypes.c_uint32),
     ]
 
 
@@ -73,6 +77,10 @@ def load_library(path: str = LIB_PATH):
         lib.kda_prefill.restype = ctypes.c_int
         lib.kda_prefill.argtypes = [ctypes.POINTER(PrefillDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                     ctypes.c_size_t, vp]
+        lib.kda_prefill_recovered.restype = ctypes.c_int
+        lib.kda_prefill_recovered.argtypes = [ctypes.POINTER(PrefillDesc), vp, ctypes.POINTER(ctypes.c_int32), vp]
+        lib.kda_prefill_set_wait_limit.restype = ctypes.c_int32
+        lib.kda_prefill_set_wait_limit.argtypes = [ctypes.c_int32]
         lib.kda_decode_step.restype = ctypes.c_int
         lib.kda_decode_step.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int,
                                         vp, vp, vp, vp, vp, vp, vp, vp]
@@ -90,7 +98,7 @@ def version() -> int:
 
 
 def make_desc(num_seqs: int, total_tokens: int, num_heads: int, dk: int, dv: int, chunk: int, io_dtype: int,
-              cu_seqlens_host: Optional[Sequence[int]] = None):
+              cu_seqlens_host: Optional[Sequence[int]] = None, flags: int = 0):
     """Build a kda_prefill_desc.  Returns (desc, keepalive) -- keep the second
     value alive while the desc is used (it owns the host offsets)."""
     keep = None
@@ -99,7 +107,7 @@ def make_desc(num_seqs: int, total_tokens: int, num_heads: int, dk: int, dv: int
         keep = (ctypes.c_int32 * len(cu_seqlens_host))(*[int(x) for x in cu_seqlens_host])
         ptr = ctypes.cast(keep, ctypes.POINTER(ctypes.c_int32))
     d = PrefillDesc(int(num_seqs), int(total_tokens), int(num_heads), int(dk), int(dv), int(chunk), int(io_dtype),
-                    ptr)
+                    ptr, int(flags))
     return d, keep
 
 
@@ -125,7 +133,7 @@ def _dtype_code(t) -> int:
     raise TypeError("q/k/v must be bfloat16 or float32, got %s" % t.dtype)
 
 
-def _dev_ptr(t, name: str, dtype=None) -> int:
+def _dev_ptr(t, name: str, dtype=None, shape=None, device=None) -> int:
     torch = _torch()
     if t is None:
         return None
@@ -135,64 +143,127 @@ def _dev_ptr(t, name: str, dtype=None) -> int:
         raise ValueError("%s must be contiguous" % name)
     if dtype is not None and t.dtype != dtype:
         raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if device is not None and t.device != device:
+        raise ValueError("%s must be on %s, got %s" % (name, device, t.device))
     return t.data_ptr()
 
 
-def _stream_ptr(stream) -> int:
+def _stream(stream):
     torch = _torch()
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return s.cuda_stream
+    return stream if stream is not None else torch.cuda.current_stream()
 
 
+# One prefill workspace per (device, stream), grown on demand.  A workspace
+# is allocated on the stream that uses it, so when it is replaced the caching
+# allocator reuses its memory only after that stream's pending work.
 _ws_cache = {}
+_ws_lock = threading.Lock()
+
+
+def _workspace(device, stream, need: int):
+    torch = _torch()
+    key = (device, stream.cuda_stream)
+    with _ws_lock:
+        ws = _ws_cache.get(key)
+        if ws is None or ws.numel() < need:
+            _ws_cache.pop(key, None)
+            del ws
+            with torch.cuda.stream(stream):
+                ws = torch.empty(need, dtype=torch.uint8, device=device)
+            _ws_cache[key] = ws
+        return ws
+
+
+def clear_workspace_cache():
+    """Drop the cached prefill workspaces (their memory returns to torch's
+    caching allocator once the streams that used them reach this point)."""
+    with _ws_lock:
+        _ws_cache.clear()
 
 
 def prefill(q, k, v, log_alpha, beta, cu_seqlens, S0=None, *, chunk: int = 64, o=None, S_T=None,
-            cu_seqlens_host: Optional[Sequence[int]] = None, workspace=None, stream=None, want_state: bool = True):
+            cu_seqlens_host: Optional[Sequence[int]] = None, workspace=None, stream=None, want_state: bool = True,
+            one_stream: bool = False):
     """KDA chunked prefill over a packed batch.
 
     q, k: [T, H, dk]; v: [T, H, dv] (bf16 or fp32, same dtype); log_alpha: [T, H, dk]
     fp32; beta: [T, H] fp32; cu_seqlens: [N+1] int32 (GPU); S0: [N, H, dk, dv] fp32 or
     None.  Returns (o, S_T); S_T is None when ``want_state`` is False.
     ``S_T`` may be passed as ``S0`` to update the state in place.
+    ``one_stream`` selects the schedule that never leaves the caller's stream.
     """
     torch = _torch()
     lib = load_library()
+    if q.dim() != 3 or v.dim() != 3 or cu_seqlens.dim() != 1:
+        raise ValueError("q, k, v must be [T, H, d] and cu_seqlens [N+1]")
     T, H, dk = q.shape
     dv = v.shape[2]
     N = cu_seqlens.shape[0] - 1
     dt = _dtype_code(q)
+    dev = q.device
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k and v must share a dtype")
     if o is None:
-        o = torch.empty((T, H, dv), dtype=q.dtype, device=q.device)
+        o = torch.empty((T, H, dv), dtype=q.dtype, device=dev)
     if S_T is None and want_state:
-        S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
-    desc, keep = make_desc(N, T, H, dk, dv, chunk, dt, cu_seqlens_host)
+        S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    s = _stream(stream)
+    desc, keep = make_desc(N, T, H, dk, dv, chunk, dt, cu_seqlens_host,
+                           KDA_PREFILL_ONE_STREAM if one_stream else 0)
     need = int(lib.kda_prefill_workspace_size(ctypes.byref(desc)))
     if need == 0:
         st = lib.kda_prefill(ctypes.byref(desc), *([None] * 10), 0, None)
         raise KdaError(st if st != KDA_OK else KDA_ERR_INVALID_ARGUMENT, "kda_prefill_workspace_size")
+    ptrs = (_dev_ptr(q, "q", None, (T, H, dk), dev), _dev_ptr(k, "k", None, (T, H, dk), dev),
+            _dev_ptr(v, "v", None, (T, H, dv), dev),
+            _dev_ptr(log_alpha, "log_alpha", torch.float32, (T, H, dk), dev),
+            _dev_ptr(beta, "beta", torch.float32, (T, H), dev),
+            _dev_ptr(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,), dev),
+            _dev_ptr(S0, "S0", torch.float32, (N, H, dk, dv), dev),
+            _dev_ptr(o, "o", q.dtype, (T, H, dv), dev),
+            _dev_ptr(S_T, "S_T", torch.float32, (N, H, dk, dv), dev))
     if workspace is None:
-        key = (q.device, need)
-        workspace = _ws_cache.get(key)
-        if workspace is None:
-            _ws_cache.clear()
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-            _ws_cache[key] = workspace
-    st = lib.kda_prefill(ctypes.byref(desc),
-                         _dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
-                         _dev_ptr(log_alpha, "log_alpha", torch.float32), _dev_ptr(beta, "beta", torch.float32),
-                         _dev_ptr(cu_seqlens, "cu_seqlens", torch.int32),
-                         _dev_ptr(S0, "S0", torch.float32) if S0 is not None else None,
-                         _dev_ptr(o, "o", q.dtype),
-                         _dev_ptr(S_T, "S_T", torch.float32) if S_T is not None else None,
-                         _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
-                         _stream_ptr(stream))
+        workspace = _workspace(dev, s, need)
+    wptr = _dev_ptr(workspace, "workspace", None, None, dev)
+    st = lib.kda_prefill(ctypes.byref(desc), *ptrs, wptr, workspace.numel() * workspace.element_size(),
+                         s.cuda_stream)
     del keep
     if st != KDA_OK:
         raise KdaError(st, "kda_prefill")
     return o, S_T
+
+
+def prefill_recovered(q, v, cu_seqlens, *, chunk: int = 64, cu_seqlens_host=None, workspace=None, stream=None,
+                      one_stream: bool = False) -> bool:
+    """Whether the last prefill call with these shapes on ``stream`` (using
+    ``workspace``, or the binding's cached one for that stream) stopped
+    waiting in its overlapped schedule and recomputed its outputs on the
+    caller's stream.  Synchronises the stream."""
+    lib = load_library()
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    N = cu_seqlens.shape[0] - 1
+    s = _stream(stream)
+    desc, keep = make_desc(N, T, H, dk, dv, chunk, _dtype_code(q), cu_seqlens_host,
+                           KDA_PREFILL_ONE_STREAM if one_stream else 0)
+    if workspace is None:
+        with _ws_lock:
+            workspace = _ws_cache.get((q.device, s.cuda_stream))
+    if workspace is None:
+        raise RuntimeError("no prefill workspace for this stream")
+    out = ctypes.c_int32(0)
+    st = lib.kda_prefill_recovered(ctypes.byref(desc), workspace.data_ptr(), ctypes.byref(out), s.cuda_stream)
+    del keep
+    if st != KDA_OK:
+        raise KdaError(st, "kda_prefill_recovered")
+    return bool(out.value)
+
+
+def set_wait_limit(polls: int) -> int:
+    """Test hook: see kda_prefill_set_wait_limit in include/kda.h."""
+    return int(load_library().kda_prefill_set_wait_limit(int(polls)))
 
 
 def decode_step(q, k, v, log_alpha, beta, S, *, o=None, stream=None):
@@ -201,14 +272,22 @@ def decode_step(q, k, v, log_alpha, beta, S, *, o=None, stream=None):
     Returns o [B, H, dv]."""
     torch = _torch()
     lib = load_library()
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be [B, H, d]")
     B, H, dk = q.shape
     dv = v.shape[2]
     dt = _dtype_code(q)
+    dev = q.device
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share a dtype")
     if o is None:
-        o = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
-    st = lib.kda_decode_step(B, H, dk, dv, dt, _dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
-                             _dev_ptr(log_alpha, "log_alpha", torch.float32), _dev_ptr(beta, "beta", torch.float32),
-                             _dev_ptr(S, "S", torch.float32), _dev_ptr(o, "o", q.dtype), _stream_ptr(stream))
+        o = torch.empty((B, H, dv), dtype=q.dtype, device=dev)
+    st = lib.kda_decode_step(B, H, dk, dv, dt, _dev_ptr(q, "q", None, (B, H, dk), dev),
+                             _dev_ptr(k, "k", None, (B, H, dk), dev), _dev_ptr(v, "v", None, (B, H, dv), dev),
+                             _dev_ptr(log_alpha, "log_alpha", torch.float32, (B, H, dk), dev),
+                             _dev_ptr(beta, "beta", torch.float32, (B, H), dev),
+                             _dev_ptr(S, "S", torch.float32, (B, H, dk, dv), dev),
+                             _dev_ptr(o, "o", q.dtype, (B, H, dv), dev), _stream(stream).cuda_stream)
     if st != KDA_OK:
         raise KdaError(st, "kda_decode_step")
     return o

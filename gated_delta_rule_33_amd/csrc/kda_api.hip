@@ -31,6 +31,7 @@ kda_status check_desc(const kda_prefill_desc* d, int64_t* max_chunks) {
   if (!dims_supported(d->dk, d->dv)) return KDA_ERR_UNSUPPORTED;
   if (d->chunk != 32 && d->chunk != 64) return KDA_ERR_UNSUPPORTED;
   if (d->num_seqs == 0 && d->total_tokens != 0) return KDA_ERR_INVALID_ARGUMENT;
+  if (d->flags & ~static_cast<uint32_t>(KDA_PREFILL_ONE_STREAM)) return KDA_ERR_INVALID_ARGUMENT;
   const int64_t C = d->chunk;
   // one chunk of rows of any per-token tensor must span fewer than 2^31
   // bytes (the kernels use 32-bit offsets within a chunk)
@@ -68,7 +69,7 @@ const char* kda_status_string(kda_status s) {
   return "KDA_ERR_UNKNOWN";
 }
 
-int32_t kda_version(void) { return 100; }
+int32_t kda_version(void) { return 20000; }
 
 size_t kda_prefill_workspace_size(const kda_prefill_desc* d) {
   int64_t mc = 0;
@@ -115,6 +116,29 @@ kda_status kda_prefill(const kda_prefill_desc* d, const void* q, const void* k, 
                                            static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KDA_OK : KDA_ERR_DEVICE;
 }
+
+kda_status kda_prefill_recovered(const kda_prefill_desc* d, const void* workspace, int32_t* recovered,
+                                 void* stream) {
+  int64_t mc = 0;
+  if (!recovered) return KDA_ERR_INVALID_ARGUMENT;
+  *recovered = 0;
+  const kda_status s = check_desc(d, &mc);
+  if (s != KDA_OK) return s;
+  kda::PrefillPlan p;
+  if (!kda::make_prefill_plan(d, mc, &p)) return KDA_ERR_UNSUPPORTED;
+  if (d->num_seqs == 0 || p.off_ready == 0) return KDA_OK;
+  if (!workspace) return KDA_ERR_INVALID_ARGUMENT;
+  int32_t flag = 0;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(&flag, static_cast<const unsigned char*>(workspace) + p.off_ready + 4, 4, hipMemcpyDeviceToHost,
+                     st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return KDA_ERR_DEVICE;
+  *recovered = flag != 0;
+  return KDA_OK;
+}
+
+int32_t kda_prefill_set_wait_limit(int32_t polls) { return kda::set_prefill_wait_polls(polls); }
 
 kda_status kda_decode_step(int32_t B, int32_t H, int32_t dk, int32_t dv, kda_dtype io_dtype, const void* q,
                            const void* k, const void* v, const float* log_alpha, const float* beta, float* S,

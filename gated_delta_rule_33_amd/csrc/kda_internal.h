@@ -21,7 +21,8 @@ struct PrefillPlan {
   int sort;            // 1: longest-first order is computed on the device
   // byte offsets inside the workspace
   size_t off_chunk_off, off_order, off_blocks;
-  size_t off_ready;  // segment counter of the overlapped schedule (0: none)
+  size_t off_ready;  // segment counter and recovery flag of the overlapped schedule (0: none)
+  size_t off_carry;  // final states of an in-place overlapped call (0: none)
   size_t total_bytes;
   // Segment length in global chunk indices for the overlapped two-stream
   // schedule (0: one prep launch, then one scan launch).
@@ -30,6 +31,11 @@ struct PrefillPlan {
 
 // Returns false when the shape is unsupported.
 bool make_prefill_plan(const kda_prefill_desc* d, int64_t max_chunks, PrefillPlan* p);
+
+// Test hook behind kda_prefill_set_wait_limit: polls > 0 sets the bound of
+// the overlapped schedule's wait, 0 makes it never wait, < 0 restores the
+// default.  Returns the previous bound.
+int set_prefill_wait_polls(int polls);
 
 hipError_t launch_prefill(const PrefillPlan& p, const void* q, const void* k, const void* v, const float* la,
                           const float* beta, const int32_t* cu, const float* S0, void* o, float* S_T,

@@ -36,25 +36,27 @@
 // With few (sequence, head) pairs the scan runs on half of the CUs beside
 // the prep of later chunks on the other half (launch_prefill below).
 //
-// Exponent safety.  e^{g_r-g_s} (s <= r, r in the 16-row block I, s in block
-// J <= I) is built from factors around references inside the blocks (m_I
-// the 9th row of I, e_J the last row of J), see the prep kernel: the row
-// operands carry e^{g_r - g_{m_I}} and the column operand e^{g_{m_J} - g_s},
-// each spanning the decay over at most 8 tokens either way.  A diagonal pair
-// (I = J) multiplies them as they are; an off-diagonal pair first turns the
-// column operand into e^{g_{e_J} - g_s} (<= 1) and then scales it by
-// e^{g_{m_I} - g_{e_J}} (<= 1, the decay over at least 9 tokens).  All
-// factors stay in the fp32 normal range when, per channel, any 9
-// consecutive tokens have log_alpha summing to at least -80 (log_alpha >= -8
-// per element suffices); an intermediate that still underflows then stands
-// for a ratio below e^{-15}.  Past the bound the last scale factor of an
-// off-diagonal block next to the diagonal underflows while the ratio it
-// stands for need not be small, so the library requires it.
+// Exponent safety.  Every gate factor is e^x of a sum x of log_alpha over a
+// contiguous token range, formed directly as such a sum (never as the
+// difference of two sums), so its rounding is relative to itself.  Inside a
+// chunk, per key channel and 16-row block I: d_r sums the block's rows up to
+// and including r, s_r the block's rows after r, D_I the whole block.  For
+// s <= r (r in block I, s in block J <= I)
+//   e^{g_r - g_s} = e^{d_r} e^{s_s} e^{D_{J+1} + ... + D_{I-1}}   (J < I)
+//                 = e^{d_r} e^{s_s} e^{-D_I}                      (J = I)
+// The row operands carry e^{d_r} <= 1 and the column operand e^{s_s} <= 1;
+// an off-diagonal pair scales the column operand by a factor <= 1, so every
+// factor is at most 1 and an underflow only stands for a negligible ratio.
+// A diagonal pair scales it by e^{-D_I} >= 1, which fp32 holds while the
+// block decays by at most 2^86 (about e^{59.6}); for channels that decay
+// faster the diagonal block's products are formed pair by pair from the
+// per-token gates (e^{g_r - g_s} as a product of alphas) instead.  The result
+// is exact up to rounding for every finite log_alpha <= 0.
 
 #include <hip/hip_ext.h>
 
 #include <cstdlib>
-#include <cstring>
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -219,6 +221,17 @@ __global__ __launch_bounds__(1024) void chunk_offsets_kernel(const int32_t* __re
 // their first thread).
 __global__ void ready_kernel(int32_t* ready, int j) {
   if (threadIdx.x == 0) __hip_atomic_store(ready, j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Overlapped schedule with S_T == S0: the state pass leaves the final states
+// in a workspace carry (S0 must survive until the call knows it needs no
+// recovery); this copies them to S_T unless the flag word is set, in which
+// case the recovery launches rewrite S_T from S0.  n4 float4 elements.
+__global__ __launch_bounds__(256) void carry_out_kernel(const f32x4* __restrict__ carry, f32x4* __restrict__ S_T,
+                                                        size_t n4, const int* flag) {
+  if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return;
+  for (size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x; i < n4; i += static_cast<size_t>(gridDim.x) * 256)
+    S_T[i] = carry[i];
 }
 
 // ---------------------------------------------------------------------------
@@ -389,16 +402,17 @@ __device__ __forceinline__ void buffer_store_raw4(__amdgpu_buffer_rsrc_t r, int 
 // rows of q, k and log_alpha.
 //
 // Gated products.  For rows r of 16-row block I and columns s of block J <= I
-//   e^{g_r - g_s} = [e^{g_r - g_{m_I}}] [e^{g_{m_J} - g_s}]                      (I = J)
-//                 = [e^{g_r - g_{m_I}}] [e^{g_{m_J} - g_s} e^{g_{e_J} - g_{m_J}}] e^{g_{m_I} - g_{e_J}}  (J < I)
-// with m_I the 9th row of block I and e_J the last row of block J.  The first
-// factor goes into the stored row operands (Krd, Qrd), e^{g_{m_J} - g_s} into
-// the stored column operand (Kc); a diagonal pair reads both raw, an
-// off-diagonal pair scales the column fragment by the two per-channel
-// vectors, left to right.  The range each factor spans is bounded in the
-// exponent-safety note at the top of this file.
+// the row operands (Krd, Qrd) hold k_r e^{d_r}, q_r e^{d_r} and the column
+// operand (Kc) k_s e^{s_s}; the pair (I, J) scales the column fragment by one
+// per-channel vector: e^{D_{J+1} + ... + D_{I-1}} (<= 1) for J < I, e^{-D_I}
+// for J = I, or 0 for a channel whose block decay is out of range, whose
+// diagonal products are then added pair by pair (see the note at the top).
 // ---------------------------------------------------------------------------
 constexpr int kPrepThreads = 512;
+// Largest block decay (base 2) a diagonal pair's column scale e^{-D_I} may
+// carry: past it the channel's diagonal products are formed pair by pair.
+constexpr float kDiagRange = 86.f;
+constexpr float kLog2e = 1.4426950408889634f;
 
 template <typename T, int C, int DK>
 struct PrepLds {
@@ -415,8 +429,8 @@ struct PrepLds {
   static constexpr size_t r0 = a16(mx(static_cast<size_t>(3) * C * RBK, szTi));
   // region 1: cumsum partials [NRB][DK] (f32) -> later A (f32)
   static constexpr size_t r1 = a16(mx(static_cast<size_t>(C) * AP * 4, static_cast<size_t>(NRB) * DK * 4));
-  // region 2: gM gE [NB][DK] (f32) -> later P staging (io)
-  static constexpr size_t r2 = a16(mx(static_cast<size_t>(2 * NB) * DK * 4, static_cast<size_t>(C) * CP * sizeof(T)));
+  // region 2: block gate sums D [NB][DK] (f32) -> later P staging (io)
+  static constexpr size_t r2 = a16(mx(static_cast<size_t>(NB) * DK * 4, static_cast<size_t>(C) * CP * sizeof(T)));
   // region 3: block-pair vectors f[NLB][DK] (f32)
   static constexpr size_t r3 = a16(static_cast<size_t>(NLB) * DK * 4);
   static constexpr size_t o0 = 0, o1 = r0, o2 = o1 + r1, o3 = o2 + r2, o4 = o3 + r3;
@@ -439,24 +453,20 @@ struct natf<bf16_t, RB> {
   __device__ __forceinline__ static bf16x8 raw(const unsigned char* t, int row, int k0, int g) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(t + loff<bf16_t, RB>(row, k0 + 8 * g)));
   }
-  // (x * a) * b per channel, in that order (x * a may underflow where the
-  // product is negligible; a * b may underflow where it is not)
-  __device__ __forceinline__ static bf16x8 scaled(const unsigned char* t, int row, const float* a, const float* b,
-                                                  int k0, int g) {
+  // x * a per channel
+  __device__ __forceinline__ static bf16x8 scaled(const unsigned char* t, int row, const float* a, int k0, int g) {
     const uint4 u = *reinterpret_cast<const uint4*>(t + loff<bf16_t, RB>(row, k0 + 8 * g));
     const f32x4 a0 = *reinterpret_cast<const f32x4*>(a + k0 + 8 * g);
     const f32x4 a1 = *reinterpret_cast<const f32x4*>(a + k0 + 8 * g + 4);
-    const f32x4 b0 = *reinterpret_cast<const f32x4*>(b + k0 + 8 * g);
-    const f32x4 b1 = *reinterpret_cast<const f32x4*>(b + k0 + 8 * g + 4);
     bf16x8 r;
-    r[0] = to_bf(__uint_as_float(u.x << 16) * a0[0] * b0[0]);
-    r[1] = to_bf(__uint_as_float(u.x & 0xFFFF0000u) * a0[1] * b0[1]);
-    r[2] = to_bf(__uint_as_float(u.y << 16) * a0[2] * b0[2]);
-    r[3] = to_bf(__uint_as_float(u.y & 0xFFFF0000u) * a0[3] * b0[3]);
-    r[4] = to_bf(__uint_as_float(u.z << 16) * a1[0] * b1[0]);
-    r[5] = to_bf(__uint_as_float(u.z & 0xFFFF0000u) * a1[1] * b1[1]);
-    r[6] = to_bf(__uint_as_float(u.w << 16) * a1[2] * b1[2]);
-    r[7] = to_bf(__uint_as_float(u.w & 0xFFFF0000u) * a1[3] * b1[3]);
+    r[0] = to_bf(__uint_as_float(u.x << 16) * a0[0]);
+    r[1] = to_bf(__uint_as_float(u.x & 0xFFFF0000u) * a0[1]);
+    r[2] = to_bf(__uint_as_float(u.y << 16) * a0[2]);
+    r[3] = to_bf(__uint_as_float(u.y & 0xFFFF0000u) * a0[3]);
+    r[4] = to_bf(__uint_as_float(u.z << 16) * a1[0]);
+    r[5] = to_bf(__uint_as_float(u.z & 0xFFFF0000u) * a1[1]);
+    r[6] = to_bf(__uint_as_float(u.w << 16) * a1[2]);
+    r[7] = to_bf(__uint_as_float(u.w & 0xFFFF0000u) * a1[3]);
     return r;
   }
 };
@@ -465,9 +475,8 @@ struct natf<float, RB> {
   __device__ __forceinline__ static float raw(const unsigned char* t, int row, int k0, int g) {
     return *reinterpret_cast<const float*>(t + loff<float, RB>(row, k0 + g));
   }
-  __device__ __forceinline__ static float scaled(const unsigned char* t, int row, const float* a, const float* b,
-                                                int k0, int g) {
-    return raw(t, row, k0, g) * a[k0 + g] * b[k0 + g];
+  __device__ __forceinline__ static float scaled(const unsigned char* t, int row, const float* a, int k0, int g) {
+    return raw(t, row, k0, g) * a[k0 + g];
   }
 };
 
@@ -513,11 +522,13 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                    const int32_t* __restrict__ cu,
                                                    const int32_t* __restrict__ chunk_off, int N, int H,
                                                    unsigned char* __restrict__ ws, int cbase, int count,
-                                                   int32_t* publish, int published) {
+                                                   int32_t* publish, int published, const int* guard) {
   typedef PrepLds<T, C, DK> L;
   typedef Blk<T, C, DK> B;
   typedef mma16<T> M;
   typedef mma16<float> MF;
+  // Recovery launch: runs only if the flag word is nonzero (see scan_kernel).
+  if (guard && __hip_atomic_load(guard, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) return;
   // Stream order started this launch after the previous one on its stream
   // had ended (and released its writes): tell the scan those blocks exist.
   if (publish && blockIdx.x == 0 && threadIdx.x == 0)
@@ -532,8 +543,7 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
   unsigned char* Kc = Qrd + C * L::RBK;
   float* Ti = reinterpret_cast<float*>(smem + L::o0);
   float* A = reinterpret_cast<float*>(smem + L::o1);
-  float* gM = reinterpret_cast<float*>(smem + L::o2);
-  float* gE = gM + NB * DK;
+  float* Dblk = reinterpret_cast<float*>(smem + L::o2);  // block gate sums [NB][DK]
   T* Ps = reinterpret_cast<T*>(smem + L::o2);
   float* fv = reinterpret_cast<float*>(smem + L::o3);
   float* bet = reinterpret_cast<float*>(smem + L::o4);
@@ -609,8 +619,7 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
     if (it.c < total) {
   unsigned char* blk = ws + (static_cast<size_t>(c) * H + h) * B::bytes;
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(blk, 0, static_cast<int>(B::bytes), 0x00020000);
-  // Gates in base 2: g2 = log2(e) * g, so every factor is one v_exp_f32.
-  constexpr float kLog2e = 1.4426950408889634f;
+  // Gates in base 2 (log2(e) * log_alpha), so every factor is one v_exp_f32.
   f32x4 lg[RPT], kv[RPT], qv[RPT];
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
@@ -619,40 +628,70 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
     qv[i] = cvt4(cur.qr[i]);
   }
   if (tid < C) bet[tid] = cur.bt;
-  (void)t0;
 
-  // ---- a2: chunk-local inclusive cumsum of log_alpha ----------------------
-  // inside the thread's rows, then across the row blocks of its channel group
-#pragma unroll
-  for (int i = 1; i < RPT; ++i) lg[i] += lg[i - 1];
+  // ---- a2: gate sums inside each 16-row block (base 2) ---------------------
+  // The thread's rows r0 .. r0 + RPT - 1 lie in block I; TPB threads of its
+  // channel group share the block.  dl[i] = d (rows of the block up to and
+  // including the row), sl[i] = s (rows after it), both summed directly.
+  constexpr int TPB = 16 / RPT;
+  const int I = r0 >> 4, pos = rbk % TPB, rb0 = rbk - pos;
+  f32x4 dl[RPT], sl[RPT];
   {
     float* part = reinterpret_cast<float*>(smem + L::o1);
-    *reinterpret_cast<f32x4*>(part + rbk * DK + c4) = lg[RPT - 1];
+    f32x4 tot = lg[0];
+#pragma unroll
+    for (int i = 1; i < RPT; ++i) tot += lg[i];
+    *reinterpret_cast<f32x4*>(part + rbk * DK + c4) = tot;
     __syncthreads();
-    f32x4 off = {0.f, 0.f, 0.f, 0.f};
-    for (int pp = 0; pp < rbk; ++pp) off += *reinterpret_cast<const f32x4*>(part + pp * DK + c4);
+    f32x4 before = {0.f, 0.f, 0.f, 0.f}, after = {0.f, 0.f, 0.f, 0.f}, whole = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int pp = 0; pp < TPB; ++pp) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(part + (rb0 + pp) * DK + c4);
+      if (pp < pos) before += x;
+      if (pp > pos) after += x;
+      whole += x;
+    }
+    f32x4 run = before;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      lg[i] += off;
-      const int r = r0 + i, I = r >> 4, rr = r & 15;
-      if (rr == 8) *reinterpret_cast<f32x4*>(gM + I * DK + c4) = lg[i];
-      if (rr == 15) *reinterpret_cast<f32x4*>(gE + I * DK + c4) = lg[i];
+      run += lg[i];
+      dl[i] = run;
     }
+    run = after;
+#pragma unroll
+    for (int i = RPT - 1; i >= 0; --i) {
+      sl[i] = run;
+      run += lg[i];
+    }
+    if (pos == 0) *reinterpret_cast<f32x4*>(Dblk + I * DK + c4) = whole;
   }
   __syncthreads();
 
-  // ---- block-pair vectors: e^{g_{m_I} - g_{e_J}} for J < I; the slot of the
-  // diagonal pair (J, J), which needs no scaling, holds e^{g_{e_J} - g_{m_J}}
+  // ---- block-pair vectors: for J < I, e^{D_{J+1} + ... + D_{I-1}} (<= 1);
+  // for the diagonal pair (J, J), e^{-D_J} (>= 1), or 0 where it would
+  // exceed 2^86 (that channel's diagonal products are formed pair by pair)
   for (int idx = tid; idx < L::NLB * DK; idx += kPrepThreads) {
     const unsigned pp = static_cast<unsigned>(idx) / DK, ch = static_cast<unsigned>(idx) % DK;
-    unsigned I = 0;
+    unsigned bI = 0;
 #pragma unroll
-    for (unsigned t = 1; t < static_cast<unsigned>(NB); ++t) I += pp >= t * (t + 1) / 2 ? 1u : 0u;
-    const unsigned J = pp - I * (I + 1) / 2;
-    fv[idx] = I == J ? __builtin_amdgcn_exp2f(gE[J * DK + ch] - gM[J * DK + ch])
-                     : __builtin_amdgcn_exp2f(gM[I * DK + ch] - gE[J * DK + ch]);
+    for (unsigned t = 1; t < static_cast<unsigned>(NB); ++t) bI += pp >= t * (t + 1) / 2 ? 1u : 0u;
+    const unsigned bJ = pp - bI * (bI + 1) / 2;
+    float x;
+    if (bI == bJ) {
+      x = -Dblk[bJ * DK + ch];
+      fv[idx] = x <= kDiagRange ? __builtin_amdgcn_exp2f(x) : 0.f;
+    } else {
+      x = 0.f;
+      for (unsigned kk = bJ + 1; kk < bI; ++kk) x += Dblk[kk * DK + ch];
+      fv[idx] = __builtin_amdgcn_exp2f(x);
+    }
   }
-  if (tid < DK) reinterpret_cast<float*>(blk + B::oG)[tid] = __builtin_amdgcn_exp2f(gE[(NB - 1) * DK + tid]);
+  if (tid < DK) {
+    float x = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < NB; ++kk) x += Dblk[kk * DK + tid];
+    reinterpret_cast<float*>(blk + B::oG)[tid] = __builtin_amdgcn_exp2f(x);  // Gamma = e^{g_last}
+  }
   if (tid < C) reinterpret_cast<float*>(blk + B::oB)[tid] = bet[tid];
 
   // The next item's gates (half of its input bytes) load from here on: this
@@ -663,42 +702,44 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
 
   // ---- element factors, S-independent outputs ---------------------------
   {
-    const int I = r0 >> 4;  // all of this thread's rows are in block I
-    const f32x4 gm = *reinterpret_cast<const f32x4*>(gM + I * DK + c4);
-    const f32x4 gz = *reinterpret_cast<const f32x4*>(gE + (NB - 1) * DK + c4);
-    f32x4 emv, eev, kb[RPT];
+    // e^{sum of D over the blocks before I} and after I, per channel
+    f32x4 sb = {0.f, 0.f, 0.f, 0.f}, sa = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < NB; ++kk) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(Dblk + kk * DK + c4);
+      if (kk < I) sb += x;
+      if (kk > I) sa += x;
+    }
+    f32x4 ebv, eav, kb[RPT];
     float bt[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) bt[i] = bet[r0 + i];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      emv[j] = __builtin_amdgcn_exp2f(gm[j]);          // e^{g_m} <= 1
-      eev[j] = __builtin_amdgcn_exp2f(gz[j] - gm[j]);  // e^{g_last - g_m} <= 1
+      ebv[j] = __builtin_amdgcn_exp2f(sb[j]);  // <= 1
+      eav[j] = __builtin_amdgcn_exp2f(sa[j]);  // <= 1
     }
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const unsigned r = static_cast<unsigned>(r0 + i);
-      // e^{g_r - g_m} and e^{g_m - g_r}: each spans the decay over at most 8
-      // tokens either way (computed directly: a product through a farther
-      // reference can underflow where the ratio does not)
-      f32x4 frd, fc;
+      f32x4 ed, es;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        frd[j] = __builtin_amdgcn_exp2f(lg[i][j] - gm[j]);
-        fc[j] = __builtin_amdgcn_exp2f(gm[j] - lg[i][j]);
+        ed[j] = __builtin_amdgcn_exp2f(dl[i][j]);  // e^{d_r} <= 1
+        es[j] = __builtin_amdgcn_exp2f(sl[i][j]);  // e^{s_r} <= 1
       }
-      const f32x4 fre = frd * emv;  // e^{g_r}: underflows only where e^{g_r} is negligible
+      const f32x4 fre = ed * ebv;  // e^{g_r}
       const unsigned lo = loff<T, L::RBK>(r, static_cast<unsigned>(c4));
-      store4(reinterpret_cast<T*>(Krd + lo), kv[i] * frd);
-      store4(reinterpret_cast<T*>(Qrd + lo), qv[i] * frd);
-      const f32x4 kc = kv[i] * fc;
+      store4(reinterpret_cast<T*>(Krd + lo), kv[i] * ed);
+      store4(reinterpret_cast<T*>(Qrd + lo), qv[i] * ed);
+      const f32x4 kc = kv[i] * es;
       store4(reinterpret_cast<T*>(Kc + lo), kc);
       const int to = static_cast<int>(toff<T, B::RB_R>(r, static_cast<unsigned>(c4)));
       buffer_store4(wr, static_cast<int>(B::oQ) + to, qv[i] * fre, static_cast<T*>(nullptr));
       buffer_store4(wr, static_cast<int>(B::oR) + to, bt[i] * (kv[i] * fre), static_cast<T*>(nullptr));
-      kb[i] = kc * eev;  // e^{g_last - g_r} k_r
+      kb[i] = kc * eav;  // e^{g_last - g_r} k_r
     }
-    // Kb^T tile (rows = key channel): this thread's rows are consecutive, so
+  // Kb^T tile (rows = key channel): this thread's rows are consecutive, so
     // groups of 4 stay contiguous under the column permutation.
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -727,17 +768,54 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
   // ---- a3: gated k k^T (A, fp32 in LDS) and q k^T (P) via MFMA, and the
   // diagonal blocks of the UT inverse T = (I + A)^{-1} ----------------------
   // Block pair (I, J <= I); returns this lane's A values (beta-scaled, masked).
-  auto pair = [&](int I, int J, bool diag) {
-    const float* fe = fv + (J * (J + 1) / 2 + J) * DK;  // e^{g_{e_J} - g_{m_J}}
-    const float* f = fv + (I * (I + 1) / 2 + J) * DK;   // e^{g_{m_I} - g_{e_J}}
+  // Channels of diagonal block I whose scale is 0 (decay beyond 2^86 across
+  // the block): their contributions to this lane's A and P values, from the
+  // per-token gates, e^{g_r - g_s} = prod_{s < u <= r} alpha_u.  Rows past
+  // the end take alpha = 1 (and are masked by beta = 0, or unused).
+  auto diag_exact = [&](int I, f32x4& aA, f32x4& aP) {
+    const float* sd = fv + (I * (I + 1) / 2 + I) * DK;
+#pragma unroll
+    for (int j = 0; j < (DK + 63) / 64; ++j) {
+      unsigned long long m = __ballot(lane < DK - 64 * j && sd[64 * j + lane] == 0.f);
+      while (m) {
+        const int ch = 64 * j + static_cast<int>(__builtin_ctzll(m));
+        m &= m - 1;
+        const int row = 16 * I + n;
+        const size_t e = (static_cast<size_t>(t0 + min(row, len - 1)) * H + h) * DK + ch;
+        const float an = row < len ? __builtin_amdgcn_exp2f(la[e] * kLog2e) : 1.f;
+        const float kn = io<T>::load(k + e), qn = io<T>::load(q + e);
+        float prod = 1.f, ef[4] = {1.f, 1.f, 1.f, 1.f}, kr[4] = {0.f, 0.f, 0.f, 0.f}, qr[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const float au = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(an), u));
+          const float ku = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(kn), u));
+          const float qu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(qn), u));
+          if (u > n) prod *= au;
+          if (g == (u >> 2)) {
+            ef[u & 3] = prod;
+            kr[u & 3] = ku;
+            qr[u & 3] = qu;
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          aA[i] += kr[i] * kn * ef[i];
+          aP[i] += qr[i] * kn * ef[i];
+        }
+      }
+    }
+  };
+  // Block pair (I, J <= I); returns this lane's A values (beta-scaled, masked).
+  auto pair = [&](int I, int J) {
+    const float* f = fv + (I * (I + 1) / 2 + J) * DK;  // column scale of the pair
     f32x4 aA = {0.f, 0.f, 0.f, 0.f}, aP = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
     for (int k0 = 0; k0 < DK; k0 += M::KS) {
-      const typename M::frag bf = diag ? natf<T, L::RBK>::raw(Kc, 16 * J + n, k0, g)
-                                       : natf<T, L::RBK>::scaled(Kc, 16 * J + n, fe, f, k0, g);
+      const typename M::frag bf = natf<T, L::RBK>::scaled(Kc, 16 * J + n, f, k0, g);
       aA = M::mma(natf<T, L::RBK>::raw(Krd, 16 * I + n, k0, g), bf, aA);
       aP = M::mma(natf<T, L::RBK>::raw(Qrd, 16 * I + n, k0, g), bf, aP);
     }
+    if (I == J) diag_exact(I, aA, aP);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int rr = 4 * g + i;
@@ -760,7 +838,7 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
   // A_II's position (c, r).
   f32x4 tii = {0.f, 0.f, 0.f, 0.f};
   if (wave < NB) {
-    const f32x4 a = pair(wave, wave, true);
+    const f32x4 a = pair(wave, wave);
     float* Ab = A + (16 * wave) * L::AP + 16 * wave;
     __builtin_amdgcn_wave_barrier();  // other lanes' A_II stores before the reads below
     f32x4 m, mt;
@@ -779,7 +857,7 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
     for (int o = wave - NB; o < NB * (NB - 1) / 2; o += kPrepThreads / 64 - NB) {
       int I = 1;
       while ((I + 1) * I / 2 <= o) ++I;
-      pair(I, o - I * (I - 1) / 2, false);
+      pair(I, o - I * (I - 1) / 2);
     }
   }
   __syncthreads();
@@ -1004,7 +1082,7 @@ template <typename T, int C, int DK, int DV, int WAVES>
 __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel(
     const T* __restrict__ v, const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_off,
     const int32_t* __restrict__ order, int N, int H, const unsigned char* __restrict__ ws, const float* S0,
-    T* __restrict__ o, float* S_T, int* ready, int seg) {
+    T* __restrict__ o, float* S_T, int* ready, int seg, int wait_polls, const int* guard) {
   typedef Blk<T, C, DK> B;
   typedef mma16<T> M;
   typedef accb<T> AB;
@@ -1024,6 +1102,9 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
   constexpr int NVG = C / VRPL;                               // wave-loads per v tile
   static_assert(VROWB % 16 == 0 && 64 % VLPR == 0 && C % VRPL == 0, "v tile geometry");
   extern __shared__ __align__(1024) unsigned char smem[];
+  // Recovery launch of the overlapped schedule: runs only if the state pass
+  // of the call stopped waiting for prepared chunks (flag word nonzero).
+  if (guard && __hip_atomic_load(guard, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) return;
 
   const int x = blockIdx.x;
   const int xcd = x & 7, slot8 = x >> 3;
@@ -1051,8 +1132,10 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
   // (wave-uniform), so the common case is one compare, not a division per
   // chunk on the scalar unit the CU's waves share.  The counter is polled
   // with device-scope loads before a block is touched.  The wait is bounded
-  // (~2^20 polls of ~500 cycles); a wave that runs out stops waiting for the
-  // rest of the launch, so a stalled producer cannot hold the GPU.
+  // (wait_polls polls of ~1 us); a wave that runs out sets the flag word
+  // beside the counter and stops waiting for the rest of the launch, so a
+  // stalled producer cannot hold the GPU, and the call's recovery launches
+  // (guarded by that flag) recompute every result on the caller's stream.
   auto upto_of = [&](int seen) { return (seen + 1) * seg - 1 - c0; };
   int upto = ready ? upto_of(0) : 0x7fffffff;
   bool patient = true;
@@ -1060,7 +1143,7 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
     const int need = min(cc, ce - 1);
     if (need <= upto || !patient) return;
     int spin = 0;
-    for (; need > upto && spin < (1 << 20); ++spin) {
+    for (; need > upto && spin < wait_polls; ++spin) {
       upto = upto_of(
           __builtin_amdgcn_readfirstlane(__hip_atomic_load(ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)));
       if (need > upto) __builtin_amdgcn_s_sleep(8);
@@ -1590,20 +1673,38 @@ bool make_prefill_plan(const kda_prefill_desc* d, int64_t max_chunks, PrefillPla
   off = align256(off);
   p->seg = 0;
   p->off_ready = 0;
-  if (narrow_scan_wgs(d->num_seqs, d->num_heads, d->dv) <= kPipeMaxScanWgs && max_chunks >= 2 * kPipeMinSeg) {
+  p->off_carry = 0;
+  if (!(d->flags & KDA_PREFILL_ONE_STREAM) && narrow_scan_wgs(d->num_seqs, d->num_heads, d->dv) <= kPipeMaxScanWgs &&
+      max_chunks >= 2 * kPipeMinSeg) {
     const int64_t seg = (max_chunks + kPipeMaxSegs - 1) / kPipeMaxSegs;
     p->seg = seg > kPipeMinSeg ? seg : kPipeMinSeg;
     p->off_ready = off;
     off += 256;
+    // final states of an in-place call, held until the call knows it needs
+    // no recovery
+    p->off_carry = off;
+    off = align256(off + static_cast<size_t>(d->num_seqs) * d->num_heads * d->dk * d->dv * 4);
   }
   p->total_bytes = align256(off);
   return true;
 }
 
+// Polls (each about a microsecond) a scan loader wave of the overlapped
+// schedule waits for a prepared segment before it gives up; a test hook
+// can lower it.
+constexpr int kDefaultWaitPolls = 1 << 17;
+static std::atomic<int> g_wait_polls{kDefaultWaitPolls};
+static int prefill_wait_polls() { return g_wait_polls.load(std::memory_order_relaxed); }
+
+int set_prefill_wait_polls(int polls) {
+  return g_wait_polls.exchange(polls > 0 ? polls : (polls == 0 ? 0 : kDefaultWaitPolls));
+}
+
 template <typename T, int C, int DK, int DV, int WAVES>
 static hipError_t launch_scan(const PrefillPlan& p, const void* v, const int32_t* cu, const int32_t* chunk_off,
                               const int32_t* order, const unsigned char* blocks, const float* S0, void* o,
-                              float* S_T, hipStream_t st, int* ready = nullptr, int seg = 1) {
+                              float* S_T, hipStream_t st, int* ready = nullptr, int seg = 1,
+                              const int* guard = nullptr) {
   typedef ScanLds<T, C, DK, 16 * WAVES> SL;
   static_assert(SL::total <= 160 * 1024, "scan LDS");
   hipError_t e = set_lds_limit(reinterpret_cast<const void*>(&scan_kernel<T, C, DK, DV, WAVES>), SL::total);
@@ -1613,31 +1714,33 @@ static hipError_t launch_scan(const PrefillPlan& p, const void* v, const int32_t
   const unsigned grid = static_cast<unsigned>((pairs + 7) / 8 * 8 * nsplit);
   hipLaunchKernelGGL((scan_kernel<T, C, DK, DV, WAVES>), dim3(grid), dim3(scan_threads<T, C, DK, WAVES>()), SL::total, st,
                      static_cast<const T*>(v), cu, chunk_off, order, p.N, p.H, blocks, S0, static_cast<T*>(o), S_T,
-                     ready, seg);
+                     ready, seg, prefill_wait_polls(), guard);
   return hipGetLastError();
 }
 
 // Compute units of the current device (cached per device).
 static hipError_t device_cus(int* cus) {
-  constexpr int kMaxDev = 64;
-  static int cache[kMaxDev] = {};
+  static int cache[64] = {};
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  if (dev >= 0 && dev < kMaxDev && cache[dev] > 0) {
+  if (dev >= 0 && dev < 64 && cache[dev] > 0) {
     *cus = cache[dev];
     return hipSuccess;
   }
   int n = 0;
   if ((e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
   if (n < 1) n = 1;
-  if (dev >= 0 && dev < kMaxDev) cache[dev] = n;
+  if (dev >= 0 && dev < 64) cache[dev] = n;
   *cus = n;
   return hipSuccess;
 }
 
 // Per-device pair of CU-masked streams (default priority) and the events of
-// the overlapped schedule; created on first use and kept for the process.
+// the overlapped schedule; created on first use and destroyed at process
+// exit (from an atexit handler, registered after the HIP runtime has
+// started, so it runs while the runtime and any tool attached to it are
+// still alive).
 struct PipeStreams {
   hipStream_t prep = nullptr, scan = nullptr;
   hipEvent_t fork = nullptr, join = nullptr, join_prep = nullptr;
@@ -1645,33 +1748,45 @@ struct PipeStreams {
   std::mutex mu;  // one schedule at a time may use the shared streams/events
 };
 
-// Returns in *out the current device's streams when the scan (scan_wgs
-// workgroups) fits on its half of the CUs, else nullptr.
-// The overlapped schedule needs the scan and the prep kernels of one call
-// to run at the same time; a tool that serialises dispatches (hardware
-// counter collection) must turn it off: KDA_PREFILL_OVERLAP=0 selects the
-// one-stream schedule (same kernels, same bytes moved).
-static bool overlap_enabled() {
-  static const bool on = [] {
-    const char* v = std::getenv("KDA_PREFILL_OVERLAP");
-    return !(v && std::strcmp(v, "0") == 0);
-  }();
-  return on;
+constexpr int kMaxDev = 64;
+static std::mutex g_pipe_mu;
+static PipeStreams* g_pipe[kMaxDev] = {};
+static bool g_pipe_unavailable[kMaxDev] = {};
+
+static void destroy_pipe(PipeStreams* ps) {
+  if (ps->scan) (void)hipStreamDestroy(ps->scan);
+  if (ps->prep) (void)hipStreamDestroy(ps->prep);
+  if (ps->fork) (void)hipEventDestroy(ps->fork);
+  if (ps->join) (void)hipEventDestroy(ps->join);
+  if (ps->join_prep) (void)hipEventDestroy(ps->join_prep);
+  delete ps;
 }
 
+static void release_pipe_streams() {
+  std::lock_guard<std::mutex> lock(g_pipe_mu);
+  for (int dev = 0; dev < kMaxDev; ++dev) {
+    if (!g_pipe[dev]) continue;
+    if (hipSetDevice(dev) == hipSuccess) {
+      (void)hipStreamSynchronize(g_pipe[dev]->scan);
+      (void)hipStreamSynchronize(g_pipe[dev]->prep);
+      destroy_pipe(g_pipe[dev]);
+    }
+    g_pipe[dev] = nullptr;
+  }
+  (void)hipGetLastError();
+}
+
+// Returns in *out the current device's streams when the scan (scan_wgs
+// workgroups) fits on its half of the CUs, else nullptr.
 static hipError_t pipe_streams(int64_t scan_wgs, PipeStreams** out) {
-  constexpr int kMaxDev = 64;
-  static std::mutex mu;
-  static PipeStreams* cache[kMaxDev] = {};
-  static bool unavailable[kMaxDev] = {};
+  static bool registered = false;
   *out = nullptr;
-  if (!overlap_enabled()) return hipSuccess;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDev) return hipSuccess;
-  std::lock_guard<std::mutex> lock(mu);
-  if (!cache[dev] && !unavailable[dev]) {
+  std::lock_guard<std::mutex> lock(g_pipe_mu);
+  if (!g_pipe[dev] && !g_pipe_unavailable[dev]) {
     hipDeviceProp_t prop;
     if ((e = hipGetDeviceProperties(&prop, dev)) != hipSuccess) return e;
     const int cus = prop.multiProcessorCount, words = (cus + 31) / 32;
@@ -1694,19 +1809,15 @@ static hipError_t pipe_streams(int64_t scan_wgs, PipeStreams** out) {
     ok = ok && hipEventCreateWithFlags(&ps->join_prep, hipEventDisableTiming) == hipSuccess;
     if (ok) {
       ps->scan_cus = ns;
-      cache[dev] = ps;
+      g_pipe[dev] = ps;
+      if (!registered) registered = std::atexit(release_pipe_streams) == 0;
     } else {  // no CU masks here: fall back to the single-stream schedule
-      if (ps->scan) (void)hipStreamDestroy(ps->scan);
-      if (ps->prep) (void)hipStreamDestroy(ps->prep);
-      if (ps->fork) (void)hipEventDestroy(ps->fork);
-      if (ps->join) (void)hipEventDestroy(ps->join);
-      if (ps->join_prep) (void)hipEventDestroy(ps->join_prep);
-      delete ps;
+      destroy_pipe(ps);
       (void)hipGetLastError();
-      unavailable[dev] = true;
+      g_pipe_unavailable[dev] = true;
     }
   }
-  if (cache[dev] && scan_wgs <= cache[dev]->scan_cus) *out = cache[dev];
+  if (g_pipe[dev] && scan_wgs <= g_pipe[dev]->scan_cus) *out = g_pipe[dev];
   return hipSuccess;
 }
 
@@ -1727,7 +1838,8 @@ static hipError_t launch_prefill_t(const PrefillPlan& p, const void* q, const vo
   static_assert(PrepLds<T, C, DK>::total <= 160 * 1024, "prep LDS");
   // Persistent prep: as many workgroups as fit on the CUs the stream may
   // use (LDS-limited), each walking (chunk, head) items.
-  auto prep = [&](int64_t cbase, int64_t count, hipStream_t s, int cus, int32_t* publish, int published) -> hipError_t {
+  auto prep = [&](int64_t cbase, int64_t count, hipStream_t s, int cus, int32_t* publish, int published,
+                  const int* guard) -> hipError_t {
     hipError_t r = set_lds_limit(reinterpret_cast<const void*>(&prep_kernel<T, C, DK>), lp);
     if (r != hipSuccess) return r;
     const int64_t per_cu = (160 * 1024) / static_cast<int64_t>(lp) > 0 ? (160 * 1024) / static_cast<int64_t>(lp) : 1;
@@ -1735,7 +1847,7 @@ static hipError_t launch_prefill_t(const PrefillPlan& p, const void* q, const vo
     const int64_t grid = items < per_cu * cus ? items : per_cu * cus;
     hipLaunchKernelGGL((prep_kernel<T, C, DK>), dim3(static_cast<unsigned>(grid)), dim3(kPrepThreads), lp, s,
                        static_cast<const T*>(q), static_cast<const T*>(k), la, beta, cu, chunk_off, p.N, p.H,
-                       blocks, static_cast<int>(cbase), static_cast<int>(count), publish, published);
+                       blocks, static_cast<int>(cbase), static_cast<int>(count), publish, published, guard);
     return hipGetLastError();
   };
   int cus = 0;
@@ -1746,6 +1858,10 @@ static hipError_t launch_prefill_t(const PrefillPlan& p, const void* q, const vo
   // raised to j - 1 by the first thread of segment j's prep launch and to
   // the last segment by a ready_kernel; both streams fork from and join
   // back into the caller's stream.  Segment 0's prep has the whole device.
+  // If a loader wave stops waiting (the device did not run the two streams
+  // side by side), the flag word ready[1] is set and the two guarded
+  // recovery launches at the end recompute every result on the caller's
+  // stream; otherwise they return at once.
   PipeStreams* ps = nullptr;
   if (p.seg > 0) {
     e = pipe_streams(narrow_scan_wgs(p.N, p.H, DV), &ps);
@@ -1753,30 +1869,45 @@ static hipError_t launch_prefill_t(const PrefillPlan& p, const void* q, const vo
   }
   if (ps) {
     const int64_t nseg = (p.max_chunks + p.seg - 1) / p.seg;
-    std::lock_guard<std::mutex> lock(ps->mu);
-    e = prep(0, p.seg < p.max_chunks ? p.seg : p.max_chunks, st, cus, nullptr, 0);
-    if (e != hipSuccess) return e;
-    if ((e = hipEventRecord(ps->fork, st)) != hipSuccess) return e;
-    if ((e = hipStreamWaitEvent(ps->prep, ps->fork, 0)) != hipSuccess) return e;
-    if ((e = hipStreamWaitEvent(ps->scan, ps->fork, 0)) != hipSuccess) return e;
-    e = launch_scan<T, C, DK, DV, 2>(p, v, cu, chunk_off, order, blocks, S0, o, S_T, ps->scan, ready,
-                                     static_cast<int>(p.seg));
-    if (e != hipSuccess) return e;
-    for (int64_t j = 1; j < nseg; ++j) {
-      const int64_t c0 = j * p.seg, c1 = c0 + p.seg < p.max_chunks ? c0 + p.seg : p.max_chunks;
-      if ((e = prep(c0, c1 - c0, ps->prep, cus - ps->scan_cus, j > 1 ? ready : nullptr, static_cast<int>(j - 1))) !=
-          hipSuccess)
-        return e;
+    const bool in_place = S_T != nullptr && S_T == S0;
+    float* carry = reinterpret_cast<float*>(w + p.off_carry);
+    const int* flag = ready + 1;
+    {
+      std::lock_guard<std::mutex> lock(ps->mu);
+      e = prep(0, p.seg < p.max_chunks ? p.seg : p.max_chunks, st, cus, nullptr, 0, nullptr);
+      if (e != hipSuccess) return e;
+      if ((e = hipEventRecord(ps->fork, st)) != hipSuccess) return e;
+      if ((e = hipStreamWaitEvent(ps->prep, ps->fork, 0)) != hipSuccess) return e;
+      if ((e = hipStreamWaitEvent(ps->scan, ps->fork, 0)) != hipSuccess) return e;
+      e = launch_scan<T, C, DK, DV, 2>(p, v, cu, chunk_off, order, blocks, S0, o, in_place ? carry : S_T, ps->scan,
+                                       ready, static_cast<int>(p.seg));
+      if (e != hipSuccess) return e;
+      for (int64_t j = 1; j < nseg; ++j) {
+        const int64_t c0 = j * p.seg, c1 = c0 + p.seg < p.max_chunks ? c0 + p.seg : p.max_chunks;
+        if ((e = prep(c0, c1 - c0, ps->prep, cus - ps->scan_cus, j > 1 ? ready : nullptr, static_cast<int>(j - 1),
+                      nullptr)) != hipSuccess)
+          return e;
+      }
+      hipLaunchKernelGGL(ready_kernel, dim3(1), dim3(64), 0, ps->prep, ready, static_cast<int>(nseg - 1));
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      if ((e = hipEventRecord(ps->join, ps->scan)) != hipSuccess) return e;
+      if ((e = hipEventRecord(ps->join_prep, ps->prep)) != hipSuccess) return e;
+      if ((e = hipStreamWaitEvent(st, ps->join, 0)) != hipSuccess) return e;
+      if ((e = hipStreamWaitEvent(st, ps->join_prep, 0)) != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(ready_kernel, dim3(1), dim3(64), 0, ps->prep, ready, static_cast<int>(nseg - 1));
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if ((e = hipEventRecord(ps->join, ps->scan)) != hipSuccess) return e;
-    if ((e = hipEventRecord(ps->join_prep, ps->prep)) != hipSuccess) return e;
-    if ((e = hipStreamWaitEvent(st, ps->join, 0)) != hipSuccess) return e;
-    return hipStreamWaitEvent(st, ps->join_prep, 0);
+    if (in_place) {
+      const size_t n4 = static_cast<size_t>(p.N) * p.H * DK * DV / 4;
+      const unsigned grid = static_cast<unsigned>(n4 / 256 < 1024 ? (n4 + 255) / 256 : 1024);
+      hipLaunchKernelGGL(carry_out_kernel, dim3(grid), dim3(256), 0, st, reinterpret_cast<const f32x4*>(carry),
+                         reinterpret_cast<f32x4*>(S_T), n4, flag);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    // recovery (runs only if the flag word is set)
+    if ((e = prep(0, p.max_chunks, st, cus, nullptr, 0, flag)) != hipSuccess) return e;
+    return launch_scan<T, C, DK, DV, 2>(p, v, cu, chunk_off, order, blocks, S0, o, S_T, st, nullptr, 1, flag);
   }
   if (p.max_chunks > 0) {
-    e = prep(0, p.max_chunks, st, cus, nullptr, 0);
+    e = prep(0, p.max_chunks, st, cus, nullptr, 0, nullptr);
     if (e != hipSuccess) return e;
   }
   // Few (sequence, head) pairs: narrower value tiles to put more CUs on the

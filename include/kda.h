@@ -31,17 +31,15 @@
  *     once under a lock: per-device kernel attributes and, for the
  *     overlapped prefill schedule, two CU-masked streams with their events
  *     per device, on which concurrent overlapped calls for one device take
- *     turns to enqueue their work.
- *   - Device-side preconditions that are documented but not checked:
- *     finite inputs; log_alpha <= 0; for the chunked prefill additionally,
- *     per channel, the log_alpha of any 9 consecutive tokens of a sequence
- *     sum to at least -80 (log_alpha >= -8 per element suffices): the
- *     intra-chunk gate ratios are factorised around references inside each
- *     16-token block, and every factor must stay inside the fp32 range
- *     (beyond it a scale factor of an off-diagonal block underflows while the
- *     ratio it stands for need not be small, so results are wrong); when no host mirror of
- *     cu_seqlens is given, cu_seqlens[0] = 0, non-decreasing and
- *     cu_seqlens[N] = total_tokens.
+ *     turns to enqueue their work; the streams are destroyed at process exit.
+ *   - Device-side preconditions that are documented but not checked: finite
+ *     inputs; log_alpha <= 0; when no host mirror of cu_seqlens is given,
+ *     cu_seqlens[0] = 0, non-decreasing and cu_seqlens[N] = total_tokens.
+ *     Any finite log_alpha <= 0 is supported (no range limit): the chunked
+ *     prefill forms every intra-chunk gate ratio from sums of log_alpha over
+ *     contiguous token ranges with factors at most 1, and forms a diagonal
+ *     16-token block's ratios token by token for channels whose decay across
+ *     the block leaves the fp32 range.
  */
 #ifndef KDA_H_
 #define KDA_H_
@@ -66,6 +64,15 @@ typedef enum {
   KDA_BF16 = 1   /* q, k, v and o in bfloat16 */
 } kda_dtype;
 
+/* kda_prefill_desc.flags */
+enum {
+  /* Run the chunk preparation and the state pass one after the other on the
+     caller's stream, never on the library's two CU-masked streams (for tools
+     that serialise kernel dispatches, such as hardware-counter collection;
+     results are identical, and the workspace is smaller). */
+  KDA_PREFILL_ONE_STREAM = 1
+};
+
 /* Problem description for the packed variable-length prefill. */
 typedef struct {
   int32_t num_seqs;      /* N >= 0 sequences packed back to back */
@@ -77,6 +84,7 @@ typedef struct {
   const int32_t* cu_seqlens_host; /* optional HOST copy of cu_seqlens [N+1]; when
                                      given it is validated and used to size the
                                      launch exactly; may be NULL */
+  uint32_t flags;        /* KDA_PREFILL_* bits; 0 for the default schedule */
 } kda_prefill_desc;
 
 /*
@@ -112,18 +120,15 @@ size_t kda_prefill_workspace_size(const kda_prefill_desc* desc);
  *   stream     hipStream_t or NULL.
  *
  * Streams: the work is ordered on `stream`.  For few (sequence, head) pairs
- * (N * H * dv / 32 <= 128) the call forks onto two library-owned streams that
- * split the CUs (one runs the serial state pass, the other prepares later
- * chunks and advances a counter in the workspace that the first waits on) and
- * joins back into `stream` with events.  That schedule needs the device to
- * run the two library streams at the same time (each has its own CU-masked
- * hardware queue): the state pass waits, for a bounded time, for the other
- * stream's prepared chunks, and if they never come (a tool that serialises
- * kernel dispatches, such as hardware-counter collection, or an
- * oversubscribed device) it stops waiting and its results are wrong; it then
- * sets the second 4-byte word of the workspace's last 256 bytes.  The
- * environment variable KDA_PREFILL_OVERLAP=0, read once per process, selects
- * the one-stream schedule (same kernels and results) for such settings.
+ * (N * H * dv / 32 <= 128), unless flags has KDA_PREFILL_ONE_STREAM, the call
+ * forks onto two library-owned streams that split the CUs (one runs the
+ * serial state pass, the other prepares later chunks and advances a counter
+ * in the workspace that the first waits on) and joins back into `stream`
+ * with events.  The wait is bounded: if the device does not run the two
+ * streams side by side (a tool that serialises dispatches, an oversubscribed
+ * device), the state pass stops waiting, and two recovery launches on
+ * `stream`, which otherwise return at once, recompute every output there.
+ * Results are correct either way; kda_prefill_recovered reports which.
  *
  * Errors: KDA_ERR_INVALID_ARGUMENT (null pointer where data is required,
  * negative sizes, bad host offsets, misaligned workspace, overlapping buffers),
@@ -137,6 +142,27 @@ kda_status kda_prefill(const kda_prefill_desc* desc,
                        const int32_t* cu_seqlens, const float* S0,
                        void* o, float* S_T,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * After a kda_prefill call that used `workspace` for `desc` on `stream`:
+ * waits for `stream` (host synchronisation) and sets *recovered to 1 if
+ * that call's overlapped schedule stopped waiting for its prepared chunks
+ * and recomputed its outputs on the caller's stream, else 0.  Calls that
+ * ran the one-stream schedule report 0 without synchronising.  Errors:
+ * KDA_ERR_INVALID_ARGUMENT (bad desc, null pointer), KDA_ERR_DEVICE.
+ */
+kda_status kda_prefill_recovered(const kda_prefill_desc* desc, const void* workspace, int32_t* recovered,
+                                 void* stream);
+
+/*
+ * Test hook (process-wide): the number of polls, each about a microsecond,
+ * for which the overlapped schedule's state pass waits for a prepared
+ * segment before it gives up and the call recovers.  polls > 0 sets it,
+ * 0 makes the state pass never wait (every overlapped call then recovers),
+ * polls < 0 restores the default.  Returns the previous value.  For tests
+ * of the recovery path; calls in flight on other threads see either value.
+ */
+int32_t kda_prefill_set_wait_limit(int32_t polls);
 
 /*
  * One decode step for B independent requests: the recurrence applied once
@@ -164,7 +190,7 @@ kda_status kda_decode_step(int32_t B, int32_t H, int32_t dk, int32_t dv, kda_dty
 /* Static, human-readable name of a status code (never NULL). */
 const char* kda_status_string(kda_status s);
 
-/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH (2.0.0: desc.flags). */
 int32_t kda_version(void);
 
 #ifdef __cplusplus

@@ -110,14 +110,17 @@ def prefill(q, k, v, log_alpha, beta, cu_seqlens, S0=None, threads: int = 0, ret
     return (o, ST, used) if return_threads else (o, ST)
 
 
-def decode_step(q, k, v, log_alpha, beta, S, threads: int = 0, lib=None):
+def decode_step(q, k, v, log_alpha, beta, S, threads: int = 0, lib=None, inplace: bool = False):
     """One recurrence step for B independent states.
 
     q, k, log_alpha: [B, H, dk]; v: [B, H, dv]; beta: [B, H]; S: [B, H, dk, dv].
-    Returns (o [B, H, dv], S_new [B, H, dk, dv]); the input S is not modified.
+    Returns (o [B, H, dv], S_new [B, H, dk, dv]); the input S is not modified,
+    unless ``inplace`` is set and S is a C-contiguous float64 array, which is
+    then updated and returned as S_new.
     """
     q, k, v, la, b = _f64(q), _f64(k), _f64(v), _f64(log_alpha), _f64(beta)
-    S = np.array(S, dtype=np.float64, copy=True, order="C")
+    if not (inplace and isinstance(S, np.ndarray) and S.dtype == np.float64 and S.flags["C_CONTIGUOUS"]):
+        S = np.array(S, dtype=np.float64, copy=True, order="C")
     B, H, dk = q.shape
     dv = v.shape[2]
     assert S.shape == (B, H, dk, dv)

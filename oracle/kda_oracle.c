@@ -62,9 +62,9 @@ static void run_pair(const pair_job *J) {
   const int H = J->H, dk = J->dk, dv = J->dv, h = J->h;
   double *S = J->S;
   double *r = (double *)malloc(sizeof(double) * (size_t)dv);
-  if (J->S0)
-    memcpy(S, J->S0, sizeof(double) * (size_t)dk * dv);
-  else
+  if (J->S0) {
+    if (J->S0 != S) memcpy(S, J->S0, sizeof(double) * (size_t)dk * dv);
+  } else
     memset(S, 0, sizeof(double) * (size_t)dk * dv);
   for (int t = 0; t < J->T; ++t) {
     const double *qt = J->q + ((size_t)t * H + h) * dk;
@@ -171,10 +171,7 @@ int kda_oracle_decode_step(int B, int H, int dk, int dv, const double *q,
   if (B < 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
   const int njobs = B * H;
   pair_job *jobs = (pair_job *)calloc((size_t)(njobs > 0 ? njobs : 1), sizeof(pair_job));
-  /* run_pair starts from S0 and writes S; for the in-place update it starts
-     from a snapshot of the incoming states. */
-  double *snap = (double *)malloc(sizeof(double) * (size_t)(njobs > 0 ? njobs : 1) * dk * dv);
-  memcpy(snap, S, sizeof(double) * (size_t)njobs * dk * dv);
+  /* run_pair starts from S0 and writes S; here S0 is S itself (in place) */
   for (int b = 0; b < B; ++b)
     for (int h = 0; h < H; ++h) {
       pair_job *J = &jobs[b * H + h];
@@ -186,7 +183,7 @@ int kda_oracle_decode_step(int B, int H, int dk, int dv, const double *q,
       J->v = v + (size_t)b * H * dv;
       J->beta = beta + (size_t)b * H;
       J->o = o + (size_t)b * H * dv;
-      J->S0 = snap + ((size_t)b * H + h) * dk * dv;
+      J->S0 = S + ((size_t)b * H + h) * dk * dv;
       J->S = S + ((size_t)b * H + h) * dk * dv;
     }
   if (nthreads <= 0) nthreads = (int)sysconf(_SC_NPROCESSORS_ONLN);
@@ -204,7 +201,6 @@ int kda_oracle_decode_step(int B, int H, int dk, int dv, const double *q,
     free(th);
   }
   pthread_mutex_destroy(&Q.mu);
-  free(snap);
   free(jobs);
   return nthreads;
 }

@@ -50,8 +50,11 @@ def rel_err(x: np.ndarray, ref: np.ndarray) -> float:
     return num / den
 
 
-def gpu_prefill(w: synth.PrefillInputs, chunk: int = None, S0=None, in_place: bool = False, host_offsets=True):
-    """Run libkda prefill on the inputs; returns (o, S_T) as float64 numpy."""
+def gpu_prefill(w: synth.PrefillInputs, chunk: int = None, S0=None, in_place: bool = False, host_offsets=True,
+                one_stream: bool = False, want_state: bool = True, report: dict = None):
+    """Run libkda prefill on the inputs; returns (o, S_T) as float64 numpy
+    (S_T None when want_state is False).  When ``report`` is a dict, its key
+    "recovered" is set to whether the call's overlapped schedule recovered."""
     import gated_delta_rule_33_amd as kda
     torch = torch_mod()
     dt = w.io_dtype
@@ -64,10 +67,14 @@ def gpu_prefill(w: synth.PrefillInputs, chunk: int = None, S0=None, in_place: bo
     if in_place:
         assert s0d is not None
         kw["S_T"] = s0d
-    o, ST = kda.prefill(q, k, v, la, b, cu, s0d, chunk=chunk or w.chunk,
-                        cu_seqlens_host=w.cu_seqlens.tolist() if host_offsets else None, **kw)
+    host_cu = w.cu_seqlens.tolist() if host_offsets else None
+    o, ST = kda.prefill(q, k, v, la, b, cu, s0d, chunk=chunk or w.chunk, cu_seqlens_host=host_cu,
+                        one_stream=one_stream, want_state=want_state, **kw)
     torch.cuda.synchronize()
-    return host(o), host(ST)
+    if report is not None:
+        report["recovered"] = kda.prefill_recovered(q, v, cu, chunk=chunk or w.chunk, cu_seqlens_host=host_cu,
+                                                    one_stream=one_stream)
+    return host(o), (host(ST) if ST is not None else None)
 
 
 def oracle_prefill(w: synth.PrefillInputs, S0=None, heads=None, threads: int = 0):
@@ -88,22 +95,8 @@ def check(name: str, got: np.ndarray, ref: np.ndarray, tol: float):
     return e
 
 
-def overlap_counters():
-    """(last segment written, gave-up flag) of the overlapped prefill
-    schedule after the most recent kda.prefill call that used the cached
-    workspace: the workspace's last 256 bytes hold these counters."""
-    import gated_delta_rule_33_amd as kda
-    torch = torch_mod()
-    torch.cuda.synchronize()
-    ws = list(kda._ws_cache.values())[0]
-    w = ws[-256:].view(torch.int32)[:2].cpu().numpy()
-    return int(w[0]), int(w[1])
-
-
-def assert_overlapped_ok():
-    """The call ran the overlapped schedule to the end: more than one segment
-    was published and no scan loader wave stopped waiting for a segment."""
-    last, gave_up = overlap_counters()
-    log("  overlapped schedule: last segment %d, gave up %d" % (last, gave_up))
-    assert gave_up == 0, "a scan loader wave stopped waiting for a prep segment"
-    assert last > 0
+def assert_not_recovered(report: dict):
+    """The call's overlapped schedule ran to the end without falling back to
+    its recovery launches (the two streams ran side by side)."""
+    log("  overlapped schedule recovered: %s" % report["recovered"])
+    assert report["recovered"] is False, "the state pass stopped waiting for a prep segment"

@@ -33,12 +33,12 @@ def test_status_strings_and_version():
     assert kda.status_string(0) == "KDA_OK"
     assert kda.status_string(3) == "KDA_ERR_WORKSPACE_TOO_SMALL"
     assert kda.status_string(99) == "KDA_ERR_UNKNOWN"
-    assert kda.version() >= 100
+    assert kda.version() >= 20000
 
 
 def desc(**kw):
     base = dict(num_seqs=2, total_tokens=100, num_heads=4, dk=128, dv=128, chunk=64, io_dtype=kda.KDA_BF16,
-                cu_seqlens_host=None)
+                cu_seqlens_host=None, flags=0)
     base.update(kw)
     return kda.make_desc(**base)
 
@@ -51,7 +51,7 @@ def test_workspace_size():
     assert 0 < exact <= bound
     for bad in (dict(dk=96), dict(chunk=48), dict(num_heads=0), dict(total_tokens=-1), dict(io_dtype=7),
                 dict(cu_seqlens_host=[0, 60, 99]), dict(cu_seqlens_host=[1, 60, 100]),
-                dict(cu_seqlens_host=[0, 70, 60])):
+                dict(cu_seqlens_host=[0, 70, 60]), dict(flags=2), dict(flags=1 << 31)):
         d3, k3 = desc(**bad)
         assert kda.prefill_workspace_size(d3) == 0, bad
 
@@ -121,7 +121,9 @@ def block_bytes(C: int, dk: int, es: int) -> int:
 
 def test_workspace_layout_sizes():
     """The workspace is the chunk-block array plus a small header (chunk
-    offsets, order and, for the overlapped schedule, the segment counter)."""
+    offsets, order and, for the overlapped schedule, the segment counter and
+    recovery flag) plus, for the overlapped schedule only, a carry of the
+    final states [N, H, dk, dv] fp32."""
     def ws(**kw):
         base = dict(num_seqs=1, total_tokens=131072, num_heads=32, dk=128, dv=128, chunk=64,
                     io_dtype=kda.KDA_BF16, cu_seqlens_host=[0, 131072])
@@ -129,15 +131,38 @@ def test_workspace_layout_sizes():
         d, keep = kda.make_desc(**base)
         return kda.prefill_workspace_size(d)
     assert block_bytes(64, 128, 2) == 62464
+    one = kda.KDA_PREFILL_ONE_STREAM
     cases = [
-        (dict(), 2048 * 32, block_bytes(64, 128, 2)),
-        (dict(io_dtype=kda.KDA_F32), 2048 * 32, block_bytes(64, 128, 4)),
-        (dict(chunk=32), 4096 * 32, block_bytes(32, 128, 2)),
-        (dict(dk=64, dv=64, num_heads=4), 2048 * 4, block_bytes(64, 64, 2)),
+        # (desc fields, chunk-heads, block bytes, carry bytes)
+        (dict(), 2048 * 32, block_bytes(64, 128, 2), 32 * 128 * 128 * 4),
+        (dict(flags=one), 2048 * 32, block_bytes(64, 128, 2), 0),
+        (dict(io_dtype=kda.KDA_F32), 2048 * 32, block_bytes(64, 128, 4), 32 * 128 * 128 * 4),
+        (dict(chunk=32), 4096 * 32, block_bytes(32, 128, 2), 32 * 128 * 128 * 4),
+        (dict(dk=64, dv=64, num_heads=4), 2048 * 4, block_bytes(64, 64, 2), 4 * 64 * 64 * 4),
         (dict(num_seqs=3, total_tokens=4161, cu_seqlens_host=[0, 65, 65, 4161], num_heads=2),
-         (2 + 0 + 64) * 2, block_bytes(64, 128, 2)),
+         (2 + 0 + 64) * 2, block_bytes(64, 128, 2), 0),
     ]
-    for kw, chunk_heads, blk in cases:
+    for kw, chunk_heads, blk, carry in cases:
         total = ws(**kw)
-        header = total - chunk_heads * blk
+        header = total - chunk_heads * blk - carry
         assert 0 < header < 4096, (kw, total, header)
+
+
+def test_recovered_query_and_wait_limit_without_device():
+    """kda_prefill_recovered validates its arguments and answers 0 for the
+    one-stream schedule without touching a device; the wait-limit test hook
+    returns the previous value and a negative argument restores the
+    default."""
+    lib = kda.load_library()
+    d, keep = desc(flags=kda.KDA_PREFILL_ONE_STREAM)
+    out = ctypes.c_int32(7)
+    assert lib.kda_prefill_recovered(ctypes.byref(d), None, None, None) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert lib.kda_prefill_recovered(ctypes.byref(d), FAKE, ctypes.byref(out), None) == kda.KDA_OK
+    assert out.value == 0
+    bad, keep2 = desc(dk=96)
+    assert lib.kda_prefill_recovered(ctypes.byref(bad), FAKE, ctypes.byref(out), None) == kda.KDA_ERR_UNSUPPORTED
+    default = kda.set_wait_limit(5)
+    assert default > 1000
+    assert kda.set_wait_limit(0) == 5
+    assert kda.set_wait_limit(-1) == 0
+    assert kda.set_wait_limit(-1) == default

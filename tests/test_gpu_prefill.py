@@ -6,7 +6,7 @@ import pytest
 
 import oracle
 import synth
-from tests.gpu_helpers import (TOL, assert_overlapped_ok, check, dev, gpu_prefill, have_gpu, host, log,
+from tests.gpu_helpers import (TOL, assert_not_recovered, check, dev, gpu_prefill, have_gpu, host, log,
                                 oracle_prefill)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not have_gpu(), reason="needs a GPU")]
@@ -95,27 +95,56 @@ def test_pure_decay_closed_form_on_gpu():
             check("o seq%d head%d" % (n, h), o[s:e, h], ref, 1e-4)
 
 
+GATE_CASES = [
+    # (name, per-channel log_alpha pattern); beta = 1
+    ("all-5", "all", -5.0), ("all-11", "all", -11.0), ("all-20", "all", -20.0), ("all-60", "all", -60.0),
+    ("half-8", "half", -8.0), ("half-30", "half", -30.0), ("half-60", "half", -60.0),
+    ("spikes-1000", "spikes", -1000.0), ("spikes-1e4", "spikes", -1e4),
+]
+
+
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
-@pytest.mark.parametrize("pattern", ["half", "all"])
-@pytest.mark.parametrize("la", [-5.0, -8.0])
-def test_gate_decay_at_documented_limit(dt, pattern, la):
-    """log_alpha = la on every token, on every channel or on every other
-    channel with no decay (log_alpha = 0) on the rest; beta = 1.  -8 is the
-    per-element bound of the chunked prefill (any 9 consecutive tokens sum to
-    -72 >= -80): the intra-chunk factors then span their widest range, up to
-    e^{64} on the row side and down to e^{-72} for a scale factor."""
+@pytest.mark.parametrize("case", GATE_CASES, ids=[c[0] for c in GATE_CASES])
+def test_gate_decay_extremes(dt, case):
+    """Any finite log_alpha <= 0: held constant on every channel ("all") or
+    on every other channel with no decay on the rest ("half"), or a cfg-like
+    gate with isolated huge decays (5% of the (token, channel) entries,
+    "spikes").  Strong decay puts a diagonal 16-token block's decay beyond
+    the fp32 range on the affected channels, so the prep forms those
+    channels' ratios token by token."""
+    name, pattern, la = case
     w = synth.make_prefill([200, 64, 17, 1], H=2, dk=128, dv=128, io_dtype=dt, seed=19, S0_std=0.05)
     if pattern == "half":
         w.log_alpha[:, :, 0::2] = la
         w.log_alpha[:, :, 1::2] = 0.0
-    else:
+    elif pattern == "all":
         w.log_alpha[:] = la
+    else:
+        rng = np.random.default_rng(190)
+        w.log_alpha[rng.random(w.log_alpha.shape) < 0.05] = la
     w.beta[:] = 1.0
-    log("prefill gate limit dt=%s pattern=%s la=%g" % (dt, pattern, la))
+    log("prefill gate extremes dt=%s case=%s" % (dt, name))
     o, S = gpu_prefill(w)
     o_ref, S_ref = oracle_prefill(w)
     check("o", o, o_ref, TOL[dt])
     check("S_T", S, S_ref, TOL[dt])
+
+
+def test_gate_extremes_long_overlapped():
+    """A 200-chunk-index batch (overlapped schedule) whose gates mix the
+    workload distribution with isolated decays of -200 and a block of
+    channels at -30, bf16."""
+    w = synth.make_prefill([9000, 4000], H=2, dk=128, dv=128, io_dtype="bf16", seed=31, S0_std=0.05)
+    rng = np.random.default_rng(310)
+    w.log_alpha[rng.random(w.log_alpha.shape) < 0.01] = -200.0
+    w.log_alpha[:, :, 64:80] = -30.0
+    log("prefill gate extremes, overlapped schedule")
+    rep = {}
+    o, S = gpu_prefill(w, report=rep)
+    assert_not_recovered(rep)
+    o_ref, S_ref = oracle_prefill(w)
+    check("o", o, o_ref, TOL["bf16"])
+    check("S_T", S, S_ref, TOL["bf16"])
 
 
 def test_prefill_equals_decode_steps():
@@ -172,18 +201,15 @@ def test_segmented_schedule(dt, chunk, mode):
     log("prefill segmented dt=%s chunk=%d mode=%s" % (dt, chunk, mode))
     w = synth.make_prefill(SEG_LENGTHS, H=4, dk=128, dv=128, io_dtype=dt, seed=20, S0_std=0.05, chunk=chunk)
     o_ref, S_ref = oracle_prefill(w)
+    rep = {}
     if mode == "state":
-        o, S = gpu_prefill(w)
+        o, S = gpu_prefill(w, report=rep)
     elif mode == "inplace":
-        o, S = gpu_prefill(w, in_place=True)
+        o, S = gpu_prefill(w, in_place=True, report=rep)
     else:
-        od, Sd = kda.prefill(dev(w.q, dt), dev(w.k, dt), dev(w.v, dt), dev(w.log_alpha), dev(w.beta),
-                             dev(w.cu_seqlens), dev(w.S0), chunk=chunk, cu_seqlens_host=w.cu_seqlens.tolist(),
-                             want_state=False)
-        torch.cuda.synchronize()
-        assert Sd is None
-        o, S = host(od), None
-    assert_overlapped_ok()
+        o, S = gpu_prefill(w, want_state=False, report=rep)
+        assert S is None
+    assert_not_recovered(rep)
     check("o", o, o_ref, TOL[dt])
     if S is not None:
         check("S_T", S, S_ref, TOL[dt])
@@ -195,46 +221,104 @@ def test_segmented_schedule_many_segments():
     lengths = [20000, 9000, 3, 14000]
     log("prefill segmented, 11 segments: %s x 2 heads" % lengths)
     w = synth.make_prefill(lengths, H=2, dk=128, dv=128, io_dtype="bf16", seed=23, S0_std=0.05)
-    o, S = gpu_prefill(w)
-    assert_overlapped_ok()
+    rep = {}
+    o, S = gpu_prefill(w, report=rep)
+    assert_not_recovered(rep)
     o_ref, S_ref = oracle_prefill(w)
     check("o", o, o_ref, TOL["bf16"])
     check("S_T", S, S_ref, TOL["bf16"])
 
 
 def test_one_stream_schedule_is_bitwise_equal():
-    """KDA_PREFILL_OVERLAP=0 (every prep segment, then the scan, on the
-    caller's stream; the schedule hardware-counter runs use) returns bitwise
-    the same o and S_T as the overlapped two-stream schedule.  The variable
-    is read once per process, so that side runs in a child process."""
-    import os
-    import subprocess
-    import sys
-    import tempfile
-    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    """KDA_PREFILL_ONE_STREAM (every prep segment, then the scan, on the
+    caller's stream) returns bitwise the same o and S_T as the overlapped
+    two-stream schedule."""
     lengths = [5000, 0, 3000, 777, 4096]
     log("prefill one-stream vs overlapped schedule, %s x 4 heads" % lengths)
     w = synth.make_prefill(lengths, H=4, dk=128, dv=128, io_dtype="bf16", seed=20, S0_std=0.05)
-    o_ov, S_ov = gpu_prefill(w)
-    assert_overlapped_ok()
-    with tempfile.TemporaryDirectory() as td:
-        out = os.path.join(td, "one_stream.npz")
-        child = (
-            "import sys, numpy as np\n"
-            "sys.path.insert(0, %r)\n"
-            "import synth\n"
-            "from tests.gpu_helpers import gpu_prefill\n"
-            "w = synth.make_prefill(%r, H=4, dk=128, dv=128, io_dtype='bf16', seed=20, S0_std=0.05)\n"
-            "o, S = gpu_prefill(w)\n"
-            "np.savez(%r, o=o, S=S)\n" % (root, lengths, out))
-        env = dict(os.environ, KDA_PREFILL_OVERLAP="0")
-        r = subprocess.run([sys.executable, "-c", child], env=env, cwd=root, timeout=300,
-                           capture_output=True, text=True)
-        assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
-        z = np.load(out)
-        o_one, S_one = z["o"], z["S"]
+    rep = {}
+    o_ov, S_ov = gpu_prefill(w, report=rep)
+    assert_not_recovered(rep)
+    o_one, S_one = gpu_prefill(w, one_stream=True, report=rep)
+    assert rep["recovered"] is False
     assert np.array_equal(o_one, o_ov)
     assert np.array_equal(S_one, S_ov)
+
+
+@pytest.mark.parametrize("mode", ["state", "inplace", "nostate"])
+def test_overlapped_recovery_path(mode):
+    """The overlapped schedule's fail-safe: with the state pass's wait bound
+    set to zero from the host, every loader wave gives up at its first
+    unpublished segment (all kernels still run to their end), the call's
+    guarded recovery launches recompute everything on the caller's stream,
+    kda_prefill_recovered reports it, and the results match the oracle --
+    including an in-place update, whose S0 must survive the abandoned pass."""
+    import gated_delta_rule_33_amd as kda
+    lengths = [5000, 0, 3000, 777, 4096]
+    log("prefill overlapped recovery path mode=%s" % mode)
+    w = synth.make_prefill(lengths, H=4, dk=128, dv=128, io_dtype="bf16", seed=21, S0_std=0.05)
+    o_ref, S_ref = oracle_prefill(w)
+    rep = {}
+    prev = kda.set_wait_limit(0)
+    try:
+        if mode == "state":
+            o, S = gpu_prefill(w, report=rep)
+        elif mode == "inplace":
+            o, S = gpu_prefill(w, in_place=True, report=rep)
+        else:
+            o, S = gpu_prefill(w, want_state=False, report=rep)
+    finally:
+        kda.set_wait_limit(prev)
+    log("  recovered: %s" % rep["recovered"])
+    assert rep["recovered"] is True
+    check("o", o, o_ref, TOL["bf16"])
+    if S is not None:
+        check("S_T", S, S_ref, TOL["bf16"])
+    # the next call, with the default bound, runs the overlapped schedule again
+    o2, S2 = gpu_prefill(w, report=rep)
+    assert_not_recovered(rep)
+    check("o (after)", o2, o_ref, TOL["bf16"])
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_sequence_order_permutation(dt):
+    """The same sequences packed in two different orders (so the chunk
+    offsets, the longest-first processing order and the workgroups that
+    take each (sequence, head) all change) give bitwise the same per-sequence
+    o and S_T."""
+    lengths = [300, 0, 1, 777, 64, 129, 2000, 65]
+    w = synth.make_prefill(lengths, H=3, dk=128, dv=64, io_dtype=dt, seed=24, S0_std=0.05)
+    perm = [6, 3, 0, 7, 2, 5, 1, 4]
+    log("prefill sequence-order permutation dt=%s perm=%s" % (dt, perm))
+    cu = w.cu_seqlens
+    segs = [slice(int(cu[i]), int(cu[i + 1])) for i in range(len(lengths))]
+    cat = lambda x: np.concatenate([x[segs[i]] for i in perm], axis=0)
+    wp = synth.PrefillInputs(cat(w.q), cat(w.k), cat(w.v), cat(w.log_alpha), cat(w.beta),
+                             np.concatenate([[0], np.cumsum([lengths[i] for i in perm])]).astype(np.int32),
+                             w.S0[perm].copy(), dt)
+    o, S = gpu_prefill(w)
+    op, Sp = gpu_prefill(wp)
+    cup = wp.cu_seqlens
+    for j, i in enumerate(perm):
+        assert np.array_equal(op[int(cup[j]):int(cup[j + 1])], o[segs[i]]), "sequence %d" % i
+        assert np.array_equal(Sp[j], S[i]), "state %d" % i
+
+
+def test_packed_equals_separate_calls():
+    """A packed batch equals one call per sequence (bf16, 2 heads)."""
+    lengths = [700, 3, 0, 1500]
+    w = synth.make_prefill(lengths, H=2, dk=128, dv=128, io_dtype="bf16", seed=25, S0_std=0.05)
+    log("prefill packed vs separate calls %s" % lengths)
+    o, S = gpu_prefill(w)
+    cu = w.cu_seqlens
+    for i, L in enumerate(lengths):
+        a, b = int(cu[i]), int(cu[i + 1])
+        wi = synth.PrefillInputs(w.q[a:b], w.k[a:b], w.v[a:b], w.log_alpha[a:b], w.beta[a:b],
+                                 np.array([0, L], np.int32), w.S0[i:i + 1].copy(), "bf16")
+        oi, Si = gpu_prefill(wi)
+        if L:
+            assert np.max(np.abs(oi - o[a:b])) <= 1e-5 * max(np.max(np.abs(o[a:b])), 1e-30), i
+        assert np.max(np.abs(Si[0] - S[i])) <= 1e-5 * np.max(np.abs(S[i])), i
 
 
 def _random_cases(n: int, seed: int):

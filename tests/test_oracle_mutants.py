@@ -37,7 +37,7 @@ MUTANTS = [
     ("gate_squared", "const double a = exp(lat[i]);", "const double a = exp(2.0 * lat[i]);"),
     ("readback_with_q", "r[j] += S[(size_t)i * dv + j] * kt[i];", "r[j] += S[(size_t)i * dv + j] * qt[i];"),
     ("output_with_k", "ot[j] += S[(size_t)i * dv + j] * qt[i];", "ot[j] += S[(size_t)i * dv + j] * kt[i];"),
-    ("ignore_S0", "  if (J->S0)\n    memcpy", "  if (0)\n    memcpy"),
+    ("ignore_S0", "  if (J->S0) {\n", "  if (0) {\n"),
     ("output_before_write",
      "    /* erase-then-write: add beta k (v - r)^T */\n"
      "    for (int i = 0; i < dk; ++i)\n"
