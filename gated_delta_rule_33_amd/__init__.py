@@ -29,8 +29,9 @@ KDA_F32 = 0
 KDA_BF16 = 1
 KDA_PREFILL_ONE_STREAM = 1
 
-EXPORTED = ("kda_prefill", "kda_prefill_workspace_size", "kda_prefill_recovered", "kda_prefill_set_wait_limit",
-            "kda_decode_step", "kda_status_string", "kda_version")
+EXPORTED = ("kda_prefill", "kda_prefill_workspace_size", "kda_prefill_noalloc", "kda_prefill_recovered",
+            "kda_prefill_set_wait_limit", "kda_decode_step", "kda_status_string", "kda_version")
+NOALLOC_SCRATCH_BYTES = 256 << 20  # KDA_NOALLOC_SCRATCH_BYTES
 
 
 class KdaError(RuntimeError):
@@ -77,6 +78,8 @@ def load_library(path: str = LIB_PATH):
         lib.kda_prefill.restype = ctypes.c_int
         lib.kda_prefill.argtypes = [ctypes.POINTER(PrefillDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                     ctypes.c_size_t, vp]
+        lib.kda_prefill_noalloc.restype = ctypes.c_int
+        lib.kda_prefill_noalloc.argtypes = [ctypes.POINTER(PrefillDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.kda_prefill_recovered.restype = ctypes.c_int
         lib.kda_prefill_recovered.argtypes = [ctypes.POINTER(PrefillDesc), vp, ctypes.POINTER(ctypes.c_int32), vp]
         lib.kda_prefill_set_wait_limit.restype = ctypes.c_int32
@@ -232,6 +235,45 @@ def prefill(q, k, v, log_alpha, beta, cu_seqlens, S0=None, *, chunk: int = 64, o
     del keep
     if st != KDA_OK:
         raise KdaError(st, "kda_prefill")
+    return o, S_T
+
+
+def prefill_noalloc(q, k, v, log_alpha, beta, cu_seqlens, S0=None, *, chunk: int = 64, o=None, S_T=None,
+                    cu_seqlens_host: Optional[Sequence[int]] = None, stream=None, want_state: bool = True):
+    """kda_prefill_noalloc: the prefill with the library's static per-GPU
+    scratch as its workspace (no device allocation inside the call; the
+    binding still allocates o and S_T unless they are passed in).  Same
+    arguments and results as ``prefill``; problems whose workspace exceeds
+    NOALLOC_SCRATCH_BYTES raise KdaError(KDA_ERR_WORKSPACE_TOO_SMALL)."""
+    torch = _torch()
+    lib = load_library()
+    if q.dim() != 3 or v.dim() != 3 or cu_seqlens.dim() != 1:
+        raise ValueError("q, k, v must be [T, H, d] and cu_seqlens [N+1]")
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    N = cu_seqlens.shape[0] - 1
+    dt = _dtype_code(q)
+    dev = q.device
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share a dtype")
+    if o is None:
+        o = torch.empty((T, H, dv), dtype=q.dtype, device=dev)
+    if S_T is None and want_state:
+        S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    desc, keep = make_desc(N, T, H, dk, dv, chunk, dt, cu_seqlens_host)
+    st = lib.kda_prefill_noalloc(ctypes.byref(desc),
+                                 _dev_ptr(q, "q", None, (T, H, dk), dev), _dev_ptr(k, "k", None, (T, H, dk), dev),
+                                 _dev_ptr(v, "v", None, (T, H, dv), dev),
+                                 _dev_ptr(log_alpha, "log_alpha", torch.float32, (T, H, dk), dev),
+                                 _dev_ptr(beta, "beta", torch.float32, (T, H), dev),
+                                 _dev_ptr(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,), dev),
+                                 _dev_ptr(S0, "S0", torch.float32, (N, H, dk, dv), dev),
+                                 _dev_ptr(o, "o", q.dtype, (T, H, dv), dev),
+                                 _dev_ptr(S_T, "S_T", torch.float32, (N, H, dk, dv), dev),
+                                 _stream(stream).cuda_stream)
+    del keep
+    if st != KDA_OK:
+        raise KdaError(st, "kda_prefill_noalloc")
     return o, S_T
 
 

@@ -56,6 +56,48 @@ kda_status check_desc(const kda_prefill_desc* d, int64_t* max_chunks) {
 
 }  // namespace
 
+namespace kda {
+
+kda_status prefill_checked(const kda_prefill_desc* d, const void* q, const void* k, const void* v,
+                           const float* log_alpha, const float* beta, const int32_t* cu_seqlens, const float* S0,
+                           void* o, float* S_T, void* workspace, size_t workspace_bytes, void* stream) {
+  int64_t mc = 0;
+  const kda_status s = check_desc(d, &mc);
+  if (s != KDA_OK) return s;
+  if (d->num_seqs == 0) return KDA_OK;
+  PrefillPlan p;
+  if (!make_prefill_plan(d, mc, &p)) return KDA_ERR_UNSUPPORTED;
+  if (!cu_seqlens) return KDA_ERR_INVALID_ARGUMENT;
+  const size_t T = static_cast<size_t>(d->total_tokens), H = static_cast<size_t>(d->num_heads);
+  const size_t es = io_size(d->io_dtype);
+  if (T > 0 && (!q || !k || !v || !log_alpha || !beta || !o)) return KDA_ERR_INVALID_ARGUMENT;
+  if (!workspace) return KDA_ERR_INVALID_ARGUMENT;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return KDA_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < p.total_bytes) return KDA_ERR_WORKSPACE_TOO_SMALL;
+  const size_t state_bytes = static_cast<size_t>(d->num_seqs) * H * d->dk * d->dv * 4;
+  const Range rq = range(q, T * H * d->dk * es), rk = range(k, T * H * d->dk * es),
+              rv = range(v, T * H * d->dv * es), rla = range(log_alpha, T * H * d->dk * 4),
+              rb = range(beta, T * H * 4), rcu = range(cu_seqlens, (static_cast<size_t>(d->num_seqs) + 1) * 4),
+              rs0 = range(S0, S0 ? state_bytes : 0), ro = range(o, T * H * d->dv * es),
+              rst = range(S_T, S_T ? state_bytes : 0), rws = range(workspace, p.total_bytes);
+  // outputs must not overlap anything else (S_T may equal S0 exactly)
+  const Range ins[] = {rq, rk, rv, rla, rb, rcu, rs0, rws};
+  for (const Range& x : ins)
+    if (overlap(ro, x)) return KDA_ERR_INVALID_ARGUMENT;
+  const Range ins2[] = {rq, rk, rv, rla, rb, rcu, ro, rws};
+  for (const Range& x : ins2)
+    if (overlap(rst, x)) return KDA_ERR_INVALID_ARGUMENT;
+  if (S_T && S0 && overlap(rst, rs0) && S_T != S0) return KDA_ERR_INVALID_ARGUMENT;
+  const Range ins3[] = {rq, rk, rv, rla, rb, rcu, rs0};
+  for (const Range& x : ins3)
+    if (overlap(rws, x)) return KDA_ERR_INVALID_ARGUMENT;
+  const hipError_t e = launch_prefill(p, q, k, v, log_alpha, beta, cu_seqlens, S0, o, S_T, workspace,
+                                      static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KDA_OK : KDA_ERR_DEVICE;
+}
+
+}  // namespace kda
+
 extern "C" {
 
 const char* kda_status_string(kda_status s) {
@@ -82,39 +124,7 @@ size_t kda_prefill_workspace_size(const kda_prefill_desc* d) {
 kda_status kda_prefill(const kda_prefill_desc* d, const void* q, const void* k, const void* v,
                        const float* log_alpha, const float* beta, const int32_t* cu_seqlens, const float* S0,
                        void* o, float* S_T, void* workspace, size_t workspace_bytes, void* stream) {
-  int64_t mc = 0;
-  const kda_status s = check_desc(d, &mc);
-  if (s != KDA_OK) return s;
-  if (d->num_seqs == 0) return KDA_OK;
-  kda::PrefillPlan p;
-  if (!kda::make_prefill_plan(d, mc, &p)) return KDA_ERR_UNSUPPORTED;
-  if (!cu_seqlens) return KDA_ERR_INVALID_ARGUMENT;
-  const size_t T = static_cast<size_t>(d->total_tokens), H = static_cast<size_t>(d->num_heads);
-  const size_t es = io_size(d->io_dtype);
-  if (T > 0 && (!q || !k || !v || !log_alpha || !beta || !o)) return KDA_ERR_INVALID_ARGUMENT;
-  if (!workspace) return KDA_ERR_INVALID_ARGUMENT;
-  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return KDA_ERR_INVALID_ARGUMENT;
-  if (workspace_bytes < p.total_bytes) return KDA_ERR_WORKSPACE_TOO_SMALL;
-  const size_t state_bytes = static_cast<size_t>(d->num_seqs) * H * d->dk * d->dv * 4;
-  const Range rq = range(q, T * H * d->dk * es), rk = range(k, T * H * d->dk * es),
-              rv = range(v, T * H * d->dv * es), rla = range(log_alpha, T * H * d->dk * 4),
-              rb = range(beta, T * H * 4), rcu = range(cu_seqlens, (static_cast<size_t>(d->num_seqs) + 1) * 4),
-              rs0 = range(S0, S0 ? state_bytes : 0), ro = range(o, T * H * d->dv * es),
-              rst = range(S_T, S_T ? state_bytes : 0), rws = range(workspace, p.total_bytes);
-  // outputs must not overlap anything else (S_T may equal S0 exactly)
-  const Range ins[] = {rq, rk, rv, rla, rb, rcu, rs0, rws};
-  for (const Range& x : ins)
-    if (overlap(ro, x)) return KDA_ERR_INVALID_ARGUMENT;
-  const Range ins2[] = {rq, rk, rv, rla, rb, rcu, ro, rws};
-  for (const Range& x : ins2)
-    if (overlap(rst, x)) return KDA_ERR_INVALID_ARGUMENT;
-  if (S_T && S0 && overlap(rst, rs0) && S_T != S0) return KDA_ERR_INVALID_ARGUMENT;
-  const Range ins3[] = {rq, rk, rv, rla, rb, rcu, rs0};
-  for (const Range& x : ins3)
-    if (overlap(rws, x)) return KDA_ERR_INVALID_ARGUMENT;
-  const hipError_t e = kda::launch_prefill(p, q, k, v, log_alpha, beta, cu_seqlens, S0, o, S_T, workspace,
-                                           static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? KDA_OK : KDA_ERR_DEVICE;
+  return kda::prefill_checked(d, q, k, v, log_alpha, beta, cu_seqlens, S0, o, S_T, workspace, workspace_bytes, stream);
 }
 
 kda_status kda_prefill_recovered(const kda_prefill_desc* d, const void* workspace, int32_t* recovered,

@@ -37,6 +37,12 @@ bool make_prefill_plan(const kda_prefill_desc* d, int64_t max_chunks, PrefillPla
 // default.  Returns the previous bound.
 int set_prefill_wait_polls(int polls);
 
+// kda_prefill after host validation (shared by the entry points that take
+// or provide a workspace).
+kda_status prefill_checked(const kda_prefill_desc* d, const void* q, const void* k, const void* v,
+                           const float* log_alpha, const float* beta, const int32_t* cu_seqlens, const float* S0,
+                           void* o, float* S_T, void* workspace, size_t workspace_bytes, void* stream);
+
 hipError_t launch_prefill(const PrefillPlan& p, const void* q, const void* k, const void* v, const float* la,
                           const float* beta, const int32_t* cu, const float* S0, void* o, float* S_T,
                           void* workspace, hipStream_t stream);

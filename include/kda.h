@@ -144,6 +144,28 @@ kda_status kda_prefill(const kda_prefill_desc* desc,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * kda_prefill for callers that cannot allocate device memory (code under
+ * stream capture, tight serving loops, harnesses that forbid allocation).
+ * The workspace is a static device array of KDA_NOALLOC_SCRATCH_BYTES that
+ * the library holds on every GPU it runs on until the process ends; the call
+ * allocates nothing.  It always runs the one-stream schedule (only kernel
+ * launches on `stream`).  Arguments and results as for kda_prefill.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (other streams, other threads) race on it and must not be issued.
+ * Errors: as kda_prefill, and KDA_ERR_WORKSPACE_TOO_SMALL when the problem
+ * needs more than KDA_NOALLOC_SCRATCH_BYTES, i.e. when
+ * kda_prefill_workspace_size of `desc` with KDA_PREFILL_ONE_STREAM set is
+ * larger (about 976 bytes per token and head for bf16, dk = 128, chunk 64:
+ * e.g. 8,000 tokens x 32 heads fit).
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES (256u << 20)
+kda_status kda_prefill_noalloc(const kda_prefill_desc* desc,
+                               const void* q, const void* k, const void* v,
+                               const float* log_alpha, const float* beta,
+                               const int32_t* cu_seqlens, const float* S0,
+                               void* o, float* S_T, void* stream);
+
+/*
  * After a kda_prefill call that used `workspace` for `desc` on `stream`:
  * waits for `stream` (host synchronisation) and sets *recovered to 1 if
  * that call's overlapped schedule stopped waiting for its prepared chunks
