@@ -69,17 +69,23 @@ def measured_traffic(key: str):
     return r.get("bytes_per_launch")
 
 
-def prefill_algorithmic(T_tok: int, N: int, H: int, dk: int, dv: int, es: int, C: int, with_s0: bool):
+GATE_WIDTH = {"channel": None, "scalar": 1, "none": 0}  # log_alpha floats per (token, head); None = dk
+
+
+def prefill_algorithmic(T_tok: int, N: int, H: int, dk: int, dv: int, es: int, C: int, with_s0: bool,
+                        gate: str = "channel"):
     """Compulsory bytes and algorithmic flops of one prefill call.
-    Bytes: read q, k (dk each), v (dv) in the io dtype, log_alpha (dk fp32),
-    beta (fp32); write o (dv, io dtype); write S_T (and read S0 when given).
+    Bytes: read q, k (dk each), v (dv) in the io dtype, log_alpha (dk fp32 per
+    token-head; 1 for the scalar gate, none without a gate), beta (fp32);
+    write o (dv, io dtype); write S_T (and read S0 when given).
     Flops per token-head: 2 [ (C/2)(3 dk + 2 dv) + 3 dk dv ] -- the two gated
     intra-chunk matrices, the WY factors and the three state contractions,
     triangular products counted at half.  The dense-tile count (as the
     matrix cores execute the triangular products, at full size) is
     2 [ C (3 dk + 2 dv) + 3 dk dv ]."""
     th = T_tok * H
-    per_th = (2 * dk + dv) * es + dk * 4 + 4 + dv * es
+    gw = dk if GATE_WIDTH[gate] is None else GATE_WIDTH[gate]
+    per_th = (2 * dk + dv) * es + gw * 4 + 4 + dv * es
     state = N * H * dk * dv * 4 * (2 if with_s0 else 1)
     flops_th = 2 * ((C // 2) * (3 * dk + 2 * dv) + 3 * dk * dv)
     return th * per_th + state, th * flops_th, per_th, flops_th
@@ -89,10 +95,12 @@ def prefill_dense_flops_th(dk: int, dv: int, C: int) -> int:
     return 2 * (C * (3 * dk + 2 * dv) + 3 * dk * dv)
 
 
-def decode_algorithmic(BH: int, dk: int, dv: int, es: int):
+def decode_algorithmic(BH: int, dk: int, dv: int, es: int, gate: str = "channel"):
     """Bytes per decode step: state read + write (fp32), q, k, v, o (io dtype),
-    log_alpha (fp32), beta."""
-    per = 2 * dk * dv * 4 + (2 * dk + 2 * dv) * es + dk * 4 + 4
+    log_alpha (fp32: dk per state, 1 for the scalar gate, none without a
+    gate), beta."""
+    gw = dk if GATE_WIDTH[gate] is None else GATE_WIDTH[gate]
+    per = 2 * dk * dv * 4 + (2 * dk + 2 * dv) * es + gw * 4 + 4
     return BH * per, per
 
 
@@ -209,7 +217,8 @@ def run_prefill_rate(wname, args, torch, kda, synth):
         return (t.to(tdt) if io else t).cuda()
 
     q, k, v = up(w.q, True), up(w.k, True), up(w.v, True)
-    la, b, cu = up(w.log_alpha), up(w.beta), up(w.cu_seqlens)
+    la = up(w.log_alpha) if w.log_alpha is not None else None
+    b, cu = up(w.beta), up(w.cu_seqlens)
     S0 = up(w.S0) if w.S0 is not None else None
     T_tok, H, dk = w.q.shape
     dv = w.v.shape[2]
@@ -231,12 +240,17 @@ def run_prefill_rate(wname, args, torch, kda, synth):
     e1.record(stream)
     torch.cuda.synchronize()
     call_s = e0.elapsed_time(e1) / n / 1e3
-    nbytes, _, _, _ = prefill_algorithmic(T_tok, N, H, dk, dv, 2 if bf else 4, w.chunk, S0 is not None)
+    recovered = kda.prefill_recovered(q, v, cu, chunk=w.chunk, cu_seqlens_host=host_cu, one_stream=args.one_stream)
+    nbytes, _, per_th, _ = prefill_algorithmic(T_tok, N, H, dk, dv, 2 if bf else 4, w.chunk, S0 is not None, w.gate)
     del q, k, v, la, b, o, ST, S0
     torch.cuda.empty_cache()
-    return dict(workload=wname, num_seqs=N, total_tokens=T_tok, heads=H, call_ms=round(call_s * 1e3, 4),
-                tokens_per_s=round(T_tok / call_s, 1),
-                hbm_frac=round(nbytes / call_s / 1e9 / HBM_PEAK_GBS, 4))
+    achieved = nbytes / call_s / 1e9
+    return dict(workload=wname, gate=w.gate, num_seqs=N, total_tokens=T_tok, heads=H,
+                call_ms=round(call_s * 1e3, 4), tokens_per_s=round(T_tok / call_s, 1),
+                hbm_frac=round(achieved / HBM_PEAK_GBS, 4), recovered=recovered,
+                roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                              frac=round(achieved / HBM_PEAK_GBS, 4), bytes_per_launch=int(nbytes),
+                              bytes_per_token_head=per_th))
 
 
 def decode_cpu_baseline(args, synth, oracle, B, H, dk, dv, std, seed):
@@ -264,9 +278,10 @@ def decode_cpu_baseline(args, synth, oracle, B, H, dk, dv, std, seed):
     return res
 
 
-def run_decode(args, torch, kda, synth, oracle=None):
+def run_decode(args, torch, kda, synth, oracle=None, gate="channel", steps=None):
     wd = synth.WORKLOADS["decode256x32_bf16"]
-    B, H, dk, dv, steps = wd["B"], wd["H"], wd["dk"], wd["dv"], args.decode_steps
+    B, H, dk, dv = wd["B"], wd["H"], wd["dk"], wd["dv"]
+    steps = steps or args.decode_steps
     seed = 1000 + wd["index"]
     t0 = time.time()
     S_host = synth.make_decode_state(B, H, dk, dv, wd["S0_std"], seed)
@@ -277,13 +292,13 @@ def run_decode(args, torch, kda, synth, oracle=None):
     blk = 64
     with concurrent.futures.ThreadPoolExecutor(max(1, min(16, os.cpu_count() or 1))) as ex:
         for s0 in range(0, steps, blk):
-            xs = list(ex.map(lambda t: synth.make_decode_step(B, H, dk, dv, "bf16", seed, t),
+            xs = list(ex.map(lambda t: synth.make_decode_step(B, H, dk, dv, "bf16", seed, t, gate=gate),
                              range(s0, min(steps, s0 + blk))))
             for x in xs:
                 qs.append(torch.from_numpy(x.q).to(torch.bfloat16).cuda())
                 ks.append(torch.from_numpy(x.k).to(torch.bfloat16).cuda())
                 vs.append(torch.from_numpy(x.v).to(torch.bfloat16).cuda())
-                las.append(torch.from_numpy(x.log_alpha).cuda())
+                las.append(torch.from_numpy(x.log_alpha).cuda() if x.log_alpha is not None else None)
                 bs.append(torch.from_numpy(x.beta).cuda())
     log("generated decode inputs (%d steps) in %.1fs" % (steps, time.time() - t0))
     S = S0.clone()
@@ -302,10 +317,10 @@ def run_decode(args, torch, kda, synth, oracle=None):
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     step_s = e0.elapsed_time(e1) / 1e3 / steps
-    nbytes, per = decode_algorithmic(B * H, dk, dv, 2)
+    nbytes, per = decode_algorithmic(B * H, dk, dv, 2, gate)
     achieved = nbytes / step_s / 1e9
     res = dict(
-        metric="decode state-updates/s", value=round(B * H * steps / wall, 1), unit="state-updates/s",
+        metric="decode state-updates/s", gate=gate, value=round(B * H * steps / wall, 1), unit="state-updates/s",
         us_per_step=round(step_s * 1e6, 2),
         event_updates_per_s=round(B * H / step_s, 1),
         roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
@@ -316,7 +331,7 @@ def run_decode(args, torch, kda, synth, oracle=None):
     )
     del qs, ks, vs, las, bs, S, S0
     torch.cuda.empty_cache()
-    if oracle is not None and not args.no_cpu_baseline:
+    if oracle is not None and not args.no_cpu_baseline and gate == "channel":
         log("cpu baseline: decode oracle ...")
         res["cpu_baseline"] = decode_cpu_baseline(args, synth, oracle, B, H, dk, dv, wd["S0_std"], seed)
     return res
@@ -369,7 +384,10 @@ def main():
     pre = run_prefill(args, torch, kda, synth, oracle)
     dec = None if args.no_decode else run_decode(args, torch, kda, synth, oracle)
     other = [] if args.no_other else [run_prefill_rate(n, args, torch, kda, synth)
-                                      for n in ("batch4x4096_bf16", "varlen64_bf16")]
+                                      for n in ("batch4x4096_bf16", "varlen64_bf16", "long131072_bf16_gdn",
+                                                "long131072_bf16_deltanet")]
+    dec_gates = [] if (args.no_decode or args.no_other) else [
+        run_decode(args, torch, kda, synth, None, gate=g, steps=min(256, args.decode_steps)) for g in ("scalar", "none")]
     wl = pre["workload"]
     line = {
         "metric": "KDA prefill tokens/s (MFMA % peak) at T=128k; decode state-updates/s (HBM %)",
@@ -398,8 +416,10 @@ def main():
         line["decode"] = dec
     if other:
         line["prefill_other"] = other
+    if dec_gates:
+        line["decode_gate_forms"] = dec_gates
     print(json.dumps(line), flush=True)
-    if pre["recovered"]:
+    if pre["recovered"] or any(x.get("recovered") for x in other):
         log("the overlapped prefill schedule fell back to its recovery launches: timing invalid")
         sys.exit(3)
     if "parity" in pre and not pre["parity"]["pass"]:

@@ -28,6 +28,9 @@ KDA_ERR_DEVICE = 4
 KDA_F32 = 0
 KDA_BF16 = 1
 KDA_PREFILL_ONE_STREAM = 1
+KDA_GATE_CHANNEL = 0
+KDA_GATE_SCALAR = 1
+KDA_GATE_NONE = 2
 
 EXPORTED = ("kda_prefill", "kda_prefill_workspace_size", "kda_prefill_noalloc", "kda_prefill_recovered",
             "kda_prefill_set_wait_limit", "kda_decode_step", "kda_status_string", "kda_version")
@@ -51,6 +54,7 @@ class PrefillDesc(ctypes.Structure):
         ("io_dtype", ctypes.c_int),
         ("cu_seqlens_host", ctypes.POINTER(ctypes.c_int32)),
         ("flags", ctypes.c_uint32),
+        ("gate", ctypes.c_int),
     ]
 
 
@@ -86,7 +90,7 @@ def load_library(path: str = LIB_PATH):
         lib.kda_prefill_set_wait_limit.argtypes = [ctypes.c_int32]
         lib.kda_decode_step.restype = ctypes.c_int
         lib.kda_decode_step.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int,
-                                        vp, vp, vp, vp, vp, vp, vp, vp]
+                                        ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp]
         if path == LIB_PATH:
             _lib = lib
         return lib
@@ -101,7 +105,7 @@ def version() -> int:
 
 
 def make_desc(num_seqs: int, total_tokens: int, num_heads: int, dk: int, dv: int, chunk: int, io_dtype: int,
-              cu_seqlens_host: Optional[Sequence[int]] = None, flags: int = 0):
+              cu_seqlens_host: Optional[Sequence[int]] = None, flags: int = 0, gate: int = 0):
     """Build a kda_prefill_desc.  Returns (desc, keepalive) -- keep the second
     value alive while the desc is used (it owns the host offsets)."""
     keep = None
@@ -110,7 +114,7 @@ def make_desc(num_seqs: int, total_tokens: int, num_heads: int, dk: int, dv: int
         keep = (ctypes.c_int32 * len(cu_seqlens_host))(*[int(x) for x in cu_seqlens_host])
         ptr = ctypes.cast(keep, ctypes.POINTER(ctypes.c_int32))
     d = PrefillDesc(int(num_seqs), int(total_tokens), int(num_heads), int(dk), int(dv), int(chunk), int(io_dtype),
-                    ptr, int(flags))
+                    ptr, int(flags), int(gate))
     return d, keep
 
 
@@ -151,6 +155,20 @@ def _dev_ptr(t, name: str, dtype=None, shape=None, device=None) -> int:
     if device is not None and t.device != device:
         raise ValueError("%s must be on %s, got %s" % (name, device, t.device))
     return t.data_ptr()
+
+
+def _gate(log_alpha, lead) -> int:
+    """Gate form from log_alpha: None -> no gate; [*lead] -> one rate per
+    head; [*lead, dk] -> one rate per key channel."""
+    if log_alpha is None:
+        return KDA_GATE_NONE
+    if log_alpha.dim() == len(lead):
+        return KDA_GATE_SCALAR
+    return KDA_GATE_CHANNEL
+
+
+def _la_shape(gate: int, lead, dk: int):
+    return None if gate == KDA_GATE_NONE else (tuple(lead) if gate == KDA_GATE_SCALAR else tuple(lead) + (dk,))
 
 
 def _stream(stream):
@@ -196,6 +214,8 @@ def prefill(q, k, v, log_alpha, beta, cu_seqlens, S0=None, *, chunk: int = 64, o
     None.  Returns (o, S_T); S_T is None when ``want_state`` is False.
     ``S_T`` may be passed as ``S0`` to update the state in place.
     ``one_stream`` selects the schedule that never leaves the caller's stream.
+    ``log_alpha`` may also be [T, H] (one rate per head: Gated DeltaNet) or
+    None (no forget gate: DeltaNet).
     """
     torch = _torch()
     lib = load_library()
@@ -213,15 +233,16 @@ def prefill(q, k, v, log_alpha, beta, cu_seqlens, S0=None, *, chunk: int = 64, o
     if S_T is None and want_state:
         S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
     s = _stream(stream)
+    gate = _gate(log_alpha, (T, H))
     desc, keep = make_desc(N, T, H, dk, dv, chunk, dt, cu_seqlens_host,
-                           KDA_PREFILL_ONE_STREAM if one_stream else 0)
+                           KDA_PREFILL_ONE_STREAM if one_stream else 0, gate)
     need = int(lib.kda_prefill_workspace_size(ctypes.byref(desc)))
     if need == 0:
         st = lib.kda_prefill(ctypes.byref(desc), *([None] * 10), 0, None)
         raise KdaError(st if st != KDA_OK else KDA_ERR_INVALID_ARGUMENT, "kda_prefill_workspace_size")
     ptrs = (_dev_ptr(q, "q", None, (T, H, dk), dev), _dev_ptr(k, "k", None, (T, H, dk), dev),
             _dev_ptr(v, "v", None, (T, H, dv), dev),
-            _dev_ptr(log_alpha, "log_alpha", torch.float32, (T, H, dk), dev),
+            _dev_ptr(log_alpha, "log_alpha", torch.float32, _la_shape(gate, (T, H), dk), dev),
             _dev_ptr(beta, "beta", torch.float32, (T, H), dev),
             _dev_ptr(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,), dev),
             _dev_ptr(S0, "S0", torch.float32, (N, H, dk, dv), dev),
@@ -260,11 +281,12 @@ def prefill_noalloc(q, k, v, log_alpha, beta, cu_seqlens, S0=None, *, chunk: int
         o = torch.empty((T, H, dv), dtype=q.dtype, device=dev)
     if S_T is None and want_state:
         S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
-    desc, keep = make_desc(N, T, H, dk, dv, chunk, dt, cu_seqlens_host)
+    gate = _gate(log_alpha, (T, H))
+    desc, keep = make_desc(N, T, H, dk, dv, chunk, dt, cu_seqlens_host, 0, gate)
     st = lib.kda_prefill_noalloc(ctypes.byref(desc),
                                  _dev_ptr(q, "q", None, (T, H, dk), dev), _dev_ptr(k, "k", None, (T, H, dk), dev),
                                  _dev_ptr(v, "v", None, (T, H, dv), dev),
-                                 _dev_ptr(log_alpha, "log_alpha", torch.float32, (T, H, dk), dev),
+                                 _dev_ptr(log_alpha, "log_alpha", torch.float32, _la_shape(gate, (T, H), dk), dev),
                                  _dev_ptr(beta, "beta", torch.float32, (T, H), dev),
                                  _dev_ptr(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,), dev),
                                  _dev_ptr(S0, "S0", torch.float32, (N, H, dk, dv), dev),
@@ -310,8 +332,9 @@ def set_wait_limit(polls: int) -> int:
 
 def decode_step(q, k, v, log_alpha, beta, S, *, o=None, stream=None):
     """One KDA step for B requests: q, k [B, H, dk]; v [B, H, dv]; log_alpha
-    [B, H, dk] fp32; beta [B, H] fp32; S [B, H, dk, dv] fp32 updated in place.
-    Returns o [B, H, dv]."""
+    [B, H, dk] fp32 ([B, H] for one rate per head, None without a gate);
+    beta [B, H] fp32; S [B, H, dk, dv] fp32 updated in place.  Returns o
+    [B, H, dv]."""
     torch = _torch()
     lib = load_library()
     if q.dim() != 3 or v.dim() != 3:
@@ -324,9 +347,10 @@ def decode_step(q, k, v, log_alpha, beta, S, *, o=None, stream=None):
         raise TypeError("q, k and v must share a dtype")
     if o is None:
         o = torch.empty((B, H, dv), dtype=q.dtype, device=dev)
-    st = lib.kda_decode_step(B, H, dk, dv, dt, _dev_ptr(q, "q", None, (B, H, dk), dev),
+    gate = _gate(log_alpha, (B, H))
+    st = lib.kda_decode_step(B, H, dk, dv, dt, gate, _dev_ptr(q, "q", None, (B, H, dk), dev),
                              _dev_ptr(k, "k", None, (B, H, dk), dev), _dev_ptr(v, "v", None, (B, H, dv), dev),
-                             _dev_ptr(log_alpha, "log_alpha", torch.float32, (B, H, dk), dev),
+                             _dev_ptr(log_alpha, "log_alpha", torch.float32, _la_shape(gate, (B, H), dk), dev),
                              _dev_ptr(beta, "beta", torch.float32, (B, H), dev),
                              _dev_ptr(S, "S", torch.float32, (B, H, dk, dv), dev),
                              _dev_ptr(o, "o", q.dtype, (B, H, dv), dev), _stream(stream).cuda_stream)

@@ -12,6 +12,9 @@ namespace {
 
 bool dims_supported(int32_t dk, int32_t dv) { return (dk == 64 || dk == 128) && (dv == 64 || dv == 128); }
 bool dtype_valid(kda_dtype dt) { return dt == KDA_F32 || dt == KDA_BF16; }
+bool gate_valid(kda_gate g) { return g == KDA_GATE_CHANNEL || g == KDA_GATE_SCALAR || g == KDA_GATE_NONE; }
+// log_alpha elements per (token, head)
+size_t gate_width(kda_gate g, int32_t dk) { return g == KDA_GATE_CHANNEL ? dk : (g == KDA_GATE_SCALAR ? 1 : 0); }
 size_t io_size(kda_dtype dt) { return dt == KDA_BF16 ? 2 : 4; }
 
 struct Range {
@@ -27,7 +30,7 @@ bool overlap(Range x, Range y) { return x.b != x.e && y.b != y.e && x.b < y.e &&
 kda_status check_desc(const kda_prefill_desc* d, int64_t* max_chunks) {
   if (!d) return KDA_ERR_INVALID_ARGUMENT;
   if (d->num_seqs < 0 || d->total_tokens < 0 || d->num_heads < 1) return KDA_ERR_INVALID_ARGUMENT;
-  if (!dtype_valid(d->io_dtype)) return KDA_ERR_INVALID_ARGUMENT;
+  if (!dtype_valid(d->io_dtype) || !gate_valid(d->gate)) return KDA_ERR_INVALID_ARGUMENT;
   if (!dims_supported(d->dk, d->dv)) return KDA_ERR_UNSUPPORTED;
   if (d->chunk != 32 && d->chunk != 64) return KDA_ERR_UNSUPPORTED;
   if (d->num_seqs == 0 && d->total_tokens != 0) return KDA_ERR_INVALID_ARGUMENT;
@@ -70,13 +73,15 @@ kda_status prefill_checked(const kda_prefill_desc* d, const void* q, const void*
   if (!cu_seqlens) return KDA_ERR_INVALID_ARGUMENT;
   const size_t T = static_cast<size_t>(d->total_tokens), H = static_cast<size_t>(d->num_heads);
   const size_t es = io_size(d->io_dtype);
-  if (T > 0 && (!q || !k || !v || !log_alpha || !beta || !o)) return KDA_ERR_INVALID_ARGUMENT;
+  const size_t gw = gate_width(d->gate, d->dk);
+  if (gw == 0) log_alpha = nullptr;
+  if (T > 0 && (!q || !k || !v || (gw && !log_alpha) || !beta || !o)) return KDA_ERR_INVALID_ARGUMENT;
   if (!workspace) return KDA_ERR_INVALID_ARGUMENT;
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return KDA_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < p.total_bytes) return KDA_ERR_WORKSPACE_TOO_SMALL;
   const size_t state_bytes = static_cast<size_t>(d->num_seqs) * H * d->dk * d->dv * 4;
   const Range rq = range(q, T * H * d->dk * es), rk = range(k, T * H * d->dk * es),
-              rv = range(v, T * H * d->dv * es), rla = range(log_alpha, T * H * d->dk * 4),
+              rv = range(v, T * H * d->dv * es), rla = range(log_alpha, log_alpha ? T * H * gw * 4 : 0),
               rb = range(beta, T * H * 4), rcu = range(cu_seqlens, (static_cast<size_t>(d->num_seqs) + 1) * 4),
               rs0 = range(S0, S0 ? state_bytes : 0), ro = range(o, T * H * d->dv * es),
               rst = range(S_T, S_T ? state_bytes : 0), rws = range(workspace, p.total_bytes);
@@ -150,24 +155,26 @@ kda_status kda_prefill_recovered(const kda_prefill_desc* d, const void* workspac
 
 int32_t kda_prefill_set_wait_limit(int32_t polls) { return kda::set_prefill_wait_polls(polls); }
 
-kda_status kda_decode_step(int32_t B, int32_t H, int32_t dk, int32_t dv, kda_dtype io_dtype, const void* q,
-                           const void* k, const void* v, const float* log_alpha, const float* beta, float* S,
-                           void* o, void* stream) {
-  if (B < 0 || H < 1 || !dtype_valid(io_dtype)) return KDA_ERR_INVALID_ARGUMENT;
+kda_status kda_decode_step(int32_t B, int32_t H, int32_t dk, int32_t dv, kda_dtype io_dtype, kda_gate gate,
+                           const void* q, const void* k, const void* v, const float* log_alpha, const float* beta,
+                           float* S, void* o, void* stream) {
+  if (B < 0 || H < 1 || !dtype_valid(io_dtype) || !gate_valid(gate)) return KDA_ERR_INVALID_ARGUMENT;
   if (!dims_supported(dk, dv)) return KDA_ERR_UNSUPPORTED;
   if (B == 0) return KDA_OK;
-  if (!q || !k || !v || !log_alpha || !beta || !S || !o) return KDA_ERR_INVALID_ARGUMENT;
+  const size_t gw = gate_width(gate, dk);
+  if (gw == 0) log_alpha = nullptr;
+  if (!q || !k || !v || (gw && !log_alpha) || !beta || !S || !o) return KDA_ERR_INVALID_ARGUMENT;
   const int64_t BH = static_cast<int64_t>(B) * H;
   if (BH > 0x7fffffff) return KDA_ERR_UNSUPPORTED;
   const size_t es = io_size(io_dtype), n = static_cast<size_t>(BH);
   const Range rs = range(S, n * dk * dv * 4), ro = range(o, n * dv * es);
   const Range others[] = {range(q, n * dk * es), range(k, n * dk * es), range(v, n * dv * es),
-                          range(log_alpha, n * dk * 4), range(beta, n * 4)};
+                          range(log_alpha, log_alpha ? n * gw * 4 : 0), range(beta, n * 4)};
   for (const Range& x : others)
     if (overlap(rs, x) || overlap(ro, x)) return KDA_ERR_INVALID_ARGUMENT;
   if (overlap(rs, ro)) return KDA_ERR_INVALID_ARGUMENT;
-  const hipError_t e = kda::launch_decode(io_dtype, dk, dv, static_cast<int>(BH), q, k, v, log_alpha, beta, S, o,
-                                          static_cast<hipStream_t>(stream));
+  const hipError_t e = kda::launch_decode(io_dtype, gate, dk, dv, static_cast<int>(BH), q, k, v, log_alpha, beta, S,
+                                          o, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KDA_OK : KDA_ERR_DEVICE;
 }
 

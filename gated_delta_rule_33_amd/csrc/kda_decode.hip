@@ -25,6 +25,10 @@
 // workgroup per state ran 13% slower, 32-column slices (128-byte pieces)
 // 7% slower, 16-column slices twice as slow.  The kernel is HBM-bound:
 // 2 * 4 * dk * dv bytes of state per update against ~4 * dk * dv flops.
+//
+// Gate forms (template G): one rate per key row (KDA), one rate for the
+// whole state (Gated DeltaNet: one 4-byte load and one exponential), or none
+// (DeltaNet: the decay is skipped).
 
 #include "kda_device.h"
 #include "kda_internal.h"
@@ -47,7 +51,7 @@ struct alignas(sizeof(T) * kNR) RowPack {
   T x[kNR];
 };
 
-template <typename T, int DK, int DV>
+template <typename T, int DK, int DV, int G>
 __global__ __launch_bounds__(DK / kNR * DecodeShape<DV>::LPR) void decode_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                               const T* __restrict__ v, const float* __restrict__ la,
                                                               const float* __restrict__ beta, float* __restrict__ S,
@@ -68,14 +72,22 @@ __global__ __launch_bounds__(DK / kNR * DecodeShape<DV>::LPR) void decode_kernel
   float* Sb = S + static_cast<size_t>(bh) * DK * DV;
   const T* qb = q + static_cast<size_t>(bh) * DK;
   const T* kb = k + static_cast<size_t>(bh) * DK;
-  const float* lab = la + static_cast<size_t>(bh) * DK;
 
   f32x4 s[kNR];
 #pragma unroll
   for (int i = 0; i < kNR; ++i)
     s[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Sb + (row0 + i) * DV + col));
 
-  const RowPack<float> lr = *reinterpret_cast<const RowPack<float>*>(lab + row0);
+  float alpha[kNR];
+  if constexpr (G == KDA_GATE_CHANNEL) {
+    const RowPack<float> lr = *reinterpret_cast<const RowPack<float>*>(la + static_cast<size_t>(bh) * DK + row0);
+#pragma unroll
+    for (int i = 0; i < kNR; ++i) alpha[i] = __expf(lr.x[i]);
+  } else if constexpr (G == KDA_GATE_SCALAR) {
+    const float a = __expf(la[bh]);
+#pragma unroll
+    for (int i = 0; i < kNR; ++i) alpha[i] = a;
+  }
   const RowPack<T> kp = *reinterpret_cast<const RowPack<T>*>(kb + row0);
   const RowPack<T> qp = *reinterpret_cast<const RowPack<T>*>(qb + row0);
   float kr[kNR];
@@ -84,10 +96,9 @@ __global__ __launch_bounds__(DK / kNR * DecodeShape<DV>::LPR) void decode_kernel
   float kq = 0.f;
 #pragma unroll
   for (int i = 0; i < kNR; ++i) {
-    const float a = __expf(lr.x[i]);
     const float kk = io<T>::load(&kp.x[i]);
     const float qq = io<T>::load(&qp.x[i]);
-    s[i] *= a;
+    if constexpr (G != KDA_GATE_NONE) s[i] *= alpha[i];
     r += kk * s[i];
     sq += qq * s[i];
     kq += kk * qq;
@@ -128,31 +139,39 @@ __global__ __launch_bounds__(DK / kNR * DecodeShape<DV>::LPR) void decode_kernel
   if (threadIdx.x < DS::LPR) store4(o + static_cast<size_t>(bh) * DV + col, sq + d * kq);
 }
 
-template <typename T, int DK, int DV>
+template <typename T, int DK, int DV, int G>
 static hipError_t launch_decode_t(int BH, const void* q, const void* k, const void* v, const float* la,
                                   const float* beta, float* S, void* o, hipStream_t st) {
-  hipLaunchKernelGGL((decode_kernel<T, DK, DV>), dim3(BH * (DV / DecodeShape<DV>::CW)),
+  hipLaunchKernelGGL((decode_kernel<T, DK, DV, G>), dim3(BH * (DV / DecodeShape<DV>::CW)),
                      dim3(DK / kNR * DecodeShape<DV>::LPR), 0, st,
                      static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), la, beta, S,
                      static_cast<T*>(o));
   return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, int G>
 static hipError_t launch_decode_dt(int dk, int dv, int BH, const void* q, const void* k, const void* v,
                                    const float* la, const float* beta, float* S, void* o, hipStream_t st) {
-  if (dk == 128 && dv == 128) return launch_decode_t<T, 128, 128>(BH, q, k, v, la, beta, S, o, st);
-  if (dk == 128 && dv == 64) return launch_decode_t<T, 128, 64>(BH, q, k, v, la, beta, S, o, st);
-  if (dk == 64 && dv == 128) return launch_decode_t<T, 64, 128>(BH, q, k, v, la, beta, S, o, st);
-  if (dk == 64 && dv == 64) return launch_decode_t<T, 64, 64>(BH, q, k, v, la, beta, S, o, st);
+  if (dk == 128 && dv == 128) return launch_decode_t<T, 128, 128, G>(BH, q, k, v, la, beta, S, o, st);
+  if (dk == 128 && dv == 64) return launch_decode_t<T, 128, 64, G>(BH, q, k, v, la, beta, S, o, st);
+  if (dk == 64 && dv == 128) return launch_decode_t<T, 64, 128, G>(BH, q, k, v, la, beta, S, o, st);
+  if (dk == 64 && dv == 64) return launch_decode_t<T, 64, 64, G>(BH, q, k, v, la, beta, S, o, st);
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_decode(kda_dtype dt, int dk, int dv, int BH, const void* q, const void* k, const void* v,
-                         const float* la, const float* beta, float* S, void* o, hipStream_t stream) {
+template <typename T>
+static hipError_t launch_decode_gate(kda_gate g, int dk, int dv, int BH, const void* q, const void* k, const void* v,
+                                     const float* la, const float* beta, float* S, void* o, hipStream_t st) {
+  if (g == KDA_GATE_CHANNEL) return launch_decode_dt<T, KDA_GATE_CHANNEL>(dk, dv, BH, q, k, v, la, beta, S, o, st);
+  if (g == KDA_GATE_SCALAR) return launch_decode_dt<T, KDA_GATE_SCALAR>(dk, dv, BH, q, k, v, la, beta, S, o, st);
+  return launch_decode_dt<T, KDA_GATE_NONE>(dk, dv, BH, q, k, v, la, beta, S, o, st);
+}
+
+hipError_t launch_decode(kda_dtype dt, kda_gate gate, int dk, int dv, int BH, const void* q, const void* k,
+                         const void* v, const float* la, const float* beta, float* S, void* o, hipStream_t stream) {
   if (BH == 0) return hipSuccess;
-  if (dt == KDA_BF16) return launch_decode_dt<bf16_t>(dk, dv, BH, q, k, v, la, beta, S, o, stream);
-  return launch_decode_dt<float>(dk, dv, BH, q, k, v, la, beta, S, o, stream);
+  if (dt == KDA_BF16) return launch_decode_gate<bf16_t>(gate, dk, dv, BH, q, k, v, la, beta, S, o, stream);
+  return launch_decode_gate<float>(gate, dk, dv, BH, q, k, v, la, beta, S, o, stream);
 }
 
 }  // namespace kda

@@ -10,13 +10,14 @@
 namespace kda {
 
 // Decode: one recurrence step for B*H states (all pointers device).
-hipError_t launch_decode(kda_dtype dt, int dk, int dv, int BH, const void* q, const void* k, const void* v,
+hipError_t launch_decode(kda_dtype dt, kda_gate gate, int dk, int dv, int BH, const void* q, const void* k, const void* v,
                          const float* la, const float* beta, float* S, void* o, hipStream_t stream);
 
 // Prefill workspace carve-up, computed on the host.
 struct PrefillPlan {
   int N, T, H, dk, dv, C;
   kda_dtype dt;
+  kda_gate gate;
   int64_t max_chunks;  // upper bound (exact when the host offsets are known)
   int sort;            // 1: longest-first order is computed on the device
   // byte offsets inside the workspace

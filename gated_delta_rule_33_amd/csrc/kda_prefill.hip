@@ -434,7 +434,11 @@ struct PrepLds {
   // region 3: block-pair vectors f[NLB][DK] (f32)
   static constexpr size_t r3 = a16(static_cast<size_t>(NLB) * DK * 4);
   static constexpr size_t o0 = 0, o1 = r0, o2 = o1 + r1, o3 = o2 + r2, o4 = o3 + r3;
-  static constexpr size_t total = o4 + static_cast<size_t>(C) * 4;  // + beta
+  // after beta: per-row and per-block gate sums of the scalar gate (not
+  // reused by later phases: the pair products read them while region 2
+  // already stages P)
+  static constexpr size_t o5 = o4 + static_cast<size_t>(C) * 4;
+  static constexpr size_t total = o5 + static_cast<size_t>(3 * C + NB) * 4;
 };
 
 // byte offset of element (row, c) in an unpadded LDS tile with RB-byte rows,
@@ -515,7 +519,12 @@ constexpr int prep_waves_per_eu() {
   return wgs * kPrepThreads / 256 < 4 ? wgs * kPrepThreads / 256 : 4;
 }
 
-template <typename T, int C, int DK>
+// G is the gate form (kda_gate): per key channel, one per head, or none.
+// With one rate per head every gate factor is a per-row scalar, the gated
+// products are the plain k k^T and q k^T products scaled element by element
+// by e^{g_r - g_s} (formed from sums over the rows in between), and without
+// a gate all factors are 1.
+template <typename T, int C, int DK, int G>
 __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(prep_waves_per_eu<T, C, DK>())))
 void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                    const float* __restrict__ la, const float* __restrict__ beta,
@@ -547,6 +556,12 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
   T* Ps = reinterpret_cast<T*>(smem + L::o2);
   float* fv = reinterpret_cast<float*>(smem + L::o3);
   float* bet = reinterpret_cast<float*>(smem + L::o4);
+  // scalar gate: per row, its log_alpha (base 2), d and s (see a2); per block D
+  float* lrow = reinterpret_cast<float*>(smem + L::o5);
+  float* drow = lrow + C;
+  float* srow = drow + C;
+  float* dsum = srow + C;
+  constexpr bool kChannel = G == KDA_GATE_CHANNEL, kScalar = G == KDA_GATE_SCALAR;
 
   // thread owns channels c4..c4+3 of rows r0..r0+RPT-1 in the elementwise steps
   constexpr int NCG = DK / 4;  // channel groups of 4
@@ -592,7 +607,14 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int e = min(fr0 + i, it.len - 1) * H * DK + fc4;  // < C H DK: 32-bit
-      if (gates) r.lg[i] = *reinterpret_cast<const f32x4*>(la + tbase + e);
+      if constexpr (kChannel) {
+        if (gates) r.lg[i] = *reinterpret_cast<const f32x4*>(la + tbase + e);
+      } else if constexpr (kScalar) {
+        if (gates) {
+          const float x = la[(static_cast<size_t>(it.t0) + min(fr0 + i, it.len - 1)) * H + it.h];
+          r.lg[i] = f32x4{x, x, x, x};
+        }
+      }
       if (qk) {
         r.kr[i] = load4raw(k + tbase + e);
         r.qr[i] = load4raw(q + tbase + e);
@@ -623,7 +645,8 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
   f32x4 lg[RPT], kv[RPT], qv[RPT];
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
-    lg[i] = r0 + i < len ? cur.lg[i] * kLog2e : f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (G == KDA_GATE_NONE) lg[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    else lg[i] = r0 + i < len ? cur.lg[i] * kLog2e : f32x4{0.f, 0.f, 0.f, 0.f};
     kv[i] = cvt4(cur.kr[i]);
     qv[i] = cvt4(cur.qr[i]);
   }
@@ -664,13 +687,24 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
       run += lg[i];
     }
     if (pos == 0) *reinterpret_cast<f32x4*>(Dblk + I * DK + c4) = whole;
+    if constexpr (kScalar) {
+      if (cg == 0) {
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+          lrow[r0 + i] = lg[i][0];
+          drow[r0 + i] = dl[i][0];
+          srow[r0 + i] = sl[i][0];
+        }
+        if (pos == 0) dsum[I] = whole[0];
+      }
+    }
   }
   __syncthreads();
 
   // ---- block-pair vectors: for J < I, e^{D_{J+1} + ... + D_{I-1}} (<= 1);
   // for the diagonal pair (J, J), e^{-D_J} (>= 1), or 0 where it would
   // exceed 2^86 (that channel's diagonal products are formed pair by pair)
-  for (int idx = tid; idx < L::NLB * DK; idx += kPrepThreads) {
+  for (int idx = tid; kChannel && idx < L::NLB * DK; idx += kPrepThreads) {
     const unsigned pp = static_cast<unsigned>(idx) / DK, ch = static_cast<unsigned>(idx) % DK;
     unsigned bI = 0;
 #pragma unroll
@@ -690,7 +724,7 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
     float x = 0.f;
 #pragma unroll
     for (int kk = 0; kk < NB; ++kk) x += Dblk[kk * DK + tid];
-    reinterpret_cast<float*>(blk + B::oG)[tid] = __builtin_amdgcn_exp2f(x);  // Gamma = e^{g_last}
+    reinterpret_cast<float*>(blk + B::oG)[tid] = G == KDA_GATE_NONE ? 1.f : __builtin_amdgcn_exp2f(x);  // e^{g_last}
   }
   if (tid < C) reinterpret_cast<float*>(blk + B::oB)[tid] = bet[tid];
 
@@ -714,26 +748,51 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
     float bt[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) bt[i] = bet[r0 + i];
+    if constexpr (kChannel) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      ebv[j] = __builtin_amdgcn_exp2f(sb[j]);  // <= 1
-      eav[j] = __builtin_amdgcn_exp2f(sa[j]);  // <= 1
+      for (int j = 0; j < 4; ++j) {
+        ebv[j] = __builtin_amdgcn_exp2f(sb[j]);  // <= 1
+        eav[j] = __builtin_amdgcn_exp2f(sa[j]);  // <= 1
+      }
+    } else if constexpr (kScalar) {
+      const float eb = __builtin_amdgcn_exp2f(sb[0]), ea = __builtin_amdgcn_exp2f(sa[0]);
+      ebv = f32x4{eb, eb, eb, eb};
+      eav = f32x4{ea, ea, ea, ea};
+    } else {
+      ebv = f32x4{1.f, 1.f, 1.f, 1.f};
+      eav = ebv;
     }
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const unsigned r = static_cast<unsigned>(r0 + i);
       f32x4 ed, es;
+      if constexpr (kChannel) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        ed[j] = __builtin_amdgcn_exp2f(dl[i][j]);  // e^{d_r} <= 1
-        es[j] = __builtin_amdgcn_exp2f(sl[i][j]);  // e^{s_r} <= 1
+        for (int j = 0; j < 4; ++j) {
+          ed[j] = __builtin_amdgcn_exp2f(dl[i][j]);  // e^{d_r} <= 1
+          es[j] = __builtin_amdgcn_exp2f(sl[i][j]);  // e^{s_r} <= 1
+        }
+      } else if constexpr (kScalar) {
+        const float a = __builtin_amdgcn_exp2f(dl[i][0]), b = __builtin_amdgcn_exp2f(sl[i][0]);
+        ed = f32x4{a, a, a, a};
+        es = f32x4{b, b, b, b};
+      } else {
+        ed = f32x4{1.f, 1.f, 1.f, 1.f};
+        es = ed;
       }
       const f32x4 fre = ed * ebv;  // e^{g_r}
       const unsigned lo = loff<T, L::RBK>(r, static_cast<unsigned>(c4));
-      store4(reinterpret_cast<T*>(Krd + lo), kv[i] * ed);
-      store4(reinterpret_cast<T*>(Qrd + lo), qv[i] * ed);
+      if constexpr (kChannel) {
+        store4(reinterpret_cast<T*>(Krd + lo), kv[i] * ed);
+        store4(reinterpret_cast<T*>(Qrd + lo), qv[i] * ed);
+        store4(reinterpret_cast<T*>(Kc + lo), kv[i] * es);
+      } else {
+        // plain operands (the column operand is Krd itself); the gate is
+        // applied to the products element by element
+        store4(reinterpret_cast<T*>(Krd + lo), kv[i]);
+        store4(reinterpret_cast<T*>(Qrd + lo), qv[i]);
+      }
       const f32x4 kc = kv[i] * es;
-      store4(reinterpret_cast<T*>(Kc + lo), kc);
       const int to = static_cast<int>(toff<T, B::RB_R>(r, static_cast<unsigned>(c4)));
       buffer_store4(wr, static_cast<int>(B::oQ) + to, qv[i] * fre, static_cast<T*>(nullptr));
       buffer_store4(wr, static_cast<int>(B::oR) + to, bt[i] * (kv[i] * fre), static_cast<T*>(nullptr));
@@ -767,7 +826,6 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
 
   // ---- a3: gated k k^T (A, fp32 in LDS) and q k^T (P) via MFMA, and the
   // diagonal blocks of the UT inverse T = (I + A)^{-1} ----------------------
-  // Block pair (I, J <= I); returns this lane's A values (beta-scaled, masked).
   // Channels of diagonal block I whose scale is 0 (decay beyond 2^86 across
   // the block): their contributions to this lane's A and P values, from the
   // per-token gates, e^{g_r - g_s} = prod_{s < u <= r} alpha_u.  Rows past
@@ -807,15 +865,51 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
   };
   // Block pair (I, J <= I); returns this lane's A values (beta-scaled, masked).
   auto pair = [&](int I, int J) {
-    const float* f = fv + (I * (I + 1) / 2 + J) * DK;  // column scale of the pair
     f32x4 aA = {0.f, 0.f, 0.f, 0.f}, aP = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (kChannel) {
+      const float* f = fv + (I * (I + 1) / 2 + J) * DK;  // column scale of the pair
 #pragma unroll 8
-    for (int k0 = 0; k0 < DK; k0 += M::KS) {
-      const typename M::frag bf = natf<T, L::RBK>::scaled(Kc, 16 * J + n, f, k0, g);
-      aA = M::mma(natf<T, L::RBK>::raw(Krd, 16 * I + n, k0, g), bf, aA);
-      aP = M::mma(natf<T, L::RBK>::raw(Qrd, 16 * I + n, k0, g), bf, aP);
+      for (int k0 = 0; k0 < DK; k0 += M::KS) {
+        const typename M::frag bf = natf<T, L::RBK>::scaled(Kc, 16 * J + n, f, k0, g);
+        aA = M::mma(natf<T, L::RBK>::raw(Krd, 16 * I + n, k0, g), bf, aA);
+        aP = M::mma(natf<T, L::RBK>::raw(Qrd, 16 * I + n, k0, g), bf, aP);
+      }
+      if (I == J) diag_exact(I, aA, aP);
+    } else {
+#pragma unroll 8
+      for (int k0 = 0; k0 < DK; k0 += M::KS) {
+        const typename M::frag bf = natf<T, L::RBK>::raw(Krd, 16 * J + n, k0, g);
+        aA = M::mma(natf<T, L::RBK>::raw(Krd, 16 * I + n, k0, g), bf, aA);
+        aP = M::mma(natf<T, L::RBK>::raw(Qrd, 16 * I + n, k0, g), bf, aP);
+      }
+      if constexpr (kScalar) {
+        // e^{g_r - g_s} for this lane's (row, column): the rows s+1 .. r of
+        // a diagonal block summed one by one, else d_r + s_s + the blocks
+        // strictly between -- every term <= 0
+        f32x4 x;
+        if (I == J) {
+          x = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int u = 1; u < 16; ++u) {
+            const float lu = lrow[16 * I + u];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (u > n && u <= 4 * g + i) x[i] += lu;
+          }
+        } else {
+          float mid = srow[16 * J + n];
+          for (int kk = J + 1; kk < I; ++kk) mid += dsum[kk];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[i] = drow[16 * I + 4 * g + i] + mid;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float w = __builtin_amdgcn_exp2f(x[i]);
+          aA[i] *= w;
+          aP[i] *= w;
+        }
+      }
     }
-    if (I == J) diag_exact(I, aA, aP);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int rr = 4 * g + i;
@@ -1662,6 +1756,7 @@ bool make_prefill_plan(const kda_prefill_desc* d, int64_t max_chunks, PrefillPla
   p->dv = d->dv;
   p->C = d->chunk;
   p->dt = d->io_dtype;
+  p->gate = d->gate;
   p->max_chunks = max_chunks;
   p->sort = d->num_seqs <= 8192;
   const size_t slots = static_cast<size_t>(max_chunks) * d->num_heads;
@@ -1821,7 +1916,7 @@ static hipError_t pipe_streams(int64_t scan_wgs, PipeStreams** out) {
   return hipSuccess;
 }
 
-template <typename T, int C, int DK, int DV>
+template <typename T, int C, int DK, int DV, int G>
 static hipError_t launch_prefill_t(const PrefillPlan& p, const void* q, const void* k, const void* v,
                                    const float* la, const float* beta, const int32_t* cu, const float* S0,
                                    void* o, float* S_T, void* ws, hipStream_t st) {
@@ -1840,12 +1935,12 @@ static hipError_t launch_prefill_t(const PrefillPlan& p, const void* q, const vo
   // use (LDS-limited), each walking (chunk, head) items.
   auto prep = [&](int64_t cbase, int64_t count, hipStream_t s, int cus, int32_t* publish, int published,
                   const int* guard) -> hipError_t {
-    hipError_t r = set_lds_limit(reinterpret_cast<const void*>(&prep_kernel<T, C, DK>), lp);
+    hipError_t r = set_lds_limit(reinterpret_cast<const void*>(&prep_kernel<T, C, DK, G>), lp);
     if (r != hipSuccess) return r;
     const int64_t per_cu = (160 * 1024) / static_cast<int64_t>(lp) > 0 ? (160 * 1024) / static_cast<int64_t>(lp) : 1;
     const int64_t items = count * p.H;
     const int64_t grid = items < per_cu * cus ? items : per_cu * cus;
-    hipLaunchKernelGGL((prep_kernel<T, C, DK>), dim3(static_cast<unsigned>(grid)), dim3(kPrepThreads), lp, s,
+    hipLaunchKernelGGL((prep_kernel<T, C, DK, G>), dim3(static_cast<unsigned>(grid)), dim3(kPrepThreads), lp, s,
                        static_cast<const T*>(q), static_cast<const T*>(k), la, beta, cu, chunk_off, p.N, p.H,
                        blocks, static_cast<int>(cbase), static_cast<int>(count), publish, published, guard);
     return hipGetLastError();
@@ -1917,14 +2012,25 @@ static hipError_t launch_prefill_t(const PrefillPlan& p, const void* q, const vo
   return launch_scan<T, C, DK, DV, 4>(p, v, cu, chunk_off, order, blocks, S0, o, S_T, st);
 }
 
+template <typename T, int C, int DK, int DV>
+static hipError_t dispatch_gate(const PrefillPlan& p, const void* q, const void* k, const void* v, const float* la,
+                                const float* beta, const int32_t* cu, const float* S0, void* o, float* S_T,
+                                void* ws, hipStream_t st) {
+  if (p.gate == KDA_GATE_CHANNEL)
+    return launch_prefill_t<T, C, DK, DV, KDA_GATE_CHANNEL>(p, q, k, v, la, beta, cu, S0, o, S_T, ws, st);
+  if (p.gate == KDA_GATE_SCALAR)
+    return launch_prefill_t<T, C, DK, DV, KDA_GATE_SCALAR>(p, q, k, v, la, beta, cu, S0, o, S_T, ws, st);
+  return launch_prefill_t<T, C, DK, DV, KDA_GATE_NONE>(p, q, k, v, la, beta, cu, S0, o, S_T, ws, st);
+}
+
 template <typename T, int C>
 static hipError_t dispatch_dims(const PrefillPlan& p, const void* q, const void* k, const void* v, const float* la,
                                 const float* beta, const int32_t* cu, const float* S0, void* o, float* S_T,
                                 void* ws, hipStream_t st) {
-  if (p.dk == 128 && p.dv == 128) return launch_prefill_t<T, C, 128, 128>(p, q, k, v, la, beta, cu, S0, o, S_T, ws, st);
-  if (p.dk == 128 && p.dv == 64) return launch_prefill_t<T, C, 128, 64>(p, q, k, v, la, beta, cu, S0, o, S_T, ws, st);
-  if (p.dk == 64 && p.dv == 128) return launch_prefill_t<T, C, 64, 128>(p, q, k, v, la, beta, cu, S0, o, S_T, ws, st);
-  if (p.dk == 64 && p.dv == 64) return launch_prefill_t<T, C, 64, 64>(p, q, k, v, la, beta, cu, S0, o, S_T, ws, st);
+  if (p.dk == 128 && p.dv == 128) return dispatch_gate<T, C, 128, 128>(p, q, k, v, la, beta, cu, S0, o, S_T, ws, st);
+  if (p.dk == 128 && p.dv == 64) return dispatch_gate<T, C, 128, 64>(p, q, k, v, la, beta, cu, S0, o, S_T, ws, st);
+  if (p.dk == 64 && p.dv == 128) return dispatch_gate<T, C, 64, 128>(p, q, k, v, la, beta, cu, S0, o, S_T, ws, st);
+  if (p.dk == 64 && p.dv == 64) return dispatch_gate<T, C, 64, 64>(p, q, k, v, la, beta, cu, S0, o, S_T, ws, st);
   return hipErrorInvalidValue;
 }
 

@@ -64,6 +64,18 @@ typedef enum {
   KDA_BF16 = 1   /* q, k, v and o in bfloat16 */
 } kda_dtype;
 
+/* Forget-gate form.  KDA's gate is one rate per key channel; the scalar
+   form (one rate per head and token) is Gated DeltaNet and no gate at all
+   (alpha = 1) is DeltaNet -- the two special cases the deep-read report
+   (sections 2.2 and 2.3) and the zhaixingw.cn explainer's KDA section (the
+   GDN update with a scalar gate) place KDA against.  They run as
+   specialisations of the same kernels with cheaper gate handling. */
+typedef enum {
+  KDA_GATE_CHANNEL = 0,  /* log_alpha [.., dk]: one rate per key channel (KDA) */
+  KDA_GATE_SCALAR = 1,   /* log_alpha [..]: one rate per head (Gated DeltaNet) */
+  KDA_GATE_NONE = 2      /* no forget gate, alpha = 1 (DeltaNet); log_alpha unused, may be NULL */
+} kda_gate;
+
 /* kda_prefill_desc.flags */
 enum {
   /* Run the chunk preparation and the state pass one after the other on the
@@ -85,6 +97,7 @@ typedef struct {
                                      given it is validated and used to size the
                                      launch exactly; may be NULL */
   uint32_t flags;        /* KDA_PREFILL_* bits; 0 for the default schedule */
+  kda_gate gate;         /* form of log_alpha; KDA_GATE_CHANNEL for KDA */
 } kda_prefill_desc;
 
 /*
@@ -107,7 +120,8 @@ size_t kda_prefill_workspace_size(const kda_prefill_desc* desc);
  *
  *   q, k       [T_tot, H, dk]  io_dtype
  *   v          [T_tot, H, dv]  io_dtype
- *   log_alpha  [T_tot, H, dk]  float32, log of the forget gate (<= 0)
+ *   log_alpha  [T_tot, H, dk]  float32, log of the forget gate (<= 0); [T_tot, H]
+ *                              for KDA_GATE_SCALAR; unused for KDA_GATE_NONE
  *   beta       [T_tot, H]      float32
  *   cu_seqlens [N + 1]         int32 offsets (device)
  *   S0         [N, H, dk, dv]  float32, or NULL for a zero initial state
@@ -195,16 +209,17 @@ int32_t kda_prefill_set_wait_limit(int32_t polls);
  *
  *   q, k       [B, H, dk]      io_dtype
  *   v          [B, H, dv]      io_dtype
- *   log_alpha  [B, H, dk]      float32
+ *   log_alpha  [B, H, dk]      float32 ([B, H] for KDA_GATE_SCALAR; unused, may be
+ *                              NULL, for KDA_GATE_NONE)
  *   beta       [B, H]          float32
  *   S          [B, H, dk, dv]  float32, read as S_{t-1} and overwritten with S_t
  *   o          [B, H, dv]      io_dtype, written
  *
- * Errors: KDA_ERR_INVALID_ARGUMENT (null pointer with B > 0, B < 0, H < 1),
- * KDA_ERR_UNSUPPORTED (dk/dv not in {64,128}), KDA_ERR_DEVICE.  B == 0 is a
+ * Errors: KDA_ERR_INVALID_ARGUMENT (null pointer with B > 0, B < 0, H < 1,
+ * unknown gate), KDA_ERR_UNSUPPORTED (dk/dv not in {64,128}), KDA_ERR_DEVICE.  B == 0 is a
  * no-op.  S must not overlap any other argument.
  */
-kda_status kda_decode_step(int32_t B, int32_t H, int32_t dk, int32_t dv, kda_dtype io_dtype,
+kda_status kda_decode_step(int32_t B, int32_t H, int32_t dk, int32_t dv, kda_dtype io_dtype, kda_gate gate,
                            const void* q, const void* k, const void* v,
                            const float* log_alpha, const float* beta,
                            float* S, void* o, void* stream);
@@ -212,7 +227,8 @@ kda_status kda_decode_step(int32_t B, int32_t H, int32_t dk, int32_t dv, kda_dty
 /* Static, human-readable name of a status code (never NULL). */
 const char* kda_status_string(kda_status s);
 
-/* Library version as MAJOR*10000 + MINOR*100 + PATCH (2.0.0: desc.flags). */
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH (2.0.0: desc.flags,
+   desc.gate and the gate argument of kda_decode_step). */
 int32_t kda_version(void);
 
 #ifdef __cplusplus

@@ -100,12 +100,23 @@ class PrefillInputs:
     q: np.ndarray            # [T_tot, H, dk] float32
     k: np.ndarray            # [T_tot, H, dk] float32
     v: np.ndarray            # [T_tot, H, dv] float32
-    log_alpha: np.ndarray    # [T_tot, H, dk] float32
+    log_alpha: Optional[np.ndarray]  # [T_tot, H, dk] (gate "channel"), [T_tot, H] ("scalar") or None ("none")
     beta: np.ndarray         # [T_tot, H]     float32
     cu_seqlens: np.ndarray   # [N + 1]        int32
     S0: Optional[np.ndarray]  # [N, H, dk, dv] float32 or None
     io_dtype: str            # 'f32' or 'bf16'
     chunk: int = 64
+    gate: str = "channel"    # forget-gate form: 'channel' (KDA), 'scalar' (GDN) or 'none' (DeltaNet)
+
+    def log_alpha_channels(self) -> np.ndarray:
+        """log_alpha as one rate per key channel [T_tot, H, dk] (the scalar
+        gate repeated over the channels, zeros without a gate)."""
+        T, H, dk = self.q.shape
+        if self.gate == "channel":
+            return self.log_alpha
+        if self.gate == "scalar":
+            return np.ascontiguousarray(np.broadcast_to(self.log_alpha[:, :, None], (T, H, dk)))
+        return np.zeros((T, H, dk), np.float32)
 
     @property
     def num_seqs(self) -> int:
@@ -122,8 +133,13 @@ class PrefillInputs:
 
 def make_prefill(lengths, H: int, dk: int, dv: int, io_dtype: str, seed: int,
                  S0_std: Optional[float] = None, long_memory_frac: float = 0.0,
-                 chunk: int = 64, lengths_from_rng=None) -> PrefillInputs:
+                 chunk: int = 64, lengths_from_rng=None, gate: str = "channel") -> PrefillInputs:
     """Generic seeded prefill inputs.
+
+    ``gate`` selects the forget-gate form: "channel" draws z_alpha per key
+    channel [.., H, dk], "scalar" one per head [.., H] (the last draw of a
+    block, so the other tensors are the same as for "channel"), "none" draws
+    no gate (log_alpha is None).
 
     lengths: list of sequence lengths, or None when ``lengths_from_rng`` (a
     callable taking the Generator) draws them first.  ``long_memory_frac``
@@ -140,7 +156,10 @@ def make_prefill(lengths, H: int, dk: int, dv: int, io_dtype: str, seed: int,
     k = np.empty((T, H, dk), np.float32)
     v = np.empty((T, H, dv), np.float32)
     beta = np.empty((T, H), np.float32)
-    la = np.empty((T, H, dk), np.float32)
+    if gate not in ("channel", "scalar", "none"):
+        raise ValueError(gate)
+    la = {"channel": lambda: np.empty((T, H, dk), np.float32), "scalar": lambda: np.empty((T, H), np.float32),
+          "none": lambda: None}[gate]()
 
     def fill(j: int):
         a, b = j * BLOCK, min(T, (j + 1) * BLOCK)
@@ -150,20 +169,21 @@ def make_prefill(lengths, H: int, dk: int, dv: int, io_dtype: str, seed: int,
         kb = rng.standard_normal((BLOCK, H, dk), dtype=np.float32)[:n]
         vb = rng.standard_normal((BLOCK, H, dv), dtype=np.float32)[:n]
         zb = rng.standard_normal((BLOCK, H), dtype=np.float32)[:n]
-        za = rng.standard_normal((BLOCK, H, dk), dtype=np.float32)[:n]
+        if gate != "none":
+            za = rng.standard_normal((BLOCK, H, dk) if gate == "channel" else (BLOCK, H), dtype=np.float32)[:n]
+            la[a:b] = neg_softplus_f32(za)
         qb, kb = l2norm_f32(qb), l2norm_f32(kb)
         if io_dtype == "bf16":
             qb, kb, vb = bf16_round(qb), bf16_round(kb), bf16_round(vb)
         q[a:b], k[a:b], v[a:b] = qb, kb, vb
         beta[a:b] = sigmoid_f32(zb)
-        la[a:b] = neg_softplus_f32(za)
 
     if io_dtype not in ("bf16", "f32"):
         raise ValueError(io_dtype)
     nblk = (T + BLOCK - 1) // BLOCK
     with concurrent.futures.ThreadPoolExecutor(_workers()) as ex:
         list(ex.map(fill, range(nblk)))
-    if long_memory_frac > 0.0:
+    if long_memory_frac > 0.0 and gate == "channel":
         nlm = int(round(long_memory_frac * dk))
         mrng = np.random.Generator(np.random.PCG64([seed, _MASK_STREAM]))
         for h in range(H):
@@ -174,7 +194,7 @@ def make_prefill(lengths, H: int, dk: int, dv: int, io_dtype: str, seed: int,
         srng = np.random.Generator(np.random.PCG64([seed, _S0_STREAM]))
         S0 = (srng.standard_normal((len(lengths), H, dk, dv), dtype=np.float32) * np.float32(S0_std)).astype(np.float32)
     return PrefillInputs(q=q, k=k, v=v, log_alpha=la, beta=beta, cu_seqlens=cu, S0=S0,
-                         io_dtype=io_dtype, chunk=chunk)
+                         io_dtype=io_dtype, chunk=chunk, gate=gate)
 
 
 def _loguniform_lengths(n: int, lo: int, hi: int):
@@ -194,6 +214,11 @@ WORKLOADS = {
                           S0_std=0.02, varlen=(64, 128, 32768)),
     "decode256x32_bf16": dict(index=4, kind="decode", B=256, H=32, dk=128, dv=128, io_dtype="bf16",
                               steps=1024, S0_std=0.02),
+    # the 131072-token shape with the scalar gate (Gated DeltaNet) and without a gate (DeltaNet)
+    "long131072_bf16_gdn": dict(index=5, kind="prefill", lengths=[131072], H=32, dk=128, dv=128, io_dtype="bf16",
+                                gate="scalar"),
+    "long131072_bf16_deltanet": dict(index=6, kind="prefill", lengths=[131072], H=32, dk=128, dv=128,
+                                     io_dtype="bf16", gate="none"),
 }
 
 
@@ -211,7 +236,7 @@ def workload_prefill(name: str, lengths_override=None, H_override=None) -> Prefi
         draw = _loguniform_lengths(n, lo, hi)
     return make_prefill(lengths, H, w["dk"], w["dv"], w["io_dtype"], seed,
                         S0_std=w.get("S0_std"), long_memory_frac=w.get("long_memory_frac", 0.0),
-                        lengths_from_rng=draw)
+                        lengths_from_rng=draw, gate=w.get("gate", "channel"))
 
 
 @dataclasses.dataclass
@@ -219,7 +244,7 @@ class DecodeStepInputs:
     q: np.ndarray          # [B, H, dk] float32 (bf16-rounded for bf16 io)
     k: np.ndarray
     v: np.ndarray          # [B, H, dv]
-    log_alpha: np.ndarray  # [B, H, dk] float32
+    log_alpha: Optional[np.ndarray]  # [B, H, dk] float32; [B, H] for the scalar gate; None without a gate
     beta: np.ndarray       # [B, H]     float32
 
 
@@ -229,15 +254,23 @@ def make_decode_state(B: int, H: int, dk: int, dv: int, std: float, seed: int) -
     return (rng.standard_normal((B, H, dk, dv), dtype=np.float32) * np.float32(std)).astype(np.float32)
 
 
-def make_decode_step(B: int, H: int, dk: int, dv: int, io_dtype: str, seed: int, step: int) -> DecodeStepInputs:
+def make_decode_step(B: int, H: int, dk: int, dv: int, io_dtype: str, seed: int, step: int,
+                     gate: str = "channel") -> DecodeStepInputs:
     """Fresh per-token decode inputs for step ``step`` (its own PCG64 stream,
-    so any step can be regenerated without drawing the earlier ones)."""
+    so any step can be regenerated without drawing the earlier ones).
+    ``gate``: "channel" (log_alpha [B, H, dk]), "scalar" ([B, H]) or "none"."""
     rng = np.random.Generator(np.random.PCG64([seed, step]))
     q = l2norm_f32(rng.standard_normal((B, H, dk), dtype=np.float32))
     k = l2norm_f32(rng.standard_normal((B, H, dk), dtype=np.float32))
     v = rng.standard_normal((B, H, dv), dtype=np.float32)
     beta = sigmoid_f32(rng.standard_normal((B, H), dtype=np.float32))
-    la = neg_softplus_f32(rng.standard_normal((B, H, dk), dtype=np.float32))
+    la = None
+    if gate == "channel":
+        la = neg_softplus_f32(rng.standard_normal((B, H, dk), dtype=np.float32))
+    elif gate == "scalar":
+        la = neg_softplus_f32(rng.standard_normal((B, H), dtype=np.float32))
+    elif gate != "none":
+        raise ValueError(gate)
     if io_dtype == "bf16":
         q, k, v = bf16_round(q), bf16_round(k), bf16_round(v)
     return DecodeStepInputs(q=q, k=k, v=v, log_alpha=la, beta=beta)

@@ -59,7 +59,8 @@ def gpu_prefill(w: synth.PrefillInputs, chunk: int = None, S0=None, in_place: bo
     torch = torch_mod()
     dt = w.io_dtype
     q, k, v = dev(w.q, dt), dev(w.k, dt), dev(w.v, dt)
-    la, b = dev(w.log_alpha), dev(w.beta)
+    la = dev(w.log_alpha) if w.log_alpha is not None else None
+    b = dev(w.beta)
     cu = dev(w.cu_seqlens)
     s0 = S0 if S0 is not None else w.S0
     s0d = dev(s0) if s0 is not None else None
@@ -80,10 +81,11 @@ def gpu_prefill(w: synth.PrefillInputs, chunk: int = None, S0=None, in_place: bo
 def oracle_prefill(w: synth.PrefillInputs, S0=None, heads=None, threads: int = 0):
     """fp64 oracle on the same values; optionally on a subset of heads."""
     s0 = S0 if S0 is not None else w.S0
+    la = w.log_alpha_channels()
     if heads is None:
-        return oracle.prefill(w.q, w.k, w.v, w.log_alpha, w.beta, w.cu_seqlens, s0, threads=threads)
+        return oracle.prefill(w.q, w.k, w.v, la, w.beta, w.cu_seqlens, s0, threads=threads)
     hs = list(heads)
-    return oracle.prefill(w.q[:, hs], w.k[:, hs], w.v[:, hs], w.log_alpha[:, hs], w.beta[:, hs], w.cu_seqlens,
+    return oracle.prefill(w.q[:, hs], w.k[:, hs], w.v[:, hs], la[:, hs], w.beta[:, hs], w.cu_seqlens,
                           None if s0 is None else s0[:, hs], threads=threads)
 
 

@@ -51,7 +51,7 @@ def test_workspace_size():
     assert 0 < exact <= bound
     for bad in (dict(dk=96), dict(chunk=48), dict(num_heads=0), dict(total_tokens=-1), dict(io_dtype=7),
                 dict(cu_seqlens_host=[0, 60, 99]), dict(cu_seqlens_host=[1, 60, 100]),
-                dict(cu_seqlens_host=[0, 70, 60]), dict(flags=2), dict(flags=1 << 31)):
+                dict(cu_seqlens_host=[0, 70, 60]), dict(flags=2), dict(flags=1 << 31), dict(gate=3), dict(gate=-1)):
         d3, k3 = desc(**bad)
         assert kda.prefill_workspace_size(d3) == 0, bad
 
@@ -76,7 +76,10 @@ def test_prefill_validation_codes():
     assert call_prefill(d, wsb=1 << 30) == kda.KDA_ERR_UNSUPPORTED
     d, keep = desc(cu_seqlens_host=[0, 50, 101])
     assert call_prefill(d, wsb=1 << 30) == kda.KDA_ERR_INVALID_ARGUMENT
+    d, keep = desc(gate=kda.KDA_GATE_SCALAR)
+    assert call_prefill(d, la=None) == kda.KDA_ERR_INVALID_ARGUMENT                   # scalar gate needs log_alpha
     d, keep = desc()
+    assert call_prefill(d, la=None) == kda.KDA_ERR_INVALID_ARGUMENT
     assert call_prefill(d, q=None) == kda.KDA_ERR_INVALID_ARGUMENT
     assert call_prefill(d, cu=None) == kda.KDA_ERR_INVALID_ARGUMENT
     assert call_prefill(d, ws=None) == kda.KDA_ERR_INVALID_ARGUMENT
@@ -95,18 +98,27 @@ def test_decode_validation_codes():
     lib = kda.load_library()
     f = lambda *a: lib.kda_decode_step(*a, None)
     ptrs = [FAKE + (i << 30) for i in range(7)]
-    assert f(-1, 2, 128, 128, kda.KDA_BF16, *ptrs) == kda.KDA_ERR_INVALID_ARGUMENT
-    assert f(4, 0, 128, 128, kda.KDA_BF16, *ptrs) == kda.KDA_ERR_INVALID_ARGUMENT
-    assert f(4, 2, 32, 128, kda.KDA_BF16, *ptrs) == kda.KDA_ERR_UNSUPPORTED
-    assert f(4, 2, 128, 128, 5, *ptrs) == kda.KDA_ERR_INVALID_ARGUMENT
-    assert f(0, 2, 128, 128, kda.KDA_BF16, *([None] * 7)) == kda.KDA_OK
-    assert f(4, 2, 128, 128, kda.KDA_BF16, None, *ptrs[1:]) == kda.KDA_ERR_INVALID_ARGUMENT
+    CH, SC = kda.KDA_GATE_CHANNEL, kda.KDA_GATE_SCALAR
+    assert f(-1, 2, 128, 128, kda.KDA_BF16, CH, *ptrs) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert f(4, 0, 128, 128, kda.KDA_BF16, CH, *ptrs) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert f(4, 2, 32, 128, kda.KDA_BF16, CH, *ptrs) == kda.KDA_ERR_UNSUPPORTED
+    assert f(4, 2, 128, 128, 5, CH, *ptrs) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert f(4, 2, 128, 128, kda.KDA_BF16, 3, *ptrs) == kda.KDA_ERR_INVALID_ARGUMENT      # unknown gate
+    assert f(0, 2, 128, 128, kda.KDA_BF16, CH, *([None] * 7)) == kda.KDA_OK
+    assert f(4, 2, 128, 128, kda.KDA_BF16, CH, None, *ptrs[1:]) == kda.KDA_ERR_INVALID_ARGUMENT
+    no_la = list(ptrs)
+    no_la[3] = None
+    assert f(4, 2, 128, 128, kda.KDA_BF16, SC, *no_la) == kda.KDA_ERR_INVALID_ARGUMENT   # scalar gate needs it
     bad = list(ptrs)
     bad[5] = ptrs[0] + 64  # S overlaps q
-    assert f(4, 2, 128, 128, kda.KDA_BF16, *bad) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert f(4, 2, 128, 128, kda.KDA_BF16, CH, *bad) == kda.KDA_ERR_INVALID_ARGUMENT
     bad = list(ptrs)
     bad[6] = ptrs[5] + 128  # o overlaps S
-    assert f(4, 2, 128, 128, kda.KDA_BF16, *bad) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert f(4, 2, 128, 128, kda.KDA_BF16, CH, *bad) == kda.KDA_ERR_INVALID_ARGUMENT
+    bad = list(ptrs)
+    bad[5] = ptrs[3] + 4 * 128 * 8 - 4  # S overlaps the last word of a [4, 2, 128] log_alpha
+    assert f(4, 2, 128, 128, kda.KDA_BF16, CH, *bad) == kda.KDA_ERR_INVALID_ARGUMENT
+
 
 
 def block_bytes(C: int, dk: int, es: int) -> int:

@@ -42,7 +42,8 @@ def _run(name, group=8, overlapped=False):
     log("full-size %s: T=%d H=%d N=%d, every head checked" % (name, T, H, w.num_seqs))
     dt = w.io_dtype
     q, k, v = dev(w.q, dt), dev(w.k, dt), dev(w.v, dt)
-    la, b, cu = dev(w.log_alpha), dev(w.beta), dev(w.cu_seqlens)
+    la = dev(w.log_alpha) if w.log_alpha is not None else None
+    b, cu = dev(w.beta), dev(w.cu_seqlens)
     S0 = dev(w.S0) if w.S0 is not None else None
     host_cu = w.cu_seqlens.tolist()
     o, S = kda.prefill(q, k, v, la, b, cu, S0, cu_seqlens_host=host_cu, chunk=w.chunk)
@@ -53,7 +54,13 @@ def _run(name, group=8, overlapped=False):
     eo, es = GlobalErr("o (all %d heads)" % H), GlobalErr("S_T (all %d heads)" % H)
     for h0 in range(0, H, group):
         hs = list(range(h0, min(H, h0 + group)))
-        o_ref, S_ref = oracle.prefill(w.q[:, hs], w.k[:, hs], w.v[:, hs], w.log_alpha[:, hs], w.beta[:, hs],
+        if w.gate == "channel":
+            la_h = w.log_alpha[:, hs]
+        elif w.gate == "scalar":
+            la_h = np.ascontiguousarray(np.broadcast_to(w.log_alpha[:, hs, None], (T, len(hs), w.q.shape[2])))
+        else:
+            la_h = np.zeros((T, len(hs), w.q.shape[2]), np.float32)
+        o_ref, S_ref = oracle.prefill(w.q[:, hs], w.k[:, hs], w.v[:, hs], la_h, w.beta[:, hs],
                                       w.cu_seqlens, None if w.S0 is None else w.S0[:, hs])
         eo.add(host(o[:, h0:h0 + len(hs)]), o_ref)
         es.add(host(S[:, h0:h0 + len(hs)]), S_ref)
@@ -72,6 +79,13 @@ def test_long131072_all_heads():
 
 def test_varlen64_all_heads():
     _run("varlen64_bf16", group=4)
+
+
+@pytest.mark.parametrize("name", ["long131072_bf16_gdn", "long131072_bf16_deltanet"])
+def test_long131072_gate_forms_all_heads(name):
+    """The 131072-token shape with one forget rate per head (Gated DeltaNet)
+    and without a gate (DeltaNet)."""
+    _run(name, overlapped=True)
 
 
 def test_decode_full_size_every_state():

@@ -54,3 +54,24 @@ def test_decode_steps_regenerate_independently():
     b = synth.make_decode_step(2, 3, 8, 4, "bf16", 99, 5)
     c = synth.make_decode_step(2, 3, 8, 4, "bf16", 99, 6)
     assert np.array_equal(a.q, b.q) and not np.array_equal(a.q, c.q)
+
+
+def test_gate_forms():
+    """The scalar gate draws one rate per (token, head) as the last draw of a
+    block (so q, k, v and beta equal the per-channel workload's), and no gate
+    draws none."""
+    ch = synth.make_prefill([100, 5000], H=3, dk=64, dv=64, io_dtype="bf16", seed=7)
+    sc = synth.make_prefill([100, 5000], H=3, dk=64, dv=64, io_dtype="bf16", seed=7, gate="scalar")
+    no = synth.make_prefill([100, 5000], H=3, dk=64, dv=64, io_dtype="bf16", seed=7, gate="none")
+    for w in (sc, no):
+        assert np.array_equal(w.q, ch.q) and np.array_equal(w.k, ch.k)
+        assert np.array_equal(w.v, ch.v) and np.array_equal(w.beta, ch.beta)
+    assert sc.log_alpha.shape == (5100, 3) and no.log_alpha is None
+    assert np.all(sc.log_alpha < 0)
+    full = sc.log_alpha_channels()
+    assert full.shape == (5100, 3, 64) and np.all(full == sc.log_alpha[:, :, None])
+    assert np.all(no.log_alpha_channels() == 0)
+    x = synth.make_decode_step(4, 2, 64, 64, "bf16", 9, 3, gate="scalar")
+    y = synth.make_decode_step(4, 2, 64, 64, "bf16", 9, 3)
+    assert x.log_alpha.shape == (4, 2) and np.array_equal(x.q, y.q) and np.array_equal(x.beta, y.beta)
+    assert synth.make_decode_step(4, 2, 64, 64, "bf16", 9, 3, gate="none").log_alpha is None
