@@ -32,10 +32,11 @@ kda_status check_desc(const kda_prefill_desc* d, int64_t* max_chunks) {
   if (d->num_seqs < 0 || d->total_tokens < 0 || d->num_heads < 1) return KDA_ERR_INVALID_ARGUMENT;
   if (!dtype_valid(d->io_dtype) || !gate_valid(d->gate)) return KDA_ERR_INVALID_ARGUMENT;
   if (!dims_supported(d->dk, d->dv)) return KDA_ERR_UNSUPPORTED;
-  if (d->chunk != 32 && d->chunk != 64) return KDA_ERR_UNSUPPORTED;
+  if (d->chunk != 16 && d->chunk != 32 && d->chunk != 64) return KDA_ERR_UNSUPPORTED;
   if (d->num_seqs == 0 && d->total_tokens != 0) return KDA_ERR_INVALID_ARGUMENT;
   if (d->flags & ~static_cast<uint32_t>(KDA_PREFILL_ONE_STREAM)) return KDA_ERR_INVALID_ARGUMENT;
-  const int64_t C = d->chunk;
+  const int64_t CL = d->chunk;                 // tokens per chunk
+  const int64_t C = d->chunk < 32 ? 32 : d->chunk;  // rows of the kernels' chunk tiles
   // one chunk of rows of any per-token tensor must span fewer than 2^31
   // bytes (the kernels use 32-bit offsets within a chunk)
   if (C * d->num_heads * (d->dk > d->dv ? d->dk : d->dv) * 4 >= (int64_t(1) << 31)) return KDA_ERR_UNSUPPORTED;
@@ -45,13 +46,13 @@ kda_status check_desc(const kda_prefill_desc* d, int64_t* max_chunks) {
     int64_t n = 0;
     for (int32_t i = 0; i < d->num_seqs; ++i) {
       if (cu[i + 1] < cu[i]) return KDA_ERR_INVALID_ARGUMENT;
-      n += (static_cast<int64_t>(cu[i + 1]) - cu[i] + C - 1) / C;
+      n += (static_cast<int64_t>(cu[i + 1]) - cu[i] + CL - 1) / CL;
     }
     if (cu[d->num_seqs] != d->total_tokens) return KDA_ERR_INVALID_ARGUMENT;
     *max_chunks = n;
   } else {
-    // sum_i ceil(L_i / C) <= (T + N (C - 1)) / C
-    *max_chunks = (static_cast<int64_t>(d->total_tokens) + static_cast<int64_t>(d->num_seqs) * (C - 1)) / C;
+    // sum_i ceil(L_i / CL) <= (T + N (CL - 1)) / CL
+    *max_chunks = (static_cast<int64_t>(d->total_tokens) + static_cast<int64_t>(d->num_seqs) * (CL - 1)) / CL;
   }
   if (*max_chunks > 0x7fffffff) return KDA_ERR_UNSUPPORTED;
   return KDA_OK;

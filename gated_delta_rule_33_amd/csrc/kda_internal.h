@@ -15,7 +15,9 @@ hipError_t launch_decode(kda_dtype dt, kda_gate gate, int dk, int dv, int BH, co
 
 // Prefill workspace carve-up, computed on the host.
 struct PrefillPlan {
-  int N, T, H, dk, dv, C;
+  int N, T, H, dk, dv;
+  int C;   // rows of the kernels' chunk tiles (32 or 64)
+  int CL;  // tokens per chunk (16, 32 or 64; at most C)
   kda_dtype dt;
   kda_gate gate;
   int64_t max_chunks;  // upper bound (exact when the host offsets are known)

@@ -531,7 +531,7 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                    const int32_t* __restrict__ cu,
                                                    const int32_t* __restrict__ chunk_off, int N, int H,
                                                    unsigned char* __restrict__ ws, int cbase, int count,
-                                                   int32_t* publish, int published, const int* guard) {
+                                                   int32_t* publish, int published, const int* guard, int cl) {
   typedef PrepLds<T, C, DK> L;
   typedef Blk<T, C, DK> B;
   typedef mma16<T> M;
@@ -585,8 +585,8 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
       const int mid = (lo + hi + 1) >> 1;
       if (chunk_off[mid] <= it.c) lo = mid; else hi = mid - 1;
     }
-    it.t0 = cu[lo] + (it.c - chunk_off[lo]) * C;
-    it.len = min(C, cu[lo + 1] - it.t0);
+    it.t0 = cu[lo] + (it.c - chunk_off[lo]) * cl;
+    it.len = min(cl, cu[lo + 1] - it.t0);
     return it;
   };
   struct Raw {
@@ -1176,7 +1176,7 @@ template <typename T, int C, int DK, int DV, int WAVES>
 __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel(
     const T* __restrict__ v, const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_off,
     const int32_t* __restrict__ order, int N, int H, const unsigned char* __restrict__ ws, const float* S0,
-    T* __restrict__ o, float* S_T, int* ready, int seg, int wait_polls, const int* guard) {
+    T* __restrict__ o, float* S_T, int* ready, int seg, int wait_polls, const int* guard, int cl) {
   typedef Blk<T, C, DK> B;
   typedef mma16<T> M;
   typedef accb<T> AB;
@@ -1213,7 +1213,7 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
   const bool loader = wave >= CW;
   const int tbeg = cu[seq], L_seq = cu[seq + 1] - tbeg;
   const int c0 = chunk_off[seq];
-  const int nch = (L_seq + C - 1) / C;
+  const int nch = (L_seq + cl - 1) / cl;
   // The whole sequence, chunks [cb, ce).  When `ready` is given, the blocks
   // of global chunks [j seg, (j + 1) seg) exist once *ready >= j (segment 0
   // from the start): the loader waves wait for that before they touch them.
@@ -1255,7 +1255,7 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
     const int lw = wave - CW;
     const unsigned char* src = ws + (static_cast<size_t>(c0 + cc) * H + h) * B::bytes;
     for (int j = lw; j < NG; j += kLoaderWaves) lds_load16(src + j * 1024 + lane * 16, smem + j * 1024);
-    const int t0 = tbeg + cc * C, len = min(C, L_seq - cc * C);
+    const int t0 = tbeg + cc * cl, len = min(cl, L_seq - cc * cl);
     for (int j = lw; j < NVG; j += kLoaderWaves) {
       const int r = j * VRPL + lane / VLPR;
       const int rr = r < len ? r : len - 1;  // rows past the end are masked by beta = 0
@@ -1314,9 +1314,9 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
             src = base + min(tile * LPT + min(lw + kLoaderWaves * lane, LPT - 1), LINES - 1) * 128;
           } else {
             const int cx = min(cc, ce - 1);
-            const int len = min(C, L_seq - cx * C);
+            const int len = min(cl, L_seq - cx * cl);
             const int r = min(lw * (C / kLoaderWaves) + min(lane - LPW, C / kLoaderWaves - 1), len - 1);
-            src = reinterpret_cast<const unsigned char*>(v + (static_cast<size_t>(tbeg + cx * C + r) * H + h) * DV +
+            src = reinterpret_cast<const unsigned char*>(v + (static_cast<size_t>(tbeg + cx * cl + r) * H + h) * DV +
                                                          tile * TILE);
           }
           __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
@@ -1344,7 +1344,7 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
           lds_load16(src + (lw + kLoaderWaves * m) * 1024, dst + (lw + kLoaderWaves * m) * 1024);
         lds_load16(src + (B::oG - B::oK), dst + (B::oG - B::oK));
         cc = min(cc, ce - 1);
-        const int t0 = tbeg + cc * C, len = min(C, L_seq - cc * C);
+        const int t0 = tbeg + cc * cl, len = min(cl, L_seq - cc * cl);
 #pragma unroll
         for (int m = 0; m < NVW; ++m) {
           const int j = (lw + kLoaderWaves * m) % NVG;
@@ -1363,9 +1363,9 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
       static_assert(!SL::stage_o || (SL::orow % 16 == 0 && 64 % LPR == 0 && C % RPI == 0), "output tile geometry");
       auto ostore = [&](int cc) {
         if constexpr (SL::stage_o) {
-          const int len = cc < cb ? 0 : min(C, L_seq - cc * C);  // nothing before the first chunk
+          const int len = cc < cb ? 0 : min(cl, L_seq - cc * cl);  // nothing before the first chunk
           const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
-              o + (static_cast<size_t>(tbeg + max(cc, 0) * C) * H + h) * DV + tile * TILE, 0,
+              o + (static_cast<size_t>(tbeg + max(cc, 0) * cl) * H + h) * DV + tile * TILE, 0,
               len * H * DV * static_cast<int>(sizeof(T)), 0x00020000);
 #pragma unroll
           for (int m = 0; m < NSW; ++m) {
@@ -1606,7 +1606,7 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
       for (int cc = cb; cc < ce; ++cc) {
         const unsigned char* eblk = eblk_of(cc);
         const unsigned char* lblk = lblk_of(cc);
-        const int t0 = tbeg + cc * C, len = min(C, L_seq - cc * C);
+        const int t0 = tbeg + cc * cl, len = min(cl, L_seq - cc * cl);
         RowFrags<T, B::RB_R, NSK> fr[MT];  // Qh rows: the early slot is refilled after M
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) fr[mt].load(eblk + B::oQ, 16 * mt + n, g);
@@ -1641,7 +1641,7 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
     for (int cc = cb; cc < ce; ++cc) {
       const unsigned char* eblk = eblk_of(cc);
       const unsigned char* lblk = lblk_of(cc);
-      const int t0 = tbeg + cc * C, len = min(C, L_seq - cc * C);
+      const int t0 = tbeg + cc * cl, len = min(cl, L_seq - cc * cl);
       // B fragments of the state (shared by R S and Qh S)
       F sb[NSK];
 #pragma unroll
@@ -1754,7 +1754,10 @@ bool make_prefill_plan(const kda_prefill_desc* d, int64_t max_chunks, PrefillPla
   p->H = d->num_heads;
   p->dk = d->dk;
   p->dv = d->dv;
-  p->C = d->chunk;
+  // chunks of 16 tokens run through the 32-row kernels (rows 16..31 stay
+  // empty, as in a partial last chunk)
+  p->C = d->chunk < 32 ? 32 : d->chunk;
+  p->CL = d->chunk;
   p->dt = d->io_dtype;
   p->gate = d->gate;
   p->max_chunks = max_chunks;
@@ -1764,7 +1767,7 @@ bool make_prefill_plan(const kda_prefill_desc* d, int64_t max_chunks, PrefillPla
   p->off_chunk_off = off; off = align256(off + 4 * (static_cast<size_t>(d->num_seqs) + 1));
   p->off_order = off;     off = align256(off + 4 * (static_cast<size_t>(d->num_seqs) + 1));
   off = (off + 1023) / 1024 * 1024;
-  p->off_blocks = off;    off += slots * block_bytes(d->io_dtype, d->chunk, d->dk);
+  p->off_blocks = off;    off += slots * block_bytes(d->io_dtype, p->C, d->dk);
   off = align256(off);
   p->seg = 0;
   p->off_ready = 0;
@@ -1809,7 +1812,7 @@ static hipError_t launch_scan(const PrefillPlan& p, const void* v, const int32_t
   const unsigned grid = static_cast<unsigned>((pairs + 7) / 8 * 8 * nsplit);
   hipLaunchKernelGGL((scan_kernel<T, C, DK, DV, WAVES>), dim3(grid), dim3(scan_threads<T, C, DK, WAVES>()), SL::total, st,
                      static_cast<const T*>(v), cu, chunk_off, order, p.N, p.H, blocks, S0, static_cast<T*>(o), S_T,
-                     ready, seg, prefill_wait_polls(), guard);
+                     ready, seg, prefill_wait_polls(), guard, p.CL);
   return hipGetLastError();
 }
 
@@ -1926,7 +1929,7 @@ static hipError_t launch_prefill_t(const PrefillPlan& p, const void* q, const vo
   unsigned char* blocks = w + p.off_blocks;
   if (p.N == 0) return hipSuccess;
   int32_t* ready = p.seg > 0 ? reinterpret_cast<int32_t*>(w + p.off_ready) : nullptr;
-  hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(1024), 0, st, cu, p.N, C, chunk_off, order, p.sort, ready);
+  hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(1024), 0, st, cu, p.N, p.CL, chunk_off, order, p.sort, ready);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t lp = PrepLds<T, C, DK>::total;
@@ -1942,7 +1945,7 @@ static hipError_t launch_prefill_t(const PrefillPlan& p, const void* q, const vo
     const int64_t grid = items < per_cu * cus ? items : per_cu * cus;
     hipLaunchKernelGGL((prep_kernel<T, C, DK, G>), dim3(static_cast<unsigned>(grid)), dim3(kPrepThreads), lp, s,
                        static_cast<const T*>(q), static_cast<const T*>(k), la, beta, cu, chunk_off, p.N, p.H,
-                       blocks, static_cast<int>(cbase), static_cast<int>(count), publish, published, guard);
+                       blocks, static_cast<int>(cbase), static_cast<int>(count), publish, published, guard, p.CL);
     return hipGetLastError();
   };
   int cus = 0;

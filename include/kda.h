@@ -91,7 +91,8 @@ typedef struct {
   int32_t total_tokens;  /* T_tot = cu_seqlens[N] >= 0 */
   int32_t num_heads;     /* H >= 1 */
   int32_t dk, dv;        /* key / value head dims, each 64 or 128 */
-  int32_t chunk;         /* tokens per chunk: 64 (32 also accepted) */
+  int32_t chunk;         /* tokens per chunk: 64 (32 and 16 also accepted; 16-token
+                            chunks run through the 32-row kernels) */
   kda_dtype io_dtype;    /* dtype of q, k, v and o */
   const int32_t* cu_seqlens_host; /* optional HOST copy of cu_seqlens [N+1]; when
                                      given it is validated and used to size the
@@ -146,7 +147,7 @@ size_t kda_prefill_workspace_size(const kda_prefill_desc* desc);
  *
  * Errors: KDA_ERR_INVALID_ARGUMENT (null pointer where data is required,
  * negative sizes, bad host offsets, misaligned workspace, overlapping buffers),
- * KDA_ERR_UNSUPPORTED (dk/dv not in {64,128}, chunk not in {32,64}),
+ * KDA_ERR_UNSUPPORTED (dk/dv not in {64,128}, chunk not in {16,32,64}),
  * KDA_ERR_WORKSPACE_TOO_SMALL, KDA_ERR_DEVICE (launch failure).  With
  * total_tokens == 0 only S_T = S0 (or zero) is written.
  */

@@ -72,7 +72,9 @@ def test_prefill_validation_codes():
     assert lib.kda_prefill(None, *([None] * 10), 0, None) == kda.KDA_ERR_INVALID_ARGUMENT
     d, keep = desc(dk=96)
     assert call_prefill(d, wsb=1 << 30) == kda.KDA_ERR_UNSUPPORTED
-    d, keep = desc(chunk=16)
+    d, keep = desc(chunk=8)
+    assert call_prefill(d, wsb=1 << 30) == kda.KDA_ERR_UNSUPPORTED
+    d, keep = desc(chunk=128)
     assert call_prefill(d, wsb=1 << 30) == kda.KDA_ERR_UNSUPPORTED
     d, keep = desc(cu_seqlens_host=[0, 50, 101])
     assert call_prefill(d, wsb=1 << 30) == kda.KDA_ERR_INVALID_ARGUMENT
@@ -150,6 +152,8 @@ def test_workspace_layout_sizes():
         (dict(flags=one), 2048 * 32, block_bytes(64, 128, 2), 0),
         (dict(io_dtype=kda.KDA_F32), 2048 * 32, block_bytes(64, 128, 4), 32 * 128 * 128 * 4),
         (dict(chunk=32), 4096 * 32, block_bytes(32, 128, 2), 32 * 128 * 128 * 4),
+        # 16-token chunks use 32-row blocks
+        (dict(chunk=16, flags=one), 8192 * 32, block_bytes(32, 128, 2), 0),
         (dict(dk=64, dv=64, num_heads=4), 2048 * 4, block_bytes(64, 64, 2), 4 * 64 * 64 * 4),
         (dict(num_seqs=3, total_tokens=4161, cu_seqlens_host=[0, 65, 65, 4161], num_heads=2),
          (2 + 0 + 64) * 2, block_bytes(64, 128, 2), 0),

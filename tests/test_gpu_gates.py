@@ -17,7 +17,7 @@ RAGGED = [1, 63, 64, 65, 200, 0, 31, 129]
 
 @pytest.mark.parametrize("gate", ["scalar", "none"])
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
-@pytest.mark.parametrize("dk,dv,chunk", [(128, 128, 64), (64, 128, 32), (128, 64, 64), (64, 64, 32)])
+@pytest.mark.parametrize("dk,dv,chunk", [(128, 128, 64), (64, 128, 32), (128, 64, 64), (64, 64, 32), (128, 128, 16)])
 def test_prefill_gate_forms(gate, dt, dk, dv, chunk):
     log("prefill gate=%s dt=%s dk=%d dv=%d chunk=%d" % (gate, dt, dk, dv, chunk))
     w = synth.make_prefill(RAGGED, H=3, dk=dk, dv=dv, io_dtype=dt, seed=51, S0_std=0.05, chunk=chunk, gate=gate)

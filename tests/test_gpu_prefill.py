@@ -27,7 +27,7 @@ RAGGED = [1, 63, 64, 65, 200, 0, 31, 129]
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 @pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (64, 128), (128, 64)])
-@pytest.mark.parametrize("chunk", [64, 32])
+@pytest.mark.parametrize("chunk", [64, 32, 16])
 def test_ragged_varlen(dt, dk, dv, chunk):
     """Packed sequences of ragged lengths (incl. 0, 1, C-1, C, C+1) with a
     nonzero initial state."""
@@ -63,13 +63,14 @@ def test_in_place_state_and_zero_tokens():
 
 
 def test_chunk_size_independence_and_resume():
-    """C=32 and C=64 agree; a split at t then resume from S_t equals the whole."""
+    """C = 16, 32 and 64 agree; a split at t then resume from S_t equals the whole."""
     w = synth.make_prefill([333], H=2, dk=128, dv=128, io_dtype="f32", seed=15, S0_std=0.05)
     log("prefill chunk independence + resume")
     o64, S64 = gpu_prefill(w, chunk=64)
-    o32, S32 = gpu_prefill(w, chunk=32)
-    assert np.max(np.abs(o64 - o32)) <= 1e-4 * np.max(np.abs(o64))
-    assert np.max(np.abs(S64 - S32)) <= 1e-4 * np.max(np.abs(S64))
+    for c in (32, 16):
+        oc, Sc = gpu_prefill(w, chunk=c)
+        assert np.max(np.abs(o64 - oc)) <= 1e-4 * np.max(np.abs(o64)), c
+        assert np.max(np.abs(S64 - Sc)) <= 1e-4 * np.max(np.abs(S64)), c
     t = 150
     a = synth.PrefillInputs(w.q[:t], w.k[:t], w.v[:t], w.log_alpha[:t], w.beta[:t], np.array([0, t], np.int32),
                             w.S0, "f32")
@@ -188,7 +189,7 @@ SEG_LENGTHS = [5000, 0, 3000, 777, 4096]
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
-@pytest.mark.parametrize("chunk", [64, 32])
+@pytest.mark.parametrize("chunk", [64, 32, 16])
 @pytest.mark.parametrize("mode", ["state", "nostate", "inplace"])
 def test_segmented_schedule(dt, chunk, mode):
     """Few (sequence, head) pairs and 200+ chunk indices: one scan launch on
@@ -335,7 +336,7 @@ def _random_cases(n: int, seed: int):
             lengths[0] = 5
         cases.append(dict(lengths=lengths, H=int(rng.integers(1, 4)),
                           dk=int(rng.choice([64, 128])), dv=int(rng.choice([64, 128])),
-                          chunk=int(rng.choice([32, 64])), dt=str(rng.choice(["bf16", "f32"])),
+                          chunk=int(rng.choice([16, 32, 64])), dt=str(rng.choice(["bf16", "f32"])),
                           s0=bool(rng.random() < 0.6), in_place=bool(rng.random() < 0.3), seed=100 + i))
     return cases
 
