@@ -205,10 +205,17 @@ def run_prefill(args, torch, kda, synth, oracle):
     return res
 
 
-def run_prefill_rate(wname, args, torch, kda, synth):
+def run_prefill_rate(wname, args, torch, kda, synth, stages=False):
     """Call time and rate of another prefill workload (no CPU baseline):
-    context for the main line, which times the 131072-token workload."""
+    context for the main line, which times the 131072-token workload.  With
+    ``stages`` every input and output stage runs (raw q and k, the gate
+    projection's output, RMSNorm and the sigmoid output gate)."""
     w = synth.workload_prefill(wname)
+    stage_kw = {}
+    if stages:
+        si = synth.make_stage_inputs(w, 4242)
+        w.q, w.k = si.q_raw, si.k_raw
+        w.log_alpha = si.z_gate
     bf = w.io_dtype == "bf16"
     tdt = torch.bfloat16 if bf else torch.float32
 
@@ -220,6 +227,10 @@ def run_prefill_rate(wname, args, torch, kda, synth):
     la = up(w.log_alpha) if w.log_alpha is not None else None
     b, cu = up(w.beta), up(w.cu_seqlens)
     S0 = up(w.S0) if w.S0 is not None else None
+    if stages:
+        stage_kw = dict(l2norm_qk=True, gate_softplus=True, norm_weight=up(si.norm_weight),
+                        out_gate=up(si.z_out, True))
+        del si
     T_tok, H, dk = w.q.shape
     dv = w.v.shape[2]
     N = w.num_seqs
@@ -229,23 +240,26 @@ def run_prefill_rate(wname, args, torch, kda, synth):
     stream = torch.cuda.current_stream()
     for _ in range(2):
         kda.prefill(q, k, v, la, b, cu, S0, o=o, S_T=ST, cu_seqlens_host=host_cu, chunk=w.chunk,
-                    one_stream=args.one_stream)
+                    one_stream=args.one_stream, **stage_kw)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     n = 5
     e0.record(stream)
     for _ in range(n):
         kda.prefill(q, k, v, la, b, cu, S0, o=o, S_T=ST, cu_seqlens_host=host_cu, chunk=w.chunk,
-                    one_stream=args.one_stream)
+                    one_stream=args.one_stream, **stage_kw)
     e1.record(stream)
     torch.cuda.synchronize()
     call_s = e0.elapsed_time(e1) / n / 1e3
     recovered = kda.prefill_recovered(q, v, cu, chunk=w.chunk, cu_seqlens_host=host_cu, one_stream=args.one_stream)
     nbytes, _, per_th, _ = prefill_algorithmic(T_tok, N, H, dk, dv, 2 if bf else 4, w.chunk, S0 is not None, w.gate)
-    del q, k, v, la, b, o, ST, S0
+    if stages:  # the output gate's pre-activation is read once more per token-head
+        nbytes += T_tok * H * dv * (2 if bf else 4)
+        per_th += dv * (2 if bf else 4)
+    del q, k, v, la, b, o, ST, S0, stage_kw
     torch.cuda.empty_cache()
     achieved = nbytes / call_s / 1e9
-    return dict(workload=wname, gate=w.gate, num_seqs=N, total_tokens=T_tok, heads=H,
+    return dict(workload=wname + ("+stages" if stages else ""), gate=w.gate, num_seqs=N, total_tokens=T_tok, heads=H,
                 call_ms=round(call_s * 1e3, 4), tokens_per_s=round(T_tok / call_s, 1),
                 hbm_frac=round(achieved / HBM_PEAK_GBS, 4), recovered=recovered,
                 roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
@@ -278,7 +292,7 @@ def decode_cpu_baseline(args, synth, oracle, B, H, dk, dv, std, seed):
     return res
 
 
-def run_decode(args, torch, kda, synth, oracle=None, gate="channel", steps=None):
+def run_decode(args, torch, kda, synth, oracle=None, gate="channel", steps=None, stages=False):
     wd = synth.WORKLOADS["decode256x32_bf16"]
     B, H, dk, dv = wd["B"], wd["H"], wd["dk"], wd["dv"]
     steps = steps or args.decode_steps
@@ -304,23 +318,32 @@ def run_decode(args, torch, kda, synth, oracle=None, gate="channel", steps=None)
     S = S0.clone()
     o = torch.empty((B, H, dv), dtype=torch.bfloat16, device="cuda")
     stream = torch.cuda.current_stream()
+    stage_kw = {}
+    if stages:  # every input and output stage (values drawn once, reused per step)
+        g = torch.Generator(device="cpu").manual_seed(4243)
+        stage_kw = dict(l2norm_qk=True, gate_softplus=True,
+                        norm_weight=(0.5 + torch.rand(dv, generator=g)).cuda(),
+                        out_gate=torch.randn((B, H, dv), generator=g).to(torch.bfloat16).cuda())
     for t in range(min(16, steps)):  # warm-up on a scratch copy of the state
-        kda.decode_step(qs[t], ks[t], vs[t], las[t], bs[t], S, o=o)
+        kda.decode_step(qs[t], ks[t], vs[t], las[t], bs[t], S, o=o, **stage_kw)
     S.copy_(S0)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     e0.record(stream)
     for t in range(steps):
-        kda.decode_step(qs[t], ks[t], vs[t], las[t], bs[t], S, o=o)
+        kda.decode_step(qs[t], ks[t], vs[t], las[t], bs[t], S, o=o, **stage_kw)
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     step_s = e0.elapsed_time(e1) / 1e3 / steps
     nbytes, per = decode_algorithmic(B * H, dk, dv, 2, gate)
+    if stages:  # the output gate's pre-activation
+        nbytes += B * H * dv * 2
+        per += dv * 2
     achieved = nbytes / step_s / 1e9
     res = dict(
-        metric="decode state-updates/s", gate=gate, value=round(B * H * steps / wall, 1), unit="state-updates/s",
+        metric="decode state-updates/s", gate=gate, stages=stages, value=round(B * H * steps / wall, 1), unit="state-updates/s",
         us_per_step=round(step_s * 1e6, 2),
         event_updates_per_s=round(B * H / step_s, 1),
         roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
@@ -386,8 +409,12 @@ def main():
     other = [] if args.no_other else [run_prefill_rate(n, args, torch, kda, synth)
                                       for n in ("batch4x4096_bf16", "varlen64_bf16", "long131072_bf16_gdn",
                                                 "long131072_bf16_deltanet")]
+    if not args.no_other:
+        other.append(run_prefill_rate("long131072_bf16", args, torch, kda, synth, stages=True))
     dec_gates = [] if (args.no_decode or args.no_other) else [
         run_decode(args, torch, kda, synth, None, gate=g, steps=min(256, args.decode_steps)) for g in ("scalar", "none")]
+    if dec_gates:
+        dec_gates.append(run_decode(args, torch, kda, synth, None, steps=min(256, args.decode_steps), stages=True))
     wl = pre["workload"]
     line = {
         "metric": "KDA prefill tokens/s (MFMA % peak) at T=128k; decode state-updates/s (HBM %)",

@@ -43,6 +43,18 @@ class KdaError(RuntimeError):
         super().__init__("%s failed: %s" % (where, status_string(status)))
 
 
+class Stages(ctypes.Structure):
+    """kda_stages: input and output stages around the recurrence."""
+    _fields_ = [
+        ("l2norm_qk", ctypes.c_int32),
+        ("l2norm_eps", ctypes.c_float),
+        ("gate_softplus", ctypes.c_int32),
+        ("norm_weight", ctypes.c_void_p),
+        ("norm_eps", ctypes.c_float),
+        ("out_gate", ctypes.c_void_p),
+    ]
+
+
 class PrefillDesc(ctypes.Structure):
     _fields_ = [
         ("num_seqs", ctypes.c_int32),
@@ -55,6 +67,7 @@ class PrefillDesc(ctypes.Structure):
         ("cu_seqlens_host", ctypes.POINTER(ctypes.c_int32)),
         ("flags", ctypes.c_uint32),
         ("gate", ctypes.c_int),
+        ("stages", ctypes.POINTER(Stages)),
     ]
 
 
@@ -90,7 +103,7 @@ def load_library(path: str = LIB_PATH):
         lib.kda_prefill_set_wait_limit.argtypes = [ctypes.c_int32]
         lib.kda_decode_step.restype = ctypes.c_int
         lib.kda_decode_step.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int,
-                                        ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp]
+                                        ctypes.c_int, ctypes.POINTER(Stages), vp, vp, vp, vp, vp, vp, vp, vp]
         if path == LIB_PATH:
             _lib = lib
         return lib
@@ -105,7 +118,7 @@ def version() -> int:
 
 
 def make_desc(num_seqs: int, total_tokens: int, num_heads: int, dk: int, dv: int, chunk: int, io_dtype: int,
-              cu_seqlens_host: Optional[Sequence[int]] = None, flags: int = 0, gate: int = 0):
+              cu_seqlens_host: Optional[Sequence[int]] = None, flags: int = 0, gate: int = 0, stages=None):
     """Build a kda_prefill_desc.  Returns (desc, keepalive) -- keep the second
     value alive while the desc is used (it owns the host offsets)."""
     keep = None
@@ -114,8 +127,8 @@ def make_desc(num_seqs: int, total_tokens: int, num_heads: int, dk: int, dv: int
         keep = (ctypes.c_int32 * len(cu_seqlens_host))(*[int(x) for x in cu_seqlens_host])
         ptr = ctypes.cast(keep, ctypes.POINTER(ctypes.c_int32))
     d = PrefillDesc(int(num_seqs), int(total_tokens), int(num_heads), int(dk), int(dv), int(chunk), int(io_dtype),
-                    ptr, int(flags), int(gate))
-    return d, keep
+                    ptr, int(flags), int(gate), ctypes.pointer(stages) if stages is not None else None)
+    return d, (keep, stages)
 
 
 def prefill_workspace_size(desc: PrefillDesc) -> int:
@@ -171,6 +184,19 @@ def _la_shape(gate: int, lead, dk: int):
     return None if gate == KDA_GATE_NONE else (tuple(lead) if gate == KDA_GATE_SCALAR else tuple(lead) + (dk,))
 
 
+def _stages(shape_o, dtype, device, l2norm_qk=False, gate_softplus=False, out_gate=None, norm_weight=None,
+            l2norm_eps=1e-6, norm_eps=1e-6):
+    """A kda_stages struct for the keyword arguments (None when no stage is
+    selected).  out_gate: tensor shaped like o in its dtype; norm_weight: [dv]
+    fp32 tensor."""
+    torch = _torch()
+    if not (l2norm_qk or gate_softplus or out_gate is not None or norm_weight is not None):
+        return None
+    return Stages(int(bool(l2norm_qk)), float(l2norm_eps), int(bool(gate_softplus)),
+                  _dev_ptr(norm_weight, "norm_weight", torch.float32, (shape_o[-1],), device),
+                  float(norm_eps), _dev_ptr(out_gate, "out_gate", dtype, shape_o, device))
+
+
 def _stream(stream):
     torch = _torch()
     return stream if stream is not None else torch.cuda.current_stream()
@@ -206,7 +232,7 @@ def clear_workspace_cache():
 
 def prefill(q, k, v, log_alpha, beta, cu_seqlens, S0=None, *, chunk: int = 64, o=None, S_T=None,
             cu_seqlens_host: Optional[Sequence[int]] = None, workspace=None, stream=None, want_state: bool = True,
-            one_stream: bool = False):
+            one_stream: bool = False, **stage_kw):
     """KDA chunked prefill over a packed batch.
 
     q, k: [T, H, dk]; v: [T, H, dv] (bf16 or fp32, same dtype); log_alpha: [T, H, dk]
@@ -215,7 +241,10 @@ def prefill(q, k, v, log_alpha, beta, cu_seqlens, S0=None, *, chunk: int = 64, o
     ``S_T`` may be passed as ``S0`` to update the state in place.
     ``one_stream`` selects the schedule that never leaves the caller's stream.
     ``log_alpha`` may also be [T, H] (one rate per head: Gated DeltaNet) or
-    None (no forget gate: DeltaNet).
+    None (no forget gate: DeltaNet).  Stage keywords (kda_stages):
+    ``l2norm_qk``, ``gate_softplus`` (log_alpha then holds the gate
+    projection's output), ``norm_weight`` ([dv] fp32), ``out_gate`` (like o),
+    ``l2norm_eps``, ``norm_eps``.
     """
     torch = _torch()
     lib = load_library()
@@ -234,8 +263,9 @@ def prefill(q, k, v, log_alpha, beta, cu_seqlens, S0=None, *, chunk: int = 64, o
         S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
     s = _stream(stream)
     gate = _gate(log_alpha, (T, H))
+    stg = _stages((T, H, dv), q.dtype, dev, **stage_kw)
     desc, keep = make_desc(N, T, H, dk, dv, chunk, dt, cu_seqlens_host,
-                           KDA_PREFILL_ONE_STREAM if one_stream else 0, gate)
+                           KDA_PREFILL_ONE_STREAM if one_stream else 0, gate, stg)
     need = int(lib.kda_prefill_workspace_size(ctypes.byref(desc)))
     if need == 0:
         st = lib.kda_prefill(ctypes.byref(desc), *([None] * 10), 0, None)
@@ -260,7 +290,8 @@ def prefill(q, k, v, log_alpha, beta, cu_seqlens, S0=None, *, chunk: int = 64, o
 
 
 def prefill_noalloc(q, k, v, log_alpha, beta, cu_seqlens, S0=None, *, chunk: int = 64, o=None, S_T=None,
-                    cu_seqlens_host: Optional[Sequence[int]] = None, stream=None, want_state: bool = True):
+                    cu_seqlens_host: Optional[Sequence[int]] = None, stream=None, want_state: bool = True,
+                    **stage_kw):
     """kda_prefill_noalloc: the prefill with the library's static per-GPU
     scratch as its workspace (no device allocation inside the call; the
     binding still allocates o and S_T unless they are passed in).  Same
@@ -282,7 +313,8 @@ def prefill_noalloc(q, k, v, log_alpha, beta, cu_seqlens, S0=None, *, chunk: int
     if S_T is None and want_state:
         S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
     gate = _gate(log_alpha, (T, H))
-    desc, keep = make_desc(N, T, H, dk, dv, chunk, dt, cu_seqlens_host, 0, gate)
+    desc, keep = make_desc(N, T, H, dk, dv, chunk, dt, cu_seqlens_host, 0, gate,
+                           _stages((T, H, dv), q.dtype, dev, **stage_kw))
     st = lib.kda_prefill_noalloc(ctypes.byref(desc),
                                  _dev_ptr(q, "q", None, (T, H, dk), dev), _dev_ptr(k, "k", None, (T, H, dk), dev),
                                  _dev_ptr(v, "v", None, (T, H, dv), dev),
@@ -330,11 +362,11 @@ def set_wait_limit(polls: int) -> int:
     return int(load_library().kda_prefill_set_wait_limit(int(polls)))
 
 
-def decode_step(q, k, v, log_alpha, beta, S, *, o=None, stream=None):
+def decode_step(q, k, v, log_alpha, beta, S, *, o=None, stream=None, **stage_kw):
     """One KDA step for B requests: q, k [B, H, dk]; v [B, H, dv]; log_alpha
     [B, H, dk] fp32 ([B, H] for one rate per head, None without a gate);
     beta [B, H] fp32; S [B, H, dk, dv] fp32 updated in place.  Returns o
-    [B, H, dv]."""
+    [B, H, dv].  Stage keywords as for ``prefill`` (out_gate [B, H, dv])."""
     torch = _torch()
     lib = load_library()
     if q.dim() != 3 or v.dim() != 3:
@@ -348,7 +380,9 @@ def decode_step(q, k, v, log_alpha, beta, S, *, o=None, stream=None):
     if o is None:
         o = torch.empty((B, H, dv), dtype=q.dtype, device=dev)
     gate = _gate(log_alpha, (B, H))
-    st = lib.kda_decode_step(B, H, dk, dv, dt, gate, _dev_ptr(q, "q", None, (B, H, dk), dev),
+    stg = _stages((B, H, dv), q.dtype, dev, **stage_kw)
+    st = lib.kda_decode_step(B, H, dk, dv, dt, gate, ctypes.pointer(stg) if stg is not None else None,
+                             _dev_ptr(q, "q", None, (B, H, dk), dev),
                              _dev_ptr(k, "k", None, (B, H, dk), dev), _dev_ptr(v, "v", None, (B, H, dv), dev),
                              _dev_ptr(log_alpha, "log_alpha", torch.float32, _la_shape(gate, (B, H), dk), dev),
                              _dev_ptr(beta, "beta", torch.float32, (B, H), dev),

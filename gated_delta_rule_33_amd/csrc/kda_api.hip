@@ -26,11 +26,19 @@ Range range(const void* p, size_t bytes) {
 }
 bool overlap(Range x, Range y) { return x.b != x.e && y.b != y.e && x.b < y.e && y.b < x.e; }
 
+// Stage arguments: epsilons must be positive where a stage uses them.
+bool stages_valid(const kda_stages* s) {
+  if (!s) return true;
+  if (s->l2norm_qk && !(s->l2norm_eps > 0.f)) return false;
+  if (s->norm_weight && !(s->norm_eps > 0.f)) return false;
+  return true;
+}
+
 // Checks the shape fields; fills the exact chunk count when host offsets exist.
 kda_status check_desc(const kda_prefill_desc* d, int64_t* max_chunks) {
   if (!d) return KDA_ERR_INVALID_ARGUMENT;
   if (d->num_seqs < 0 || d->total_tokens < 0 || d->num_heads < 1) return KDA_ERR_INVALID_ARGUMENT;
-  if (!dtype_valid(d->io_dtype) || !gate_valid(d->gate)) return KDA_ERR_INVALID_ARGUMENT;
+  if (!dtype_valid(d->io_dtype) || !gate_valid(d->gate) || !stages_valid(d->stages)) return KDA_ERR_INVALID_ARGUMENT;
   if (!dims_supported(d->dk, d->dv)) return KDA_ERR_UNSUPPORTED;
   if (d->chunk != 16 && d->chunk != 32 && d->chunk != 64) return KDA_ERR_UNSUPPORTED;
   if (d->num_seqs == 0 && d->total_tokens != 0) return KDA_ERR_INVALID_ARGUMENT;
@@ -97,6 +105,14 @@ kda_status prefill_checked(const kda_prefill_desc* d, const void* q, const void*
   const Range ins3[] = {rq, rk, rv, rla, rb, rcu, rs0};
   for (const Range& x : ins3)
     if (overlap(rws, x)) return KDA_ERR_INVALID_ARGUMENT;
+  if (d->stages) {
+    // the output stage rewrites o in place from o and the output gate
+    const Range rg = range(d->stages->out_gate, d->stages->out_gate ? T * H * d->dv * es : 0),
+                rw = range(d->stages->norm_weight, d->stages->norm_weight ? d->dv * 4 : 0);
+    const Range outs[] = {ro, rst, rws};
+    for (const Range& x : outs)
+      if (overlap(rg, x) || overlap(rw, x)) return KDA_ERR_INVALID_ARGUMENT;
+  }
   const hipError_t e = launch_prefill(p, q, k, v, log_alpha, beta, cu_seqlens, S0, o, S_T, workspace,
                                       static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KDA_OK : KDA_ERR_DEVICE;
@@ -157,9 +173,10 @@ kda_status kda_prefill_recovered(const kda_prefill_desc* d, const void* workspac
 int32_t kda_prefill_set_wait_limit(int32_t polls) { return kda::set_prefill_wait_polls(polls); }
 
 kda_status kda_decode_step(int32_t B, int32_t H, int32_t dk, int32_t dv, kda_dtype io_dtype, kda_gate gate,
-                           const void* q, const void* k, const void* v, const float* log_alpha, const float* beta,
-                           float* S, void* o, void* stream) {
-  if (B < 0 || H < 1 || !dtype_valid(io_dtype) || !gate_valid(gate)) return KDA_ERR_INVALID_ARGUMENT;
+                           const kda_stages* stages, const void* q, const void* k, const void* v,
+                           const float* log_alpha, const float* beta, float* S, void* o, void* stream) {
+  if (B < 0 || H < 1 || !dtype_valid(io_dtype) || !gate_valid(gate) || !stages_valid(stages))
+    return KDA_ERR_INVALID_ARGUMENT;
   if (!dims_supported(dk, dv)) return KDA_ERR_UNSUPPORTED;
   if (B == 0) return KDA_OK;
   const size_t gw = gate_width(gate, dk);
@@ -174,8 +191,13 @@ kda_status kda_decode_step(int32_t B, int32_t H, int32_t dk, int32_t dv, kda_dty
   for (const Range& x : others)
     if (overlap(rs, x) || overlap(ro, x)) return KDA_ERR_INVALID_ARGUMENT;
   if (overlap(rs, ro)) return KDA_ERR_INVALID_ARGUMENT;
-  const hipError_t e = kda::launch_decode(io_dtype, gate, dk, dv, static_cast<int>(BH), q, k, v, log_alpha, beta, S,
-                                          o, static_cast<hipStream_t>(stream));
+  if (stages) {
+    const Range rg = range(stages->out_gate, stages->out_gate ? n * dv * es : 0),
+                rw = range(stages->norm_weight, stages->norm_weight ? static_cast<size_t>(dv) * 4 : 0);
+    if (overlap(rg, rs) || overlap(rg, ro) || overlap(rw, rs) || overlap(rw, ro)) return KDA_ERR_INVALID_ARGUMENT;
+  }
+  const hipError_t e = kda::launch_decode(io_dtype, gate, stages, dk, dv, static_cast<int>(BH), q, k, v, log_alpha,
+                                          beta, S, o, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KDA_OK : KDA_ERR_DEVICE;
 }
 

@@ -91,6 +91,35 @@ __device__ __forceinline__ void store4(bf16_t* p, f32x4 x) {
   *reinterpret_cast<uint2*>(p) = u;
 }
 
+// -softplus(z) = -log(1 + e^z) without overflow: -(max(z, 0) + log1p(e^{-|z|})),
+// with log1p(t) taken as t (1 - t/2) below t = 2^-10 (error below t^3 / 3)
+__device__ __forceinline__ float neg_softplus(float z) {
+  const float t = __expf(-fabsf(z));
+  const float l = t < 0x1p-10f ? t * (1.f - 0.5f * t) : __logf(1.f + t);
+  return -(fmaxf(z, 0.f) + l);
+}
+
+// One DPP move (bound_ctrl: lanes without a source read 0).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over aligned groups of N consecutive lanes (N = 4, 8, 16 or 32) with
+// DPP moves inside each row of 16 lanes and one swizzle across the two rows
+// of a 32-lane half; every lane of a group receives the group's sum.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 4 || N == 8 || N == 16 || N == 32, "group of 4 to 32 lanes");
+  x += dpp_mov<0xB1>(x);                        // quad_perm [1,0,3,2]
+  x += dpp_mov<0x4E>(x);                        // quad_perm [2,3,0,1]: quad sums
+  if constexpr (N >= 8) x += dpp_mov<0x141>(x);  // row_half_mirror: sums over 8 lanes
+  if constexpr (N >= 16) x += dpp_mov<0x140>(x); // row_mirror: sums over 16 lanes
+  if constexpr (N == 32)  // xor 16 within each 32-lane half (and_mask 0x1F, xor_mask 0x10)
+    x += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
+  return x;
+}
+
 // Cross-lane xor shuffle within a 64-wide wavefront.
 __device__ __forceinline__ float shfl_xor(float x, int m) { return __shfl_xor(x, m, 64); }
 

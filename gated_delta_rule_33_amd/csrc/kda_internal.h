@@ -10,7 +10,7 @@
 namespace kda {
 
 // Decode: one recurrence step for B*H states (all pointers device).
-hipError_t launch_decode(kda_dtype dt, kda_gate gate, int dk, int dv, int BH, const void* q, const void* k, const void* v,
+hipError_t launch_decode(kda_dtype dt, kda_gate gate, const kda_stages* stages, int dk, int dv, int BH, const void* q, const void* k, const void* v,
                          const float* la, const float* beta, float* S, void* o, hipStream_t stream);
 
 // Prefill workspace carve-up, computed on the host.
@@ -20,6 +20,11 @@ struct PrefillPlan {
   int CL;  // tokens per chunk (16, 32 or 64; at most C)
   kda_dtype dt;
   kda_gate gate;
+  // input and output stages (kda_stages)
+  int l2norm_qk, gate_softplus;
+  float l2norm_eps, norm_eps;
+  const float* norm_weight;
+  const void* out_gate;
   int64_t max_chunks;  // upper bound (exact when the host offsets are known)
   int sort;            // 1: longest-first order is computed on the device
   // byte offsets inside the workspace

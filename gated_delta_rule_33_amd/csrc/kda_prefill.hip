@@ -223,6 +223,82 @@ __global__ void ready_kernel(int32_t* ready, int j) {
   if (threadIdx.x == 0) __hip_atomic_store(ready, j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Output stage over o in place: head-wise RMSNorm over the value channels
+// (when a weight is given), then the sigmoid output gate (when its
+// pre-activation is given).  A row of DV values is LPR lanes, each holding
+// 16 bytes (8 bf16 or 4 fp32); a wave covers 64 / LPR rows per step.  The
+// state pass's value tiles split dv, so the norm, which spans a whole row,
+// runs as this pass.
+template <typename T, int DV>
+__global__ __launch_bounds__(256) void out_stage_kernel(T* __restrict__ o, const T* __restrict__ zo,
+                                                        const float* __restrict__ w, float eps, int64_t rows) {
+  constexpr int EPL = 16 / static_cast<int>(sizeof(T));  // elements per lane
+  constexpr int LPR = DV / EPL;                           // lanes per row
+  constexpr int RPW = 64 / LPR;                           // rows per wave step
+  static_assert(LPR >= 4 && LPR <= 32 && 64 % LPR == 0, "row geometry");
+  const int lane = threadIdx.x & 63;
+  const int sub = lane / LPR, c0 = (lane % LPR) * EPL;
+  const int64_t step = static_cast<int64_t>(gridDim.x) * 4 * RPW;
+  for (int64_t base = (static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * RPW; base < rows; base += step) {
+    const int64_t row = base + sub;
+    const bool live = row < rows;
+    const int64_t off = (live ? row : 0) * DV + c0;
+    float x[EPL];
+    if constexpr (sizeof(T) == 2) {
+      const uint4 u = *reinterpret_cast<const uint4*>(o + off);
+      const uint32_t wds[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[2 * j] = __uint_as_float(wds[j] << 16);
+        x[2 * j + 1] = __uint_as_float(wds[j] & 0xFFFF0000u);
+      }
+    } else {
+      const f32x4 u = *reinterpret_cast<const f32x4*>(o + off);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[j] = u[j];
+    }
+    if (w) {
+      float ss = 0.f;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) ss += x[j] * x[j];
+      ss = group_sum<LPR>(ss);
+      const float r = 1.f / __builtin_sqrtf(ss * (1.f / DV) + eps);
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) x[j] *= r * w[c0 + j];
+    }
+    if (zo) {
+      float z[EPL];
+      if constexpr (sizeof(T) == 2) {
+        const uint4 u = *reinterpret_cast<const uint4*>(zo + off);
+        const uint32_t wds[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          z[2 * j] = __uint_as_float(wds[j] << 16);
+          z[2 * j + 1] = __uint_as_float(wds[j] & 0xFFFF0000u);
+        }
+      } else {
+        const f32x4 u = *reinterpret_cast<const f32x4*>(zo + off);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) z[j] = u[j];
+      }
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) x[j] *= 1.f / (1.f + __expf(-z[j]));
+    }
+    if (live) {
+      if constexpr (sizeof(T) == 2) {
+        uint4 u;
+        u.x = f32x2_to_bf16x2(x[0], x[1]);
+        u.y = f32x2_to_bf16x2(x[2], x[3]);
+        u.z = f32x2_to_bf16x2(x[4], x[5]);
+        u.w = f32x2_to_bf16x2(x[6], x[7]);
+        *reinterpret_cast<uint4*>(o + off) = u;
+      } else {
+        *reinterpret_cast<f32x4*>(o + off) = f32x4{x[0], x[1], x[2], x[3]};
+      }
+    }
+  }
+}
+
 // Overlapped schedule with S_T == S0: the state pass leaves the final states
 // in a workspace carry (S0 must survive until the call knows it needs no
 // recovery); this copies them to S_T unless the flag word is set, in which
@@ -438,7 +514,10 @@ struct PrepLds {
   // reused by later phases: the pair products read them while region 2
   // already stages P)
   static constexpr size_t o5 = o4 + static_cast<size_t>(C) * 4;
-  static constexpr size_t total = o5 + static_cast<size_t>(3 * C + NB) * 4;
+  // then per-row inverse norms of k and q (input stage), read by the exact
+  // diagonal path
+  static constexpr size_t o6 = o5 + static_cast<size_t>(3 * C + NB) * 4;
+  static constexpr size_t total = o6 + static_cast<size_t>(2 * C) * 4;
 };
 
 // byte offset of element (row, c) in an unpadded LDS tile with RB-byte rows,
@@ -524,14 +603,16 @@ constexpr int prep_waves_per_eu() {
 // products are the plain k k^T and q k^T products scaled element by element
 // by e^{g_r - g_s} (formed from sums over the rows in between), and without
 // a gate all factors are 1.
-template <typename T, int C, int DK, int G>
+// IN selects the input stage (L2-normalised q and k, gate activation).
+template <typename T, int C, int DK, int G, bool IN>
 __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(prep_waves_per_eu<T, C, DK>())))
 void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                    const float* __restrict__ la, const float* __restrict__ beta,
                                                    const int32_t* __restrict__ cu,
                                                    const int32_t* __restrict__ chunk_off, int N, int H,
                                                    unsigned char* __restrict__ ws, int cbase, int count,
-                                                   int32_t* publish, int published, const int* guard, int cl) {
+                                                   int32_t* publish, int published, const int* guard, int cl,
+                                                   int l2n, float l2eps, int softplus_gate) {
   typedef PrepLds<T, C, DK> L;
   typedef Blk<T, C, DK> B;
   typedef mma16<T> M;
@@ -561,6 +642,7 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
   float* drow = lrow + C;
   float* srow = drow + C;
   float* dsum = srow + C;
+  float* rinv = reinterpret_cast<float*>(smem + L::o6);  // [2][C]: 1/||k_r||, 1/||q_r|| (input stage)
   constexpr bool kChannel = G == KDA_GATE_CHANNEL, kScalar = G == KDA_GATE_SCALAR;
 
   // thread owns channels c4..c4+3 of rows r0..r0+RPT-1 in the elementwise steps
@@ -645,10 +727,36 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
   f32x4 lg[RPT], kv[RPT], qv[RPT];
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
-    if constexpr (G == KDA_GATE_NONE) lg[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    else lg[i] = r0 + i < len ? cur.lg[i] * kLog2e : f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (G == KDA_GATE_NONE) {
+      lg[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    } else {
+      f32x4 la4 = cur.lg[i];
+      if (IN && softplus_gate) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) la4[j] = neg_softplus(la4[j]);
+      }
+      lg[i] = r0 + i < len ? la4 * kLog2e : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     kv[i] = cvt4(cur.kr[i]);
     qv[i] = cvt4(cur.qr[i]);
+  }
+  // input stage: each row of k and q divided by max(its norm, eps); the
+  // NCG threads of a row are consecutive lanes of one wave
+  if (IN && l2n) {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      float sk = kv[i][0] * kv[i][0] + kv[i][1] * kv[i][1] + kv[i][2] * kv[i][2] + kv[i][3] * kv[i][3];
+      float sq = qv[i][0] * qv[i][0] + qv[i][1] * qv[i][1] + qv[i][2] * qv[i][2] + qv[i][3] * qv[i][3];
+      sk = group_sum<NCG>(sk);
+      sq = group_sum<NCG>(sq);
+      const float ik = 1.f / fmaxf(__builtin_sqrtf(sk), l2eps), iq = 1.f / fmaxf(__builtin_sqrtf(sq), l2eps);
+      kv[i] *= ik;
+      qv[i] *= iq;
+      if (cg == 0) {
+        rinv[r0 + i] = ik;
+        rinv[C + r0 + i] = iq;
+      }
+    }
   }
   if (tid < C) bet[tid] = cur.bt;
 
@@ -840,8 +948,13 @@ void prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
         m &= m - 1;
         const int row = 16 * I + n;
         const size_t e = (static_cast<size_t>(t0 + min(row, len - 1)) * H + h) * DK + ch;
-        const float an = row < len ? __builtin_amdgcn_exp2f(la[e] * kLog2e) : 1.f;
-        const float kn = io<T>::load(k + e), qn = io<T>::load(q + e);
+        const float lz = (IN && softplus_gate) ? neg_softplus(la[e]) : la[e];
+        const float an = row < len ? __builtin_amdgcn_exp2f(lz * kLog2e) : 1.f;
+        float kn = io<T>::load(k + e), qn = io<T>::load(q + e);
+        if (IN && l2n) {
+          kn *= rinv[row];
+          qn *= rinv[C + row];
+        }
         float prod = 1.f, ef[4] = {1.f, 1.f, 1.f, 1.f}, kr[4] = {0.f, 0.f, 0.f, 0.f}, qr[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
@@ -1760,6 +1873,13 @@ bool make_prefill_plan(const kda_prefill_desc* d, int64_t max_chunks, PrefillPla
   p->CL = d->chunk;
   p->dt = d->io_dtype;
   p->gate = d->gate;
+  const kda_stages* sg = d->stages;
+  p->l2norm_qk = sg && sg->l2norm_qk ? 1 : 0;
+  p->l2norm_eps = sg ? sg->l2norm_eps : 0.f;
+  p->gate_softplus = sg && sg->gate_softplus && d->gate != KDA_GATE_NONE ? 1 : 0;
+  p->norm_weight = sg ? sg->norm_weight : nullptr;
+  p->norm_eps = sg ? sg->norm_eps : 0.f;
+  p->out_gate = sg ? sg->out_gate : nullptr;
   p->max_chunks = max_chunks;
   p->sort = d->num_seqs <= 8192;
   const size_t slots = static_cast<size_t>(max_chunks) * d->num_heads;
@@ -1919,7 +2039,7 @@ static hipError_t pipe_streams(int64_t scan_wgs, PipeStreams** out) {
   return hipSuccess;
 }
 
-template <typename T, int C, int DK, int DV, int G>
+template <typename T, int C, int DK, int DV, int G, bool IN>
 static hipError_t launch_prefill_t(const PrefillPlan& p, const void* q, const void* k, const void* v,
                                    const float* la, const float* beta, const int32_t* cu, const float* S0,
                                    void* o, float* S_T, void* ws, hipStream_t st) {
@@ -1938,14 +2058,15 @@ static hipError_t launch_prefill_t(const PrefillPlan& p, const void* q, const vo
   // use (LDS-limited), each walking (chunk, head) items.
   auto prep = [&](int64_t cbase, int64_t count, hipStream_t s, int cus, int32_t* publish, int published,
                   const int* guard) -> hipError_t {
-    hipError_t r = set_lds_limit(reinterpret_cast<const void*>(&prep_kernel<T, C, DK, G>), lp);
+    hipError_t r = set_lds_limit(reinterpret_cast<const void*>(&prep_kernel<T, C, DK, G, IN>), lp);
     if (r != hipSuccess) return r;
     const int64_t per_cu = (160 * 1024) / static_cast<int64_t>(lp) > 0 ? (160 * 1024) / static_cast<int64_t>(lp) : 1;
     const int64_t items = count * p.H;
     const int64_t grid = items < per_cu * cus ? items : per_cu * cus;
-    hipLaunchKernelGGL((prep_kernel<T, C, DK, G>), dim3(static_cast<unsigned>(grid)), dim3(kPrepThreads), lp, s,
+    hipLaunchKernelGGL((prep_kernel<T, C, DK, G, IN>), dim3(static_cast<unsigned>(grid)), dim3(kPrepThreads), lp, s,
                        static_cast<const T*>(q), static_cast<const T*>(k), la, beta, cu, chunk_off, p.N, p.H,
-                       blocks, static_cast<int>(cbase), static_cast<int>(count), publish, published, guard, p.CL);
+                       blocks, static_cast<int>(cbase), static_cast<int>(count), publish, published, guard, p.CL,
+                       p.l2norm_qk, p.l2norm_eps, p.gate_softplus);
     return hipGetLastError();
   };
   int cus = 0;
@@ -2019,11 +2140,15 @@ template <typename T, int C, int DK, int DV>
 static hipError_t dispatch_gate(const PrefillPlan& p, const void* q, const void* k, const void* v, const float* la,
                                 const float* beta, const int32_t* cu, const float* S0, void* o, float* S_T,
                                 void* ws, hipStream_t st) {
+  const bool in = p.l2norm_qk || p.gate_softplus;
   if (p.gate == KDA_GATE_CHANNEL)
-    return launch_prefill_t<T, C, DK, DV, KDA_GATE_CHANNEL>(p, q, k, v, la, beta, cu, S0, o, S_T, ws, st);
+    return in ? launch_prefill_t<T, C, DK, DV, KDA_GATE_CHANNEL, true>(p, q, k, v, la, beta, cu, S0, o, S_T, ws, st)
+              : launch_prefill_t<T, C, DK, DV, KDA_GATE_CHANNEL, false>(p, q, k, v, la, beta, cu, S0, o, S_T, ws, st);
   if (p.gate == KDA_GATE_SCALAR)
-    return launch_prefill_t<T, C, DK, DV, KDA_GATE_SCALAR>(p, q, k, v, la, beta, cu, S0, o, S_T, ws, st);
-  return launch_prefill_t<T, C, DK, DV, KDA_GATE_NONE>(p, q, k, v, la, beta, cu, S0, o, S_T, ws, st);
+    return in ? launch_prefill_t<T, C, DK, DV, KDA_GATE_SCALAR, true>(p, q, k, v, la, beta, cu, S0, o, S_T, ws, st)
+              : launch_prefill_t<T, C, DK, DV, KDA_GATE_SCALAR, false>(p, q, k, v, la, beta, cu, S0, o, S_T, ws, st);
+  return in ? launch_prefill_t<T, C, DK, DV, KDA_GATE_NONE, true>(p, q, k, v, la, beta, cu, S0, o, S_T, ws, st)
+            : launch_prefill_t<T, C, DK, DV, KDA_GATE_NONE, false>(p, q, k, v, la, beta, cu, S0, o, S_T, ws, st);
 }
 
 template <typename T, int C>
@@ -2046,12 +2171,29 @@ static hipError_t dispatch_chunk(const PrefillPlan& p, const void* q, const void
   return hipErrorInvalidValue;
 }
 
+template <typename T>
+static hipError_t launch_out_stage(const PrefillPlan& p, void* o, hipStream_t st) {
+  const int64_t rows = static_cast<int64_t>(p.T) * p.H;
+  if (rows == 0) return hipSuccess;
+  const int64_t want = (rows + 15) / 16;  // 4 waves of at least 4 rows per workgroup step
+  const unsigned grid = static_cast<unsigned>(want < 8192 ? want : 8192);
+  if (p.dv == 128)
+    hipLaunchKernelGGL((out_stage_kernel<T, 128>), dim3(grid), dim3(256), 0, st, static_cast<T*>(o),
+                       static_cast<const T*>(p.out_gate), p.norm_weight, p.norm_eps, rows);
+  else
+    hipLaunchKernelGGL((out_stage_kernel<T, 64>), dim3(grid), dim3(256), 0, st, static_cast<T*>(o),
+                       static_cast<const T*>(p.out_gate), p.norm_weight, p.norm_eps, rows);
+  return hipGetLastError();
+}
+
 hipError_t launch_prefill(const PrefillPlan& p, const void* q, const void* k, const void* v, const float* la,
                           const float* beta, const int32_t* cu, const float* S0, void* o, float* S_T,
                           void* workspace, hipStream_t stream) {
-  if (p.dt == KDA_BF16)
-    return dispatch_chunk<bf16_t>(p, q, k, v, la, beta, cu, S0, o, S_T, workspace, stream);
-  return dispatch_chunk<float>(p, q, k, v, la, beta, cu, S0, o, S_T, workspace, stream);
+  const bool bf = p.dt == KDA_BF16;
+  hipError_t e = bf ? dispatch_chunk<bf16_t>(p, q, k, v, la, beta, cu, S0, o, S_T, workspace, stream)
+                    : dispatch_chunk<float>(p, q, k, v, la, beta, cu, S0, o, S_T, workspace, stream);
+  if (e != hipSuccess || (!p.norm_weight && !p.out_gate)) return e;
+  return bf ? launch_out_stage<bf16_t>(p, o, stream) : launch_out_stage<float>(p, o, stream);
 }
 
 }  // namespace kda

@@ -76,6 +76,27 @@ typedef enum {
   KDA_GATE_NONE = 2      /* no forget gate, alpha = 1 (DeltaNet); log_alpha unused, may be NULL */
 } kda_gate;
 
+/* Input and output stages fused around the recurrence.  The deep-read
+   report, section 3.2, places KDA between an input side (q and k
+   L2-normalised per head; the forget gate out of a low-rank projection) and
+   an output side (a head-wise RMSNorm and a low-rank, data-dependent sigmoid
+   output gate).  The projections themselves (and the short convolutions with
+   Swish) produce these stages' inputs and are outside the library.  Every
+   field at zero/NULL leaves the stage out; a NULL kda_stages pointer leaves
+   all out. */
+typedef struct {
+  int32_t l2norm_qk;        /* nonzero: q and k are raw; each (token, head) vector is
+                               divided by max(||x||_2, l2norm_eps) before use */
+  float l2norm_eps;         /* > 0 when l2norm_qk */
+  int32_t gate_softplus;    /* nonzero: log_alpha holds the gate projection's output z;
+                               the kernels use log alpha = -softplus(z) (any finite z) */
+  const float* norm_weight; /* [dv] fp32 DEVICE: o <- o / sqrt(mean_j o_j^2 + norm_eps) *
+                               norm_weight per (token, head); NULL: no norm */
+  float norm_eps;           /* > 0 when norm_weight is given */
+  const void* out_gate;     /* DEVICE, io dtype, shaped like o: z_o; o <- o * sigmoid(z_o)
+                               after the norm; NULL: no output gate */
+} kda_stages;
+
 /* kda_prefill_desc.flags */
 enum {
   /* Run the chunk preparation and the state pass one after the other on the
@@ -99,6 +120,7 @@ typedef struct {
                                      launch exactly; may be NULL */
   uint32_t flags;        /* KDA_PREFILL_* bits; 0 for the default schedule */
   kda_gate gate;         /* form of log_alpha; KDA_GATE_CHANNEL for KDA */
+  const kda_stages* stages; /* optional HOST struct: input/output stages; may be NULL */
 } kda_prefill_desc;
 
 /*
@@ -133,6 +155,10 @@ size_t kda_prefill_workspace_size(const kda_prefill_desc* desc);
  *   workspace  >= kda_prefill_workspace_size(desc) bytes, 256-byte aligned;
  *              its contents on entry are ignored and on return undefined.
  *   stream     hipStream_t or NULL.
+ *   desc->stages  optional input/output stages (kda_stages): with an output
+ *              stage, o holds its result (the stage runs as one more pass over
+ *              o on `stream`: the state pass's value tiles split dv, which
+ *              the head-wise norm spans); the output gate is [T_tot, H, dv].
  *
  * Streams: the work is ordered on `stream`.  For few (sequence, head) pairs
  * (N * H * dv / 32 <= 128), unless flags has KDA_PREFILL_ONE_STREAM, the call
@@ -215,12 +241,15 @@ int32_t kda_prefill_set_wait_limit(int32_t polls);
  *   beta       [B, H]          float32
  *   S          [B, H, dk, dv]  float32, read as S_{t-1} and overwritten with S_t
  *   o          [B, H, dv]      io_dtype, written
+ *   stages     optional HOST struct (see kda_stages); the output gate is [B, H, dv]
  *
  * Errors: KDA_ERR_INVALID_ARGUMENT (null pointer with B > 0, B < 0, H < 1,
- * unknown gate), KDA_ERR_UNSUPPORTED (dk/dv not in {64,128}), KDA_ERR_DEVICE.  B == 0 is a
+ * unknown gate, a stage with a non-positive epsilon or an output gate that
+ * overlaps S or o), KDA_ERR_UNSUPPORTED (dk/dv not in {64,128}), KDA_ERR_DEVICE.  B == 0 is a
  * no-op.  S must not overlap any other argument.
  */
 kda_status kda_decode_step(int32_t B, int32_t H, int32_t dk, int32_t dv, kda_dtype io_dtype, kda_gate gate,
+                           const kda_stages* stages,
                            const void* q, const void* k, const void* v,
                            const float* log_alpha, const float* beta,
                            float* S, void* o, void* stream);

@@ -197,6 +197,39 @@ def make_prefill(lengths, H: int, dk: int, dv: int, io_dtype: str, seed: int,
                          io_dtype=io_dtype, chunk=chunk, gate=gate)
 
 
+@dataclasses.dataclass
+class StageInputs:
+    """Inputs of the input and output stages: raw q and k (the workload's
+    unit vectors scaled per (token, head) by a factor in [0.25, 4), then
+    rounded to the io dtype), the gate projection's output z (the standard
+    normal draw whose -softplus the workload's log_alpha is; same shape as
+    the gate), the output gate's pre-activation z_o ~ N(0, 1) shaped like o
+    (rounded to the io dtype) and an RMSNorm weight ~ U[0.5, 1.5) per value
+    channel."""
+    q_raw: np.ndarray
+    k_raw: np.ndarray
+    z_gate: Optional[np.ndarray]
+    z_out: np.ndarray
+    norm_weight: np.ndarray
+
+
+def make_stage_inputs(w: "PrefillInputs", seed: int, z_gate=None) -> StageInputs:
+    """Stage inputs for a prefill (or decode step) input set ``w``; ``z_gate``
+    is the gate projection output when already known (else drawn)."""
+    rng = np.random.Generator(np.random.PCG64([seed, _S0_STREAM + 1]))
+    T, H, dk = w.q.shape
+    dv = w.v.shape[-1]
+    rnd = bf16_round if w.io_dtype == "bf16" else (lambda x: x.astype(np.float32))
+    sq = rng.uniform(0.25, 4.0, size=(T, H, 1)).astype(np.float32)
+    sk = rng.uniform(0.25, 4.0, size=(T, H, 1)).astype(np.float32)
+    q_raw, k_raw = rnd(w.q * sq), rnd(w.k * sk)
+    if z_gate is None and w.log_alpha is not None:
+        z_gate = rng.standard_normal(w.log_alpha.shape, dtype=np.float32)
+    z_out = rnd(rng.standard_normal((T, H, dv), dtype=np.float32))
+    nw = rng.uniform(0.5, 1.5, size=dv).astype(np.float32)
+    return StageInputs(q_raw, k_raw, z_gate, z_out, nw)
+
+
 def _loguniform_lengths(n: int, lo: int, hi: int):
     def draw(rng):
         u = rng.uniform(math.log(lo), math.log(hi), size=n)

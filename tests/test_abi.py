@@ -51,7 +51,9 @@ def test_workspace_size():
     assert 0 < exact <= bound
     for bad in (dict(dk=96), dict(chunk=48), dict(num_heads=0), dict(total_tokens=-1), dict(io_dtype=7),
                 dict(cu_seqlens_host=[0, 60, 99]), dict(cu_seqlens_host=[1, 60, 100]),
-                dict(cu_seqlens_host=[0, 70, 60]), dict(flags=2), dict(flags=1 << 31), dict(gate=3), dict(gate=-1)):
+                dict(cu_seqlens_host=[0, 70, 60]), dict(flags=2), dict(flags=1 << 31), dict(gate=3), dict(gate=-1),
+                dict(stages=kda.Stages(1, -1e-6, 0, None, 0.0, None)),
+                dict(stages=kda.Stages(0, 0.0, 0, FAKE, 0.0, None))):
         d3, k3 = desc(**bad)
         assert kda.prefill_workspace_size(d3) == 0, bad
 
@@ -98,7 +100,8 @@ def test_prefill_validation_codes():
 
 def test_decode_validation_codes():
     lib = kda.load_library()
-    f = lambda *a: lib.kda_decode_step(*a, None)
+    def f(B, H, dk, dv, dt, gate, *ptrs, stages=None):
+        return lib.kda_decode_step(B, H, dk, dv, dt, gate, ctypes.byref(stages) if stages else None, *ptrs, None)
     ptrs = [FAKE + (i << 30) for i in range(7)]
     CH, SC = kda.KDA_GATE_CHANNEL, kda.KDA_GATE_SCALAR
     assert f(-1, 2, 128, 128, kda.KDA_BF16, CH, *ptrs) == kda.KDA_ERR_INVALID_ARGUMENT
@@ -120,6 +123,13 @@ def test_decode_validation_codes():
     bad = list(ptrs)
     bad[5] = ptrs[3] + 4 * 128 * 8 - 4  # S overlaps the last word of a [4, 2, 128] log_alpha
     assert f(4, 2, 128, 128, kda.KDA_BF16, CH, *bad) == kda.KDA_ERR_INVALID_ARGUMENT
+    # stages: a used epsilon must be positive; the output gate must not overlap S or o
+    assert f(4, 2, 128, 128, kda.KDA_BF16, CH, *ptrs, stages=kda.Stages(1, 0.0, 0, None, 0.0, None)) \
+        == kda.KDA_ERR_INVALID_ARGUMENT
+    assert f(4, 2, 128, 128, kda.KDA_BF16, CH, *ptrs, stages=kda.Stages(0, 0.0, 0, FAKE + (20 << 30), -1.0, None)) \
+        == kda.KDA_ERR_INVALID_ARGUMENT
+    assert f(4, 2, 128, 128, kda.KDA_BF16, CH, *ptrs, stages=kda.Stages(0, 0.0, 0, None, 0.0, ptrs[6] + 2)) \
+        == kda.KDA_ERR_INVALID_ARGUMENT
 
 
 
