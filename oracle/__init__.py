@@ -13,6 +13,9 @@ Two independent definitions live here:
   section 2.3 (per-channel diagonal forget gate; forget, erase along k, write
   beta k v^T, in that order) and the zhaixingw.cn explainer's KDA section
   (one forget rate per key channel).
+* ``backward`` -- the reverse-mode derivative of that recurrence (same C
+  file), for the loss sum_t <dO_t, o_t> + <dS_T, S_T>: the chain rule taken
+  through the forward loop's lines in reverse order, token by token.
 * ``brute.unified_form`` -- the unified recurrent form of the report's
   section 2.4 / 6.1 (o_t as a sum over j of q_t^T times the product of the
   transition matrices A_i times k_j v_j^T), evaluated with explicit dk x dk
@@ -58,6 +61,10 @@ def load_library(path: str):
     lib.kda_oracle_decode_step.argtypes = [
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
         dp, dp, dp, dp, dp, dp, dp, ctypes.c_int]
+    lib.kda_oracle_backward.restype = ctypes.c_int
+    lib.kda_oracle_backward.argtypes = [
+        ctypes.c_int, ctypes.POINTER(ctypes.c_int32), ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int]
     return lib
 
 
@@ -130,3 +137,38 @@ def decode_step(q, k, v, log_alpha, beta, S, threads: int = 0, lib=None, inplace
     if used < 0:
         raise ValueError("oracle rejected its arguments")
     return o, S
+
+
+def backward(q, k, v, log_alpha, beta, cu_seqlens, S0, dO, dS_T=None, threads: int = 0, lib=None):
+    """Gradients of L = sum <dO, o> + <dS_T, S_T> through the recurrence.
+
+    Shapes as for ``prefill`` (log_alpha per channel, [T_tot, H, dk]); dO like
+    o, dS_T like S_T (None = zero).  Returns a dict with dq, dk, dv,
+    dlog_alpha, dbeta ([T_tot, H]) and dS0 ([N, H, dk, dv]), float64.
+    """
+    q, k, v, la, b, dO = _f64(q), _f64(k), _f64(v), _f64(log_alpha), _f64(beta), _f64(dO)
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+    T_tot, H, dk = q.shape
+    dv = v.shape[2]
+    N = cu.shape[0] - 1
+    assert k.shape == (T_tot, H, dk) and la.shape == (T_tot, H, dk)
+    assert v.shape == (T_tot, H, dv) and b.shape == (T_tot, H) and dO.shape == (T_tot, H, dv)
+    assert int(cu[-1]) == T_tot
+    s0 = None if S0 is None else _f64(S0)
+    dst = None if dS_T is None else _f64(dS_T)
+    for x in (s0, dst):
+        if x is not None:
+            assert x.shape == (N, H, dk, dv)
+    out = {"dq": np.zeros((T_tot, H, dk)), "dk": np.zeros((T_tot, H, dk)), "dv": np.zeros((T_tot, H, dv)),
+           "dlog_alpha": np.zeros((T_tot, H, dk)), "dbeta": np.zeros((T_tot, H)),
+           "dS0": np.zeros((N, H, dk, dv))}
+    null = ctypes.POINTER(ctypes.c_double)()
+    used = (lib or _load()).kda_oracle_backward(
+        N, cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), H, dk, dv,
+        _ptr(q), _ptr(k), _ptr(v), _ptr(la), _ptr(b), _ptr(s0) if s0 is not None else null,
+        _ptr(dO), _ptr(dst) if dst is not None else null,
+        _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dlog_alpha"]), _ptr(out["dbeta"]),
+        _ptr(out["dS0"]), int(threads))
+    if used < 0:
+        raise ValueError("oracle rejected its arguments")
+    return out
