@@ -9,6 +9,7 @@ these functions raise.
     o, S_T = prefill(q, k, v, log_alpha, beta, cu_seqlens, S0=None)
     o      = decode_step(q, k, v, log_alpha, beta, S)      # S updated in place
     prefill_recovered(...)   # did the last overlapped call fall back?
+    g = prefill_backward(q, k, v, log_alpha, beta, cu_seqlens, S0, dO, dS_T)
 """
 from __future__ import annotations
 
@@ -33,7 +34,8 @@ KDA_GATE_SCALAR = 1
 KDA_GATE_NONE = 2
 
 EXPORTED = ("kda_prefill", "kda_prefill_workspace_size", "kda_prefill_noalloc", "kda_prefill_recovered",
-            "kda_prefill_set_wait_limit", "kda_decode_step", "kda_status_string", "kda_version")
+            "kda_prefill_set_wait_limit", "kda_decode_step", "kda_prefill_backward_workspace_size",
+            "kda_prefill_backward", "kda_status_string", "kda_version")
 NOALLOC_SCRATCH_BYTES = 256 << 20  # KDA_NOALLOC_SCRATCH_BYTES
 
 
@@ -101,6 +103,10 @@ def load_library(path: str = LIB_PATH):
         lib.kda_prefill_recovered.argtypes = [ctypes.POINTER(PrefillDesc), vp, ctypes.POINTER(ctypes.c_int32), vp]
         lib.kda_prefill_set_wait_limit.restype = ctypes.c_int32
         lib.kda_prefill_set_wait_limit.argtypes = [ctypes.c_int32]
+        lib.kda_prefill_backward_workspace_size.restype = ctypes.c_size_t
+        lib.kda_prefill_backward_workspace_size.argtypes = [ctypes.POINTER(PrefillDesc)]
+        lib.kda_prefill_backward.restype = ctypes.c_int
+        lib.kda_prefill_backward.argtypes = [ctypes.POINTER(PrefillDesc)] + [vp] * 16 + [ctypes.c_size_t, vp]
         lib.kda_decode_step.restype = ctypes.c_int
         lib.kda_decode_step.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int,
                                         ctypes.c_int, ctypes.POINTER(Stages), vp, vp, vp, vp, vp, vp, vp, vp]
@@ -209,9 +215,9 @@ _ws_cache = {}
 _ws_lock = threading.Lock()
 
 
-def _workspace(device, stream, need: int):
+def _workspace(device, stream, need: int, kind: str = "prefill"):
     torch = _torch()
-    key = (device, stream.cuda_stream)
+    key = (device, stream.cuda_stream) if kind == "prefill" else (device, stream.cuda_stream, kind)
     with _ws_lock:
         ws = _ws_cache.get(key)
         if ws is None or ws.numel() < need:
@@ -355,6 +361,61 @@ def prefill_recovered(q, v, cu_seqlens, *, chunk: int = 64, cu_seqlens_host=None
     if st != KDA_OK:
         raise KdaError(st, "kda_prefill_recovered")
     return bool(out.value)
+
+
+def prefill_backward(q, k, v, log_alpha, beta, cu_seqlens, S0, dO, dS_T=None, *, want_dS0: bool = True,
+                     cu_seqlens_host: Optional[Sequence[int]] = None, workspace=None, stream=None):
+    """Gradients of sum <dO, o> + <dS_T, S_T> through ``prefill`` (64-token
+    chunks, no stages).  Arguments as for ``prefill``; dO like o, dS_T like
+    S_T (or None).  Returns a dict: dq, dk, dv (the io dtype), dlog_alpha
+    (fp32, shaped like log_alpha; None without a gate), dbeta (fp32) and dS0
+    (fp32, None when ``want_dS0`` is False).  The backward workspace is
+    cached per (device, stream) like the prefill's."""
+    torch = _torch()
+    lib = load_library()
+    if q.dim() != 3 or v.dim() != 3 or cu_seqlens.dim() != 1:
+        raise ValueError("q, k, v must be [T, H, d] and cu_seqlens [N+1]")
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    N = cu_seqlens.shape[0] - 1
+    dt = _dtype_code(q)
+    dev = q.device
+    if k.dtype != q.dtype or v.dtype != q.dtype or dO.dtype != q.dtype:
+        raise TypeError("q, k, v and dO must share a dtype")
+    gate = _gate(log_alpha, (T, H))
+    la_shape = _la_shape(gate, (T, H), dk)
+    s = _stream(stream)
+    desc, keep = make_desc(N, T, H, dk, dv, 64, dt, cu_seqlens_host, 0, gate)
+    need = int(lib.kda_prefill_backward_workspace_size(ctypes.byref(desc)))
+    if need == 0:
+        st = lib.kda_prefill_backward(ctypes.byref(desc), *([None] * 16), 0, None)
+        raise KdaError(st if st != KDA_OK else KDA_ERR_INVALID_ARGUMENT, "kda_prefill_backward_workspace_size")
+    out = {"dq": torch.empty((T, H, dk), dtype=q.dtype, device=dev),
+           "dk": torch.empty((T, H, dk), dtype=q.dtype, device=dev),
+           "dv": torch.empty((T, H, dv), dtype=q.dtype, device=dev),
+           "dlog_alpha": None if la_shape is None else torch.empty(la_shape, dtype=torch.float32, device=dev),
+           "dbeta": torch.empty((T, H), dtype=torch.float32, device=dev),
+           "dS0": torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev) if want_dS0 else None}
+    ptrs = (_dev_ptr(q, "q", None, (T, H, dk), dev), _dev_ptr(k, "k", None, (T, H, dk), dev),
+            _dev_ptr(v, "v", None, (T, H, dv), dev),
+            _dev_ptr(log_alpha, "log_alpha", torch.float32, la_shape, dev),
+            _dev_ptr(beta, "beta", torch.float32, (T, H), dev),
+            _dev_ptr(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,), dev),
+            _dev_ptr(S0, "S0", torch.float32, (N, H, dk, dv), dev),
+            _dev_ptr(dO, "dO", q.dtype, (T, H, dv), dev),
+            _dev_ptr(dS_T, "dS_T", torch.float32, (N, H, dk, dv), dev),
+            _dev_ptr(out["dq"], "dq"), _dev_ptr(out["dk"], "dk"), _dev_ptr(out["dv"], "dv"),
+            _dev_ptr(out["dlog_alpha"], "dlog_alpha"), _dev_ptr(out["dbeta"], "dbeta"),
+            _dev_ptr(out["dS0"], "dS0"))
+    if workspace is None:
+        workspace = _workspace(dev, s, need, "backward")
+    wptr = _dev_ptr(workspace, "workspace", None, None, dev)
+    st = lib.kda_prefill_backward(ctypes.byref(desc), *ptrs, wptr, workspace.numel() * workspace.element_size(),
+                                  s.cuda_stream)
+    del keep
+    if st != KDA_OK:
+        raise KdaError(st, "kda_prefill_backward")
+    return out
 
 
 def set_wait_limit(polls: int) -> int:

@@ -133,7 +133,7 @@ const char* kda_status_string(kda_status s) {
   return "KDA_ERR_UNKNOWN";
 }
 
-int32_t kda_version(void) { return 20000; }
+int32_t kda_version(void) { return 20100; }
 
 size_t kda_prefill_workspace_size(const kda_prefill_desc* d) {
   int64_t mc = 0;
@@ -147,6 +147,58 @@ kda_status kda_prefill(const kda_prefill_desc* d, const void* q, const void* k, 
                        const float* log_alpha, const float* beta, const int32_t* cu_seqlens, const float* S0,
                        void* o, float* S_T, void* workspace, size_t workspace_bytes, void* stream) {
   return kda::prefill_checked(d, q, k, v, log_alpha, beta, cu_seqlens, S0, o, S_T, workspace, workspace_bytes, stream);
+}
+
+size_t kda_prefill_backward_workspace_size(const kda_prefill_desc* d) {
+  int64_t mc = 0;
+  if (check_desc(d, &mc) != KDA_OK || d->chunk != 64 || d->stages) return 0;
+  kda::BackwardPlan p;
+  if (!kda::make_backward_plan(d, mc, &p)) return 0;
+  return p.total_bytes;
+}
+
+kda_status kda_prefill_backward(const kda_prefill_desc* d, const void* q, const void* k, const void* v,
+                                const float* log_alpha, const float* beta, const int32_t* cu_seqlens,
+                                const float* S0, const void* dO, const float* dS_T, void* dq, void* dk, void* dv,
+                                float* dlog_alpha, float* dbeta, float* dS0, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  int64_t mc = 0;
+  const kda_status s = check_desc(d, &mc);
+  if (s != KDA_OK) return s;
+  if (d->chunk != 64 || d->stages) return KDA_ERR_UNSUPPORTED;
+  if (d->num_seqs == 0) return KDA_OK;
+  kda::BackwardPlan p;
+  if (!kda::make_backward_plan(d, mc, &p)) return KDA_ERR_UNSUPPORTED;
+  if (!cu_seqlens) return KDA_ERR_INVALID_ARGUMENT;
+  const size_t T = static_cast<size_t>(d->total_tokens), H = static_cast<size_t>(d->num_heads);
+  const size_t es = io_size(d->io_dtype);
+  const size_t gw = gate_width(d->gate, d->dk);
+  if (gw == 0) log_alpha = nullptr, dlog_alpha = nullptr;
+  if (T > 0 && (!q || !k || !v || (gw && (!log_alpha || !dlog_alpha)) || !beta || !dO || !dq || !dk || !dv ||
+                !dbeta))
+    return KDA_ERR_INVALID_ARGUMENT;
+  if (!workspace) return KDA_ERR_INVALID_ARGUMENT;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return KDA_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < p.total_bytes) return KDA_ERR_WORKSPACE_TOO_SMALL;
+  const size_t state_bytes = static_cast<size_t>(d->num_seqs) * H * d->dk * d->dv * 4;
+  const Range ins[] = {range(q, T * H * d->dk * es), range(k, T * H * d->dk * es), range(v, T * H * d->dv * es),
+                       range(log_alpha, log_alpha ? T * H * gw * 4 : 0), range(beta, T * H * 4),
+                       range(cu_seqlens, (static_cast<size_t>(d->num_seqs) + 1) * 4),
+                       range(S0, S0 ? state_bytes : 0), range(dO, T * H * d->dv * es),
+                       range(dS_T, dS_T ? state_bytes : 0)};
+  const Range outs[] = {range(dq, T * H * d->dk * es), range(dk, T * H * d->dk * es), range(dv, T * H * d->dv * es),
+                        range(dlog_alpha, dlog_alpha ? T * H * gw * 4 : 0), range(dbeta, T * H * 4),
+                        range(dS0, dS0 ? state_bytes : 0), range(workspace, p.total_bytes)};
+  constexpr int NO = sizeof(outs) / sizeof(outs[0]);
+  for (int a = 0; a < NO; ++a) {
+    for (const Range& x : ins)
+      if (overlap(outs[a], x)) return KDA_ERR_INVALID_ARGUMENT;
+    for (int b = a + 1; b < NO; ++b)
+      if (overlap(outs[a], outs[b])) return KDA_ERR_INVALID_ARGUMENT;
+  }
+  const hipError_t e = kda::launch_backward(p, q, k, v, log_alpha, beta, cu_seqlens, S0, dO, dS_T, dq, dk, dv,
+                                            dlog_alpha, dbeta, dS0, workspace, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KDA_OK : KDA_ERR_DEVICE;
 }
 
 kda_status kda_prefill_recovered(const kda_prefill_desc* d, const void* workspace, int32_t* recovered,

@@ -1,0 +1,1101 @@
+// kda_backward.hip -- chunkwise backward pass of the KDA prefill (gfx950).
+//
+// The model of the "Kimi Linear" deep-read report (zako-mio knowledge base)
+// is trained (section 3.4, training recipe); the pages give the forward
+// recurrence (section 2.3: S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1}
+// + beta_t k_t v_t^T, o_t = S_t^T q_t) and its chunked form (section 3.1:
+// WY / UT representation, sequential state passing between chunks) but no
+// gradient.  This file computes the gradient of
+//   L = sum_t <dO_t, o_t> + <dS_T, S_T>
+// with respect to q, k, v, log alpha, beta and S0 through the same chunked
+// form.  Per chunk of C = 64 tokens (chunk-local cumulative gate G_r =
+// sum_{u <= r} log alpha_u, per key channel; gamma = e^{G_C}):
+//
+//   forward   Kg = k e^{G}, Qg = q e^{G}, Kb = k e^{G_C - G}
+//             A[r][s] = sum_i k_ri k_si e^{G_ri - G_si}  (s < r)
+//             P[r][s] = sum_i q_ri k_si e^{G_ri - G_si}  (s <= r)
+//             T = (I + Diag(beta) A)^{-1}
+//             W = Diag(beta)(V - Kg S0), U = T W
+//             O = Qg S0 + P U,  S_C = Diag(gamma) S0 + Kb^T U
+//   backward  dU = P^T dO + Kb dS_C,  dW = T^T dU,  dV = Diag(beta) dW
+//             dS0 = Diag(gamma) dS_C + Qg^T dO - Kg^T dV
+//             dbeta_r = <dW_r, (V - Kg S0)_r> + sum_s dM[r][s] A[r][s],
+//             dM = -dW U^T (s < r),  dA = Diag(beta) dM,  dP = dO U^T (s <= r)
+//             dQg = dO S0^T, dKg = -dV S0^T, dKb = U dS_C^T,
+//             dgamma_i = sum_j S0[i][j] dS_C[i][j]
+//   and the gated pair sums give dq, dk and dG (hence dlog alpha, a
+//   reverse running sum of dG inside the chunk).
+//
+// Kernels, in stream order:
+//   prep      (chunk, head) parallel: G, Kg, Kb, Qg, A, P, T, gamma -> block
+//   state     sequential over chunks per (sequence, head, 16 value columns):
+//             the chunk-entry states S_c
+//   dstate    sequential in reverse: the cotangents dS of every chunk's
+//             final state, and dS0
+//   grad_v    (chunk, head) parallel over value columns: dv, dbeta and the
+//             value-side cotangents dQg, dKg, dKb, dP, dA, dgamma (written
+//             over the chunk's block)
+//   grad_k    (chunk, head, 32 key channels) parallel: the gated pair sums,
+//             dq, dk and dlog alpha
+//
+// Exactness of the gates.  Every factor e^{G_r - G_s} (s <= r) is at most 1.
+// For a pair of 16-row blocks I > J the factor is split at a reference row
+// between them (e^{G_r - G_ref} e^{G_ref - G_s}, both <= 1), so an underflow
+// only ever stands for a negligible product; inside a diagonal 16 x 16 block
+// each pair's factor is formed directly.  No range condition on log alpha.
+#include <hip/hip_runtime.h>
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+constexpr int BC = 64;   // tokens per chunk
+constexpr int P20 = 20;  // LDS pitch (floats) of 16-column tiles
+constexpr int LPC = BC + 4;  // LDS pitch of chunk x chunk matrices
+
+__device__ __forceinline__ f32x4 mf(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Per-(chunk, head) block, fp32, row-major (offsets in floats).
+template <int DK>
+struct BwdBlk {
+  static constexpr size_t oKg = 0;                                   // [BC][DK]
+  static constexpr size_t oKb = oKg + static_cast<size_t>(BC) * DK;  // [BC][DK]
+  static constexpr size_t oQg = oKb + static_cast<size_t>(BC) * DK;  // [BC][DK]
+  static constexpr size_t oT = oQg + static_cast<size_t>(BC) * DK;   // [BC][BC] lower, unit diagonal
+  static constexpr size_t oA = oT + BC * BC;                         // [BC][BC] strictly lower
+  static constexpr size_t oP = oA + BC * BC;                         // [BC][BC] lower incl. diagonal
+  static constexpr size_t oGam = oP + BC * BC;                       // [DK]
+  static constexpr size_t oBeta = oGam + DK;                         // [BC] (0 past the sequence)
+  static constexpr size_t floats = (oBeta + BC + 63) / 64 * 64;
+  // the value-side cotangents grad_v writes over the block it has read
+  static constexpr size_t odQg = oKg, odKg = oKb, odKb = oQg, odP = oT, odA = oA, odGam = oGam;
+};
+
+size_t blk_floats(int dk) { return dk == 128 ? BwdBlk<128>::floats : BwdBlk<64>::floats; }
+
+// (sequence, chunk, token range) of global chunk j (chunk_off non-decreasing,
+// chunk_off[N] > j).
+struct ChunkLoc {
+  int n, t0, len;
+};
+__device__ __forceinline__ ChunkLoc locate(const int32_t* cu, const int32_t* chunk_off, int N, int j) {
+  int lo = 0, hi = N;  // chunk_off[lo] <= j < chunk_off[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (chunk_off[mid] <= j) lo = mid;
+    else hi = mid;
+  }
+  const int t0 = cu[lo] + (j - chunk_off[lo]) * BC;
+  return ChunkLoc{lo, t0, min(BC, cu[lo + 1] - t0)};
+}
+
+// Eight consecutive io elements as floats, and back.
+__device__ __forceinline__ void load8(const float* p, float* x) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = a[i], x[4 + i] = b[i];
+}
+__device__ __forceinline__ void load8(const bf16_t* p, float* x) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[2 * i] = __uint_as_float(w[i] << 16), x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+}
+__device__ __forceinline__ void store8(float* p, const float* x) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{x[0], x[1], x[2], x[3]};
+  *reinterpret_cast<f32x4*>(p + 4) = f32x4{x[4], x[5], x[6], x[7]};
+}
+__device__ __forceinline__ void store8(bf16_t* p, const float* x) {
+  *reinterpret_cast<uint4*>(p) = uint4{f32x2_to_bf16x2(x[0], x[1]), f32x2_to_bf16x2(x[2], x[3]),
+                                       f32x2_to_bf16x2(x[4], x[5]), f32x2_to_bf16x2(x[6], x[7])};
+}
+
+// log alpha of token t, head h, channel ch for the three gate forms.
+template <int G, int DK>
+__device__ __forceinline__ float gate_at(const float* la, size_t t, int H, int h, int ch) {
+  if constexpr (G == KDA_GATE_CHANNEL) return la[(t * H + h) * DK + ch];
+  else if constexpr (G == KDA_GATE_SCALAR) return la[t * H + h];
+  else return 0.f;
+}
+
+// Inclusive running sum over the 64 rows of a 32-channel slice in LDS
+// (pitch PS), forward (REV = false) or from the last row back (REV = true).
+// 256 threads: thread (channel t % 32, segment t / 32) owns 8 rows.
+template <bool REV, int PS>
+__device__ __forceinline__ void row_scan32(float* x, float* tot /* [8][32] */) {
+  const int ch = threadIdx.x & 31, seg = threadIdx.x >> 5;
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = x[(seg * 8 + i) * PS + ch];
+  if constexpr (!REV) {
+#pragma unroll
+    for (int i = 1; i < 8; ++i) v[i] += v[i - 1];
+    tot[seg * 32 + ch] = v[7];
+  } else {
+#pragma unroll
+    for (int i = 6; i >= 0; --i) v[i] += v[i + 1];
+    tot[seg * 32 + ch] = v[0];
+  }
+  __syncthreads();
+  float off = 0.f;
+  if constexpr (!REV) {
+    for (int s = 0; s < seg; ++s) off += tot[s * 32 + ch];
+  } else {
+    for (int s = seg + 1; s < 8; ++s) off += tot[s * 32 + ch];
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[(seg * 8 + i) * PS + ch] = v[i] + off;
+  __syncthreads();
+}
+
+
+// ---------------------------------------------------------------------------
+// prep: one workgroup (4 waves) per (chunk, head); grid (chunks, H).  The key
+// channels are taken 32 at a time; A and P accumulate over the slices in
+// MFMA tiles: wave w holds the diagonal block pair (w, w) and up to two
+// off-diagonal pairs.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int off_pair_i(int w, int u) {
+  return u == 0 ? (w == 0 ? 1 : (w == 3 ? 3 : 2)) : (w == 0 ? 3 : (w == 1 ? 3 : -1));
+}
+__device__ __forceinline__ int off_pair_j(int w, int u) {
+  return u == 0 ? (w == 2 ? 1 : (w == 3 ? 2 : 0)) : (w == 0 ? 0 : 1);
+}
+
+template <typename T, int DK, int G>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                       const float* __restrict__ la, const float* __restrict__ beta,
+                                                       const int32_t* __restrict__ cu,
+                                                       const int32_t* __restrict__ chunk_off, int N, int H,
+                                                       float* __restrict__ blk) {
+  typedef BwdBlk<DK> B;
+  constexpr int PS = 33;  // pitch of the 32-channel slices
+  __shared__ float qs[BC * PS], ks[BC * PS], gs[BC * PS];
+  __shared__ float Lm[BC * LPC], Tm[BC * LPC];
+  __shared__ float Xs[4][16 * 17];
+  __shared__ float tot[8 * 32];
+  __shared__ float bet[BC];
+  const int j = blockIdx.x, h = blockIdx.y;
+  if (j >= chunk_off[N]) return;
+  const ChunkLoc cl = locate(cu, chunk_off, N, j);
+  float* bk = blk + (static_cast<size_t>(j) * H + h) * B::floats;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
+  if (tid < BC) {
+    const float b = tid < cl.len ? beta[static_cast<size_t>(cl.t0 + tid) * H + h] : 0.f;
+    bet[tid] = b;
+    bk[B::oBeta + tid] = b;
+  }
+  f32x4 aD = zero4(), pD = zero4(), aO[2] = {zero4(), zero4()}, pO[2] = {zero4(), zero4()};
+  for (int sl = 0; sl < DK / 32; ++sl) {
+    const int c0 = sl * 32;
+    for (int e = tid; e < BC * 8; e += 256) {
+      const int row = e >> 3, c4 = (e & 7) * 4;
+      f32x4 xq = zero4(), xk = zero4();
+      if (row < cl.len) {
+        const size_t o = (static_cast<size_t>(cl.t0 + row) * H + h) * DK + c0 + c4;
+        xq = load4(q + o);
+        xk = load4(k + o);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qs[row * PS + c4 + i] = xq[i], ks[row * PS + c4 + i] = xk[i];
+    }
+    {
+      const int ch = tid & 31, seg = tid >> 5;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int row = seg * 8 + i;
+        gs[row * PS + ch] = row < cl.len ? gate_at<G, DK>(la, static_cast<size_t>(cl.t0 + row), H, h, c0 + ch) : 0.f;
+      }
+    }
+    __syncthreads();
+    row_scan32<false, PS>(gs, tot);
+    for (int e = tid; e < BC * 32; e += 256) {
+      const int row = e >> 5, ch = e & 31;
+      const float Gr = gs[row * PS + ch], GC = gs[(BC - 1) * PS + ch];
+      const float eg = __expf(Gr), eb = __expf(GC - Gr);
+      const float kv = ks[row * PS + ch], qv = qs[row * PS + ch];
+      const size_t o = static_cast<size_t>(row) * DK + c0 + ch;
+      bk[B::oKg + o] = kv * eg;
+      bk[B::oKb + o] = kv * eb;
+      bk[B::oQg + o] = qv * eg;
+    }
+    if (tid < 32) bk[B::oGam + c0 + tid] = __expf(gs[(BC - 1) * PS + tid]);
+    // off-diagonal block pairs (I, J < I), split at row 16 I - 1
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int I = off_pair_i(w, u), J = off_pair_j(w, u);
+      if (I < 0) continue;
+      const int ref = 16 * I - 1, ri = 16 * I + r, sj = 16 * J + r;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const int ch = 4 * kk + g;
+        const float gr = gs[ref * PS + ch];
+        const float er = __expf(gs[ri * PS + ch] - gr);
+        const float b = ks[sj * PS + ch] * __expf(gr - gs[sj * PS + ch]);
+        aO[u] = mf(ks[ri * PS + ch] * er, b, aO[u]);
+        pO[u] = mf(qs[ri * PS + ch] * er, b, pO[u]);
+      }
+    }
+    // diagonal block pair (w, w): each entry's factors formed pair by pair
+    {
+      const int s = 16 * w + r;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int ri = 16 * w + 4 * g + m;
+        if (s <= ri) {
+          float sa = 0.f, sp = 0.f;
+#pragma unroll 8
+          for (int ch = 0; ch < 32; ++ch) {
+            const float kE = ks[s * PS + ch] * __expf(gs[ri * PS + ch] - gs[s * PS + ch]);
+            sa += ks[ri * PS + ch] * kE;
+            sp += qs[ri * PS + ch] * kE;
+          }
+          if (s < ri) aD[m] += sa;
+          pD[m] += sp;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  // A and P to the block (upper blocks zero), L = Diag(beta) A and T = 0 in LDS
+  auto put = [&](int I, int J, f32x4 a, f32x4 p) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int row = 16 * I + 4 * g + m, col = 16 * J + r;
+      bk[B::oA + row * BC + col] = a[m];
+      bk[B::oP + row * BC + col] = p[m];
+      Lm[row * LPC + col] = bet[row] * a[m];
+    }
+  };
+  put(w, w, aD, pD);
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+    if (off_pair_i(w, u) >= 0) put(off_pair_i(w, u), off_pair_j(w, u), aO[u], pO[u]);
+  for (int e = tid; e < BC * BC; e += 256) {
+    const int row = e >> 6, col = e & 63;
+    if ((col >> 4) > (row >> 4)) {
+      bk[B::oA + e] = 0.f;
+      bk[B::oP + e] = 0.f;
+      Lm[row * LPC + col] = 0.f;
+    }
+    Tm[row * LPC + col] = 0.f;
+  }
+  __syncthreads();
+  // T = (I + L)^{-1}, unit lower triangular.  Diagonal 16-blocks: one
+  // thread per column, forward substitution.
+  if (tid < BC) {
+    const int base = tid & ~15, c = tid & 15;
+    float x[16];
+#pragma unroll
+    for (int a = 0; a < 16; ++a) x[a] = a == c ? 1.f : 0.f;
+#pragma unroll
+    for (int a = 1; a < 16; ++a) {
+      float s = 0.f;
+#pragma unroll
+      for (int b = 0; b < a; ++b) s += Lm[(base + a) * LPC + base + b] * x[b];
+      if (a > c) x[a] = -s;
+    }
+#pragma unroll
+    for (int a = 0; a < 16; ++a) Tm[(base + a) * LPC + base + c] = x[a];
+  }
+  __syncthreads();
+  // Off-diagonal blocks, one block row at a time:
+  // T_IJ = -T_II sum_{K=J}^{I-1} L_IK T_KJ (wave J of block row I).
+  for (int I = 1; I < 4; ++I) {
+    const bool act = w < I;
+    if (act) {
+      f32x4 acc = zero4();
+      for (int K = w; K < I; ++K)
+#pragma unroll
+        for (int kk = 0; kk < 16; kk += 4)
+          acc = mf(Lm[(16 * I + r) * LPC + 16 * K + kk + g], Tm[(16 * K + kk + g) * LPC + 16 * w + r], acc);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) Xs[w][(4 * g + m) * 17 + r] = acc[m];
+    }
+    __syncthreads();
+    if (act) {
+      f32x4 t = zero4();
+#pragma unroll
+      for (int kk = 0; kk < 16; kk += 4) t = mf(Tm[(16 * I + r) * LPC + 16 * I + kk + g], Xs[w][(kk + g) * 17 + r], t);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) Tm[(16 * I + 4 * g + m) * LPC + 16 * w + r] = -t[m];
+    }
+    __syncthreads();
+  }
+  for (int e = tid; e < BC * BC; e += 256) bk[B::oT + e] = Tm[(e >> 6) * LPC + (e & 63)];
+}
+
+// ---------------------------------------------------------------------------
+// state: the chunk-entry states.  One workgroup (4 waves) per (sequence,
+// head, 16 value columns), walking the sequence's chunks in order; the
+// state (DK x 16) is held in MFMA accumulators, wave w owning key-channel
+// rows [16 TPW w, 16 TPW (w + 1)).  Per chunk:
+//   W = Diag(beta)(V - Kg S)   (wave w: rows 16 w .. 16 w + 15)
+//   U = T W
+//   S = Diag(gamma) S + Kb^T U
+// Each wave reads the block operands it needs straight into registers, one
+// chunk ahead.  Workgroup x: the value slices of a (sequence, head) share an
+// XCD (x % 8), so the slices read each block through one L2.
+// ---------------------------------------------------------------------------
+template <typename T, int DK, int DV>
+__global__ __launch_bounds__(256) void bwd_state_kernel(const T* __restrict__ v, const int32_t* __restrict__ cu,
+                                                        const int32_t* __restrict__ chunk_off,
+                                                        const int32_t* __restrict__ order, int N, int H,
+                                                        const float* __restrict__ blk, const float* __restrict__ S0,
+                                                        float* __restrict__ sc) {
+  typedef BwdBlk<DK> B;
+  constexpr int NSP = DV / 16, NKB = DK / 16, TPW = NKB / 4;
+  __shared__ float Xl[DK * P20], Wl[BC * P20], Ul[BC * P20];
+  const int x = blockIdx.x, xcd = x & 7, s8 = x >> 3, sp = s8 % NSP, p = (s8 / NSP) * 8 + xcd;
+  if (p >= N * H) return;
+  const int n = order[p / H], h = p % H;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
+  const int tb = cu[n], L = cu[n + 1] - tb, nch = (L + BC - 1) / BC, j0 = chunk_off[n];
+  const int col = sp * 16 + r;
+  const size_t sbase = (static_cast<size_t>(n) * H + h) * DK * DV;
+  f32x4 X[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int row = 16 * (w * TPW + t) + 4 * g + m;
+      X[t][m] = S0 ? S0[sbase + static_cast<size_t>(row) * DV + col] : 0.f;
+    }
+  struct Ops {
+    f32x4 kg[NKB];
+    float kbt[TPW][16];
+    f32x4 tt[4];
+    float vv[4], bet[4], gam[TPW][4];
+  };
+  auto load = [&](int c, Ops& o) {
+    const float* bk = blk + (static_cast<size_t>(j0 + c) * H + h) * B::floats;
+    const int row = 16 * w + r;
+#pragma unroll
+    for (int b = 0; b < NKB; ++b) o.kg[b] = *reinterpret_cast<const f32x4*>(bk + B::oKg + row * DK + 16 * b + 4 * g);
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int s = 0; s < 16; ++s) o.kbt[t][s] = bk[B::oKb + (4 * s + g) * DK + 16 * (w * TPW + t) + r];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      o.tt[b] = b <= w ? *reinterpret_cast<const f32x4*>(bk + B::oT + row * BC + 16 * b + 4 * g) : zero4();
+    const int t0 = tb + c * BC, len = min(BC, L - c * BC);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int rr = 16 * w + 4 * g + m;
+      o.vv[m] = rr < len ? io<T>::load(v + (static_cast<size_t>(t0 + rr) * H + h) * DV + col) : 0.f;
+      o.bet[m] = bk[B::oBeta + rr];
+    }
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) o.gam[t][m] = bk[B::oGam + 16 * (w * TPW + t) + 4 * g + m];
+  };
+  Ops cur, nxt;
+  if (nch > 0) load(0, cur);
+  for (int c = 0; c < nch; ++c) {
+    float* so = sc + (static_cast<size_t>(j0 + c) * H + h) * DK * DV;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int row = 16 * (w * TPW + t) + 4 * g + m;
+        Xl[row * P20 + r] = X[t][m];
+        so[static_cast<size_t>(row) * DV + col] = X[t][m];
+      }
+    __syncthreads();
+    if (c + 1 < nch) load(c + 1, nxt);
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int b = 0; b < NKB; ++b)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) acc = mf(cur.kg[b][m], Xl[(16 * b + 4 * g + m) * P20 + r], acc);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) Wl[(16 * w + 4 * g + m) * P20 + r] = cur.bet[m] * (cur.vv[m] - acc[m]);
+    __syncthreads();
+    acc = zero4();
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      if (b <= w)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) acc = mf(cur.tt[b][m], Wl[(16 * b + 4 * g + m) * P20 + r], acc);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) Ul[(16 * w + 4 * g + m) * P20 + r] = acc[m];
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) X[t][m] *= cur.gam[t][m];
+#pragma unroll
+      for (int s = 0; s < 16; ++s) X[t] = mf(cur.kbt[t][s], Ul[(4 * s + g) * P20 + r], X[t]);
+    }
+    cur = nxt;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dstate: the cotangents of the chunk-final states, in reverse chunk order,
+// with the same workgroup layout as the state pass.  Per chunk (X = dS of
+// the chunk's final state on entry, of its entry state on exit):
+//   Z = P^T dO + Kb X,  Y = T^T Z,  X = Diag(gamma) X + Qg^T dO - Kg^T Diag(beta) Y
+// ---------------------------------------------------------------------------
+template <typename T, int DK, int DV>
+__global__ __launch_bounds__(256) void bwd_dstate_kernel(const T* __restrict__ dO, const int32_t* __restrict__ cu,
+                                                         const int32_t* __restrict__ chunk_off,
+                                                         const int32_t* __restrict__ order, int N, int H,
+                                                         const float* __restrict__ blk, const float* __restrict__ dST,
+                                                         float* __restrict__ dsc, float* __restrict__ dS0) {
+  typedef BwdBlk<DK> B;
+  constexpr int NSP = DV / 16, NKB = DK / 16, TPW = NKB / 4;
+  __shared__ float Xl[DK * P20], Dl[BC * P20], Zl[BC * P20], Yl[BC * P20];
+  const int x = blockIdx.x, xcd = x & 7, s8 = x >> 3, sp = s8 % NSP, p = (s8 / NSP) * 8 + xcd;
+  if (p >= N * H) return;
+  const int n = order[p / H], h = p % H;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
+  const int tb = cu[n], L = cu[n + 1] - tb, nch = (L + BC - 1) / BC, j0 = chunk_off[n];
+  const int col = sp * 16 + r;
+  const size_t sbase = (static_cast<size_t>(n) * H + h) * DK * DV;
+  f32x4 X[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int row = 16 * (w * TPW + t) + 4 * g + m;
+      X[t][m] = dST ? dST[sbase + static_cast<size_t>(row) * DV + col] : 0.f;
+    }
+  typedef typename raw4<T>::type R4;
+  struct Ops {
+    f32x4 kb[NKB];
+    float pt[16], tt[16];
+    float qgt[TPW][16], kgt[TPW][16];
+    R4 dov;
+    float bet[4], gam[TPW][4];
+  };
+  const int drow = tid >> 2, dc4 = (tid & 3) * 4;  // this thread's 4 dO values for the LDS tile
+  auto load = [&](int c, Ops& o) {
+    const float* bk = blk + (static_cast<size_t>(j0 + c) * H + h) * B::floats;
+    const int row = 16 * w + r;
+#pragma unroll
+    for (int b = 0; b < NKB; ++b) o.kb[b] = *reinterpret_cast<const f32x4*>(bk + B::oKb + row * DK + 16 * b + 4 * g);
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const bool on = s >= 4 * w;
+      o.pt[s] = on ? bk[B::oP + (4 * s + g) * BC + row] : 0.f;
+      o.tt[s] = on ? bk[B::oT + (4 * s + g) * BC + row] : 0.f;
+    }
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        const int o2 = (4 * s + g) * DK + 16 * (w * TPW + t) + r;
+        o.qgt[t][s] = bk[B::oQg + o2];
+        o.kgt[t][s] = bk[B::oKg + o2];
+      }
+    const int t0 = tb + c * BC, len = min(BC, L - c * BC);
+    o.dov = R4{};
+    if (drow < len) o.dov = load4raw(dO + (static_cast<size_t>(t0 + drow) * H + h) * DV + sp * 16 + dc4);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) o.bet[m] = bk[B::oBeta + 16 * w + 4 * g + m];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) o.gam[t][m] = bk[B::oGam + 16 * (w * TPW + t) + 4 * g + m];
+  };
+  Ops cur, nxt;
+  if (nch > 0) load(nch - 1, cur);
+  for (int c = nch - 1; c >= 0; --c) {
+    float* so = dsc + (static_cast<size_t>(j0 + c) * H + h) * DK * DV;
+    __syncthreads();  // the previous chunk's readers of Dl and Yl are done
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int row = 16 * (w * TPW + t) + 4 * g + m;
+        Xl[row * P20 + r] = X[t][m];
+        so[static_cast<size_t>(row) * DV + col] = X[t][m];
+      }
+    {
+      const f32x4 d = cvt4(cur.dov);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Dl[drow * P20 + dc4 + i] = d[i];
+    }
+    __syncthreads();
+    if (c > 0) load(c - 1, nxt);
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+      if (s >= 4 * w) acc = mf(cur.pt[s], Dl[(4 * s + g) * P20 + r], acc);
+#pragma unroll
+    for (int b = 0; b < NKB; ++b)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) acc = mf(cur.kb[b][m], Xl[(16 * b + 4 * g + m) * P20 + r], acc);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) Zl[(16 * w + 4 * g + m) * P20 + r] = acc[m];
+    __syncthreads();
+    acc = zero4();
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+      if (s >= 4 * w) acc = mf(cur.tt[s], Zl[(4 * s + g) * P20 + r], acc);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) Yl[(16 * w + 4 * g + m) * P20 + r] = -cur.bet[m] * acc[m];
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) X[t][m] *= cur.gam[t][m];
+#pragma unroll
+      for (int s = 0; s < 16; ++s) X[t] = mf(cur.qgt[t][s], Dl[(4 * s + g) * P20 + r], X[t]);
+#pragma unroll
+      for (int s = 0; s < 16; ++s) X[t] = mf(cur.kgt[t][s], Yl[(4 * s + g) * P20 + r], X[t]);
+    }
+    cur = nxt;
+  }
+  if (dS0) {
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int row = 16 * (w * TPW + t) + 4 * g + m;
+        dS0[sbase + static_cast<size_t>(row) * DV + col] = X[t][m];
+      }
+  }
+}
+
+
+// ---------------------------------------------------------------------------
+// grad_v: one workgroup (4 waves) per (chunk, head); grid (chunks, H).  Walks
+// the value columns 16 at a time.  Per slice, wave w on rows 16 w .. 16 w + 15:
+//   Vt = V - Kg S0, W = Diag(beta) Vt, U = T W
+//   dU = P^T dO + Kb dS_C, dW = T^T dU, dv = Diag(beta) dW
+// then every wave adds the slice's share of the contractions over value
+// columns into its MFMA tiles: dP, dM = -dW U^T, dQg, dKg = -dv S0^T, dKb.
+// At the end dbeta and dv are written out, and dQg, dKg, dKb, dP, dA =
+// Diag(beta) dM, dgamma over the chunk's block (everything it read from the
+// block has been consumed by then).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void tri_ij(int e, int& I, int& J) {
+  I = e >= 6 ? 3 : (e >= 3 ? 2 : (e >= 1 ? 1 : 0));
+  J = e - I * (I + 1) / 2;
+}
+
+template <typename T, int DK, int DV>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_grad_v_kernel(const T* __restrict__ v, const T* __restrict__ dO,
+                                                         const int32_t* __restrict__ cu,
+                                                         const int32_t* __restrict__ chunk_off, int N, int H,
+                                                         float* __restrict__ blk, const float* __restrict__ sc,
+                                                         const float* __restrict__ dsc, T* __restrict__ dv,
+                                                         float* __restrict__ dbeta) {
+  typedef BwdBlk<DK> B;
+  constexpr int NSP = DV / 16, NKB = DK / 16;
+  constexpr int NTILE = 20 + 3 * 4 * NKB;  // dP (10), dM (10), dQg, dKg, dKb (4 NKB each)
+  constexpr int NT = (NTILE + 3) / 4;
+  __shared__ float S0l[DK * P20], dSl[DK * P20];
+  __shared__ float Vl[BC * P20], Dl[BC * P20], Vtl[BC * P20], Wl[BC * P20], Ul[BC * P20], dUl[BC * P20],
+      dWl[BC * P20];
+  __shared__ float betl[BC], dbp[BC * 5];  // dbeta parts: [row][J] from dM tiles, [row][4] from dW . Vt
+  const int j = blockIdx.x, h = blockIdx.y;
+  if (j >= chunk_off[N]) return;
+  const ChunkLoc cl = locate(cu, chunk_off, N, j);
+  float* bk = blk + (static_cast<size_t>(j) * H + h) * B::floats;
+  const float* s0 = sc + (static_cast<size_t>(j) * H + h) * DK * DV;
+  const float* dsC = dsc + (static_cast<size_t>(j) * H + h) * DK * DV;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
+  const int rt = w;  // row tile of the wave
+  if (tid < BC) betl[tid] = bk[B::oBeta + tid];
+  for (int e = tid; e < BC * 5; e += 256) dbp[e] = 0.f;
+  // block operands of the wave's row tile, read once
+  f32x4 kg[NKB], kb[NKB], tt[4];
+  float pt[16], ttt[16], bet[4];
+  {
+    const int row = 16 * rt + r;
+#pragma unroll
+    for (int b = 0; b < NKB; ++b) {
+      kg[b] = *reinterpret_cast<const f32x4*>(bk + B::oKg + row * DK + 16 * b + 4 * g);
+      kb[b] = *reinterpret_cast<const f32x4*>(bk + B::oKb + row * DK + 16 * b + 4 * g);
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      tt[b] = b <= rt ? *reinterpret_cast<const f32x4*>(bk + B::oT + row * BC + 16 * b + 4 * g) : zero4();
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const bool on = s >= 4 * rt;
+      pt[s] = on ? bk[B::oP + (4 * s + g) * BC + row] : 0.f;
+      ttt[s] = on ? bk[B::oT + (4 * s + g) * BC + row] : 0.f;
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) bet[m] = bk[B::oBeta + 16 * rt + 4 * g + m];
+  }
+  f32x4 acc[NT];
+#pragma unroll
+  for (int u = 0; u < NT; ++u) acc[u] = zero4();
+  float db1[4] = {0.f, 0.f, 0.f, 0.f}, dg = 0.f;
+  for (int sp = 0; sp < NSP; ++sp) {
+    // slice inputs: S0 and dS_C columns (DK x 16), v and dO rows (BC x 16)
+    for (int e = tid; e < DK * 4; e += 256) {
+      const int row = e >> 2, c4 = (e & 3) * 4;
+      const f32x4 a = *reinterpret_cast<const f32x4*>(s0 + static_cast<size_t>(row) * DV + sp * 16 + c4);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(dsC + static_cast<size_t>(row) * DV + sp * 16 + c4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S0l[row * P20 + c4 + i] = a[i], dSl[row * P20 + c4 + i] = b[i];
+    }
+    {
+      const int row = tid >> 2, c4 = (tid & 3) * 4;
+      f32x4 x = zero4(), y = zero4();
+      if (row < cl.len) {
+        const size_t o = (static_cast<size_t>(cl.t0 + row) * H + h) * DV + sp * 16 + c4;
+        x = load4(v + o);
+        y = load4(dO + o);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Vl[row * P20 + c4 + i] = x[i], Dl[row * P20 + c4 + i] = y[i];
+    }
+    __syncthreads();
+    {
+      f32x4 a = zero4();
+#pragma unroll
+      for (int b = 0; b < NKB; ++b)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) a = mf(kg[b][m], S0l[(16 * b + 4 * g + m) * P20 + r], a);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int row = 16 * rt + 4 * g + m;
+        const float vt = Vl[row * P20 + r] - a[m];
+        Vtl[row * P20 + r] = vt;
+        Wl[row * P20 + r] = bet[m] * vt;
+      }
+    }
+    {
+      f32x4 a = zero4();
+#pragma unroll
+      for (int s = 0; s < 16; ++s)
+        if (s >= 4 * rt) a = mf(pt[s], Dl[(4 * s + g) * P20 + r], a);
+#pragma unroll
+      for (int b = 0; b < NKB; ++b)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) a = mf(kb[b][m], dSl[(16 * b + 4 * g + m) * P20 + r], a);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) dUl[(16 * rt + 4 * g + m) * P20 + r] = a[m];
+    }
+    __syncthreads();
+    {
+      f32x4 a = zero4();
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        if (b <= rt)
+#pragma unroll
+          for (int m = 0; m < 4; ++m) a = mf(tt[b][m], Wl[(16 * b + 4 * g + m) * P20 + r], a);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) Ul[(16 * rt + 4 * g + m) * P20 + r] = a[m];
+    }
+    {
+      f32x4 a = zero4();
+#pragma unroll
+      for (int s = 0; s < 16; ++s)
+        if (s >= 4 * rt) a = mf(ttt[s], dUl[(4 * s + g) * P20 + r], a);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int row = 16 * rt + 4 * g + m;
+        dWl[row * P20 + r] = a[m];
+        db1[m] += a[m] * Vtl[row * P20 + r];
+        if (row < cl.len) io<T>::store(dv + (static_cast<size_t>(cl.t0 + row) * H + h) * DV + sp * 16 + r, bet[m] * a[m]);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+      const int tau = w + 4 * u;
+      if (tau >= NTILE) break;
+      if (tau < 20) {
+        int I, J;
+        tri_ij(tau % 10, I, J);
+        const float* Am = tau < 10 ? Dl : dWl;
+#pragma unroll
+        for (int kk = 0; kk < 16; kk += 4)
+          acc[u] = mf(Am[(16 * I + r) * P20 + kk + g], Ul[(16 * J + r) * P20 + kk + g], acc[u]);
+      } else {
+        const int e = tau - 20, kind = e / (4 * NKB), rem = e % (4 * NKB), I = rem / NKB, Jc = rem % NKB;
+        const float* Bm = kind == 2 ? dSl : S0l;
+#pragma unroll
+        for (int kk = 0; kk < 16; kk += 4) {
+          float a;
+          if (kind == 0) a = Dl[(16 * I + r) * P20 + kk + g];
+          else if (kind == 1) a = betl[16 * I + r] * dWl[(16 * I + r) * P20 + kk + g];
+          else a = Ul[(16 * I + r) * P20 + kk + g];
+          acc[u] = mf(a, Bm[(16 * Jc + r) * P20 + kk + g], acc[u]);
+        }
+      }
+    }
+    if (tid < DK) {
+#pragma unroll
+      for (int c = 0; c < 16; ++c) dg += S0l[tid * P20 + c] * dSl[tid * P20 + c];
+    }
+    __syncthreads();
+  }
+  // dbeta: the write's share (dW . Vt, summed over value columns) and the
+  // inverse's share (sum_s dM[r][s] A[r][s]), each part in its own slot and
+  // summed in a fixed order
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const float x = group_sum<16>(db1[m]);
+    if (r == 0) dbp[(16 * rt + 4 * g + m) * 5 + 4] = x;
+  }
+#pragma unroll
+  for (int u = 0; u < NT; ++u) {
+    const int tau = w + 4 * u;
+    if (tau >= 10 && tau < 20) {
+      int I, J;
+      tri_ij(tau - 10, I, J);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int row = 16 * I + 4 * g + m;
+        const float x = group_sum<16>(-acc[u][m] * bk[B::oA + row * BC + 16 * J + r]);
+        if (r == 0) dbp[row * 5 + J] = x;
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < cl.len) {
+    const float* x = dbp + tid * 5;
+    dbeta[static_cast<size_t>(cl.t0 + tid) * H + h] = x[4] + x[0] + x[1] + x[2] + x[3];
+  }
+#pragma unroll
+  for (int u = 0; u < NT; ++u) {
+    const int tau = w + 4 * u;
+    if (tau >= NTILE) break;
+    if (tau < 20) {
+      int I, J;
+      tri_ij(tau % 10, I, J);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int row = 16 * I + 4 * g + m, col = 16 * J + r;
+        if (tau < 10) bk[B::odP + row * BC + col] = (I == J && col > row) ? 0.f : acc[u][m];
+        else bk[B::odA + row * BC + col] = (I == J && col >= row) ? 0.f : -betl[row] * acc[u][m];
+      }
+    } else {
+      const int e = tau - 20, kind = e / (4 * NKB), rem = e % (4 * NKB), I = rem / NKB, Jc = rem % NKB;
+      const size_t o = kind == 0 ? B::odQg : (kind == 1 ? B::odKg : B::odKb);
+      const float sgn = kind == 1 ? -1.f : 1.f;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) bk[o + (16 * I + 4 * g + m) * DK + 16 * Jc + r] = sgn * acc[u][m];
+    }
+  }
+  if (tid < DK) bk[B::odGam + tid] = dg;
+}
+
+// ---------------------------------------------------------------------------
+// grad_k: one workgroup (4 waves) per (chunk, head, 32 key channels) -- or,
+// for the one-rate-per-head gate, per (chunk, head) over every channel, so
+// that the per-head gate cotangent is summed inside one workgroup.  Grid
+// (chunks, H, slices).  Thread t works on row t / 4, channels 8 (t % 4) ..
+// 8 (t % 4) + 7 of the slice.
+//   GQ[r]  = sum_{s <= r} dP[r][s] k_s e^{G_r - G_s}
+//   GA[r]  = sum_{s <  r} dA[r][s] k_s e^{G_r - G_s}
+//   G2[s]  = sum_{r >= s} (dP[r][s] q_r + dA[r][s] k_r) e^{G_r - G_s}
+//   dq = dQg e^{G} + GQ,   dk = dKg e^{G} + dKb e^{G_C - G} + GA + G2
+//   dG = dQg Qg + dKg Kg - dKb Kb + q GQ + k (GA - G2)
+//        (+ sum_s dKb_s Kb_s + dgamma gamma on the last row, for G_C)
+//   dlog alpha_u = sum_{r >= u} dG_r
+// Off-diagonal block pairs use operands scaled at a reference row (row-side:
+// rows s < 16 I scaled by e^{G_{16I-1} - G_s}; column side: rows r > 16 J + 15
+// scaled by e^{G_r - G_{16J+15}}), diagonal blocks pair by pair.
+// ---------------------------------------------------------------------------
+template <typename T, int DK, int G>
+__global__ __launch_bounds__(256) void bwd_grad_k_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                         const float* __restrict__ la, const int32_t* __restrict__ cu,
+                                                         const int32_t* __restrict__ chunk_off, int N, int H,
+                                                         const float* __restrict__ blk, T* __restrict__ dq,
+                                                         T* __restrict__ dk, float* __restrict__ dla) {
+  typedef BwdBlk<DK> B;
+  constexpr int PS = 36;  // pitch of the 32-channel slices (16-byte rows)
+  constexpr int NSW = G == KDA_GATE_SCALAR ? DK / 32 : 1;  // slices per workgroup
+  __shared__ float qs[BC * PS], ks[BC * PS], gs[BC * PS];
+  __shared__ float dPl[BC * LPC], dAl[BC * LPC];
+  __shared__ float Ksc[96 * PS], Xq[96 * PS], Xk[96 * PS];
+  __shared__ float tot[8 * 32], rsum[BC];
+  const int j = blockIdx.x, h = blockIdx.y;
+  if (j >= chunk_off[N]) return;
+  const ChunkLoc cl = locate(cu, chunk_off, N, j);
+  const float* bk = blk + (static_cast<size_t>(j) * H + h) * B::floats;
+  const int tid = threadIdx.x;
+  for (int e = tid; e < BC * BC / 4; e += 256) {
+    const int row = e >> 4, c4 = (e & 15) * 4;
+    const f32x4 a = *reinterpret_cast<const f32x4*>(bk + B::odP + row * BC + c4);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(bk + B::odA + row * BC + c4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dPl[row * LPC + c4 + i] = a[i], dAl[row * LPC + c4 + i] = b[i];
+  }
+  if (tid < BC) rsum[tid] = 0.f;
+  const int row = tid >> 2, c8 = (tid & 3) * 8;
+  const int I = row >> 4;
+  for (int si = 0; si < NSW; ++si) {
+    const int c0 = (blockIdx.z * NSW + si) * 32;
+    {
+      float xq[8], xk[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) xq[i] = xk[i] = 0.f;
+      if (row < cl.len) {
+        const size_t o = (static_cast<size_t>(cl.t0 + row) * H + h) * DK + c0 + c8;
+        load8(q + o, xq);
+        load8(k + o, xk);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qs[row * PS + c8 + i] = xq[i], ks[row * PS + c8 + i] = xk[i];
+      const int ch = tid & 31, seg = tid >> 5;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int rr = seg * 8 + i;
+        gs[rr * PS + ch] = rr < cl.len ? gate_at<G, DK>(la, static_cast<size_t>(cl.t0 + rr), H, h, c0 + ch) : 0.f;
+      }
+    }
+    __syncthreads();
+    row_scan32<false, PS>(gs, tot);
+    // scaled operands of the off-diagonal block pairs
+    for (int e = tid; e < 96 * 32; e += 256) {
+      const int r96 = e >> 5, ch = e & 31;
+      {
+        const int Ib = r96 < 16 ? 1 : (r96 < 48 ? 2 : 3);
+        const int s = r96 - (Ib == 1 ? 0 : (Ib == 2 ? 16 : 48));
+        Ksc[r96 * PS + ch] = ks[s * PS + ch] * __expf(gs[(16 * Ib - 1) * PS + ch] - gs[s * PS + ch]);
+      }
+      {
+        const int Jb = r96 < 48 ? 0 : (r96 < 80 ? 1 : 2);
+        const int rr = 16 * Jb + 16 + r96 - (Jb == 0 ? 0 : (Jb == 1 ? 48 : 80));
+        const float E = __expf(gs[rr * PS + ch] - gs[(16 * Jb + 15) * PS + ch]);
+        Xq[r96 * PS + ch] = qs[rr * PS + ch] * E;
+        Xk[r96 * PS + ch] = ks[rr * PS + ch] * E;
+      }
+    }
+    __syncthreads();
+    float GQ[8], GA[8], G2[8], Gr[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) GQ[i] = GA[i] = G2[i] = 0.f, Gr[i] = gs[row * PS + c8 + i];
+    // row side
+    if (I > 0) {
+      const int off = I == 1 ? 0 : (I == 2 ? 16 : 48);
+      for (int s = 0; s < 16 * I; ++s) {
+        const float dp = dPl[row * LPC + s], da = dAl[row * LPC + s];
+        const float* kp = Ksc + (off + s) * PS + c8;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) GQ[i] += dp * kp[i], GA[i] += da * kp[i];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float sc_ = __expf(Gr[i] - gs[(16 * I - 1) * PS + c8 + i]);
+        GQ[i] *= sc_;
+        GA[i] *= sc_;
+      }
+    }
+    for (int s = 16 * I; s < row; ++s) {
+      const float dp = dPl[row * LPC + s], da = dAl[row * LPC + s];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float kE = ks[s * PS + c8 + i] * __expf(Gr[i] - gs[s * PS + c8 + i]);
+        GQ[i] += dp * kE;
+        GA[i] += da * kE;
+      }
+    }
+    // column side (this thread's row is the column index s)
+    if (I < 3) {
+      const int off = I == 0 ? 0 : (I == 1 ? 48 : 80);
+      for (int rr = 16 * I + 16; rr < BC; ++rr) {
+        const float dp = dPl[rr * LPC + row], da = dAl[rr * LPC + row];
+        const float* xq = Xq + (off + rr - 16 * I - 16) * PS + c8;
+        const float* xk = Xk + (off + rr - 16 * I - 16) * PS + c8;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) G2[i] += dp * xq[i] + da * xk[i];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) G2[i] *= __expf(gs[(16 * I + 15) * PS + c8 + i] - Gr[i]);
+    }
+    for (int rr = row + 1; rr < 16 * I + 16; ++rr) {
+      const float dp = dPl[rr * LPC + row], da = dAl[rr * LPC + row];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        G2[i] += (dp * qs[rr * PS + c8 + i] + da * ks[rr * PS + c8 + i]) * __expf(gs[rr * PS + c8 + i] - Gr[i]);
+    }
+    // elementwise
+    float dQg[8], dKg[8], dKb[8], dqv[8], dkv[8], dG[8], cs[8];
+    {
+      const size_t o = static_cast<size_t>(row) * DK + c0 + c8;
+      load8(bk + B::odQg + o, dQg);
+      load8(bk + B::odKg + o, dKg);
+      load8(bk + B::odKb + o, dKb);
+    }
+    // The pair s = r enters P with factor 1 and its contributions to dG
+    // (q_r dP_rr k_r - k_r dP_rr q_r) cancel exactly, as do the last token's
+    // own dKb Kb terms (its factor e^{G_C - G_r} is 1; in a partial chunk the
+    // last token is row len - 1, the rows after it have no decay): both are
+    // left out of dG rather than added and subtracted, which would leave
+    // rounding error of the size of the terms where the true dG is tiny
+    // (strong decay).
+    const float dpd = dPl[row * LPC + row];
+    const bool last = row == BC - 1 || row == cl.len - 1;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float qv = qs[row * PS + c8 + i], kv = ks[row * PS + c8 + i];
+      const float eg = __expf(Gr[i]), eb = __expf(gs[(BC - 1) * PS + c8 + i] - Gr[i]);
+      dqv[i] = dQg[i] * eg + GQ[i] + dpd * kv;
+      dkv[i] = dKg[i] * eg + dKb[i] * eb + GA[i] + G2[i] + dpd * qv;
+      cs[i] = last ? 0.f : dKb[i] * kv * eb;
+      dG[i] = (dQg[i] * qv + dKg[i] * kv) * eg - cs[i] + qv * GQ[i] + kv * (GA[i] - G2[i]);
+    }
+    if (row < cl.len) {
+      const size_t o = (static_cast<size_t>(cl.t0 + row) * H + h) * DK + c0 + c8;
+      store8(dq + o, dqv);
+      store8(dk + o, dkv);
+    }
+    if constexpr (G != KDA_GATE_NONE) {
+      __syncthreads();  // every reader of qs and Xk is done
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qs[row * PS + c8 + i] = dG[i], Xk[row * PS + c8 + i] = cs[i];
+      __syncthreads();
+      if (tid < 32) {  // G_C: the column sum of dKb Kb over the other rows (fixed order), dgamma gamma
+        float x = 0.f;
+        for (int rr = 0; rr < BC; ++rr) x += Xk[rr * PS + tid];
+        qs[(BC - 1) * PS + tid] += x + bk[B::odGam + c0 + tid] * __expf(gs[(BC - 1) * PS + tid]);
+      }
+      __syncthreads();
+      row_scan32<true, PS>(qs, tot);
+      if constexpr (G == KDA_GATE_CHANNEL) {
+        if (row < cl.len) {
+          float x[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) x[i] = qs[row * PS + c8 + i];
+          store8(dla + (static_cast<size_t>(cl.t0 + row) * H + h) * DK + c0 + c8, x);
+        }
+      } else {
+        float x = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x += qs[row * PS + c8 + i];
+        x = group_sum<4>(x);  // the row's four threads are one lane quad
+        if ((tid & 3) == 0) rsum[row] += x;
+      }
+    }
+    __syncthreads();
+  }
+  if constexpr (G == KDA_GATE_SCALAR) {
+    if (tid < cl.len) dla[static_cast<size_t>(cl.t0 + tid) * H + h] = rsum[tid];
+  }
+}
+
+}  // namespace
+}  // namespace kda
+
+namespace kda {
+
+static size_t align256b(size_t x) { return (x + 255) / 256 * 256; }
+
+bool make_backward_plan(const kda_prefill_desc* d, int64_t max_chunks, BackwardPlan* p) {
+  p->N = d->num_seqs;
+  p->T = d->total_tokens;
+  p->H = d->num_heads;
+  p->dk = d->dk;
+  p->dv = d->dv;
+  p->dt = d->io_dtype;
+  p->gate = d->gate;
+  p->max_chunks = max_chunks;
+  p->sort = d->num_seqs <= 8192;
+  const size_t slots = static_cast<size_t>(max_chunks) * d->num_heads;
+  size_t off = 0;
+  p->off_chunk_off = off; off = align256b(off + 4 * (static_cast<size_t>(d->num_seqs) + 1));
+  p->off_order = off;     off = align256b(off + 4 * (static_cast<size_t>(d->num_seqs) + 1));
+  p->off_blocks = off;    off = align256b(off + slots * blk_floats(d->dk) * 4);
+  p->off_states = off;    off = align256b(off + slots * d->dk * d->dv * 4);
+  p->off_dstates = off;   off = align256b(off + slots * d->dk * d->dv * 4);
+  p->total_bytes = off;
+  return true;
+}
+
+template <typename T, int DK, int DV, int G>
+static hipError_t launch_backward_t(const BackwardPlan& p, const void* q, const void* k, const void* v,
+                                    const float* la, const float* beta, const int32_t* cu, const float* S0,
+                                    const void* dO, const float* dS_T, void* dq, void* dk, void* dv, float* dla,
+                                    float* dbeta, float* dS0, void* ws, hipStream_t st) {
+  unsigned char* w = static_cast<unsigned char*>(ws);
+  int32_t* chunk_off = reinterpret_cast<int32_t*>(w + p.off_chunk_off);
+  int32_t* order = reinterpret_cast<int32_t*>(w + p.off_order);
+  float* blk = reinterpret_cast<float*>(w + p.off_blocks);
+  float* sc = reinterpret_cast<float*>(w + p.off_states);
+  float* dsc = reinterpret_cast<float*>(w + p.off_dstates);
+  hipError_t e = launch_chunk_offsets(cu, p.N, BC, chunk_off, order, p.sort, st);
+  if (e != hipSuccess) return e;
+  const unsigned mc = static_cast<unsigned>(p.max_chunks);
+  const T* tq = static_cast<const T*>(q);
+  const T* tk = static_cast<const T*>(k);
+  const T* tv = static_cast<const T*>(v);
+  const T* tdo = static_cast<const T*>(dO);
+  if (mc > 0) {
+    hipLaunchKernelGGL((bwd_prep_kernel<T, DK, G>), dim3(mc, p.H), dim3(256), 0, st, tq, tk, la, beta, cu, chunk_off,
+                       p.N, p.H, blk);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  const int64_t NH = static_cast<int64_t>(p.N) * p.H;
+  const unsigned seq_wgs = static_cast<unsigned>((NH + 7) / 8 * 8 * (DV / 16));
+  hipLaunchKernelGGL((bwd_state_kernel<T, DK, DV>), dim3(seq_wgs), dim3(256), 0, st, tv, cu, chunk_off, order, p.N,
+                     p.H, blk, S0, sc);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dstate_kernel<T, DK, DV>), dim3(seq_wgs), dim3(256), 0, st, tdo, cu, chunk_off, order,
+                     p.N, p.H, blk, dS_T, dsc, dS0);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (mc > 0) {
+    hipLaunchKernelGGL((bwd_grad_v_kernel<T, DK, DV>), dim3(mc, p.H), dim3(256), 0, st, tv, tdo, cu, chunk_off, p.N,
+                       p.H, blk, sc, dsc, static_cast<T*>(dv), dbeta);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const unsigned nz = G == KDA_GATE_SCALAR ? 1u : static_cast<unsigned>(DK / 32);
+    hipLaunchKernelGGL((bwd_grad_k_kernel<T, DK, G>), dim3(mc, p.H, nz), dim3(256), 0, st, tq, tk, la, cu,
+                       chunk_off, p.N, p.H, blk, static_cast<T*>(dq), static_cast<T*>(dk), dla);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <typename T, int DK, int DV>
+static hipError_t backward_gate(const BackwardPlan& p, const void* q, const void* k, const void* v, const float* la,
+                                const float* beta, const int32_t* cu, const float* S0, const void* dO,
+                                const float* dS_T, void* dq, void* dk, void* dv, float* dla, float* dbeta,
+                                float* dS0, void* ws, hipStream_t st) {
+  if (p.gate == KDA_GATE_CHANNEL)
+    return launch_backward_t<T, DK, DV, KDA_GATE_CHANNEL>(p, q, k, v, la, beta, cu, S0, dO, dS_T, dq, dk, dv, dla,
+                                                          dbeta, dS0, ws, st);
+  if (p.gate == KDA_GATE_SCALAR)
+    return launch_backward_t<T, DK, DV, KDA_GATE_SCALAR>(p, q, k, v, la, beta, cu, S0, dO, dS_T, dq, dk, dv, dla,
+                                                         dbeta, dS0, ws, st);
+  return launch_backward_t<T, DK, DV, KDA_GATE_NONE>(p, q, k, v, la, beta, cu, S0, dO, dS_T, dq, dk, dv, dla, dbeta,
+                                                     dS0, ws, st);
+}
+
+template <typename T>
+static hipError_t backward_dims(const BackwardPlan& p, const void* q, const void* k, const void* v, const float* la,
+                                const float* beta, const int32_t* cu, const float* S0, const void* dO,
+                                const float* dS_T, void* dq, void* dk, void* dv, float* dla, float* dbeta,
+                                float* dS0, void* ws, hipStream_t st) {
+  if (p.dk == 128 && p.dv == 128)
+    return backward_gate<T, 128, 128>(p, q, k, v, la, beta, cu, S0, dO, dS_T, dq, dk, dv, dla, dbeta, dS0, ws, st);
+  if (p.dk == 128 && p.dv == 64)
+    return backward_gate<T, 128, 64>(p, q, k, v, la, beta, cu, S0, dO, dS_T, dq, dk, dv, dla, dbeta, dS0, ws, st);
+  if (p.dk == 64 && p.dv == 128)
+    return backward_gate<T, 64, 128>(p, q, k, v, la, beta, cu, S0, dO, dS_T, dq, dk, dv, dla, dbeta, dS0, ws, st);
+  return backward_gate<T, 64, 64>(p, q, k, v, la, beta, cu, S0, dO, dS_T, dq, dk, dv, dla, dbeta, dS0, ws, st);
+}
+
+hipError_t launch_backward(const BackwardPlan& p, const void* q, const void* k, const void* v, const float* la,
+                           const float* beta, const int32_t* cu, const float* S0, const void* dO, const float* dS_T,
+                           void* dq, void* dk, void* dv, float* dla, float* dbeta, float* dS0, void* workspace,
+                           hipStream_t stream) {
+  if (p.N == 0) return hipSuccess;
+  if (p.dt == KDA_BF16)
+    return backward_dims<bf16_t>(p, q, k, v, la, beta, cu, S0, dO, dS_T, dq, dk, dv, dla, dbeta, dS0, workspace,
+                                 stream);
+  return backward_dims<float>(p, q, k, v, la, beta, cu, S0, dO, dS_T, dq, dk, dv, dla, dbeta, dS0, workspace,
+                              stream);
+}
+
+}  // namespace kda

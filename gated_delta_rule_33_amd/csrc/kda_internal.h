@@ -55,4 +55,26 @@ hipError_t launch_prefill(const PrefillPlan& p, const void* q, const void* k, co
                           const float* beta, const int32_t* cu, const float* S0, void* o, float* S_T,
                           void* workspace, hipStream_t stream);
 
+// Chunk offsets per sequence (chunk_off[n] = sum_{i<n} ceil(L_i / C), [N + 1])
+// and the longest-first sequence order (identity when sort is 0).
+hipError_t launch_chunk_offsets(const int32_t* cu, int N, int C, int32_t* chunk_off, int32_t* order, int sort,
+                                hipStream_t st);
+
+// Backward workspace carve-up, computed on the host.
+struct BackwardPlan {
+  int N, T, H, dk, dv;
+  kda_dtype dt;
+  kda_gate gate;
+  int64_t max_chunks;
+  int sort;
+  size_t off_chunk_off, off_order, off_blocks, off_states, off_dstates, total_bytes;
+};
+
+bool make_backward_plan(const kda_prefill_desc* d, int64_t max_chunks, BackwardPlan* p);
+
+hipError_t launch_backward(const BackwardPlan& p, const void* q, const void* k, const void* v, const float* la,
+                           const float* beta, const int32_t* cu, const float* S0, const void* dO, const float* dS_T,
+                           void* dq, void* dk, void* dv, float* dla, float* dbeta, float* dS0, void* workspace,
+                           hipStream_t stream);
+
 }  // namespace kda

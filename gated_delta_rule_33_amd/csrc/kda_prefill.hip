@@ -214,6 +214,12 @@ __global__ __launch_bounds__(1024) void chunk_offsets_kernel(const int32_t* __re
   }
 }
 
+hipError_t launch_chunk_offsets(const int32_t* cu, int N, int C, int32_t* chunk_off, int32_t* order, int sort,
+                                hipStream_t st) {
+  hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(1024), 0, st, cu, N, C, chunk_off, order, sort, nullptr);
+  return hipGetLastError();
+}
+
 // Overlapped schedule: segments 0 .. j of the workspace blocks are written.
 // Launched on the prep stream after the last segment's prep, so the prep's
 // writes are complete and visible before the counter moves (the prep

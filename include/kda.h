@@ -254,11 +254,66 @@ kda_status kda_decode_step(int32_t B, int32_t H, int32_t dk, int32_t dv, kda_dty
                            const float* log_alpha, const float* beta,
                            float* S, void* o, void* stream);
 
+/*
+ * Bytes of device workspace kda_prefill_backward needs for `desc` (256-byte
+ * aligned pointer expected): per (64-token chunk, head) a block of chunk
+ * factors and two dk x dv states, fp32 (273 KiB for dk = dv = 128; the
+ * 131,072-token, 32-head case takes 17.9 GB).  Returns 0 for an invalid or
+ * unsupported desc.  Host-only; launches nothing.
+ */
+size_t kda_prefill_backward_workspace_size(const kda_prefill_desc* desc);
+
+/*
+ * Backward pass of kda_prefill (training).  The deep-read report trains the
+ * model (section 3.4) and gives the chunked forward (section 3.1) but no
+ * gradient; this is the exact derivative of the recurrence above, computed
+ * through the same chunked form (64-token chunks): for the scalar
+ *
+ *     L = sum_t <dO_t, o_t> + sum_{n,h} <dS_T[n,h], S_T[n,h]>
+ *
+ * it writes dL/dq, dL/dk, dL/dv, dL/dlog_alpha, dL/dbeta and dL/dS0.
+ *
+ *   q, k, v, log_alpha, beta, cu_seqlens, S0   as passed to kda_prefill
+ *   dO         [T_tot, H, dv]  io_dtype, cotangent of o
+ *   dS_T       [N, H, dk, dv]  float32 cotangent of S_T, or NULL (zero)
+ *   dq, dk     [T_tot, H, dk]  io_dtype, written
+ *   dv         [T_tot, H, dv]  io_dtype, written
+ *   dlog_alpha float32, written, shaped like log_alpha ([T_tot, H, dk]; [T_tot, H]
+ *              for KDA_GATE_SCALAR, where it is the sum over key channels);
+ *              unused (may be NULL) for KDA_GATE_NONE
+ *   dbeta      [T_tot, H]      float32, written
+ *   dS0        [N, H, dk, dv]  float32, written; NULL to skip
+ *   workspace  >= kda_prefill_backward_workspace_size(desc) bytes, 256-byte
+ *              aligned; contents on entry ignored, on return undefined.
+ *
+ * desc: as for kda_prefill, with chunk = 64 and no stages (the stages'
+ * derivatives are left to the caller's framework).  flags are ignored: the
+ * backward runs on `stream` only.  Outputs must not overlap any input, the
+ * workspace or each other.  Same device-side preconditions as kda_prefill
+ * (any finite log_alpha <= 0).  Results are deterministic: the same inputs
+ * give the same bits.
+ *
+ * Errors: KDA_ERR_INVALID_ARGUMENT (null pointer where data is required,
+ * overlapping buffers, misaligned workspace, bad host offsets),
+ * KDA_ERR_UNSUPPORTED (dk/dv not in {64,128}, chunk != 64, stages given),
+ * KDA_ERR_WORKSPACE_TOO_SMALL, KDA_ERR_DEVICE.  With total_tokens == 0 only
+ * dS0 = dS_T (or zero) is written.
+ */
+kda_status kda_prefill_backward(const kda_prefill_desc* desc,
+                                const void* q, const void* k, const void* v,
+                                const float* log_alpha, const float* beta,
+                                const int32_t* cu_seqlens, const float* S0,
+                                const void* dO, const float* dS_T,
+                                void* dq, void* dk, void* dv, float* dlog_alpha,
+                                float* dbeta, float* dS0,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* kda_status_string(kda_status s);
 
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH (2.0.0: desc.flags,
-   desc.gate and the gate argument of kda_decode_step). */
+   desc.gate and the gate argument of kda_decode_step; 2.1.0: the prefill
+   backward). */
 int32_t kda_version(void);
 
 #ifdef __cplusplus

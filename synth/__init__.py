@@ -40,6 +40,7 @@ import numpy as np
 BLOCK = 4096
 _MASK_STREAM = 1 << 20
 _S0_STREAM = 1 << 21
+_COT_STREAM = 1 << 22
 
 
 def _workers() -> int:
@@ -228,6 +229,39 @@ def make_stage_inputs(w: "PrefillInputs", seed: int, z_gate=None) -> StageInputs
     z_out = rnd(rng.standard_normal((T, H, dv), dtype=np.float32))
     nw = rng.uniform(0.5, 1.5, size=dv).astype(np.float32)
     return StageInputs(q_raw, k_raw, z_gate, z_out, nw)
+
+
+@dataclasses.dataclass
+class Cotangents:
+    """Cotangents for the backward pass: dO ~ N(0, 1) shaped like o (rounded
+    to the io dtype) and dS_T ~ N(0, dS_T_std^2) shaped like S_T, float32, or
+    None."""
+    dO: np.ndarray
+    dS_T: Optional[np.ndarray]
+
+
+def make_cotangents(w: "PrefillInputs", seed: int, dS_T_std: Optional[float] = 1.0) -> Cotangents:
+    """Seeded cotangents for the prefill input set ``w``: drawn in blocks of
+    BLOCK tokens from ``PCG64([seed, 2**22, j])`` (dO), then dS_T from
+    ``PCG64([seed, 2**22 + 1])``."""
+    T, H, dk = w.q.shape
+    dv = w.v.shape[-1]
+    N = len(w.cu_seqlens) - 1
+    rnd = bf16_round if w.io_dtype == "bf16" else (lambda x: x.astype(np.float32))
+    dO = np.empty((T, H, dv), np.float32)
+
+    def fill(j: int):
+        a, b = j * BLOCK, min(T, (j + 1) * BLOCK)
+        rng = np.random.Generator(np.random.PCG64([seed, _COT_STREAM, j]))
+        dO[a:b] = rnd(rng.standard_normal((BLOCK, H, dv), dtype=np.float32)[:b - a])
+
+    with concurrent.futures.ThreadPoolExecutor(_workers()) as ex:
+        list(ex.map(fill, range((T + BLOCK - 1) // BLOCK)))
+    dST = None
+    if dS_T_std is not None:
+        rng = np.random.Generator(np.random.PCG64([seed, _COT_STREAM + 1]))
+        dST = (rng.standard_normal((N, H, dk, dv), dtype=np.float32) * np.float32(dS_T_std)).astype(np.float32)
+    return Cotangents(dO, dST)
 
 
 def _loguniform_lengths(n: int, lo: int, hi: int):

@@ -192,3 +192,51 @@ def test_recovered_query_and_wait_limit_without_device():
     assert kda.set_wait_limit(0) == 5
     assert kda.set_wait_limit(-1) == 0
     assert kda.set_wait_limit(-1) == default
+
+
+def call_backward(d, ws=FAKE + (40 << 30), wsb=None, **over):
+    """kda_prefill_backward with disjoint fake device ranges (1 GiB apart)."""
+    lib = kda.load_library()
+    names = ["q", "k", "v", "la", "b", "cu", "S0", "dO", "dST", "dq", "dk", "dv", "dla", "db", "dS0"]
+    ptrs = {n: FAKE + ((10 + i) << 30) for i, n in enumerate(names)}
+    ptrs["S0"] = ptrs["dST"] = None
+    ptrs.update(over)
+    if wsb is None:
+        wsb = lib.kda_prefill_backward_workspace_size(ctypes.byref(d))
+    return lib.kda_prefill_backward(ctypes.byref(d), *[ptrs[n] for n in names], ws, wsb, None)
+
+
+def test_backward_workspace_and_validation_codes():
+    lib = kda.load_library()
+    d, keep = desc(cu_seqlens_host=[0, 60, 100])
+    need = lib.kda_prefill_backward_workspace_size(ctypes.byref(d))
+    # chunks: ceil(60/64) + ceil(40/64) = 2, heads 4; block + two states per slot
+    blk = (3 * 64 * 128 + 3 * 64 * 64 + 128 + 64 + 63) // 64 * 64 * 4
+    slots = 2 * 4
+    assert need >= slots * (blk + 2 * 128 * 128 * 4)
+    assert need < slots * (blk + 2 * 128 * 128 * 4) + 4096
+    for bad in (dict(chunk=32), dict(chunk=16), dict(dk=96),
+                dict(stages=kda.Stages(1, 1e-6, 0, None, 0.0, None))):
+        d2, k2 = desc(cu_seqlens_host=[0, 60, 100], **bad)
+        assert lib.kda_prefill_backward_workspace_size(ctypes.byref(d2)) == 0, bad
+    assert lib.kda_prefill_backward(None, *([None] * 16), 0, None) == kda.KDA_ERR_INVALID_ARGUMENT
+    for bad, code in ((dict(chunk=32), kda.KDA_ERR_UNSUPPORTED), (dict(dk=96), kda.KDA_ERR_UNSUPPORTED),
+                      (dict(stages=kda.Stages(1, 1e-6, 0, None, 0.0, None)), kda.KDA_ERR_UNSUPPORTED),
+                      (dict(cu_seqlens_host=[0, 70, 60]), kda.KDA_ERR_INVALID_ARGUMENT)):
+        d2, k2 = desc(**bad)
+        assert call_backward(d2, wsb=1 << 40) == code, bad
+    # missing required pointers, misaligned or short workspace, overlaps
+    for over in (dict(dO=None), dict(dq=None), dict(dla=None), dict(db=None), dict(cu=None)):
+        assert call_backward(d, **over) == kda.KDA_ERR_INVALID_ARGUMENT, over
+    assert call_backward(d, ws=FAKE + (40 << 30) + 16) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert call_backward(d, ws=None) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert call_backward(d, wsb=need - 1) == kda.KDA_ERR_WORKSPACE_TOO_SMALL
+    assert call_backward(d, dq=FAKE + (10 << 30)) == kda.KDA_ERR_INVALID_ARGUMENT  # dq on q
+    assert call_backward(d, dk=FAKE + (19 << 30) + 64) == kda.KDA_ERR_INVALID_ARGUMENT  # dk inside dq
+    assert call_backward(d, dS0=FAKE + (40 << 30)) == kda.KDA_ERR_INVALID_ARGUMENT  # dS0 on the workspace
+    # no gate: log_alpha and dlog_alpha are unused and may be NULL
+    d3, k3 = desc(cu_seqlens_host=[0, 60, 100], gate=kda.KDA_GATE_NONE)
+    assert lib.kda_prefill_backward_workspace_size(ctypes.byref(d3)) == need
+    # no sequences: nothing to do
+    d4, k4 = desc(num_seqs=0, total_tokens=0)
+    assert call_backward(d4, wsb=0) == kda.KDA_OK
