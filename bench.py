@@ -9,7 +9,10 @@ the final state.  Inputs are resident in HBM before timing starts.  The
 decode workload (256 requests x 32 heads, fp32 128x128 states updated in
 place for 1024 tokens) is timed in the same run and reported under "decode";
 the call rates of the 4 x 4096-token batch and of the 64-sequence varlen
-workload follow under "prefill_other" (skip with --no-other).
+workload follow under "prefill_other" (skip with --no-other), and the
+backward pass (kda_prefill_backward) on the 4 x 4096-token batch, checked
+against the oracle's backward, and on the long workload under "backward"
+(skip with --no-backward).
 
 Prints ONE JSON line.  `value` is prefill tokens/s.  Each roofline block
 prices the operator's algorithmic bytes per launch against MI355X's 8 TB/s
@@ -46,15 +49,19 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def source_digest() -> str:
-    """sha256 over the HIP sources; hardware-counter traffic is only reported
-    while it was measured on the same kernels."""
+# The source files that define each measured kernel sequence (with the
+# shared device header): hardware-counter traffic is reported only while
+# these are byte-identical to the ones it was measured on.
+TRAFFIC_SOURCES = {"prefill": ("kda_prefill.hip", "kda_device.h"), "decode": ("kda_decode.hip", "kda_device.h")}
+
+
+def source_digest(key: str) -> str:
+    """sha256 over the HIP sources of the kernels behind ``key``."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "gated_delta_rule_33_amd", "csrc")
-    for f in sorted(os.listdir(d)):
-        if f.endswith((".hip", ".h")):
-            h.update(f.encode())
-            h.update(open(os.path.join(d, f), "rb").read())
+    for f in TRAFFIC_SOURCES[key.split("_")[0]]:
+        h.update(f.encode())
+        h.update(open(os.path.join(d, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -64,7 +71,7 @@ def measured_traffic(key: str):
     except Exception:
         return None
     r = rec.get(key)
-    if not r or r.get("source_digest") != source_digest():
+    if not r or r.get("source_digest") != source_digest(key):
         return None
     return r.get("bytes_per_launch")
 
@@ -267,6 +274,98 @@ def run_prefill_rate(wname, args, torch, kda, synth, stages=False):
                               bytes_per_token_head=per_th))
 
 
+FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X dense fp32 MFMA
+
+
+def backward_algorithmic(T_tok: int, N: int, H: int, dk: int, dv: int, es: int, C: int, with_s0: bool,
+                         gate: str = "channel"):
+    """Compulsory bytes and method flops of one kda_prefill_backward call.
+    Bytes: read q, k, v, dO (io dtype), log_alpha (gate width x 4), beta;
+    write dq, dk, dv (io dtype), dlog_alpha, dbeta; states: read S0 and dS_T,
+    write dS0 (fp32).  Flops per token-head of the chunked backward (64-token
+    chunks, triangular C x C products at half): 20 dk dv (forward recompute
+    4 + 2, state cotangents 6, value-side cotangents 8) + 6 C dk (the gated
+    pair matrices A and P, 2; the gated pair sums, 4) + 8 C dv (the
+    triangular products with T, P and their transposes in the two state
+    passes and the value-side kernel, 6; the cotangent pair matrices dP and
+    dM, 2)."""
+    th = T_tok * H
+    gw = dk if GATE_WIDTH[gate] is None else GATE_WIDTH[gate]
+    per_th = 2 * ((2 * dk + dv) * es + gw * 4 + 4) + dv * es
+    state = N * H * dk * dv * 4 * (3 if with_s0 else 2)
+    flops_th = 20 * dk * dv + 6 * C * dk + 8 * C * dv
+    return th * per_th + state, th * flops_th, per_th, flops_th
+
+
+def run_backward(wname, args, torch, kda, synth, oracle, check: bool):
+    """kda_prefill_backward on a workload: call time, roofline against the
+    fp32 MFMA peak (the backward's products run in fp32), and, when
+    ``check``, the fp64 oracle's backward timed on the host over the whole
+    workload and compared element by element."""
+    w = synth.workload_prefill(wname)
+    cot = synth.make_cotangents(w, 7000 + synth.WORKLOADS[wname]["index"], dS_T_std=0.1)
+    bf = w.io_dtype == "bf16"
+    tdt = torch.bfloat16 if bf else torch.float32
+
+    def up(x, io=False):
+        t = torch.from_numpy(np.ascontiguousarray(x))
+        return (t.to(tdt) if io else t).cuda()
+
+    T_tok, H, dk = w.q.shape
+    dv = w.v.shape[2]
+    N = w.num_seqs
+    args_d = [up(w.q, True), up(w.k, True), up(w.v, True), up(w.log_alpha) if w.log_alpha is not None else None,
+              up(w.beta), up(w.cu_seqlens), up(w.S0) if w.S0 is not None else None, up(cot.dO, True), up(cot.dS_T)]
+    host_cu = w.cu_seqlens.tolist()
+    for _ in range(2):
+        g = kda.prefill_backward(*args_d, cu_seqlens_host=host_cu)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 5
+    e0.record(stream)
+    for _ in range(n):
+        g = kda.prefill_backward(*args_d, cu_seqlens_host=host_cu)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    call_s = e0.elapsed_time(e1) / n / 1e3
+    nbytes, nflops, per_th, flops_th = backward_algorithmic(T_tok, N, H, dk, dv, 2 if bf else 4, 64,
+                                                            w.S0 is not None, w.gate)
+    tfl = nflops / call_s / 1e12
+    res = dict(workload=wname, num_seqs=N, total_tokens=T_tok, heads=H, call_ms=round(call_s * 1e3, 4),
+               tokens_per_s=round(T_tok / call_s, 1),
+               roofline=dict(bound="mfma", achieved=round(tfl, 2), peak=FP32_MFMA_PEAK_TFLOPS, unit="TFLOP/s",
+                             frac=round(tfl / FP32_MFMA_PEAK_TFLOPS, 4), traffic=None,
+                             kernel="kda_prefill_backward (prep, state, dstate, grad_v, grad_k)",
+                             flops_per_launch=int(nflops), flops_per_token_head=flops_th,
+                             hbm_achieved=round(nbytes / call_s / 1e9, 1), hbm_frac=round(nbytes / call_s / 1e9 / HBM_PEAK_GBS, 4),
+                             bytes_per_launch=int(nbytes), bytes_per_token_head=per_th))
+    if check:
+        log("backward cpu baseline: oracle backward on %d tokens x %d heads ..." % (T_tok, H))
+        t1 = time.perf_counter()
+        ref = oracle.backward(w.q, w.k, w.v, w.log_alpha_channels(), w.beta, w.cu_seqlens, w.S0, cot.dO, cot.dS_T,
+                              threads=args.cpu_threads)
+        dt = time.perf_counter() - t1
+        cores = os.cpu_count() if args.cpu_threads <= 0 else args.cpu_threads
+        res["cpu_baseline"] = dict(value=round(T_tok / dt, 1), unit="tokens/s", cores=int(min(cores, N * H)),
+                                   kind="oracle", sample="whole workload (%d x %d tokens, %d heads), fp64 reverse-mode "
+                                                         "recurrence, %.1f s" % (N, T_tok // max(N, 1), H, dt))
+        if w.gate == "scalar":
+            ref["dlog_alpha"] = ref["dlog_alpha"].sum(axis=-1)
+        par = dict(tol=1e-2 if bf else 1e-4)
+        for name in ("dq", "dk", "dv", "dlog_alpha", "dbeta", "dS0"):
+            if g[name] is None or ref[name] is None:
+                continue
+            x = g[name].float().cpu().numpy().astype(np.float64)
+            par[name + "_rel_err"] = float(np.max(np.abs(x - ref[name])) / np.max(np.abs(ref[name])))
+        par["pass"] = all(v_ <= par["tol"] for k_, v_ in par.items() if k_.endswith("_rel_err"))
+        res["parity"] = par
+    del args_d, g
+    kda.clear_workspace_cache()
+    torch.cuda.empty_cache()
+    return res
+
+
 def decode_cpu_baseline(args, synth, oracle, B, H, dk, dv, std, seed):
     """fp64 oracle decode rate: the first steps of the decode workload on all
     host cores (every state), and on one thread (a slice of the states)."""
@@ -387,6 +486,7 @@ def main():
     ap.add_argument("--one-stream", action="store_true",
                     help="prefill on the caller's stream only (for hardware-counter runs)")
     ap.add_argument("--copy-probe", type=int, default=0, help="run only a device copy of this many bytes")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass lines")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this library has no multi-GPU path (each GPU would run "
@@ -415,6 +515,9 @@ def main():
         run_decode(args, torch, kda, synth, None, gate=g, steps=min(256, args.decode_steps)) for g in ("scalar", "none")]
     if dec_gates:
         dec_gates.append(run_decode(args, torch, kda, synth, None, steps=min(256, args.decode_steps), stages=True))
+    bwd = [] if args.no_backward else [
+        run_backward("batch4x4096_bf16", args, torch, kda, synth, oracle, check=not args.no_cpu_baseline),
+        run_backward(args.workload, args, torch, kda, synth, oracle, check=False)]
     wl = pre["workload"]
     line = {
         "metric": "KDA prefill tokens/s (MFMA % peak) at T=128k; decode state-updates/s (HBM %)",
@@ -445,12 +548,17 @@ def main():
         line["prefill_other"] = other
     if dec_gates:
         line["decode_gate_forms"] = dec_gates
+    if bwd:
+        line["backward"] = bwd
     print(json.dumps(line), flush=True)
     if pre["recovered"] or any(x.get("recovered") for x in other):
         log("the overlapped prefill schedule fell back to its recovery launches: timing invalid")
         sys.exit(3)
     if "parity" in pre and not pre["parity"]["pass"]:
         log("parity of the last timed call failed")
+        sys.exit(4)
+    if any("parity" in x and not x["parity"]["pass"] for x in bwd):
+        log("backward parity failed")
         sys.exit(4)
 
 
