@@ -35,7 +35,7 @@
 //   grad_v    (chunk, head) parallel over value columns: dv, dbeta and the
 //             value-side cotangents dQg, dKg, dKb, dP, dA, dgamma (written
 //             over the chunk's block)
-//   grad_k    (chunk, head, 32 key channels) parallel: the gated pair sums,
+//   grad_k    (chunk, head, 16 key channels) parallel: the gated pair sums,
 //             dq, dk and dlog alpha
 //
 // Exactness of the gates.  Every factor e^{G_r - G_s} (s <= r) is at most 1.
@@ -63,20 +63,39 @@ __device__ __forceinline__ f32x4 mf(float a, float b, f32x4 c) {
 }
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
-// Per-(chunk, head) block, fp32, row-major (offsets in floats).
+// Workgroup barrier for LDS hand-overs: waits for this wave's LDS traffic
+// only (lgkmcnt 0), not for its global loads and stores, so loads issued
+// ahead (the next chunk's operands) stay in flight across it.  Every
+// exchange between waves in this file goes through LDS; global results are
+// only read by later kernels.
+__device__ __forceinline__ void lds_sync() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt 63, expcnt 7, lgkmcnt 0
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Per-(chunk, head) block, fp32 (offsets in floats).  Each factor is stored
+// in the orientation its consumers read it in: an MFMA operand fragment is
+// then four consecutive floats of one row (16-byte loads), never a gather.
+// "T" planes are transposed: KbT[i][r] = Kb[r][i], PT[s][r] = P[r][s].
 template <int DK>
 struct BwdBlk {
-  static constexpr size_t oKg = 0;                                   // [BC][DK]
-  static constexpr size_t oKb = oKg + static_cast<size_t>(BC) * DK;  // [BC][DK]
-  static constexpr size_t oQg = oKb + static_cast<size_t>(BC) * DK;  // [BC][DK]
-  static constexpr size_t oT = oQg + static_cast<size_t>(BC) * DK;   // [BC][BC] lower, unit diagonal
-  static constexpr size_t oA = oT + BC * BC;                         // [BC][BC] strictly lower
-  static constexpr size_t oP = oA + BC * BC;                         // [BC][BC] lower incl. diagonal
-  static constexpr size_t oGam = oP + BC * BC;                       // [DK]
-  static constexpr size_t oBeta = oGam + DK;                         // [BC] (0 past the sequence)
+  static constexpr size_t CD = static_cast<size_t>(BC) * DK;
+  static constexpr size_t oKg = 0;              // [BC][DK]  k e^{G}
+  static constexpr size_t oKb = oKg + CD;       // [BC][DK]  k e^{G_C - G}
+  static constexpr size_t oKbT = oKb + CD;      // [DK][BC]
+  static constexpr size_t oKgT = oKbT + CD;     // [DK][BC]
+  static constexpr size_t oQgT = oKgT + CD;     // [DK][BC]  (q e^{G})^T
+  static constexpr size_t oT = oQgT + CD;       // [BC][BC]  lower, unit diagonal
+  static constexpr size_t oTT = oT + BC * BC;   // [BC][BC]  T^T
+  static constexpr size_t oPT = oTT + BC * BC;  // [BC][BC]  P^T (P lower incl. diagonal)
+  static constexpr size_t oA = oPT + BC * BC;   // [BC][BC]  strictly lower
+  static constexpr size_t oGam = oA + BC * BC;  // [DK]
+  static constexpr size_t oBeta = oGam + DK;    // [BC] (0 past the sequence)
   static constexpr size_t floats = (oBeta + BC + 63) / 64 * 64;
   // the value-side cotangents grad_v writes over the block it has read
-  static constexpr size_t odQg = oKg, odKg = oKb, odKb = oQg, odP = oT, odA = oA, odGam = oGam;
+  static constexpr size_t odQg = oKg, odKg = oKb, odKb = oKbT, odP = oT, odA = oA, odGam = oGam;
 };
 
 size_t blk_floats(int dk) { return dk == 128 ? BwdBlk<128>::floats : BwdBlk<64>::floats; }
@@ -118,6 +137,23 @@ __device__ __forceinline__ void store8(bf16_t* p, const float* x) {
                                        f32x2_to_bf16x2(x[4], x[5]), f32x2_to_bf16x2(x[6], x[7])};
 }
 
+// N (4 or 8) consecutive elements as floats, and back.
+template <int N, typename E>
+__device__ __forceinline__ void loadn(const E* p, float* x) {
+  if constexpr (N == 8) {
+    load8(p, x);
+  } else {
+    const f32x4 a = load4(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = a[i];
+  }
+}
+template <int N, typename E>
+__device__ __forceinline__ void storen(E* p, const float* x) {
+  if constexpr (N == 8) store8(p, x);
+  else store4(p, f32x4{x[0], x[1], x[2], x[3]});
+}
+
 // log alpha of token t, head h, channel ch for the three gate forms.
 template <int G, int DK>
 __device__ __forceinline__ float gate_at(const float* la, size_t t, int H, int h, int ch) {
@@ -126,34 +162,36 @@ __device__ __forceinline__ float gate_at(const float* la, size_t t, int H, int h
   else return 0.f;
 }
 
-// Inclusive running sum over the 64 rows of a 32-channel slice in LDS
+// Inclusive running sum over the 64 rows of an NCH-channel slice in LDS
 // (pitch PS), forward (REV = false) or from the last row back (REV = true).
-// 256 threads: thread (channel t % 32, segment t / 32) owns 8 rows.
-template <bool REV, int PS>
-__device__ __forceinline__ void row_scan32(float* x, float* tot /* [8][32] */) {
-  const int ch = threadIdx.x & 31, seg = threadIdx.x >> 5;
-  float v[8];
+// 256 threads: thread (channel t % NCH, segment t / NCH) owns 64 NCH / 256
+// consecutive rows.
+template <bool REV, int PS, int NCH = 32>
+__device__ __forceinline__ void row_scan(float* x, float* tot /* [256 / NCH][NCH] */) {
+  constexpr int SEG = 256 / NCH, RPS = BC / SEG;
+  const int ch = threadIdx.x % NCH, seg = threadIdx.x / NCH;
+  float v[RPS];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = x[(seg * 8 + i) * PS + ch];
+  for (int i = 0; i < RPS; ++i) v[i] = x[(seg * RPS + i) * PS + ch];
   if constexpr (!REV) {
 #pragma unroll
-    for (int i = 1; i < 8; ++i) v[i] += v[i - 1];
-    tot[seg * 32 + ch] = v[7];
+    for (int i = 1; i < RPS; ++i) v[i] += v[i - 1];
+    tot[seg * NCH + ch] = v[RPS - 1];
   } else {
 #pragma unroll
-    for (int i = 6; i >= 0; --i) v[i] += v[i + 1];
-    tot[seg * 32 + ch] = v[0];
+    for (int i = RPS - 2; i >= 0; --i) v[i] += v[i + 1];
+    tot[seg * NCH + ch] = v[0];
   }
-  __syncthreads();
+  lds_sync();
   float off = 0.f;
   if constexpr (!REV) {
-    for (int s = 0; s < seg; ++s) off += tot[s * 32 + ch];
+    for (int s = 0; s < seg; ++s) off += tot[s * NCH + ch];
   } else {
-    for (int s = seg + 1; s < 8; ++s) off += tot[s * 32 + ch];
+    for (int s = seg + 1; s < SEG; ++s) off += tot[s * NCH + ch];
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) x[(seg * 8 + i) * PS + ch] = v[i] + off;
-  __syncthreads();
+  for (int i = 0; i < RPS; ++i) x[(seg * RPS + i) * PS + ch] = v[i] + off;
+  lds_sync();
 }
 
 
@@ -215,17 +253,25 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, 
         gs[row * PS + ch] = row < cl.len ? gate_at<G, DK>(la, static_cast<size_t>(cl.t0 + row), H, h, c0 + ch) : 0.f;
       }
     }
-    __syncthreads();
-    row_scan32<false, PS>(gs, tot);
+    lds_sync();
+    row_scan<false, PS>(gs, tot);
     for (int e = tid; e < BC * 32; e += 256) {
       const int row = e >> 5, ch = e & 31;
       const float Gr = gs[row * PS + ch], GC = gs[(BC - 1) * PS + ch];
       const float eg = __expf(Gr), eb = __expf(GC - Gr);
-      const float kv = ks[row * PS + ch], qv = qs[row * PS + ch];
+      const float kv = ks[row * PS + ch];
       const size_t o = static_cast<size_t>(row) * DK + c0 + ch;
       bk[B::oKg + o] = kv * eg;
       bk[B::oKb + o] = kv * eb;
-      bk[B::oQg + o] = qv * eg;
+    }
+    for (int e = tid; e < BC * 32; e += 256) {  // transposed planes: consecutive threads, consecutive rows
+      const int row = e & 63, ch = e >> 6;
+      const float Gr = gs[row * PS + ch], GC = gs[(BC - 1) * PS + ch];
+      const float eg = __expf(Gr), eb = __expf(GC - Gr);
+      const size_t o = static_cast<size_t>(c0 + ch) * BC + row;
+      bk[B::oKbT + o] = ks[row * PS + ch] * eb;
+      bk[B::oKgT + o] = ks[row * PS + ch] * eg;
+      bk[B::oQgT + o] = qs[row * PS + ch] * eg;
     }
     if (tid < 32) bk[B::oGam + c0 + tid] = __expf(gs[(BC - 1) * PS + tid]);
     // off-diagonal block pairs (I, J < I), split at row 16 I - 1
@@ -263,7 +309,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, 
         }
       }
     }
-    __syncthreads();
+    lds_sync();
   }
   // A and P to the block (upper blocks zero), L = Diag(beta) A and T = 0 in LDS
   auto put = [&](int I, int J, f32x4 a, f32x4 p) {
@@ -271,9 +317,10 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, 
     for (int m = 0; m < 4; ++m) {
       const int row = 16 * I + 4 * g + m, col = 16 * J + r;
       bk[B::oA + row * BC + col] = a[m];
-      bk[B::oP + row * BC + col] = p[m];
       Lm[row * LPC + col] = bet[row] * a[m];
     }
+    // P^T: rows 16 I + 4 g .. + 3 of P are four consecutive floats of row col
+    *reinterpret_cast<f32x4*>(bk + B::oPT + (16 * J + r) * BC + 16 * I + 4 * g) = p;
   };
   put(w, w, aD, pD);
 #pragma unroll
@@ -283,12 +330,12 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, 
     const int row = e >> 6, col = e & 63;
     if ((col >> 4) > (row >> 4)) {
       bk[B::oA + e] = 0.f;
-      bk[B::oP + e] = 0.f;
+      bk[B::oPT + col * BC + row] = 0.f;
       Lm[row * LPC + col] = 0.f;
     }
     Tm[row * LPC + col] = 0.f;
   }
-  __syncthreads();
+  lds_sync();
   // T = (I + L)^{-1}, unit lower triangular.  Diagonal 16-blocks: one
   // thread per column, forward substitution.
   if (tid < BC) {
@@ -306,7 +353,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, 
 #pragma unroll
     for (int a = 0; a < 16; ++a) Tm[(base + a) * LPC + base + c] = x[a];
   }
-  __syncthreads();
+  lds_sync();
   // Off-diagonal blocks, one block row at a time:
   // T_IJ = -T_II sum_{K=J}^{I-1} L_IK T_KJ (wave J of block row I).
   for (int I = 1; I < 4; ++I) {
@@ -320,7 +367,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, 
 #pragma unroll
       for (int m = 0; m < 4; ++m) Xs[w][(4 * g + m) * 17 + r] = acc[m];
     }
-    __syncthreads();
+    lds_sync();
     if (act) {
       f32x4 t = zero4();
 #pragma unroll
@@ -328,9 +375,12 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, 
 #pragma unroll
       for (int m = 0; m < 4; ++m) Tm[(16 * I + 4 * g + m) * LPC + 16 * w + r] = -t[m];
     }
-    __syncthreads();
+    lds_sync();
   }
-  for (int e = tid; e < BC * BC; e += 256) bk[B::oT + e] = Tm[(e >> 6) * LPC + (e & 63)];
+  for (int e = tid; e < BC * BC; e += 256) {
+    bk[B::oT + e] = Tm[(e >> 6) * LPC + (e & 63)];
+    bk[B::oTT + e] = Tm[(e & 63) * LPC + (e >> 6)];
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -371,7 +421,7 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(const T* __restrict__ v,
     }
   struct Ops {
     f32x4 kg[NKB];
-    float kbt[TPW][16];
+    f32x4 kbt[TPW][4];
     f32x4 tt[4];
     float vv[4], bet[4], gam[TPW][4];
   };
@@ -383,15 +433,18 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(const T* __restrict__ v,
 #pragma unroll
     for (int t = 0; t < TPW; ++t)
 #pragma unroll
-      for (int s = 0; s < 16; ++s) o.kbt[t][s] = bk[B::oKb + (4 * s + g) * DK + 16 * (w * TPW + t) + r];
+      for (int b = 0; b < 4; ++b)
+        o.kbt[t][b] = *reinterpret_cast<const f32x4*>(bk + B::oKbT + (16 * (w * TPW + t) + r) * BC + 16 * b + 4 * g);
 #pragma unroll
     for (int b = 0; b < 4; ++b)
       o.tt[b] = b <= w ? *reinterpret_cast<const f32x4*>(bk + B::oT + row * BC + 16 * b + 4 * g) : zero4();
     const int t0 = tb + c * BC, len = min(BC, L - c * BC);
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      const int rr = 16 * w + 4 * g + m;
-      o.vv[m] = rr < len ? io<T>::load(v + (static_cast<size_t>(t0 + rr) * H + h) * DV + col) : 0.f;
+      // rows past the sequence read the last row: their beta is 0, so W is 0
+      // there whatever v holds (no branch, no wait on the load here)
+      const int rr = 16 * w + 4 * g + m, rc = min(rr, len - 1);
+      o.vv[m] = io<T>::load(v + (static_cast<size_t>(t0 + rc) * H + h) * DV + col);
       o.bet[m] = bk[B::oBeta + rr];
     }
 #pragma unroll
@@ -402,6 +455,10 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(const T* __restrict__ v,
   Ops cur, nxt;
   if (nch > 0) load(0, cur);
   for (int c = 0; c < nch; ++c) {
+    // next chunk's operands first: the memory counter is in order, so the
+    // wait for these loads at the end of the chunk does not also wait for the
+    // state stores issued after them
+    if (c + 1 < nch) load(c + 1, nxt);
     float* so = sc + (static_cast<size_t>(j0 + c) * H + h) * DK * DV;
 #pragma unroll
     for (int t = 0; t < TPW; ++t)
@@ -411,8 +468,7 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(const T* __restrict__ v,
         Xl[row * P20 + r] = X[t][m];
         so[static_cast<size_t>(row) * DV + col] = X[t][m];
       }
-    __syncthreads();
-    if (c + 1 < nch) load(c + 1, nxt);
+    lds_sync();
     f32x4 acc = zero4();
 #pragma unroll
     for (int b = 0; b < NKB; ++b)
@@ -420,7 +476,7 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(const T* __restrict__ v,
       for (int m = 0; m < 4; ++m) acc = mf(cur.kg[b][m], Xl[(16 * b + 4 * g + m) * P20 + r], acc);
 #pragma unroll
     for (int m = 0; m < 4; ++m) Wl[(16 * w + 4 * g + m) * P20 + r] = cur.bet[m] * (cur.vv[m] - acc[m]);
-    __syncthreads();
+    lds_sync();
     acc = zero4();
 #pragma unroll
     for (int b = 0; b < 4; ++b)
@@ -429,13 +485,15 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(const T* __restrict__ v,
         for (int m = 0; m < 4; ++m) acc = mf(cur.tt[b][m], Wl[(16 * b + 4 * g + m) * P20 + r], acc);
 #pragma unroll
     for (int m = 0; m < 4; ++m) Ul[(16 * w + 4 * g + m) * P20 + r] = acc[m];
-    __syncthreads();
+    lds_sync();
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
 #pragma unroll
       for (int m = 0; m < 4; ++m) X[t][m] *= cur.gam[t][m];
 #pragma unroll
-      for (int s = 0; s < 16; ++s) X[t] = mf(cur.kbt[t][s], Ul[(4 * s + g) * P20 + r], X[t]);
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) X[t] = mf(cur.kbt[t][b][m], Ul[(16 * b + 4 * g + m) * P20 + r], X[t]);
     }
     cur = nxt;
   }
@@ -474,10 +532,25 @@ __global__ __launch_bounds__(256) void bwd_dstate_kernel(const T* __restrict__ d
   typedef typename raw4<T>::type R4;
   struct Ops {
     f32x4 kb[NKB];
-    float pt[16], tt[16];
-    float qgt[TPW][16], kgt[TPW][16];
+    f32x4 pt[4], tt[4];
     R4 dov;
     float bet[4], gam[TPW][4];
+  };
+  // Qg^T and Kg^T rows of the wave's key channels: read at the start of the
+  // chunk that uses them (last phase), not a chunk ahead, to bound registers
+  struct OpsLate {
+    f32x4 qgt[TPW][4], kgt[TPW][4];
+  };
+  auto load_late = [&](int c, OpsLate& o) {
+    const float* bk = blk + (static_cast<size_t>(j0 + c) * H + h) * B::floats;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int o2 = (16 * (w * TPW + t) + r) * BC + 16 * b + 4 * g;
+        o.qgt[t][b] = *reinterpret_cast<const f32x4*>(bk + B::oQgT + o2);
+        o.kgt[t][b] = *reinterpret_cast<const f32x4*>(bk + B::oKgT + o2);
+      }
   };
   const int drow = tid >> 2, dc4 = (tid & 3) * 4;  // this thread's 4 dO values for the LDS tile
   auto load = [&](int c, Ops& o) {
@@ -486,22 +559,15 @@ __global__ __launch_bounds__(256) void bwd_dstate_kernel(const T* __restrict__ d
 #pragma unroll
     for (int b = 0; b < NKB; ++b) o.kb[b] = *reinterpret_cast<const f32x4*>(bk + B::oKb + row * DK + 16 * b + 4 * g);
 #pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      const bool on = s >= 4 * w;
-      o.pt[s] = on ? bk[B::oP + (4 * s + g) * BC + row] : 0.f;
-      o.tt[s] = on ? bk[B::oT + (4 * s + g) * BC + row] : 0.f;
+    for (int b = 0; b < 4; ++b) {
+      const bool on = b >= w;
+      o.pt[b] = on ? *reinterpret_cast<const f32x4*>(bk + B::oPT + row * BC + 16 * b + 4 * g) : zero4();
+      o.tt[b] = on ? *reinterpret_cast<const f32x4*>(bk + B::oTT + row * BC + 16 * b + 4 * g) : zero4();
     }
-#pragma unroll
-    for (int t = 0; t < TPW; ++t)
-#pragma unroll
-      for (int s = 0; s < 16; ++s) {
-        const int o2 = (4 * s + g) * DK + 16 * (w * TPW + t) + r;
-        o.qgt[t][s] = bk[B::oQg + o2];
-        o.kgt[t][s] = bk[B::oKg + o2];
-      }
     const int t0 = tb + c * BC, len = min(BC, L - c * BC);
-    o.dov = R4{};
-    if (drow < len) o.dov = load4raw(dO + (static_cast<size_t>(t0 + drow) * H + h) * DV + sp * 16 + dc4);
+    // rows past the sequence read the last row: P and Qg are zero in those
+    // rows, so their dO never contributes (no branch, no wait on the load here)
+    o.dov = load4raw(dO + (static_cast<size_t>(t0 + min(drow, len - 1)) * H + h) * DV + sp * 16 + dc4);
 #pragma unroll
     for (int m = 0; m < 4; ++m) o.bet[m] = bk[B::oBeta + 16 * w + 4 * g + m];
 #pragma unroll
@@ -512,8 +578,11 @@ __global__ __launch_bounds__(256) void bwd_dstate_kernel(const T* __restrict__ d
   Ops cur, nxt;
   if (nch > 0) load(nch - 1, cur);
   for (int c = nch - 1; c >= 0; --c) {
+    OpsLate late;
+    load_late(c, late);
+    if (c > 0) load(c - 1, nxt);  // before the state stores (see bwd_state_kernel)
     float* so = dsc + (static_cast<size_t>(j0 + c) * H + h) * DK * DV;
-    __syncthreads();  // the previous chunk's readers of Dl and Yl are done
+    lds_sync();  // the previous chunk's readers of Dl and Yl are done
 #pragma unroll
     for (int t = 0; t < TPW; ++t)
 #pragma unroll
@@ -527,34 +596,40 @@ __global__ __launch_bounds__(256) void bwd_dstate_kernel(const T* __restrict__ d
 #pragma unroll
       for (int i = 0; i < 4; ++i) Dl[drow * P20 + dc4 + i] = d[i];
     }
-    __syncthreads();
-    if (c > 0) load(c - 1, nxt);
+    lds_sync();
     f32x4 acc = zero4();
 #pragma unroll
-    for (int s = 0; s < 16; ++s)
-      if (s >= 4 * w) acc = mf(cur.pt[s], Dl[(4 * s + g) * P20 + r], acc);
+    for (int b = 0; b < 4; ++b)
+      if (b >= w)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) acc = mf(cur.pt[b][m], Dl[(16 * b + 4 * g + m) * P20 + r], acc);
 #pragma unroll
     for (int b = 0; b < NKB; ++b)
 #pragma unroll
       for (int m = 0; m < 4; ++m) acc = mf(cur.kb[b][m], Xl[(16 * b + 4 * g + m) * P20 + r], acc);
 #pragma unroll
     for (int m = 0; m < 4; ++m) Zl[(16 * w + 4 * g + m) * P20 + r] = acc[m];
-    __syncthreads();
+    lds_sync();
     acc = zero4();
 #pragma unroll
-    for (int s = 0; s < 16; ++s)
-      if (s >= 4 * w) acc = mf(cur.tt[s], Zl[(4 * s + g) * P20 + r], acc);
+    for (int b = 0; b < 4; ++b)
+      if (b >= w)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) acc = mf(cur.tt[b][m], Zl[(16 * b + 4 * g + m) * P20 + r], acc);
 #pragma unroll
     for (int m = 0; m < 4; ++m) Yl[(16 * w + 4 * g + m) * P20 + r] = -cur.bet[m] * acc[m];
-    __syncthreads();
+    lds_sync();
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
 #pragma unroll
       for (int m = 0; m < 4; ++m) X[t][m] *= cur.gam[t][m];
 #pragma unroll
-      for (int s = 0; s < 16; ++s) X[t] = mf(cur.qgt[t][s], Dl[(4 * s + g) * P20 + r], X[t]);
+      for (int b = 0; b < 4; ++b)
 #pragma unroll
-      for (int s = 0; s < 16; ++s) X[t] = mf(cur.kgt[t][s], Yl[(4 * s + g) * P20 + r], X[t]);
+        for (int m = 0; m < 4; ++m) {
+          X[t] = mf(late.qgt[t][b][m], Dl[(16 * b + 4 * g + m) * P20 + r], X[t]);
+          X[t] = mf(late.kgt[t][b][m], Yl[(16 * b + 4 * g + m) * P20 + r], X[t]);
+        }
     }
     cur = nxt;
   }
@@ -571,36 +646,106 @@ __global__ __launch_bounds__(256) void bwd_dstate_kernel(const T* __restrict__ d
 
 
 // ---------------------------------------------------------------------------
+// Split-bf16 products.  An fp32 operand x is carried as hi = bf16(x) and
+// lo = bf16(x - hi) (hi + lo = x to ~2^-17 relative); a product of two such
+// operands is formed by three bf16 MFMAs (lo*hi + hi*lo + hi*hi, the small
+// terms first), dropping lo*lo: ~2^-16 relative per product, at 16,384 flops
+// per 16x16x32 instruction against 2,048 for the fp32 16x16x4 MFMA.
+// Fragments use the natural k map: lane (row or column l % 16, group
+// g = l / 16) holds k = 8 g .. 8 g + 7 of the 32-wide k step.
+// ---------------------------------------------------------------------------
+struct F3 {
+  bf16x8 h, l;
+};
+__device__ __forceinline__ F3 split8(f32x4 a, f32x4 b, float scale = 1.f) {
+  F3 f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float x = a[i] * scale, y = b[i] * scale;
+    f.h[i] = static_cast<__bf16>(x);
+    f.h[4 + i] = static_cast<__bf16>(y);
+    f.l[i] = static_cast<__bf16>(x - static_cast<float>(f.h[i]));
+    f.l[4 + i] = static_cast<__bf16>(y - static_cast<float>(f.h[4 + i]));
+  }
+  return f;
+}
+// eight consecutive floats (16-byte aligned) from LDS or global memory
+__device__ __forceinline__ F3 split8(const float* p, float scale = 1.f) {
+  return split8(*reinterpret_cast<const f32x4*>(p), *reinterpret_cast<const f32x4*>(p + 4), scale);
+}
+__device__ __forceinline__ f32x4 mm3(const F3& a, const F3& b, f32x4 c) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.l, b.h, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.h, b.l, c, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.h, b.h, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
 // grad_v: one workgroup (4 waves) per (chunk, head); grid (chunks, H).  Walks
-// the value columns 16 at a time.  Per slice, wave w on rows 16 w .. 16 w + 15:
+// the value columns 32 at a time (one 32-wide k step of the products over
+// value columns).  Per slice, wave w on rows 16 w .. 16 w + 15:
 //   Vt = V - Kg S0, W = Diag(beta) Vt, U = T W
 //   dU = P^T dO + Kb dS_C, dW = T^T dU, dv = Diag(beta) dW
 // then every wave adds the slice's share of the contractions over value
 // columns into its MFMA tiles: dP, dM = -dW U^T, dQg, dKg = -dv S0^T, dKb.
-// At the end dbeta and dv are written out, and dQg, dKg, dKb, dP, dA =
-// Diag(beta) dM, dgamma over the chunk's block (everything it read from the
-// block has been consumed by then).
+// Each operand sits in LDS in the orientation whose fragments are eight
+// consecutive floats (the S0, dS_C and dO slices both ways, W, dU transposed,
+// U and dW by rows).  At the end dbeta and dv are written out, and dQg, dKg,
+// dKb, dP, dA = Diag(beta) dM, dgamma over the chunk's block (everything it
+// read from the block has been consumed by then).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void tri_ij(int e, int& I, int& J) {
   I = e >= 6 ? 3 : (e >= 3 ? 2 : (e >= 1 ? 1 : 0));
   J = e - I * (I + 1) / 2;
 }
 
+template <int DK>
+struct GradVLds {
+  static constexpr int PW = 36;       // pitch of [*][32] slices
+  static constexpr int PC = BC + 4;   // pitch of [*][64] (transposed, k = chunk row)
+  static constexpr int PK = DK + 4;   // pitch of [*][DK] (transposed, k = key channel)
+  static constexpr int oS0 = 0;                    // [DK][PW]  S0 columns of the slice
+  static constexpr int oS0T = oS0 + DK * PW;       // [32][PK]
+  static constexpr int odS = oS0T + 32 * PK;       // [DK][PW]
+  static constexpr int odST = odS + DK * PW;       // [32][PK]
+  static constexpr int odO = odST + 32 * PK;       // [BC][PW]
+  static constexpr int odOT = odO + BC * PW;       // [32][PC]
+  static constexpr int oV = odOT + 32 * PC;        // [BC][PW]
+  static constexpr int oVt = oV + BC * PW;         // [BC][PW]
+  static constexpr int oWT = oVt + BC * PW;        // [32][PC]
+  static constexpr int odUT = oWT + 32 * PC;       // [32][PC]
+  static constexpr int oU = odUT + 32 * PC;        // [BC][PW]
+  static constexpr int odW = oU + BC * PW;         // [BC][PW]
+  static constexpr int oBet = odW + BC * PW;       // [BC]
+  static constexpr int oDbp = oBet + BC;           // [BC][5]
+  static constexpr int floats = oDbp + BC * 5;
+};
+
 template <typename T, int DK, int DV>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_grad_v_kernel(const T* __restrict__ v, const T* __restrict__ dO,
-                                                         const int32_t* __restrict__ cu,
-                                                         const int32_t* __restrict__ chunk_off, int N, int H,
-                                                         float* __restrict__ blk, const float* __restrict__ sc,
-                                                         const float* __restrict__ dsc, T* __restrict__ dv,
-                                                         float* __restrict__ dbeta) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_grad_v_kernel(
+    const T* __restrict__ v, const T* __restrict__ dO, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ chunk_off, int N, int H, float* __restrict__ blk, const float* __restrict__ sc,
+    const float* __restrict__ dsc, T* __restrict__ dv, float* __restrict__ dbeta) {
   typedef BwdBlk<DK> B;
-  constexpr int NSP = DV / 16, NKB = DK / 16;
+  typedef GradVLds<DK> LL;
+  constexpr int NSP = DV / 32, NKB = DK / 16, NKS = DK / 32;
   constexpr int NTILE = 20 + 3 * 4 * NKB;  // dP (10), dM (10), dQg, dKg, dKb (4 NKB each)
   constexpr int NT = (NTILE + 3) / 4;
-  __shared__ float S0l[DK * P20], dSl[DK * P20];
-  __shared__ float Vl[BC * P20], Dl[BC * P20], Vtl[BC * P20], Wl[BC * P20], Ul[BC * P20], dUl[BC * P20],
-      dWl[BC * P20];
-  __shared__ float betl[BC], dbp[BC * 5];  // dbeta parts: [row][J] from dM tiles, [row][4] from dW . Vt
+  constexpr int PW = LL::PW, PC = LL::PC, PK = LL::PK;
+  __shared__ __align__(16) float lds[LL::floats];
+  float* S0l = lds + LL::oS0;
+  float* S0T = lds + LL::oS0T;
+  float* dSl = lds + LL::odS;
+  float* dST = lds + LL::odST;
+  float* Dl = lds + LL::odO;
+  float* DT = lds + LL::odOT;
+  float* Vl = lds + LL::oV;
+  float* Vtl = lds + LL::oVt;
+  float* WT = lds + LL::oWT;
+  float* dUT = lds + LL::odUT;
+  float* Ul = lds + LL::oU;
+  float* dWl = lds + LL::odW;
+  float* betl = lds + LL::oBet;
+  float* dbp = lds + LL::oDbp;
   const int j = blockIdx.x, h = blockIdx.y;
   if (j >= chunk_off[N]) return;
   const ChunkLoc cl = locate(cu, chunk_off, N, j);
@@ -608,107 +753,105 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const float* s0 = sc + (static_cast<size_t>(j) * H + h) * DK * DV;
   const float* dsC = dsc + (static_cast<size_t>(j) * H + h) * DK * DV;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
-  const int rt = w;  // row tile of the wave
   if (tid < BC) betl[tid] = bk[B::oBeta + tid];
   for (int e = tid; e < BC * 5; e += 256) dbp[e] = 0.f;
-  // block operands of the wave's row tile, read once
-  f32x4 kg[NKB], kb[NKB], tt[4];
-  float pt[16], ttt[16], bet[4];
+  // block operands of the wave's row tile (rows 16 w + r), split once
+  F3 kgf[NKS], kbf[NKS], tf[2], ptf[2], ttf[2];
   {
-    const int row = 16 * rt + r;
+    const int row = 16 * w + r;
 #pragma unroll
-    for (int b = 0; b < NKB; ++b) {
-      kg[b] = *reinterpret_cast<const f32x4*>(bk + B::oKg + row * DK + 16 * b + 4 * g);
-      kb[b] = *reinterpret_cast<const f32x4*>(bk + B::oKb + row * DK + 16 * b + 4 * g);
+    for (int kk = 0; kk < NKS; ++kk) {
+      kgf[kk] = split8(bk + B::oKg + row * DK + 32 * kk + 8 * g);
+      kbf[kk] = split8(bk + B::oKb + row * DK + 32 * kk + 8 * g);
     }
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
-      tt[b] = b <= rt ? *reinterpret_cast<const f32x4*>(bk + B::oT + row * BC + 16 * b + 4 * g) : zero4();
-#pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      const bool on = s >= 4 * rt;
-      pt[s] = on ? bk[B::oP + (4 * s + g) * BC + row] : 0.f;
-      ttt[s] = on ? bk[B::oT + (4 * s + g) * BC + row] : 0.f;
+    for (int kk = 0; kk < 2; ++kk) {
+      tf[kk] = split8(bk + B::oT + row * BC + 32 * kk + 8 * g);
+      ptf[kk] = split8(bk + B::oPT + row * BC + 32 * kk + 8 * g);
+      ttf[kk] = split8(bk + B::oTT + row * BC + 32 * kk + 8 * g);
     }
-#pragma unroll
-    for (int m = 0; m < 4; ++m) bet[m] = bk[B::oBeta + 16 * rt + 4 * g + m];
   }
+  float bet[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) bet[m] = bk[B::oBeta + 16 * w + 4 * g + m];
+  // k steps (32 chunk rows each) a triangular factor of row tile w needs:
+  // T (lower): rows <= 16 w + 15;  T^T, P^T: rows >= 16 w
+  const int kT1 = w >= 2 ? 1 : 0, kU0 = w >= 2 ? 1 : 0;
   f32x4 acc[NT];
 #pragma unroll
   for (int u = 0; u < NT; ++u) acc[u] = zero4();
   float db1[4] = {0.f, 0.f, 0.f, 0.f}, dg = 0.f;
   for (int sp = 0; sp < NSP; ++sp) {
-    // slice inputs: S0 and dS_C columns (DK x 16), v and dO rows (BC x 16)
-    for (int e = tid; e < DK * 4; e += 256) {
-      const int row = e >> 2, c4 = (e & 3) * 4;
-      const f32x4 a = *reinterpret_cast<const f32x4*>(s0 + static_cast<size_t>(row) * DV + sp * 16 + c4);
-      const f32x4 b = *reinterpret_cast<const f32x4*>(dsC + static_cast<size_t>(row) * DV + sp * 16 + c4);
+    // slice inputs, both orientations
+    for (int e = tid; e < DK * 8; e += 256) {
+      const int row = e >> 3, c4 = (e & 7) * 4;
+      const f32x4 a = *reinterpret_cast<const f32x4*>(s0 + static_cast<size_t>(row) * DV + sp * 32 + c4);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(dsC + static_cast<size_t>(row) * DV + sp * 32 + c4);
+      *reinterpret_cast<f32x4*>(S0l + row * PW + c4) = a;
+      *reinterpret_cast<f32x4*>(dSl + row * PW + c4) = b;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) S0l[row * P20 + c4 + i] = a[i], dSl[row * P20 + c4 + i] = b[i];
+      for (int i = 0; i < 4; ++i) S0T[(c4 + i) * PK + row] = a[i], dST[(c4 + i) * PK + row] = b[i];
     }
-    {
-      const int row = tid >> 2, c4 = (tid & 3) * 4;
+    for (int e = tid; e < BC * 8; e += 256) {
+      const int row = e >> 3, c4 = (e & 7) * 4;
       f32x4 x = zero4(), y = zero4();
       if (row < cl.len) {
-        const size_t o = (static_cast<size_t>(cl.t0 + row) * H + h) * DV + sp * 16 + c4;
+        const size_t o = (static_cast<size_t>(cl.t0 + row) * H + h) * DV + sp * 32 + c4;
         x = load4(v + o);
         y = load4(dO + o);
       }
+      *reinterpret_cast<f32x4*>(Vl + row * PW + c4) = x;
+      *reinterpret_cast<f32x4*>(Dl + row * PW + c4) = y;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Vl[row * P20 + c4 + i] = x[i], Dl[row * P20 + c4 + i] = y[i];
+      for (int i = 0; i < 4; ++i) DT[(c4 + i) * PC + row] = y[i];
     }
-    __syncthreads();
-    {
-      f32x4 a = zero4();
+    lds_sync();
+    // Vt, W = beta Vt (transposed) and dU (transposed) for the two 16-column tiles
 #pragma unroll
-      for (int b = 0; b < NKB; ++b)
+    for (int nt = 0; nt < 2; ++nt) {
+      const int n = 16 * nt + r;
+      f32x4 a = zero4(), d = zero4();
 #pragma unroll
-        for (int m = 0; m < 4; ++m) a = mf(kg[b][m], S0l[(16 * b + 4 * g + m) * P20 + r], a);
+      for (int kk = 0; kk < NKS; ++kk) {
+        a = mm3(kgf[kk], split8(S0T + n * PK + 32 * kk + 8 * g), a);
+        d = mm3(kbf[kk], split8(dST + n * PK + 32 * kk + 8 * g), d);
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+        if (kk >= kU0) d = mm3(ptf[kk], split8(DT + n * PC + 32 * kk + 8 * g), d);
+      f32x4 wv;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const int row = 16 * rt + 4 * g + m;
-        const float vt = Vl[row * P20 + r] - a[m];
-        Vtl[row * P20 + r] = vt;
-        Wl[row * P20 + r] = bet[m] * vt;
+        const int row = 16 * w + 4 * g + m;
+        const float vt = Vl[row * PW + n] - a[m];
+        Vtl[row * PW + n] = vt;
+        wv[m] = bet[m] * vt;
       }
+      *reinterpret_cast<f32x4*>(WT + n * PC + 16 * w + 4 * g) = wv;
+      *reinterpret_cast<f32x4*>(dUT + n * PC + 16 * w + 4 * g) = d;
     }
-    {
-      f32x4 a = zero4();
+    lds_sync();
+    // U = T W (rows) and dW = T^T dU (rows), dv, dbeta's write share
 #pragma unroll
-      for (int s = 0; s < 16; ++s)
-        if (s >= 4 * rt) a = mf(pt[s], Dl[(4 * s + g) * P20 + r], a);
+    for (int nt = 0; nt < 2; ++nt) {
+      const int n = 16 * nt + r;
+      f32x4 a = zero4(), d = zero4();
 #pragma unroll
-      for (int b = 0; b < NKB; ++b)
-#pragma unroll
-        for (int m = 0; m < 4; ++m) a = mf(kb[b][m], dSl[(16 * b + 4 * g + m) * P20 + r], a);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) dUl[(16 * rt + 4 * g + m) * P20 + r] = a[m];
-    }
-    __syncthreads();
-    {
-      f32x4 a = zero4();
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-        if (b <= rt)
-#pragma unroll
-          for (int m = 0; m < 4; ++m) a = mf(tt[b][m], Wl[(16 * b + 4 * g + m) * P20 + r], a);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) Ul[(16 * rt + 4 * g + m) * P20 + r] = a[m];
-    }
-    {
-      f32x4 a = zero4();
-#pragma unroll
-      for (int s = 0; s < 16; ++s)
-        if (s >= 4 * rt) a = mf(ttt[s], dUl[(4 * s + g) * P20 + r], a);
+      for (int kk = 0; kk < 2; ++kk) {
+        if (kk <= kT1) a = mm3(tf[kk], split8(WT + n * PC + 32 * kk + 8 * g), a);
+        if (kk >= kU0) d = mm3(ttf[kk], split8(dUT + n * PC + 32 * kk + 8 * g), d);
+      }
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const int row = 16 * rt + 4 * g + m;
-        dWl[row * P20 + r] = a[m];
-        db1[m] += a[m] * Vtl[row * P20 + r];
-        if (row < cl.len) io<T>::store(dv + (static_cast<size_t>(cl.t0 + row) * H + h) * DV + sp * 16 + r, bet[m] * a[m]);
+        const int row = 16 * w + 4 * g + m;
+        Ul[row * PW + n] = a[m];
+        dWl[row * PW + n] = d[m];
+        db1[m] += d[m] * Vtl[row * PW + n];
+        if (row < cl.len) io<T>::store(dv + (static_cast<size_t>(cl.t0 + row) * H + h) * DV + sp * 32 + n, bet[m] * d[m]);
       }
     }
-    __syncthreads();
+    lds_sync();
+    // the slice's share of the contractions over value columns
 #pragma unroll
     for (int u = 0; u < NT; ++u) {
       const int tau = w + 4 * u;
@@ -717,27 +860,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         int I, J;
         tri_ij(tau % 10, I, J);
         const float* Am = tau < 10 ? Dl : dWl;
-#pragma unroll
-        for (int kk = 0; kk < 16; kk += 4)
-          acc[u] = mf(Am[(16 * I + r) * P20 + kk + g], Ul[(16 * J + r) * P20 + kk + g], acc[u]);
+        acc[u] = mm3(split8(Am + (16 * I + r) * PW + 8 * g), split8(Ul + (16 * J + r) * PW + 8 * g), acc[u]);
       } else {
         const int e = tau - 20, kind = e / (4 * NKB), rem = e % (4 * NKB), I = rem / NKB, Jc = rem % NKB;
+        const float* Am = kind == 0 ? Dl : (kind == 1 ? dWl : Ul);
         const float* Bm = kind == 2 ? dSl : S0l;
-#pragma unroll
-        for (int kk = 0; kk < 16; kk += 4) {
-          float a;
-          if (kind == 0) a = Dl[(16 * I + r) * P20 + kk + g];
-          else if (kind == 1) a = betl[16 * I + r] * dWl[(16 * I + r) * P20 + kk + g];
-          else a = Ul[(16 * I + r) * P20 + kk + g];
-          acc[u] = mf(a, Bm[(16 * Jc + r) * P20 + kk + g], acc[u]);
-        }
+        const float sa = kind == 1 ? betl[16 * I + r] : 1.f;
+        acc[u] = mm3(split8(Am + (16 * I + r) * PW + 8 * g, sa), split8(Bm + (16 * Jc + r) * PW + 8 * g), acc[u]);
       }
     }
     if (tid < DK) {
 #pragma unroll
-      for (int c = 0; c < 16; ++c) dg += S0l[tid * P20 + c] * dSl[tid * P20 + c];
+      for (int c = 0; c < 32; ++c) dg += S0l[tid * PW + c] * dSl[tid * PW + c];
     }
-    __syncthreads();
+    lds_sync();
   }
   // dbeta: the write's share (dW . Vt, summed over value columns) and the
   // inverse's share (sum_s dM[r][s] A[r][s]), each part in its own slot and
@@ -745,7 +881,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     const float x = group_sum<16>(db1[m]);
-    if (r == 0) dbp[(16 * rt + 4 * g + m) * 5 + 4] = x;
+    if (r == 0) dbp[(16 * w + 4 * g + m) * 5 + 4] = x;
   }
 #pragma unroll
   for (int u = 0; u < NT; ++u) {
@@ -761,7 +897,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       }
     }
   }
-  __syncthreads();
+  lds_sync();
   if (tid < cl.len) {
     const float* x = dbp + tid * 5;
     dbeta[static_cast<size_t>(cl.t0 + tid) * H + h] = x[4] + x[0] + x[1] + x[2] + x[3];
@@ -791,11 +927,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 }
 
 // ---------------------------------------------------------------------------
-// grad_k: one workgroup (4 waves) per (chunk, head, 32 key channels) -- or,
+// grad_k: one workgroup (4 waves) per (chunk, head, SW key channels) -- or,
 // for the one-rate-per-head gate, per (chunk, head) over every channel, so
 // that the per-head gate cotangent is summed inside one workgroup.  Grid
-// (chunks, H, slices).  Thread t works on row t / 4, channels 8 (t % 4) ..
-// 8 (t % 4) + 7 of the slice.
+// (chunks, H, slices).  Thread t works on row t / 4 and SW / 4 consecutive
+// channels of the slice; SW = 16 keeps the LDS of two workgroups on a CU.
 //   GQ[r]  = sum_{s <= r} dP[r][s] k_s e^{G_r - G_s}
 //   GA[r]  = sum_{s <  r} dA[r][s] k_s e^{G_r - G_s}
 //   G2[s]  = sum_{r >= s} (dP[r][s] q_r + dA[r][s] k_r) e^{G_r - G_s}
@@ -807,19 +943,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // rows s < 16 I scaled by e^{G_{16I-1} - G_s}; column side: rows r > 16 J + 15
 // scaled by e^{G_r - G_{16J+15}}), diagonal blocks pair by pair.
 // ---------------------------------------------------------------------------
-template <typename T, int DK, int G>
+template <typename T, int DK, int G, int SW>
 __global__ __launch_bounds__(256) void bwd_grad_k_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                          const float* __restrict__ la, const int32_t* __restrict__ cu,
                                                          const int32_t* __restrict__ chunk_off, int N, int H,
                                                          const float* __restrict__ blk, T* __restrict__ dq,
                                                          T* __restrict__ dk, float* __restrict__ dla) {
   typedef BwdBlk<DK> B;
-  constexpr int PS = 36;  // pitch of the 32-channel slices (16-byte rows)
-  constexpr int NSW = G == KDA_GATE_SCALAR ? DK / 32 : 1;  // slices per workgroup
+  constexpr int PS = SW + 4;  // pitch of the SW-channel slices (16-byte rows)
+  constexpr int CPT = SW / 4;  // channels per thread (a row's four threads cover the slice)
+  constexpr int NSW = G == KDA_GATE_SCALAR ? DK / SW : 1;  // slices per workgroup
   __shared__ float qs[BC * PS], ks[BC * PS], gs[BC * PS];
   __shared__ float dPl[BC * LPC], dAl[BC * LPC];
   __shared__ float Ksc[96 * PS], Xq[96 * PS], Xk[96 * PS];
-  __shared__ float tot[8 * 32], rsum[BC];
+  __shared__ float tot[256], rsum[BC];
   const int j = blockIdx.x, h = blockIdx.y;
   if (j >= chunk_off[N]) return;
   const ChunkLoc cl = locate(cu, chunk_off, N, j);
@@ -833,33 +970,34 @@ __global__ __launch_bounds__(256) void bwd_grad_k_kernel(const T* __restrict__ q
     for (int i = 0; i < 4; ++i) dPl[row * LPC + c4 + i] = a[i], dAl[row * LPC + c4 + i] = b[i];
   }
   if (tid < BC) rsum[tid] = 0.f;
-  const int row = tid >> 2, c8 = (tid & 3) * 8;
+  const int row = tid >> 2, c8 = (tid & 3) * CPT;
   const int I = row >> 4;
   for (int si = 0; si < NSW; ++si) {
-    const int c0 = (blockIdx.z * NSW + si) * 32;
+    const int c0 = (blockIdx.z * NSW + si) * SW;
     {
-      float xq[8], xk[8];
+      float xq[CPT], xk[CPT];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) xq[i] = xk[i] = 0.f;
+      for (int i = 0; i < CPT; ++i) xq[i] = xk[i] = 0.f;
       if (row < cl.len) {
         const size_t o = (static_cast<size_t>(cl.t0 + row) * H + h) * DK + c0 + c8;
-        load8(q + o, xq);
-        load8(k + o, xk);
+        loadn<CPT>(q + o, xq);
+        loadn<CPT>(k + o, xk);
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) qs[row * PS + c8 + i] = xq[i], ks[row * PS + c8 + i] = xk[i];
-      const int ch = tid & 31, seg = tid >> 5;
+      for (int i = 0; i < CPT; ++i) qs[row * PS + c8 + i] = xq[i], ks[row * PS + c8 + i] = xk[i];
+      constexpr int RPS = BC * SW / 256;  // rows per thread of the gate load
+      const int ch = tid % SW, seg = tid / SW;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int rr = seg * 8 + i;
+      for (int i = 0; i < RPS; ++i) {
+        const int rr = seg * RPS + i;
         gs[rr * PS + ch] = rr < cl.len ? gate_at<G, DK>(la, static_cast<size_t>(cl.t0 + rr), H, h, c0 + ch) : 0.f;
       }
     }
-    __syncthreads();
-    row_scan32<false, PS>(gs, tot);
+    lds_sync();
+    row_scan<false, PS, SW>(gs, tot);
     // scaled operands of the off-diagonal block pairs
-    for (int e = tid; e < 96 * 32; e += 256) {
-      const int r96 = e >> 5, ch = e & 31;
+    for (int e = tid; e < 96 * SW; e += 256) {
+      const int r96 = e / SW, ch = e % SW;
       {
         const int Ib = r96 < 16 ? 1 : (r96 < 48 ? 2 : 3);
         const int s = r96 - (Ib == 1 ? 0 : (Ib == 2 ? 16 : 48));
@@ -873,10 +1011,10 @@ __global__ __launch_bounds__(256) void bwd_grad_k_kernel(const T* __restrict__ q
         Xk[r96 * PS + ch] = ks[rr * PS + ch] * E;
       }
     }
-    __syncthreads();
-    float GQ[8], GA[8], G2[8], Gr[8];
+    lds_sync();
+    float GQ[CPT], GA[CPT], G2[CPT], Gr[CPT];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) GQ[i] = GA[i] = G2[i] = 0.f, Gr[i] = gs[row * PS + c8 + i];
+    for (int i = 0; i < CPT; ++i) GQ[i] = GA[i] = G2[i] = 0.f, Gr[i] = gs[row * PS + c8 + i];
     // row side
     if (I > 0) {
       const int off = I == 1 ? 0 : (I == 2 ? 16 : 48);
@@ -884,10 +1022,10 @@ __global__ __launch_bounds__(256) void bwd_grad_k_kernel(const T* __restrict__ q
         const float dp = dPl[row * LPC + s], da = dAl[row * LPC + s];
         const float* kp = Ksc + (off + s) * PS + c8;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) GQ[i] += dp * kp[i], GA[i] += da * kp[i];
+        for (int i = 0; i < CPT; ++i) GQ[i] += dp * kp[i], GA[i] += da * kp[i];
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < CPT; ++i) {
         const float sc_ = __expf(Gr[i] - gs[(16 * I - 1) * PS + c8 + i]);
         GQ[i] *= sc_;
         GA[i] *= sc_;
@@ -896,7 +1034,7 @@ __global__ __launch_bounds__(256) void bwd_grad_k_kernel(const T* __restrict__ q
     for (int s = 16 * I; s < row; ++s) {
       const float dp = dPl[row * LPC + s], da = dAl[row * LPC + s];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < CPT; ++i) {
         const float kE = ks[s * PS + c8 + i] * __expf(Gr[i] - gs[s * PS + c8 + i]);
         GQ[i] += dp * kE;
         GA[i] += da * kE;
@@ -910,24 +1048,24 @@ __global__ __launch_bounds__(256) void bwd_grad_k_kernel(const T* __restrict__ q
         const float* xq = Xq + (off + rr - 16 * I - 16) * PS + c8;
         const float* xk = Xk + (off + rr - 16 * I - 16) * PS + c8;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) G2[i] += dp * xq[i] + da * xk[i];
+        for (int i = 0; i < CPT; ++i) G2[i] += dp * xq[i] + da * xk[i];
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) G2[i] *= __expf(gs[(16 * I + 15) * PS + c8 + i] - Gr[i]);
+      for (int i = 0; i < CPT; ++i) G2[i] *= __expf(gs[(16 * I + 15) * PS + c8 + i] - Gr[i]);
     }
     for (int rr = row + 1; rr < 16 * I + 16; ++rr) {
       const float dp = dPl[rr * LPC + row], da = dAl[rr * LPC + row];
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < CPT; ++i)
         G2[i] += (dp * qs[rr * PS + c8 + i] + da * ks[rr * PS + c8 + i]) * __expf(gs[rr * PS + c8 + i] - Gr[i]);
     }
     // elementwise
-    float dQg[8], dKg[8], dKb[8], dqv[8], dkv[8], dG[8], cs[8];
+    float dQg[CPT], dKg[CPT], dKb[CPT], dqv[CPT], dkv[CPT], dG[CPT], cs[CPT];
     {
       const size_t o = static_cast<size_t>(row) * DK + c0 + c8;
-      load8(bk + B::odQg + o, dQg);
-      load8(bk + B::odKg + o, dKg);
-      load8(bk + B::odKb + o, dKb);
+      loadn<CPT>(bk + B::odQg + o, dQg);
+      loadn<CPT>(bk + B::odKg + o, dKg);
+      loadn<CPT>(bk + B::odKb + o, dKb);
     }
     // The pair s = r enters P with factor 1 and its contributions to dG
     // (q_r dP_rr k_r - k_r dP_rr q_r) cancel exactly, as do the last token's
@@ -939,7 +1077,7 @@ __global__ __launch_bounds__(256) void bwd_grad_k_kernel(const T* __restrict__ q
     const float dpd = dPl[row * LPC + row];
     const bool last = row == BC - 1 || row == cl.len - 1;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < CPT; ++i) {
       const float qv = qs[row * PS + c8 + i], kv = ks[row * PS + c8 + i];
       const float eg = __expf(Gr[i]), eb = __expf(gs[(BC - 1) * PS + c8 + i] - Gr[i]);
       dqv[i] = dQg[i] * eg + GQ[i] + dpd * kv;
@@ -949,37 +1087,37 @@ __global__ __launch_bounds__(256) void bwd_grad_k_kernel(const T* __restrict__ q
     }
     if (row < cl.len) {
       const size_t o = (static_cast<size_t>(cl.t0 + row) * H + h) * DK + c0 + c8;
-      store8(dq + o, dqv);
-      store8(dk + o, dkv);
+      storen<CPT>(dq + o, dqv);
+      storen<CPT>(dk + o, dkv);
     }
     if constexpr (G != KDA_GATE_NONE) {
-      __syncthreads();  // every reader of qs and Xk is done
+      lds_sync();  // every reader of qs and Xk is done
 #pragma unroll
-      for (int i = 0; i < 8; ++i) qs[row * PS + c8 + i] = dG[i], Xk[row * PS + c8 + i] = cs[i];
-      __syncthreads();
-      if (tid < 32) {  // G_C: the column sum of dKb Kb over the other rows (fixed order), dgamma gamma
+      for (int i = 0; i < CPT; ++i) qs[row * PS + c8 + i] = dG[i], Xk[row * PS + c8 + i] = cs[i];
+      lds_sync();
+      if (tid < SW) {  // G_C: the column sum of dKb Kb over the other rows (fixed order), dgamma gamma
         float x = 0.f;
         for (int rr = 0; rr < BC; ++rr) x += Xk[rr * PS + tid];
         qs[(BC - 1) * PS + tid] += x + bk[B::odGam + c0 + tid] * __expf(gs[(BC - 1) * PS + tid]);
       }
-      __syncthreads();
-      row_scan32<true, PS>(qs, tot);
+      lds_sync();
+      row_scan<true, PS, SW>(qs, tot);
       if constexpr (G == KDA_GATE_CHANNEL) {
         if (row < cl.len) {
-          float x[8];
+          float x[CPT];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) x[i] = qs[row * PS + c8 + i];
-          store8(dla + (static_cast<size_t>(cl.t0 + row) * H + h) * DK + c0 + c8, x);
+          for (int i = 0; i < CPT; ++i) x[i] = qs[row * PS + c8 + i];
+          storen<CPT>(dla + (static_cast<size_t>(cl.t0 + row) * H + h) * DK + c0 + c8, x);
         }
       } else {
         float x = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) x += qs[row * PS + c8 + i];
+        for (int i = 0; i < CPT; ++i) x += qs[row * PS + c8 + i];
         x = group_sum<4>(x);  // the row's four threads are one lane quad
         if ((tid & 3) == 0) rsum[row] += x;
       }
     }
-    __syncthreads();
+    lds_sync();
   }
   if constexpr (G == KDA_GATE_SCALAR) {
     if (tid < cl.len) dla[static_cast<size_t>(cl.t0 + tid) * H + h] = rsum[tid];
@@ -1049,8 +1187,9 @@ static hipError_t launch_backward_t(const BackwardPlan& p, const void* q, const 
     hipLaunchKernelGGL((bwd_grad_v_kernel<T, DK, DV>), dim3(mc, p.H), dim3(256), 0, st, tv, tdo, cu, chunk_off, p.N,
                        p.H, blk, sc, dsc, static_cast<T*>(dv), dbeta);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const unsigned nz = G == KDA_GATE_SCALAR ? 1u : static_cast<unsigned>(DK / 32);
-    hipLaunchKernelGGL((bwd_grad_k_kernel<T, DK, G>), dim3(mc, p.H, nz), dim3(256), 0, st, tq, tk, la, cu,
+    constexpr int SW = 16;  // key channels per grad_k slice (LDS for two workgroups per CU)
+    const unsigned nz = G == KDA_GATE_SCALAR ? 1u : static_cast<unsigned>(DK / SW);
+    hipLaunchKernelGGL((bwd_grad_k_kernel<T, DK, G, SW>), dim3(mc, p.H, nz), dim3(256), 0, st, tq, tk, la, cu,
                        chunk_off, p.N, p.H, blk, static_cast<T*>(dq), static_cast<T*>(dk), dla);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }

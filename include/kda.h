@@ -257,8 +257,8 @@ kda_status kda_decode_step(int32_t B, int32_t H, int32_t dk, int32_t dv, kda_dty
 /*
  * Bytes of device workspace kda_prefill_backward needs for `desc` (256-byte
  * aligned pointer expected): per (64-token chunk, head) a block of chunk
- * factors and two dk x dv states, fp32 (273 KiB for dk = dv = 128; the
- * 131,072-token, 32-head case takes 17.9 GB).  Returns 0 for an invalid or
+ * factors and two dk x dv states, fp32 (353 KiB for dk = dv = 128; the
+ * 131,072-token, 32-head case takes 23.7 GB).  Returns 0 for an invalid or
  * unsupported desc.  Host-only; launches nothing.
  */
 size_t kda_prefill_backward_workspace_size(const kda_prefill_desc* desc);

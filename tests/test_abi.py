@@ -211,7 +211,7 @@ def test_backward_workspace_and_validation_codes():
     d, keep = desc(cu_seqlens_host=[0, 60, 100])
     need = lib.kda_prefill_backward_workspace_size(ctypes.byref(d))
     # chunks: ceil(60/64) + ceil(40/64) = 2, heads 4; block + two states per slot
-    blk = (3 * 64 * 128 + 3 * 64 * 64 + 128 + 64 + 63) // 64 * 64 * 4
+    blk = (5 * 64 * 128 + 4 * 64 * 64 + 128 + 64 + 63) // 64 * 64 * 4
     slots = 2 * 4
     assert need >= slots * (blk + 2 * 128 * 128 * 4)
     assert need < slots * (blk + 2 * 128 * 128 * 4) + 4096
