@@ -121,3 +121,37 @@ def test_decode_full_size_every_state():
     es = GlobalErr("S after %d steps (all states)" % steps)
     es.add(host(Sd), Sref)
     es.check(TOL["bf16"])
+
+
+def _run_backward(name, group=8):
+    """kda_prefill_backward over the whole workload against the oracle's
+    backward, every element of every gradient (heads in groups)."""
+    import torch
+    import gated_delta_rule_33_amd as kda
+    w = synth.workload_prefill(name)
+    cot = synth.make_cotangents(w, 7000 + synth.WORKLOADS[name]["index"], dS_T_std=0.1)
+    T, H = w.total_tokens, w.num_heads
+    log("full-size backward %s: T=%d H=%d N=%d, every head checked" % (name, T, H, w.num_seqs))
+    dt = w.io_dtype
+    g = kda.prefill_backward(dev(w.q, dt), dev(w.k, dt), dev(w.v, dt), dev(w.log_alpha), dev(w.beta),
+                             dev(w.cu_seqlens), dev(w.S0) if w.S0 is not None else None, dev(cot.dO, dt),
+                             dev(cot.dS_T), cu_seqlens_host=w.cu_seqlens.tolist())
+    torch.cuda.synchronize()
+    kda.clear_workspace_cache()
+    names = ("dq", "dk", "dv", "dlog_alpha", "dbeta", "dS0")
+    errs = {n: GlobalErr("%s (all %d heads)" % (n, H)) for n in names}
+    la = w.log_alpha_channels()
+    for h0 in range(0, H, group):
+        hs = list(range(h0, min(H, h0 + group)))
+        ref = oracle.backward(w.q[:, hs], w.k[:, hs], w.v[:, hs], la[:, hs], w.beta[:, hs], w.cu_seqlens,
+                              None if w.S0 is None else w.S0[:, hs], cot.dO[:, hs], cot.dS_T[:, hs])
+        for n in names:
+            sl = g[n][:, h0:h0 + len(hs)]
+            errs[n].add(host(sl), ref[n])
+        del ref
+        log("  heads %d..%d done" % (hs[0], hs[-1]))
+    return {n: errs[n].check(TOL[dt]) for n in names}
+
+
+def test_backward_long131072_all_heads():
+    _run_backward("long131072_bf16", group=16)
