@@ -52,7 +52,8 @@ def log(msg):
 # The source files that define each measured kernel sequence (with the
 # shared device header): hardware-counter traffic is reported only while
 # these are byte-identical to the ones it was measured on.
-TRAFFIC_SOURCES = {"prefill": ("kda_prefill.hip", "kda_device.h"), "decode": ("kda_decode.hip", "kda_device.h")}
+TRAFFIC_SOURCES = {"prefill": ("kda_prefill.hip", "kda_device.h"), "decode": ("kda_decode.hip", "kda_device.h"),
+                   "backward": ("kda_backward.hip", "kda_prefill.hip", "kda_device.h")}
 
 
 def source_digest(key: str) -> str:
@@ -335,7 +336,7 @@ def run_backward(wname, args, torch, kda, synth, oracle, check: bool):
     res = dict(workload=wname, num_seqs=N, total_tokens=T_tok, heads=H, call_ms=round(call_s * 1e3, 4),
                tokens_per_s=round(T_tok / call_s, 1),
                roofline=dict(bound="mfma", achieved=round(tfl, 2), peak=FP32_MFMA_PEAK_TFLOPS, unit="TFLOP/s",
-                             frac=round(tfl / FP32_MFMA_PEAK_TFLOPS, 4), traffic=None,
+                             frac=round(tfl / FP32_MFMA_PEAK_TFLOPS, 4), traffic=measured_traffic("backward_" + wname),
                              kernel="kda_prefill_backward (prep, state, dstate, grad_v, grad_k)",
                              flops_per_launch=int(nflops), flops_per_token_head=flops_th,
                              hbm_achieved=round(nbytes / call_s / 1e9, 1), hbm_frac=round(nbytes / call_s / 1e9 / HBM_PEAK_GBS, 4),
@@ -487,6 +488,8 @@ def main():
                     help="prefill on the caller's stream only (for hardware-counter runs)")
     ap.add_argument("--copy-probe", type=int, default=0, help="run only a device copy of this many bytes")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass lines")
+    ap.add_argument("--backward-workloads", default="batch4x4096_bf16,long131072_bf16",
+                    help="comma list of workloads for the backward lines (the first is checked against the oracle)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this library has no multi-GPU path (each GPU would run "
@@ -516,8 +519,8 @@ def main():
     if dec_gates:
         dec_gates.append(run_decode(args, torch, kda, synth, None, steps=min(256, args.decode_steps), stages=True))
     bwd = [] if args.no_backward else [
-        run_backward("batch4x4096_bf16", args, torch, kda, synth, oracle, check=not args.no_cpu_baseline),
-        run_backward(args.workload, args, torch, kda, synth, oracle, check=False)]
+        run_backward(name, args, torch, kda, synth, oracle, check=(i == 0 and not args.no_cpu_baseline))
+        for i, name in enumerate(x for x in args.backward_workloads.split(",") if x)]
     wl = pre["workload"]
     line = {
         "metric": "KDA prefill tokens/s (MFMA % peak) at T=128k; decode state-updates/s (HBM %)",

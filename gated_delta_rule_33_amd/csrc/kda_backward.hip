@@ -698,26 +698,52 @@ __device__ __forceinline__ void tri_ij(int e, int& I, int& J) {
   J = e - I * (I + 1) / 2;
 }
 
+// A split-bf16 matrix in LDS: hi and lo planes with a row pitch of P
+// elements (P * 2 bytes a multiple of 16, so a fragment is one 16-byte read).
+struct Plane {
+  __bf16* h;
+  __bf16* l;
+  int P;
+  __device__ __forceinline__ F3 frag(int row, int k0) const {
+    return F3{*reinterpret_cast<const bf16x8*>(h + row * P + k0), *reinterpret_cast<const bf16x8*>(l + row * P + k0)};
+  }
+  __device__ __forceinline__ void put(int row, int col, float x) const {
+    const __bf16 hi = static_cast<__bf16>(x);
+    h[row * P + col] = hi;
+    l[row * P + col] = static_cast<__bf16>(x - static_cast<float>(hi));
+  }
+  // four consecutive elements of one row (8-byte aligned)
+  __device__ __forceinline__ void put4(int row, int col, f32x4 x) const {
+    bf16x4 hi, lo;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      hi[i] = static_cast<__bf16>(x[i]);
+      lo[i] = static_cast<__bf16>(x[i] - static_cast<float>(hi[i]));
+    }
+    *reinterpret_cast<bf16x4*>(h + row * P + col) = hi;
+    *reinterpret_cast<bf16x4*>(l + row * P + col) = lo;
+  }
+};
+
 template <int DK>
 struct GradVLds {
-  static constexpr int PW = 36;       // pitch of [*][32] slices
-  static constexpr int PC = BC + 4;   // pitch of [*][64] (transposed, k = chunk row)
-  static constexpr int PK = DK + 4;   // pitch of [*][DK] (transposed, k = key channel)
-  static constexpr int oS0 = 0;                    // [DK][PW]  S0 columns of the slice
-  static constexpr int oS0T = oS0 + DK * PW;       // [32][PK]
-  static constexpr int odS = oS0T + 32 * PK;       // [DK][PW]
-  static constexpr int odST = odS + DK * PW;       // [32][PK]
-  static constexpr int odO = odST + 32 * PK;       // [BC][PW]
-  static constexpr int odOT = odO + BC * PW;       // [32][PC]
-  static constexpr int oV = odOT + 32 * PC;        // [BC][PW]
-  static constexpr int oVt = oV + BC * PW;         // [BC][PW]
-  static constexpr int oWT = oVt + BC * PW;        // [32][PC]
-  static constexpr int odUT = oWT + 32 * PC;       // [32][PC]
-  static constexpr int oU = odUT + 32 * PC;        // [BC][PW]
-  static constexpr int odW = oU + BC * PW;         // [BC][PW]
-  static constexpr int oBet = odW + BC * PW;       // [BC]
-  static constexpr int oDbp = oBet + BC;           // [BC][5]
-  static constexpr int floats = oDbp + BC * 5;
+  static constexpr int PW = 40;       // pitch of [*][32] planes (k = value column)
+  static constexpr int PC = BC + 8;   // pitch of [32][BC] planes (k = chunk row)
+  static constexpr int PK = DK + 8;   // pitch of [32][DK] planes (k = key channel)
+  // element offsets of each plane's hi part; its lo part follows at + rows * pitch
+  static constexpr int oS0 = 0;                          // [DK][PW]  S0 columns of the slice
+  static constexpr int oS0T = oS0 + 2 * DK * PW;         // [32][PK]
+  static constexpr int odS = oS0T + 2 * 32 * PK;         // [DK][PW]
+  static constexpr int odST = odS + 2 * DK * PW;         // [32][PK]
+  static constexpr int odO = odST + 2 * 32 * PK;         // [BC][PW]
+  static constexpr int odOT = odO + 2 * BC * PW;         // [32][PC]
+  static constexpr int oWT = odOT + 2 * 32 * PC;         // [32][PC]
+  static constexpr int odUT = oWT + 2 * 32 * PC;         // [32][PC]
+  static constexpr int oU = odUT + 2 * 32 * PC;          // [BC][PW]
+  static constexpr int odW = oU + 2 * BC * PW;           // [BC][PW]
+  static constexpr int odV = odW + 2 * BC * PW;          // [BC][PW]  dv = beta dW
+  static constexpr int elems = odV + 2 * BC * PW;        // bf16 elements
+  static constexpr int bytes = elems * 2;
 };
 
 template <typename T, int DK, int DV>
@@ -731,21 +757,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr int NTILE = 20 + 3 * 4 * NKB;  // dP (10), dM (10), dQg, dKg, dKb (4 NKB each)
   constexpr int NT = (NTILE + 3) / 4;
   constexpr int PW = LL::PW, PC = LL::PC, PK = LL::PK;
-  __shared__ __align__(16) float lds[LL::floats];
-  float* S0l = lds + LL::oS0;
-  float* S0T = lds + LL::oS0T;
-  float* dSl = lds + LL::odS;
-  float* dST = lds + LL::odST;
-  float* Dl = lds + LL::odO;
-  float* DT = lds + LL::odOT;
-  float* Vl = lds + LL::oV;
-  float* Vtl = lds + LL::oVt;
-  float* WT = lds + LL::oWT;
-  float* dUT = lds + LL::odUT;
-  float* Ul = lds + LL::oU;
-  float* dWl = lds + LL::odW;
-  float* betl = lds + LL::oBet;
-  float* dbp = lds + LL::oDbp;
+  __shared__ __align__(16) __bf16 lds[LL::elems];
+  __shared__ float betl[BC], dbp[BC * 5];
+  auto plane = [&](int off, int rows, int pitch) { return Plane{lds + off, lds + off + rows * pitch, pitch}; };
+  const Plane S0p = plane(LL::oS0, DK, PW), S0T = plane(LL::oS0T, 32, PK);
+  const Plane dSp = plane(LL::odS, DK, PW), dST = plane(LL::odST, 32, PK);
+  const Plane Dp = plane(LL::odO, BC, PW), DT = plane(LL::odOT, 32, PC);
+  const Plane WT = plane(LL::oWT, 32, PC), dUT = plane(LL::odUT, 32, PC);
+  const Plane Up = plane(LL::oU, BC, PW), dWp = plane(LL::odW, BC, PW), dVp = plane(LL::odV, BC, PW);
   const int j = blockIdx.x, h = blockIdx.y;
   if (j >= chunk_off[N]) return;
   const ChunkLoc cl = locate(cu, chunk_off, N, j);
@@ -782,53 +801,58 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   for (int u = 0; u < NT; ++u) acc[u] = zero4();
   float db1[4] = {0.f, 0.f, 0.f, 0.f}, dg = 0.f;
   for (int sp = 0; sp < NSP; ++sp) {
-    // slice inputs, both orientations
+    // slice inputs, split once, both orientations
     for (int e = tid; e < DK * 8; e += 256) {
       const int row = e >> 3, c4 = (e & 7) * 4;
       const f32x4 a = *reinterpret_cast<const f32x4*>(s0 + static_cast<size_t>(row) * DV + sp * 32 + c4);
       const f32x4 b = *reinterpret_cast<const f32x4*>(dsC + static_cast<size_t>(row) * DV + sp * 32 + c4);
-      *reinterpret_cast<f32x4*>(S0l + row * PW + c4) = a;
-      *reinterpret_cast<f32x4*>(dSl + row * PW + c4) = b;
+      S0p.put4(row, c4, a);
+      dSp.put4(row, c4, b);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) S0T[(c4 + i) * PK + row] = a[i], dST[(c4 + i) * PK + row] = b[i];
+      for (int i = 0; i < 4; ++i) S0T.put(c4 + i, row, a[i]), dST.put(c4 + i, row, b[i]);
     }
     for (int e = tid; e < BC * 8; e += 256) {
       const int row = e >> 3, c4 = (e & 7) * 4;
-      f32x4 x = zero4(), y = zero4();
-      if (row < cl.len) {
-        const size_t o = (static_cast<size_t>(cl.t0 + row) * H + h) * DV + sp * 32 + c4;
-        x = load4(v + o);
-        y = load4(dO + o);
-      }
-      *reinterpret_cast<f32x4*>(Vl + row * PW + c4) = x;
-      *reinterpret_cast<f32x4*>(Dl + row * PW + c4) = y;
+      f32x4 y = zero4();
+      if (row < cl.len) y = load4(dO + (static_cast<size_t>(cl.t0 + row) * H + h) * DV + sp * 32 + c4);
+      Dp.put4(row, c4, y);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) DT[(c4 + i) * PC + row] = y[i];
+      for (int i = 0; i < 4; ++i) DT.put(c4 + i, row, y[i]);
+    }
+    if (tid < DK) {  // dgamma straight from the slice in global memory (L2), fixed order
+#pragma unroll 4
+      for (int c = 0; c < 32; c += 4) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(s0 + static_cast<size_t>(tid) * DV + sp * 32 + c);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(dsC + static_cast<size_t>(tid) * DV + sp * 32 + c);
+        dg += a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
+      }
     }
     lds_sync();
     // Vt, W = beta Vt (transposed) and dU (transposed) for the two 16-column tiles
+    f32x4 vt[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       const int n = 16 * nt + r;
       f32x4 a = zero4(), d = zero4();
 #pragma unroll
       for (int kk = 0; kk < NKS; ++kk) {
-        a = mm3(kgf[kk], split8(S0T + n * PK + 32 * kk + 8 * g), a);
-        d = mm3(kbf[kk], split8(dST + n * PK + 32 * kk + 8 * g), d);
+        a = mm3(kgf[kk], S0T.frag(n, 32 * kk + 8 * g), a);
+        d = mm3(kbf[kk], dST.frag(n, 32 * kk + 8 * g), d);
       }
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
-        if (kk >= kU0) d = mm3(ptf[kk], split8(DT + n * PC + 32 * kk + 8 * g), d);
+        if (kk >= kU0) d = mm3(ptf[kk], DT.frag(n, 32 * kk + 8 * g), d);
       f32x4 wv;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const int row = 16 * w + 4 * g + m;
-        const float vt = Vl[row * PW + n] - a[m];
-        Vtl[row * PW + n] = vt;
-        wv[m] = bet[m] * vt;
+        // rows past the sequence read its last row: beta, dU and dW are 0 there
+        const float vv = io<T>::load(v + (static_cast<size_t>(cl.t0 + min(row, cl.len - 1)) * H + h) * DV + sp * 32 + n);
+        vt[nt][m] = vv - a[m];
+        wv[m] = bet[m] * vt[nt][m];
       }
-      *reinterpret_cast<f32x4*>(WT + n * PC + 16 * w + 4 * g) = wv;
-      *reinterpret_cast<f32x4*>(dUT + n * PC + 16 * w + 4 * g) = d;
+      WT.put4(n, 16 * w + 4 * g, wv);
+      dUT.put4(n, 16 * w + 4 * g, d);
     }
     lds_sync();
     // U = T W (rows) and dW = T^T dU (rows), dv, dbeta's write share
@@ -838,15 +862,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       f32x4 a = zero4(), d = zero4();
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        if (kk <= kT1) a = mm3(tf[kk], split8(WT + n * PC + 32 * kk + 8 * g), a);
-        if (kk >= kU0) d = mm3(ttf[kk], split8(dUT + n * PC + 32 * kk + 8 * g), d);
+        if (kk <= kT1) a = mm3(tf[kk], WT.frag(n, 32 * kk + 8 * g), a);
+        if (kk >= kU0) d = mm3(ttf[kk], dUT.frag(n, 32 * kk + 8 * g), d);
       }
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const int row = 16 * w + 4 * g + m;
-        Ul[row * PW + n] = a[m];
-        dWl[row * PW + n] = d[m];
-        db1[m] += d[m] * Vtl[row * PW + n];
+        Up.put(row, n, a[m]);
+        dWp.put(row, n, d[m]);
+        dVp.put(row, n, bet[m] * d[m]);
+        db1[m] += d[m] * vt[nt][m];
         if (row < cl.len) io<T>::store(dv + (static_cast<size_t>(cl.t0 + row) * H + h) * DV + sp * 32 + n, bet[m] * d[m]);
       }
     }
@@ -859,19 +884,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       if (tau < 20) {
         int I, J;
         tri_ij(tau % 10, I, J);
-        const float* Am = tau < 10 ? Dl : dWl;
-        acc[u] = mm3(split8(Am + (16 * I + r) * PW + 8 * g), split8(Ul + (16 * J + r) * PW + 8 * g), acc[u]);
+        const Plane& Am = tau < 10 ? Dp : dWp;
+        acc[u] = mm3(Am.frag(16 * I + r, 8 * g), Up.frag(16 * J + r, 8 * g), acc[u]);
       } else {
         const int e = tau - 20, kind = e / (4 * NKB), rem = e % (4 * NKB), I = rem / NKB, Jc = rem % NKB;
-        const float* Am = kind == 0 ? Dl : (kind == 1 ? dWl : Ul);
-        const float* Bm = kind == 2 ? dSl : S0l;
-        const float sa = kind == 1 ? betl[16 * I + r] : 1.f;
-        acc[u] = mm3(split8(Am + (16 * I + r) * PW + 8 * g, sa), split8(Bm + (16 * Jc + r) * PW + 8 * g), acc[u]);
+        const Plane& Am = kind == 0 ? Dp : (kind == 1 ? dVp : Up);
+        const Plane& Bm = kind == 2 ? dSp : S0p;
+        acc[u] = mm3(Am.frag(16 * I + r, 8 * g), Bm.frag(16 * Jc + r, 8 * g), acc[u]);
       }
-    }
-    if (tid < DK) {
-#pragma unroll
-      for (int c = 0; c < 32; ++c) dg += S0l[tid * PW + c] * dSl[tid * PW + c];
     }
     lds_sync();
   }
@@ -1018,6 +1038,7 @@ __global__ __launch_bounds__(256) void bwd_grad_k_kernel(const T* __restrict__ q
     // row side
     if (I > 0) {
       const int off = I == 1 ? 0 : (I == 2 ? 16 : 48);
+#pragma unroll 4
       for (int s = 0; s < 16 * I; ++s) {
         const float dp = dPl[row * LPC + s], da = dAl[row * LPC + s];
         const float* kp = Ksc + (off + s) * PS + c8;
@@ -1031,6 +1052,7 @@ __global__ __launch_bounds__(256) void bwd_grad_k_kernel(const T* __restrict__ q
         GA[i] *= sc_;
       }
     }
+#pragma unroll 2
     for (int s = 16 * I; s < row; ++s) {
       const float dp = dPl[row * LPC + s], da = dAl[row * LPC + s];
 #pragma unroll
@@ -1043,6 +1065,7 @@ __global__ __launch_bounds__(256) void bwd_grad_k_kernel(const T* __restrict__ q
     // column side (this thread's row is the column index s)
     if (I < 3) {
       const int off = I == 0 ? 0 : (I == 1 ? 48 : 80);
+#pragma unroll 4
       for (int rr = 16 * I + 16; rr < BC; ++rr) {
         const float dp = dPl[rr * LPC + row], da = dAl[rr * LPC + row];
         const float* xq = Xq + (off + rr - 16 * I - 16) * PS + c8;
@@ -1053,6 +1076,7 @@ __global__ __launch_bounds__(256) void bwd_grad_k_kernel(const T* __restrict__ q
 #pragma unroll
       for (int i = 0; i < CPT; ++i) G2[i] *= __expf(gs[(16 * I + 15) * PS + c8 + i] - Gr[i]);
     }
+#pragma unroll 2
     for (int rr = row + 1; rr < 16 * I + 16; ++rr) {
       const float dp = dPl[rr * LPC + row], da = dAl[rr * LPC + row];
 #pragma unroll
