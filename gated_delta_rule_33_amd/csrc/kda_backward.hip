@@ -396,15 +396,15 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, 
 // XCD (x % 8), so the slices read each block through one L2.
 // ---------------------------------------------------------------------------
 template <typename T, int DK, int DV>
-__global__ __launch_bounds__(256) void bwd_state_kernel(const T* __restrict__ v, const int32_t* __restrict__ cu,
-                                                        const int32_t* __restrict__ chunk_off,
-                                                        const int32_t* __restrict__ order, int N, int H,
-                                                        const float* __restrict__ blk, const float* __restrict__ S0,
-                                                        float* __restrict__ sc) {
+__device__ __forceinline__ void bwd_state_body(int x, const T* __restrict__ v, const int32_t* __restrict__ cu,
+                                               const int32_t* __restrict__ chunk_off,
+                                               const int32_t* __restrict__ order, int N, int H,
+                                               const float* __restrict__ blk, const float* __restrict__ S0,
+                                               float* __restrict__ sc) {
   typedef BwdBlk<DK> B;
   constexpr int NSP = DV / 16, NKB = DK / 16, TPW = NKB / 4;
   __shared__ float Xl[DK * P20], Wl[BC * P20], Ul[BC * P20];
-  const int x = blockIdx.x, xcd = x & 7, s8 = x >> 3, sp = s8 % NSP, p = (s8 / NSP) * 8 + xcd;
+  const int xcd = x & 7, s8 = x >> 3, sp = s8 % NSP, p = (s8 / NSP) * 8 + xcd;
   if (p >= N * H) return;
   const int n = order[p / H], h = p % H;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
@@ -421,20 +421,28 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(const T* __restrict__ v,
     }
   struct Ops {
     f32x4 kg[NKB];
-    f32x4 kbt[TPW][4];
     f32x4 tt[4];
     float vv[4], bet[4], gam[TPW][4];
+  };
+  // Kb^T rows of the wave's key channels (used in the chunk's last phase):
+  // read at the start of that chunk, not a chunk ahead (register budget of
+  // two workgroups per CU)
+  struct OpsLate {
+    f32x4 kbt[TPW][4];
+  };
+  auto load_late = [&](int c, OpsLate& o) {
+    const float* bk = blk + (static_cast<size_t>(j0 + c) * H + h) * B::floats;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        o.kbt[t][b] = *reinterpret_cast<const f32x4*>(bk + B::oKbT + (16 * (w * TPW + t) + r) * BC + 16 * b + 4 * g);
   };
   auto load = [&](int c, Ops& o) {
     const float* bk = blk + (static_cast<size_t>(j0 + c) * H + h) * B::floats;
     const int row = 16 * w + r;
 #pragma unroll
     for (int b = 0; b < NKB; ++b) o.kg[b] = *reinterpret_cast<const f32x4*>(bk + B::oKg + row * DK + 16 * b + 4 * g);
-#pragma unroll
-    for (int t = 0; t < TPW; ++t)
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-        o.kbt[t][b] = *reinterpret_cast<const f32x4*>(bk + B::oKbT + (16 * (w * TPW + t) + r) * BC + 16 * b + 4 * g);
 #pragma unroll
     for (int b = 0; b < 4; ++b)
       o.tt[b] = b <= w ? *reinterpret_cast<const f32x4*>(bk + B::oT + row * BC + 16 * b + 4 * g) : zero4();
@@ -455,6 +463,8 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(const T* __restrict__ v,
   Ops cur, nxt;
   if (nch > 0) load(0, cur);
   for (int c = 0; c < nch; ++c) {
+    OpsLate late;
+    load_late(c, late);
     // next chunk's operands first: the memory counter is in order, so the
     // wait for these loads at the end of the chunk does not also wait for the
     // state stores issued after them
@@ -493,7 +503,7 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(const T* __restrict__ v,
 #pragma unroll
       for (int b = 0; b < 4; ++b)
 #pragma unroll
-        for (int m = 0; m < 4; ++m) X[t] = mf(cur.kbt[t][b][m], Ul[(16 * b + 4 * g + m) * P20 + r], X[t]);
+        for (int m = 0; m < 4; ++m) X[t] = mf(late.kbt[t][b][m], Ul[(16 * b + 4 * g + m) * P20 + r], X[t]);
     }
     cur = nxt;
   }
@@ -506,15 +516,15 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(const T* __restrict__ v,
 //   Z = P^T dO + Kb X,  Y = T^T Z,  X = Diag(gamma) X + Qg^T dO - Kg^T Diag(beta) Y
 // ---------------------------------------------------------------------------
 template <typename T, int DK, int DV>
-__global__ __launch_bounds__(256) void bwd_dstate_kernel(const T* __restrict__ dO, const int32_t* __restrict__ cu,
-                                                         const int32_t* __restrict__ chunk_off,
-                                                         const int32_t* __restrict__ order, int N, int H,
-                                                         const float* __restrict__ blk, const float* __restrict__ dST,
-                                                         float* __restrict__ dsc, float* __restrict__ dS0) {
+__device__ __forceinline__ void bwd_dstate_body(int x, const T* __restrict__ dO, const int32_t* __restrict__ cu,
+                                                const int32_t* __restrict__ chunk_off,
+                                                const int32_t* __restrict__ order, int N, int H,
+                                                const float* __restrict__ blk, const float* __restrict__ dST,
+                                                float* __restrict__ dsc, float* __restrict__ dS0) {
   typedef BwdBlk<DK> B;
   constexpr int NSP = DV / 16, NKB = DK / 16, TPW = NKB / 4;
   __shared__ float Xl[DK * P20], Dl[BC * P20], Zl[BC * P20], Yl[BC * P20];
-  const int x = blockIdx.x, xcd = x & 7, s8 = x >> 3, sp = s8 % NSP, p = (s8 / NSP) * 8 + xcd;
+  const int xcd = x & 7, s8 = x >> 3, sp = s8 % NSP, p = (s8 / NSP) * 8 + xcd;
   if (p >= N * H) return;
   const int n = order[p / H], h = p % H;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
@@ -531,15 +541,22 @@ __global__ __launch_bounds__(256) void bwd_dstate_kernel(const T* __restrict__ d
     }
   typedef typename raw4<T>::type R4;
   struct Ops {
-    f32x4 kb[NKB];
     f32x4 pt[4], tt[4];
     R4 dov;
     float bet[4], gam[TPW][4];
   };
-  // Qg^T and Kg^T rows of the wave's key channels: read at the start of the
-  // chunk that uses them (last phase), not a chunk ahead, to bound registers
+  // Kb rows and the Qg^T, Kg^T rows of the wave's key channels: read at the
+  // start of the chunk that uses them, not a chunk ahead, so that the pass
+  // fits the register budget of two workgroups per CU
+  // (Kb for the first phase, Qg^T and Kg^T issued after it, for the last)
   struct OpsLate {
     f32x4 qgt[TPW][4], kgt[TPW][4];
+  };
+  auto load_kb = [&](int c, f32x4* kb) {
+    const float* bk = blk + (static_cast<size_t>(j0 + c) * H + h) * B::floats;
+#pragma unroll
+    for (int b = 0; b < NKB; ++b)
+      kb[b] = *reinterpret_cast<const f32x4*>(bk + B::oKb + (16 * w + r) * DK + 16 * b + 4 * g);
   };
   auto load_late = [&](int c, OpsLate& o) {
     const float* bk = blk + (static_cast<size_t>(j0 + c) * H + h) * B::floats;
@@ -556,8 +573,6 @@ __global__ __launch_bounds__(256) void bwd_dstate_kernel(const T* __restrict__ d
   auto load = [&](int c, Ops& o) {
     const float* bk = blk + (static_cast<size_t>(j0 + c) * H + h) * B::floats;
     const int row = 16 * w + r;
-#pragma unroll
-    for (int b = 0; b < NKB; ++b) o.kb[b] = *reinterpret_cast<const f32x4*>(bk + B::oKb + row * DK + 16 * b + 4 * g);
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const bool on = b >= w;
@@ -578,8 +593,8 @@ __global__ __launch_bounds__(256) void bwd_dstate_kernel(const T* __restrict__ d
   Ops cur, nxt;
   if (nch > 0) load(nch - 1, cur);
   for (int c = nch - 1; c >= 0; --c) {
-    OpsLate late;
-    load_late(c, late);
+    f32x4 kb[NKB];
+    load_kb(c, kb);
     if (c > 0) load(c - 1, nxt);  // before the state stores (see bwd_state_kernel)
     float* so = dsc + (static_cast<size_t>(j0 + c) * H + h) * DK * DV;
     lds_sync();  // the previous chunk's readers of Dl and Yl are done
@@ -606,9 +621,11 @@ __global__ __launch_bounds__(256) void bwd_dstate_kernel(const T* __restrict__ d
 #pragma unroll
     for (int b = 0; b < NKB; ++b)
 #pragma unroll
-      for (int m = 0; m < 4; ++m) acc = mf(cur.kb[b][m], Xl[(16 * b + 4 * g + m) * P20 + r], acc);
+      for (int m = 0; m < 4; ++m) acc = mf(kb[b][m], Xl[(16 * b + 4 * g + m) * P20 + r], acc);
 #pragma unroll
     for (int m = 0; m < 4; ++m) Zl[(16 * w + 4 * g + m) * P20 + r] = acc[m];
+    OpsLate late;
+    load_late(c, late);
     lds_sync();
     acc = zero4();
 #pragma unroll
@@ -642,6 +659,24 @@ __global__ __launch_bounds__(256) void bwd_dstate_kernel(const T* __restrict__ d
         dS0[sbase + static_cast<size_t>(row) * DV + col] = X[t][m];
       }
   }
+}
+
+// The two state passes in one launch: workgroups [0, half) run the forward
+// state pass, [half, 2 half) the reverse cotangent pass.  They share no data,
+// and two of these workgroups fit on a CU (LDS and registers), so the two
+// latency-bound chains interleave on every CU instead of running one after
+// the other.
+template <typename T, int DK, int DV>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_states_kernel(const T* __restrict__ v, const T* __restrict__ dO,
+                                                         const int32_t* __restrict__ cu,
+                                                         const int32_t* __restrict__ chunk_off,
+                                                         const int32_t* __restrict__ order, int N, int H,
+                                                         const float* __restrict__ blk, const float* __restrict__ S0,
+                                                         const float* __restrict__ dST, float* __restrict__ sc,
+                                                         float* __restrict__ dsc, float* __restrict__ dS0, int half) {
+  const int x = blockIdx.x;
+  if (x < half) bwd_state_body<T, DK, DV>(x, v, cu, chunk_off, order, N, H, blk, S0, sc);
+  else bwd_dstate_body<T, DK, DV>(x - half, dO, cu, chunk_off, order, N, H, blk, dST, dsc, dS0);
 }
 
 
@@ -1201,11 +1236,8 @@ static hipError_t launch_backward_t(const BackwardPlan& p, const void* q, const 
   }
   const int64_t NH = static_cast<int64_t>(p.N) * p.H;
   const unsigned seq_wgs = static_cast<unsigned>((NH + 7) / 8 * 8 * (DV / 16));
-  hipLaunchKernelGGL((bwd_state_kernel<T, DK, DV>), dim3(seq_wgs), dim3(256), 0, st, tv, cu, chunk_off, order, p.N,
-                     p.H, blk, S0, sc);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dstate_kernel<T, DK, DV>), dim3(seq_wgs), dim3(256), 0, st, tdo, cu, chunk_off, order,
-                     p.N, p.H, blk, dS_T, dsc, dS0);
+  hipLaunchKernelGGL((bwd_states_kernel<T, DK, DV>), dim3(2 * seq_wgs), dim3(256), 0, st, tv, tdo, cu, chunk_off,
+                     order, p.N, p.H, blk, S0, dS_T, sc, dsc, dS0, static_cast<int>(seq_wgs));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (mc > 0) {
     hipLaunchKernelGGL((bwd_grad_v_kernel<T, DK, DV>), dim3(mc, p.H), dim3(256), 0, st, tv, tdo, cu, chunk_off, p.N,
