@@ -984,8 +984,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // ---------------------------------------------------------------------------
 // grad_k: one workgroup (4 waves) per (chunk, head, SW key channels) -- or,
 // for the one-rate-per-head gate, per (chunk, head) over every channel, so
-// that the per-head gate cotangent is summed inside one workgroup.  Grid
-// (chunks, H, slices).  Thread t works on row t / 4 and SW / 4 consecutive
+// that the per-head gate cotangent is summed inside one workgroup (1-D
+// XCD-aware grid, below).  Thread t works on row t / 4 and SW / 4 consecutive
 // channels of the slice; SW = 16 keeps the LDS of two workgroups on a CU.
 //   GQ[r]  = sum_{s <= r} dP[r][s] k_s e^{G_r - G_s}
 //   GA[r]  = sum_{s <  r} dA[r][s] k_s e^{G_r - G_s}
@@ -1012,7 +1012,12 @@ __global__ __launch_bounds__(256) void bwd_grad_k_kernel(const T* __restrict__ q
   __shared__ float dPl[BC * LPC], dAl[BC * LPC];
   __shared__ float Ksc[96 * PS], Xq[96 * PS], Xk[96 * PS];
   __shared__ float tot[256], rsum[BC];
-  const int j = blockIdx.x, h = blockIdx.y;
+  // 1-D grid, XCD-aware: the NZ channel slices of one (chunk, head) get
+  // workgroup ids that differ by multiples of 8, i.e. one XCD and adjacent
+  // dispatch, so the dP and dA they all read come through one L2
+  constexpr int NZ = G == KDA_GATE_SCALAR ? 1 : DK / SW;
+  const int x = blockIdx.x, xcd = x & 7, rest = x >> 3, zs = rest % NZ, item = (rest / NZ) * 8 + xcd;
+  const int j = item / H, h = item % H;
   if (j >= chunk_off[N]) return;
   const ChunkLoc cl = locate(cu, chunk_off, N, j);
   const float* bk = blk + (static_cast<size_t>(j) * H + h) * B::floats;
@@ -1028,7 +1033,7 @@ __global__ __launch_bounds__(256) void bwd_grad_k_kernel(const T* __restrict__ q
   const int row = tid >> 2, c8 = (tid & 3) * CPT;
   const int I = row >> 4;
   for (int si = 0; si < NSW; ++si) {
-    const int c0 = (blockIdx.z * NSW + si) * SW;
+    const int c0 = (zs * NSW + si) * SW;
     {
       float xq[CPT], xk[CPT];
 #pragma unroll
@@ -1245,7 +1250,8 @@ static hipError_t launch_backward_t(const BackwardPlan& p, const void* q, const 
     if ((e = hipGetLastError()) != hipSuccess) return e;
     constexpr int SW = 16;  // key channels per grad_k slice (LDS for two workgroups per CU)
     const unsigned nz = G == KDA_GATE_SCALAR ? 1u : static_cast<unsigned>(DK / SW);
-    hipLaunchKernelGGL((bwd_grad_k_kernel<T, DK, G, SW>), dim3(mc, p.H, nz), dim3(256), 0, st, tq, tk, la, cu,
+    const unsigned items = (mc * static_cast<unsigned>(p.H) + 7u) / 8u * 8u;
+    hipLaunchKernelGGL((bwd_grad_k_kernel<T, DK, G, SW>), dim3(items * nz), dim3(256), 0, st, tq, tk, la, cu,
                        chunk_off, p.N, p.H, blk, static_cast<T*>(dq), static_cast<T*>(dk), dla);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
