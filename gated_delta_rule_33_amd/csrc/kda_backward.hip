@@ -75,10 +75,13 @@ __device__ __forceinline__ void lds_sync() {
   asm volatile("" ::: "memory");
 }
 
-// Per-(chunk, head) block, fp32 (offsets in floats).  Each factor is stored
-// in the orientation its consumers read it in: an MFMA operand fragment is
-// then four consecutive floats of one row (16-byte loads), never a gather.
-// "T" planes are transposed: KbT[i][r] = Kb[r][i], PT[s][r] = P[r][s].
+// Per-(chunk, head) block (offsets in floats).  The factors the products
+// read are split-bf16 planes (below): an R x K plane takes R K floats'
+// bytes, hi and lo bf16 of each 8-element group of a row side by side, so
+// an MFMA fragment (eight consecutive k of one row) is one 32-byte read with
+// no conversion.  Each factor is stored in the orientation its consumers
+// read it in ("T" planes are transposed: KbT[i][r] = Kb[r][i], PT[s][r] =
+// P[r][s]).  A, gamma and beta are fp32.
 template <int DK>
 struct BwdBlk {
   static constexpr size_t CD = static_cast<size_t>(BC) * DK;
@@ -99,6 +102,58 @@ struct BwdBlk {
 };
 
 size_t blk_floats(int dk) { return dk == 128 ? BwdBlk<128>::floats : BwdBlk<64>::floats; }
+
+// ---------------------------------------------------------------------------
+// Split-bf16 products.  An fp32 operand x is carried as hi = bf16(x) and
+// lo = bf16(x - hi) (hi + lo = x to ~2^-17 relative); a product of two such
+// operands is formed by three bf16 MFMAs (lo*hi + hi*lo + hi*hi, the small
+// terms first), dropping lo*lo: ~2^-16 relative per product, at 16,384 flops
+// per 16x16x32 instruction against 2,048 for the fp32 16x16x4 MFMA.
+// Fragments use the natural k map: lane (row or column l % 16, group
+// g = l / 16) holds k = 8 g .. 8 g + 7 of the 32-wide k step.
+// ---------------------------------------------------------------------------
+struct F3 {
+  bf16x8 h, l;
+};
+__device__ __forceinline__ F3 split8(f32x4 a, f32x4 b, float scale = 1.f) {
+  F3 f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float x = a[i] * scale, y = b[i] * scale;
+    f.h[i] = static_cast<__bf16>(x);
+    f.h[4 + i] = static_cast<__bf16>(y);
+    f.l[i] = static_cast<__bf16>(x - static_cast<float>(f.h[i]));
+    f.l[4 + i] = static_cast<__bf16>(y - static_cast<float>(f.h[4 + i]));
+  }
+  return f;
+}
+// eight consecutive floats (16-byte aligned) from LDS or global memory
+__device__ __forceinline__ F3 split8(const float* p, float scale = 1.f) {
+  return split8(*reinterpret_cast<const f32x4*>(p), *reinterpret_cast<const f32x4*>(p + 4), scale);
+}
+__device__ __forceinline__ f32x4 mm3(const F3& a, const F3& b, f32x4 c) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.l, b.h, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.h, b.l, c, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.h, b.h, c, 0, 0, 0);
+}
+
+// Split-bf16 plane of K columns: element (row, k) is bf16 (row * (K / 8) +
+// k / 8) * 16 + k % 8 (hi), + 8 (lo).  k0 below is a multiple of 8.
+__device__ __forceinline__ F3 pfrag(const float* plane, int K, int row, int k0) {
+  const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const __bf16*>(plane) + (row * (K / 8) + k0 / 8) * 16);
+  return F3{__builtin_bit_cast(bf16x8, p[0]), __builtin_bit_cast(bf16x8, p[1])};
+}
+__device__ __forceinline__ void pstore8(float* plane, int K, int row, int k0, const float* x) {
+  F3 f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    f.h[i] = static_cast<__bf16>(x[i]);
+    f.l[i] = static_cast<__bf16>(x[i] - static_cast<float>(f.h[i]));
+  }
+  uint4* p = reinterpret_cast<uint4*>(reinterpret_cast<__bf16*>(plane) + (row * (K / 8) + k0 / 8) * 16);
+  p[0] = __builtin_bit_cast(uint4, f.h);
+  p[1] = __builtin_bit_cast(uint4, f.l);
+}
 
 // (sequence, chunk, token range) of global chunk j (chunk_off non-decreasing,
 // chunk_off[N] > j).
@@ -255,23 +310,36 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, 
     }
     lds_sync();
     row_scan<false, PS>(gs, tot);
-    for (int e = tid; e < BC * 32; e += 256) {
-      const int row = e >> 5, ch = e & 31;
-      const float Gr = gs[row * PS + ch], GC = gs[(BC - 1) * PS + ch];
-      const float eg = __expf(Gr), eb = __expf(GC - Gr);
-      const float kv = ks[row * PS + ch];
-      const size_t o = static_cast<size_t>(row) * DK + c0 + ch;
-      bk[B::oKg + o] = kv * eg;
-      bk[B::oKb + o] = kv * eb;
+    {  // Kg, Kb: thread (row, 8-channel group) writes one fragment group of each
+      const int row = tid >> 2, c8 = (tid & 3) * 8;
+      float xg[8], xb[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int ch = c8 + i;
+        const float Gr = gs[row * PS + ch], GC = gs[(BC - 1) * PS + ch];
+        const float kv = ks[row * PS + ch];
+        xg[i] = kv * __expf(Gr);
+        xb[i] = kv * __expf(GC - Gr);
+      }
+      pstore8(bk + B::oKg, DK, row, c0 + c8, xg);
+      pstore8(bk + B::oKb, DK, row, c0 + c8, xb);
     }
-    for (int e = tid; e < BC * 32; e += 256) {  // transposed planes: consecutive threads, consecutive rows
-      const int row = e & 63, ch = e >> 6;
-      const float Gr = gs[row * PS + ch], GC = gs[(BC - 1) * PS + ch];
-      const float eg = __expf(Gr), eb = __expf(GC - Gr);
-      const size_t o = static_cast<size_t>(c0 + ch) * BC + row;
-      bk[B::oKbT + o] = ks[row * PS + ch] * eb;
-      bk[B::oKgT + o] = ks[row * PS + ch] * eg;
-      bk[B::oQgT + o] = qs[row * PS + ch] * eg;
+    {  // transposed planes: thread (channel, 8-row group)
+      const int ch = tid >> 3, r8 = (tid & 7) * 8;
+      float xb[8], xg[8], xq[8];
+      const float GC = gs[(BC - 1) * PS + ch];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int row = r8 + i;
+        const float Gr = gs[row * PS + ch];
+        const float eg = __expf(Gr);
+        xb[i] = ks[row * PS + ch] * __expf(GC - Gr);
+        xg[i] = ks[row * PS + ch] * eg;
+        xq[i] = qs[row * PS + ch] * eg;
+      }
+      pstore8(bk + B::oKbT, BC, c0 + ch, r8, xb);
+      pstore8(bk + B::oKgT, BC, c0 + ch, r8, xg);
+      pstore8(bk + B::oQgT, BC, c0 + ch, r8, xq);
     }
     if (tid < 32) bk[B::oGam + c0 + tid] = __expf(gs[(BC - 1) * PS + tid]);
     // off-diagonal block pairs (I, J < I), split at row 16 I - 1
@@ -311,26 +379,24 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, 
     }
     lds_sync();
   }
-  // A and P to the block (upper blocks zero), L = Diag(beta) A and T = 0 in LDS
-  auto put = [&](int I, int J, f32x4 a, f32x4 p) {
+  // A to the block (upper blocks zero), L = Diag(beta) A and T = 0 in LDS
+  // (P stays in its accumulators until T is done; it then goes through Lm)
+  auto putA = [&](int I, int J, f32x4 a) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int row = 16 * I + 4 * g + m, col = 16 * J + r;
       bk[B::oA + row * BC + col] = a[m];
       Lm[row * LPC + col] = bet[row] * a[m];
     }
-    // P^T: rows 16 I + 4 g .. + 3 of P are four consecutive floats of row col
-    *reinterpret_cast<f32x4*>(bk + B::oPT + (16 * J + r) * BC + 16 * I + 4 * g) = p;
   };
-  put(w, w, aD, pD);
+  putA(w, w, aD);
 #pragma unroll
   for (int u = 0; u < 2; ++u)
-    if (off_pair_i(w, u) >= 0) put(off_pair_i(w, u), off_pair_j(w, u), aO[u], pO[u]);
+    if (off_pair_i(w, u) >= 0) putA(off_pair_i(w, u), off_pair_j(w, u), aO[u]);
   for (int e = tid; e < BC * BC; e += 256) {
     const int row = e >> 6, col = e & 63;
     if ((col >> 4) > (row >> 4)) {
       bk[B::oA + e] = 0.f;
-      bk[B::oPT + col * BC + row] = 0.f;
       Lm[row * LPC + col] = 0.f;
     }
     Tm[row * LPC + col] = 0.f;
@@ -377,9 +443,33 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, 
     }
     lds_sync();
   }
+  // P into Lm (L is no longer needed), zero above the diagonal blocks
+  auto putP = [&](int I, int J, f32x4 pv) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) Lm[(16 * I + 4 * g + m) * LPC + 16 * J + r] = pv[m];
+  };
+  putP(w, w, pD);
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+    if (off_pair_i(w, u) >= 0) putP(off_pair_i(w, u), off_pair_j(w, u), pO[u]);
   for (int e = tid; e < BC * BC; e += 256) {
-    bk[B::oT + e] = Tm[(e >> 6) * LPC + (e & 63)];
-    bk[B::oTT + e] = Tm[(e & 63) * LPC + (e >> 6)];
+    const int row = e >> 6, col = e & 63;
+    if ((col >> 4) > (row >> 4)) Lm[row * LPC + col] = 0.f;
+  }
+  lds_sync();
+  // T, T^T and P^T planes: thread (row, 8-column group), two groups each
+  for (int e = tid; e < BC * 8; e += 256) {
+    const int row = e >> 3, c8 = (e & 7) * 8;
+    float xt[8], xtt[8], xpt[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      xt[i] = Tm[row * LPC + c8 + i];
+      xtt[i] = Tm[(c8 + i) * LPC + row];
+      xpt[i] = Lm[(c8 + i) * LPC + row];
+    }
+    pstore8(bk + B::oT, BC, row, c8, xt);
+    pstore8(bk + B::oTT, BC, row, c8, xtt);
+    pstore8(bk + B::oPT, BC, row, c8, xpt);
   }
 }
 
@@ -391,10 +481,42 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, 
 //   W = Diag(beta)(V - Kg S)   (wave w: rows 16 w .. 16 w + 15)
 //   U = T W
 //   S = Diag(gamma) S + Kb^T U
-// Each wave reads the block operands it needs straight into registers, one
-// chunk ahead.  Workgroup x: the value slices of a (sequence, head) share an
-// XCD (x % 8), so the slices read each block through one L2.
+// as split-bf16 products: the block factors are read as ready-split
+// fragments; S, W and U are split once, when they are handed over through
+// LDS (transposed, so that a B fragment is eight consecutive k of one
+// column).  Each wave reads the next chunk's W and U operands one chunk
+// ahead, and its Kb^T fragments at the start of the chunk that uses them.
+// Workgroup x: the value slices of a (sequence, head) share an XCD (x % 8),
+// so the slices read each block through one L2.
 // ---------------------------------------------------------------------------
+// A split-bf16 [16][K] hand-over tile in LDS (16 columns of a 16-column
+// slice, k contiguous): hi plane then lo plane, pitch K + 8 elements.
+template <int K>
+struct Tile16 {
+  static constexpr int P = K + 8;
+  static constexpr int elems = 2 * 16 * P;
+  __bf16* b;
+  __device__ __forceinline__ F3 frag(int n, int k0) const {
+    return F3{*reinterpret_cast<const bf16x8*>(b + n * P + k0), *reinterpret_cast<const bf16x8*>(b + 16 * P + n * P + k0)};
+  }
+  // four consecutive k of column n (8-byte aligned)
+  __device__ __forceinline__ void put4(int n, int k, f32x4 x) const {
+    bf16x4 hi, lo;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      hi[i] = static_cast<__bf16>(x[i]);
+      lo[i] = static_cast<__bf16>(x[i] - static_cast<float>(hi[i]));
+    }
+    *reinterpret_cast<bf16x4*>(b + n * P + k) = hi;
+    *reinterpret_cast<bf16x4*>(b + 16 * P + n * P + k) = lo;
+  }
+  __device__ __forceinline__ void put(int n, int k, float x) const {
+    const __bf16 hi = static_cast<__bf16>(x);
+    b[n * P + k] = hi;
+    b[16 * P + n * P + k] = static_cast<__bf16>(x - static_cast<float>(hi));
+  }
+};
+
 template <typename T, int DK, int DV>
 __device__ __forceinline__ void bwd_state_body(int x, const T* __restrict__ v, const int32_t* __restrict__ cu,
                                                const int32_t* __restrict__ chunk_off,
@@ -402,8 +524,10 @@ __device__ __forceinline__ void bwd_state_body(int x, const T* __restrict__ v, c
                                                const float* __restrict__ blk, const float* __restrict__ S0,
                                                float* __restrict__ sc) {
   typedef BwdBlk<DK> B;
-  constexpr int NSP = DV / 16, NKB = DK / 16, TPW = NKB / 4;
-  __shared__ float Xl[DK * P20], Wl[BC * P20], Ul[BC * P20];
+  constexpr int NSP = DV / 16, NKB = DK / 16, TPW = NKB / 4, NKS = DK / 32;
+  __shared__ __align__(16) __bf16 lds_s[Tile16<DK>::elems + 2 * Tile16<BC>::elems];
+  const Tile16<DK> XT{lds_s};
+  const Tile16<BC> WT{lds_s + Tile16<DK>::elems}, UT{lds_s + Tile16<DK>::elems + Tile16<BC>::elems};
   const int xcd = x & 7, s8 = x >> 3, sp = s8 % NSP, p = (s8 / NSP) * 8 + xcd;
   if (p >= N * H) return;
   const int n = order[p / H], h = p % H;
@@ -411,6 +535,7 @@ __device__ __forceinline__ void bwd_state_body(int x, const T* __restrict__ v, c
   const int tb = cu[n], L = cu[n + 1] - tb, nch = (L + BC - 1) / BC, j0 = chunk_off[n];
   const int col = sp * 16 + r;
   const size_t sbase = (static_cast<size_t>(n) * H + h) * DK * DV;
+  const int kT1 = w >= 2 ? 1 : 0;  // k steps of T's row tile w: rows <= 16 w + 15
   f32x4 X[TPW];
 #pragma unroll
   for (int t = 0; t < TPW; ++t)
@@ -420,36 +545,21 @@ __device__ __forceinline__ void bwd_state_body(int x, const T* __restrict__ v, c
       X[t][m] = S0 ? S0[sbase + static_cast<size_t>(row) * DV + col] : 0.f;
     }
   struct Ops {
-    f32x4 kg[NKB];
-    f32x4 tt[4];
+    F3 kg[NKS];
+    F3 tt[2];
     float vv[4], bet[4], gam[TPW][4];
-  };
-  // Kb^T rows of the wave's key channels (used in the chunk's last phase):
-  // read at the start of that chunk, not a chunk ahead (register budget of
-  // two workgroups per CU)
-  struct OpsLate {
-    f32x4 kbt[TPW][4];
-  };
-  auto load_late = [&](int c, OpsLate& o) {
-    const float* bk = blk + (static_cast<size_t>(j0 + c) * H + h) * B::floats;
-#pragma unroll
-    for (int t = 0; t < TPW; ++t)
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-        o.kbt[t][b] = *reinterpret_cast<const f32x4*>(bk + B::oKbT + (16 * (w * TPW + t) + r) * BC + 16 * b + 4 * g);
   };
   auto load = [&](int c, Ops& o) {
     const float* bk = blk + (static_cast<size_t>(j0 + c) * H + h) * B::floats;
     const int row = 16 * w + r;
 #pragma unroll
-    for (int b = 0; b < NKB; ++b) o.kg[b] = *reinterpret_cast<const f32x4*>(bk + B::oKg + row * DK + 16 * b + 4 * g);
+    for (int kk = 0; kk < NKS; ++kk) o.kg[kk] = pfrag(bk + B::oKg, DK, row, 32 * kk + 8 * g);
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
-      o.tt[b] = b <= w ? *reinterpret_cast<const f32x4*>(bk + B::oT + row * BC + 16 * b + 4 * g) : zero4();
+    for (int kk = 0; kk < 2; ++kk) o.tt[kk] = pfrag(bk + B::oT, BC, row, 32 * kk + 8 * g);
     const int t0 = tb + c * BC, len = min(BC, L - c * BC);
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      // rows past the sequence read the last row: their beta is 0, so W is 0
+      // rows past the sequence read its last row: their beta is 0, so W is 0
       // there whatever v holds (no branch, no wait on the load here)
       const int rr = 16 * w + 4 * g + m, rc = min(rr, len - 1);
       o.vv[m] = io<T>::load(v + (static_cast<size_t>(t0 + rc) * H + h) * DV + col);
@@ -463,47 +573,45 @@ __device__ __forceinline__ void bwd_state_body(int x, const T* __restrict__ v, c
   Ops cur, nxt;
   if (nch > 0) load(0, cur);
   for (int c = 0; c < nch; ++c) {
-    OpsLate late;
-    load_late(c, late);
-    // next chunk's operands first: the memory counter is in order, so the
-    // wait for these loads at the end of the chunk does not also wait for the
-    // state stores issued after them
+    F3 kbt[TPW][2];  // Kb^T rows of the wave's channels, for the last phase
+    {
+      const float* bk = blk + (static_cast<size_t>(j0 + c) * H + h) * B::floats;
+#pragma unroll
+      for (int t = 0; t < TPW; ++t)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) kbt[t][kk] = pfrag(bk + B::oKbT, BC, 16 * (w * TPW + t) + r, 32 * kk + 8 * g);
+    }
+    // next chunk's operands before the state stores: the memory counter is in
+    // order, so waiting for these loads does not also wait for the stores
     if (c + 1 < nch) load(c + 1, nxt);
     float* so = sc + (static_cast<size_t>(j0 + c) * H + h) * DK * DV;
 #pragma unroll
-    for (int t = 0; t < TPW; ++t)
+    for (int t = 0; t < TPW; ++t) {
+      XT.put4(r, 16 * (w * TPW + t) + 4 * g, X[t]);
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int row = 16 * (w * TPW + t) + 4 * g + m;
-        Xl[row * P20 + r] = X[t][m];
-        so[static_cast<size_t>(row) * DV + col] = X[t][m];
-      }
+      for (int m = 0; m < 4; ++m) so[static_cast<size_t>(16 * (w * TPW + t) + 4 * g + m) * DV + col] = X[t][m];
+    }
     lds_sync();
     f32x4 acc = zero4();
 #pragma unroll
-    for (int b = 0; b < NKB; ++b)
+    for (int kk = 0; kk < NKS; ++kk) acc = mm3(cur.kg[kk], XT.frag(r, 32 * kk + 8 * g), acc);
+    f32x4 wv;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) acc = mf(cur.kg[b][m], Xl[(16 * b + 4 * g + m) * P20 + r], acc);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) Wl[(16 * w + 4 * g + m) * P20 + r] = cur.bet[m] * (cur.vv[m] - acc[m]);
+    for (int m = 0; m < 4; ++m) wv[m] = cur.bet[m] * (cur.vv[m] - acc[m]);
+    WT.put4(r, 16 * w + 4 * g, wv);
     lds_sync();
     acc = zero4();
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
-      if (b <= w)
-#pragma unroll
-        for (int m = 0; m < 4; ++m) acc = mf(cur.tt[b][m], Wl[(16 * b + 4 * g + m) * P20 + r], acc);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) Ul[(16 * w + 4 * g + m) * P20 + r] = acc[m];
+    for (int kk = 0; kk < 2; ++kk)
+      if (kk <= kT1) acc = mm3(cur.tt[kk], WT.frag(r, 32 * kk + 8 * g), acc);
+    UT.put4(r, 16 * w + 4 * g, acc);
     lds_sync();
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
 #pragma unroll
       for (int m = 0; m < 4; ++m) X[t][m] *= cur.gam[t][m];
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
-#pragma unroll
-        for (int m = 0; m < 4; ++m) X[t] = mf(late.kbt[t][b][m], Ul[(16 * b + 4 * g + m) * P20 + r], X[t]);
+      for (int kk = 0; kk < 2; ++kk) X[t] = mm3(kbt[t][kk], UT.frag(r, 32 * kk + 8 * g), X[t]);
     }
     cur = nxt;
   }
@@ -514,6 +622,10 @@ __device__ __forceinline__ void bwd_state_body(int x, const T* __restrict__ v, c
 // with the same workgroup layout as the state pass.  Per chunk (X = dS of
 // the chunk's final state on entry, of its entry state on exit):
 //   Z = P^T dO + Kb X,  Y = T^T Z,  X = Diag(gamma) X + Qg^T dO - Kg^T Diag(beta) Y
+// as split-bf16 products (dO, Z and -beta Y handed over through LDS,
+// transposed).  P^T and T^T rows are read a chunk ahead; Kb at the start of
+// the chunk, Qg^T and Kg^T after its first phase (register budget of two
+// workgroups per CU).
 // ---------------------------------------------------------------------------
 template <typename T, int DK, int DV>
 __device__ __forceinline__ void bwd_dstate_body(int x, const T* __restrict__ dO, const int32_t* __restrict__ cu,
@@ -522,8 +634,11 @@ __device__ __forceinline__ void bwd_dstate_body(int x, const T* __restrict__ dO,
                                                 const float* __restrict__ blk, const float* __restrict__ dST,
                                                 float* __restrict__ dsc, float* __restrict__ dS0) {
   typedef BwdBlk<DK> B;
-  constexpr int NSP = DV / 16, NKB = DK / 16, TPW = NKB / 4;
-  __shared__ float Xl[DK * P20], Dl[BC * P20], Zl[BC * P20], Yl[BC * P20];
+  constexpr int NSP = DV / 16, NKB = DK / 16, TPW = NKB / 4, NKS = DK / 32;
+  __shared__ __align__(16) __bf16 lds_d[Tile16<DK>::elems + 3 * Tile16<BC>::elems];
+  const Tile16<DK> XT{lds_d};
+  const Tile16<BC> DT{lds_d + Tile16<DK>::elems}, ZT{lds_d + Tile16<DK>::elems + Tile16<BC>::elems},
+      YT{lds_d + Tile16<DK>::elems + 2 * Tile16<BC>::elems};
   const int xcd = x & 7, s8 = x >> 3, sp = s8 % NSP, p = (s8 / NSP) * 8 + xcd;
   if (p >= N * H) return;
   const int n = order[p / H], h = p % H;
@@ -531,6 +646,7 @@ __device__ __forceinline__ void bwd_dstate_body(int x, const T* __restrict__ dO,
   const int tb = cu[n], L = cu[n + 1] - tb, nch = (L + BC - 1) / BC, j0 = chunk_off[n];
   const int col = sp * 16 + r;
   const size_t sbase = (static_cast<size_t>(n) * H + h) * DK * DV;
+  const int kU0 = w >= 2 ? 1 : 0;  // k steps of P^T, T^T row tile w: rows >= 16 w
   f32x4 X[TPW];
 #pragma unroll
   for (int t = 0; t < TPW; ++t)
@@ -541,43 +657,18 @@ __device__ __forceinline__ void bwd_dstate_body(int x, const T* __restrict__ dO,
     }
   typedef typename raw4<T>::type R4;
   struct Ops {
-    f32x4 pt[4], tt[4];
+    F3 pt[2], tt[2];
     R4 dov;
     float bet[4], gam[TPW][4];
   };
-  // Kb rows and the Qg^T, Kg^T rows of the wave's key channels: read at the
-  // start of the chunk that uses them, not a chunk ahead, so that the pass
-  // fits the register budget of two workgroups per CU
-  // (Kb for the first phase, Qg^T and Kg^T issued after it, for the last)
-  struct OpsLate {
-    f32x4 qgt[TPW][4], kgt[TPW][4];
-  };
-  auto load_kb = [&](int c, f32x4* kb) {
-    const float* bk = blk + (static_cast<size_t>(j0 + c) * H + h) * B::floats;
-#pragma unroll
-    for (int b = 0; b < NKB; ++b)
-      kb[b] = *reinterpret_cast<const f32x4*>(bk + B::oKb + (16 * w + r) * DK + 16 * b + 4 * g);
-  };
-  auto load_late = [&](int c, OpsLate& o) {
-    const float* bk = blk + (static_cast<size_t>(j0 + c) * H + h) * B::floats;
-#pragma unroll
-    for (int t = 0; t < TPW; ++t)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int o2 = (16 * (w * TPW + t) + r) * BC + 16 * b + 4 * g;
-        o.qgt[t][b] = *reinterpret_cast<const f32x4*>(bk + B::oQgT + o2);
-        o.kgt[t][b] = *reinterpret_cast<const f32x4*>(bk + B::oKgT + o2);
-      }
-  };
-  const int drow = tid >> 2, dc4 = (tid & 3) * 4;  // this thread's 4 dO values for the LDS tile
+  const int drow = tid >> 2, dc4 = (tid & 3) * 4;  // this thread's 4 dO values for the hand-over tile
   auto load = [&](int c, Ops& o) {
     const float* bk = blk + (static_cast<size_t>(j0 + c) * H + h) * B::floats;
     const int row = 16 * w + r;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const bool on = b >= w;
-      o.pt[b] = on ? *reinterpret_cast<const f32x4*>(bk + B::oPT + row * BC + 16 * b + 4 * g) : zero4();
-      o.tt[b] = on ? *reinterpret_cast<const f32x4*>(bk + B::oTT + row * BC + 16 * b + 4 * g) : zero4();
+    for (int kk = 0; kk < 2; ++kk) {
+      o.pt[kk] = pfrag(bk + B::oPT, BC, row, 32 * kk + 8 * g);
+      o.tt[kk] = pfrag(bk + B::oTT, BC, row, 32 * kk + 8 * g);
     }
     const int t0 = tb + c * BC, len = min(BC, L - c * BC);
     // rows past the sequence read the last row: P and Qg are zero in those
@@ -593,60 +684,59 @@ __device__ __forceinline__ void bwd_dstate_body(int x, const T* __restrict__ dO,
   Ops cur, nxt;
   if (nch > 0) load(nch - 1, cur);
   for (int c = nch - 1; c >= 0; --c) {
-    f32x4 kb[NKB];
-    load_kb(c, kb);
-    if (c > 0) load(c - 1, nxt);  // before the state stores (see bwd_state_kernel)
+    const float* bkc = blk + (static_cast<size_t>(j0 + c) * H + h) * B::floats;
+    F3 kb[NKS];
+#pragma unroll
+    for (int kk = 0; kk < NKS; ++kk) kb[kk] = pfrag(bkc + B::oKb, DK, 16 * w + r, 32 * kk + 8 * g);
+    if (c > 0) load(c - 1, nxt);  // before the state stores (see bwd_state_body)
     float* so = dsc + (static_cast<size_t>(j0 + c) * H + h) * DK * DV;
-    lds_sync();  // the previous chunk's readers of Dl and Yl are done
+    lds_sync();  // the previous chunk's readers of DT and YT are done
 #pragma unroll
-    for (int t = 0; t < TPW; ++t)
+    for (int t = 0; t < TPW; ++t) {
+      XT.put4(r, 16 * (w * TPW + t) + 4 * g, X[t]);
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int row = 16 * (w * TPW + t) + 4 * g + m;
-        Xl[row * P20 + r] = X[t][m];
-        so[static_cast<size_t>(row) * DV + col] = X[t][m];
-      }
+      for (int m = 0; m < 4; ++m) so[static_cast<size_t>(16 * (w * TPW + t) + 4 * g + m) * DV + col] = X[t][m];
+    }
     {
       const f32x4 d = cvt4(cur.dov);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Dl[drow * P20 + dc4 + i] = d[i];
+      for (int i = 0; i < 4; ++i) DT.put(dc4 + i, drow, d[i]);
     }
     lds_sync();
     f32x4 acc = zero4();
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
-      if (b >= w)
+    for (int kk = 0; kk < 2; ++kk)
+      if (kk >= kU0) acc = mm3(cur.pt[kk], DT.frag(r, 32 * kk + 8 * g), acc);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) acc = mf(cur.pt[b][m], Dl[(16 * b + 4 * g + m) * P20 + r], acc);
+    for (int kk = 0; kk < NKS; ++kk) acc = mm3(kb[kk], XT.frag(r, 32 * kk + 8 * g), acc);
+    ZT.put4(r, 16 * w + 4 * g, acc);
+    F3 qgt[TPW][2], kgt[TPW][2];
 #pragma unroll
-    for (int b = 0; b < NKB; ++b)
+    for (int t = 0; t < TPW; ++t)
 #pragma unroll
-      for (int m = 0; m < 4; ++m) acc = mf(kb[b][m], Xl[(16 * b + 4 * g + m) * P20 + r], acc);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) Zl[(16 * w + 4 * g + m) * P20 + r] = acc[m];
-    OpsLate late;
-    load_late(c, late);
+      for (int kk = 0; kk < 2; ++kk) {
+        qgt[t][kk] = pfrag(bkc + B::oQgT, BC, 16 * (w * TPW + t) + r, 32 * kk + 8 * g);
+        kgt[t][kk] = pfrag(bkc + B::oKgT, BC, 16 * (w * TPW + t) + r, 32 * kk + 8 * g);
+      }
     lds_sync();
     acc = zero4();
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
-      if (b >= w)
+    for (int kk = 0; kk < 2; ++kk)
+      if (kk >= kU0) acc = mm3(cur.tt[kk], ZT.frag(r, 32 * kk + 8 * g), acc);
+    f32x4 yb;
 #pragma unroll
-        for (int m = 0; m < 4; ++m) acc = mf(cur.tt[b][m], Zl[(16 * b + 4 * g + m) * P20 + r], acc);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) Yl[(16 * w + 4 * g + m) * P20 + r] = -cur.bet[m] * acc[m];
+    for (int m = 0; m < 4; ++m) yb[m] = -cur.bet[m] * acc[m];
+    YT.put4(r, 16 * w + 4 * g, yb);
     lds_sync();
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
 #pragma unroll
       for (int m = 0; m < 4; ++m) X[t][m] *= cur.gam[t][m];
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          X[t] = mf(late.qgt[t][b][m], Dl[(16 * b + 4 * g + m) * P20 + r], X[t]);
-          X[t] = mf(late.kgt[t][b][m], Yl[(16 * b + 4 * g + m) * P20 + r], X[t]);
-        }
+      for (int kk = 0; kk < 2; ++kk) {
+        X[t] = mm3(qgt[t][kk], DT.frag(r, 32 * kk + 8 * g), X[t]);
+        X[t] = mm3(kgt[t][kk], YT.frag(r, 32 * kk + 8 * g), X[t]);
+      }
     }
     cur = nxt;
   }
@@ -680,39 +770,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 
-// ---------------------------------------------------------------------------
-// Split-bf16 products.  An fp32 operand x is carried as hi = bf16(x) and
-// lo = bf16(x - hi) (hi + lo = x to ~2^-17 relative); a product of two such
-// operands is formed by three bf16 MFMAs (lo*hi + hi*lo + hi*hi, the small
-// terms first), dropping lo*lo: ~2^-16 relative per product, at 16,384 flops
-// per 16x16x32 instruction against 2,048 for the fp32 16x16x4 MFMA.
-// Fragments use the natural k map: lane (row or column l % 16, group
-// g = l / 16) holds k = 8 g .. 8 g + 7 of the 32-wide k step.
-// ---------------------------------------------------------------------------
-struct F3 {
-  bf16x8 h, l;
-};
-__device__ __forceinline__ F3 split8(f32x4 a, f32x4 b, float scale = 1.f) {
-  F3 f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float x = a[i] * scale, y = b[i] * scale;
-    f.h[i] = static_cast<__bf16>(x);
-    f.h[4 + i] = static_cast<__bf16>(y);
-    f.l[i] = static_cast<__bf16>(x - static_cast<float>(f.h[i]));
-    f.l[4 + i] = static_cast<__bf16>(y - static_cast<float>(f.h[4 + i]));
-  }
-  return f;
-}
-// eight consecutive floats (16-byte aligned) from LDS or global memory
-__device__ __forceinline__ F3 split8(const float* p, float scale = 1.f) {
-  return split8(*reinterpret_cast<const f32x4*>(p), *reinterpret_cast<const f32x4*>(p + 4), scale);
-}
-__device__ __forceinline__ f32x4 mm3(const F3& a, const F3& b, f32x4 c) {
-  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.l, b.h, c, 0, 0, 0);
-  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.h, b.l, c, 0, 0, 0);
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.h, b.h, c, 0, 0, 0);
-}
 
 // ---------------------------------------------------------------------------
 // grad_v: one workgroup (4 waves) per (chunk, head); grid (chunks, H).  Walks
@@ -809,20 +866,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
   if (tid < BC) betl[tid] = bk[B::oBeta + tid];
   for (int e = tid; e < BC * 5; e += 256) dbp[e] = 0.f;
-  // block operands of the wave's row tile (rows 16 w + r), split once
+  // block operands of the wave's row tile (rows 16 w + r), ready split
   F3 kgf[NKS], kbf[NKS], tf[2], ptf[2], ttf[2];
   {
     const int row = 16 * w + r;
 #pragma unroll
     for (int kk = 0; kk < NKS; ++kk) {
-      kgf[kk] = split8(bk + B::oKg + row * DK + 32 * kk + 8 * g);
-      kbf[kk] = split8(bk + B::oKb + row * DK + 32 * kk + 8 * g);
+      kgf[kk] = pfrag(bk + B::oKg, DK, row, 32 * kk + 8 * g);
+      kbf[kk] = pfrag(bk + B::oKb, DK, row, 32 * kk + 8 * g);
     }
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      tf[kk] = split8(bk + B::oT + row * BC + 32 * kk + 8 * g);
-      ptf[kk] = split8(bk + B::oPT + row * BC + 32 * kk + 8 * g);
-      ttf[kk] = split8(bk + B::oTT + row * BC + 32 * kk + 8 * g);
+      tf[kk] = pfrag(bk + B::oT, BC, row, 32 * kk + 8 * g);
+      ptf[kk] = pfrag(bk + B::oPT, BC, row, 32 * kk + 8 * g);
+      ttf[kk] = pfrag(bk + B::oTT, BC, row, 32 * kk + 8 * g);
     }
   }
   float bet[4];
