@@ -77,9 +77,8 @@ __device__ __forceinline__ void lds_sync() {
 
 // Per-(chunk, head) block (offsets in floats).  The factors the products
 // read are split-bf16 planes (below): an R x K plane takes R K floats'
-// bytes, hi and lo bf16 of each 8-element group of a row side by side, so
-// an MFMA fragment (eight consecutive k of one row) is one 32-byte read with
-// no conversion.  Each factor is stored in the orientation its consumers
+// bytes, in 16 x 32 fragment tiles, so a wave reads an MFMA fragment as two
+// contiguous kilobytes with no conversion.  Each factor is stored in the orientation its consumers
 // read it in ("T" planes are transposed: KbT[i][r] = Kb[r][i], PT[s][r] =
 // P[r][s]).  A, gamma and beta are fp32.
 template <int DK>
@@ -137,11 +136,18 @@ __device__ __forceinline__ f32x4 mm3(const F3& a, const F3& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.h, b.h, c, 0, 0, 0);
 }
 
-// Split-bf16 plane of K columns: element (row, k) is bf16 (row * (K / 8) +
-// k / 8) * 16 + k % 8 (hi), + 8 (lo).  k0 below is a multiple of 8.
+// Split-bf16 plane of R x K (R a multiple of 16, K of 32), stored as
+// fragment tiles: tile (row / 16, k / 32) is 1,024 bf16, the 16 x 32 hi
+// values then the lo values, each in fragment order (eight consecutive k of
+// one row at (((k / 8) % 4) * 16 + row % 16) * 8).  A wave's fragment read
+// (lane = row % 16 + 16 ((k / 8) % 4)) is then one contiguous kilobyte per
+// half.  k0 below is a multiple of 8.
+__device__ __forceinline__ size_t ptile(int K, int row, int k0) {
+  return static_cast<size_t>((row >> 4) * (K >> 5) + (k0 >> 5)) * 1024 + (((k0 >> 3) & 3) * 16 + (row & 15)) * 8;
+}
 __device__ __forceinline__ F3 pfrag(const float* plane, int K, int row, int k0) {
-  const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const __bf16*>(plane) + (row * (K / 8) + k0 / 8) * 16);
-  return F3{__builtin_bit_cast(bf16x8, p[0]), __builtin_bit_cast(bf16x8, p[1])};
+  const __bf16* p = reinterpret_cast<const __bf16*>(plane) + ptile(K, row, k0);
+  return F3{*reinterpret_cast<const bf16x8*>(p), *reinterpret_cast<const bf16x8*>(p + 512)};
 }
 __device__ __forceinline__ void pstore8(float* plane, int K, int row, int k0, const float* x) {
   F3 f;
@@ -150,10 +156,27 @@ __device__ __forceinline__ void pstore8(float* plane, int K, int row, int k0, co
     f.h[i] = static_cast<__bf16>(x[i]);
     f.l[i] = static_cast<__bf16>(x[i] - static_cast<float>(f.h[i]));
   }
-  uint4* p = reinterpret_cast<uint4*>(reinterpret_cast<__bf16*>(plane) + (row * (K / 8) + k0 / 8) * 16);
-  p[0] = __builtin_bit_cast(uint4, f.h);
-  p[1] = __builtin_bit_cast(uint4, f.l);
+  __bf16* p = reinterpret_cast<__bf16*>(plane) + ptile(K, row, k0);
+  *reinterpret_cast<bf16x8*>(p) = f.h;
+  *reinterpret_cast<bf16x8*>(p + 512) = f.l;
 }
+
+// One io element kept as loaded (bf16 bits or fp32) until it is used, so a
+// load issued ahead is not waited for at the load.
+template <typename T>
+struct raw1;
+template <>
+struct raw1<float> {
+  typedef float type;
+  __device__ __forceinline__ static float load(const float* p) { return *p; }
+  __device__ __forceinline__ static float cvt(float x) { return x; }
+};
+template <>
+struct raw1<bf16_t> {
+  typedef uint32_t type;
+  __device__ __forceinline__ static uint32_t load(const bf16_t* p) { return p->bits; }
+  __device__ __forceinline__ static float cvt(uint32_t b) { return __uint_as_float(b << 16); }
+};
 
 // (sequence, chunk, token range) of global chunk j (chunk_off non-decreasing,
 // chunk_off[N] > j).
@@ -517,6 +540,17 @@ struct Tile16 {
   }
 };
 
+// Loop-carried accumulators that start from a global load: the compiler's
+// memory-counter bookkeeping cannot tell the first iteration from the
+// others, so inside the loop it would wait at every step for loads issued
+// after these (the next chunk's operands).  Redefining the registers once,
+// before the loop, ends that: the wait happens here, once.
+template <int N>
+__device__ __forceinline__ void settle(f32x4 (&x)[N]) {
+#pragma unroll
+  for (int t = 0; t < N; ++t) asm volatile("" : "+v"(x[t]));
+}
+
 template <typename T, int DK, int DV>
 __device__ __forceinline__ void bwd_state_body(int x, const T* __restrict__ v, const int32_t* __restrict__ cu,
                                                const int32_t* __restrict__ chunk_off,
@@ -544,10 +578,12 @@ __device__ __forceinline__ void bwd_state_body(int x, const T* __restrict__ v, c
       const int row = 16 * (w * TPW + t) + 4 * g + m;
       X[t][m] = S0 ? S0[sbase + static_cast<size_t>(row) * DV + col] : 0.f;
     }
+  settle(X);
   struct Ops {
     F3 kg[NKS];
     F3 tt[2];
-    float vv[4], bet[4], gam[TPW][4];
+    typename raw1<T>::type vv[4];
+    float bet[4], gam[TPW][4];
   };
   auto load = [&](int c, Ops& o) {
     const float* bk = blk + (static_cast<size_t>(j0 + c) * H + h) * B::floats;
@@ -562,7 +598,7 @@ __device__ __forceinline__ void bwd_state_body(int x, const T* __restrict__ v, c
       // rows past the sequence read its last row: their beta is 0, so W is 0
       // there whatever v holds (no branch, no wait on the load here)
       const int rr = 16 * w + 4 * g + m, rc = min(rr, len - 1);
-      o.vv[m] = io<T>::load(v + (static_cast<size_t>(t0 + rc) * H + h) * DV + col);
+      o.vv[m] = raw1<T>::load(v + (static_cast<size_t>(t0 + rc) * H + h) * DV + col);
       o.bet[m] = bk[B::oBeta + rr];
     }
 #pragma unroll
@@ -597,7 +633,7 @@ __device__ __forceinline__ void bwd_state_body(int x, const T* __restrict__ v, c
     for (int kk = 0; kk < NKS; ++kk) acc = mm3(cur.kg[kk], XT.frag(r, 32 * kk + 8 * g), acc);
     f32x4 wv;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) wv[m] = cur.bet[m] * (cur.vv[m] - acc[m]);
+    for (int m = 0; m < 4; ++m) wv[m] = cur.bet[m] * (raw1<T>::cvt(cur.vv[m]) - acc[m]);
     WT.put4(r, 16 * w + 4 * g, wv);
     lds_sync();
     acc = zero4();
@@ -655,6 +691,7 @@ __device__ __forceinline__ void bwd_dstate_body(int x, const T* __restrict__ dO,
       const int row = 16 * (w * TPW + t) + 4 * g + m;
       X[t][m] = dST ? dST[sbase + static_cast<size_t>(row) * DV + col] : 0.f;
     }
+  settle(X);
   typedef typename raw4<T>::type R4;
   struct Ops {
     F3 pt[2], tt[2];
@@ -866,20 +903,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
   if (tid < BC) betl[tid] = bk[B::oBeta + tid];
   for (int e = tid; e < BC * 5; e += 256) dbp[e] = 0.f;
-  // block operands of the wave's row tile (rows 16 w + r), ready split
+  // block operands of the wave's row tile (rows 16 w + r), split once
   F3 kgf[NKS], kbf[NKS], tf[2], ptf[2], ttf[2];
   {
     const int row = 16 * w + r;
 #pragma unroll
     for (int kk = 0; kk < NKS; ++kk) {
-      kgf[kk] = pfrag(bk + B::oKg, DK, row, 32 * kk + 8 * g);
-      kbf[kk] = pfrag(bk + B::oKb, DK, row, 32 * kk + 8 * g);
+      kgf[kk] = split8(bk + B::oKg + row * DK + 32 * kk + 8 * g);
+      kbf[kk] = split8(bk + B::oKb + row * DK + 32 * kk + 8 * g);
     }
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      tf[kk] = pfrag(bk + B::oT, BC, row, 32 * kk + 8 * g);
-      ptf[kk] = pfrag(bk + B::oPT, BC, row, 32 * kk + 8 * g);
-      ttf[kk] = pfrag(bk + B::oTT, BC, row, 32 * kk + 8 * g);
+      tf[kk] = split8(bk + B::oT + row * BC + 32 * kk + 8 * g);
+      ptf[kk] = split8(bk + B::oPT + row * BC + 32 * kk + 8 * g);
+      ttf[kk] = split8(bk + B::oTT + row * BC + 32 * kk + 8 * g);
     }
   }
   float bet[4];
