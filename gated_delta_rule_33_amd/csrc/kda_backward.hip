@@ -903,20 +903,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
   if (tid < BC) betl[tid] = bk[B::oBeta + tid];
   for (int e = tid; e < BC * 5; e += 256) dbp[e] = 0.f;
-  // block operands of the wave's row tile (rows 16 w + r), split once
+  // block operands of the wave's row tile (rows 16 w + r), ready split
   F3 kgf[NKS], kbf[NKS], tf[2], ptf[2], ttf[2];
   {
     const int row = 16 * w + r;
 #pragma unroll
     for (int kk = 0; kk < NKS; ++kk) {
-      kgf[kk] = split8(bk + B::oKg + row * DK + 32 * kk + 8 * g);
-      kbf[kk] = split8(bk + B::oKb + row * DK + 32 * kk + 8 * g);
+      kgf[kk] = pfrag(bk + B::oKg, DK, row, 32 * kk + 8 * g);
+      kbf[kk] = pfrag(bk + B::oKb, DK, row, 32 * kk + 8 * g);
     }
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      tf[kk] = split8(bk + B::oT + row * BC + 32 * kk + 8 * g);
-      ptf[kk] = split8(bk + B::oPT + row * BC + 32 * kk + 8 * g);
-      ttf[kk] = split8(bk + B::oTT + row * BC + 32 * kk + 8 * g);
+      tf[kk] = pfrag(bk + B::oT, BC, row, 32 * kk + 8 * g);
+      ptf[kk] = pfrag(bk + B::oPT, BC, row, 32 * kk + 8 * g);
+      ttf[kk] = pfrag(bk + B::oTT, BC, row, 32 * kk + 8 * g);
     }
   }
   float bet[4];
