@@ -1505,17 +1505,32 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
         const int b = (cc - cb) & 1;
         ensure(cc + 1);
         late(cc + 1, b ^ 1);
-        ostore(cc - 1);
-        // in flight, oldest first: early part of chunk cc + 1, the previous
-        // prefetch, late part of cc + 1, output stores of cc - 1
-        wait_vm<NPF + NLT + NSW>();  // early part of chunk cc + 1 resident
-        lds_barrier();  // M(cc): early slot b free; the state waves read chunk cc + 1's R rows from here on
-        ensure(cc + 2);
-        early(cc + 2, b);
-        prefetch(cc + 4);
-        wait_vm<NE + NPF>();  // all but the early part of chunk cc + 2 and the prefetch: chunk cc + 1 resident
+        if constexpr (SL::split) {
+          // With split roles the output wave stages chunk cc - 1's tile
+          // between the end of that chunk and M(cc), so it is stored after M.
+          // In flight, oldest first: early part of chunk cc + 1, the
+          // previous prefetch, late part of cc + 1.
+          wait_vm<NPF + NLT>();  // early part of chunk cc + 1 resident
+          lds_barrier();  // M(cc): early slot b free; the state waves read chunk cc + 1's R rows from here on
+          ostore(cc - 1);
+          ensure(cc + 2);
+          early(cc + 2, b);
+          prefetch(cc + 4);
+          wait_vm<NSW + NE + NPF>();  // all but the stores, chunk cc + 2's early part and the prefetch
+        } else {
+          ostore(cc - 1);
+          // in flight, oldest first: early part of chunk cc + 1, the previous
+          // prefetch, late part of cc + 1, output stores of cc - 1
+          wait_vm<NPF + NLT + NSW>();  // early part of chunk cc + 1 resident
+          lds_barrier();  // M(cc): early slot b free; the state waves read chunk cc + 1's R rows from here on
+          ensure(cc + 2);
+          early(cc + 2, b);
+          prefetch(cc + 4);
+          wait_vm<NE + NPF>();  // all but the early part of chunk cc + 2 and the prefetch: chunk cc + 1 resident
+        }
         lds_barrier();  // end of chunk cc
       }
+      if constexpr (SL::split) lds_barrier();  // F: the last chunk's output tile staged
       ostore(ce - 1);
       return;
     }
@@ -1686,6 +1701,11 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
         const unsigned char* lblk = lblk_of(cc);
         DIn din;
         load_din(lblk, din);
+        // Kb^T rows for the state update, read now so their latency hides
+        // under R S and D
+        RowFrags<T, B::RB_K, NSC> kf[ST];
+#pragma unroll
+        for (int st = 0; st < ST; ++st) kf[st].load(lblk, 16 * st + n, g);
         F sb[NSK];
 #pragma unroll
         for (int s = 0; s < NSK; ++s) {
@@ -1695,6 +1715,10 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
         f32x4 Y[MT];
         rows_x_state(fr, sb, Y);
         lds_barrier();  // M: early slot consumed; state fragments in LDS
+        // next chunk's R rows (resident from M on; past the last chunk: a
+        // slot no load is filling, values unused), read before D is formed
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) fr[mt].load(eblk_of(cc + 1) + B::oR, 16 * mt + n, g);
         F dh[NSC], dl[NSC];
         make_d(din, Y, dh, dl);
 #pragma unroll
@@ -1705,13 +1729,6 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
         // hand D over: the counter is raised once this wave's D writes are done
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt 0
         if (lane == 0) __hip_atomic_store(xfl, cc - cb + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        RowFrags<T, B::RB_K, NSC> kf[ST];
-#pragma unroll
-        for (int st = 0; st < ST; ++st) kf[st].load(lblk, 16 * st + n, g);
-        // next chunk's R rows (past the last chunk: a slot no load is
-        // filling, values unused)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) fr[mt].load(eblk_of(cc + 1) + B::oR, 16 * mt + n, g);
         update_s(lblk, kf, dh);
         chunk_end();
       }
@@ -1721,22 +1738,32 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
 #pragma unroll
           for (int i = 0; i < 4; ++i) s_out[sbase + static_cast<size_t>(16 * st + 4 * g + i) * DV + col] = S[st][i];
       }
+      if (ce > cb) lds_barrier();  // F (see the output wave)
     } else {
+      // Chunk cc's P D and its output tile are finished at the start of
+      // chunk cc + 1 (before M), off the path from the state wave's D to the
+      // end-of-chunk barrier: O, the P fragments and D are carried across
+      // the barrier in registers (the late slot holding P is refilled after
+      // it), and the loader waves store the staged tile after M.
+      f32x4 O[MT];
+      TriFrags<T, C, NSC> pf[MT];
+      F dh[NSC], dl[NSC];
       for (int cc = cb; cc < ce; ++cc) {
         const unsigned char* eblk = eblk_of(cc);
         const unsigned char* lblk = lblk_of(cc);
-        const int t0 = tbeg + cc * cl, len = min(cl, L_seq - cc * cl);
+        if (cc > cb) {
+          add_pd(pf, dh, dl, O);
+          put_o(O, 0, 0);  // staged in LDS (split roles come with the staged output)
+        }
         RowFrags<T, B::RB_R, NSK> fr[MT];  // Qh rows: the early slot is refilled after M
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) fr[mt].load(eblk + B::oQ, 16 * mt + n, g);
-        TriFrags<T, C, NSC> pf[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) pf[mt].load(lblk + (B::oP - B::oK), mt, n, g);
         lds_barrier();  // M
         F sb[NSK];
 #pragma unroll
         for (int s = 0; s < NSK; ++s) sb[s] = sxp[64 * s];
-        f32x4 O[MT];
         rows_x_state(fr, sb, O);
         // wait for the state wave's D of this chunk (bounded: the state wave
         // raises the counter without waiting on this wave)
@@ -1745,15 +1772,17 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
           __builtin_amdgcn_s_sleep(1);
         }
         asm volatile("" ::: "memory");
-        F dh[NSC], dl[NSC];
 #pragma unroll
         for (int s = 0; s < NSC; ++s) {
           dh[s] = dxp[64 * s];
           if (SP::has_lo) dl[s] = dxp[64 * (NSC + s)];
         }
-        add_pd(pf, dh, dl, O);
-        put_o(O, t0, len);
         chunk_end();
+      }
+      if (ce > cb) {
+        add_pd(pf, dh, dl, O);
+        put_o(O, 0, 0);
+        lds_barrier();  // F: the last output tile staged for the loader waves
       }
     }
   } else {
