@@ -1116,35 +1116,56 @@ __global__ __launch_bounds__(256) void bwd_grad_k_kernel(const T* __restrict__ q
   const ChunkLoc cl = locate(cu, chunk_off, N, j);
   const float* bk = blk + (static_cast<size_t>(j) * H + h) * B::floats;
   const int tid = threadIdx.x;
-  for (int e = tid; e < BC * BC / 4; e += 256) {
-    const int row = e >> 4, c4 = (e & 15) * 4;
-    const f32x4 a = *reinterpret_cast<const f32x4*>(bk + B::odP + row * BC + c4);
-    const f32x4 b = *reinterpret_cast<const f32x4*>(bk + B::odA + row * BC + c4);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dPl[row * LPC + c4 + i] = a[i], dAl[row * LPC + c4 + i] = b[i];
-  }
-  if (tid < BC) rsum[tid] = 0.f;
   const int row = tid >> 2, c8 = (tid & 3) * CPT;
   const int I = row >> 4;
+  // Every global input of a slice is issued before the first is used, so
+  // their latencies overlap: the slice's q, k, gates and the dQg, dKg, dKb
+  // cotangents (read at the end), then (first slice) dP and dA into LDS.
+  // Rows past the sequence read its last row and are zeroed at the use.
+  constexpr int RPS = BC * SW / 256;  // rows per thread of the gate load
+  const int gch = tid % SW, gseg = tid / SW;
+  const int rowc = min(row, cl.len - 1);
+  float xq[CPT], xk[CPT], xg[RPS], dQg[CPT], dKg[CPT], dKb[CPT];
+  auto issue = [&](int c0) {
+    const size_t o = (static_cast<size_t>(cl.t0 + rowc) * H + h) * DK + c0 + c8;
+    loadn<CPT>(q + o, xq);
+    loadn<CPT>(k + o, xk);
+#pragma unroll
+    for (int i = 0; i < RPS; ++i)
+      xg[i] = gate_at<G, DK>(la, static_cast<size_t>(cl.t0 + min(gseg * RPS + i, cl.len - 1)), H, h, c0 + gch);
+    const size_t ob = static_cast<size_t>(row) * DK + c0 + c8;
+    loadn<CPT>(bk + B::odQg + ob, dQg);
+    loadn<CPT>(bk + B::odKg + ob, dKg);
+    loadn<CPT>(bk + B::odKb + ob, dKb);
+  };
+  issue(zs * NSW * SW);
+  {
+    f32x4 a[BC * BC / 4 / 256], b[BC * BC / 4 / 256];
+#pragma unroll
+    for (int u = 0; u < BC * BC / 4 / 256; ++u) {
+      const int e = tid + 256 * u, rr = e >> 4, c4 = (e & 15) * 4;
+      a[u] = *reinterpret_cast<const f32x4*>(bk + B::odP + rr * BC + c4);
+      b[u] = *reinterpret_cast<const f32x4*>(bk + B::odA + rr * BC + c4);
+    }
+#pragma unroll
+    for (int u = 0; u < BC * BC / 4 / 256; ++u) {
+      const int e = tid + 256 * u, rr = e >> 4, c4 = (e & 15) * 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dPl[rr * LPC + c4 + i] = a[u][i], dAl[rr * LPC + c4 + i] = b[u][i];
+    }
+  }
+  if (tid < BC) rsum[tid] = 0.f;
   for (int si = 0; si < NSW; ++si) {
     const int c0 = (zs * NSW + si) * SW;
+    if (si > 0) issue(c0);
     {
-      float xq[CPT], xk[CPT];
+      const bool live = row < cl.len;
 #pragma unroll
-      for (int i = 0; i < CPT; ++i) xq[i] = xk[i] = 0.f;
-      if (row < cl.len) {
-        const size_t o = (static_cast<size_t>(cl.t0 + row) * H + h) * DK + c0 + c8;
-        loadn<CPT>(q + o, xq);
-        loadn<CPT>(k + o, xk);
-      }
-#pragma unroll
-      for (int i = 0; i < CPT; ++i) qs[row * PS + c8 + i] = xq[i], ks[row * PS + c8 + i] = xk[i];
-      constexpr int RPS = BC * SW / 256;  // rows per thread of the gate load
-      const int ch = tid % SW, seg = tid / SW;
+      for (int i = 0; i < CPT; ++i) qs[row * PS + c8 + i] = live ? xq[i] : 0.f, ks[row * PS + c8 + i] = live ? xk[i] : 0.f;
 #pragma unroll
       for (int i = 0; i < RPS; ++i) {
-        const int rr = seg * RPS + i;
-        gs[rr * PS + ch] = rr < cl.len ? gate_at<G, DK>(la, static_cast<size_t>(cl.t0 + rr), H, h, c0 + ch) : 0.f;
+        const int rr = gseg * RPS + i;
+        gs[rr * PS + gch] = rr < cl.len ? xg[i] : 0.f;
       }
     }
     lds_sync();
@@ -1218,13 +1239,7 @@ __global__ __launch_bounds__(256) void bwd_grad_k_kernel(const T* __restrict__ q
         G2[i] += (dp * qs[rr * PS + c8 + i] + da * ks[rr * PS + c8 + i]) * __expf(gs[rr * PS + c8 + i] - Gr[i]);
     }
     // elementwise
-    float dQg[CPT], dKg[CPT], dKb[CPT], dqv[CPT], dkv[CPT], dG[CPT], cs[CPT];
-    {
-      const size_t o = static_cast<size_t>(row) * DK + c0 + c8;
-      loadn<CPT>(bk + B::odQg + o, dQg);
-      loadn<CPT>(bk + B::odKg + o, dKg);
-      loadn<CPT>(bk + B::odKb + o, dKb);
-    }
+    float dqv[CPT], dkv[CPT], dG[CPT], cs[CPT];
     // The pair s = r enters P with factor 1 and its contributions to dG
     // (q_r dP_rr k_r - k_r dP_rr q_r) cancel exactly, as do the last token's
     // own dKb Kb terms (its factor e^{G_C - G_r} is 1; in a partial chunk the
