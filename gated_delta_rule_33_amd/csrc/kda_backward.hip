@@ -498,29 +498,32 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, 
 
 // ---------------------------------------------------------------------------
 // state: the chunk-entry states.  One workgroup (4 waves) per (sequence,
-// head, 16 value columns), walking the sequence's chunks in order; the
-// state (DK x 16) is held in MFMA accumulators, wave w owning key-channel
-// rows [16 TPW w, 16 TPW (w + 1)).  Per chunk:
+// head, 32 value columns), walking the sequence's chunks in order; the
+// state (DK x 32) is held in MFMA accumulators, wave w owning key-channel
+// rows [16 TPW w, 16 TPW (w + 1)) of both 16-column halves.  Per chunk:
 //   W = Diag(beta)(V - Kg S)   (wave w: rows 16 w .. 16 w + 15)
 //   U = T W
 //   S = Diag(gamma) S + Kb^T U
 // as split-bf16 products: the block factors are read as ready-split
-// fragments; S, W and U are split once, when they are handed over through
-// LDS (transposed, so that a B fragment is eight consecutive k of one
-// column).  Each wave reads the next chunk's W and U operands one chunk
-// ahead, and its Kb^T fragments at the start of the chunk that uses them.
-// Workgroup x: the value slices of a (sequence, head) share an XCD (x % 8),
-// so the slices read each block through one L2.
+// fragments, shared by the two halves; S, W and U are split once, when they
+// are handed over through LDS (transposed, so that a B fragment is eight
+// consecutive k of one column).  Every operand of chunk c + 1 is read into
+// registers during chunk c, a third in each phase (one workgroup per CU,
+// one wave per SIMD, so each wave has the whole register file for it).  Workgroup x: the value
+// slices of a (sequence, head) share an XCD (x % 8), so they read each
+// block through one L2.
 // ---------------------------------------------------------------------------
-// A split-bf16 [16][K] hand-over tile in LDS (16 columns of a 16-column
-// slice, k contiguous): hi plane then lo plane, pitch K + 8 elements.
-template <int K>
-struct Tile16 {
+constexpr int SCOLS = 32;  // value columns per state-pass workgroup
+
+// A split-bf16 [NC][K] hand-over tile in LDS (NC columns, k contiguous): hi
+// plane then lo plane, pitch K + 8 elements.
+template <int K, int NC = SCOLS>
+struct HTile {
   static constexpr int P = K + 8;
-  static constexpr int elems = 2 * 16 * P;
+  static constexpr int elems = 2 * NC * P;
   __bf16* b;
   __device__ __forceinline__ F3 frag(int n, int k0) const {
-    return F3{*reinterpret_cast<const bf16x8*>(b + n * P + k0), *reinterpret_cast<const bf16x8*>(b + 16 * P + n * P + k0)};
+    return F3{*reinterpret_cast<const bf16x8*>(b + n * P + k0), *reinterpret_cast<const bf16x8*>(b + NC * P + n * P + k0)};
   }
   // four consecutive k of column n (8-byte aligned)
   __device__ __forceinline__ void put4(int n, int k, f32x4 x) const {
@@ -531,12 +534,12 @@ struct Tile16 {
       lo[i] = static_cast<__bf16>(x[i] - static_cast<float>(hi[i]));
     }
     *reinterpret_cast<bf16x4*>(b + n * P + k) = hi;
-    *reinterpret_cast<bf16x4*>(b + 16 * P + n * P + k) = lo;
+    *reinterpret_cast<bf16x4*>(b + NC * P + n * P + k) = lo;
   }
   __device__ __forceinline__ void put(int n, int k, float x) const {
     const __bf16 hi = static_cast<__bf16>(x);
     b[n * P + k] = hi;
-    b[16 * P + n * P + k] = static_cast<__bf16>(x - static_cast<float>(hi));
+    b[NC * P + n * P + k] = static_cast<__bf16>(x - static_cast<float>(hi));
   }
 };
 
@@ -551,6 +554,29 @@ __device__ __forceinline__ void settle(f32x4 (&x)[N]) {
   for (int t = 0; t < N; ++t) asm volatile("" : "+v"(x[t]));
 }
 
+// Eight consecutive io elements kept as loaded until they are used.
+template <typename T>
+struct raw8;
+template <>
+struct raw8<float> {
+  struct type {
+    f32x4 a, b;
+  };
+  __device__ __forceinline__ static type load(const float* p) {
+    return type{*reinterpret_cast<const f32x4*>(p), *reinterpret_cast<const f32x4*>(p + 4)};
+  }
+  __device__ __forceinline__ static float get(const type& x, int i) { return i < 4 ? x.a[i] : x.b[i - 4]; }
+};
+template <>
+struct raw8<bf16_t> {
+  typedef uint4 type;
+  __device__ __forceinline__ static type load(const bf16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ static float get(const type& x, int i) {
+    const uint32_t w = i < 2 ? x.x : (i < 4 ? x.y : (i < 6 ? x.z : x.w));
+    return __uint_as_float((i & 1) ? (w & 0xFFFF0000u) : (w << 16));
+  }
+};
+
 template <typename T, int DK, int DV>
 __device__ __forceinline__ void bwd_state_body(int x, const T* __restrict__ v, const int32_t* __restrict__ cu,
                                                const int32_t* __restrict__ chunk_off,
@@ -558,47 +584,63 @@ __device__ __forceinline__ void bwd_state_body(int x, const T* __restrict__ v, c
                                                const float* __restrict__ blk, const float* __restrict__ S0,
                                                float* __restrict__ sc) {
   typedef BwdBlk<DK> B;
-  constexpr int NSP = DV / 16, NKB = DK / 16, TPW = NKB / 4, NKS = DK / 32;
-  __shared__ __align__(16) __bf16 lds_s[Tile16<DK>::elems + 2 * Tile16<BC>::elems];
-  const Tile16<DK> XT{lds_s};
-  const Tile16<BC> WT{lds_s + Tile16<DK>::elems}, UT{lds_s + Tile16<DK>::elems + Tile16<BC>::elems};
+  constexpr int NSP = DV / SCOLS, NKB = DK / 16, TPW = NKB / 4, NKS = DK / 32;
+  __shared__ __align__(16) __bf16 lds_s[HTile<DK>::elems + 2 * HTile<BC>::elems];
+  const HTile<DK> XT{lds_s};
+  const HTile<BC> WT{lds_s + HTile<DK>::elems}, UT{lds_s + HTile<DK>::elems + HTile<BC>::elems};
   const int xcd = x & 7, s8 = x >> 3, sp = s8 % NSP, p = (s8 / NSP) * 8 + xcd;
   if (p >= N * H) return;
   const int n = order[p / H], h = p % H;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
   const int tb = cu[n], L = cu[n + 1] - tb, nch = (L + BC - 1) / BC, j0 = chunk_off[n];
-  const int col = sp * 16 + r;
+  const int col0 = sp * SCOLS + r;  // column of half hf: col0 + 16 hf
   const size_t sbase = (static_cast<size_t>(n) * H + h) * DK * DV;
   const int kT1 = w >= 2 ? 1 : 0;  // k steps of T's row tile w: rows <= 16 w + 15
-  f32x4 X[TPW];
+  f32x4 X[TPW][2];
 #pragma unroll
   for (int t = 0; t < TPW; ++t)
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int row = 16 * (w * TPW + t) + 4 * g + m;
-      X[t][m] = S0 ? S0[sbase + static_cast<size_t>(row) * DV + col] : 0.f;
-    }
-  settle(X);
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int row = 16 * (w * TPW + t) + 4 * g + m;
+        X[t][hf][m] = S0 ? S0[sbase + static_cast<size_t>(row) * DV + col0 + 16 * hf] : 0.f;
+      }
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) settle(X[t]);
   struct Ops {
-    F3 kg[NKS];
-    F3 tt[2];
-    typename raw1<T>::type vv[4];
+    F3 kg[NKS], tt[2], kbt[TPW][2];
+    typename raw1<T>::type vv[2][4];
     float bet[4], gam[TPW][4];
   };
-  auto load = [&](int c, Ops& o) {
+  // A chunk's operands in three parts (the parts of chunk c + 1 are issued
+  // in the three phases of chunk c, so the memory pipe drains while the
+  // wave computes instead of holding it at the chunk's start)
+  auto load_a = [&](int c, Ops& o) {
     const float* bk = blk + (static_cast<size_t>(j0 + c) * H + h) * B::floats;
-    const int row = 16 * w + r;
 #pragma unroll
-    for (int kk = 0; kk < NKS; ++kk) o.kg[kk] = pfrag(bk + B::oKg, DK, row, 32 * kk + 8 * g);
+    for (int kk = 0; kk < NKS; ++kk) o.kg[kk] = pfrag(bk + B::oKg, DK, 16 * w + r, 32 * kk + 8 * g);
+  };
+  auto load_c = [&](int c, Ops& o) {
+    const float* bk = blk + (static_cast<size_t>(j0 + c) * H + h) * B::floats;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) o.tt[kk] = pfrag(bk + B::oT, BC, row, 32 * kk + 8 * g);
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) o.kbt[t][kk] = pfrag(bk + B::oKbT, BC, 16 * (w * TPW + t) + r, 32 * kk + 8 * g);
+  };
+  auto load_b = [&](int c, Ops& o) {
+    const float* bk = blk + (static_cast<size_t>(j0 + c) * H + h) * B::floats;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) o.tt[kk] = pfrag(bk + B::oT, BC, 16 * w + r, 32 * kk + 8 * g);
     const int t0 = tb + c * BC, len = min(BC, L - c * BC);
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       // rows past the sequence read its last row: their beta is 0, so W is 0
       // there whatever v holds (no branch, no wait on the load here)
       const int rr = 16 * w + 4 * g + m, rc = min(rr, len - 1);
-      o.vv[m] = raw1<T>::load(v + (static_cast<size_t>(t0 + rc) * H + h) * DV + col);
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+        o.vv[hf][m] = raw1<T>::load(v + (static_cast<size_t>(t0 + rc) * H + h) * DV + col0 + 16 * hf);
       o.bet[m] = bk[B::oBeta + rr];
     }
 #pragma unroll
@@ -607,48 +649,56 @@ __device__ __forceinline__ void bwd_state_body(int x, const T* __restrict__ v, c
       for (int m = 0; m < 4; ++m) o.gam[t][m] = bk[B::oGam + 16 * (w * TPW + t) + 4 * g + m];
   };
   Ops cur, nxt;
-  if (nch > 0) load(0, cur);
+  if (nch > 0) {
+    load_a(0, cur);
+    load_b(0, cur);
+    load_c(0, cur);
+  }
   for (int c = 0; c < nch; ++c) {
-    F3 kbt[TPW][2];  // Kb^T rows of the wave's channels, for the last phase
-    {
-      const float* bk = blk + (static_cast<size_t>(j0 + c) * H + h) * B::floats;
-#pragma unroll
-      for (int t = 0; t < TPW; ++t)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) kbt[t][kk] = pfrag(bk + B::oKbT, BC, 16 * (w * TPW + t) + r, 32 * kk + 8 * g);
-    }
-    // next chunk's operands before the state stores: the memory counter is in
-    // order, so waiting for these loads does not also wait for the stores
-    if (c + 1 < nch) load(c + 1, nxt);
+    const bool more = c + 1 < nch;
     float* so = sc + (static_cast<size_t>(j0 + c) * H + h) * DK * DV;
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-      XT.put4(r, 16 * (w * TPW + t) + 4 * g, X[t]);
+    for (int t = 0; t < TPW; ++t)
 #pragma unroll
-      for (int m = 0; m < 4; ++m) so[static_cast<size_t>(16 * (w * TPW + t) + 4 * g + m) * DV + col] = X[t][m];
+      for (int hf = 0; hf < 2; ++hf) {
+        XT.put4(16 * hf + r, 16 * (w * TPW + t) + 4 * g, X[t][hf]);
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          so[static_cast<size_t>(16 * (w * TPW + t) + 4 * g + m) * DV + col0 + 16 * hf] = X[t][hf][m];
+      }
+    lds_sync();
+    if (more) load_a(c + 1, nxt);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int kk = 0; kk < NKS; ++kk) acc = mm3(cur.kg[kk], XT.frag(16 * hf + r, 32 * kk + 8 * g), acc);
+      f32x4 wv;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) wv[m] = cur.bet[m] * (raw1<T>::cvt(cur.vv[hf][m]) - acc[m]);
+      WT.put4(16 * hf + r, 16 * w + 4 * g, wv);
     }
     lds_sync();
-    f32x4 acc = zero4();
+    if (more) load_b(c + 1, nxt);
 #pragma unroll
-    for (int kk = 0; kk < NKS; ++kk) acc = mm3(cur.kg[kk], XT.frag(r, 32 * kk + 8 * g), acc);
-    f32x4 wv;
+    for (int hf = 0; hf < 2; ++hf) {
+      f32x4 acc = zero4();
 #pragma unroll
-    for (int m = 0; m < 4; ++m) wv[m] = cur.bet[m] * (raw1<T>::cvt(cur.vv[m]) - acc[m]);
-    WT.put4(r, 16 * w + 4 * g, wv);
-    lds_sync();
-    acc = zero4();
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-      if (kk <= kT1) acc = mm3(cur.tt[kk], WT.frag(r, 32 * kk + 8 * g), acc);
-    UT.put4(r, 16 * w + 4 * g, acc);
-    lds_sync();
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-#pragma unroll
-      for (int m = 0; m < 4; ++m) X[t][m] *= cur.gam[t][m];
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) X[t] = mm3(kbt[t][kk], UT.frag(r, 32 * kk + 8 * g), X[t]);
+      for (int kk = 0; kk < 2; ++kk)
+        if (kk <= kT1) acc = mm3(cur.tt[kk], WT.frag(16 * hf + r, 32 * kk + 8 * g), acc);
+      UT.put4(16 * hf + r, 16 * w + 4 * g, acc);
     }
+    lds_sync();
+    if (more) load_c(c + 1, nxt);
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) X[t][hf][m] *= cur.gam[t][m];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) X[t][hf] = mm3(cur.kbt[t][kk], UT.frag(16 * hf + r, 32 * kk + 8 * g), X[t][hf]);
+      }
     cur = nxt;
   }
 }
@@ -659,9 +709,8 @@ __device__ __forceinline__ void bwd_state_body(int x, const T* __restrict__ v, c
 // the chunk's final state on entry, of its entry state on exit):
 //   Z = P^T dO + Kb X,  Y = T^T Z,  X = Diag(gamma) X + Qg^T dO - Kg^T Diag(beta) Y
 // as split-bf16 products (dO, Z and -beta Y handed over through LDS,
-// transposed).  P^T and T^T rows are read a chunk ahead; Kb at the start of
-// the chunk, Qg^T and Kg^T after its first phase (register budget of two
-// workgroups per CU).
+// transposed); every operand of chunk c - 1 is read during chunk c, a third
+// in each phase.
 // ---------------------------------------------------------------------------
 template <typename T, int DK, int DV>
 __device__ __forceinline__ void bwd_dstate_body(int x, const T* __restrict__ dO, const int32_t* __restrict__ cu,
@@ -670,47 +719,64 @@ __device__ __forceinline__ void bwd_dstate_body(int x, const T* __restrict__ dO,
                                                 const float* __restrict__ blk, const float* __restrict__ dST,
                                                 float* __restrict__ dsc, float* __restrict__ dS0) {
   typedef BwdBlk<DK> B;
-  constexpr int NSP = DV / 16, NKB = DK / 16, TPW = NKB / 4, NKS = DK / 32;
-  __shared__ __align__(16) __bf16 lds_d[Tile16<DK>::elems + 3 * Tile16<BC>::elems];
-  const Tile16<DK> XT{lds_d};
-  const Tile16<BC> DT{lds_d + Tile16<DK>::elems}, ZT{lds_d + Tile16<DK>::elems + Tile16<BC>::elems},
-      YT{lds_d + Tile16<DK>::elems + 2 * Tile16<BC>::elems};
+  constexpr int NSP = DV / SCOLS, NKB = DK / 16, TPW = NKB / 4, NKS = DK / 32;
+  __shared__ __align__(16) __bf16 lds_d[HTile<DK>::elems + 3 * HTile<BC>::elems];
+  const HTile<DK> XT{lds_d};
+  const HTile<BC> DT{lds_d + HTile<DK>::elems}, ZT{lds_d + HTile<DK>::elems + HTile<BC>::elems},
+      YT{lds_d + HTile<DK>::elems + 2 * HTile<BC>::elems};
   const int xcd = x & 7, s8 = x >> 3, sp = s8 % NSP, p = (s8 / NSP) * 8 + xcd;
   if (p >= N * H) return;
   const int n = order[p / H], h = p % H;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
   const int tb = cu[n], L = cu[n + 1] - tb, nch = (L + BC - 1) / BC, j0 = chunk_off[n];
-  const int col = sp * 16 + r;
+  const int col0 = sp * SCOLS + r;
   const size_t sbase = (static_cast<size_t>(n) * H + h) * DK * DV;
   const int kU0 = w >= 2 ? 1 : 0;  // k steps of P^T, T^T row tile w: rows >= 16 w
-  f32x4 X[TPW];
+  f32x4 X[TPW][2];
 #pragma unroll
   for (int t = 0; t < TPW; ++t)
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int row = 16 * (w * TPW + t) + 4 * g + m;
-      X[t][m] = dST ? dST[sbase + static_cast<size_t>(row) * DV + col] : 0.f;
-    }
-  settle(X);
-  typedef typename raw4<T>::type R4;
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int row = 16 * (w * TPW + t) + 4 * g + m;
+        X[t][hf][m] = dST ? dST[sbase + static_cast<size_t>(row) * DV + col0 + 16 * hf] : 0.f;
+      }
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) settle(X[t]);
   struct Ops {
-    F3 pt[2], tt[2];
-    R4 dov;
+    F3 pt[2], tt[2], kb[NKS], qgt[TPW][2], kgt[TPW][2];
+    typename raw8<T>::type dov;
     float bet[4], gam[TPW][4];
   };
-  const int drow = tid >> 2, dc4 = (tid & 3) * 4;  // this thread's 4 dO values for the hand-over tile
-  auto load = [&](int c, Ops& o) {
+  const int drow = tid >> 2, dc8 = (tid & 3) * 8;  // this thread's 8 dO values for the hand-over tile
+  // a chunk's operands in three parts, issued in the three phases of the
+  // chunk before (see bwd_state_body)
+  auto load_a = [&](int c, Ops& o) {
     const float* bk = blk + (static_cast<size_t>(j0 + c) * H + h) * B::floats;
-    const int row = 16 * w + r;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      o.pt[kk] = pfrag(bk + B::oPT, BC, row, 32 * kk + 8 * g);
-      o.tt[kk] = pfrag(bk + B::oTT, BC, row, 32 * kk + 8 * g);
-    }
+    for (int kk = 0; kk < 2; ++kk) o.pt[kk] = pfrag(bk + B::oPT, BC, 16 * w + r, 32 * kk + 8 * g);
+#pragma unroll
+    for (int kk = 0; kk < NKS; ++kk) o.kb[kk] = pfrag(bk + B::oKb, DK, 16 * w + r, 32 * kk + 8 * g);
+  };
+  auto load_c = [&](int c, Ops& o) {
+    const float* bk = blk + (static_cast<size_t>(j0 + c) * H + h) * B::floats;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        o.qgt[t][kk] = pfrag(bk + B::oQgT, BC, 16 * (w * TPW + t) + r, 32 * kk + 8 * g);
+        o.kgt[t][kk] = pfrag(bk + B::oKgT, BC, 16 * (w * TPW + t) + r, 32 * kk + 8 * g);
+      }
+  };
+  auto load_b = [&](int c, Ops& o) {
+    const float* bk = blk + (static_cast<size_t>(j0 + c) * H + h) * B::floats;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) o.tt[kk] = pfrag(bk + B::oTT, BC, 16 * w + r, 32 * kk + 8 * g);
     const int t0 = tb + c * BC, len = min(BC, L - c * BC);
     // rows past the sequence read the last row: P and Qg are zero in those
     // rows, so their dO never contributes (no branch, no wait on the load here)
-    o.dov = load4raw(dO + (static_cast<size_t>(t0 + min(drow, len - 1)) * H + h) * DV + sp * 16 + dc4);
+    o.dov = raw8<T>::load(dO + (static_cast<size_t>(t0 + min(drow, len - 1)) * H + h) * DV + sp * SCOLS + dc8);
 #pragma unroll
     for (int m = 0; m < 4; ++m) o.bet[m] = bk[B::oBeta + 16 * w + 4 * g + m];
 #pragma unroll
@@ -719,74 +785,80 @@ __device__ __forceinline__ void bwd_dstate_body(int x, const T* __restrict__ dO,
       for (int m = 0; m < 4; ++m) o.gam[t][m] = bk[B::oGam + 16 * (w * TPW + t) + 4 * g + m];
   };
   Ops cur, nxt;
-  if (nch > 0) load(nch - 1, cur);
+  if (nch > 0) {
+    load_a(nch - 1, cur);
+    load_b(nch - 1, cur);
+    load_c(nch - 1, cur);
+  }
   for (int c = nch - 1; c >= 0; --c) {
-    const float* bkc = blk + (static_cast<size_t>(j0 + c) * H + h) * B::floats;
-    F3 kb[NKS];
-#pragma unroll
-    for (int kk = 0; kk < NKS; ++kk) kb[kk] = pfrag(bkc + B::oKb, DK, 16 * w + r, 32 * kk + 8 * g);
-    if (c > 0) load(c - 1, nxt);  // before the state stores (see bwd_state_body)
+    const bool more = c > 0;
     float* so = dsc + (static_cast<size_t>(j0 + c) * H + h) * DK * DV;
     lds_sync();  // the previous chunk's readers of DT and YT are done
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-      XT.put4(r, 16 * (w * TPW + t) + 4 * g, X[t]);
+    for (int t = 0; t < TPW; ++t)
 #pragma unroll
-      for (int m = 0; m < 4; ++m) so[static_cast<size_t>(16 * (w * TPW + t) + 4 * g + m) * DV + col] = X[t][m];
-    }
-    {
-      const f32x4 d = cvt4(cur.dov);
+      for (int hf = 0; hf < 2; ++hf) {
+        XT.put4(16 * hf + r, 16 * (w * TPW + t) + 4 * g, X[t][hf]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) DT.put(dc4 + i, drow, d[i]);
+        for (int m = 0; m < 4; ++m)
+          so[static_cast<size_t>(16 * (w * TPW + t) + 4 * g + m) * DV + col0 + 16 * hf] = X[t][hf][m];
+      }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) DT.put(dc8 + i, drow, raw8<T>::get(cur.dov, i));
+    lds_sync();
+    if (more) load_a(c - 1, nxt);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+        if (kk >= kU0) acc = mm3(cur.pt[kk], DT.frag(16 * hf + r, 32 * kk + 8 * g), acc);
+#pragma unroll
+      for (int kk = 0; kk < NKS; ++kk) acc = mm3(cur.kb[kk], XT.frag(16 * hf + r, 32 * kk + 8 * g), acc);
+      ZT.put4(16 * hf + r, 16 * w + 4 * g, acc);
     }
     lds_sync();
-    f32x4 acc = zero4();
+    if (more) load_b(c - 1, nxt);
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-      if (kk >= kU0) acc = mm3(cur.pt[kk], DT.frag(r, 32 * kk + 8 * g), acc);
+    for (int hf = 0; hf < 2; ++hf) {
+      f32x4 acc = zero4();
 #pragma unroll
-    for (int kk = 0; kk < NKS; ++kk) acc = mm3(kb[kk], XT.frag(r, 32 * kk + 8 * g), acc);
-    ZT.put4(r, 16 * w + 4 * g, acc);
-    F3 qgt[TPW][2], kgt[TPW][2];
+      for (int kk = 0; kk < 2; ++kk)
+        if (kk >= kU0) acc = mm3(cur.tt[kk], ZT.frag(16 * hf + r, 32 * kk + 8 * g), acc);
+      f32x4 yb;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) yb[m] = -cur.bet[m] * acc[m];
+      YT.put4(16 * hf + r, 16 * w + 4 * g, yb);
+    }
+    lds_sync();
+    if (more) load_c(c - 1, nxt);
 #pragma unroll
     for (int t = 0; t < TPW; ++t)
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        qgt[t][kk] = pfrag(bkc + B::oQgT, BC, 16 * (w * TPW + t) + r, 32 * kk + 8 * g);
-        kgt[t][kk] = pfrag(bkc + B::oKgT, BC, 16 * (w * TPW + t) + r, 32 * kk + 8 * g);
+      for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) X[t][hf][m] *= cur.gam[t][m];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          X[t][hf] = mm3(cur.qgt[t][kk], DT.frag(16 * hf + r, 32 * kk + 8 * g), X[t][hf]);
+          X[t][hf] = mm3(cur.kgt[t][kk], YT.frag(16 * hf + r, 32 * kk + 8 * g), X[t][hf]);
+        }
       }
-    lds_sync();
-    acc = zero4();
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-      if (kk >= kU0) acc = mm3(cur.tt[kk], ZT.frag(r, 32 * kk + 8 * g), acc);
-    f32x4 yb;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) yb[m] = -cur.bet[m] * acc[m];
-    YT.put4(r, 16 * w + 4 * g, yb);
-    lds_sync();
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-#pragma unroll
-      for (int m = 0; m < 4; ++m) X[t][m] *= cur.gam[t][m];
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        X[t] = mm3(qgt[t][kk], DT.frag(r, 32 * kk + 8 * g), X[t]);
-        X[t] = mm3(kgt[t][kk], YT.frag(r, 32 * kk + 8 * g), X[t]);
-      }
-    }
     cur = nxt;
   }
   if (dS0) {
 #pragma unroll
     for (int t = 0; t < TPW; ++t)
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int row = 16 * (w * TPW + t) + 4 * g + m;
-        dS0[sbase + static_cast<size_t>(row) * DV + col] = X[t][m];
-      }
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int row = 16 * (w * TPW + t) + 4 * g + m;
+          dS0[sbase + static_cast<size_t>(row) * DV + col0 + 16 * hf] = X[t][hf][m];
+        }
   }
 }
+
 
 // The two state passes in one launch: workgroups [0, half) run the forward
 // state pass, [half, 2 half) the reverse cotangent pass.  They share no data,
@@ -794,7 +866,7 @@ __device__ __forceinline__ void bwd_dstate_body(int x, const T* __restrict__ dO,
 // latency-bound chains interleave on every CU instead of running one after
 // the other.
 template <typename T, int DK, int DV>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_states_kernel(const T* __restrict__ v, const T* __restrict__ dO,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_states_kernel(const T* __restrict__ v, const T* __restrict__ dO,
                                                          const int32_t* __restrict__ cu,
                                                          const int32_t* __restrict__ chunk_off,
                                                          const int32_t* __restrict__ order, int N, int H,
@@ -1349,7 +1421,7 @@ static hipError_t launch_backward_t(const BackwardPlan& p, const void* q, const 
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const int64_t NH = static_cast<int64_t>(p.N) * p.H;
-  const unsigned seq_wgs = static_cast<unsigned>((NH + 7) / 8 * 8 * (DV / 16));
+  const unsigned seq_wgs = static_cast<unsigned>((NH + 7) / 8 * 8 * (DV / SCOLS));
   hipLaunchKernelGGL((bwd_states_kernel<T, DK, DV>), dim3(2 * seq_wgs), dim3(256), 0, st, tv, tdo, cu, chunk_off,
                      order, p.N, p.H, blk, S0, dS_T, sc, dsc, dS0, static_cast<int>(seq_wgs));
   if ((e = hipGetLastError()) != hipSuccess) return e;
