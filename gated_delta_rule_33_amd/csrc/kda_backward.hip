@@ -1001,12 +1001,54 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
   for (int u = 0; u < NT; ++u) acc[u] = zero4();
   float db1[4] = {0.f, 0.f, 0.f, 0.f}, dg = 0.f;
+  // The slice inputs land raw in LDS by direct global-to-LDS loads, all
+  // issued at once (no registers held, one memory latency per slice), in
+  // the area of the W, dU, U, dW, dV planes, which a slice writes only
+  // after its inputs are split: S0 and dS_C [DK][32] fp32, dO [BC][32] io,
+  // and v [BC][32] io at the end of the area (in the dV plane, written in
+  // the second phase, after v is read in the first).
+  constexpr int VROW = 32 * static_cast<int>(sizeof(T));  // bytes of a 32-column io row
+  constexpr int RAW_V = LL::bytes - (LL::oWT * 2) - BC * VROW;  // v's offset in the area
+  static_assert(2 * DK * 128 + BC * VROW <= RAW_V, "raw slice inputs fit the area");
+  unsigned char* const raw = reinterpret_cast<unsigned char*>(lds + LL::oWT);
+  const float* const rS0 = reinterpret_cast<const float*>(raw);
+  const float* const rdS = reinterpret_cast<const float*>(raw + DK * 128);
+  const T* const rdO = reinterpret_cast<const T*>(raw + 2 * DK * 128);
+  const T* const rv = reinterpret_cast<const T*>(raw + RAW_V);
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  auto dma = [&](const void* src, int dst_off) {  // one wave: 64 lanes x 16 bytes to raw + dst_off (wave-uniform)
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(raw + dst_off), 16, 0, 0);
+  };
   for (int sp = 0; sp < NSP; ++sp) {
+    {
+      // S0, dS_C: a wave load is 8 rows x 128 bytes
+#pragma unroll
+      for (int i = 0; i < DK / 32; ++i) {
+        const int r0 = 8 * (wu + 4 * i), row = r0 + (lane >> 3);
+        const size_t o = static_cast<size_t>(row) * DV + sp * 32 + (lane & 7) * 4;
+        dma(s0 + o, r0 * 128);
+        dma(dsC + o, DK * 128 + r0 * 128);
+      }
+      // dO, v: a wave load is 1024 / VROW rows; rows past the sequence read
+      // its last row (dO zeroed below; beta is 0 there)
+      constexpr int RPL = 1024 / VROW, LPR = VROW / 16, NL = BC / RPL;
+#pragma unroll
+      for (int i = 0; i < (NL + 3) / 4; ++i) {
+        const int li = min(wu + 4 * i, NL - 1);  // a wave past the last load repeats it (same bytes)
+        const int row = li * RPL + lane / LPR;
+        const size_t o = (static_cast<size_t>(cl.t0 + min(row, cl.len - 1)) * H + h) * DV + sp * 32 +
+                         (lane % LPR) * (16 / sizeof(T));
+        dma(dO + o, 2 * DK * 128 + li * 1024);
+        dma(v + o, RAW_V + li * 1024);
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0: this wave's loads are in LDS
+      lds_sync();
+    }
     // slice inputs, split once, both orientations
     for (int e = tid; e < DK * 8; e += 256) {
       const int row = e >> 3, c4 = (e & 7) * 4;
-      const f32x4 a = *reinterpret_cast<const f32x4*>(s0 + static_cast<size_t>(row) * DV + sp * 32 + c4);
-      const f32x4 b = *reinterpret_cast<const f32x4*>(dsC + static_cast<size_t>(row) * DV + sp * 32 + c4);
+      const f32x4 a = *reinterpret_cast<const f32x4*>(rS0 + row * 32 + c4);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(rdS + row * 32 + c4);
       S0p.put4(row, c4, a);
       dSp.put4(row, c4, b);
 #pragma unroll
@@ -1014,17 +1056,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
     for (int e = tid; e < BC * 8; e += 256) {
       const int row = e >> 3, c4 = (e & 7) * 4;
-      f32x4 y = zero4();
-      if (row < cl.len) y = load4(dO + (static_cast<size_t>(cl.t0 + row) * H + h) * DV + sp * 32 + c4);
+      const f32x4 y = row < cl.len ? load4(rdO + row * 32 + c4) : zero4();
       Dp.put4(row, c4, y);
 #pragma unroll
       for (int i = 0; i < 4; ++i) DT.put(c4 + i, row, y[i]);
     }
-    if (tid < DK) {  // dgamma straight from the slice in global memory (L2), fixed order
+    if (tid < DK) {  // dgamma's share of the slice, fixed order
 #pragma unroll 4
       for (int c = 0; c < 32; c += 4) {
-        const f32x4 a = *reinterpret_cast<const f32x4*>(s0 + static_cast<size_t>(tid) * DV + sp * 32 + c);
-        const f32x4 b = *reinterpret_cast<const f32x4*>(dsC + static_cast<size_t>(tid) * DV + sp * 32 + c);
+        const f32x4 a = *reinterpret_cast<const f32x4*>(rS0 + tid * 32 + c);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(rdS + tid * 32 + c);
         dg += a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
       }
     }
@@ -1046,9 +1087,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       f32x4 wv;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const int row = 16 * w + 4 * g + m;
-        // rows past the sequence read its last row: beta, dU and dW are 0 there
-        const float vv = io<T>::load(v + (static_cast<size_t>(cl.t0 + min(row, cl.len - 1)) * H + h) * DV + sp * 32 + n);
+        // rows past the sequence hold its last row: beta, dU and dW are 0 there
+        const float vv = io<T>::load(rv + (16 * w + 4 * g + m) * 32 + n);
         vt[nt][m] = vv - a[m];
         wv[m] = bet[m] * vt[nt][m];
       }
