@@ -1227,9 +1227,12 @@ __global__ __launch_bounds__(256) void bwd_grad_k_kernel(const T* __restrict__ q
   if (j >= chunk_off[N]) return;
   const ChunkLoc cl = locate(cu, chunk_off, N, j);
   const float* bk = blk + (static_cast<size_t>(j) * H + h) * B::floats;
-  const int tid = threadIdx.x;
-  const int row = tid >> 2, c8 = (tid & 3) * CPT;
-  const int I = row >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
+  // thread: row 16 w + l % 16 of 16-row block I = w, channels CPT (l / 16) .. + CPT - 1,
+  // the output layout of the transposed MFMA tiles below
+  static_assert(CPT == 4, "four channels per thread (the MFMA output rows)");
+  const int row = 16 * (tid >> 6) + ln, c8 = lg * CPT;
+  const int I = __builtin_amdgcn_readfirstlane(tid >> 6);  // = row / 16, the wave's block (uniform)
   // Every global input of a slice is issued before the first is used, so
   // their latencies overlap: the slice's q, k, gates and the dQg, dKg, dKb
   // cotangents (read at the end), then (first slice) dP and dA into LDS.
@@ -1302,21 +1305,26 @@ __global__ __launch_bounds__(256) void bwd_grad_k_kernel(const T* __restrict__ q
     float GQ[CPT], GA[CPT], G2[CPT], Gr[CPT];
 #pragma unroll
     for (int i = 0; i < CPT; ++i) GQ[i] = GA[i] = G2[i] = 0.f, Gr[i] = gs[row * PS + c8 + i];
-    // row side
+    // Off-diagonal block pairs on fp32 MFMA (exact fp32 products), each
+    // computed transposed, C^T = X^T D^T, so that output lane l holds row
+    // l % 16 and channels 4 (l / 16) .. + 3: this thread's.  Row side over
+    // the earlier blocks s < 16 I (operands scaled at row 16 I - 1), column
+    // side over the later rows r > 16 I + 15 (scaled at row 16 I + 15); the
+    // block index is the wave's, so the k loops are uniform.
     if (I > 0) {
       const int off = I == 1 ? 0 : (I == 2 ? 16 : 48);
-#pragma unroll 4
-      for (int s = 0; s < 16 * I; ++s) {
-        const float dp = dPl[row * LPC + s], da = dAl[row * LPC + s];
-        const float* kp = Ksc + (off + s) * PS + c8;
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) GQ[i] += dp * kp[i], GA[i] += da * kp[i];
+      f32x4 aq = zero4(), aa = zero4();
+      for (int ks = 0; ks < 4 * I; ++ks) {
+        const int s = 4 * ks + lg;
+        const float a = Ksc[(off + s) * PS + ln];
+        aq = mf(a, dPl[(16 * I + ln) * LPC + s], aq);
+        aa = mf(a, dAl[(16 * I + ln) * LPC + s], aa);
       }
 #pragma unroll
       for (int i = 0; i < CPT; ++i) {
         const float sc_ = __expf(Gr[i] - gs[(16 * I - 1) * PS + c8 + i]);
-        GQ[i] *= sc_;
-        GA[i] *= sc_;
+        GQ[i] = aq[i] * sc_;
+        GA[i] = aa[i] * sc_;
       }
     }
 #pragma unroll 2
@@ -1332,16 +1340,14 @@ __global__ __launch_bounds__(256) void bwd_grad_k_kernel(const T* __restrict__ q
     // column side (this thread's row is the column index s)
     if (I < 3) {
       const int off = I == 0 ? 0 : (I == 1 ? 48 : 80);
-#pragma unroll 4
-      for (int rr = 16 * I + 16; rr < BC; ++rr) {
-        const float dp = dPl[rr * LPC + row], da = dAl[rr * LPC + row];
-        const float* xq = Xq + (off + rr - 16 * I - 16) * PS + c8;
-        const float* xk = Xk + (off + rr - 16 * I - 16) * PS + c8;
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) G2[i] += dp * xq[i] + da * xk[i];
+      f32x4 a2 = zero4();
+      for (int ks = 0; ks < 12 - 4 * I; ++ks) {
+        const int rp = 4 * ks + lg, rr = 16 * I + 16 + rp;
+        a2 = mf(Xq[(off + rp) * PS + ln], dPl[rr * LPC + 16 * I + ln], a2);
+        a2 = mf(Xk[(off + rp) * PS + ln], dAl[rr * LPC + 16 * I + ln], a2);
       }
 #pragma unroll
-      for (int i = 0; i < CPT; ++i) G2[i] *= __expf(gs[(16 * I + 15) * PS + c8 + i] - Gr[i]);
+      for (int i = 0; i < CPT; ++i) G2[i] = a2[i] * __expf(gs[(16 * I + 15) * PS + c8 + i] - Gr[i]);
     }
 #pragma unroll 2
     for (int rr = row + 1; rr < 16 * I + 16; ++rr) {
@@ -1398,8 +1404,9 @@ __global__ __launch_bounds__(256) void bwd_grad_k_kernel(const T* __restrict__ q
         float x = 0.f;
 #pragma unroll
         for (int i = 0; i < CPT; ++i) x += qs[row * PS + c8 + i];
-        x = group_sum<4>(x);  // the row's four threads are one lane quad
-        if ((tid & 3) == 0) rsum[row] += x;
+        x += shfl_xor(x, 16);  // the row's four threads are lanes l % 16 + 16 j
+        x += shfl_xor(x, 32);
+        if (lg == 0) rsum[row] += x;
       }
     }
     lds_sync();
