@@ -155,3 +155,10 @@ def _run_backward(name, group=8):
 
 def test_backward_long131072_all_heads():
     _run_backward("long131072_bf16", group=16)
+
+
+def test_backward_varlen64_all_heads():
+    """64 sequences of ragged lengths (422,049 tokens), 32 heads, S0 given:
+    the backward over many sequences at once (partial last chunks, chunk
+    offsets, the longest-first order), every element of every gradient."""
+    _run_backward("varlen64_bf16", group=4)
