@@ -310,26 +310,46 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, 
     bk[B::oBeta + tid] = b;
   }
   f32x4 aD = zero4(), pD = zero4(), aO[2] = {zero4(), zero4()}, pO[2] = {zero4(), zero4()};
+  // A slice's q, k (raw, thread (row, 4 channels), two rows each) and gates
+  // (thread (channel, 8 rows)), read one slice ahead so the loads of slice
+  // sl + 1 are in flight while slice sl computes; rows past the sequence
+  // read its last row and are zeroed when written to LDS.
+  typedef typename raw4<T>::type R4;
+  struct SliceIn {
+    R4 q[2], k[2];
+    float gt[8];
+  };
+  const int gch = tid & 31, gseg = tid >> 5;
+  auto issue = [&](int sl, SliceIn& in) {
+    const int c0 = sl * 32;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int e = tid + 256 * u, row = min(e >> 3, cl.len - 1), c4 = (e & 7) * 4;
+      const size_t o = (static_cast<size_t>(cl.t0 + row) * H + h) * DK + c0 + c4;
+      in.q[u] = load4raw(q + o);
+      in.k[u] = load4raw(k + o);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      in.gt[i] = gate_at<G, DK>(la, static_cast<size_t>(cl.t0 + min(gseg * 8 + i, cl.len - 1)), H, h, c0 + gch);
+  };
+  SliceIn cur, nxt;
+  issue(0, cur);
   for (int sl = 0; sl < DK / 32; ++sl) {
     const int c0 = sl * 32;
-    for (int e = tid; e < BC * 8; e += 256) {
-      const int row = e >> 3, c4 = (e & 7) * 4;
-      f32x4 xq = zero4(), xk = zero4();
-      if (row < cl.len) {
-        const size_t o = (static_cast<size_t>(cl.t0 + row) * H + h) * DK + c0 + c4;
-        xq = load4(q + o);
-        xk = load4(k + o);
-      }
+    if (sl + 1 < DK / 32) issue(sl + 1, nxt);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) qs[row * PS + c4 + i] = xq[i], ks[row * PS + c4 + i] = xk[i];
+    for (int u = 0; u < 2; ++u) {
+      const int e = tid + 256 * u, row = e >> 3, c4 = (e & 7) * 4;
+      const bool live = row < cl.len;
+      const f32x4 xq = cvt4(cur.q[u]), xk = cvt4(cur.k[u]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qs[row * PS + c4 + i] = live ? xq[i] : 0.f, ks[row * PS + c4 + i] = live ? xk[i] : 0.f;
     }
-    {
-      const int ch = tid & 31, seg = tid >> 5;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int row = seg * 8 + i;
-        gs[row * PS + ch] = row < cl.len ? gate_at<G, DK>(la, static_cast<size_t>(cl.t0 + row), H, h, c0 + ch) : 0.f;
-      }
+    for (int i = 0; i < 8; ++i) {
+      const int row = gseg * 8 + i;
+      gs[row * PS + gch] = row < cl.len ? cur.gt[i] : 0.f;
     }
     lds_sync();
     row_scan<false, PS>(gs, tot);
@@ -401,6 +421,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, 
       }
     }
     lds_sync();
+    cur = nxt;
   }
   // A to the block (upper blocks zero), L = Diag(beta) A and T = 0 in LDS
   // (P stays in its accumulators until T is done; it then goes through Lm)
