@@ -575,6 +575,14 @@ __device__ __forceinline__ void settle(f32x4 (&x)[N]) {
   for (int t = 0; t < N; ++t) asm volatile("" : "+v"(x[t]));
 }
 
+// A per-lane index the compiler cannot see through: addresses derived from it
+// inside a loop are formed where they are used instead of being hoisted out
+// of the loop and held (or spilled) across it.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // Eight consecutive io elements kept as loaded until they are used.
 template <typename T>
 struct raw8;
@@ -911,7 +919,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // columns into its MFMA tiles: dP, dM = -dW U^T, dQg, dKg = -dv S0^T, dKb.
 // Each operand sits in LDS in the orientation whose fragments are eight
 // consecutive floats (the S0, dS_C and dO slices both ways, W, dU transposed,
-// U and dW by rows).  At the end dbeta and dv are written out, and dQg, dKg,
+// U and dW by rows); a slice's inputs are loaded while the previous slice
+// runs.  At the end dbeta and dv are written out, and dQg, dKg,
 // dKb, dP, dA = Diag(beta) dM, dgamma over the chunk's block (everything it
 // read from the block has been consumed by then).
 // ---------------------------------------------------------------------------
@@ -954,18 +963,20 @@ struct GradVLds {
   static constexpr int PK = DK + 8;   // pitch of [32][DK] planes (k = key channel)
   // element offsets of each plane's hi part; its lo part follows at + rows * pitch
   static constexpr int oS0 = 0;                          // [DK][PW]  S0 columns of the slice
-  static constexpr int oS0T = oS0 + 2 * DK * PW;         // [32][PK]
-  static constexpr int odS = oS0T + 2 * 32 * PK;         // [DK][PW]
-  static constexpr int odST = odS + 2 * DK * PW;         // [32][PK]
-  static constexpr int odO = odST + 2 * 32 * PK;         // [BC][PW]
-  static constexpr int odOT = odO + 2 * BC * PW;         // [32][PC]
-  static constexpr int oWT = odOT + 2 * 32 * PC;         // [32][PC]
+  static constexpr int odS = oS0 + 2 * DK * PW;          // [DK][PW]
+  static constexpr int odO = odS + 2 * DK * PW;          // [BC][PW]
+  static constexpr int oWT = odO + 2 * BC * PW;          // [32][PC]
   static constexpr int odUT = oWT + 2 * 32 * PC;         // [32][PC]
   static constexpr int oU = odUT + 2 * 32 * PC;          // [BC][PW]
   static constexpr int odW = oU + 2 * BC * PW;           // [BC][PW]
   static constexpr int odV = odW + 2 * BC * PW;          // [BC][PW]  dv = beta dW
   static constexpr int elems = odV + 2 * BC * PW;        // bf16 elements
-  static constexpr int bytes = elems * 2;
+  // the transposed slice inputs, an array of their own (it takes the next
+  // slice's raw inputs while the rest of the slice runs)
+  static constexpr int tS0 = 0;                          // [32][PK]
+  static constexpr int tdS = tS0 + 2 * 32 * PK;          // [32][PK]
+  static constexpr int tdO = tdS + 2 * 32 * PK;          // [32][PC]
+  static constexpr int telems = tdO + 2 * 32 * PC;
 };
 
 template <typename T, int DK, int DV>
@@ -980,11 +991,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr int NT = (NTILE + 3) / 4;
   constexpr int PW = LL::PW, PC = LL::PC, PK = LL::PK;
   __shared__ __align__(16) __bf16 lds[LL::elems];
+  __shared__ __align__(16) __bf16 ldsT[LL::telems];
   __shared__ float betl[BC], dbp[BC * 5];
+  __shared__ __align__(16) float Al[10 * 256];
   auto plane = [&](int off, int rows, int pitch) { return Plane{lds + off, lds + off + rows * pitch, pitch}; };
-  const Plane S0p = plane(LL::oS0, DK, PW), S0T = plane(LL::oS0T, 32, PK);
-  const Plane dSp = plane(LL::odS, DK, PW), dST = plane(LL::odST, 32, PK);
-  const Plane Dp = plane(LL::odO, BC, PW), DT = plane(LL::odOT, 32, PC);
+  auto tplane = [&](int off, int pitch) { return Plane{ldsT + off, ldsT + off + 32 * pitch, pitch}; };
+  const Plane S0p = plane(LL::oS0, DK, PW), S0T = tplane(LL::tS0, PK);
+  const Plane dSp = plane(LL::odS, DK, PW), dST = tplane(LL::tdS, PK);
+  const Plane Dp = plane(LL::odO, BC, PW), DT = tplane(LL::tdO, PC);
   const Plane WT = plane(LL::oWT, 32, PC), dUT = plane(LL::odUT, 32, PC);
   const Plane Up = plane(LL::oU, BC, PW), dWp = plane(LL::odW, BC, PW), dVp = plane(LL::odV, BC, PW);
   const int j = blockIdx.x, h = blockIdx.y;
@@ -1021,75 +1035,116 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   f32x4 acc[NT];
 #pragma unroll
   for (int u = 0; u < NT; ++u) acc[u] = zero4();
-  float db1[4] = {0.f, 0.f, 0.f, 0.f}, dg = 0.f;
-  // The slice inputs land raw in LDS by direct global-to-LDS loads, all
-  // issued at once (no registers held, one memory latency per slice), in
-  // the area of the W, dU, U, dW, dV planes, which a slice writes only
-  // after its inputs are split: S0 and dS_C [DK][32] fp32, dO [BC][32] io,
-  // and v [BC][32] io at the end of the area (in the dV plane, written in
-  // the second phase, after v is read in the first).
-  constexpr int VROW = 32 * static_cast<int>(sizeof(T));  // bytes of a 32-column io row
-  constexpr int RAW_V = LL::bytes - (LL::oWT * 2) - BC * VROW;  // v's offset in the area
-  static_assert(2 * DK * 128 + BC * VROW <= RAW_V, "raw slice inputs fit the area");
-  unsigned char* const raw = reinterpret_cast<unsigned char*>(lds + LL::oWT);
-  const float* const rS0 = reinterpret_cast<const float*>(raw);
-  const float* const rdS = reinterpret_cast<const float*>(raw + DK * 128);
-  const T* const rdO = reinterpret_cast<const T*>(raw + 2 * DK * 128);
-  const T* const rv = reinterpret_cast<const T*>(raw + RAW_V);
+  float db1[4] = {0.f, 0.f, 0.f, 0.f};
+  float dg[DK / 32];  // dgamma of rows (tid >> 3) + 32 i (every lane of a row's eight holds it)
+#pragma unroll
+  for (int i = 0; i < DK / 32; ++i) dg[i] = 0.f;
+  // The slice inputs (S0 and dS_C [DK][32] fp32, dO [BC][32] io) land raw in
+  // LDS by direct global-to-LDS loads, in the area of the transposed S0, dS_C
+  // and dO planes.  Those planes are read only in the first phase, so the
+  // loads of slice sp + 1 are issued right after it and arrive while slice sp
+  // finishes; the split of a slice writes the row planes from the raw inputs
+  // and then copies them into the transposed planes, over the raw inputs.
+  // The area is an LDS array of its own: the compiler then knows that the
+  // reads of the other planes do not wait for those loads.
+  unsigned char* const rawS0 = reinterpret_cast<unsigned char*>(ldsT + LL::tS0);
+  unsigned char* const rawdS = reinterpret_cast<unsigned char*>(ldsT + LL::tdS);
+  unsigned char* const rawdO = reinterpret_cast<unsigned char*>(ldsT + LL::tdO);
+  static_assert(DK * 128 <= 2 * 32 * PK * 2 && BC * 32 * static_cast<int>(sizeof(T)) <= 2 * 32 * PC * 2,
+                "raw slice inputs fit the transposed planes");
+  static_assert((LL::tdS * 2) % 16 == 0 && (LL::tdO * 2) % 16 == 0, "raw areas are 16-byte aligned");
   const int wu = __builtin_amdgcn_readfirstlane(w);
-  auto dma = [&](const void* src, int dst_off) {  // one wave: 64 lanes x 16 bytes to raw + dst_off (wave-uniform)
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(raw + dst_off), 16, 0, 0);
+  auto dma = [&](const void* src, void* dst) {  // one wave: 64 lanes x 16 bytes to dst (wave-uniform)
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
   };
-  for (int sp = 0; sp < NSP; ++sp) {
-    {
-      // S0, dS_C: a wave load is 8 rows x 128 bytes
+  auto issue = [&](int sp) {
+    const int ln = opaque(lane);
+    // S0, dS_C: a wave load is 8 rows x 128 bytes
 #pragma unroll
-      for (int i = 0; i < DK / 32; ++i) {
-        const int r0 = 8 * (wu + 4 * i), row = r0 + (lane >> 3);
-        const size_t o = static_cast<size_t>(row) * DV + sp * 32 + (lane & 7) * 4;
-        dma(s0 + o, r0 * 128);
-        dma(dsC + o, DK * 128 + r0 * 128);
-      }
-      // dO, v: a wave load is 1024 / VROW rows; rows past the sequence read
-      // its last row (dO zeroed below; beta is 0 there)
-      constexpr int RPL = 1024 / VROW, LPR = VROW / 16, NL = BC / RPL;
-#pragma unroll
-      for (int i = 0; i < (NL + 3) / 4; ++i) {
-        const int li = min(wu + 4 * i, NL - 1);  // a wave past the last load repeats it (same bytes)
-        const int row = li * RPL + lane / LPR;
-        const size_t o = (static_cast<size_t>(cl.t0 + min(row, cl.len - 1)) * H + h) * DV + sp * 32 +
-                         (lane % LPR) * (16 / sizeof(T));
-        dma(dO + o, 2 * DK * 128 + li * 1024);
-        dma(v + o, RAW_V + li * 1024);
-      }
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0: this wave's loads are in LDS
-      lds_sync();
+    for (int i = 0; i < DK / 32; ++i) {
+      const int r0 = 8 * (wu + 4 * i), row = r0 + (ln >> 3);
+      const size_t o = static_cast<size_t>(row) * DV + sp * 32 + (ln & 7) * 4;
+      dma(s0 + o, rawS0 + r0 * 128);
+      dma(dsC + o, rawdS + r0 * 128);
     }
-    // slice inputs, split once, both orientations
-    for (int e = tid; e < DK * 8; e += 256) {
-      const int row = e >> 3, c4 = (e & 7) * 4;
-      const f32x4 a = *reinterpret_cast<const f32x4*>(rS0 + row * 32 + c4);
-      const f32x4 b = *reinterpret_cast<const f32x4*>(rdS + row * 32 + c4);
+    // dO: a wave load is 1024 / VROW rows; rows past the sequence read its
+    // last row (zeroed at the split)
+    constexpr int VROW = 32 * static_cast<int>(sizeof(T)), RPL = 1024 / VROW, LPR = VROW / 16, NL = BC / RPL;
+#pragma unroll
+    for (int i = 0; i < (NL + 3) / 4; ++i) {
+      const int li = min(wu + 4 * i, NL - 1);  // a wave past the last load repeats it (same bytes)
+      const int row = li * RPL + ln / LPR;
+      const size_t o = (static_cast<size_t>(cl.t0 + min(row, cl.len - 1)) * H + h) * DV + sp * 32 +
+                       (ln % LPR) * (16 / static_cast<int>(sizeof(T)));
+      dma(dO + o, rawdO + li * 1024);
+    }
+  };
+  // v where the first phase uses it (rows 16 w + 4 g + m, columns 16 nt + r
+  // of the slice), read one slice ahead; rows past the sequence read its
+  // last row (beta, dU and dW are 0 there)
+  typename raw1<T>::type vr[2][4];
+  auto issue_v = [&](int sp) {
+    const int ln = opaque(lane), rb = 16 * w + 4 * (ln >> 4);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int row = min(rb + m, cl.len - 1);
+        vr[nt][m] = raw1<T>::load(v + (static_cast<size_t>(cl.t0 + row) * H + h) * DV + sp * 32 + 16 * nt + (ln & 15));
+      }
+  };
+  // A's ten lower 16 x 16 blocks, for dbeta's inverse share at the end
+  for (int t = wu; t < 10; t += 4) {
+    int I, J;
+    tri_ij(t, I, J);
+    dma(bk + B::oA + (16 * I + (lane >> 2)) * BC + 16 * J + (lane & 3) * 4, Al + t * 256);
+  }
+  issue(0);
+  issue_v(0);
+  const T* const rdO = reinterpret_cast<const T*>(rawdO);
+  for (int sp = 0; sp < NSP; ++sp) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0: this wave's loads of the slice are in LDS
+    lds_sync();
+    // slice inputs, split once, by rows; dgamma's share of the slice (a
+    // row's 32 columns, fixed order)
+    const int c4 = (tid & 7) * 4;
+#pragma unroll
+    for (int i = 0; i < DK / 32; ++i) {
+      const int row = (tid >> 3) + 32 * i;
+      const f32x4 a = *reinterpret_cast<const f32x4*>(rawS0 + (row * 32 + c4) * 4);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(rawdS + (row * 32 + c4) * 4);
       S0p.put4(row, c4, a);
       dSp.put4(row, c4, b);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) S0T.put(c4 + i, row, a[i]), dST.put(c4 + i, row, b[i]);
+      float pr = a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
+      pr += __shfl_xor(pr, 1);
+      pr += __shfl_xor(pr, 2);
+      pr += __shfl_xor(pr, 4);
+      dg[i] += pr;
     }
-    for (int e = tid; e < BC * 8; e += 256) {
-      const int row = e >> 3, c4 = (e & 7) * 4;
-      const f32x4 y = row < cl.len ? load4(rdO + row * 32 + c4) : zero4();
-      Dp.put4(row, c4, y);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) DT.put(c4 + i, row, y[i]);
+    for (int i = 0; i < 2; ++i) {
+      const int row = (tid >> 3) + 32 * i;
+      Dp.put4(row, c4, row < cl.len ? load4(rdO + row * 32 + c4) : zero4());
     }
-    if (tid < DK) {  // dgamma's share of the slice, fixed order
-#pragma unroll 4
-      for (int c = 0; c < 32; c += 4) {
-        const f32x4 a = *reinterpret_cast<const f32x4*>(rS0 + tid * 32 + c);
-        const f32x4 b = *reinterpret_cast<const f32x4*>(rdS + tid * 32 + c);
-        dg += a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
+    lds_sync();
+    // the raw inputs are read: the transposed planes, copied from the split
+    // rows, go over them
+    auto tput = [&](const Plane& src, const Plane& dst, int row) {
+      const bf16x4 hi = *reinterpret_cast<const bf16x4*>(src.h + row * src.P + c4);
+      const bf16x4 lo = *reinterpret_cast<const bf16x4*>(src.l + row * src.P + c4);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        dst.h[(c4 + c) * dst.P + row] = hi[c];
+        dst.l[(c4 + c) * dst.P + row] = lo[c];
       }
+    };
+#pragma unroll
+    for (int i = 0; i < DK / 32; ++i) {
+      tput(S0p, S0T, (tid >> 3) + 32 * i);
+      tput(dSp, dST, (tid >> 3) + 32 * i);
     }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) tput(Dp, DT, (tid >> 3) + 32 * i);
     lds_sync();
     // Vt, W = beta Vt (transposed) and dU (transposed) for the two 16-column tiles
     f32x4 vt[2];
@@ -1108,16 +1163,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       f32x4 wv;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        // rows past the sequence hold its last row: beta, dU and dW are 0 there
-        const float vv = io<T>::load(rv + (16 * w + 4 * g + m) * 32 + n);
-        vt[nt][m] = vv - a[m];
+        vt[nt][m] = raw1<T>::cvt(vr[nt][m]) - a[m];
         wv[m] = bet[m] * vt[nt][m];
       }
       WT.put4(n, 16 * w + 4 * g, wv);
       dUT.put4(n, 16 * w + 4 * g, d);
     }
     lds_sync();
+    if (sp + 1 < NSP) {  // the transposed planes are free: the next slice's inputs go there
+      issue(sp + 1);
+      issue_v(sp + 1);
+    }
     // U = T W (rows) and dW = T^T dU (rows), dv, dbeta's write share
+    const int ln2 = opaque(lane);
+    T* const dvrow = dv + (static_cast<size_t>(cl.t0 + 16 * w + 4 * (ln2 >> 4)) * H + h) * DV + sp * 32 + (ln2 & 15);
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       const int n = 16 * nt + r;
@@ -1134,28 +1193,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         dWp.put(row, n, d[m]);
         dVp.put(row, n, bet[m] * d[m]);
         db1[m] += d[m] * vt[nt][m];
-        if (row < cl.len) io<T>::store(dv + (static_cast<size_t>(cl.t0 + row) * H + h) * DV + sp * 32 + n, bet[m] * d[m]);
+        if (row < cl.len) io<T>::store(dvrow + static_cast<size_t>(m) * H * DV + 16 * nt, bet[m] * d[m]);
       }
     }
     lds_sync();
-    // the slice's share of the contractions over value columns
+    // the slice's share of the contractions over value columns.  Every
+    // operand is a [rows][PW] plane, so a fragment is the lane's base
+    // (r PW + 8 g) plus a wave-uniform offset: no per-wave code paths.
+    {
+      const __bf16* const lb = lds + opaque(r * PW + 8 * g);
 #pragma unroll
-    for (int u = 0; u < NT; ++u) {
-      const int tau = w + 4 * u;
-      if (tau >= NTILE) break;
-      if (tau < 20) {
-        int I, J;
-        tri_ij(tau % 10, I, J);
-        const Plane& Am = tau < 10 ? Dp : dWp;
-        acc[u] = mm3(Am.frag(16 * I + r, 8 * g), Up.frag(16 * J + r, 8 * g), acc[u]);
-      } else {
-        const int e = tau - 20, kind = e / (4 * NKB), rem = e % (4 * NKB), I = rem / NKB, Jc = rem % NKB;
-        const Plane& Am = kind == 0 ? Dp : (kind == 1 ? dVp : Up);
-        const Plane& Bm = kind == 2 ? dSp : S0p;
-        acc[u] = mm3(Am.frag(16 * I + r, 8 * g), Bm.frag(16 * Jc + r, 8 * g), acc[u]);
+      for (int u = 0; u < NT; ++u) {
+        const int tau = w + 4 * u;
+        if (tau >= NTILE) break;
+        int oa, ob, la, lo;  // hi-plane offsets of the A and B rows, lo-plane displacements
+        if (u < 5) {         // dP (tau < 10) and dM tiles: rows of dO or dW against rows of U
+          int I, J;
+          tri_ij(tau % 10, I, J);
+          oa = (tau < 10 ? LL::odO : LL::odW) + 16 * I * PW;
+          ob = LL::oU + 16 * J * PW;
+          la = BC * PW;
+          lo = BC * PW;
+        } else {  // dQg (dO S0^T), dKg (dv S0^T), dKb (U dS^T): kind and row tile fixed by u
+          const int e = tau - 20, kind = e / (4 * NKB), rem = e % (4 * NKB), I = rem / NKB, Jc = rem % NKB;
+          oa = (kind == 0 ? LL::odO : (kind == 1 ? LL::odV : LL::oU)) + 16 * I * PW;
+          ob = (kind == 2 ? LL::odS : LL::oS0) + 16 * Jc * PW;
+          la = BC * PW;
+          lo = DK * PW;
+        }
+        oa = __builtin_amdgcn_readfirstlane(oa);
+        ob = __builtin_amdgcn_readfirstlane(ob);
+        const F3 fa{*reinterpret_cast<const bf16x8*>(lb + oa), *reinterpret_cast<const bf16x8*>(lb + oa + la)};
+        const F3 fb{*reinterpret_cast<const bf16x8*>(lb + ob), *reinterpret_cast<const bf16x8*>(lb + ob + lo)};
+        acc[u] = mm3(fa, fb, acc[u]);
       }
     }
-    lds_sync();
   }
   // dbeta: the write's share (dW . Vt, summed over value columns) and the
   // inverse's share (sum_s dM[r][s] A[r][s]), each part in its own slot and
@@ -1174,7 +1246,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const int row = 16 * I + 4 * g + m;
-        const float x = group_sum<16>(-acc[u][m] * bk[B::oA + row * BC + 16 * J + r]);
+        const float x = group_sum<16>(-acc[u][m] * Al[(tau - 10) * 256 + (4 * g + m) * 16 + r]);
         if (r == 0) dbp[row * 5 + J] = x;
       }
     }
@@ -1205,7 +1277,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       for (int m = 0; m < 4; ++m) bk[o + (16 * I + 4 * g + m) * DK + 16 * Jc + r] = sgn * acc[u][m];
     }
   }
-  if (tid < DK) bk[B::odGam + tid] = dg;
+  if ((tid & 7) == 0) {
+#pragma unroll
+    for (int i = 0; i < DK / 32; ++i) bk[B::odGam + (tid >> 3) + 32 * i] = dg[i];
+  }
 }
 
 // ---------------------------------------------------------------------------
