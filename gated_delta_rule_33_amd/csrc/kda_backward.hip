@@ -49,6 +49,8 @@
 #include <stdint.h>
 
 #include "kda_device.h"
+#include <algorithm>
+
 #include "kda_internal.h"
 
 namespace kda {
@@ -910,8 +912,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
 
 // ---------------------------------------------------------------------------
-// grad_v: one workgroup (4 waves) per (chunk, head); grid (chunks, H).  Walks
-// the value columns 32 at a time (one 32-wide k step of the products over
+// grad_v: persistent workgroups (4 waves, one per CU), each taking (chunk,
+// head) items in turn; per item it walks the value columns 32 at a time (one 32-wide k step of the products over
 // value columns).  Per slice, wave w on rows 16 w .. 16 w + 15:
 //   Vt = V - Kg S0, W = Diag(beta) Vt, U = T W
 //   dU = P^T dO + Kb dS_C, dW = T^T dU, dv = Diag(beta) dW
@@ -920,7 +922,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // Each operand sits in LDS in the orientation whose fragments are eight
 // consecutive floats (the S0, dS_C and dO slices both ways, W, dU transposed,
 // U and dW by rows); a slice's inputs are loaded while the previous slice
-// runs.  At the end dbeta and dv are written out, and dQg, dKg,
+// runs, and the next item's first slice and block operands while the
+// current item's last slice runs.  At the end dbeta and dv are written out, and dQg, dKg,
 // dKb, dP, dA = Diag(beta) dM, dgamma over the chunk's block (everything it
 // read from the block has been consumed by then).
 // ---------------------------------------------------------------------------
@@ -1001,48 +1004,67 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const Plane Dp = plane(LL::odO, BC, PW), DT = tplane(LL::tdO, PC);
   const Plane WT = plane(LL::oWT, 32, PC), dUT = plane(LL::odUT, 32, PC);
   const Plane Up = plane(LL::oU, BC, PW), dWp = plane(LL::odW, BC, PW), dVp = plane(LL::odV, BC, PW);
-  const int j = blockIdx.x, h = blockIdx.y;
-  if (j >= chunk_off[N]) return;
-  const ChunkLoc cl = locate(cu, chunk_off, N, j);
-  float* bk = blk + (static_cast<size_t>(j) * H + h) * B::floats;
-  const float* s0 = sc + (static_cast<size_t>(j) * H + h) * DK * DV;
-  const float* dsC = dsc + (static_cast<size_t>(j) * H + h) * DK * DV;
+  const int nch = chunk_off[N], items = nch * H;
+  int it = blockIdx.x;
+  if (it >= items) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g = lane >> 4;
-  if (tid < BC) betl[tid] = bk[B::oBeta + tid];
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  // dbeta's partial sums (five per row); the slots of blocks above the
+  // diagonal are never written and stay 0 for every item
   for (int e = tid; e < BC * 5; e += 256) dbp[e] = 0.f;
-  // block operands of the wave's row tile (rows 16 w + r), ready split
+  // Work item i: chunk i % nch of head i / nch (chunks of a head adjacent)
+  struct Item {
+    int h;
+    ChunkLoc cl;
+    float* bk;
+    const float* s0;
+    const float* dsC;
+  };
+  auto item_at = [&](int i) {
+    Item x;
+    const int j = i % nch;
+    x.h = i / nch;
+    x.cl = locate(cu, chunk_off, N, j);
+    const size_t slot = static_cast<size_t>(j) * H + x.h;
+    x.bk = blk + slot * B::floats;
+    x.s0 = sc + slot * DK * DV;
+    x.dsC = dsc + slot * DK * DV;
+    return x;
+  };
+  // block operands of the wave's row tile (rows 16 w + r), ready split:
+  // Kg, Kb, P^T (first phase), T, T^T and beta (second phase)
   F3 kgf[NKS], kbf[NKS], tf[2], ptf[2], ttf[2];
-  {
-    const int row = 16 * w + r;
+  float bet[4];
+  // (the addresses below, and in the other per-item steps, are formed from
+  // an opaque lane index so that they are not held across the item loop)
+  auto load_first = [&](const Item& x) {
+    const int ln = opaque(lane), row = 16 * w + (ln & 15), k8 = 8 * (ln >> 4);
 #pragma unroll
     for (int kk = 0; kk < NKS; ++kk) {
-      kgf[kk] = pfrag(bk + B::oKg, DK, row, 32 * kk + 8 * g);
-      kbf[kk] = pfrag(bk + B::oKb, DK, row, 32 * kk + 8 * g);
+      kgf[kk] = pfrag(x.bk + B::oKg, DK, row, 32 * kk + k8);
+      kbf[kk] = pfrag(x.bk + B::oKb, DK, row, 32 * kk + k8);
     }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) ptf[kk] = pfrag(x.bk + B::oPT, BC, row, 32 * kk + k8);
+  };
+  auto load_second = [&](const Item& x) {
+    const int ln = opaque(lane), row = 16 * w + (ln & 15), k8 = 8 * (ln >> 4);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      tf[kk] = pfrag(bk + B::oT, BC, row, 32 * kk + 8 * g);
-      ptf[kk] = pfrag(bk + B::oPT, BC, row, 32 * kk + 8 * g);
-      ttf[kk] = pfrag(bk + B::oTT, BC, row, 32 * kk + 8 * g);
+      tf[kk] = pfrag(x.bk + B::oT, BC, row, 32 * kk + k8);
+      ttf[kk] = pfrag(x.bk + B::oTT, BC, row, 32 * kk + k8);
     }
-  }
-  float bet[4];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) bet[m] = bk[B::oBeta + 16 * w + 4 * g + m];
+    for (int m = 0; m < 4; ++m) bet[m] = x.bk[B::oBeta + 16 * w + 4 * (ln >> 4) + m];
+  };
   // k steps (32 chunk rows each) a triangular factor of row tile w needs:
   // T (lower): rows <= 16 w + 15;  T^T, P^T: rows >= 16 w
   const int kT1 = w >= 2 ? 1 : 0, kU0 = w >= 2 ? 1 : 0;
-  f32x4 acc[NT];
-#pragma unroll
-  for (int u = 0; u < NT; ++u) acc[u] = zero4();
-  float db1[4] = {0.f, 0.f, 0.f, 0.f};
-  float dg[DK / 32];  // dgamma of rows (tid >> 3) + 32 i (every lane of a row's eight holds it)
-#pragma unroll
-  for (int i = 0; i < DK / 32; ++i) dg[i] = 0.f;
   // The slice inputs (S0 and dS_C [DK][32] fp32, dO [BC][32] io) land raw in
   // LDS by direct global-to-LDS loads, in the area of the transposed S0, dS_C
   // and dO planes.  Those planes are read only in the first phase, so the
-  // loads of slice sp + 1 are issued right after it and arrive while slice sp
+  // loads of the next slice (the next item's first slice, after an item's
+  // last) are issued right after it and arrive while the current slice
   // finishes; the split of a slice writes the row planes from the raw inputs
   // and then copies them into the transposed planes, over the raw inputs.
   // The area is an LDS array of its own: the compiler then knows that the
@@ -1053,19 +1075,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   static_assert(DK * 128 <= 2 * 32 * PK * 2 && BC * 32 * static_cast<int>(sizeof(T)) <= 2 * 32 * PC * 2,
                 "raw slice inputs fit the transposed planes");
   static_assert((LL::tdS * 2) % 16 == 0 && (LL::tdO * 2) % 16 == 0, "raw areas are 16-byte aligned");
-  const int wu = __builtin_amdgcn_readfirstlane(w);
   auto dma = [&](const void* src, void* dst) {  // one wave: 64 lanes x 16 bytes to dst (wave-uniform)
     __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
   };
-  auto issue = [&](int sp) {
+  auto issue = [&](const Item& x, int sp) {
     const int ln = opaque(lane);
     // S0, dS_C: a wave load is 8 rows x 128 bytes
 #pragma unroll
     for (int i = 0; i < DK / 32; ++i) {
       const int r0 = 8 * (wu + 4 * i), row = r0 + (ln >> 3);
       const size_t o = static_cast<size_t>(row) * DV + sp * 32 + (ln & 7) * 4;
-      dma(s0 + o, rawS0 + r0 * 128);
-      dma(dsC + o, rawdS + r0 * 128);
+      dma(x.s0 + o, rawS0 + r0 * 128);
+      dma(x.dsC + o, rawdS + r0 * 128);
     }
     // dO: a wave load is 1024 / VROW rows; rows past the sequence read its
     // last row (zeroed at the split)
@@ -1074,7 +1095,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int i = 0; i < (NL + 3) / 4; ++i) {
       const int li = min(wu + 4 * i, NL - 1);  // a wave past the last load repeats it (same bytes)
       const int row = li * RPL + ln / LPR;
-      const size_t o = (static_cast<size_t>(cl.t0 + min(row, cl.len - 1)) * H + h) * DV + sp * 32 +
+      const size_t o = (static_cast<size_t>(x.cl.t0 + min(row, x.cl.len - 1)) * H + x.h) * DV + sp * 32 +
                        (ln % LPR) * (16 / static_cast<int>(sizeof(T)));
       dma(dO + o, rawdO + li * 1024);
     }
@@ -1083,203 +1104,243 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // of the slice), read one slice ahead; rows past the sequence read its
   // last row (beta, dU and dW are 0 there)
   typename raw1<T>::type vr[2][4];
-  auto issue_v = [&](int sp) {
+  auto issue_v = [&](const Item& x, int sp) {
     const int ln = opaque(lane), rb = 16 * w + 4 * (ln >> 4);
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const int row = min(rb + m, cl.len - 1);
-        vr[nt][m] = raw1<T>::load(v + (static_cast<size_t>(cl.t0 + row) * H + h) * DV + sp * 32 + 16 * nt + (ln & 15));
+        const int row = min(rb + m, x.cl.len - 1);
+        vr[nt][m] = raw1<T>::load(v + (static_cast<size_t>(x.cl.t0 + row) * H + x.h) * DV + sp * 32 + 16 * nt +
+                                  (ln & 15));
       }
   };
   // A's ten lower 16 x 16 blocks, for dbeta's inverse share at the end
-  for (int t = wu; t < 10; t += 4) {
-    int I, J;
-    tri_ij(t, I, J);
-    dma(bk + B::oA + (16 * I + (lane >> 2)) * BC + 16 * J + (lane & 3) * 4, Al + t * 256);
-  }
-  issue(0);
-  issue_v(0);
+  auto issue_A = [&](const Item& x) {
+    const int ln = opaque(lane);
+    for (int t = wu; t < 10; t += 4) {
+      int I, J;
+      tri_ij(t, I, J);
+      dma(x.bk + B::oA + (16 * I + (ln >> 2)) * BC + 16 * J + (ln & 3) * 4, Al + t * 256);
+    }
+  };
+  Item cur = item_at(it);
+  load_first(cur);
+  load_second(cur);
+  issue_A(cur);
+  issue(cur, 0);
+  issue_v(cur, 0);
   const T* const rdO = reinterpret_cast<const T*>(rawdO);
-  for (int sp = 0; sp < NSP; ++sp) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0: this wave's loads of the slice are in LDS
-    lds_sync();
-    // slice inputs, split once, by rows; dgamma's share of the slice (a
-    // row's 32 columns, fixed order)
-    const int c4 = (tid & 7) * 4;
+  for (;;) {
+    const int nx = it + static_cast<int>(gridDim.x);
+    const bool more = nx < items;
+    const Item nxt = item_at(more ? nx : it);
+    f32x4 acc[NT];
 #pragma unroll
-    for (int i = 0; i < DK / 32; ++i) {
-      const int row = (tid >> 3) + 32 * i;
-      const f32x4 a = *reinterpret_cast<const f32x4*>(rawS0 + (row * 32 + c4) * 4);
-      const f32x4 b = *reinterpret_cast<const f32x4*>(rawdS + (row * 32 + c4) * 4);
-      S0p.put4(row, c4, a);
-      dSp.put4(row, c4, b);
-      float pr = a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
-      pr += __shfl_xor(pr, 1);
-      pr += __shfl_xor(pr, 2);
-      pr += __shfl_xor(pr, 4);
-      dg[i] += pr;
-    }
+    for (int u = 0; u < NT; ++u) acc[u] = zero4();
+    float db1[4] = {0.f, 0.f, 0.f, 0.f};
+    float dg[DK / 32];  // dgamma of rows (tid >> 3) + 32 i (every lane of a row's eight holds it)
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = (tid >> 3) + 32 * i;
-      Dp.put4(row, c4, row < cl.len ? load4(rdO + row * 32 + c4) : zero4());
-    }
-    lds_sync();
-    // the raw inputs are read: the transposed planes, copied from the split
-    // rows, go over them
-    auto tput = [&](const Plane& src, const Plane& dst, int row) {
-      const bf16x4 hi = *reinterpret_cast<const bf16x4*>(src.h + row * src.P + c4);
-      const bf16x4 lo = *reinterpret_cast<const bf16x4*>(src.l + row * src.P + c4);
+    for (int i = 0; i < DK / 32; ++i) dg[i] = 0.f;
+    for (int sp = 0; sp < NSP; ++sp) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0: this wave's loads of the slice are in LDS
+      lds_sync();
+      if (sp == 0 && r == 0) {  // beta of the item's rows, for the end (read after several barriers)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        dst.h[(c4 + c) * dst.P + row] = hi[c];
-        dst.l[(c4 + c) * dst.P + row] = lo[c];
+        for (int m = 0; m < 4; ++m) betl[16 * w + 4 * g + m] = bet[m];
       }
-    };
+      // slice inputs, split once, by rows; dgamma's share of the slice (a
+      // row's 32 columns, fixed order)
+      const int c4 = (tid & 7) * 4;
 #pragma unroll
-    for (int i = 0; i < DK / 32; ++i) {
-      tput(S0p, S0T, (tid >> 3) + 32 * i);
-      tput(dSp, dST, (tid >> 3) + 32 * i);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) tput(Dp, DT, (tid >> 3) + 32 * i);
-    lds_sync();
-    // Vt, W = beta Vt (transposed) and dU (transposed) for the two 16-column tiles
-    f32x4 vt[2];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int n = 16 * nt + r;
-      f32x4 a = zero4(), d = zero4();
-#pragma unroll
-      for (int kk = 0; kk < NKS; ++kk) {
-        a = mm3(kgf[kk], S0T.frag(n, 32 * kk + 8 * g), a);
-        d = mm3(kbf[kk], dST.frag(n, 32 * kk + 8 * g), d);
+      for (int i = 0; i < DK / 32; ++i) {
+        const int row = (tid >> 3) + 32 * i;
+        const f32x4 a = *reinterpret_cast<const f32x4*>(rawS0 + (row * 32 + c4) * 4);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(rawdS + (row * 32 + c4) * 4);
+        S0p.put4(row, c4, a);
+        dSp.put4(row, c4, b);
+        float pr = a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
+        pr += __shfl_xor(pr, 1);
+        pr += __shfl_xor(pr, 2);
+        pr += __shfl_xor(pr, 4);
+        dg[i] += pr;
       }
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-        if (kk >= kU0) d = mm3(ptf[kk], DT.frag(n, 32 * kk + 8 * g), d);
-      f32x4 wv;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        vt[nt][m] = raw1<T>::cvt(vr[nt][m]) - a[m];
-        wv[m] = bet[m] * vt[nt][m];
+      for (int i = 0; i < 2; ++i) {
+        const int row = (tid >> 3) + 32 * i;
+        Dp.put4(row, c4, row < cur.cl.len ? load4(rdO + row * 32 + c4) : zero4());
       }
-      WT.put4(n, 16 * w + 4 * g, wv);
-      dUT.put4(n, 16 * w + 4 * g, d);
-    }
-    lds_sync();
-    if (sp + 1 < NSP) {  // the transposed planes are free: the next slice's inputs go there
-      issue(sp + 1);
-      issue_v(sp + 1);
-    }
-    // U = T W (rows) and dW = T^T dU (rows), dv, dbeta's write share
-    const int ln2 = opaque(lane);
-    T* const dvrow = dv + (static_cast<size_t>(cl.t0 + 16 * w + 4 * (ln2 >> 4)) * H + h) * DV + sp * 32 + (ln2 & 15);
+      lds_sync();
+      // the raw inputs are read: the transposed planes, copied from the split
+      // rows, go over them
+      auto tput = [&](const Plane& src, const Plane& dst, int row) {
+        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(src.h + row * src.P + c4);
+        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(src.l + row * src.P + c4);
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int n = 16 * nt + r;
-      f32x4 a = zero4(), d = zero4();
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        if (kk <= kT1) a = mm3(tf[kk], WT.frag(n, 32 * kk + 8 * g), a);
-        if (kk >= kU0) d = mm3(ttf[kk], dUT.frag(n, 32 * kk + 8 * g), d);
-      }
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int row = 16 * w + 4 * g + m;
-        Up.put(row, n, a[m]);
-        dWp.put(row, n, d[m]);
-        dVp.put(row, n, bet[m] * d[m]);
-        db1[m] += d[m] * vt[nt][m];
-        if (row < cl.len) io<T>::store(dvrow + static_cast<size_t>(m) * H * DV + 16 * nt, bet[m] * d[m]);
-      }
-    }
-    lds_sync();
-    // the slice's share of the contractions over value columns.  Every
-    // operand is a [rows][PW] plane, so a fragment is the lane's base
-    // (r PW + 8 g) plus a wave-uniform offset: no per-wave code paths.
-    {
-      const __bf16* const lb = lds + opaque(r * PW + 8 * g);
-#pragma unroll
-      for (int u = 0; u < NT; ++u) {
-        const int tau = w + 4 * u;
-        if (tau >= NTILE) break;
-        int oa, ob, la, lo;  // hi-plane offsets of the A and B rows, lo-plane displacements
-        if (u < 5) {         // dP (tau < 10) and dM tiles: rows of dO or dW against rows of U
-          int I, J;
-          tri_ij(tau % 10, I, J);
-          oa = (tau < 10 ? LL::odO : LL::odW) + 16 * I * PW;
-          ob = LL::oU + 16 * J * PW;
-          la = BC * PW;
-          lo = BC * PW;
-        } else {  // dQg (dO S0^T), dKg (dv S0^T), dKb (U dS^T): kind and row tile fixed by u
-          const int e = tau - 20, kind = e / (4 * NKB), rem = e % (4 * NKB), I = rem / NKB, Jc = rem % NKB;
-          oa = (kind == 0 ? LL::odO : (kind == 1 ? LL::odV : LL::oU)) + 16 * I * PW;
-          ob = (kind == 2 ? LL::odS : LL::oS0) + 16 * Jc * PW;
-          la = BC * PW;
-          lo = DK * PW;
+        for (int c = 0; c < 4; ++c) {
+          dst.h[(c4 + c) * dst.P + row] = hi[c];
+          dst.l[(c4 + c) * dst.P + row] = lo[c];
         }
-        oa = __builtin_amdgcn_readfirstlane(oa);
-        ob = __builtin_amdgcn_readfirstlane(ob);
-        const F3 fa{*reinterpret_cast<const bf16x8*>(lb + oa), *reinterpret_cast<const bf16x8*>(lb + oa + la)};
-        const F3 fb{*reinterpret_cast<const bf16x8*>(lb + ob), *reinterpret_cast<const bf16x8*>(lb + ob + lo)};
-        acc[u] = mm3(fa, fb, acc[u]);
+      };
+#pragma unroll
+      for (int i = 0; i < DK / 32; ++i) {
+        tput(S0p, S0T, (tid >> 3) + 32 * i);
+        tput(dSp, dST, (tid >> 3) + 32 * i);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) tput(Dp, DT, (tid >> 3) + 32 * i);
+      lds_sync();
+      // Vt, W = beta Vt (transposed) and dU (transposed) for the two 16-column tiles
+      f32x4 vt[2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int n = 16 * nt + r;
+        f32x4 a = zero4(), d = zero4();
+#pragma unroll
+        for (int kk = 0; kk < NKS; ++kk) {
+          a = mm3(kgf[kk], S0T.frag(n, 32 * kk + 8 * g), a);
+          d = mm3(kbf[kk], dST.frag(n, 32 * kk + 8 * g), d);
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+          if (kk >= kU0) d = mm3(ptf[kk], DT.frag(n, 32 * kk + 8 * g), d);
+        f32x4 wv;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          vt[nt][m] = raw1<T>::cvt(vr[nt][m]) - a[m];
+          wv[m] = bet[m] * vt[nt][m];
+        }
+        WT.put4(n, 16 * w + 4 * g, wv);
+        dUT.put4(n, 16 * w + 4 * g, d);
+      }
+      lds_sync();
+      // the transposed planes are free: the next slice's inputs go there
+      // (after the item's last slice, the next item's first, with its
+      // first-phase block operands)
+      // (one call site each: the loads then go straight into the registers
+      // that carry them, with no copy that would wait for them)
+      const bool same = sp + 1 < NSP;
+      if (same || more) {
+        const Item& x = same ? cur : nxt;
+        issue(x, same ? sp + 1 : 0);
+        issue_v(x, same ? sp + 1 : 0);
+      }
+      if (!same && more) load_first(nxt);
+      // U = T W (rows) and dW = T^T dU (rows), dv, dbeta's write share
+      const int ln2 = opaque(lane);
+      T* const dvrow =
+          dv + (static_cast<size_t>(cur.cl.t0 + 16 * w + 4 * (ln2 >> 4)) * H + cur.h) * DV + sp * 32 + (ln2 & 15);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int n = 16 * nt + r;
+        f32x4 a = zero4(), d = zero4();
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          if (kk <= kT1) a = mm3(tf[kk], WT.frag(n, 32 * kk + 8 * g), a);
+          if (kk >= kU0) d = mm3(ttf[kk], dUT.frag(n, 32 * kk + 8 * g), d);
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int row = 16 * w + 4 * g + m;
+          Up.put(row, n, a[m]);
+          dWp.put(row, n, d[m]);
+          dVp.put(row, n, bet[m] * d[m]);
+          db1[m] += d[m] * vt[nt][m];
+          if (row < cur.cl.len) io<T>::store(dvrow + static_cast<size_t>(m) * H * DV + 16 * nt, bet[m] * d[m]);
+        }
+      }
+      if (sp + 1 == NSP && more) load_second(nxt);  // the second-phase operands are used
+      lds_sync();
+      // the slice's share of the contractions over value columns.  Every
+      // operand is a [rows][PW] plane, so a fragment is the lane's base
+      // (r PW + 8 g) plus a wave-uniform offset: no per-wave code paths.
+      {
+        const __bf16* const lb = lds + opaque(r * PW + 8 * g);
+#pragma unroll
+        for (int u = 0; u < NT; ++u) {
+          const int tau = w + 4 * u;
+          if (tau >= NTILE) break;
+          int oa, ob, la, lo;  // hi-plane offsets of the A and B rows, lo-plane displacements
+          if (u < 5) {         // dP (tau < 10) and dM tiles: rows of dO or dW against rows of U
+            int I, J;
+            tri_ij(tau % 10, I, J);
+            oa = (tau < 10 ? LL::odO : LL::odW) + 16 * I * PW;
+            ob = LL::oU + 16 * J * PW;
+            la = BC * PW;
+            lo = BC * PW;
+          } else {  // dQg (dO S0^T), dKg (dv S0^T), dKb (U dS^T): kind and row tile fixed by u
+            const int e = tau - 20, kind = e / (4 * NKB), rem = e % (4 * NKB), I = rem / NKB, Jc = rem % NKB;
+            oa = (kind == 0 ? LL::odO : (kind == 1 ? LL::odV : LL::oU)) + 16 * I * PW;
+            ob = (kind == 2 ? LL::odS : LL::oS0) + 16 * Jc * PW;
+            la = BC * PW;
+            lo = DK * PW;
+          }
+          oa = __builtin_amdgcn_readfirstlane(oa);
+          ob = __builtin_amdgcn_readfirstlane(ob);
+          const F3 fa{*reinterpret_cast<const bf16x8*>(lb + oa), *reinterpret_cast<const bf16x8*>(lb + oa + la)};
+          const F3 fb{*reinterpret_cast<const bf16x8*>(lb + ob), *reinterpret_cast<const bf16x8*>(lb + ob + lo)};
+          acc[u] = mm3(fa, fb, acc[u]);
+        }
       }
     }
-  }
-  // dbeta: the write's share (dW . Vt, summed over value columns) and the
-  // inverse's share (sum_s dM[r][s] A[r][s]), each part in its own slot and
-  // summed in a fixed order
+    // dbeta: the write's share (dW . Vt, summed over value columns) and the
+    // inverse's share (sum_s dM[r][s] A[r][s]), each part in its own slot and
+    // summed in a fixed order
+    const int ln3 = opaque(lane), r3 = ln3 & 15, g3 = ln3 >> 4;
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const float x = group_sum<16>(db1[m]);
-    if (r == 0) dbp[(16 * w + 4 * g + m) * 5 + 4] = x;
-  }
+    for (int m = 0; m < 4; ++m) {
+      const float x = group_sum<16>(db1[m]);
+      if (r == 0) dbp[(16 * w + 4 * g + m) * 5 + 4] = x;
+    }
 #pragma unroll
-  for (int u = 0; u < NT; ++u) {
-    const int tau = w + 4 * u;
-    if (tau >= 10 && tau < 20) {
-      int I, J;
-      tri_ij(tau - 10, I, J);
+    for (int u = 0; u < NT; ++u) {
+      const int tau = w + 4 * u;
+      if (tau >= 10 && tau < 20) {
+        int I, J;
+        tri_ij(tau - 10, I, J);
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int row = 16 * I + 4 * g + m;
-        const float x = group_sum<16>(-acc[u][m] * Al[(tau - 10) * 256 + (4 * g + m) * 16 + r]);
-        if (r == 0) dbp[row * 5 + J] = x;
+        for (int m = 0; m < 4; ++m) {
+          const int row = 16 * I + 4 * g3 + m;
+          const float x = group_sum<16>(-acc[u][m] * Al[(tau - 10) * 256 + (4 * g3 + m) * 16 + r3]);
+          if (r3 == 0) dbp[row * 5 + J] = x;
+        }
       }
     }
-  }
-  lds_sync();
-  if (tid < cl.len) {
-    const float* x = dbp + tid * 5;
-    dbeta[static_cast<size_t>(cl.t0 + tid) * H + h] = x[4] + x[0] + x[1] + x[2] + x[3];
-  }
-#pragma unroll
-  for (int u = 0; u < NT; ++u) {
-    const int tau = w + 4 * u;
-    if (tau >= NTILE) break;
-    if (tau < 20) {
-      int I, J;
-      tri_ij(tau % 10, I, J);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int row = 16 * I + 4 * g + m, col = 16 * J + r;
-        if (tau < 10) bk[B::odP + row * BC + col] = (I == J && col > row) ? 0.f : acc[u][m];
-        else bk[B::odA + row * BC + col] = (I == J && col >= row) ? 0.f : -betl[row] * acc[u][m];
-      }
-    } else {
-      const int e = tau - 20, kind = e / (4 * NKB), rem = e % (4 * NKB), I = rem / NKB, Jc = rem % NKB;
-      const size_t o = kind == 0 ? B::odQg : (kind == 1 ? B::odKg : B::odKb);
-      const float sgn = kind == 1 ? -1.f : 1.f;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) bk[o + (16 * I + 4 * g + m) * DK + 16 * Jc + r] = sgn * acc[u][m];
+    lds_sync();
+    if (more) issue_A(nxt);  // A is read: the next item's goes there
+    float* const bk = cur.bk;
+    if (tid < cur.cl.len) {
+      const float* x = dbp + tid * 5;
+      dbeta[static_cast<size_t>(cur.cl.t0 + tid) * H + cur.h] = x[4] + x[0] + x[1] + x[2] + x[3];
     }
-  }
-  if ((tid & 7) == 0) {
 #pragma unroll
-    for (int i = 0; i < DK / 32; ++i) bk[B::odGam + (tid >> 3) + 32 * i] = dg[i];
+    for (int u = 0; u < NT; ++u) {
+      const int tau = w + 4 * u;
+      if (tau >= NTILE) break;
+      if (tau < 20) {
+        int I, J;
+        tri_ij(tau % 10, I, J);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int row = 16 * I + 4 * g3 + m, col = 16 * J + r3;
+          if (tau < 10) bk[B::odP + row * BC + col] = (I == J && col > row) ? 0.f : acc[u][m];
+          else bk[B::odA + row * BC + col] = (I == J && col >= row) ? 0.f : -betl[row] * acc[u][m];
+        }
+      } else {
+        const int e = tau - 20, kind = e / (4 * NKB), rem = e % (4 * NKB), I = rem / NKB, Jc = rem % NKB;
+        const size_t o = kind == 0 ? B::odQg : (kind == 1 ? B::odKg : B::odKb);
+        const float sgn = kind == 1 ? -1.f : 1.f;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) bk[o + (16 * I + 4 * g3 + m) * DK + 16 * Jc + r3] = sgn * acc[u][m];
+      }
+    }
+    if ((tid & 7) == 0) {
+#pragma unroll
+      for (int i = 0; i < DK / 32; ++i) bk[B::odGam + (tid >> 3) + 32 * i] = dg[i];
+    }
+    if (!more) break;
+    it = nx;
+    cur = nxt;
   }
 }
 
@@ -1569,8 +1630,13 @@ static hipError_t launch_backward_t(const BackwardPlan& p, const void* q, const 
                      order, p.N, p.H, blk, S0, dS_T, sc, dsc, dS0, static_cast<int>(seq_wgs));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (mc > 0) {
-    hipLaunchKernelGGL((bwd_grad_v_kernel<T, DK, DV>), dim3(mc, p.H), dim3(256), 0, st, tv, tdo, cu, chunk_off, p.N,
-                       p.H, blk, sc, dsc, static_cast<T*>(dv), dbeta);
+    // persistent: one workgroup per CU (its LDS allows no more), each walking
+    // the (chunk, head) items gridDim apart
+    int cus = 0;
+    if ((e = device_cus(&cus)) != hipSuccess) return e;
+    const unsigned gv = static_cast<unsigned>(std::min<int64_t>(static_cast<int64_t>(mc) * p.H, cus));
+    hipLaunchKernelGGL((bwd_grad_v_kernel<T, DK, DV>), dim3(gv), dim3(256), 0, st, tv, tdo, cu, chunk_off, p.N, p.H,
+                       blk, sc, dsc, static_cast<T*>(dv), dbeta);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     constexpr int SW = 16;  // key channels per grad_k slice (LDS for two workgroups per CU)
     const unsigned nz = G == KDA_GATE_SCALAR ? 1u : static_cast<unsigned>(DK / SW);

@@ -60,6 +60,9 @@ hipError_t launch_prefill(const PrefillPlan& p, const void* q, const void* k, co
 hipError_t launch_chunk_offsets(const int32_t* cu, int N, int C, int32_t* chunk_off, int32_t* order, int sort,
                                 hipStream_t st);
 
+// Compute units of the current device (cached per device).
+hipError_t device_cus(int* cus);
+
 // Backward workspace carve-up, computed on the host.
 struct BackwardPlan {
   int N, T, H, dk, dv;

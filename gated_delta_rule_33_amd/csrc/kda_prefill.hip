@@ -1972,7 +1972,7 @@ static hipError_t launch_scan(const PrefillPlan& p, const void* v, const int32_t
 }
 
 // Compute units of the current device (cached per device).
-static hipError_t device_cus(int* cus) {
+hipError_t device_cus(int* cus) {
   static int cache[64] = {};
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
