@@ -59,6 +59,10 @@ namespace {
 constexpr int BC = 64;   // tokens per chunk
 constexpr int P20 = 20;  // LDS pitch (floats) of 16-column tiles
 constexpr int LPC = BC + 4;  // LDS pitch of chunk x chunk matrices
+// Largest decay (natural log) across a 16-row block for which the prep forms
+// the block's own gated products from operands scaled at the row before it:
+// the column factor e^{G_ref - G_s} then stays below e^{59.6} < 2^86.
+constexpr float kBwdDiagRange = 59.6f;
 
 __device__ __forceinline__ f32x4 mf(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -289,7 +293,7 @@ __device__ __forceinline__ int off_pair_j(int w, int u) {
 }
 
 template <typename T, int DK, int G>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                        const float* __restrict__ la, const float* __restrict__ beta,
                                                        const int32_t* __restrict__ cu,
                                                        const int32_t* __restrict__ chunk_off, int N, int H,
@@ -403,27 +407,54 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ q, 
         pO[u] = mf(qs[ri * PS + ch] * er, b, pO[u]);
       }
     }
-    // diagonal block pair (w, w): each entry's factors formed pair by pair
+    // diagonal block pair (w, w) on fp32 MFMA, its operands scaled at the
+    // row before the block: k_r e^{G_r - G_ref} (<= 1) against
+    // k_s e^{G_ref - G_s} (>= 1, at most e^{kBwdDiagRange} for a channel
+    // whose decay across the block is within range; the entries on and
+    // above the diagonal are dropped after the last slice).  A channel that
+    // decays faster takes the pair-by-pair path below instead.
+    unsigned bad = 0;  // the slice's out-of-range channels (wave-uniform)
+    {
+      const int rr = 16 * w + r;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const int ch = 4 * kk + g;
+        const float gref = w > 0 ? gs[(16 * w - 1) * PS + ch] : 0.f;
+        const bool inr = gref - gs[(16 * w + 15) * PS + ch] <= kBwdDiagRange;
+        const float gr = gs[rr * PS + ch], kv = ks[rr * PS + ch];
+        const float er = __expf(gr - gref);
+        const float b = inr ? kv * __expf(gref - gr) : 0.f;
+        aD = mf(kv * er, b, aD);
+        pD = mf(qs[rr * PS + ch] * er, b, pD);
+        const unsigned long long bl = __ballot(!inr);  // lane (r, g) holds channel 4 kk + g
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) bad |= ((bl >> (16 * gg)) & 1ull) ? (1u << (4 * kk + gg)) : 0u;
+      }
+    }
     {
       const int s = 16 * w + r;
+      while (bad) {
+        const int ch = __builtin_ctz(bad);
+        bad &= bad - 1;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int ri = 16 * w + 4 * g + m;
-        if (s <= ri) {
-          float sa = 0.f, sp = 0.f;
-#pragma unroll 8
-          for (int ch = 0; ch < 32; ++ch) {
+        for (int m = 0; m < 4; ++m) {
+          const int ri = 16 * w + 4 * g + m;
+          if (s <= ri) {
             const float kE = ks[s * PS + ch] * __expf(gs[ri * PS + ch] - gs[s * PS + ch]);
-            sa += ks[ri * PS + ch] * kE;
-            sp += qs[ri * PS + ch] * kE;
+            if (s < ri) aD[m] += ks[ri * PS + ch] * kE;
+            pD[m] += qs[ri * PS + ch] * kE;
           }
-          if (s < ri) aD[m] += sa;
-          pD[m] += sp;
         }
       }
     }
     lds_sync();
     cur = nxt;
+  }
+  // the diagonal block's products hold every pair: keep s < r for A, s <= r for P
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    if (r >= 4 * g + m) aD[m] = 0.f;
+    if (r > 4 * g + m) pD[m] = 0.f;
   }
   // A to the block (upper blocks zero), L = Diag(beta) A and T = 0 in LDS
   // (P stays in its accumulators until T is done; it then goes through Lm)

@@ -80,17 +80,17 @@ def test_backward_matches_oracle(lengths, H, dk, dv, io, gate, s0std, seed):
     compare(gpu_backward(w, cot), oracle_backward(w, cot), TOL[io])
 
 
-@pytest.mark.parametrize("la_kind", ["const-11", "const-60", "mixed-30"])
+@pytest.mark.parametrize("la_kind", ["const-11", "const-60", "mixed-30", "const-3.7"])
 def test_backward_extreme_gates(la_kind):
     """Constant log alpha of -11 and -60 per token (a 16-token block decays by
-    e^-176 and e^-960: far past fp32) and half the channels at -30, the rest
-    at 0 (no decay): exact for every finite gate."""
+    e^-176 and e^-960: far past fp32), half the channels at -30, the rest at 0
+    (no decay), and -3.7 (a 16-token block decays by e^-59.2, just inside the
+    range where a block's own products use operands scaled at the row before
+    it, so the column factors reach e^59): exact for every finite gate."""
     log("backward gates: %s" % la_kind)
     w = synth.make_prefill([150, 70], 2, 64, 64, "f32", 11, S0_std=0.5)
-    if la_kind == "const-11":
-        w.log_alpha[:] = -11.0
-    elif la_kind == "const-60":
-        w.log_alpha[:] = -60.0
+    if la_kind.startswith("const-"):
+        w.log_alpha[:] = -float(la_kind[len("const-"):])
     else:
         w.log_alpha[:] = 0.0
         w.log_alpha[:, :, ::2] = -30.0
