@@ -1388,9 +1388,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 //   dG = dQg Qg + dKg Kg - dKb Kb + q GQ + k (GA - G2)
 //        (+ sum_s dKb_s Kb_s + dgamma gamma on the last row, for G_C)
 //   dlog alpha_u = sum_{r >= u} dG_r
-// Off-diagonal block pairs use operands scaled at a reference row (row-side:
-// rows s < 16 I scaled by e^{G_{16I-1} - G_s}; column side: rows r > 16 J + 15
-// scaled by e^{G_r - G_{16J+15}}), diagonal blocks pair by pair.
+// Block pairs use operands scaled at a reference row (row side: rows s of
+// the earlier blocks and of the block itself scaled by e^{G_{16I-1} - G_s};
+// column side: rows r of the block and the later ones by e^{G_r - G_{16I+15}});
+// the block's own pairs of a channel that decays by more than e^{59.6}
+// across it are taken pair by pair instead.
 // ---------------------------------------------------------------------------
 template <typename T, int DK, int G, int SW>
 __global__ __launch_bounds__(256) void bwd_grad_k_kernel(const T* __restrict__ q, const T* __restrict__ k,
@@ -1492,57 +1494,88 @@ __global__ __launch_bounds__(256) void bwd_grad_k_kernel(const T* __restrict__ q
     lds_sync();
     float GQ[CPT], GA[CPT], G2[CPT], Gr[CPT];
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) GQ[i] = GA[i] = G2[i] = 0.f, Gr[i] = gs[row * PS + c8 + i];
-    // Off-diagonal block pairs on fp32 MFMA (exact fp32 products), each
-    // computed transposed, C^T = X^T D^T, so that output lane l holds row
-    // l % 16 and channels 4 (l / 16) .. + 3: this thread's.  Row side over
-    // the earlier blocks s < 16 I (operands scaled at row 16 I - 1), column
-    // side over the later rows r > 16 I + 15 (scaled at row 16 I + 15); the
-    // block index is the wave's, so the k loops are uniform.
-    if (I > 0) {
+    for (int i = 0; i < CPT; ++i) Gr[i] = gs[row * PS + c8 + i];
+    // A channel whose decay across the wave's block is within range has the
+    // block's own pairs on the MFMA path too; one that decays faster takes
+    // them pair by pair (below).
+    const float gpre = I > 0 ? gs[(16 * I - 1) * PS + ln] : 0.f, gend = gs[(16 * I + 15) * PS + ln];
+    const bool inr = gpre - gend <= kBwdDiagRange;  // channel ln (the MFMA row operand's)
+    bool bad[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+      bad[i] = (I > 0 ? gs[(16 * I - 1) * PS + c8 + i] : 0.f) - gs[(16 * I + 15) * PS + c8 + i] > kBwdDiagRange;
+    // Block pairs on fp32 MFMA (exact fp32 products), each computed
+    // transposed, C^T = X^T D^T, so that output lane l holds row l % 16 and
+    // channels 4 (l / 16) .. + 3: this thread's.  Row side over the rows
+    // s < r up to the wave's block (operands scaled at row 16 I - 1: the
+    // earlier blocks' from LDS, the block's own formed here, masked to s < r),
+    // column side over the rows r > s from the wave's block on (scaled at
+    // row 16 I + 15; the block's own masked to r > s); the block index is
+    // the wave's, so the k loops are uniform.
+    {
       const int off = I == 1 ? 0 : (I == 2 ? 16 : 48);
       f32x4 aq = zero4(), aa = zero4();
-      for (int ks = 0; ks < 4 * I; ++ks) {
-        const int s = 4 * ks + lg;
+      for (int kq = 0; kq < 4 * I; ++kq) {
+        const int s = 4 * kq + lg;
         const float a = Ksc[(off + s) * PS + ln];
         aq = mf(a, dPl[(16 * I + ln) * LPC + s], aq);
         aa = mf(a, dAl[(16 * I + ln) * LPC + s], aa);
       }
 #pragma unroll
+      for (int kq = 0; kq < 4; ++kq) {
+        const int sl = 4 * kq + lg, s = 16 * I + sl;
+        const float a = inr ? ks[s * PS + ln] * __expf(gpre - gs[s * PS + ln]) : 0.f;
+        const bool lower = sl < ln;
+        aq = mf(a, lower ? dPl[(16 * I + ln) * LPC + s] : 0.f, aq);
+        aa = mf(a, lower ? dAl[(16 * I + ln) * LPC + s] : 0.f, aa);
+      }
+#pragma unroll
       for (int i = 0; i < CPT; ++i) {
-        const float sc_ = __expf(Gr[i] - gs[(16 * I - 1) * PS + c8 + i]);
+        const float sc_ = __expf(Gr[i] - (I > 0 ? gs[(16 * I - 1) * PS + c8 + i] : 0.f));
         GQ[i] = aq[i] * sc_;
         GA[i] = aa[i] * sc_;
       }
     }
-#pragma unroll 2
-    for (int s = 16 * I; s < row; ++s) {
-      const float dp = dPl[row * LPC + s], da = dAl[row * LPC + s];
-#pragma unroll
-      for (int i = 0; i < CPT; ++i) {
-        const float kE = ks[s * PS + c8 + i] * __expf(Gr[i] - gs[s * PS + c8 + i]);
-        GQ[i] += dp * kE;
-        GA[i] += da * kE;
-      }
-    }
     // column side (this thread's row is the column index s)
-    if (I < 3) {
+    {
       const int off = I == 0 ? 0 : (I == 1 ? 48 : 80);
       f32x4 a2 = zero4();
-      for (int ks = 0; ks < 12 - 4 * I; ++ks) {
-        const int rp = 4 * ks + lg, rr = 16 * I + 16 + rp;
+      for (int kq = 0; kq < 12 - 4 * I; ++kq) {
+        const int rp = 4 * kq + lg, rr = 16 * I + 16 + rp;
         a2 = mf(Xq[(off + rp) * PS + ln], dPl[rr * LPC + 16 * I + ln], a2);
         a2 = mf(Xk[(off + rp) * PS + ln], dAl[rr * LPC + 16 * I + ln], a2);
       }
 #pragma unroll
+      for (int kq = 0; kq < 4; ++kq) {
+        const int rl = 4 * kq + lg, rr = 16 * I + rl;
+        const float E = inr ? __expf(gs[rr * PS + ln] - gend) : 0.f;
+        const bool upper = rl > ln;
+        a2 = mf(qs[rr * PS + ln] * E, upper ? dPl[rr * LPC + 16 * I + ln] : 0.f, a2);
+        a2 = mf(ks[rr * PS + ln] * E, upper ? dAl[rr * LPC + 16 * I + ln] : 0.f, a2);
+      }
+#pragma unroll
       for (int i = 0; i < CPT; ++i) G2[i] = a2[i] * __expf(gs[(16 * I + 15) * PS + c8 + i] - Gr[i]);
     }
-#pragma unroll 2
-    for (int rr = row + 1; rr < 16 * I + 16; ++rr) {
-      const float dp = dPl[rr * LPC + row], da = dAl[rr * LPC + row];
+    // the block's own pairs, one by one, for the channels out of range
+    if (__ballot(bad[0] || bad[1] || bad[2] || bad[3])) {
+      for (int s = 16 * I; s < row; ++s) {
+        const float dp = dPl[row * LPC + s], da = dAl[row * LPC + s];
 #pragma unroll
-      for (int i = 0; i < CPT; ++i)
-        G2[i] += (dp * qs[rr * PS + c8 + i] + da * ks[rr * PS + c8 + i]) * __expf(gs[rr * PS + c8 + i] - Gr[i]);
+        for (int i = 0; i < CPT; ++i) {
+          if (bad[i]) {
+            const float kE = ks[s * PS + c8 + i] * __expf(Gr[i] - gs[s * PS + c8 + i]);
+            GQ[i] += dp * kE;
+            GA[i] += da * kE;
+          }
+        }
+      }
+      for (int rr = row + 1; rr < 16 * I + 16; ++rr) {
+        const float dp = dPl[rr * LPC + row], da = dAl[rr * LPC + row];
+#pragma unroll
+        for (int i = 0; i < CPT; ++i)
+          if (bad[i])
+            G2[i] += (dp * qs[rr * PS + c8 + i] + da * ks[rr * PS + c8 + i]) * __expf(gs[rr * PS + c8 + i] - Gr[i]);
+      }
     }
     // elementwise
     float dqv[CPT], dkv[CPT], dG[CPT], cs[CPT];
