@@ -1203,23 +1203,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       }
       lds_sync();
       // the raw inputs are read: the transposed planes, copied from the split
-      // rows, go over them
-      auto tput = [&](const Plane& src, const Plane& dst, int row) {
-        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(src.h + row * src.P + c4);
-        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(src.l + row * src.P + c4);
+      // rows, go over them.  A lane takes two consecutive rows (2 p, 2 p + 1)
+      // of four columns (4 q ..) and writes each column's pair as one dword;
+      // a wave covers 16 row pairs x 4 column quads, so its writes fall in
+      // distinct banks.
+      auto tput = [&](const Plane& src, const Plane& dst, int p, int q) {
+        const int r0 = 2 * p, c0 = 4 * q;
+        const bf16x4 h0 = *reinterpret_cast<const bf16x4*>(src.h + r0 * src.P + c0);
+        const bf16x4 h1 = *reinterpret_cast<const bf16x4*>(src.h + (r0 + 1) * src.P + c0);
+        const bf16x4 l0 = *reinterpret_cast<const bf16x4*>(src.l + r0 * src.P + c0);
+        const bf16x4 l1 = *reinterpret_cast<const bf16x4*>(src.l + (r0 + 1) * src.P + c0);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          dst.h[(c4 + c) * dst.P + row] = hi[c];
-          dst.l[(c4 + c) * dst.P + row] = lo[c];
+          bf16x2 hp, lp;
+          hp[0] = h0[c], hp[1] = h1[c];
+          lp[0] = l0[c], lp[1] = l1[c];
+          *reinterpret_cast<bf16x2*>(dst.h + (c0 + c) * dst.P + r0) = hp;
+          *reinterpret_cast<bf16x2*>(dst.l + (c0 + c) * dst.P + r0) = lp;
         }
       };
+      // task t of a plane with R rows: row pair 16 (t / 2) + lane % 16,
+      // column quad 4 (t % 2) + lane / 16; R / 32 * 2 tasks, wave w takes w, w + 4, ..
+      const int tl = opaque(lane);
 #pragma unroll
-      for (int i = 0; i < DK / 32; ++i) {
-        tput(S0p, S0T, (tid >> 3) + 32 * i);
-        tput(dSp, dST, (tid >> 3) + 32 * i);
+      for (int t = w; t < DK / 16; t += 4) {
+        tput(S0p, S0T, 16 * (t >> 1) + (tl & 15), 4 * (t & 1) + (tl >> 4));
+        tput(dSp, dST, 16 * (t >> 1) + (tl & 15), 4 * (t & 1) + (tl >> 4));
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i) tput(Dp, DT, (tid >> 3) + 32 * i);
+      for (int t = w; t < BC / 16; t += 4) tput(Dp, DT, 16 * (t >> 1) + (tl & 15), 4 * (t & 1) + (tl >> 4));
       lds_sync();
       // Vt, W = beta Vt (transposed) and dU (transposed) for the two 16-column tiles
       f32x4 vt[2];

@@ -8,6 +8,7 @@ namespace kda {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
@@ -24,7 +25,6 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
 // float -> bfloat16, round to nearest even (one v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f)); }
 __device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
-  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
   const bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
   return __builtin_bit_cast(uint32_t, v);
 }

@@ -140,3 +140,14 @@ def test_backward_4096_tokens_bf16():
     w = synth.make_prefill([4096], 4, 128, 128, "bf16", 16, S0_std=0.05)
     cot = synth.make_cotangents(w, 116, dS_T_std=0.1)
     compare(gpu_backward(w, cot), oracle_backward(w, cot), TOL["bf16"])
+
+
+def test_backward_varlen_many_items_bf16():
+    """Three ragged sequences (2500, 1700, 900 tokens: 82 chunks), 6 heads,
+    bf16: more (chunk, head) items than a GPU has CUs, so the persistent
+    workgroups each take several items in turn, across sequence and head
+    boundaries."""
+    log("backward: lengths [2500, 1700, 900] x 6 heads bf16")
+    w = synth.make_prefill([2500, 1700, 900], 6, 128, 128, "bf16", 17, S0_std=0.05)
+    cot = synth.make_cotangents(w, 117, dS_T_std=0.1)
+    compare(gpu_backward(w, cot), oracle_backward(w, cot), TOL["bf16"])
