@@ -710,13 +710,17 @@ __device__ __forceinline__ void bwd_state_body(int x, const T* __restrict__ v, c
 #pragma unroll
       for (int m = 0; m < 4; ++m) o.gam[t][m] = bk[B::oGam + 16 * (w * TPW + t) + 4 * g + m];
   };
-  Ops cur, nxt;
+  // Two operand sets used in turn (the loop is unrolled by two), so chunk
+  // c + 1's operands stay in the registers they were loaded into: with one
+  // set copied into the other at the end of every chunk, the copy would wait
+  // there for the loads issued in the chunk's last phase.
+  Ops opa, opb;
   if (nch > 0) {
-    load_a(0, cur);
-    load_b(0, cur);
-    load_c(0, cur);
+    load_a(0, opa);
+    load_b(0, opa);
+    load_c(0, opa);
   }
-  for (int c = 0; c < nch; ++c) {
+  auto step = [&](int c, const Ops& cur, Ops& nxt) {
     const bool more = c + 1 < nch;
     float* so = sc + (static_cast<size_t>(j0 + c) * H + h) * DK * DV;
 #pragma unroll
@@ -761,7 +765,10 @@ __device__ __forceinline__ void bwd_state_body(int x, const T* __restrict__ v, c
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) X[t][hf] = mm3(cur.kbt[t][kk], UT.frag(16 * hf + r, 32 * kk + 8 * g), X[t][hf]);
       }
-    cur = nxt;
+  };
+  for (int c = 0; c < nch; c += 2) {
+    step(c, opa, opb);
+    if (c + 1 < nch) step(c + 1, opb, opa);
   }
 }
 
@@ -846,13 +853,14 @@ __device__ __forceinline__ void bwd_dstate_body(int x, const T* __restrict__ dO,
 #pragma unroll
       for (int m = 0; m < 4; ++m) o.gam[t][m] = bk[B::oGam + 16 * (w * TPW + t) + 4 * g + m];
   };
-  Ops cur, nxt;
+  // two operand sets used in turn, as in the state pass
+  Ops opa, opb;
   if (nch > 0) {
-    load_a(nch - 1, cur);
-    load_b(nch - 1, cur);
-    load_c(nch - 1, cur);
+    load_a(nch - 1, opa);
+    load_b(nch - 1, opa);
+    load_c(nch - 1, opa);
   }
-  for (int c = nch - 1; c >= 0; --c) {
+  auto step = [&](int c, const Ops& cur, Ops& nxt) {
     const bool more = c > 0;
     float* so = dsc + (static_cast<size_t>(j0 + c) * H + h) * DK * DV;
     lds_sync();  // the previous chunk's readers of DT and YT are done
@@ -906,7 +914,10 @@ __device__ __forceinline__ void bwd_dstate_body(int x, const T* __restrict__ dO,
           X[t][hf] = mm3(cur.kgt[t][kk], YT.frag(16 * hf + r, 32 * kk + 8 * g), X[t][hf]);
         }
       }
-    cur = nxt;
+  };
+  for (int c = nch - 1; c >= 0; c -= 2) {
+    step(c, opa, opb);
+    if (c > 0) step(c - 1, opb, opa);
   }
   if (dS0) {
 #pragma unroll
