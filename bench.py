@@ -12,7 +12,8 @@ the call rates of the 4 x 4096-token batch and of the 64-sequence varlen
 workload follow under "prefill_other" (skip with --no-other), and the
 backward pass (kda_prefill_backward) on the 4 x 4096-token batch, checked
 against the oracle's backward, and on the long workload under "backward"
-(skip with --no-backward).
+(skip with --no-backward).  "prefill_other" also times the long and varlen
+workloads under the bounded-workspace schedule inside 1 GiB.
 
 Prints ONE JSON line.  `value` is prefill tokens/s.  Each roofline block
 prices the operator's algorithmic bytes per launch against MI355X's 8 TB/s
@@ -213,11 +214,12 @@ def run_prefill(args, torch, kda, synth, oracle):
     return res
 
 
-def run_prefill_rate(wname, args, torch, kda, synth, stages=False):
+def run_prefill_rate(wname, args, torch, kda, synth, stages=False, bounded=None):
     """Call time and rate of another prefill workload (no CPU baseline):
     context for the main line, which times the 131072-token workload.  With
     ``stages`` every input and output stage runs (raw q and k, the gate
-    projection's output, RMSNorm and the sigmoid output gate)."""
+    projection's output, RMSNorm and the sigmoid output gate).  ``bounded``
+    (bytes) runs the bounded-workspace schedule inside that much workspace."""
     w = synth.workload_prefill(wname)
     stage_kw = {}
     if stages:
@@ -246,20 +248,26 @@ def run_prefill_rate(wname, args, torch, kda, synth, stages=False):
     ST = torch.empty((N, H, dk, dv), dtype=torch.float32, device="cuda")
     host_cu = w.cu_seqlens.tolist()
     stream = torch.cuda.current_stream()
+    if bounded:
+        kda.clear_workspace_cache()  # the bounded call gets a workspace of its own size
+        torch.cuda.empty_cache()
     for _ in range(2):
         kda.prefill(q, k, v, la, b, cu, S0, o=o, S_T=ST, cu_seqlens_host=host_cu, chunk=w.chunk,
-                    one_stream=args.one_stream, **stage_kw)
+                    one_stream=args.one_stream, max_workspace_bytes=bounded, **stage_kw)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     n = 5
     e0.record(stream)
     for _ in range(n):
         kda.prefill(q, k, v, la, b, cu, S0, o=o, S_T=ST, cu_seqlens_host=host_cu, chunk=w.chunk,
-                    one_stream=args.one_stream, **stage_kw)
+                    one_stream=args.one_stream, max_workspace_bytes=bounded, **stage_kw)
     e1.record(stream)
     torch.cuda.synchronize()
     call_s = e0.elapsed_time(e1) / n / 1e3
-    recovered = kda.prefill_recovered(q, v, cu, chunk=w.chunk, cu_seqlens_host=host_cu, one_stream=args.one_stream)
+    recovered = kda.prefill_recovered(q, v, cu, chunk=w.chunk, cu_seqlens_host=host_cu, one_stream=args.one_stream,
+                                      max_workspace_bytes=bounded)
+    if bounded:
+        kda.clear_workspace_cache()
     nbytes, _, per_th, _ = prefill_algorithmic(T_tok, N, H, dk, dv, 2 if bf else 4, w.chunk, S0 is not None, w.gate)
     if stages:  # the output gate's pre-activation is read once more per token-head
         nbytes += T_tok * H * dv * (2 if bf else 4)
@@ -267,8 +275,9 @@ def run_prefill_rate(wname, args, torch, kda, synth, stages=False):
     del q, k, v, la, b, o, ST, S0, stage_kw
     torch.cuda.empty_cache()
     achieved = nbytes / call_s / 1e9
-    return dict(workload=wname + ("+stages" if stages else ""), gate=w.gate, num_seqs=N, total_tokens=T_tok, heads=H,
-                call_ms=round(call_s * 1e3, 4), tokens_per_s=round(T_tok / call_s, 1),
+    label = wname + ("+stages" if stages else "") + ("+bounded%dMiB" % (bounded >> 20) if bounded else "")
+    return dict(workload=label, gate=w.gate, num_seqs=N, total_tokens=T_tok, heads=H,
+                workspace_limit_bytes=bounded, call_ms=round(call_s * 1e3, 4), tokens_per_s=round(T_tok / call_s, 1),
                 hbm_frac=round(achieved / HBM_PEAK_GBS, 4), recovered=recovered,
                 roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                               frac=round(achieved / HBM_PEAK_GBS, 4), bytes_per_launch=int(nbytes),
@@ -521,6 +530,9 @@ def main():
                                                 "long131072_bf16_deltanet")]
     if not args.no_other:
         other.append(run_prefill_rate("long131072_bf16", args, torch, kda, synth, stages=True))
+        # the bounded-workspace schedule inside 1 GiB (the one-stream workspace is 4.1 GB and 13.2 GB)
+        other += [run_prefill_rate(n, args, torch, kda, synth, bounded=1 << 30)
+                  for n in ("long131072_bf16", "varlen64_bf16")]
     dec_gates = [] if (args.no_decode or args.no_other) else [
         run_decode(args, torch, kda, synth, None, gate=g, steps=min(256, args.decode_steps)) for g in ("scalar", "none")]
     if dec_gates:

@@ -29,6 +29,7 @@ KDA_ERR_DEVICE = 4
 KDA_F32 = 0
 KDA_BF16 = 1
 KDA_PREFILL_ONE_STREAM = 1
+KDA_PREFILL_BOUNDED = 2
 KDA_GATE_CHANNEL = 0
 KDA_GATE_SCALAR = 1
 KDA_GATE_NONE = 2
@@ -238,7 +239,7 @@ def clear_workspace_cache():
 
 def prefill(q, k, v, log_alpha, beta, cu_seqlens, S0=None, *, chunk: int = 64, o=None, S_T=None,
             cu_seqlens_host: Optional[Sequence[int]] = None, workspace=None, stream=None, want_state: bool = True,
-            one_stream: bool = False, **stage_kw):
+            one_stream: bool = False, max_workspace_bytes: Optional[int] = None, **stage_kw):
     """KDA chunked prefill over a packed batch.
 
     q, k: [T, H, dk]; v: [T, H, dv] (bf16 or fp32, same dtype); log_alpha: [T, H, dk]
@@ -246,6 +247,9 @@ def prefill(q, k, v, log_alpha, beta, cu_seqlens, S0=None, *, chunk: int = 64, o
     None.  Returns (o, S_T); S_T is None when ``want_state`` is False.
     ``S_T`` may be passed as ``S0`` to update the state in place.
     ``one_stream`` selects the schedule that never leaves the caller's stream.
+    ``max_workspace_bytes`` selects the bounded schedule (KDA_PREFILL_BOUNDED):
+    the library uses at most that many workspace bytes, whatever the token
+    count, taking the chunks in segments that fit.
     ``log_alpha`` may also be [T, H] (one rate per head: Gated DeltaNet) or
     None (no forget gate: DeltaNet).  Stage keywords (kda_stages):
     ``l2norm_qk``, ``gate_softplus`` (log_alpha then holds the gate
@@ -270,12 +274,20 @@ def prefill(q, k, v, log_alpha, beta, cu_seqlens, S0=None, *, chunk: int = 64, o
     s = _stream(stream)
     gate = _gate(log_alpha, (T, H))
     stg = _stages((T, H, dv), q.dtype, dev, **stage_kw)
-    desc, keep = make_desc(N, T, H, dk, dv, chunk, dt, cu_seqlens_host,
-                           KDA_PREFILL_ONE_STREAM if one_stream else 0, gate, stg)
+    flags = (KDA_PREFILL_ONE_STREAM if one_stream else 0) | (KDA_PREFILL_BOUNDED if max_workspace_bytes else 0)
+    desc, keep = make_desc(N, T, H, dk, dv, chunk, dt, cu_seqlens_host, flags, gate, stg)
     need = int(lib.kda_prefill_workspace_size(ctypes.byref(desc)))
     if need == 0:
         st = lib.kda_prefill(ctypes.byref(desc), *([None] * 10), 0, None)
         raise KdaError(st if st != KDA_OK else KDA_ERR_INVALID_ARGUMENT, "kda_prefill_workspace_size")
+    if max_workspace_bytes:
+        if need > max_workspace_bytes:
+            raise KdaError(KDA_ERR_WORKSPACE_TOO_SMALL, "kda_prefill (bounded: %d bytes at least)" % need)
+        # beyond the one-stream schedule's workspace (plus the carried
+        # states) a longer segment gains nothing
+        one, keep1 = make_desc(N, T, H, dk, dv, chunk, dt, cu_seqlens_host, KDA_PREFILL_ONE_STREAM, gate, stg)
+        full = int(lib.kda_prefill_workspace_size(ctypes.byref(one))) + N * H * dk * dv * 4 + 256
+        need = min(int(max_workspace_bytes) // 256 * 256, full)
     ptrs = (_dev_ptr(q, "q", None, (T, H, dk), dev), _dev_ptr(k, "k", None, (T, H, dk), dev),
             _dev_ptr(v, "v", None, (T, H, dv), dev),
             _dev_ptr(log_alpha, "log_alpha", torch.float32, _la_shape(gate, (T, H), dk), dev),
@@ -287,8 +299,10 @@ def prefill(q, k, v, log_alpha, beta, cu_seqlens, S0=None, *, chunk: int = 64, o
     if workspace is None:
         workspace = _workspace(dev, s, need)
     wptr = _dev_ptr(workspace, "workspace", None, None, dev)
-    st = lib.kda_prefill(ctypes.byref(desc), *ptrs, wptr, workspace.numel() * workspace.element_size(),
-                         s.cuda_stream)
+    wbytes = workspace.numel() * workspace.element_size()
+    if max_workspace_bytes:
+        wbytes = min(wbytes, need)
+    st = lib.kda_prefill(ctypes.byref(desc), *ptrs, wptr, wbytes, s.cuda_stream)
     del keep
     if st != KDA_OK:
         raise KdaError(st, "kda_prefill")
@@ -338,11 +352,15 @@ def prefill_noalloc(q, k, v, log_alpha, beta, cu_seqlens, S0=None, *, chunk: int
 
 
 def prefill_recovered(q, v, cu_seqlens, *, chunk: int = 64, cu_seqlens_host=None, workspace=None, stream=None,
-                      one_stream: bool = False) -> bool:
+                      one_stream: bool = False, max_workspace_bytes: Optional[int] = None) -> bool:
     """Whether the last prefill call with these shapes on ``stream`` (using
     ``workspace``, or the binding's cached one for that stream) stopped
     waiting in its overlapped schedule and recomputed its outputs on the
-    caller's stream.  Synchronises the stream."""
+    caller's stream.  Synchronises the stream.  Pass the call's
+    ``one_stream`` and ``max_workspace_bytes``: those schedules never wait
+    (False without a look at the workspace)."""
+    if max_workspace_bytes:
+        return False
     lib = load_library()
     T, H, dk = q.shape
     dv = v.shape[2]

@@ -42,7 +42,7 @@ kda_status check_desc(const kda_prefill_desc* d, int64_t* max_chunks) {
   if (!dims_supported(d->dk, d->dv)) return KDA_ERR_UNSUPPORTED;
   if (d->chunk != 16 && d->chunk != 32 && d->chunk != 64) return KDA_ERR_UNSUPPORTED;
   if (d->num_seqs == 0 && d->total_tokens != 0) return KDA_ERR_INVALID_ARGUMENT;
-  if (d->flags & ~static_cast<uint32_t>(KDA_PREFILL_ONE_STREAM)) return KDA_ERR_INVALID_ARGUMENT;
+  if (d->flags & ~static_cast<uint32_t>(KDA_PREFILL_ONE_STREAM | KDA_PREFILL_BOUNDED)) return KDA_ERR_INVALID_ARGUMENT;
   const int64_t CL = d->chunk;                 // tokens per chunk
   const int64_t C = d->chunk < 32 ? 32 : d->chunk;  // rows of the kernels' chunk tiles
   // one chunk of rows of any per-token tensor must span fewer than 2^31
@@ -87,7 +87,13 @@ kda_status prefill_checked(const kda_prefill_desc* d, const void* q, const void*
   if (T > 0 && (!q || !k || !v || (gw && !log_alpha) || !beta || !o)) return KDA_ERR_INVALID_ARGUMENT;
   if (!workspace) return KDA_ERR_INVALID_ARGUMENT;
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return KDA_ERR_INVALID_ARGUMENT;
-  if (workspace_bytes < p.total_bytes) return KDA_ERR_WORKSPACE_TOO_SMALL;
+  if (d->flags & KDA_PREFILL_BOUNDED) {
+    // segments as long as the given workspace allows (the carried states in
+    // S_T when the caller wants it, else in the workspace)
+    if (!make_bounded_plan(d, mc, workspace_bytes, S_T == nullptr, &p)) return KDA_ERR_WORKSPACE_TOO_SMALL;
+  } else if (workspace_bytes < p.total_bytes) {
+    return KDA_ERR_WORKSPACE_TOO_SMALL;
+  }
   const size_t state_bytes = static_cast<size_t>(d->num_seqs) * H * d->dk * d->dv * 4;
   const Range rq = range(q, T * H * d->dk * es), rk = range(k, T * H * d->dk * es),
               rv = range(v, T * H * d->dv * es), rla = range(log_alpha, log_alpha ? T * H * gw * 4 : 0),
@@ -138,6 +144,7 @@ int32_t kda_version(void) { return 20100; }
 size_t kda_prefill_workspace_size(const kda_prefill_desc* d) {
   int64_t mc = 0;
   if (check_desc(d, &mc) != KDA_OK) return 0;
+  if (d->flags & KDA_PREFILL_BOUNDED) return kda::bounded_min_bytes(d, mc);
   kda::PrefillPlan p;
   if (!kda::make_prefill_plan(d, mc, &p)) return 0;
   return p.total_bytes;

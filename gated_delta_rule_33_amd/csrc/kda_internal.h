@@ -35,10 +35,24 @@ struct PrefillPlan {
   // Segment length in global chunk indices for the overlapped two-stream
   // schedule (0: one prep launch, then one scan launch).
   int64_t seg;
+  // Bounded schedule (bseg > 0): segments of bseg global chunk indices, each
+  // prepared into the one block area and then passed over by the state
+  // pass, which resumes every (sequence, head) from the state the previous
+  // segment left; that state is kept at off_bcarry (0: in S_T).
+  int64_t bseg;
+  size_t off_bcarry;
 };
 
 // Returns false when the shape is unsupported.
 bool make_prefill_plan(const kda_prefill_desc* d, int64_t max_chunks, PrefillPlan* p);
+// Plan of the bounded schedule inside workspace_bytes (the carried states in
+// the workspace when carry_in_ws, else in S_T); false if not even one chunk
+// index per segment fits.
+bool make_bounded_plan(const kda_prefill_desc* d, int64_t max_chunks, size_t workspace_bytes, bool carry_in_ws,
+                       PrefillPlan* p);
+// Smallest workspace of the bounded schedule (room for the carried states
+// included).
+size_t bounded_min_bytes(const kda_prefill_desc* d, int64_t max_chunks);
 
 // Test hook behind kda_prefill_set_wait_limit: polls > 0 sets the bound of
 // the overlapped schedule's wait, 0 makes it never wait, < 0 restores the

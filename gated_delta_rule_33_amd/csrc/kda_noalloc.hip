@@ -50,7 +50,10 @@ extern "C" kda_status kda_prefill_noalloc(const kda_prefill_desc* d, const void*
   one.flags |= KDA_PREFILL_ONE_STREAM;
   const size_t need = kda_prefill_workspace_size(&one);
   if (need == 0) return kda_prefill(&one, q, k, v, log_alpha, beta, cu_seqlens, S0, o, S_T, nullptr, 0, stream);
-  if (need > KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_WORKSPACE_TOO_SMALL;
+  // larger problems run the bounded schedule, in segments that fit the
+  // array; the call is refused (KDA_ERR_WORKSPACE_TOO_SMALL, nothing
+  // launched) only when not even one chunk index per segment fits
+  if (need > KDA_NOALLOC_SCRATCH_BYTES) one.flags |= KDA_PREFILL_BOUNDED;
   if (one.num_seqs == 0) return KDA_OK;
   void* ws = nullptr;
   if (scratch_ptr(&ws) != hipSuccess) return KDA_ERR_DEVICE;

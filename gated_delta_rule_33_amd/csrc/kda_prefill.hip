@@ -1295,7 +1295,8 @@ template <typename T, int C, int DK, int DV, int WAVES>
 __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel(
     const T* __restrict__ v, const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_off,
     const int32_t* __restrict__ order, int N, int H, const unsigned char* __restrict__ ws, const float* S0,
-    T* __restrict__ o, float* S_T, int* ready, int seg, int wait_polls, const int* guard, int cl) {
+    T* __restrict__ o, float* S_T, int* ready, int seg, int wait_polls, const int* guard, int cl, float* carry,
+    int gb, int ge) {
   typedef Blk<T, C, DK> B;
   typedef mma16<T> M;
   typedef accb<T> AB;
@@ -1333,12 +1334,23 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
   const int tbeg = cu[seq], L_seq = cu[seq + 1] - tbeg;
   const int c0 = chunk_off[seq];
   const int nch = (L_seq + cl - 1) / cl;
-  // The whole sequence, chunks [cb, ce).  When `ready` is given, the blocks
-  // of global chunks [j seg, (j + 1) seg) exist once *ready >= j (segment 0
-  // from the start): the loader waves wait for that before they touch them.
-  const int cb = 0, ce = nch;
+  // The sequence's chunks [cb, ce): all of them, or with `carry` (bounded
+  // schedule) those among global chunks [gb, ge), starting from the state
+  // the previous segment left in `carry` unless the sequence starts here and
+  // leaving it there unless the sequence ends here.  When `ready` is given,
+  // the blocks of global chunks [j seg, (j + 1) seg) exist once *ready >= j
+  // (segment 0 from the start): the loader waves wait for that before they
+  // touch them.
+  int cb = 0, ce = nch;
   const float* s_in = S0;
   float* s_out = S_T;
+  if (carry) {
+    cb = min(max(gb - c0, 0), nch);
+    ce = min(max(ge - c0, 0), nch);
+    if (cb == ce && !(nch == 0 && gb == 0)) return;  // nothing of this sequence in the segment
+    if (cb > 0) s_in = carry;
+    if (ce < nch) s_out = carry;
+  }
 
   // Loader waves: `upto` is the last chunk of this sequence (index relative
   // to it) whose segment the counter showed as written when last read
@@ -1927,7 +1939,7 @@ bool make_prefill_plan(const kda_prefill_desc* d, int64_t max_chunks, PrefillPla
   p->seg = 0;
   p->off_ready = 0;
   p->off_carry = 0;
-  if (!(d->flags & KDA_PREFILL_ONE_STREAM) && narrow_scan_wgs(d->num_seqs, d->num_heads, d->dv) <= kPipeMaxScanWgs &&
+  if (!(d->flags & (KDA_PREFILL_ONE_STREAM | KDA_PREFILL_BOUNDED)) && narrow_scan_wgs(d->num_seqs, d->num_heads, d->dv) <= kPipeMaxScanWgs &&
       max_chunks >= 2 * kPipeMinSeg) {
     const int64_t seg = (max_chunks + kPipeMaxSegs - 1) / kPipeMaxSegs;
     p->seg = seg > kPipeMinSeg ? seg : kPipeMinSeg;
@@ -1939,7 +1951,39 @@ bool make_prefill_plan(const kda_prefill_desc* d, int64_t max_chunks, PrefillPla
     off = align256(off + static_cast<size_t>(d->num_seqs) * d->num_heads * d->dk * d->dv * 4);
   }
   p->total_bytes = align256(off);
+  p->bseg = 0;
+  p->off_bcarry = 0;
   return true;
+}
+
+bool make_bounded_plan(const kda_prefill_desc* d, int64_t max_chunks, size_t workspace_bytes, bool carry_in_ws,
+                       PrefillPlan* p) {
+  kda_prefill_desc one = *d;
+  one.flags |= KDA_PREFILL_ONE_STREAM;
+  if (!make_prefill_plan(&one, max_chunks, p)) return false;
+  const size_t chunk_bytes = static_cast<size_t>(d->num_heads) * block_bytes(d->io_dtype, p->C, d->dk);
+  const size_t carry =
+      carry_in_ws ? align256(static_cast<size_t>(d->num_seqs) * d->num_heads * d->dk * d->dv * 4) : 0;
+  if (max_chunks < 1) return true;  // nothing to segment: the one-stream plan
+  if (workspace_bytes < p->off_blocks + carry + chunk_bytes) return false;
+  int64_t seg = static_cast<int64_t>((workspace_bytes - p->off_blocks - carry) / chunk_bytes);
+  if (seg > max_chunks) seg = max_chunks;
+  p->bseg = seg;
+  // the block area ends on a 1024-byte boundary (off_blocks and chunk_bytes are multiples)
+  const size_t end = p->off_blocks + static_cast<size_t>(seg) * chunk_bytes;
+  p->off_bcarry = carry ? end : 0;
+  p->total_bytes = end + carry;
+  return true;
+}
+
+size_t bounded_min_bytes(const kda_prefill_desc* d, int64_t max_chunks) {
+  PrefillPlan p;
+  kda_prefill_desc one = *d;
+  one.flags |= KDA_PREFILL_ONE_STREAM;
+  if (!make_prefill_plan(&one, max_chunks, &p)) return 0;
+  if (max_chunks < 1) return p.total_bytes;
+  return p.off_blocks + static_cast<size_t>(d->num_heads) * block_bytes(d->io_dtype, p.C, d->dk) +
+         align256(static_cast<size_t>(d->num_seqs) * d->num_heads * d->dk * d->dv * 4);
 }
 
 // Polls (each about a microsecond) a scan loader wave of the overlapped
@@ -1957,7 +2001,8 @@ template <typename T, int C, int DK, int DV, int WAVES>
 static hipError_t launch_scan(const PrefillPlan& p, const void* v, const int32_t* cu, const int32_t* chunk_off,
                               const int32_t* order, const unsigned char* blocks, const float* S0, void* o,
                               float* S_T, hipStream_t st, int* ready = nullptr, int seg = 1,
-                              const int* guard = nullptr) {
+                              const int* guard = nullptr, float* carry = nullptr, int64_t gb = 0,
+                              int64_t ge = 0) {
   typedef ScanLds<T, C, DK, 16 * WAVES> SL;
   static_assert(SL::total <= 160 * 1024, "scan LDS");
   hipError_t e = set_lds_limit(reinterpret_cast<const void*>(&scan_kernel<T, C, DK, DV, WAVES>), SL::total);
@@ -1967,7 +2012,8 @@ static hipError_t launch_scan(const PrefillPlan& p, const void* v, const int32_t
   const unsigned grid = static_cast<unsigned>((pairs + 7) / 8 * 8 * nsplit);
   hipLaunchKernelGGL((scan_kernel<T, C, DK, DV, WAVES>), dim3(grid), dim3(scan_threads<T, C, DK, WAVES>()), SL::total, st,
                      static_cast<const T*>(v), cu, chunk_off, order, p.N, p.H, blocks, S0, static_cast<T*>(o), S_T,
-                     ready, seg, prefill_wait_polls(), guard, p.CL);
+                     ready, seg, prefill_wait_polls(), guard, p.CL, carry, static_cast<int>(gb),
+                     static_cast<int>(ge));
   return hipGetLastError();
 }
 
@@ -2092,7 +2138,7 @@ static hipError_t launch_prefill_t(const PrefillPlan& p, const void* q, const vo
   // Persistent prep: as many workgroups as fit on the CUs the stream may
   // use (LDS-limited), each walking (chunk, head) items.
   auto prep = [&](int64_t cbase, int64_t count, hipStream_t s, int cus, int32_t* publish, int published,
-                  const int* guard) -> hipError_t {
+                  const int* guard, unsigned char* blks) -> hipError_t {
     hipError_t r = set_lds_limit(reinterpret_cast<const void*>(&prep_kernel<T, C, DK, G, IN>), lp);
     if (r != hipSuccess) return r;
     const int64_t per_cu = (160 * 1024) / static_cast<int64_t>(lp) > 0 ? (160 * 1024) / static_cast<int64_t>(lp) : 1;
@@ -2100,7 +2146,7 @@ static hipError_t launch_prefill_t(const PrefillPlan& p, const void* q, const vo
     const int64_t grid = items < per_cu * cus ? items : per_cu * cus;
     hipLaunchKernelGGL((prep_kernel<T, C, DK, G, IN>), dim3(static_cast<unsigned>(grid)), dim3(kPrepThreads), lp, s,
                        static_cast<const T*>(q), static_cast<const T*>(k), la, beta, cu, chunk_off, p.N, p.H,
-                       blocks, static_cast<int>(cbase), static_cast<int>(count), publish, published, guard, p.CL,
+                       blks, static_cast<int>(cbase), static_cast<int>(count), publish, published, guard, p.CL,
                        p.l2norm_qk, p.l2norm_eps, p.gate_softplus);
     return hipGetLastError();
   };
@@ -2128,7 +2174,7 @@ static hipError_t launch_prefill_t(const PrefillPlan& p, const void* q, const vo
     const int* flag = ready + 1;
     {
       std::lock_guard<std::mutex> lock(ps->mu);
-      e = prep(0, p.seg < p.max_chunks ? p.seg : p.max_chunks, st, cus, nullptr, 0, nullptr);
+      e = prep(0, p.seg < p.max_chunks ? p.seg : p.max_chunks, st, cus, nullptr, 0, nullptr, blocks);
       if (e != hipSuccess) return e;
       if ((e = hipEventRecord(ps->fork, st)) != hipSuccess) return e;
       if ((e = hipStreamWaitEvent(ps->prep, ps->fork, 0)) != hipSuccess) return e;
@@ -2139,7 +2185,7 @@ static hipError_t launch_prefill_t(const PrefillPlan& p, const void* q, const vo
       for (int64_t j = 1; j < nseg; ++j) {
         const int64_t c0 = j * p.seg, c1 = c0 + p.seg < p.max_chunks ? c0 + p.seg : p.max_chunks;
         if ((e = prep(c0, c1 - c0, ps->prep, cus - ps->scan_cus, j > 1 ? ready : nullptr, static_cast<int>(j - 1),
-                      nullptr)) != hipSuccess)
+                      nullptr, blocks)) != hipSuccess)
           return e;
       }
       hipLaunchKernelGGL(ready_kernel, dim3(1), dim3(64), 0, ps->prep, ready, static_cast<int>(nseg - 1));
@@ -2157,16 +2203,36 @@ static hipError_t launch_prefill_t(const PrefillPlan& p, const void* q, const vo
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     // recovery (runs only if the flag word is set)
-    if ((e = prep(0, p.max_chunks, st, cus, nullptr, 0, flag)) != hipSuccess) return e;
+    if ((e = prep(0, p.max_chunks, st, cus, nullptr, 0, flag, blocks)) != hipSuccess) return e;
     return launch_scan<T, C, DK, DV, 2>(p, v, cu, chunk_off, order, blocks, S0, o, S_T, st, nullptr, 1, flag);
-  }
-  if (p.max_chunks > 0) {
-    e = prep(0, p.max_chunks, st, cus, nullptr, 0, nullptr);
-    if (e != hipSuccess) return e;
   }
   // Few (sequence, head) pairs: narrower value tiles to put more CUs on the
   // serial pass; many pairs: wider tiles to load each chunk block fewer times.
   const long wide_wgs = static_cast<long>(p.N) * p.H * (DV / 64);
+  if (p.bseg > 0) {
+    // Bounded schedule: segment by segment of global chunk indices, the
+    // prep fills the one block area (addressed as if it started at the
+    // segment's first chunk) and the state pass resumes every (sequence,
+    // head) from the state in `carry`; stream order separates the launches.
+    float* carry = p.off_bcarry ? reinterpret_cast<float*>(w + p.off_bcarry) : S_T;
+    const size_t chunk_bytes = static_cast<size_t>(p.H) * Blk<T, C, DK>::bytes;
+    for (int64_t gb = 0; gb < p.max_chunks; gb += p.bseg) {
+      const int64_t ge = gb + p.bseg < p.max_chunks ? gb + p.bseg : p.max_chunks;
+      unsigned char* seg_blocks =
+          reinterpret_cast<unsigned char*>(reinterpret_cast<uintptr_t>(blocks) - static_cast<uintptr_t>(gb) * chunk_bytes);
+      if ((e = prep(gb, ge - gb, st, cus, nullptr, 0, nullptr, seg_blocks)) != hipSuccess) return e;
+      e = wide_wgs < 512 ? launch_scan<T, C, DK, DV, 2>(p, v, cu, chunk_off, order, seg_blocks, S0, o, S_T, st, nullptr,
+                                                         1, nullptr, carry, gb, ge)
+                         : launch_scan<T, C, DK, DV, 4>(p, v, cu, chunk_off, order, seg_blocks, S0, o, S_T, st, nullptr,
+                                                         1, nullptr, carry, gb, ge);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  if (p.max_chunks > 0) {
+    e = prep(0, p.max_chunks, st, cus, nullptr, 0, nullptr, blocks);
+    if (e != hipSuccess) return e;
+  }
   if (wide_wgs < 512) return launch_scan<T, C, DK, DV, 2>(p, v, cu, chunk_off, order, blocks, S0, o, S_T, st);
   return launch_scan<T, C, DK, DV, 4>(p, v, cu, chunk_off, order, blocks, S0, o, S_T, st);
 }

@@ -103,7 +103,20 @@ enum {
      caller's stream, never on the library's two CU-masked streams (for tools
      that serialise kernel dispatches, such as hardware-counter collection;
      results are identical, and the workspace is smaller). */
-  KDA_PREFILL_ONE_STREAM = 1
+  KDA_PREFILL_ONE_STREAM = 1,
+  /* Bounded workspace: kda_prefill_workspace_size returns the smallest
+     workspace kda_prefill then accepts (the chunk table, the blocks of one
+     chunk index for every head, and room for N*H*dk*dv fp32 carried states),
+     and kda_prefill takes the chunks in segments of global chunk indices as
+     long as the workspace it is given allows: each segment is prepared into
+     the one block area, then the state pass resumes every (sequence, head)
+     from the state the previous segment left (kept in S_T, or in the
+     workspace when S_T is NULL), all on `stream`.  The workspace need not
+     grow with the number of tokens; results are bit-identical to
+     KDA_PREFILL_ONE_STREAM, which is what a workspace of at least that
+     flag's size amounts to (one segment).  Shorter segments cost time: each
+     segment's state pass waits for the longest chain in it. */
+  KDA_PREFILL_BOUNDED = 2
 };
 
 /* Problem description for the packed variable-length prefill. */
@@ -154,6 +167,8 @@ size_t kda_prefill_workspace_size(const kda_prefill_desc* desc);
  *                              other overlap between buffers is invalid.
  *   workspace  >= kda_prefill_workspace_size(desc) bytes, 256-byte aligned;
  *              its contents on entry are ignored and on return undefined.
+ *              With KDA_PREFILL_BOUNDED, workspace_bytes sets the segment
+ *              length (see the flag).
  *   stream     hipStream_t or NULL.
  *   desc->stages  optional input/output stages (kda_stages): with an output
  *              stage, o holds its result (the stage runs as one more pass over
@@ -190,14 +205,18 @@ kda_status kda_prefill(const kda_prefill_desc* desc,
  * The workspace is a static device array of KDA_NOALLOC_SCRATCH_BYTES that
  * the library holds on every GPU it runs on until the process ends; the call
  * allocates nothing.  It always runs the one-stream schedule (only kernel
- * launches on `stream`).  Arguments and results as for kda_prefill.
- * Every call on one GPU shares that GPU's array: calls that overlap on one
- * GPU (other streams, other threads) race on it and must not be issued.
- * Errors: as kda_prefill, and KDA_ERR_WORKSPACE_TOO_SMALL when the problem
- * needs more than KDA_NOALLOC_SCRATCH_BYTES, i.e. when
- * kda_prefill_workspace_size of `desc` with KDA_PREFILL_ONE_STREAM set is
- * larger (about 976 bytes per token and head for bf16, dk = 128, chunk 64:
- * e.g. 8,000 tokens x 32 heads fit).
+ * launches on `stream`); a problem whose one-stream workspace
+ * (kda_prefill_workspace_size with KDA_PREFILL_ONE_STREAM: about 976 bytes
+ * per token and head for bf16, dk = 128, chunk 64, so about 8,000 tokens x
+ * 32 heads) exceeds the array runs the bounded schedule of
+ * KDA_PREFILL_BOUNDED inside it, with identical results.  Arguments and
+ * results as for kda_prefill.  Every call on one GPU shares that GPU's
+ * array: calls that overlap on one GPU (other streams, other threads) race
+ * on it and must not be issued.  Errors: as kda_prefill, and
+ * KDA_ERR_WORKSPACE_TOO_SMALL (nothing launched) when not even the bounded
+ * schedule fits: the blocks of one chunk index for every head (about 61 KB
+ * per head) plus, when S_T is NULL, the N*H*dk*dv fp32 carried states, more
+ * than the array holds.
  */
 #define KDA_NOALLOC_SCRATCH_BYTES (256u << 20)
 kda_status kda_prefill_noalloc(const kda_prefill_desc* desc,

@@ -51,7 +51,8 @@ def rel_err(x: np.ndarray, ref: np.ndarray) -> float:
 
 
 def gpu_prefill(w: synth.PrefillInputs, chunk: int = None, S0=None, in_place: bool = False, host_offsets=True,
-                one_stream: bool = False, want_state: bool = True, report: dict = None, **stage_kw):
+                one_stream: bool = False, want_state: bool = True, report: dict = None, max_workspace_bytes=None,
+                **stage_kw):
     """Run libkda prefill on the inputs; returns (o, S_T) as float64 numpy
     (S_T None when want_state is False).  When ``report`` is a dict, its key
     "recovered" is set to whether the call's overlapped schedule recovered."""
@@ -70,11 +71,12 @@ def gpu_prefill(w: synth.PrefillInputs, chunk: int = None, S0=None, in_place: bo
         kw["S_T"] = s0d
     host_cu = w.cu_seqlens.tolist() if host_offsets else None
     o, ST = kda.prefill(q, k, v, la, b, cu, s0d, chunk=chunk or w.chunk, cu_seqlens_host=host_cu,
-                        one_stream=one_stream, want_state=want_state, **kw, **stage_kw)
+                        one_stream=one_stream, want_state=want_state, max_workspace_bytes=max_workspace_bytes,
+                        **kw, **stage_kw)
     torch.cuda.synchronize()
     if report is not None:
         report["recovered"] = kda.prefill_recovered(q, v, cu, chunk=chunk or w.chunk, cu_seqlens_host=host_cu,
-                                                    one_stream=one_stream)
+                                                    one_stream=one_stream, max_workspace_bytes=max_workspace_bytes)
     return host(o), (host(ST) if ST is not None else None)
 
 

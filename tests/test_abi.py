@@ -51,7 +51,7 @@ def test_workspace_size():
     assert 0 < exact <= bound
     for bad in (dict(dk=96), dict(chunk=48), dict(num_heads=0), dict(total_tokens=-1), dict(io_dtype=7),
                 dict(cu_seqlens_host=[0, 60, 99]), dict(cu_seqlens_host=[1, 60, 100]),
-                dict(cu_seqlens_host=[0, 70, 60]), dict(flags=2), dict(flags=1 << 31), dict(gate=3), dict(gate=-1),
+                dict(cu_seqlens_host=[0, 70, 60]), dict(flags=4), dict(flags=1 << 31), dict(gate=3), dict(gate=-1),
                 dict(stages=kda.Stages(1, -1e-6, 0, None, 0.0, None)),
                 dict(stages=kda.Stages(0, 0.0, 0, FAKE, 0.0, None))):
         d3, k3 = desc(**bad)
@@ -240,3 +240,31 @@ def test_backward_workspace_and_validation_codes():
     # no sequences: nothing to do
     d4, k4 = desc(num_seqs=0, total_tokens=0)
     assert call_backward(d4, wsb=0) == kda.KDA_OK
+
+
+def test_bounded_workspace_does_not_grow_with_tokens():
+    """With KDA_PREFILL_BOUNDED the workspace size query returns the smallest
+    workspace the bounded schedule accepts: a small header, the blocks of one
+    chunk index for every head and the carried states [N, H, dk, dv] fp32 --
+    the same for 4,096 and 131,072 tokens.  One byte less is refused before
+    anything is launched, and the recovery query answers 0 for that
+    schedule without a device."""
+    b = kda.KDA_PREFILL_BOUNDED
+    sizes = []
+    for T in (4096, 131072):
+        d, keep = kda.make_desc(1, T, 32, 128, 128, 64, kda.KDA_BF16, [0, T], b)
+        sizes.append(kda.prefill_workspace_size(d))
+        full, keep2 = kda.make_desc(1, T, 32, 128, 128, 64, kda.KDA_BF16, [0, T], kda.KDA_PREFILL_ONE_STREAM)
+        assert sizes[-1] < kda.prefill_workspace_size(full)
+    assert sizes[0] == sizes[1]
+    header = sizes[0] - 32 * block_bytes(64, 128, 2) - 32 * 128 * 128 * 4
+    assert 0 < header < 4096, header
+    d, keep = kda.make_desc(3, 500, 4, 64, 128, 32, kda.KDA_F32, [0, 100, 100, 500], b)
+    need = kda.prefill_workspace_size(d)
+    assert need == kda.prefill_workspace_size(kda.make_desc(3, 50000, 4, 64, 128, 32, kda.KDA_F32,
+                                                            [0, 100, 100, 50000], b)[0])
+    assert call_prefill(d, wsb=need - 1) == kda.KDA_ERR_WORKSPACE_TOO_SMALL
+    lib = kda.load_library()
+    out = ctypes.c_int32(7)
+    assert lib.kda_prefill_recovered(ctypes.byref(d), FAKE, ctypes.byref(out), None) == kda.KDA_OK
+    assert out.value == 0

@@ -1,0 +1,67 @@
+"""The bounded-workspace schedule (KDA_PREFILL_BOUNDED) on the GPU: with a
+workspace far smaller than the one-stream schedule's, the chunks run in
+segments of global chunk indices whose boundaries fall inside sequences; the
+states carried between segments pass through fp32 memory unchanged, so o and
+S_T must equal the one-stream schedule's bit for bit, and match the oracle."""
+import numpy as np
+import pytest
+
+import synth
+from tests.gpu_helpers import TOL, check, gpu_prefill, have_gpu, log, oracle_prefill
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not have_gpu(), reason="needs a GPU")]
+
+
+def _min_bytes(w):
+    import gated_delta_rule_33_amd as kda
+    T, H, dk = w.q.shape
+    d, keep = kda.make_desc(w.num_seqs, T, H, dk, w.v.shape[2], w.chunk,
+                            kda.KDA_BF16 if w.io_dtype == "bf16" else kda.KDA_F32, w.cu_seqlens.tolist(),
+                            kda.KDA_PREFILL_BOUNDED)
+    return kda.prefill_workspace_size(d)
+
+
+def _block_bytes(w):
+    es = 2 if w.io_dtype == "bf16" else 4
+    C = max(w.chunk, 32)
+    dk = w.q.shape[2]
+    tri = 32 * (C // 2) * es + (C - 32) * C * es if C == 64 else C * C * es
+    return (3 * C * dk * es + 2 * tri + dk * 4 + C * 4 + 1023) // 1024 * 1024
+
+
+CASES = [
+    # (lengths, H, dk, dv, dtype, chunk, extra chunk indices per segment beyond one)
+    ([700, 1, 0, 1300, 64, 257], 4, 128, 128, "bf16", 64, 3),
+    ([700, 1, 0, 1300, 64, 257], 4, 128, 128, "bf16", 64, 0),   # the smallest workspace
+    ([300, 129, 33], 2, 64, 128, "f32", 32, 4),
+    ([2000], 2, 128, 64, "bf16", 16, 10),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_bounded_equals_one_stream(case):
+    lengths, H, dk, dv, dt, chunk, extra = CASES[case]
+    w = synth.make_prefill(lengths, H=H, dk=dk, dv=dv, io_dtype=dt, seed=900 + case, S0_std=0.05, chunk=chunk)
+    cap = _min_bytes(w) + extra * H * _block_bytes(w)
+    log("prefill bounded case %d: %s H=%d dk=%d dv=%d %s chunk %d, workspace %d bytes" %
+        (case, lengths, H, dk, dv, dt, chunk, cap))
+    o_b, S_b = gpu_prefill(w, max_workspace_bytes=cap)
+    o_1, S_1 = gpu_prefill(w, one_stream=True)
+    assert np.array_equal(o_b, o_1)
+    assert np.array_equal(S_b, S_1)
+    o_ref, S_ref = oracle_prefill(w)
+    check("o bounded", o_b, o_ref, TOL[dt])
+    check("S_T bounded", S_b, S_ref, TOL[dt])
+
+
+def test_bounded_without_state_and_in_place():
+    w = synth.make_prefill([900, 5, 1100], H=4, dk=128, dv=128, io_dtype="bf16", seed=911, S0_std=0.05)
+    cap = _min_bytes(w) + 2 * 4 * _block_bytes(w)
+    log("prefill bounded: no S_T (carry in the workspace), then in place")
+    o_n, S_n = gpu_prefill(w, max_workspace_bytes=cap, want_state=False)
+    o_1, S_1 = gpu_prefill(w, one_stream=True)
+    assert S_n is None
+    assert np.array_equal(o_n, o_1)
+    o_i, S_i = gpu_prefill(w, max_workspace_bytes=cap, in_place=True)
+    assert np.array_equal(o_i, o_1)
+    assert np.array_equal(S_i, S_1)

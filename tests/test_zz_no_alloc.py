@@ -1,7 +1,9 @@
 """kda_prefill_noalloc -- the prefill whose workspace is the library's static
 per-GPU scratch array -- against kda_prefill on the same inputs: two calls in
 a row, the second smaller (the array keeps the first call's contents), then
-a problem too large for the array, which must be refused."""
+problems whose one-stream workspace exceeds the array, which run the bounded
+schedule inside it with identical results, and one that does not fit even
+so, which must be refused."""
 import numpy as np
 import pytest
 
@@ -47,17 +49,29 @@ def test_noalloc_in_place_and_size_limit():
     o_ref, S_ref = oracle_prefill(w)
     check("o (in place)", o, o_ref, TOL["bf16"])
     check("S_T (in place)", S, S_ref, TOL["bf16"])
-    # 16384 tokens x 32 heads need ~ 500 MB of workspace: refused, nothing launched
+    # 16384 tokens x 32 heads need ~ 500 MB of one-stream workspace: the
+    # call runs the bounded schedule inside the array, with the same bits
     T, H = 16384, 32
     desc, keep = kda.make_desc(1, T, H, 128, 128, 64, kda.KDA_BF16, [0, T], kda.KDA_PREFILL_ONE_STREAM)
     assert kda.prefill_workspace_size(desc) > kda.NOALLOC_SCRATCH_BYTES
-    q = torch.zeros((T, H, 128), dtype=torch.bfloat16, device="cuda")
-    la = torch.zeros((T, H, 128), dtype=torch.float32, device="cuda")
-    b = torch.zeros((T, H), dtype=torch.float32, device="cuda")
-    cu = torch.tensor([0, T], dtype=torch.int32, device="cuda")
+    w = synth.make_prefill([T], H=H, dk=128, dv=128, io_dtype="bf16", seed=44, S0_std=0.05)
+    log("noalloc bounded: %d tokens x %d heads" % (T, H))
+    o_na, S_na = _noalloc(w)
+    o_ws, S_ws = gpu_prefill(w, one_stream=True)
+    assert np.array_equal(o_na, o_ws)
+    assert np.array_equal(S_na, S_ws)
+    # 160 one-token sequences x 32 heads: with S_T the carried states live
+    # there and the call runs; without it they would need 320 MiB of the
+    # array: refused, nothing launched
+    N = 160
+    w = synth.make_prefill([1] * N, H=H, dk=128, dv=128, io_dtype="bf16", seed=45, S0_std=0.05)
+    log("noalloc bounded: %d one-token sequences x %d heads, then refused without S_T" % (N, H))
+    o_na, S_na = _noalloc(w)
+    o_ws, S_ws = gpu_prefill(w, one_stream=True)
+    assert np.array_equal(o_na, o_ws)
+    assert np.array_equal(S_na, S_ws)
+    q = dev(w.q, "bf16")
     with pytest.raises(kda.KdaError) as ei:
-        kda.prefill_noalloc(q, q.clone(), q.clone(), la, b, cu, cu_seqlens_host=[0, T])
+        kda.prefill_noalloc(q, dev(w.k, "bf16"), dev(w.v, "bf16"), dev(w.log_alpha), dev(w.beta), dev(w.cu_seqlens),
+                            dev(w.S0), cu_seqlens_host=w.cu_seqlens.tolist(), want_state=False)
     assert ei.value.status == kda.KDA_ERR_WORKSPACE_TOO_SMALL
-    # the largest documented size fits
-    desc, keep = kda.make_desc(1, 8000, 32, 128, 128, 64, kda.KDA_BF16, [0, 8000], kda.KDA_PREFILL_ONE_STREAM)
-    assert kda.prefill_workspace_size(desc) <= kda.NOALLOC_SCRATCH_BYTES
