@@ -41,6 +41,10 @@ struct PrefillPlan {
   // segment left; that state is kept at off_bcarry (0: in S_T).
   int64_t bseg;
   size_t off_bcarry;
+  // Its ring form for few (sequence, head) pairs (rslots >= 2): segments of
+  // rseg chunk indices in rslots slots of the block area, prepared on one
+  // half of the CUs while the state pass runs on the other (0: none).
+  int64_t rseg, rslots;
 };
 
 // Returns false when the shape is unsupported.

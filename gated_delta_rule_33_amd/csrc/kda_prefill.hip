@@ -1953,6 +1953,8 @@ bool make_prefill_plan(const kda_prefill_desc* d, int64_t max_chunks, PrefillPla
   p->total_bytes = align256(off);
   p->bseg = 0;
   p->off_bcarry = 0;
+  p->rseg = 0;
+  p->rslots = 0;
   return true;
 }
 
@@ -1969,6 +1971,19 @@ bool make_bounded_plan(const kda_prefill_desc* d, int64_t max_chunks, size_t wor
   int64_t seg = static_cast<int64_t>((workspace_bytes - p->off_blocks - carry) / chunk_bytes);
   if (seg > max_chunks) seg = max_chunks;
   p->bseg = seg;
+  // Few (sequence, head) pairs: a ring of segments of the overlapped
+  // schedule's length, when at least two fit (see launch_prefill_t)
+  if (!(d->flags & KDA_PREFILL_ONE_STREAM) && narrow_scan_wgs(d->num_seqs, d->num_heads, d->dv) <= kPipeMaxScanWgs &&
+      max_chunks >= 2 * kPipeMinSeg) {
+    int64_t rseg = (max_chunks + kPipeMaxSegs - 1) / kPipeMaxSegs;
+    if (rseg < kPipeMinSeg) rseg = kPipeMinSeg;
+    const int64_t nseg = (max_chunks + rseg - 1) / rseg;
+    const int64_t slots = seg / rseg < nseg ? seg / rseg : nseg;
+    if (slots >= 2) {
+      p->rseg = rseg;
+      p->rslots = slots;
+    }
+  }
   // the block area ends on a 1024-byte boundary (off_blocks and chunk_bytes are multiples)
   const size_t end = p->off_blocks + static_cast<size_t>(seg) * chunk_bytes;
   p->off_bcarry = carry ? end : 0;
@@ -2043,6 +2058,8 @@ hipError_t device_cus(int* cus) {
 struct PipeStreams {
   hipStream_t prep = nullptr, scan = nullptr;
   hipEvent_t fork = nullptr, join = nullptr, join_prep = nullptr;
+  // ring schedule: segment j prepared / passed over by the state pass
+  hipEvent_t prepped[kPipeMaxSegs] = {}, scanned[kPipeMaxSegs] = {};
   int scan_cus = 0;
   std::mutex mu;  // one schedule at a time may use the shared streams/events
 };
@@ -2058,6 +2075,10 @@ static void destroy_pipe(PipeStreams* ps) {
   if (ps->fork) (void)hipEventDestroy(ps->fork);
   if (ps->join) (void)hipEventDestroy(ps->join);
   if (ps->join_prep) (void)hipEventDestroy(ps->join_prep);
+  for (int i = 0; i < kPipeMaxSegs; ++i) {
+    if (ps->prepped[i]) (void)hipEventDestroy(ps->prepped[i]);
+    if (ps->scanned[i]) (void)hipEventDestroy(ps->scanned[i]);
+  }
   delete ps;
 }
 
@@ -2106,6 +2127,9 @@ static hipError_t pipe_streams(int64_t scan_wgs, PipeStreams** out) {
               hipEventCreateWithFlags(&ps->fork, hipEventDisableTiming) == hipSuccess &&
               hipEventCreateWithFlags(&ps->join, hipEventDisableTiming) == hipSuccess;
     ok = ok && hipEventCreateWithFlags(&ps->join_prep, hipEventDisableTiming) == hipSuccess;
+    for (int i = 0; ok && i < kPipeMaxSegs; ++i)
+      ok = hipEventCreateWithFlags(&ps->prepped[i], hipEventDisableTiming) == hipSuccess &&
+           hipEventCreateWithFlags(&ps->scanned[i], hipEventDisableTiming) == hipSuccess;
     if (ok) {
       ps->scan_cus = ns;
       g_pipe[dev] = ps;
@@ -2216,6 +2240,53 @@ static hipError_t launch_prefill_t(const PrefillPlan& p, const void* q, const vo
     // head) from the state in `carry`; stream order separates the launches.
     float* carry = p.off_bcarry ? reinterpret_cast<float*>(w + p.off_bcarry) : S_T;
     const size_t chunk_bytes = static_cast<size_t>(p.H) * Blk<T, C, DK>::bytes;
+    PipeStreams* ps = nullptr;
+    if (p.rslots >= 2) {
+      e = pipe_streams(narrow_scan_wgs(p.N, p.H, DV), &ps);
+      if (e != hipSuccess) return e;
+    }
+    if (ps) {
+      // Ring: segment j (rseg global chunk indices) is prepared into slot
+      // j mod rslots on the prep stream (half of the CUs) once the state
+      // pass of segment j - rslots, the slot's previous reader, has ended,
+      // and passed over by a state-pass launch of its own on the scan
+      // stream (the other half) once its prep has ended.  Every dependency
+      // is a stream event: no kernel waits on another.  Segment 0 is
+      // prepared on the caller's stream over the whole device first.
+      const int64_t nseg = (p.max_chunks + p.rseg - 1) / p.rseg;
+      auto ring_blocks = [&](int64_t j) {
+        const uintptr_t slot = reinterpret_cast<uintptr_t>(blocks) +
+                               static_cast<uintptr_t>(j % p.rslots) * static_cast<uintptr_t>(p.rseg) * chunk_bytes;
+        return reinterpret_cast<unsigned char*>(slot - static_cast<uintptr_t>(j * p.rseg) * chunk_bytes);
+      };
+      std::lock_guard<std::mutex> lock(ps->mu);
+      if ((e = prep(0, p.rseg < p.max_chunks ? p.rseg : p.max_chunks, st, cus, nullptr, 0, nullptr,
+                    ring_blocks(0))) != hipSuccess)
+        return e;
+      if ((e = hipEventRecord(ps->fork, st)) != hipSuccess) return e;
+      if ((e = hipStreamWaitEvent(ps->prep, ps->fork, 0)) != hipSuccess) return e;
+      if ((e = hipStreamWaitEvent(ps->scan, ps->fork, 0)) != hipSuccess) return e;
+      for (int64_t j = 0; j < nseg; ++j) {
+        const int64_t gb = j * p.rseg, ge = gb + p.rseg < p.max_chunks ? gb + p.rseg : p.max_chunks;
+        if (j > 0) {
+          if (j >= p.rslots && (e = hipStreamWaitEvent(ps->prep, ps->scanned[j - p.rslots], 0)) != hipSuccess)
+            return e;
+          if ((e = prep(gb, ge - gb, ps->prep, cus - ps->scan_cus, nullptr, 0, nullptr, ring_blocks(j))) !=
+              hipSuccess)
+            return e;
+          if ((e = hipEventRecord(ps->prepped[j], ps->prep)) != hipSuccess) return e;
+          if ((e = hipStreamWaitEvent(ps->scan, ps->prepped[j], 0)) != hipSuccess) return e;
+        }
+        if ((e = launch_scan<T, C, DK, DV, 2>(p, v, cu, chunk_off, order, ring_blocks(j), S0, o, S_T, ps->scan,
+                                              nullptr, 1, nullptr, carry, gb, ge)) != hipSuccess)
+          return e;
+        if ((e = hipEventRecord(ps->scanned[j], ps->scan)) != hipSuccess) return e;
+      }
+      if ((e = hipEventRecord(ps->join, ps->scan)) != hipSuccess) return e;
+      if ((e = hipEventRecord(ps->join_prep, ps->prep)) != hipSuccess) return e;
+      if ((e = hipStreamWaitEvent(st, ps->join, 0)) != hipSuccess) return e;
+      return hipStreamWaitEvent(st, ps->join_prep, 0);
+    }
     for (int64_t gb = 0; gb < p.max_chunks; gb += p.bseg) {
       const int64_t ge = gb + p.bseg < p.max_chunks ? gb + p.bseg : p.max_chunks;
       unsigned char* seg_blocks =

@@ -2,7 +2,10 @@
 workspace far smaller than the one-stream schedule's, the chunks run in
 segments of global chunk indices whose boundaries fall inside sequences; the
 states carried between segments pass through fp32 memory unchanged, so o and
-S_T must equal the one-stream schedule's bit for bit, and match the oracle."""
+S_T must equal the one-stream schedule's bit for bit, and match the oracle.
+With few (sequence, head) pairs and room for two or more segments of 64+
+chunk indices, the segments rotate through a ring of block slots, prepared
+on one half of the CUs while the state pass runs on the other."""
 import numpy as np
 import pytest
 
@@ -65,3 +68,30 @@ def test_bounded_without_state_and_in_place():
     o_i, S_i = gpu_prefill(w, max_workspace_bytes=cap, in_place=True)
     assert np.array_equal(o_i, o_1)
     assert np.array_equal(S_i, S_1)
+
+
+RING_CASES = [
+    # (lengths, H, dtype, slots of 64 chunk indices the workspace holds)
+    ([16384], 4, "bf16", 2),
+    ([5000, 3000, 9000], 2, "bf16", 3),
+    ([9000, 700], 2, "f32", 2),
+]
+
+
+@pytest.mark.parametrize("case", range(len(RING_CASES)))
+def test_bounded_ring_equals_one_stream(case):
+    lengths, H, dt, slots = RING_CASES[case]
+    w = synth.make_prefill(lengths, H=H, dk=128, dv=128, io_dtype=dt, seed=950 + case, S0_std=0.05)
+    carry = w.num_seqs * H * 128 * 128 * 4
+    cap = _min_bytes(w) - carry - H * _block_bytes(w) + (slots * 64 + 5) * H * _block_bytes(w)
+    log("prefill bounded ring case %d: %s H=%d %s, %d slots (workspace %d bytes)" % (case, lengths, H, dt, slots, cap))
+    o_b, S_b = gpu_prefill(w, max_workspace_bytes=cap)
+    o_1, S_1 = gpu_prefill(w, one_stream=True)
+    assert np.array_equal(o_b, o_1)
+    assert np.array_equal(S_b, S_1)
+    o_i, S_i = gpu_prefill(w, max_workspace_bytes=cap, in_place=True)
+    assert np.array_equal(o_i, o_1)
+    assert np.array_equal(S_i, S_1)
+    o_ref, S_ref = oracle_prefill(w)
+    check("o bounded ring", o_b, o_ref, TOL[dt])
+    check("S_T bounded ring", S_b, S_ref, TOL[dt])
