@@ -351,7 +351,7 @@ def run_backward(wname, args, torch, kda, synth, oracle, check: bool):
                roofline=dict(bound="mfma", achieved=round(tfl, 2), peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
                              frac=round(tfl / MFMA_BF16_PEAK_TFLOPS, 4), traffic=traffic,
                              kernel="kda_prefill_backward (prep, states, grad_v, grad_k)",
-                             products="split-bf16 (3 bf16 MFMA per product)",
+                             products="split-bf16 (3 bf16 MFMAs per product; the chain passes with bf16 io: 2, single-bf16 block factors)",
                              fp32_mfma_frac=round(tfl / FP32_MFMA_PEAK_TFLOPS, 4),
                              flops_per_launch=int(nflops), flops_per_token_head=flops_th,
                              hbm_achieved=round(nbytes / call_s / 1e9, 1), hbm_frac=round(nbytes / call_s / 1e9 / HBM_PEAK_GBS, 4),

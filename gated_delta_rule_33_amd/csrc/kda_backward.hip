@@ -155,6 +155,26 @@ __device__ __forceinline__ F3 pfrag(const float* plane, int K, int row, int k0) 
   const __bf16* p = reinterpret_cast<const __bf16*>(plane) + ptile(K, row, k0);
   return F3{*reinterpret_cast<const bf16x8*>(p), *reinterpret_cast<const bf16x8*>(p + 512)};
 }
+// The two chain passes with bf16 io read the block factors as single bf16
+// (their hi planes) and form each product from the hi part of the factor
+// and both parts of the value handed along the chain: two MFMAs instead of
+// three and half the bytes per chunk, which is what bounds these passes;
+// fp32 io keeps both parts of both.
+template <bool HI>
+__device__ __forceinline__ F3 pfragx(const float* plane, int K, int row, int k0) {
+  const __bf16* p = reinterpret_cast<const __bf16*>(plane) + ptile(K, row, k0);
+  if constexpr (HI) return F3{*reinterpret_cast<const bf16x8*>(p), bf16x8{}};
+  else return F3{*reinterpret_cast<const bf16x8*>(p), *reinterpret_cast<const bf16x8*>(p + 512)};
+}
+template <bool HI>
+__device__ __forceinline__ f32x4 mmx(const F3& a, const F3& b, f32x4 c) {
+  if constexpr (HI) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.h, b.l, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.h, b.h, c, 0, 0, 0);
+  } else {
+    return mm3(a, b, c);
+  }
+}
 __device__ __forceinline__ void pstore8(float* plane, int K, int row, int k0, const float* x) {
   F3 f;
 #pragma unroll
@@ -646,6 +666,7 @@ __device__ __forceinline__ void bwd_state_body(int x, const T* __restrict__ v, c
                                                const float* __restrict__ blk, const float* __restrict__ S0,
                                                float* __restrict__ sc) {
   typedef BwdBlk<DK> B;
+  constexpr bool kHi = sizeof(T) == 2;  // bf16 io: single-bf16 block factors
   constexpr int NSP = DV / SCOLS, NKB = DK / 16, TPW = NKB / 4, NKS = DK / 32;
   __shared__ __align__(16) __bf16 lds_s[HTile<DK>::elems + 2 * HTile<BC>::elems];
   const HTile<DK> XT{lds_s};
@@ -681,19 +702,19 @@ __device__ __forceinline__ void bwd_state_body(int x, const T* __restrict__ v, c
   auto load_a = [&](int c, Ops& o) {
     const float* bk = blk + (static_cast<size_t>(j0 + c) * H + h) * B::floats;
 #pragma unroll
-    for (int kk = 0; kk < NKS; ++kk) o.kg[kk] = pfrag(bk + B::oKg, DK, 16 * w + r, 32 * kk + 8 * g);
+    for (int kk = 0; kk < NKS; ++kk) o.kg[kk] = pfragx<kHi>(bk + B::oKg, DK, 16 * w + r, 32 * kk + 8 * g);
   };
   auto load_c = [&](int c, Ops& o) {
     const float* bk = blk + (static_cast<size_t>(j0 + c) * H + h) * B::floats;
 #pragma unroll
     for (int t = 0; t < TPW; ++t)
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) o.kbt[t][kk] = pfrag(bk + B::oKbT, BC, 16 * (w * TPW + t) + r, 32 * kk + 8 * g);
+      for (int kk = 0; kk < 2; ++kk) o.kbt[t][kk] = pfragx<kHi>(bk + B::oKbT, BC, 16 * (w * TPW + t) + r, 32 * kk + 8 * g);
   };
   auto load_b = [&](int c, Ops& o) {
     const float* bk = blk + (static_cast<size_t>(j0 + c) * H + h) * B::floats;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) o.tt[kk] = pfrag(bk + B::oT, BC, 16 * w + r, 32 * kk + 8 * g);
+    for (int kk = 0; kk < 2; ++kk) o.tt[kk] = pfragx<kHi>(bk + B::oT, BC, 16 * w + r, 32 * kk + 8 * g);
     const int t0 = tb + c * BC, len = min(BC, L - c * BC);
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -738,7 +759,7 @@ __device__ __forceinline__ void bwd_state_body(int x, const T* __restrict__ v, c
     for (int hf = 0; hf < 2; ++hf) {
       f32x4 acc = zero4();
 #pragma unroll
-      for (int kk = 0; kk < NKS; ++kk) acc = mm3(cur.kg[kk], XT.frag(16 * hf + r, 32 * kk + 8 * g), acc);
+      for (int kk = 0; kk < NKS; ++kk) acc = mmx<kHi>(cur.kg[kk], XT.frag(16 * hf + r, 32 * kk + 8 * g), acc);
       f32x4 wv;
 #pragma unroll
       for (int m = 0; m < 4; ++m) wv[m] = cur.bet[m] * (raw1<T>::cvt(cur.vv[hf][m]) - acc[m]);
@@ -751,7 +772,7 @@ __device__ __forceinline__ void bwd_state_body(int x, const T* __restrict__ v, c
       f32x4 acc = zero4();
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
-        if (kk <= kT1) acc = mm3(cur.tt[kk], WT.frag(16 * hf + r, 32 * kk + 8 * g), acc);
+        if (kk <= kT1) acc = mmx<kHi>(cur.tt[kk], WT.frag(16 * hf + r, 32 * kk + 8 * g), acc);
       UT.put4(16 * hf + r, 16 * w + 4 * g, acc);
     }
     lds_sync();
@@ -763,7 +784,7 @@ __device__ __forceinline__ void bwd_state_body(int x, const T* __restrict__ v, c
 #pragma unroll
         for (int m = 0; m < 4; ++m) X[t][hf][m] *= cur.gam[t][m];
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) X[t][hf] = mm3(cur.kbt[t][kk], UT.frag(16 * hf + r, 32 * kk + 8 * g), X[t][hf]);
+        for (int kk = 0; kk < 2; ++kk) X[t][hf] = mmx<kHi>(cur.kbt[t][kk], UT.frag(16 * hf + r, 32 * kk + 8 * g), X[t][hf]);
       }
   };
   for (int c = 0; c < nch; c += 2) {
@@ -788,6 +809,7 @@ __device__ __forceinline__ void bwd_dstate_body(int x, const T* __restrict__ dO,
                                                 const float* __restrict__ blk, const float* __restrict__ dST,
                                                 float* __restrict__ dsc, float* __restrict__ dS0) {
   typedef BwdBlk<DK> B;
+  constexpr bool kHi = sizeof(T) == 2;  // bf16 io: single-bf16 block factors
   constexpr int NSP = DV / SCOLS, NKB = DK / 16, TPW = NKB / 4, NKS = DK / 32;
   __shared__ __align__(16) __bf16 lds_d[HTile<DK>::elems + 3 * HTile<BC>::elems];
   const HTile<DK> XT{lds_d};
@@ -824,9 +846,9 @@ __device__ __forceinline__ void bwd_dstate_body(int x, const T* __restrict__ dO,
   auto load_a = [&](int c, Ops& o) {
     const float* bk = blk + (static_cast<size_t>(j0 + c) * H + h) * B::floats;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) o.pt[kk] = pfrag(bk + B::oPT, BC, 16 * w + r, 32 * kk + 8 * g);
+    for (int kk = 0; kk < 2; ++kk) o.pt[kk] = pfragx<kHi>(bk + B::oPT, BC, 16 * w + r, 32 * kk + 8 * g);
 #pragma unroll
-    for (int kk = 0; kk < NKS; ++kk) o.kb[kk] = pfrag(bk + B::oKb, DK, 16 * w + r, 32 * kk + 8 * g);
+    for (int kk = 0; kk < NKS; ++kk) o.kb[kk] = pfragx<kHi>(bk + B::oKb, DK, 16 * w + r, 32 * kk + 8 * g);
   };
   auto load_c = [&](int c, Ops& o) {
     const float* bk = blk + (static_cast<size_t>(j0 + c) * H + h) * B::floats;
@@ -834,14 +856,14 @@ __device__ __forceinline__ void bwd_dstate_body(int x, const T* __restrict__ dO,
     for (int t = 0; t < TPW; ++t)
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        o.qgt[t][kk] = pfrag(bk + B::oQgT, BC, 16 * (w * TPW + t) + r, 32 * kk + 8 * g);
-        o.kgt[t][kk] = pfrag(bk + B::oKgT, BC, 16 * (w * TPW + t) + r, 32 * kk + 8 * g);
+        o.qgt[t][kk] = pfragx<kHi>(bk + B::oQgT, BC, 16 * (w * TPW + t) + r, 32 * kk + 8 * g);
+        o.kgt[t][kk] = pfragx<kHi>(bk + B::oKgT, BC, 16 * (w * TPW + t) + r, 32 * kk + 8 * g);
       }
   };
   auto load_b = [&](int c, Ops& o) {
     const float* bk = blk + (static_cast<size_t>(j0 + c) * H + h) * B::floats;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) o.tt[kk] = pfrag(bk + B::oTT, BC, 16 * w + r, 32 * kk + 8 * g);
+    for (int kk = 0; kk < 2; ++kk) o.tt[kk] = pfragx<kHi>(bk + B::oTT, BC, 16 * w + r, 32 * kk + 8 * g);
     const int t0 = tb + c * BC, len = min(BC, L - c * BC);
     // rows past the sequence read the last row: P and Qg are zero in those
     // rows, so their dO never contributes (no branch, no wait on the load here)
@@ -882,9 +904,9 @@ __device__ __forceinline__ void bwd_dstate_body(int x, const T* __restrict__ dO,
       f32x4 acc = zero4();
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
-        if (kk >= kU0) acc = mm3(cur.pt[kk], DT.frag(16 * hf + r, 32 * kk + 8 * g), acc);
+        if (kk >= kU0) acc = mmx<kHi>(cur.pt[kk], DT.frag(16 * hf + r, 32 * kk + 8 * g), acc);
 #pragma unroll
-      for (int kk = 0; kk < NKS; ++kk) acc = mm3(cur.kb[kk], XT.frag(16 * hf + r, 32 * kk + 8 * g), acc);
+      for (int kk = 0; kk < NKS; ++kk) acc = mmx<kHi>(cur.kb[kk], XT.frag(16 * hf + r, 32 * kk + 8 * g), acc);
       ZT.put4(16 * hf + r, 16 * w + 4 * g, acc);
     }
     lds_sync();
@@ -894,7 +916,7 @@ __device__ __forceinline__ void bwd_dstate_body(int x, const T* __restrict__ dO,
       f32x4 acc = zero4();
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
-        if (kk >= kU0) acc = mm3(cur.tt[kk], ZT.frag(16 * hf + r, 32 * kk + 8 * g), acc);
+        if (kk >= kU0) acc = mmx<kHi>(cur.tt[kk], ZT.frag(16 * hf + r, 32 * kk + 8 * g), acc);
       f32x4 yb;
 #pragma unroll
       for (int m = 0; m < 4; ++m) yb[m] = -cur.bet[m] * acc[m];
@@ -910,8 +932,8 @@ __device__ __forceinline__ void bwd_dstate_body(int x, const T* __restrict__ dO,
         for (int m = 0; m < 4; ++m) X[t][hf][m] *= cur.gam[t][m];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          X[t][hf] = mm3(cur.qgt[t][kk], DT.frag(16 * hf + r, 32 * kk + 8 * g), X[t][hf]);
-          X[t][hf] = mm3(cur.kgt[t][kk], YT.frag(16 * hf + r, 32 * kk + 8 * g), X[t][hf]);
+          X[t][hf] = mmx<kHi>(cur.qgt[t][kk], DT.frag(16 * hf + r, 32 * kk + 8 * g), X[t][hf]);
+          X[t][hf] = mmx<kHi>(cur.kgt[t][kk], YT.frag(16 * hf + r, 32 * kk + 8 * g), X[t][hf]);
         }
       }
   };
