@@ -155,6 +155,14 @@ __device__ __forceinline__ F3 pfrag(const float* plane, int K, int row, int k0) 
   const __bf16* p = reinterpret_cast<const __bf16*>(plane) + ptile(K, row, k0);
   return F3{*reinterpret_cast<const bf16x8*>(p), *reinterpret_cast<const bf16x8*>(p + 512)};
 }
+// hi part only (planes read only as single bf16)
+__device__ __forceinline__ void pstore8_hi(float* plane, int K, int row, int k0, const float* x) {
+  bf16x8 h;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) h[i] = static_cast<__bf16>(x[i]);
+  *reinterpret_cast<bf16x8*>(reinterpret_cast<__bf16*>(plane) + ptile(K, row, k0)) = h;
+}
+
 // The two chain passes with bf16 io read the block factors as single bf16
 // (their hi planes) and form each product from the hi part of the factor
 // and both parts of the value handed along the chain: two MFMAs instead of
@@ -406,9 +414,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         xg[i] = ks[row * PS + ch] * eg;
         xq[i] = qs[row * PS + ch] * eg;
       }
-      pstore8(bk + B::oKbT, BC, c0 + ch, r8, xb);
-      pstore8(bk + B::oKgT, BC, c0 + ch, r8, xg);
-      pstore8(bk + B::oQgT, BC, c0 + ch, r8, xq);
+      // read only by the chain passes: with bf16 io only as single bf16
+      if constexpr (sizeof(T) == 2) {
+        pstore8_hi(bk + B::oKbT, BC, c0 + ch, r8, xb);
+        pstore8_hi(bk + B::oKgT, BC, c0 + ch, r8, xg);
+        pstore8_hi(bk + B::oQgT, BC, c0 + ch, r8, xq);
+      } else {
+        pstore8(bk + B::oKbT, BC, c0 + ch, r8, xb);
+        pstore8(bk + B::oKgT, BC, c0 + ch, r8, xg);
+        pstore8(bk + B::oQgT, BC, c0 + ch, r8, xq);
+      }
     }
     if (tid < 32) bk[B::oGam + c0 + tid] = __expf(gs[(BC - 1) * PS + tid]);
     // off-diagonal block pairs (I, J < I), split at row 16 I - 1
