@@ -1291,7 +1291,7 @@ constexpr int scan_threads() {
   return 64 * (WAVES * ScanLds<T, C, DK, 16 * WAVES>::roles + kLoaderWaves);
 }
 
-template <typename T, int C, int DK, int DV, int WAVES>
+template <typename T, int C, int DK, int DV, int WAVES, bool SEG>
 __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel(
     const T* __restrict__ v, const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_off,
     const int32_t* __restrict__ order, int N, int H, const unsigned char* __restrict__ ws, const float* S0,
@@ -1334,7 +1334,7 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
   const int tbeg = cu[seq], L_seq = cu[seq + 1] - tbeg;
   const int c0 = chunk_off[seq];
   const int nch = (L_seq + cl - 1) / cl;
-  // The sequence's chunks [cb, ce): all of them, or with `carry` (bounded
+  // The sequence's chunks [cb, ce): all of them, or with SEG (bounded
   // schedule) those among global chunks [gb, ge), starting from the state
   // the previous segment left in `carry` unless the sequence starts here and
   // leaving it there unless the sequence ends here.  When `ready` is given,
@@ -1344,7 +1344,7 @@ __global__ __launch_bounds__((scan_threads<T, C, DK, WAVES>())) void scan_kernel
   int cb = 0, ce = nch;
   const float* s_in = S0;
   float* s_out = S_T;
-  if (carry) {
+  if constexpr (SEG) {
     cb = min(max(gb - c0, 0), nch);
     ce = min(max(ge - c0, 0), nch);
     if (cb == ce && !(nch == 0 && gb == 0)) return;  // nothing of this sequence in the segment
@@ -2012,7 +2012,7 @@ int set_prefill_wait_polls(int polls) {
   return g_wait_polls.exchange(polls > 0 ? polls : (polls == 0 ? 0 : kDefaultWaitPolls));
 }
 
-template <typename T, int C, int DK, int DV, int WAVES>
+template <typename T, int C, int DK, int DV, int WAVES, bool SEG = false>
 static hipError_t launch_scan(const PrefillPlan& p, const void* v, const int32_t* cu, const int32_t* chunk_off,
                               const int32_t* order, const unsigned char* blocks, const float* S0, void* o,
                               float* S_T, hipStream_t st, int* ready = nullptr, int seg = 1,
@@ -2020,12 +2020,12 @@ static hipError_t launch_scan(const PrefillPlan& p, const void* v, const int32_t
                               int64_t ge = 0) {
   typedef ScanLds<T, C, DK, 16 * WAVES> SL;
   static_assert(SL::total <= 160 * 1024, "scan LDS");
-  hipError_t e = set_lds_limit(reinterpret_cast<const void*>(&scan_kernel<T, C, DK, DV, WAVES>), SL::total);
+  hipError_t e = set_lds_limit(reinterpret_cast<const void*>(&scan_kernel<T, C, DK, DV, WAVES, SEG>), SL::total);
   if (e != hipSuccess) return e;
   const int pairs = p.N * p.H;
   const int nsplit = DV / (16 * WAVES);
   const unsigned grid = static_cast<unsigned>((pairs + 7) / 8 * 8 * nsplit);
-  hipLaunchKernelGGL((scan_kernel<T, C, DK, DV, WAVES>), dim3(grid), dim3(scan_threads<T, C, DK, WAVES>()), SL::total, st,
+  hipLaunchKernelGGL((scan_kernel<T, C, DK, DV, WAVES, SEG>), dim3(grid), dim3(scan_threads<T, C, DK, WAVES>()), SL::total, st,
                      static_cast<const T*>(v), cu, chunk_off, order, p.N, p.H, blocks, S0, static_cast<T*>(o), S_T,
                      ready, seg, prefill_wait_polls(), guard, p.CL, carry, static_cast<int>(gb),
                      static_cast<int>(ge));
@@ -2277,7 +2277,7 @@ static hipError_t launch_prefill_t(const PrefillPlan& p, const void* q, const vo
           if ((e = hipEventRecord(ps->prepped[j], ps->prep)) != hipSuccess) return e;
           if ((e = hipStreamWaitEvent(ps->scan, ps->prepped[j], 0)) != hipSuccess) return e;
         }
-        if ((e = launch_scan<T, C, DK, DV, 2>(p, v, cu, chunk_off, order, ring_blocks(j), S0, o, S_T, ps->scan,
+        if ((e = launch_scan<T, C, DK, DV, 2, true>(p, v, cu, chunk_off, order, ring_blocks(j), S0, o, S_T, ps->scan,
                                               nullptr, 1, nullptr, carry, gb, ge)) != hipSuccess)
           return e;
         if ((e = hipEventRecord(ps->scanned[j], ps->scan)) != hipSuccess) return e;
@@ -2292,10 +2292,10 @@ static hipError_t launch_prefill_t(const PrefillPlan& p, const void* q, const vo
       unsigned char* seg_blocks =
           reinterpret_cast<unsigned char*>(reinterpret_cast<uintptr_t>(blocks) - static_cast<uintptr_t>(gb) * chunk_bytes);
       if ((e = prep(gb, ge - gb, st, cus, nullptr, 0, nullptr, seg_blocks)) != hipSuccess) return e;
-      e = wide_wgs < 512 ? launch_scan<T, C, DK, DV, 2>(p, v, cu, chunk_off, order, seg_blocks, S0, o, S_T, st, nullptr,
-                                                         1, nullptr, carry, gb, ge)
-                         : launch_scan<T, C, DK, DV, 4>(p, v, cu, chunk_off, order, seg_blocks, S0, o, S_T, st, nullptr,
-                                                         1, nullptr, carry, gb, ge);
+      e = wide_wgs < 512 ? launch_scan<T, C, DK, DV, 2, true>(p, v, cu, chunk_off, order, seg_blocks, S0, o, S_T, st,
+                                                               nullptr, 1, nullptr, carry, gb, ge)
+                         : launch_scan<T, C, DK, DV, 4, true>(p, v, cu, chunk_off, order, seg_blocks, S0, o, S_T, st,
+                                                               nullptr, 1, nullptr, carry, gb, ge);
       if (e != hipSuccess) return e;
     }
     return hipSuccess;
