@@ -95,3 +95,15 @@ def test_bounded_ring_equals_one_stream(case):
     o_ref, S_ref = oracle_prefill(w)
     check("o bounded ring", o_b, o_ref, TOL[dt])
     check("S_T bounded ring", S_b, S_ref, TOL[dt])
+
+
+@pytest.mark.parametrize("gate", ["scalar", "none"])
+def test_bounded_gate_forms(gate):
+    """The gate forms run the same segmented state pass."""
+    w = synth.make_prefill([1500, 40, 700], H=2, dk=128, dv=128, io_dtype="bf16", seed=960, S0_std=0.05, gate=gate)
+    cap = _min_bytes(w) + 4 * 2 * _block_bytes(w)
+    log("prefill bounded, gate %s (workspace %d bytes)" % (gate, cap))
+    o_b, S_b = gpu_prefill(w, max_workspace_bytes=cap)
+    o_1, S_1 = gpu_prefill(w, one_stream=True)
+    assert np.array_equal(o_b, o_1)
+    assert np.array_equal(S_b, S_1)
