@@ -29,9 +29,10 @@
  *     exception crosses this boundary.
  *   - Calls are thread-safe.  The library's only process state is created
  *     once under a lock: per-device kernel attributes and, for the
- *     overlapped prefill schedule, two CU-masked streams with their events
- *     per device, on which concurrent overlapped calls for one device take
- *     turns to enqueue their work; the streams are destroyed at process exit.
+ *     overlapped prefill schedule (and the ring form of KDA_PREFILL_BOUNDED),
+ *     two CU-masked streams with their events per device, on which
+ *     concurrent calls for one device take turns to enqueue their work; the
+ *     streams are destroyed at process exit.
  *   - Device-side preconditions that are documented but not checked: finite
  *     inputs; log_alpha <= 0; when no host mirror of cu_seqlens is given,
  *     cu_seqlens[0] = 0, non-decreasing and cu_seqlens[N] = total_tokens.
@@ -185,6 +186,11 @@ size_t kda_prefill_workspace_size(const kda_prefill_desc* desc);
  * device), the state pass stops waiting, and two recovery launches on
  * `stream`, which otherwise return at once, recompute every output there.
  * Results are correct either way; kda_prefill_recovered reports which.
+ * With KDA_PREFILL_BOUNDED and such few pairs, when two or more segments
+ * fit the workspace, the segments rotate through slots of it on the same
+ * two streams, every dependency a stream event (nothing waits inside a
+ * kernel, nothing to recover); otherwise that flag runs every launch on
+ * `stream`.
  *
  * Errors: KDA_ERR_INVALID_ARGUMENT (null pointer where data is required,
  * negative sizes, bad host offsets, misaligned workspace, overlapping buffers),
