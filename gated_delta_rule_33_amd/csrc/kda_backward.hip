@@ -1436,11 +1436,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 }
 
 // ---------------------------------------------------------------------------
-// grad_k: one workgroup (4 waves) per (chunk, head, SW key channels) -- or,
-// for the one-rate-per-head gate, per (chunk, head) over every channel, so
-// that the per-head gate cotangent is summed inside one workgroup (1-D
-// XCD-aware grid, below).  Thread t works on row t / 4 and SW / 4 consecutive
-// channels of the slice; SW = 16 keeps the LDS of two workgroups on a CU.
+// grad_k: one workgroup (4 waves) per (chunk, head), walking the key
+// channels SW at a time (for the one-rate-per-head gate the per-head gate
+// cotangent is then summed inside the workgroup).  Thread t works on row
+// t / 4 and SW / 4 consecutive channels of the slice; SW = 16 keeps the LDS
+// of two workgroups on a CU.
 //   GQ[r]  = sum_{s <= r} dP[r][s] k_s e^{G_r - G_s}
 //   GA[r]  = sum_{s <  r} dA[r][s] k_s e^{G_r - G_s}
 //   G2[s]  = sum_{r >= s} (dP[r][s] q_r + dA[r][s] k_r) e^{G_r - G_s}
@@ -1463,7 +1463,10 @@ __global__ __launch_bounds__(256) void bwd_grad_k_kernel(const T* __restrict__ q
   typedef BwdBlk<DK> B;
   constexpr int PS = SW + 4;  // pitch of the SW-channel slices (16-byte rows)
   constexpr int CPT = SW / 4;  // channels per thread (a row's four threads cover the slice)
-  constexpr int NSW = G == KDA_GATE_SCALAR ? DK / SW : 1;  // slices per workgroup
+  // every slice of the (chunk, head) in one workgroup: dP and dA are staged
+  // in LDS once for all of them (with one workgroup per slice they were
+  // loaded DK / SW times: 3.5% of the backward call at 131k)
+  constexpr int NSW = DK / SW;
   __shared__ float qs[BC * PS], ks[BC * PS], gs[BC * PS];
   __shared__ float dPl[BC * LPC], dAl[BC * LPC];
   __shared__ float Ksc[96 * PS], Xq[96 * PS], Xk[96 * PS];
@@ -1471,7 +1474,7 @@ __global__ __launch_bounds__(256) void bwd_grad_k_kernel(const T* __restrict__ q
   // 1-D grid, XCD-aware: the NZ channel slices of one (chunk, head) get
   // workgroup ids that differ by multiples of 8, i.e. one XCD and adjacent
   // dispatch, so the dP and dA they all read come through one L2
-  constexpr int NZ = G == KDA_GATE_SCALAR ? 1 : DK / SW;
+  constexpr int NZ = DK / SW / NSW;
   const int x = blockIdx.x, xcd = x & 7, rest = x >> 3, zs = rest % NZ, item = (rest / NZ) * 8 + xcd;
   const int j = item / H, h = item % H;
   if (j >= chunk_off[N]) return;
@@ -1763,7 +1766,7 @@ static hipError_t launch_backward_t(const BackwardPlan& p, const void* q, const 
                        blk, sc, dsc, static_cast<T*>(dv), dbeta);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     constexpr int SW = 16;  // key channels per grad_k slice (LDS for two workgroups per CU)
-    const unsigned nz = G == KDA_GATE_SCALAR ? 1u : static_cast<unsigned>(DK / SW);
+    const unsigned nz = 1u;  // one workgroup per (chunk, head): every channel slice inside it
     const unsigned items = (mc * static_cast<unsigned>(p.H) + 7u) / 8u * 8u;
     hipLaunchKernelGGL((bwd_grad_k_kernel<T, DK, G, SW>), dim3(items * nz), dim3(256), 0, st, tq, tk, la, cu,
                        chunk_off, p.N, p.H, blk, static_cast<T*>(dq), static_cast<T*>(dk), dla);
