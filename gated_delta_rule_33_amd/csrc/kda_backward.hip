@@ -1493,20 +1493,25 @@ __global__ __launch_bounds__(256) void bwd_grad_k_kernel(const T* __restrict__ q
   constexpr int RPS = BC * SW / 256;  // rows per thread of the gate load
   const int gch = tid % SW, gseg = tid / SW;
   const int rowc = min(row, cl.len - 1);
-  float xq[CPT], xk[CPT], xg[RPS], dQg[CPT], dKg[CPT], dKb[CPT];
-  auto issue = [&](int c0) {
+  // two sets used in turn: a slice's inputs are issued into the other set
+  // while the slice before it computes
+  struct KIn {
+    float xq[CPT], xk[CPT], xg[RPS], dQg[CPT], dKg[CPT], dKb[CPT];
+  };
+  auto issue = [&](int c0, KIn& in) {
     const size_t o = (static_cast<size_t>(cl.t0 + rowc) * H + h) * DK + c0 + c8;
-    loadn<CPT>(q + o, xq);
-    loadn<CPT>(k + o, xk);
+    loadn<CPT>(q + o, in.xq);
+    loadn<CPT>(k + o, in.xk);
 #pragma unroll
     for (int i = 0; i < RPS; ++i)
-      xg[i] = gate_at<G, DK>(la, static_cast<size_t>(cl.t0 + min(gseg * RPS + i, cl.len - 1)), H, h, c0 + gch);
+      in.xg[i] = gate_at<G, DK>(la, static_cast<size_t>(cl.t0 + min(gseg * RPS + i, cl.len - 1)), H, h, c0 + gch);
     const size_t ob = static_cast<size_t>(row) * DK + c0 + c8;
-    loadn<CPT>(bk + B::odQg + ob, dQg);
-    loadn<CPT>(bk + B::odKg + ob, dKg);
-    loadn<CPT>(bk + B::odKb + ob, dKb);
+    loadn<CPT>(bk + B::odQg + ob, in.dQg);
+    loadn<CPT>(bk + B::odKg + ob, in.dKg);
+    loadn<CPT>(bk + B::odKb + ob, in.dKb);
   };
-  issue(zs * NSW * SW);
+  KIn ina, inb;
+  issue(zs * NSW * SW, ina);
   {
     f32x4 a[BC * BC / 4 / 256], b[BC * BC / 4 / 256];
 #pragma unroll
@@ -1523,20 +1528,20 @@ __global__ __launch_bounds__(256) void bwd_grad_k_kernel(const T* __restrict__ q
     }
   }
   if (tid < BC) rsum[tid] = 0.f;
-  for (int si = 0; si < NSW; ++si) {
+  auto slice = [&](int si, const KIn& cur, KIn& nxt) {
     const int c0 = (zs * NSW + si) * SW;
-    if (si > 0) issue(c0);
     {
       const bool live = row < cl.len;
 #pragma unroll
-      for (int i = 0; i < CPT; ++i) qs[row * PS + c8 + i] = live ? xq[i] : 0.f, ks[row * PS + c8 + i] = live ? xk[i] : 0.f;
+      for (int i = 0; i < CPT; ++i) qs[row * PS + c8 + i] = live ? cur.xq[i] : 0.f, ks[row * PS + c8 + i] = live ? cur.xk[i] : 0.f;
 #pragma unroll
       for (int i = 0; i < RPS; ++i) {
         const int rr = gseg * RPS + i;
-        gs[rr * PS + gch] = rr < cl.len ? xg[i] : 0.f;
+        gs[rr * PS + gch] = rr < cl.len ? cur.xg[i] : 0.f;
       }
     }
     lds_sync();
+    if (si + 1 < NSW) issue(c0 + SW, nxt);  // this slice's inputs are in LDS or kept in cur
     row_scan<false, PS, SW>(gs, tot);
     // scaled operands of the off-diagonal block pairs
     for (int e = tid; e < 96 * SW; e += 256) {
@@ -1655,10 +1660,10 @@ __global__ __launch_bounds__(256) void bwd_grad_k_kernel(const T* __restrict__ q
     for (int i = 0; i < CPT; ++i) {
       const float qv = qs[row * PS + c8 + i], kv = ks[row * PS + c8 + i];
       const float eg = __expf(Gr[i]), eb = __expf(gs[(BC - 1) * PS + c8 + i] - Gr[i]);
-      dqv[i] = dQg[i] * eg + GQ[i] + dpd * kv;
-      dkv[i] = dKg[i] * eg + dKb[i] * eb + GA[i] + G2[i] + dpd * qv;
-      cs[i] = last ? 0.f : dKb[i] * kv * eb;
-      dG[i] = (dQg[i] * qv + dKg[i] * kv) * eg - cs[i] + qv * GQ[i] + kv * (GA[i] - G2[i]);
+      dqv[i] = cur.dQg[i] * eg + GQ[i] + dpd * kv;
+      dkv[i] = cur.dKg[i] * eg + cur.dKb[i] * eb + GA[i] + G2[i] + dpd * qv;
+      cs[i] = last ? 0.f : cur.dKb[i] * kv * eb;
+      dG[i] = (cur.dQg[i] * qv + cur.dKg[i] * kv) * eg - cs[i] + qv * GQ[i] + kv * (GA[i] - G2[i]);
     }
     if (row < cl.len) {
       const size_t o = (static_cast<size_t>(cl.t0 + row) * H + h) * DK + c0 + c8;
@@ -1694,6 +1699,11 @@ __global__ __launch_bounds__(256) void bwd_grad_k_kernel(const T* __restrict__ q
       }
     }
     lds_sync();
+    };
+  static_assert(NSW % 2 == 0, "slices taken two at a time");
+  for (int si = 0; si < NSW; si += 2) {
+    slice(si, ina, inb);
+    slice(si + 1, inb, ina);
   }
   if constexpr (G == KDA_GATE_SCALAR) {
     if (tid < cl.len) dla[static_cast<size_t>(cl.t0 + tid) * H + h] = rsum[tid];
