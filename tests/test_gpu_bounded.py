@@ -107,3 +107,43 @@ def test_bounded_gate_forms(gate):
     o_1, S_1 = gpu_prefill(w, one_stream=True)
     assert np.array_equal(o_b, o_1)
     assert np.array_equal(S_b, S_1)
+
+
+def test_two_streams_overlapped_and_ring():
+    """An overlapped call and a bounded ring call enqueued on two caller
+    streams at once, three times, with nothing synchronised in between: both
+    share the library's per-device streams and events, each keeps its own
+    workspace (one per caller stream), and each result equals its one-stream
+    result bit for bit."""
+    import torch
+    import gated_delta_rule_33_amd as kda
+    from tests.gpu_helpers import dev, host
+    w1 = synth.make_prefill([9000], H=4, dk=128, dv=128, io_dtype="bf16", seed=970, S0_std=0.05)
+    w2 = synth.make_prefill([5000, 4000], H=2, dk=128, dv=128, io_dtype="bf16", seed=971, S0_std=0.05)
+    carry2 = w2.num_seqs * 2 * 128 * 128 * 4
+    cap2 = _min_bytes(w2) - carry2 - 2 * _block_bytes(w2) + (2 * 64 + 3) * 2 * _block_bytes(w2)
+    log("two streams: overlapped %s x 4 heads, bounded ring %s x 2 heads" % ([9000], [5000, 4000]))
+    o1_ref, S1_ref = gpu_prefill(w1, one_stream=True)
+    o2_ref, S2_ref = gpu_prefill(w2, one_stream=True)
+
+    def up(w):
+        return dict(q=dev(w.q, "bf16"), k=dev(w.k, "bf16"), v=dev(w.v, "bf16"), la=dev(w.log_alpha),
+                    b=dev(w.beta), cu=dev(w.cu_seqlens), S0=dev(w.S0), hc=w.cu_seqlens.tolist())
+    a, b = up(w1), up(w2)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            r1 = kda.prefill(a["q"], a["k"], a["v"], a["la"], a["b"], a["cu"], a["S0"], cu_seqlens_host=a["hc"],
+                             stream=s1)
+        with torch.cuda.stream(s2):
+            r2 = kda.prefill(b["q"], b["k"], b["v"], b["la"], b["b"], b["cu"], b["S0"], cu_seqlens_host=b["hc"],
+                             stream=s2, max_workspace_bytes=cap2)
+        outs.append((r1, r2))
+    torch.cuda.synchronize()
+    for (o1, S1), (o2, S2) in outs:
+        assert np.array_equal(host(o1), o1_ref)
+        assert np.array_equal(host(S1), S1_ref)
+        assert np.array_equal(host(o2), o2_ref)
+        assert np.array_equal(host(S2), S2_ref)
